@@ -1,0 +1,98 @@
+/*
+ * oracle.h -- plain CPU reference of the fast-multipole gravity evaluation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this; only the test-suite, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no source, header or table with the GPU
+ * library.
+ *
+ * Everything is fp64 (fp32 inputs are widened exactly by the caller), G = 1,
+ * no softening.  Source: the jz-fmm project page (sections "From particle pairs
+ * to node pairs", "Describing the source and the receiving region",
+ * "Calculating a node-node interaction", "Combining near and far
+ * interactions").  The readings taken where the page is silent are listed in
+ * oracle.c next to the code that implements them.
+ *
+ * Coefficient layout used by the copy-out functions (shared *convention*
+ * with the GPU library's introspection call, not shared code): multi-indices
+ * (a,b,c) with a+b+c <= p, ordered by total degree d = 0..p, then a
+ * descending, then b descending.  Multipoles are the raw power sums
+ * M_(a,b,c) = sum_j m_j sx^a sy^b sz^c about the cell centre; locals are the
+ * derivatives L_(a,b,c) = d^a_x d^b_y d^c_z Phi at the cell centre.
+ */
+#ifndef MBG_ORACLE_H
+#define MBG_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ORACLE_OK = 0,
+  ORACLE_ERR_ARG = -1,
+  ORACLE_ERR_OOM = -3,
+  ORACLE_ERR_NONFINITE = -5
+};
+
+typedef struct oracle_result oracle_result;
+
+/* Number of coefficients of an expansion of total degree p: C(p+3,3). */
+int oracle_ncoef(int order);
+
+/* Thread count for the OpenMP loops (0 = leave the runtime default). */
+void oracle_set_threads(int n);
+
+/* O(N^2) direct sum, self term omitted by index.  Targets are indices into
+ * pos; phi[t], acc[3t..3t+2] receive target t's results. */
+int oracle_direct(int64_t n, const double* pos, const double* mass,
+                  int64_t n_targets, const int64_t* targets,
+                  double* phi, double* acc);
+
+/* Full FMM evaluation.  If n_sample > 0, only the leaves holding the listed
+ * particles (and their ancestors) are treated as targets: the tree, keys and
+ * all multipoles are complete, the interaction lists are exact for the marked
+ * targets and empty for the others, and phi/acc are valid for every particle
+ * of a marked leaf (NaN elsewhere).  stage_mask bit 0 = run the numeric
+ * passes (clear it to stop after the walk). */
+int oracle_fmm(int64_t n, const double* pos, const double* mass, int order,
+               double theta, int leaf_size, int64_t n_sample,
+               const int64_t* sample, int stage_mask, oracle_result** out);
+void oracle_free(oracle_result* r);
+
+/* sizes[0..6] = n_nodes, n_leaves, depth, n_m2l, n_p2p, n_marked_nodes, K */
+void oracle_sizes(const oracle_result* r, int64_t* sizes);
+/* root cube: lo[3] anchor, *side = power-of-two cube side */
+void oracle_root(const oracle_result* r, double* lo, double* side);
+/* stage wall times in seconds: [keys+sort, tree, walk, p2m+m2m, m2l, l2l+l2p, p2p, total] */
+void oracle_times(const oracle_result* r, double* t8);
+void oracle_copy_keys(const oracle_result* r, uint64_t* sorted_keys, int32_t* perm);
+void oracle_copy_tree(const oracle_result* r, uint8_t* level, uint64_t* prefix,
+                      int32_t* begin, int32_t* count, int32_t* parent,
+                      int32_t* first_child, uint8_t* n_child);
+void oracle_copy_lists(const oracle_result* r, int64_t* m2l_off, int32_t* m2l_src,
+                       int64_t* p2p_off, int32_t* p2p_src);
+void oracle_copy_mark(const oracle_result* r, uint8_t* node_mark);
+/* node_count x K arrays in the layout above; NULL skips one */
+void oracle_copy_expansions(const oracle_result* r, double* mpole, double* local);
+/* results in the caller's particle order */
+void oracle_copy_result(const oracle_result* r, double* phi, double* acc);
+
+/* Single-operator entry points, for pinning each step on its own. */
+int oracle_p2m(int order, int64_t n, const double* pos, const double* mass,
+               const double* centre, double* mpole);
+int oracle_m2m(int order, const double* mpole_child, const double* d,
+               double* mpole_parent_accum);
+int oracle_dtensor(int order, const double* r, double* dtens);
+int oracle_m2l(int order, const double* mpole, const double* r, double* local_accum);
+int oracle_l2l(int order, const double* local_parent, const double* d,
+               double* local_child_accum);
+int oracle_l2p(int order, const double* local, const double* delta,
+               double* phi, double* acc);
+int oracle_morton(int64_t n, const double* pos, double* lo, double* side,
+                  uint64_t* keys);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
