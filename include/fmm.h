@@ -1,0 +1,146 @@
+/*
+ * fmm.h -- C-ABI of the MI355X (gfx950) fast-multipole gravity library
+ * (libmbg_fmm.so).
+ *
+ * What it computes (jz-fmm project page):
+ *   phi_i = -G sum_{j != i} m_j / |x_i - x_j|        ("From particle pairs to
+ *   a_i   = -grad phi_i                                node pairs", direct-sum
+ *                                                      equation; self term omitted)
+ * approximated by the fast multipole method: Cartesian multipole moments of
+ * every octree cell ("Describing the source and the receiving region", moment
+ * equations), multipole-to-local translations of accepted cell pairs into local
+ * Taylor coefficients ("Calculating a node-node interaction", the two closed
+ * forms), the opening criterion theta = |l_A + l_B| / |c_A - c_B| with the pair
+ * opened iff theta >= theta_max (same section), and the upward / interaction /
+ * downward passes with a direct near field ("Combining near and far
+ * interactions").  G = 1 (scale the outputs by G), no softening.
+ *
+ * Conventions shared by every call:
+ *   - Order p: multipoles and locals keep total degree <= p and the
+ *     translation keeps |n| + |m| <= p.  0 <= p <= FMM_MAX_ORDER.
+ *   - The octree root is the cube anchored at the per-axis minimum of the
+ *     positions with the smallest power-of-two side >= the largest extent;
+ *     keys have 21 bits per axis (x the most significant bit of each triple);
+ *     a cell is a leaf iff it holds <= leaf_size particles or is at level 21;
+ *     expansion centres are geometric cell centres; cells are numbered
+ *     breadth first (level, then key).  The criterion is evaluated exactly in
+ *     integer cell units: accept iff 3 (h_A + h_B)^2 < fl(theta^2) |c_A - c_B|^2.
+ *   - The walk splits the coarser non-leaf of a rejected pair (both when the
+ *     levels are equal); accepted pairs are translated (M2L), rejected leaf
+ *     pairs are summed directly (P2P).  Lists are directed, per target, with
+ *     sources ascending.
+ *   - Positions are row-major [N][3], masses [N], phi [N], acc [N][3], all in
+ *     the plan's dtype and all DEVICE pointers owned by the caller; outputs are
+ *     in the caller's particle order.
+ *   - Every call returns an fmm_status code and never aborts.  Work is ordered
+ *     on the HIP stream passed in (NULL = the default stream).  A plan is not
+ *     thread-safe; distinct plans may run concurrently on distinct streams.
+ *   - The same inputs and plan give bitwise-identical results on the same GPU:
+ *     every accumulation has a fixed owner and a fixed order (no floating-point
+ *     atomics).  (jz-fmm page, "Why reversibility matters": the force must be
+ *     reproducible.)
+ */
+#ifndef MBG_FMM_H
+#define MBG_FMM_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FMM_MAX_ORDER 8
+
+typedef struct fmm_plan_s* fmm_plan_t; /* opaque, owned by the library */
+
+enum fmm_dtype { FMM_F32 = 0, FMM_F64 = 1 };
+
+enum fmm_status {
+  FMM_OK = 0,
+  FMM_ERR_ARG = -1,       /* argument out of range / NULL pointer */
+  FMM_ERR_STATE = -2,     /* eval or copy before a successful build */
+  FMM_ERR_OOM = -3,       /* device allocation failed */
+  FMM_ERR_HIP = -4,       /* a HIP runtime call failed */
+  FMM_ERR_NONFINITE = -5, /* NaN or Inf in positions or masses */
+  FMM_ERR_NODEVICE = -6   /* no HIP device visible */
+};
+
+/* Stage indices of fmm_stats_t.stage_ms (filled when timing is enabled). */
+enum fmm_stage {
+  FMM_STAGE_KEYS = 0,  /* bounding box + Morton keys            */
+  FMM_STAGE_SORT = 1,  /* radix sort + gather into sorted order */
+  FMM_STAGE_TREE = 2,  /* octree build                          */
+  FMM_STAGE_WALK = 3,  /* dual-tree walk, M2L and P2P lists     */
+  FMM_STAGE_UP = 4,    /* P2M + M2M                             */
+  FMM_STAGE_M2L = 5,   /* the single M2L launch                 */
+  FMM_STAGE_DOWN = 6,  /* L2L + L2P                             */
+  FMM_STAGE_P2P = 7,   /* the single P2P (+ combine) launch     */
+  FMM_N_STAGES = 8
+};
+
+typedef struct {
+  int64_t n, n_nodes, n_leaves, n_m2l, n_p2p;
+  int32_t depth, order, leaf_size, dtype;
+  double theta;
+  double lo[3], side;    /* root cube */
+  float stage_ms[FMM_N_STAGES]; /* last build/eval, when timing is on */
+  int32_t walk_retries;  /* workspace regrowths during the last walk */
+  int32_t reserved[7];
+} fmm_stats_t;
+
+/* Create a plan for N particles.  N in [1, 2^31), order in [0, FMM_MAX_ORDER],
+ * theta in (0, 1), leaf_size >= 1, dtype FMM_F32 or FMM_F64.  Allocates the
+ * N-sized device workspace on the current device; data-dependent buffers grow
+ * on demand during builds (grow-only, freed by fmm_destroy). */
+int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size, int dtype);
+
+/* Sort the particles, build the octree and the interaction lists.  pos [N][3]
+ * and mass [N] are device arrays in the plan's dtype; they are copied into the
+ * plan's sorted layout, so the caller may reuse them once `stream` has passed
+ * this call.  Synchronizes `stream` twice (tree size, list sizes).  Returns
+ * FMM_ERR_NONFINITE (and leaves the plan un-built) if any input is NaN/Inf. */
+int fmm_build(fmm_plan_t plan, const void* pos, const void* mass, void* stream);
+
+/* Evaluate potential and acceleration of every particle: P2M, M2M, M2L, L2L,
+ * L2P, P2P, written in the caller's order.  phi [N] and acc [N][3] are device
+ * arrays in the plan's dtype.  Asynchronous on `stream`; may be repeated after
+ * one build. */
+int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
+
+/* Free the plan and its workspace (synchronizes the device). */
+int fmm_destroy(fmm_plan_t plan);
+
+/* Static string for a status code. */
+const char* fmm_strerror(int code);
+
+/* Turn per-stage HIP-event timing on (1) or off (0); read via fmm_stats. */
+int fmm_set_timing(fmm_plan_t plan, int enable);
+
+/* Sizes of the last build and, with timing on, stage times (synchronizes). */
+int fmm_stats(fmm_plan_t plan, fmm_stats_t* out);
+
+/* ---- introspection (host copies for parity checks; each synchronizes) ---- */
+
+/* sorted_keys [N] and perm [N] (perm[k] = caller index of sorted particle k). */
+int fmm_copy_keys(fmm_plan_t plan, uint64_t* sorted_keys, int32_t* perm);
+
+/* Node arrays [n_nodes], breadth-first order; NULL skips an array.
+ * first_child is -1 for leaves. */
+int fmm_copy_tree(fmm_plan_t plan, uint8_t* level, uint64_t* prefix, int32_t* begin,
+                  int32_t* count, int32_t* parent, int32_t* first_child, uint8_t* n_child);
+
+/* Interaction lists in CSR by target node: m2l_off [n_nodes+1], m2l_src
+ * [n_m2l], p2p_off [n_nodes+1], p2p_src [n_p2p]; NULL skips an array. */
+int fmm_copy_lists(fmm_plan_t plan, int64_t* m2l_off, int32_t* m2l_src, int64_t* p2p_off,
+                   int32_t* p2p_src);
+
+/* Multipoles and locals after the last eval, [n_nodes][C(p+3,3)] fp64, for
+ * multi-indices (a,b,c) ordered by degree, then a descending, then b
+ * descending.  mpole = raw moments sum_j m_j s^(a,b,c) about the cell centre;
+ * local = derivatives d^(a,b,c) phi at the cell centre (with every ancestor's
+ * contribution translated in).  NULL skips one. */
+int fmm_copy_expansions(fmm_plan_t plan, double* mpole, double* local);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,488 @@
+// fmm_api.hip -- host side of the C-ABI in include/fmm.h: plan and workspace
+// management, stage sequencing, the two build synchronizations, timing and
+// introspection copies.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "fmm_internal.h"
+
+using namespace mbg;
+
+namespace mbg {
+hipError_t launch_walk_root(int pass, int root_leaf, const WalkArgs& a, hipStream_t st);
+hipError_t launch_walk_reset(Control* ctrl, hipStream_t st);
+hipError_t launch_walk_totals(const int64_t* m2l_total, const int64_t* p2p_total, Control* ctrl,
+                              hipStream_t st);
+}  // namespace mbg
+
+namespace {
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return FMM_OK;
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return FMM_ERR_OOM;
+  return FMM_ERR_HIP;
+}
+
+#define TRY_HIP(x)                     \
+  do {                                 \
+    hipError_t _e = (x);               \
+    if (_e != hipSuccess) return status_of(_e); \
+  } while (0)
+#define TRY(x)                    \
+  do {                            \
+    int _r = (x);                 \
+    if (_r != FMM_OK) return _r;  \
+  } while (0)
+
+// Grow-only allocation (with 1/8 slack so that small fluctuations between
+// builds do not reallocate).
+int grow(DBuf& b, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  if (bytes <= b.cap) return FMM_OK;
+  if (b.p) {
+    hipError_t e = hipFree(b.p);
+    if (e != hipSuccess) return status_of(e);
+  }
+  b.p = nullptr;
+  b.cap = 0;
+  size_t want = bytes + bytes / 8;
+  want = (want + 255) & ~(size_t)255;
+  if (hipMalloc(&b.p, want) != hipSuccess) {
+    b.p = nullptr;
+    return FMM_ERR_OOM;
+  }
+  b.cap = want;
+  return FMM_OK;
+}
+
+void release(DBuf& b) {
+  if (b.p) (void)hipFree(b.p);
+  b.p = nullptr;
+  b.cap = 0;
+}
+
+template <typename T>
+T* P(DBuf& b) {
+  return static_cast<T*>(b.p);
+}
+
+size_t wbytes(int dtype) { return dtype == FMM_F64 ? 8 : 4; }
+
+void rec(fmm_plan_t p, int stage, int end, hipStream_t st) {
+  if (p->timing) (void)hipEventRecord(p->ev[2 * stage + end], st);
+}
+
+int bbox_blocks(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  return (int)std::min<int64_t>(std::max<int64_t>(b, 1), 1024);
+}
+
+int sync_ctrl(fmm_plan_t p, hipStream_t st) {
+  TRY_HIP(hipMemcpyAsync(p->ctrl_host, p->ctrl.p, sizeof(Control), hipMemcpyDeviceToHost, st));
+  TRY_HIP(hipStreamSynchronize(st));
+  return FMM_OK;
+}
+
+// ---------------- walk ----------------
+int run_walk(fmm_plan_t p, hipStream_t st) {
+  const int depth = p->depth;
+  const int64_t nn = p->n_nodes;
+  // item capacities: type-A items of step s come from leaf items of step s-1
+  int64_t amax[MAX_LEVELS + 2] = {0}, base[MAX_LEVELS + 3] = {0};
+  for (int s = 1; s <= depth + 1; s++) {
+    int64_t leaves_prev = (s - 1 <= MAX_LEVELS - 1) ? p->leaves_at_level[s - 1] : 0;
+    amax[s] = amax[s - 1] + leaves_prev;
+  }
+  for (int s = 0; s <= depth + 1; s++) {
+    int64_t lc = (s <= depth) ? p->level_off[s + 1] - p->level_off[s] : 0;
+    base[s + 1] = base[s] + amax[s] + lc;
+  }
+  const int64_t n_items = base[depth + 2];
+  for (int s = 0; s <= depth + 1; s++) {
+    p->item_base[s] = base[s];
+    p->item_amax[s] = amax[s];
+  }
+  // item SoA: tgt i32, gen_off i64, gen_cnt i32, carry_off i64, carry_cnt i32
+  TRY(grow(p->items, (size_t)n_items * 28 + 64));
+  char* ib = P<char>(p->items);
+  WalkItems it;
+  it.gen_off = (int64_t*)ib;
+  it.carry_off = it.gen_off + n_items;
+  it.tgt = (int32_t*)(it.carry_off + n_items);
+  it.gen_cnt = it.tgt + n_items;
+  it.carry_cnt = it.gen_cnt + n_items;
+
+  TRY(grow(p->tot_m2l, (size_t)(nn + 1) * 8));
+  TRY(grow(p->tot_p2p, (size_t)(nn + 1) * 8));
+  TRY(grow(p->cur_m2l, (size_t)(nn + 1) * 8));
+  TRY(grow(p->cur_p2p, (size_t)(nn + 1) * 8));
+  TRY(grow(p->m2l_off, (size_t)(nn + 1) * 8));
+  TRY(grow(p->p2p_off, (size_t)(nn + 1) * 8));
+  TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
+  if (p->carry_cap < 64 * nn + 1024) {
+    p->carry_cap = std::max<int64_t>(p->carry_cap, 160 * nn + 1024);
+  }
+  TRY(grow(p->carry, (size_t)p->carry_cap * 4));
+
+  WalkArgs a{};
+  a.level = P<uint8_t>(p->nlevel);
+  a.q = P<uint64_t>(p->nq);
+  a.first_child = P<int32_t>(p->nfirst);
+  a.n_child = P<uint8_t>(p->nnchild);
+  a.parent = P<int32_t>(p->nparent);
+  a.t2 = p->t2;
+  a.it = it;
+  a.carry = P<int32_t>(p->carry);
+  a.carry_cap = p->carry_cap;
+  a.tot_m2l = P<int64_t>(p->tot_m2l);
+  a.tot_p2p = P<int64_t>(p->tot_p2p);
+  a.cur_m2l = P<int64_t>(p->cur_m2l);
+  a.cur_p2p = P<int64_t>(p->cur_p2p);
+  a.m2l_off = P<int64_t>(p->m2l_off);
+  a.p2p_off = P<int64_t>(p->p2p_off);
+  a.ctrl = P<Control>(p->ctrl);
+  const int root_leaf = (depth == 0) ? 1 : 0;
+  auto step_args = [&](int s) {
+    WalkArgs b = a;
+    b.step = s;
+    b.lvl_begin = p->level_off[s];
+    b.lvl_count = p->level_off[s + 1] - p->level_off[s];
+    b.prev_lvl_begin = s > 0 ? p->level_off[s - 1] : 0;
+    b.base = base[s];
+    b.amax = amax[s];
+    b.prev_base = s > 0 ? base[s - 1] : 0;
+    b.prev_amax = s > 0 ? amax[s - 1] : 0;
+    b.next_base = base[s + 1];
+    b.next_amax = amax[s + 1];
+    return b;
+  };
+
+  p->walk_retries = 0;
+  for (;;) {
+    TRY_HIP(launch_fill_zero(p->tot_m2l.p, (size_t)(nn + 1) * 8, st));
+    TRY_HIP(launch_fill_zero(p->tot_p2p.p, (size_t)(nn + 1) * 8, st));
+    TRY_HIP(launch_walk_reset(P<Control>(p->ctrl), st));
+    TRY_HIP(launch_walk_root(1, root_leaf, step_args(0), st));
+    for (int s = 1; s <= depth; s++) TRY_HIP(launch_walk_pass1(step_args(s), st));
+    TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_m2l), P<int64_t>(p->m2l_off), nn,
+                               P<int64_t>(p->m2l_off) + nn, p->scan_tmp.p, st));
+    TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_p2p), P<int64_t>(p->p2p_off), nn,
+                               P<int64_t>(p->p2p_off) + nn, p->scan_tmp.p, st));
+    TRY_HIP(launch_walk_totals(P<int64_t>(p->m2l_off) + nn, P<int64_t>(p->p2p_off) + nn,
+                               P<Control>(p->ctrl), st));
+    TRY(sync_ctrl(p, st));
+    if (!p->ctrl_host->carry_overflow) break;
+    if (++p->walk_retries > 4) return FMM_ERR_OOM;
+    int64_t need = p->ctrl_host->carry_used;
+    p->carry_cap = std::max<int64_t>(need + need / 4 + 1024, 2 * p->carry_cap);
+    TRY(grow(p->carry, (size_t)p->carry_cap * 4));
+    a.carry = P<int32_t>(p->carry);
+    a.carry_cap = p->carry_cap;
+  }
+  p->n_m2l = p->ctrl_host->n_m2l;
+  p->n_p2p = p->ctrl_host->n_p2p;
+  TRY(grow(p->m2l_src, (size_t)p->n_m2l * 4));
+  TRY(grow(p->p2p_src, (size_t)p->n_p2p * 4));
+  a.m2l_src = P<int32_t>(p->m2l_src);
+  a.p2p_src = P<int32_t>(p->p2p_src);
+  TRY_HIP(launch_fill_zero(p->cur_m2l.p, (size_t)(nn + 1) * 8, st));
+  TRY_HIP(launch_fill_zero(p->cur_p2p.p, (size_t)(nn + 1) * 8, st));
+  TRY_HIP(launch_walk_root(2, root_leaf, step_args(0), st));
+  for (int s = 1; s <= depth; s++) TRY_HIP(launch_walk_pass2(step_args(s), st));
+  return FMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fmm_strerror(int code) {
+  switch (code) {
+    case FMM_OK: return "ok";
+    case FMM_ERR_ARG: return "invalid argument";
+    case FMM_ERR_STATE: return "plan not built";
+    case FMM_ERR_OOM: return "device out of memory";
+    case FMM_ERR_HIP: return "HIP runtime error";
+    case FMM_ERR_NONFINITE: return "non-finite position or mass";
+    case FMM_ERR_NODEVICE: return "no HIP device";
+    default: return "unknown status";
+  }
+}
+
+int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size, int dtype) {
+  if (!out) return FMM_ERR_ARG;
+  *out = nullptr;
+  if (n < 1 || n >= ((int64_t)1 << 31) || order < 0 || order > FMM_MAX_ORDER || !(theta > 0.0) ||
+      !(theta < 1.0) || leaf_size < 1 || (dtype != FMM_F32 && dtype != FMM_F64))
+    return FMM_ERR_ARG;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return FMM_ERR_NODEVICE;
+  fmm_plan_t p = new (std::nothrow) fmm_plan_s();
+  if (!p) return FMM_ERR_OOM;
+  p->n = n;
+  p->order = order;
+  p->K = ncoef(order);
+  p->leaf = leaf_size;
+  p->dtype = dtype;
+  p->theta = theta;
+  p->t2 = theta * theta;  // one rounding, as the criterion specifies
+  int rc = FMM_OK;
+  auto fail = [&](int r) {
+    fmm_destroy(p);
+    return r;
+  };
+  if (hipGetDevice(&p->device) != hipSuccess) return fail(FMM_ERR_HIP);
+  const size_t w = wbytes(dtype);
+  if ((rc = grow(p->keys, 8 * n)) || (rc = grow(p->keys_alt, 8 * n)) || (rc = grow(p->idx, 4 * n)) ||
+      (rc = grow(p->idx_alt, 4 * n)) || (rc = grow(p->pts, 4 * w * n)) ||
+      (rc = grow(p->far, 4 * w * n)) || (rc = grow(p->lcp, n)) || (rc = grow(p->leaf_level, n)) ||
+      (rc = grow(p->leaf_of, 4 * n)) || (rc = grow(p->radix_hist, 4 * radix_hist_ints(n))) ||
+      (rc = grow(p->scan_tmp, scan_tmp_bytes(std::max<int64_t>(n, 1 << 20)))) ||
+      (rc = grow(p->root, sizeof(RootInfo))) || (rc = grow(p->ctrl, sizeof(Control))) ||
+      (rc = grow(p->bbox_part, 6 * 8 * 1024)) || (rc = grow(p->lvl_blkcnt, 8 * tree_blkcnt_len(n))))
+    return fail(rc);
+  if ((int64_t)leaf_size < n) {
+    if ((rc = grow(p->wlev, (size_t)(n + leaf_size))) || (rc = grow(p->wtmp, (size_t)(n + leaf_size))))
+      return fail(rc);
+  }
+  if (hipHostMalloc((void**)&p->ctrl_host, sizeof(Control), hipHostMallocDefault) != hipSuccess)
+    return fail(FMM_ERR_OOM);
+  for (int i = 0; i < 2 * FMM_N_STAGES; i++)
+    if (hipEventCreate(&p->ev[i]) != hipSuccess) return fail(FMM_ERR_HIP);
+  *out = p;
+  return FMM_OK;
+}
+
+int fmm_destroy(fmm_plan_t p) {
+  if (!p) return FMM_ERR_ARG;
+  (void)hipDeviceSynchronize();
+  DBuf* bufs[] = {&p->keys, &p->keys_alt, &p->idx, &p->idx_alt, &p->pts, &p->far, &p->perm_inv,
+                  &p->lcp, &p->wlev, &p->wtmp, &p->leaf_level, &p->leaf_of, &p->radix_hist,
+                  &p->scan_tmp, &p->root, &p->ctrl, &p->bbox_part, &p->nlevel, &p->nprefix,
+                  &p->nbegin, &p->ncount, &p->nparent, &p->nfirst, &p->nnchild, &p->ncentre,
+                  &p->nq, &p->leaves, &p->lvl_blkcnt, &p->mpole, &p->local, &p->items, &p->carry,
+                  &p->tot_m2l, &p->tot_p2p, &p->cur_m2l, &p->cur_p2p, &p->m2l_off, &p->m2l_src,
+                  &p->p2p_off, &p->p2p_src};
+  for (DBuf* b : bufs) release(*b);
+  if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);
+  for (int i = 0; i < 2 * FMM_N_STAGES; i++)
+    if (p->ev[i]) (void)hipEventDestroy(p->ev[i]);
+  delete p;
+  return FMM_OK;
+}
+
+int fmm_set_timing(fmm_plan_t p, int enable) {
+  if (!p) return FMM_ERR_ARG;
+  p->timing = enable != 0;
+  return FMM_OK;
+}
+
+int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
+  if (!p || !pos || !mass) return FMM_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  TRY_HIP(hipSetDevice(p->device));
+  p->built = false;
+  p->evaluated = false;
+  const int64_t n = p->n;
+  Control* ctrl = P<Control>(p->ctrl);
+  RootInfo* root = P<RootInfo>(p->root);
+
+  rec(p, FMM_STAGE_KEYS, 0, st);
+  TRY_HIP(launch_fill_zero(ctrl, sizeof(Control), st));
+  const int nbb = bbox_blocks(n);
+  TRY_HIP(launch_bbox(pos, mass, n, p->dtype, P<double>(p->bbox_part), nbb, root, ctrl, st));
+  TRY_HIP(launch_keys(pos, n, p->dtype, root, P<uint64_t>(p->keys), P<int32_t>(p->idx), st));
+  rec(p, FMM_STAGE_KEYS, 1, st);
+
+  rec(p, FMM_STAGE_SORT, 0, st);
+  TRY_HIP(launch_radix_sort(P<uint64_t>(p->keys), P<int32_t>(p->idx), P<uint64_t>(p->keys_alt),
+                            P<int32_t>(p->idx_alt), n, P<int32_t>(p->radix_hist),
+                            P<int32_t>(p->scan_tmp), st));
+  TRY_HIP(launch_gather(pos, mass, P<int32_t>(p->idx), n, p->dtype, p->pts.p, st));
+  rec(p, FMM_STAGE_SORT, 1, st);
+
+  rec(p, FMM_STAGE_TREE, 0, st);
+  TRY_HIP(launch_tree_phase1(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
+                             P<int8_t>(p->wlev), P<int8_t>(p->wtmp), P<int8_t>(p->leaf_level),
+                             P<int64_t>(p->lvl_blkcnt), p->scan_tmp.p, ctrl, st));
+  TRY_HIP(hipMemcpyAsync(&p->root_host, root, sizeof(RootInfo), hipMemcpyDeviceToHost, st));
+  TRY(sync_ctrl(p, st));
+  if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;
+  const Control& c = *p->ctrl_host;
+  const int64_t nn = c.level_off[MAX_LEVELS];
+  p->n_nodes = nn;
+  p->depth = 0;
+  p->n_leaves = 0;
+  for (int l = 0; l <= MAX_LEVELS; l++) p->level_off[l] = c.level_off[l];
+  for (int l = 0; l < MAX_LEVELS; l++) {
+    p->leaves_at_level[l] = c.leaves_at_level[l];
+    p->n_leaves += c.leaves_at_level[l];
+    if (c.level_off[l + 1] > c.level_off[l]) p->depth = l;
+  }
+  const size_t w = wbytes(p->dtype);
+  TRY(grow(p->nlevel, nn));
+  TRY(grow(p->nprefix, 8 * nn));
+  TRY(grow(p->nbegin, 4 * nn));
+  TRY(grow(p->ncount, 4 * nn));
+  TRY(grow(p->nparent, 4 * nn));
+  TRY(grow(p->nfirst, 4 * nn));
+  TRY(grow(p->nnchild, nn));
+  TRY(grow(p->ncentre, 24 * nn));
+  TRY(grow(p->nq, 8 * nn));
+  TRY(grow(p->leaves, 4 * (3 * nn + 2)));
+  TRY(grow(p->mpole, w * p->K * nn));
+  TRY(grow(p->local, w * p->K * nn));
+  TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
+  TreeArrays t{P<uint8_t>(p->nlevel),  P<uint64_t>(p->nprefix), P<int32_t>(p->nbegin),
+               P<int32_t>(p->ncount),  P<int32_t>(p->nparent),  P<int32_t>(p->nfirst),
+               P<uint8_t>(p->nnchild), P<double>(p->ncentre),   P<uint64_t>(p->nq)};
+  int32_t* leaves = P<int32_t>(p->leaves);
+  TRY_HIP(launch_tree_phase2(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
+                             P<int8_t>(p->leaf_level), P<int64_t>(p->lvl_blkcnt), nn, p->level_off,
+                             root, t, leaves + nn, leaves + 2 * nn + 1, leaves,
+                             P<int32_t>(p->leaf_of), p->scan_tmp.p, ctrl, st));
+  rec(p, FMM_STAGE_TREE, 1, st);
+
+  rec(p, FMM_STAGE_WALK, 0, st);
+  TRY(run_walk(p, st));
+  rec(p, FMM_STAGE_WALK, 1, st);
+  p->built = true;
+  return FMM_OK;
+}
+
+int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
+  if (!p || !phi || !acc) return FMM_ERR_ARG;
+  if (!p->built) return FMM_ERR_STATE;
+  hipStream_t st = (hipStream_t)stream;
+  TRY_HIP(hipSetDevice(p->device));
+  const int dt = p->dtype, ord = p->order;
+  const double* centre = P<double>(p->ncentre);
+  int32_t* leaves = P<int32_t>(p->leaves);
+
+  rec(p, FMM_STAGE_UP, 0, st);
+  TRY_HIP(launch_p2m(dt, ord, p->pts.p, leaves, p->n_leaves, P<int32_t>(p->nbegin),
+                     P<int32_t>(p->ncount), centre, p->mpole.p, st));
+  for (int l = p->depth - 1; l >= 0; l--)
+    TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                       P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, st));
+  rec(p, FMM_STAGE_UP, 1, st);
+
+  rec(p, FMM_STAGE_M2L, 0, st);
+  TRY_HIP(launch_m2l(dt, ord, p->n_nodes, P<int64_t>(p->m2l_off), P<int32_t>(p->m2l_src), centre,
+                     p->mpole.p, p->local.p, st));
+  rec(p, FMM_STAGE_M2L, 1, st);
+
+  rec(p, FMM_STAGE_DOWN, 0, st);
+  for (int l = 1; l <= p->depth; l++)
+    TRY_HIP(launch_l2l(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                       P<int32_t>(p->nparent), centre, p->local.p, st));
+  TRY_HIP(launch_l2p(dt, ord, p->n, p->pts.p, P<int32_t>(p->leaf_of), centre, p->local.p,
+                     p->far.p, st));
+  rec(p, FMM_STAGE_DOWN, 1, st);
+
+  rec(p, FMM_STAGE_P2P, 0, st);
+  TRY_HIP(launch_p2p(dt, leaves, p->n_leaves, P<int32_t>(p->nbegin), P<int32_t>(p->ncount),
+                     P<int64_t>(p->p2p_off), P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
+                     P<int32_t>(p->idx), phi, acc, st));
+  rec(p, FMM_STAGE_P2P, 1, st);
+  p->evaluated = true;
+  return FMM_OK;
+}
+
+int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
+  if (!p || !out) return FMM_ERR_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->n = p->n;
+  out->order = p->order;
+  out->leaf_size = p->leaf;
+  out->dtype = p->dtype;
+  out->theta = p->theta;
+  out->walk_retries = p->walk_retries;
+  if (p->built) {
+    out->n_nodes = p->n_nodes;
+    out->n_leaves = p->n_leaves;
+    out->n_m2l = p->n_m2l;
+    out->n_p2p = p->n_p2p;
+    out->depth = p->depth;
+    for (int a = 0; a < 3; a++) out->lo[a] = p->root_host.lo[a];
+    out->side = p->root_host.side;
+  }
+  if (p->timing) {
+    TRY_HIP(hipDeviceSynchronize());
+    for (int s = 0; s < FMM_N_STAGES; s++) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, p->ev[2 * s], p->ev[2 * s + 1]) == hipSuccess)
+        out->stage_ms[s] = ms;
+      else
+        out->stage_ms[s] = -1.f;
+    }
+    (void)hipGetLastError();
+  }
+  return FMM_OK;
+}
+
+int fmm_copy_keys(fmm_plan_t p, uint64_t* keys, int32_t* perm) {
+  if (!p) return FMM_ERR_ARG;
+  if (!p->built) return FMM_ERR_STATE;
+  TRY_HIP(hipDeviceSynchronize());
+  if (keys) TRY_HIP(hipMemcpy(keys, p->keys.p, 8 * p->n, hipMemcpyDeviceToHost));
+  if (perm) TRY_HIP(hipMemcpy(perm, p->idx.p, 4 * p->n, hipMemcpyDeviceToHost));
+  return FMM_OK;
+}
+
+int fmm_copy_tree(fmm_plan_t p, uint8_t* level, uint64_t* prefix, int32_t* begin, int32_t* count,
+                  int32_t* parent, int32_t* first_child, uint8_t* n_child) {
+  if (!p) return FMM_ERR_ARG;
+  if (!p->built) return FMM_ERR_STATE;
+  TRY_HIP(hipDeviceSynchronize());
+  const size_t m = (size_t)p->n_nodes;
+  if (level) TRY_HIP(hipMemcpy(level, p->nlevel.p, m, hipMemcpyDeviceToHost));
+  if (prefix) TRY_HIP(hipMemcpy(prefix, p->nprefix.p, 8 * m, hipMemcpyDeviceToHost));
+  if (begin) TRY_HIP(hipMemcpy(begin, p->nbegin.p, 4 * m, hipMemcpyDeviceToHost));
+  if (count) TRY_HIP(hipMemcpy(count, p->ncount.p, 4 * m, hipMemcpyDeviceToHost));
+  if (parent) TRY_HIP(hipMemcpy(parent, p->nparent.p, 4 * m, hipMemcpyDeviceToHost));
+  if (first_child) TRY_HIP(hipMemcpy(first_child, p->nfirst.p, 4 * m, hipMemcpyDeviceToHost));
+  if (n_child) TRY_HIP(hipMemcpy(n_child, p->nnchild.p, m, hipMemcpyDeviceToHost));
+  return FMM_OK;
+}
+
+int fmm_copy_lists(fmm_plan_t p, int64_t* m2l_off, int32_t* m2l_src, int64_t* p2p_off,
+                   int32_t* p2p_src) {
+  if (!p) return FMM_ERR_ARG;
+  if (!p->built) return FMM_ERR_STATE;
+  TRY_HIP(hipDeviceSynchronize());
+  const size_t m = (size_t)p->n_nodes + 1;
+  if (m2l_off) TRY_HIP(hipMemcpy(m2l_off, p->m2l_off.p, 8 * m, hipMemcpyDeviceToHost));
+  if (p2p_off) TRY_HIP(hipMemcpy(p2p_off, p->p2p_off.p, 8 * m, hipMemcpyDeviceToHost));
+  if (m2l_src && p->n_m2l)
+    TRY_HIP(hipMemcpy(m2l_src, p->m2l_src.p, 4 * (size_t)p->n_m2l, hipMemcpyDeviceToHost));
+  if (p2p_src && p->n_p2p)
+    TRY_HIP(hipMemcpy(p2p_src, p->p2p_src.p, 4 * (size_t)p->n_p2p, hipMemcpyDeviceToHost));
+  return FMM_OK;
+}
+
+int fmm_copy_expansions(fmm_plan_t p, double* mpole, double* local) {
+  if (!p) return FMM_ERR_ARG;
+  if (!p->evaluated) return FMM_ERR_STATE;
+  TRY_HIP(hipDeviceSynchronize());
+  const size_t m = (size_t)p->n_nodes * p->K;
+  double *dm = nullptr, *dl = nullptr;
+  if (hipMalloc(&dm, 8 * m) != hipSuccess) return FMM_ERR_OOM;
+  if (hipMalloc(&dl, 8 * m) != hipSuccess) {
+    (void)hipFree(dm);
+    return FMM_ERR_OOM;
+  }
+  int rc = status_of(launch_export_expansions(p->dtype, p->order, p->n_nodes, p->mpole.p,
+                                              p->local.p, dm, dl, nullptr));
+  if (rc == FMM_OK) rc = status_of(hipDeviceSynchronize());
+  if (rc == FMM_OK && mpole) rc = status_of(hipMemcpy(mpole, dm, 8 * m, hipMemcpyDeviceToHost));
+  if (rc == FMM_OK && local) rc = status_of(hipMemcpy(local, dl, 8 * m, hipMemcpyDeviceToHost));
+  (void)hipFree(dm);
+  (void)hipFree(dl);
+  return rc;
+}
+
+}  // extern "C"

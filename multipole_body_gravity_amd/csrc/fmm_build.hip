@@ -1,0 +1,626 @@
+// fmm_build.hip -- build-stage kernels: bounding box, Morton keys, LSD radix
+// sort, gather into sorted order, device-wide scans and the octree.
+//
+// The jz-fmm project page ("Why this works well on GPUs") keeps sorting and tree
+// construction on the GPU with neighbouring particles and sibling nodes next to
+// each other in memory; the layout rules (root cube, 21-bit keys, leaf rule,
+// breadth-first numbering) are documented in include/fmm.h.
+#include "fmm_device.h"
+#include "fmm_internal.h"
+
+namespace mbg {
+
+// ===================================================================
+// device-wide exclusive scan (reduce -> scan block sums -> apply)
+// ===================================================================
+constexpr int SCAN_THREADS = 256;
+constexpr int SCAN_ITEMS = 8;
+constexpr int SCAN_TILE = SCAN_THREADS * SCAN_ITEMS;
+
+template <typename I>
+__device__ I block_excl_scan(I v, I* total) {
+  __shared__ I wsum[SCAN_THREADS / WAVE];
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  I inc = wave_incl_scan(v);
+  if (l == WAVE - 1) wsum[w] = inc;
+  __syncthreads();
+  I off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_THREADS / WAVE; i++) {
+    if (i < w) off += wsum[i];
+    tot += wsum[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
+template <typename I>
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_reduce(const I* in, int64_t n, I* sums) {
+  int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+  I s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; i++)
+    if (base + i < n) s += in[base + i];
+  I tot;
+  block_excl_scan(s, &tot);
+  if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+template <typename I>
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_top(I* sums, int64_t nb, I* total) {
+  __shared__ I carry_s;
+  if (threadIdx.x == 0) carry_s = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < nb; base += SCAN_THREADS) {
+    int64_t i = base + threadIdx.x;
+    I v = i < nb ? sums[i] : 0;
+    I tot;
+    I ex = block_excl_scan(v, &tot);
+    I c = carry_s;
+    if (i < nb) sums[i] = c + ex;
+    __syncthreads();
+    if (threadIdx.x == 0) carry_s = c + tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && total) *total = carry_s;
+}
+
+template <typename I>
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply(const I* in, I* out, int64_t n,
+                                                             const I* sums) {
+  int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+  I v[SCAN_ITEMS];
+  I s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; i++) {
+    v[i] = (base + i < n) ? in[base + i] : 0;
+    s += v[i];
+  }
+  I tot;
+  I ex = block_excl_scan(s, &tot) + sums[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; i++) {
+    if (base + i < n) out[base + i] = ex;
+    ex += v[i];
+  }
+}
+
+size_t scan_tmp_bytes(int64_t n) {
+  int64_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
+  return (size_t)(nb + 1) * sizeof(int64_t);
+}
+
+template <typename I>
+__global__ void k_set_zero(I* p) {
+  if (threadIdx.x == 0) *p = 0;
+}
+
+template <typename I>
+static hipError_t scan_excl(const I* in, I* out, int64_t n, I* total, void* tmp, hipStream_t st) {
+  if (n <= 0) {
+    if (total) k_set_zero<I><<<1, 64, 0, st>>>(total);
+    return hipGetLastError();
+  }
+  int64_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
+  I* sums = (I*)tmp;
+  k_scan_reduce<I><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(in, n, sums);
+  k_scan_top<I><<<1, SCAN_THREADS, 0, st>>>(sums, nb, total);
+  k_scan_apply<I><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(in, out, n, sums);
+  return hipGetLastError();
+}
+
+hipError_t scan_exclusive_i64(const int64_t* in, int64_t* out, int64_t n, int64_t* total,
+                              void* tmp, hipStream_t st) {
+  return scan_excl<int64_t>(in, out, n, total, tmp, st);
+}
+hipError_t scan_exclusive_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total,
+                              void* tmp, hipStream_t st) {
+  return scan_excl<int32_t>(in, out, n, total, tmp, st);
+}
+
+// ===================================================================
+// bounding box (exact min / max) and non-finite detection
+// ===================================================================
+constexpr int BB_THREADS = 256;
+
+template <typename T>
+__global__ void __launch_bounds__(BB_THREADS)
+    k_bbox_partial(const T* pos, const T* mass, int64_t n, double* part, Control* ctrl) {
+  double lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+  int bad = 0;
+  for (int64_t i = blockIdx.x * (int64_t)BB_THREADS + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * BB_THREADS) {
+#pragma unroll
+    for (int a = 0; a < 3; a++) {
+      double v = (double)pos[3 * i + a];
+      bad |= !isfinite(v);
+      lo[a] = fmin(lo[a], v);
+      hi[a] = fmax(hi[a], v);
+    }
+    bad |= !isfinite((double)mass[i]);
+  }
+  __shared__ double s[6][BB_THREADS / WAVE];
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+#pragma unroll
+  for (int a = 0; a < 3; a++) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo[a] = fmin(lo[a], __shfl_xor(lo[a], o, WAVE));
+      hi[a] = fmax(hi[a], __shfl_xor(hi[a], o, WAVE));
+    }
+  }
+  if (l == 0) {
+    for (int a = 0; a < 3; a++) {
+      s[a][w] = lo[a];
+      s[3 + a][w] = hi[a];
+    }
+  }
+  if (__ballot(bad) != 0ull && l == 0) atomicOr(&ctrl->nonfinite, 1);
+  __syncthreads();
+  if (threadIdx.x < 6) {
+    double v = s[threadIdx.x][0];
+    for (int i = 1; i < BB_THREADS / WAVE; i++)
+      v = threadIdx.x < 3 ? fmin(v, s[threadIdx.x][i]) : fmax(v, s[threadIdx.x][i]);
+    part[6 * blockIdx.x + threadIdx.x] = v;
+  }
+}
+
+__global__ void k_bbox_final(const double* part, int nblk, RootInfo* root) {
+  if (threadIdx.x != 0) return;
+  double lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+  for (int b = 0; b < nblk; b++)
+    for (int a = 0; a < 3; a++) {
+      lo[a] = fmin(lo[a], part[6 * b + a]);
+      hi[a] = fmax(hi[a], part[6 * b + 3 + a]);
+    }
+  double ext = 0.0;
+  for (int a = 0; a < 3; a++) ext = fmax(ext, __dsub_rn(hi[a], lo[a]));
+  // smallest power of two >= ext (1 if ext == 0)
+  double side = 1.0;
+  if (ext > 0.0 && isfinite(ext)) {
+    int e;
+    double f = frexp(ext, &e);
+    side = (f == 0.5) ? ext : ldexp(1.0, e);
+  }
+  int e2;
+  frexp(side, &e2);
+  for (int a = 0; a < 3; a++) root->lo[a] = isfinite(lo[a]) ? lo[a] : 0.0;
+  root->side = side;
+  root->scale = ldexp(1.0, KEY_BITS - (e2 - 1));
+}
+
+hipError_t launch_bbox(const void* pos, const void* mass, int64_t n, int dtype, double* part,
+                       int nblk, RootInfo* root, Control* ctrl, hipStream_t st) {
+  if (dtype == FMM_F64)
+    k_bbox_partial<double><<<nblk, BB_THREADS, 0, st>>>((const double*)pos, (const double*)mass, n,
+                                                        part, ctrl);
+  else
+    k_bbox_partial<float><<<nblk, BB_THREADS, 0, st>>>((const float*)pos, (const float*)mass, n,
+                                                       part, ctrl);
+  k_bbox_final<<<1, 64, 0, st>>>(part, nblk, root);
+  return hipGetLastError();
+}
+
+// ===================================================================
+// Morton keys: u = floor((x - lo) * 2^21 / side) clamped, bits interleaved
+// ===================================================================
+template <typename T>
+__global__ void k_keys(const T* pos, int64_t n, const RootInfo* root, uint64_t* keys,
+                       int32_t* idx) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const double umax = (double)((1u << KEY_BITS) - 1u);
+  uint32_t u[3];
+#pragma unroll
+  for (int a = 0; a < 3; a++) {
+    // one rounding in the subtraction; the scale is an exact power of two
+    double s = __dsub_rn((double)pos[3 * i + a], root->lo[a]);
+    double v = floor(__dmul_rn(s, root->scale));
+    v = fmin(fmax(v, 0.0), umax);
+    u[a] = (uint32_t)v;
+  }
+  keys[i] = (spread3(u[0]) << 2) | (spread3(u[1]) << 1) | spread3(u[2]);
+  idx[i] = (int32_t)i;
+}
+
+hipError_t launch_keys(const void* pos, int64_t n, int dtype, const RootInfo* root,
+                       uint64_t* keys, int32_t* idx, hipStream_t st) {
+  unsigned g = (unsigned)((n + 255) / 256);
+  if (dtype == FMM_F64)
+    k_keys<double><<<g, 256, 0, st>>>((const double*)pos, n, root, keys, idx);
+  else
+    k_keys<float><<<g, 256, 0, st>>>((const float*)pos, n, root, keys, idx);
+  return hipGetLastError();
+}
+
+// ===================================================================
+// LSD radix sort of (u64 key, i32 index), 8-bit digits, stable
+// ===================================================================
+constexpr int RS_THREADS = 256;
+constexpr int RS_ROUNDS = 16;
+constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
+
+size_t radix_hist_ints(int64_t n) {
+  int64_t nb = (n + RS_TILE - 1) / RS_TILE;
+  return (size_t)(256 * nb);
+}
+
+__global__ void __launch_bounds__(RS_THREADS)
+    k_radix_hist(const uint64_t* keys, int64_t n, int shift, int32_t* hist, int nblk) {
+  __shared__ int h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  int64_t base = (int64_t)blockIdx.x * RS_TILE;
+#pragma unroll 4
+  for (int r = 0; r < RS_ROUNDS; r++) {
+    int64_t i = base + r * RS_THREADS + threadIdx.x;
+    if (i < n) atomicAdd(&h[(keys[i] >> shift) & 255u], 1);
+  }
+  __syncthreads();
+  hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+}
+
+// Elements of a tile are visited in input order (round-major, then thread):
+// within a round, ranks among equal digits come from wave ballots (lower
+// lanes first) and per-wave counts (lower waves first), so the scatter is
+// stable.
+__global__ void __launch_bounds__(RS_THREADS)
+    k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
+                    int64_t n, int shift, const int32_t* hist_scan, int nblk) {
+  __shared__ int bin_base[256];
+  __shared__ int wcnt[RS_THREADS / WAVE][256];
+  const int tid = threadIdx.x, w = tid / WAVE;
+  bin_base[tid] = hist_scan[(int64_t)tid * nblk + blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < RS_THREADS / WAVE; i++) wcnt[i][tid] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RS_TILE;
+  const uint64_t lt = lanemask_lt();
+  for (int r = 0; r < RS_ROUNDS; r++) {
+    int64_t i = base + r * RS_THREADS + tid;
+    bool valid = i < n;
+    uint64_t key = valid ? kin[i] : 0ull;
+    int32_t val = valid ? vin[i] : 0;
+    int d = (int)((key >> shift) & 255u);
+    uint64_t mask = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+      uint64_t bb = __ballot((d >> b) & 1);
+      mask &= ((d >> b) & 1) ? bb : ~bb;
+    }
+    int rank = __popcll(mask & lt);
+    if (valid && rank == 0) wcnt[w][d] = __popcll(mask);
+    __syncthreads();
+    int pos = 0;
+    if (valid) {
+      pos = bin_base[d] + rank;
+      for (int j = 0; j < w; j++) pos += wcnt[j][d];
+    }
+    __syncthreads();
+    {
+      int s = 0;
+#pragma unroll
+      for (int j = 0; j < RS_THREADS / WAVE; j++) {
+        s += wcnt[j][tid];
+        wcnt[j][tid] = 0;
+      }
+      bin_base[tid] += s;
+    }
+    __syncthreads();
+    if (valid) {
+      kout[pos] = key;
+      vout[pos] = val;
+    }
+  }
+}
+
+hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
+                             int64_t n, int32_t* hist, int32_t* scan_tmp, hipStream_t st) {
+  int nblk = (int)((n + RS_TILE - 1) / RS_TILE);
+  uint64_t *ka = keys, *kb = keys_alt;
+  int32_t *va = idx, *vb = idx_alt;
+  for (int pass = 0; pass < 8; pass++) {
+    int shift = 8 * pass;
+    k_radix_hist<<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, hist, nblk);
+    hipError_t e = scan_excl<int32_t>(hist, hist, (int64_t)256 * nblk, nullptr, scan_tmp, st);
+    if (e != hipSuccess) return e;
+    k_radix_scatter<<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, hist, nblk);
+    uint64_t* tk = ka;
+    ka = kb;
+    kb = tk;
+    int32_t* tv = va;
+    va = vb;
+    vb = tv;
+  }
+  // 8 passes: the result is back in (keys, idx)
+  return hipGetLastError();
+}
+
+// ===================================================================
+// gather into sorted (x, y, z, m) records
+// ===================================================================
+template <typename T>
+__global__ void k_gather(const T* pos, const T* mass, const int32_t* perm, int64_t n, P4<T>* pts) {
+  int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  int64_t i = perm[k];
+  P4<T> p;
+  p.x = pos[3 * i];
+  p.y = pos[3 * i + 1];
+  p.z = pos[3 * i + 2];
+  p.m = mass[i];
+  pts[k] = p;
+}
+
+hipError_t launch_gather(const void* pos, const void* mass, const int32_t* perm, int64_t n,
+                         int dtype, void* pts, hipStream_t st) {
+  unsigned g = (unsigned)((n + 255) / 256);
+  if (dtype == FMM_F64)
+    k_gather<double><<<g, 256, 0, st>>>((const double*)pos, (const double*)mass, perm, n,
+                                        (P4<double>*)pts);
+  else
+    k_gather<float><<<g, 256, 0, st>>>((const float*)pos, (const float*)mass, perm, n,
+                                       (P4<float>*)pts);
+  return hipGetLastError();
+}
+
+// ===================================================================
+// octree
+//
+// With sorted keys, particle k's cell at level l holds more than S particles
+// iff some window of S+1 consecutive particles containing k lies in one level-l
+// cell, i.e. iff l <= W(k) = max over windows [j, j+S] that contain k of the
+// level shared by key[j] and key[j+S].  So k's leaf is at level min(W(k)+1, 21)
+// (level 0 when N <= S), and a node of level l starts at k iff k starts a
+// level-l cell (the level shared with key[k-1] is < l) and l <= leaf level of k.
+// Counting those starts per level and block, one scan gives every node its
+// breadth-first id.
+// ===================================================================
+constexpr int TR_THREADS = 256;
+
+size_t tree_blkcnt_len(int64_t n) {
+  int64_t nb = (n + TR_THREADS - 1) / TR_THREADS;
+  return (size_t)(2 * MAX_LEVELS * nb + 1);  // + one slot for the scan total
+}
+
+// lcp[k] = level shared with key[k-1] (-1 for k = 0); wpad[i] = level shared by
+// the window starting at j = i - S (or -1 if that window does not exist).
+__global__ void k_tree_lcp(const uint64_t* keys, int64_t n, int S, int8_t* lcp, int8_t* wpad,
+                           int64_t wlen) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) lcp[i] = (int8_t)(i == 0 ? -1 : shared_level(keys[i - 1], keys[i]));
+  if (wpad && i < wlen) {
+    int64_t j = i - S;
+    int8_t v = -1;
+    if (j >= 0 && j + S < n) v = (int8_t)shared_level(keys[j], keys[j + S]);
+    wpad[i] = v;
+  }
+}
+
+__global__ void k_tree_stmax(const int8_t* in, int8_t* out, int64_t len, int64_t half) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= len) return;
+  int8_t v = in[i];
+  if (i + half < len) v = max(v, in[i + half]);
+  out[i] = v;
+}
+
+// leaf level per particle; per-block counts of node starts and leaf starts at
+// every level (blkcnt[l * nblk + b] and blkcnt[(MAX_LEVELS + l) * nblk + b]).
+__global__ void __launch_bounds__(TR_THREADS)
+    k_tree_leafcount(const int8_t* lcp, const int8_t* stj, int64_t n, int S, int64_t span2,
+                     int8_t* leaf_level, int64_t* blkcnt, int nblk) {
+  int64_t k = blockIdx.x * (int64_t)TR_THREADS + threadIdx.x;
+  int lo = 99, ll = -1;
+  if (k < n) {
+    int W;
+    if (stj == nullptr) {
+      W = -1;
+    } else {
+      // window starts j = k-S..k sit at wpad indices k..k+S; two overlapping
+      // power-of-two spans cover them
+      W = max((int)stj[k], (int)stj[k + S + 1 - span2]);
+    }
+    ll = min(W + 1, KEY_BITS);
+    leaf_level[k] = (int8_t)ll;
+    lo = lcp[k];
+  }
+  __shared__ int cnt[2 * MAX_LEVELS];
+  if (threadIdx.x < 2 * MAX_LEVELS) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  for (int l = 0; l < MAX_LEVELS; l++) {
+    uint64_t bn = __ballot(lo < l && l <= ll);
+    uint64_t bl = __ballot(lo < l && l == ll);
+    if (__lane_id() == 0) {
+      if (bn) atomicAdd(&cnt[l], __popcll(bn));
+      if (bl) atomicAdd(&cnt[MAX_LEVELS + l], __popcll(bl));
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 2 * MAX_LEVELS) blkcnt[(int64_t)threadIdx.x * nblk + blockIdx.x] = cnt[threadIdx.x];
+}
+
+__global__ void k_tree_levelinfo(const int64_t* scanned, int nblk, const int64_t* total,
+                                 const int64_t* leafcnt_raw, Control* ctrl) {
+  int l = threadIdx.x;
+  if (l < MAX_LEVELS) ctrl->level_off[l] = scanned[(int64_t)l * nblk];
+  if (l == MAX_LEVELS) ctrl->level_off[MAX_LEVELS] = *total;
+  if (l == 0) ctrl->n_nodes = *total;
+}
+
+// leaves per level = sum over blocks of the leaf-start counts (the upper half
+// of blkcnt); reduced in a fixed order by one thread per level
+__global__ void k_tree_leaflevels(const int64_t* blkcnt, int nblk, int64_t* out) {
+  int l = threadIdx.x;
+  if (l >= MAX_LEVELS) return;
+  int64_t s = 0;
+  for (int b = 0; b < nblk; b++) s += blkcnt[(int64_t)(MAX_LEVELS + l) * nblk + b];
+  out[l] = s;
+}
+
+hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t* lcp, int8_t* wlev,
+                              int8_t* wtmp, int8_t* leaf_level, int64_t* blkcnt, void* scan_tmp,
+                              Control* ctrl, hipStream_t st) {
+  const int S = leaf;
+  int nblk = (int)((n + TR_THREADS - 1) / TR_THREADS);
+  const int8_t* stj = nullptr;
+  int64_t span2 = 1;
+  if ((int64_t)S < n) {
+    int64_t wlen = n + S;
+    k_tree_lcp<<<(unsigned)((wlen + 255) / 256), 256, 0, st>>>(keys, n, S, lcp, wlev, wlen);
+    // sparse-table levels until the span 2^J <= S + 1 < 2^(J+1)
+    int8_t *a = wlev, *b = wtmp;
+    while (span2 * 2 <= (int64_t)S + 1) {
+      k_tree_stmax<<<(unsigned)((wlen + 255) / 256), 256, 0, st>>>(a, b, wlen, span2);
+      int8_t* t = a;
+      a = b;
+      b = t;
+      span2 *= 2;
+    }
+    stj = a;
+  } else {
+    k_tree_lcp<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, S, lcp, nullptr, 0);
+  }
+  k_tree_leafcount<<<nblk, TR_THREADS, 0, st>>>(lcp, stj, n, S, span2, leaf_level, blkcnt, nblk);
+  // leaf counts per level live in the upper half and are not scanned
+  k_tree_leaflevels<<<1, 64, 0, st>>>(blkcnt, nblk, ctrl->leaves_at_level);
+  int64_t total_len = (int64_t)MAX_LEVELS * nblk;
+  int64_t* total = blkcnt + 2 * total_len;  // the spare slot after both halves
+  hipError_t e = scan_excl<int64_t>(blkcnt, blkcnt, total_len, total, scan_tmp, st);
+  if (e != hipSuccess) return e;
+  k_tree_levelinfo<<<1, 64, 0, st>>>(blkcnt, nblk, total, nullptr, ctrl);
+  return hipGetLastError();
+}
+
+// ---- phase 2: node records ----
+__global__ void __launch_bounds__(TR_THREADS)
+    k_tree_emit(const uint64_t* keys, int64_t n, const int8_t* lcp, const int8_t* leaf_level,
+                const int64_t* scanned, int nblk, uint8_t* level, uint64_t* prefix,
+                int32_t* begin) {
+  int64_t k = blockIdx.x * (int64_t)TR_THREADS + threadIdx.x;
+  int lo = 99, ll = -1;
+  uint64_t key = 0;
+  if (k < n) {
+    lo = lcp[k];
+    ll = leaf_level[k];
+    key = keys[k];
+  }
+  __shared__ int wtot[TR_THREADS / WAVE];
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const uint64_t lt = lanemask_lt();
+  for (int l = 0; l < MAX_LEVELS; l++) {
+    bool f = lo < l && l <= ll;
+    uint64_t b = __ballot(f);
+    if (lane == 0) wtot[w] = __popcll(b);
+    __syncthreads();
+    if (f) {
+      int64_t id = scanned[(int64_t)l * nblk + blockIdx.x] + __popcll(b & lt);
+      for (int j = 0; j < w; j++) id += wtot[j];
+      level[id] = (uint8_t)l;
+      begin[id] = (int32_t)k;
+      prefix[id] = (l == 0) ? 0ull : (key >> (3 * (KEY_BITS - l)));
+    }
+    __syncthreads();
+  }
+}
+
+// first index in [lo, hi) with keys[i] >= v
+__device__ int64_t lower_bound_u64(const uint64_t* keys, int64_t lo, int64_t hi, uint64_t v) {
+  while (lo < hi) {
+    int64_t mid = (lo + hi) >> 1;
+    if (keys[mid] < v)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+// first index in [lo, hi) with a[i] >= v
+__device__ int64_t lower_bound_i32(const int32_t* a, int64_t lo, int64_t hi, int32_t v) {
+  while (lo < hi) {
+    int64_t mid = (lo + hi) >> 1;
+    if (a[mid] < v)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+struct LevelOff {
+  int64_t o[MAX_LEVELS + 2];
+};
+
+__global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t n_nodes, LevelOff lo_,
+                             const RootInfo* root, TreeArrays t, int32_t* leaf_flag) {
+  int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (id >= n_nodes) return;
+  const int l = t.level[id];
+  const int64_t k = t.begin[id];
+  const uint64_t P = t.prefix[id];
+  int64_t end = n;
+  if (l > 0) end = lower_bound_u64(keys, k, n, (P + 1) << (3 * (KEY_BITS - l)));
+  const int64_t cnt = end - k;
+  t.count[id] = (int32_t)cnt;
+  // parent: the level l-1 node whose range starts at or before k (last such)
+  int32_t par = -1;
+  if (l > 0) {
+    int64_t j = lower_bound_i32(t.begin, lo_.o[l - 1], lo_.o[l], (int32_t)(k + 1));
+    par = (int32_t)(j - 1);
+  }
+  t.parent[id] = par;
+  const bool leaf = cnt <= S || l == KEY_BITS;
+  int32_t fc = -1;
+  int nc = 0;
+  if (!leaf) {
+    int64_t a = lower_bound_i32(t.begin, lo_.o[l + 1], lo_.o[l + 2], (int32_t)k);
+    int64_t b = lower_bound_i32(t.begin, a, lo_.o[l + 2], (int32_t)(k + cnt));
+    fc = (int32_t)a;
+    nc = (int)(b - a);
+  }
+  t.first_child[id] = fc;
+  t.n_child[id] = (uint8_t)nc;
+  leaf_flag[id] = leaf ? 1 : 0;
+  // integer cell coordinates and geometric centre
+  uint32_t qx = compact3(P >> 2), qy = compact3(P >> 1), qz = compact3(P);
+  t.q[id] = ((uint64_t)qx << 42) | ((uint64_t)qy << 21) | (uint64_t)qz;
+  const double w = ldexp(root->side, -l);
+  const uint32_t q[3] = {qx, qy, qz};
+#pragma unroll
+  for (int a = 0; a < 3; a++)
+    t.centre[3 * id + a] = __dadd_rn(root->lo[a], __dmul_rn((double)q[a] + 0.5, w));
+}
+
+__global__ void k_tree_leaves(const int32_t* leaf_flag, const int32_t* scan, int64_t n_nodes,
+                              const int32_t* begin, const int32_t* count, int32_t* leaves,
+                              int32_t* leaf_of) {
+  int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (id >= n_nodes || !leaf_flag[id]) return;
+  leaves[scan[id]] = (int32_t)id;
+  for (int32_t k = begin[id]; k < begin[id] + count[id]; k++) leaf_of[k] = (int32_t)id;
+}
+
+hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const int8_t* lcp,
+                              const int8_t* leaf_level, const int64_t* blkcnt_scanned,
+                              int64_t n_nodes, const int64_t* level_off_host, const RootInfo* root,
+                              const TreeArrays& t, int32_t* leaf_flag, int32_t* leaf_scan,
+                              int32_t* leaves, int32_t* leaf_of, void* scan_tmp, Control* ctrl,
+                              hipStream_t st) {
+  int nblk = (int)((n + TR_THREADS - 1) / TR_THREADS);
+  k_tree_emit<<<nblk, TR_THREADS, 0, st>>>(keys, n, lcp, leaf_level, blkcnt_scanned, nblk,
+                                           t.level, t.prefix, t.begin);
+  LevelOff lo_;
+  for (int l = 0; l <= MAX_LEVELS; l++) lo_.o[l] = level_off_host[l];
+  lo_.o[MAX_LEVELS + 1] = level_off_host[MAX_LEVELS];
+  unsigned g = (unsigned)((n_nodes + 255) / 256);
+  k_tree_nodes<<<g, 256, 0, st>>>(keys, n, leaf, n_nodes, lo_, root, t, leaf_flag);
+  hipError_t e = scan_excl<int32_t>(leaf_flag, leaf_scan, n_nodes, nullptr, scan_tmp, st);
+  if (e != hipSuccess) return e;
+  k_tree_leaves<<<g, 256, 0, st>>>(leaf_flag, leaf_scan, n_nodes, t.begin, t.count, leaves,
+                                   leaf_of);
+  (void)ctrl;
+  return hipGetLastError();
+}
+
+}  // namespace mbg

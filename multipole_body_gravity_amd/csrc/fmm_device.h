@@ -1,0 +1,199 @@
+// fmm_device.h -- device helpers for the gfx950 kernels: wave64 primitives,
+// Morton bit spreading, compile-time multi-index tables.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+#include <utility>
+
+namespace mbg {
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (1ull << __lane_id()) - 1ull;
+}
+
+// Wave-wide sum with a fixed butterfly order: every lane gets the same,
+// bit-reproducible result.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+template <typename I>
+__device__ __forceinline__ I wave_incl_scan(I v) {
+  const int l = __lane_id();
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    I t = __shfl_up(v, o, WAVE);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Spread the low 21 bits of v to every third bit (bit b -> bit 3b).
+__device__ __forceinline__ uint64_t spread3(uint32_t v) {
+  uint64_t x = v & 0x1fffffull;
+  x = (x | (x << 32)) & 0x001f00000000ffffull;
+  x = (x | (x << 16)) & 0x001f0000ff0000ffull;
+  x = (x | (x << 8)) & 0x100f00f00f00f00full;
+  x = (x | (x << 4)) & 0x10c30c30c30c30c3ull;
+  x = (x | (x << 2)) & 0x1249249249249249ull;
+  return x;
+}
+// Inverse of spread3: gather every third bit (bit 3b -> bit b).
+__host__ __device__ __forceinline__ uint32_t compact3(uint64_t x) {
+  x &= 0x1249249249249249ull;
+  x = (x ^ (x >> 2)) & 0x10c30c30c30c30c3ull;
+  x = (x ^ (x >> 4)) & 0x100f00f00f00f00full;
+  x = (x ^ (x >> 8)) & 0x001f0000ff0000ffull;
+  x = (x ^ (x >> 16)) & 0x001f00000000ffffull;
+  x = (x ^ (x >> 32)) & 0x1fffffull;
+  return (uint32_t)x;
+}
+
+// Deepest level at which two keys share a cell (21 if equal).
+__device__ __forceinline__ int shared_level(uint64_t a, uint64_t b) {
+  uint64_t x = a ^ b;
+  if (x == 0) return 21;
+  return (__clzll(x) - 1) / 3;  // bit 63 of a key is always 0
+}
+
+// ---- multi-indices (a,b,c), |.| <= p, graded: degree, then a desc, b desc ----
+__host__ __device__ constexpr int mi_index(int a, int b, int c) {
+  int d = a + b + c;
+  return d * (d + 1) * (d + 2) / 6 + (b + c) * (b + c + 1) / 2 + c;
+}
+
+template <int P>
+struct MI {
+  static constexpr int K = (P + 1) * (P + 2) * (P + 3) / 6;
+  int a[K], b[K], c[K], d[K];
+  constexpr MI() : a(), b(), c(), d() {
+    int k = 0;
+    for (int dd = 0; dd <= P; dd++)
+      for (int aa = dd; aa >= 0; aa--)
+        for (int bb = dd - aa; bb >= 0; bb--) {
+          a[k] = aa;
+          b[k] = bb;
+          c[k] = dd - aa - bb;
+          d[k] = dd;
+          k++;
+        }
+  }
+};
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = B .. E-1, in order.
+template <int B, typename F, int... I>
+__host__ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, B + I>{}), ...);
+}
+template <int B, int E, typename F>
+__host__ __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (E - B <= 512) {
+    static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
+  } else {
+    constexpr int M = B + (E - B) / 2;
+    static_for<B, M>(f);
+    static_for<M, E>(f);
+  }
+}
+
+__host__ __device__ constexpr int binom_c(int n, int k) {
+  int r = 1;
+  for (int i = 1; i <= k; i++) r = r * (n - k + i) / i;
+  return r;
+}
+
+// Tables for order P, usable as constant expressions in device code:
+//   coefficient k <-> (a, b, c);
+//   contraction triples (n, m, n+m) with |n| + |m| <= P;
+//   the derivative recurrence over levels j = P .. 0, flattened: entry e of
+//   level j (multi-index k, |k| <= P - j) is built from two entries of level j+1.
+template <int P>
+struct Tabs {
+  static constexpr int K = (P + 1) * (P + 2) * (P + 3) / 6;
+  static constexpr int NT = binom_c(P + 6, 6);
+  static constexpr int NR = binom_c(P + 4, 4);
+  int a[K], b[K], c[K], d[K];
+  int tn[NT], tm[NT], tk[NT];
+  int roff[P + 2];           // flat offset of level j
+  int rlev[NR], rk[NR];      // level and multi-index of every flat entry
+  int raxis[NR];             // -1: level head g_j; else axis 0/1/2
+  int rs1[NR], rs2[NR];      // flat sources (rs2 = -1 when absent)
+  int rc2[NR];               // integer factor of the second source
+  constexpr Tabs()
+      : a(), b(), c(), d(), tn(), tm(), tk(), roff(), rlev(), rk(), raxis(), rs1(), rs2(), rc2() {
+    int k = 0;
+    for (int dd = 0; dd <= P; dd++)
+      for (int aa = dd; aa >= 0; aa--)
+        for (int bb = dd - aa; bb >= 0; bb--) {
+          a[k] = aa;
+          b[k] = bb;
+          c[k] = dd - aa - bb;
+          d[k] = dd;
+          k++;
+        }
+    int t = 0;
+    for (int n = 0; n < K; n++)
+      for (int m = 0; m < K; m++)
+        if (d[n] + d[m] <= P) {
+          tn[t] = n;
+          tm[t] = m;
+          tk[t] = mi_index(a[n] + a[m], b[n] + b[m], c[n] + c[m]);
+          t++;
+        }
+    // level j has C(P-j+3,3) entries; levels stored from j = P down to 0
+    int off = 0;
+    for (int j = P; j >= 0; j--) {
+      roff[j] = off;
+      off += binom_c(P - j + 3, 3);
+    }
+    roff[P + 1] = 0;
+    for (int j = P; j >= 0; j--) {
+      int n_j = binom_c(P - j + 3, 3);
+      for (int q = 0; q < n_j; q++) {
+        int e = roff[j] + q;
+        rlev[e] = j;
+        rk[e] = q;
+        if (q == 0) {
+          raxis[e] = -1;
+          rs1[e] = rs2[e] = -1;
+          rc2[e] = 0;
+          continue;
+        }
+        int ka = a[q], kb = b[q], kc = c[q];
+        int ax = ka > 0 ? 0 : (kb > 0 ? 1 : 2);
+        int ia = ka, ib = kb, ic = kc;  // k - e_ax
+        if (ax == 0) ia--;
+        if (ax == 1) ib--;
+        if (ax == 2) ic--;
+        raxis[e] = ax;
+        rs1[e] = roff[j + 1] + mi_index(ia, ib, ic);
+        int prev = ax == 0 ? ia : (ax == 1 ? ib : ic);  // (k - e_ax)_ax
+        if (prev > 0) {
+          rs2[e] = roff[j + 1] + mi_index(ia - (ax == 0), ib - (ax == 1), ic - (ax == 2));
+          rc2[e] = prev;
+        } else {
+          rs2[e] = -1;
+          rc2[e] = 0;
+        }
+      }
+    }
+  }
+};
+
+template <int P>
+inline constexpr Tabs<P> tabs{};
+
+template <typename T>
+struct alignas(4 * sizeof(T)) P4 {
+  T x, y, z, m;
+};
+
+}  // namespace mbg

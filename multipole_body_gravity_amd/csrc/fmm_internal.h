@@ -1,0 +1,188 @@
+// fmm_internal.h -- plan object and kernel-launcher declarations shared by the
+// HIP sources of libmbg_fmm.so.  Not installed; the public interface is
+// include/fmm.h.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/fmm.h"
+
+namespace mbg {
+
+constexpr int KEY_BITS = 21;
+constexpr int MAX_LEVELS = KEY_BITS + 1;  // levels 0..21
+
+// Number of Cartesian coefficients of total degree <= p: C(p+3, 3).
+constexpr int ncoef(int p) { return (p + 1) * (p + 2) * (p + 3) / 6; }
+
+// Root cube and key scale, computed on the device.
+struct RootInfo {
+  double lo[3];
+  double side;   // power of two
+  double scale;  // 2^21 / side (exact)
+};
+
+// Device scalars written by kernels and read back at the two build syncs.
+struct Control {
+  int32_t nonfinite;
+  int32_t carry_overflow;
+  int64_t carry_used;     // entries requested from the carry pool
+  int64_t n_nodes;
+  int64_t n_leaves;
+  int64_t level_off[MAX_LEVELS + 1];
+  int64_t leaves_at_level[MAX_LEVELS];
+  int64_t n_m2l;
+  int64_t n_p2p;
+  int32_t nA[MAX_LEVELS + 1];  // walk: type-A (pending leaf) items per step
+};
+
+// Grow-only device buffer.
+struct DBuf {
+  void* p = nullptr;
+  size_t cap = 0;
+};
+
+struct fmm_plan_impl;
+
+}  // namespace mbg
+
+struct fmm_plan_s {
+  int64_t n;
+  int order, K, leaf, dtype;
+  double theta, t2;
+  int device;
+  bool built = false, evaluated = false, timing = false;
+
+  // N-sized
+  mbg::DBuf keys, keys_alt, idx, idx_alt, pts, far, perm_inv;
+  mbg::DBuf lcp, wlev, wtmp, leaf_level, leaf_of;
+  mbg::DBuf radix_hist, scan_tmp;
+  mbg::DBuf root, ctrl, bbox_part;
+  // node-sized
+  mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq;
+  mbg::DBuf leaves, lvl_blkcnt;
+  mbg::DBuf mpole, local;
+  // walk
+  mbg::DBuf items, carry, tot_m2l, tot_p2p, cur_m2l, cur_p2p;
+  mbg::DBuf m2l_off, m2l_src, p2p_off, p2p_src;
+
+  // host copies of the last build's sizes
+  int64_t n_nodes = 0, n_leaves = 0, n_m2l = 0, n_p2p = 0;
+  int depth = 0;
+  int64_t level_off[mbg::MAX_LEVELS + 1] = {0};
+  int64_t leaves_at_level[mbg::MAX_LEVELS + 1] = {0};
+  int walk_retries = 0;
+  mbg::RootInfo root_host{};
+
+  // walk item bookkeeping (host-computed capacities)
+  int64_t item_base[mbg::MAX_LEVELS + 2] = {0};
+  int64_t item_amax[mbg::MAX_LEVELS + 2] = {0};
+  int64_t carry_cap = 0;
+
+  mbg::Control* ctrl_host = nullptr;  // pinned
+  hipEvent_t ev[2 * FMM_N_STAGES] = {};
+  float stage_ms[FMM_N_STAGES] = {0};
+};
+
+namespace mbg {
+
+// ---- launchers (each enqueues on `st`; return hipError_t) ----
+hipError_t launch_bbox(const void* pos, const void* mass, int64_t n, int dtype, double* part,
+                       int nblk, RootInfo* root, Control* ctrl, hipStream_t st);
+hipError_t launch_keys(const void* pos, int64_t n, int dtype, const RootInfo* root,
+                       uint64_t* keys, int32_t* idx, hipStream_t st);
+hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
+                             int64_t n, int32_t* hist, int32_t* scan_tmp, hipStream_t st);
+hipError_t launch_gather(const void* pos, const void* mass, const int32_t* perm, int64_t n,
+                         int dtype, void* pts, hipStream_t st);
+size_t radix_hist_ints(int64_t n);
+size_t scan_tmp_bytes(int64_t n);
+
+// Exclusive scan of int64 (in may alias out).  If total != nullptr the grand
+// total is written there.
+hipError_t scan_exclusive_i64(const int64_t* in, int64_t* out, int64_t n, int64_t* total,
+                              void* tmp, hipStream_t st);
+hipError_t scan_exclusive_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total,
+                              void* tmp, hipStream_t st);
+
+struct TreeArrays {
+  uint8_t* level;
+  uint64_t* prefix;
+  int32_t *begin, *count, *parent, *first_child;
+  uint8_t* n_child;
+  double* centre;  // [n_nodes][3]
+  uint64_t* q;     // packed integer cell coords qx<<42 | qy<<21 | qz
+};
+
+hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t* lcp, int8_t* wlev,
+                              int8_t* wtmp, int8_t* leaf_level, int64_t* blkcnt, void* scan_tmp,
+                              Control* ctrl, hipStream_t st);
+size_t tree_blkcnt_len(int64_t n);
+hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const int8_t* lcp,
+                              const int8_t* leaf_level, const int64_t* blkcnt_scanned,
+                              int64_t n_nodes, const int64_t* level_off_host, const RootInfo* root,
+                              const TreeArrays& t, int32_t* leaf_flag, int32_t* leaf_scan,
+                              int32_t* leaves, int32_t* leaf_of, void* scan_tmp, Control* ctrl,
+                              hipStream_t st);
+
+// ---- walk ----
+struct WalkItems {  // SoA over the global item index space
+  int32_t* tgt;
+  int64_t* gen_off;
+  int32_t* gen_cnt;
+  int64_t* carry_off;
+  int32_t* carry_cnt;
+};
+struct WalkArgs {
+  const uint8_t* level;
+  const uint64_t* q;
+  const int32_t* first_child;
+  const uint8_t* n_child;
+  const int32_t* parent;
+  double t2;
+  int step;
+  int64_t lvl_begin, lvl_count;      // nodes at level `step`
+  int64_t prev_lvl_begin;            // nodes at level step-1
+  int64_t base, amax;                // this step's item range
+  int64_t prev_base, prev_amax;      // previous step's item range
+  int64_t next_base;                 // next step's item base (type-A writes)
+  int64_t next_amax;
+  WalkItems it;
+  int32_t* carry;
+  int64_t carry_cap;
+  int64_t *tot_m2l, *tot_p2p;
+  int64_t *cur_m2l, *cur_p2p;
+  const int64_t *m2l_off, *p2p_off;
+  int32_t *m2l_src, *p2p_src;
+  Control* ctrl;
+};
+hipError_t launch_walk_pass1(const WalkArgs& a, hipStream_t st);
+hipError_t launch_walk_pass2(const WalkArgs& a, hipStream_t st);
+
+// ---- numeric passes ----
+hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leaves,
+                      int64_t n_leaves, const int32_t* begin, const int32_t* count,
+                      const double* centre, void* mpole, hipStream_t st);
+hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
+                      const int32_t* first_child, const uint8_t* n_child, const double* centre,
+                      void* mpole, hipStream_t st);
+hipError_t launch_m2l(int dtype, int order, int64_t n_nodes, const int64_t* off,
+                      const int32_t* src, const double* centre, const void* mpole, void* local,
+                      hipStream_t st);
+hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
+                      const int32_t* parent, const double* centre, void* local, hipStream_t st);
+hipError_t launch_l2p(int dtype, int order, int64_t n, const void* pts, const int32_t* leaf_of,
+                      const double* centre, const void* local, void* far, hipStream_t st);
+hipError_t launch_p2p(int dtype, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
+                      const int32_t* count, const int64_t* off, const int32_t* src,
+                      const void* pts, const void* far, const int32_t* perm, void* phi,
+                      void* acc, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// expansions in the plan's dtype/convention -> fp64 raw moments / derivatives
+hipError_t launch_export_expansions(int dtype, int order, int64_t n_nodes, const void* mpole,
+                                    const void* local, double* mp_out, double* lc_out,
+                                    hipStream_t st);
+
+}  // namespace mbg

@@ -1,0 +1,63 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/fmm.h declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fmm_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from multipole_body_gravity_amd import fmm
+    return fmm.load_library()
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for want in ["fmm_plan", "fmm_build", "fmm_eval", "fmm_destroy", "fmm_strerror",
+                 "fmm_set_timing", "fmm_stats", "fmm_copy_keys", "fmm_copy_tree",
+                 "fmm_copy_lists", "fmm_copy_expansions"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror(lib):
+    for code in [0, -1, -2, -3, -4, -5, -6]:
+        s = lib.fmm_strerror(code)
+        assert s and s != b"unknown status"
+    assert lib.fmm_strerror(12345) == b"unknown status"
+
+
+@pytest.mark.parametrize("args", [
+    (0, 4, 0.7, 32, 1), (-5, 4, 0.7, 32, 1), (2 ** 31, 4, 0.7, 32, 1),
+    (10, -1, 0.7, 32, 1), (10, 9, 0.7, 32, 1),
+    (10, 4, 0.0, 32, 1), (10, 4, 1.0, 32, 1), (10, 4, float("nan"), 32, 1),
+    (10, 4, 0.7, 0, 1), (10, 4, 0.7, 32, 2), (10, 4, 0.7, 32, -1)])
+def test_plan_rejects_bad_arguments(lib, args):
+    h = ctypes.c_void_p()
+    assert lib.fmm_plan(ctypes.byref(h), *args) == -1
+    assert not h.value
+
+
+def test_null_plan_calls(lib):
+    P = ctypes.c_void_p
+    assert lib.fmm_build(None, P(1), P(1), None) == -1
+    assert lib.fmm_eval(None, P(1), P(1), None) == -1
+    assert lib.fmm_destroy(None) == -1
+    assert lib.fmm_set_timing(None, 1) == -1
+    assert lib.fmm_copy_keys(None, None, None) == -1
+    assert lib.fmm_plan(None, 10, 4, 0.7, 32, 1) == -1
