@@ -11,12 +11,6 @@
 
 using namespace mbg;
 
-namespace mbg {
-hipError_t launch_walk_root(int pass, int root_leaf, const WalkArgs& a, hipStream_t st);
-hipError_t launch_walk_reset(Control* ctrl, hipStream_t st);
-hipError_t launch_walk_totals(const int64_t* m2l_total, const int64_t* p2p_total, Control* ctrl,
-                              hipStream_t st);
-}  // namespace mbg
 
 namespace {
 
@@ -87,45 +81,33 @@ int sync_ctrl(fmm_plan_t p, hipStream_t st) {
 }
 
 // ---------------- walk ----------------
+int bits_for(int64_t v) {  // bits to hold 0..v
+  int b = 1;
+  while (b < 62 && ((int64_t)1 << b) <= v) b++;
+  return b;
+}
+
 int run_walk(fmm_plan_t p, hipStream_t st) {
   const int depth = p->depth;
   const int64_t nn = p->n_nodes;
-  // item capacities: type-A items of step s come from leaf items of step s-1
-  int64_t amax[MAX_LEVELS + 2] = {0}, base[MAX_LEVELS + 3] = {0};
-  for (int s = 1; s <= depth + 1; s++) {
-    int64_t leaves_prev = (s - 1 <= MAX_LEVELS - 1) ? p->leaves_at_level[s - 1] : 0;
-    amax[s] = amax[s - 1] + leaves_prev;
-  }
-  for (int s = 0; s <= depth + 1; s++) {
-    int64_t lc = (s <= depth) ? p->level_off[s + 1] - p->level_off[s] : 0;
-    base[s + 1] = base[s] + amax[s] + lc;
-  }
-  const int64_t n_items = base[depth + 2];
-  for (int s = 0; s <= depth + 1; s++) {
-    p->item_base[s] = base[s];
-    p->item_amax[s] = amax[s];
-  }
-  // item SoA: tgt i32, gen_off i64, gen_cnt i32, carry_off i64, carry_cnt i32
-  TRY(grow(p->items, (size_t)n_items * 28 + 64));
-  char* ib = P<char>(p->items);
-  WalkItems it;
-  it.gen_off = (int64_t*)ib;
-  it.carry_off = it.gen_off + n_items;
-  it.tgt = (int32_t*)(it.carry_off + n_items);
-  it.gen_cnt = it.tgt + n_items;
-  it.carry_cnt = it.gen_cnt + n_items;
-
+  const int64_t nl = p->n_leaves;
+  TRY(grow(p->carry_off, (size_t)nn * 8));
+  TRY(grow(p->carry_cnt, (size_t)nn * 4));
+  TRY(grow(p->own_m2l, (size_t)nn * 4));
+  TRY(grow(p->own_p2p, (size_t)nn * 4));
+  TRY(grow(p->tr_cnt_m2l, (size_t)2 * nn * 4));  // [kind][node]
+  TRY(grow(p->tr_start_m2l, (size_t)2 * nn * 8));
   TRY(grow(p->tot_m2l, (size_t)(nn + 1) * 8));
   TRY(grow(p->tot_p2p, (size_t)(nn + 1) * 8));
-  TRY(grow(p->cur_m2l, (size_t)(nn + 1) * 8));
-  TRY(grow(p->cur_p2p, (size_t)(nn + 1) * 8));
   TRY(grow(p->m2l_off, (size_t)(nn + 1) * 8));
   TRY(grow(p->p2p_off, (size_t)(nn + 1) * 8));
-  TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
-  if (p->carry_cap < 64 * nn + 1024) {
-    p->carry_cap = std::max<int64_t>(p->carry_cap, 160 * nn + 1024);
-  }
-  TRY(grow(p->carry, (size_t)p->carry_cap * 4));
+  TRY(grow(p->p2p_toff, (size_t)(nl + 1) * 8));
+  TRY(grow(p->p2p_poff, (size_t)(nl + 1) * 8));
+  TRY(grow(p->scan_tmp, scan_tmp_bytes(std::max(nn, nl) + 1)));
+  // first guesses for the pools (regrown from the measured use on overflow)
+  const int64_t guess[3] = {96 * nn + 4096, 24 * nn + 4096, 12 * nn + 4096};
+  for (int k = 0; k < 3; k++)
+    p->shard_cap[k] = std::max<int64_t>(p->shard_cap[k], guess[k] / POOL_SHARDS + 64);
 
   WalkArgs a{};
   a.level = P<uint8_t>(p->nlevel);
@@ -134,64 +116,112 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   a.n_child = P<uint8_t>(p->nnchild);
   a.parent = P<int32_t>(p->nparent);
   a.t2 = p->t2;
-  a.it = it;
-  a.carry = P<int32_t>(p->carry);
-  a.carry_cap = p->carry_cap;
-  a.tot_m2l = P<int64_t>(p->tot_m2l);
-  a.tot_p2p = P<int64_t>(p->tot_p2p);
-  a.cur_m2l = P<int64_t>(p->cur_m2l);
-  a.cur_p2p = P<int64_t>(p->cur_p2p);
+  a.carry_off = P<int64_t>(p->carry_off);
+  a.carry_cnt = P<int32_t>(p->carry_cnt);
+  a.own_m2l = P<int32_t>(p->own_m2l);
+  a.own_p2p = P<int32_t>(p->own_p2p);
   a.m2l_off = P<int64_t>(p->m2l_off);
   a.p2p_off = P<int64_t>(p->p2p_off);
+  a.key_shift = bits_for(nn);
+  const int kind_bit = 2 * a.key_shift;
   a.ctrl = P<Control>(p->ctrl);
+  Control* dctrl = P<Control>(p->ctrl);
   const int root_leaf = (depth == 0) ? 1 : 0;
   auto step_args = [&](int s) {
     WalkArgs b = a;
     b.step = s;
     b.lvl_begin = p->level_off[s];
     b.lvl_count = p->level_off[s + 1] - p->level_off[s];
-    b.prev_lvl_begin = s > 0 ? p->level_off[s - 1] : 0;
-    b.base = base[s];
-    b.amax = amax[s];
-    b.prev_base = s > 0 ? base[s - 1] : 0;
-    b.prev_amax = s > 0 ? amax[s - 1] : 0;
-    b.next_base = base[s + 1];
-    b.next_amax = amax[s + 1];
     return b;
   };
+  int32_t* leaves = P<int32_t>(p->leaves);
+  int64_t* toff = P<int64_t>(p->p2p_toff);
+  int64_t* poff = P<int64_t>(p->p2p_poff);
 
   p->walk_retries = 0;
   for (;;) {
-    TRY_HIP(launch_fill_zero(p->tot_m2l.p, (size_t)(nn + 1) * 8, st));
-    TRY_HIP(launch_fill_zero(p->tot_p2p.p, (size_t)(nn + 1) * 8, st));
-    TRY_HIP(launch_walk_reset(P<Control>(p->ctrl), st));
+    TRY(grow(p->carry, (size_t)p->shard_cap[0] * POOL_SHARDS * 4));
+    TRY(grow(p->trm_pool, (size_t)p->shard_cap[1] * POOL_SHARDS * 8));
+    TRY(grow(p->trp_pool, (size_t)p->shard_cap[2] * POOL_SHARDS * 8));
+    a.carry = Pool<int32_t>{P<int32_t>(p->carry), p->shard_cap[0], dctrl->pool_used[0]};
+    a.trm = Pool<uint64_t>{P<uint64_t>(p->trm_pool), p->shard_cap[1], dctrl->pool_used[1]};
+    a.trp = Pool<uint64_t>{P<uint64_t>(p->trp_pool), p->shard_cap[2], dctrl->pool_used[2]};
+    TRY_HIP(launch_walk_reset(dctrl, st));
     TRY_HIP(launch_walk_root(1, root_leaf, step_args(0), st));
     for (int s = 1; s <= depth; s++) TRY_HIP(launch_walk_pass1(step_args(s), st));
-    TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_m2l), P<int64_t>(p->m2l_off), nn,
-                               P<int64_t>(p->m2l_off) + nn, p->scan_tmp.p, st));
-    TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_p2p), P<int64_t>(p->p2p_off), nn,
-                               P<int64_t>(p->p2p_off) + nn, p->scan_tmp.p, st));
-    TRY_HIP(launch_walk_totals(P<int64_t>(p->m2l_off) + nn, P<int64_t>(p->p2p_off) + nn,
-                               P<Control>(p->ctrl), st));
+    TRY_HIP(launch_walk_own_totals(nn, a.own_m2l, a.own_p2p, dctrl, st));
     TRY(sync_ctrl(p, st));
-    if (!p->ctrl_host->carry_overflow) break;
+    if (!p->ctrl_host->pool_overflow) break;
     if (++p->walk_retries > 4) return FMM_ERR_OOM;
-    int64_t need = p->ctrl_host->carry_used;
-    p->carry_cap = std::max<int64_t>(need + need / 4 + 1024, 2 * p->carry_cap);
-    TRY(grow(p->carry, (size_t)p->carry_cap * 4));
-    a.carry = P<int32_t>(p->carry);
-    a.carry_cap = p->carry_cap;
+    for (int k = 0; k < 3; k++) {
+      int64_t mx = 0;
+      for (int sh = 0; sh < POOL_SHARDS; sh++) mx = std::max(mx, p->ctrl_host->pool_used[k][sh]);
+      if (mx > p->shard_cap[k]) p->shard_cap[k] = mx + mx / 2 + 64;
+    }
   }
-  p->n_m2l = p->ctrl_host->n_m2l;
-  p->n_p2p = p->ctrl_host->n_p2p;
+  const Control& c = *p->ctrl_host;
+  int64_t ntm = 0, ntp = 0;
+  for (int sh = 0; sh < POOL_SHARDS; sh++) {
+    ntm += c.pool_used[1][sh];
+    ntp += c.pool_used[2][sh];
+  }
+  const int64_t ntr = ntm + ntp;
+  p->n_m2l = c.own_m2l_total + ntm;
+  p->n_p2p = c.own_p2p_total + ntp;
   TRY(grow(p->m2l_src, (size_t)p->n_m2l * 4));
   TRY(grow(p->p2p_src, (size_t)p->n_p2p * 4));
   a.m2l_src = P<int32_t>(p->m2l_src);
   a.p2p_src = P<int32_t>(p->p2p_src);
-  TRY_HIP(launch_fill_zero(p->cur_m2l.p, (size_t)(nn + 1) * 8, st));
-  TRY_HIP(launch_fill_zero(p->cur_p2p.p, (size_t)(nn + 1) * 8, st));
+
+  // transposed entries: dense copy, sort by (kind, target, source), run lengths
+  int32_t* tr_cnt = P<int32_t>(p->tr_cnt_m2l);
+  int64_t* tr_start = P<int64_t>(p->tr_start_m2l);
+  TRY_HIP(launch_fill_zero(tr_cnt, (size_t)2 * nn * 4, st));
+  const uint64_t* sorted = nullptr;
+  if (ntr > 0) {
+    TRY(grow(p->tr_keys, (size_t)ntr * 8));
+    TRY(grow(p->tr_keys_alt, (size_t)ntr * 8));
+    TRY(grow(p->tr_vals, (size_t)ntr * 4));
+    TRY(grow(p->tr_vals_alt, (size_t)ntr * 4));
+    TRY(grow(p->radix_hist, 4 * radix_hist_ints(ntr)));
+    TRY(grow(p->scan_tmp, scan_tmp_bytes((int64_t)radix_hist_ints(ntr))));
+    TRY_HIP(launch_tr_compact(a, kind_bit, P<uint64_t>(p->tr_keys), st));
+    bool in_alt = false;
+    TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), P<int32_t>(p->tr_vals),
+                                   P<uint64_t>(p->tr_keys_alt), P<int32_t>(p->tr_vals_alt), ntr,
+                                   kind_bit + 1, P<int32_t>(p->radix_hist),
+                                   P<int32_t>(p->scan_tmp), &in_alt, st));
+    sorted = in_alt ? P<uint64_t>(p->tr_keys_alt) : P<uint64_t>(p->tr_keys);
+    TRY_HIP(launch_tr_runs(sorted, ntr, a.key_shift, kind_bit, nn, tr_start, tr_cnt, st));
+  }
+  TRY_HIP(launch_walk_offsets(nn, a.own_m2l, a.own_p2p, tr_cnt, tr_cnt + nn,
+                              P<int64_t>(p->tot_m2l), P<int64_t>(p->tot_p2p), st));
+  TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_m2l), P<int64_t>(p->m2l_off), nn,
+                             P<int64_t>(p->m2l_off) + nn, p->scan_tmp.p, st));
+  TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_p2p), P<int64_t>(p->p2p_off), nn,
+                             P<int64_t>(p->p2p_off) + nn, p->scan_tmp.p, st));
   TRY_HIP(launch_walk_root(2, root_leaf, step_args(0), st));
   for (int s = 1; s <= depth; s++) TRY_HIP(launch_walk_pass2(step_args(s), st));
+  if (ntr > 0)
+    TRY_HIP(launch_tr_scatter(sorted, ntr, a.key_shift, kind_bit, nn, P<int64_t>(p->m2l_off),
+                              a.own_m2l, tr_start, a.m2l_src, P<int64_t>(p->p2p_off), a.own_p2p,
+                              tr_start + nn, a.p2p_src, st));
+
+  // near-field tasks
+  TRY_HIP(launch_p2p_task_count(leaves, nl, P<int64_t>(p->p2p_off), P<int32_t>(p->ncount), toff,
+                                poff, st));
+  TRY_HIP(scan_exclusive_i64(toff, toff, nl, toff + nl, p->scan_tmp.p, st));
+  TRY_HIP(scan_exclusive_i64(poff, poff, nl, poff + nl, p->scan_tmp.p, st));
+  TRY_HIP(launch_walk_copy_totals(P<int64_t>(p->m2l_off) + nn, P<int64_t>(p->p2p_off) + nn,
+                                  toff + nl, poff + nl, dctrl, st));
+  TRY(sync_ctrl(p, st));
+  if (p->ctrl_host->n_m2l != p->n_m2l || p->ctrl_host->n_p2p != p->n_p2p) return FMM_ERR_HIP;
+  p->n_p2p_tasks = p->ctrl_host->n_p2p_tasks;
+  p->n_p2p_part = p->ctrl_host->n_p2p_part;
+  TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
+  TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
+  TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, P<int64_t>(p->p2p_off),
+                               P<int32_t>(p->ncount), p->p2p_task.p, st));
   return FMM_OK;
 }
 
@@ -263,9 +293,13 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->lcp, &p->wlev, &p->wtmp, &p->leaf_level, &p->leaf_of, &p->radix_hist,
                   &p->scan_tmp, &p->root, &p->ctrl, &p->bbox_part, &p->nlevel, &p->nprefix,
                   &p->nbegin, &p->ncount, &p->nparent, &p->nfirst, &p->nnchild, &p->ncentre,
-                  &p->nq, &p->leaves, &p->lvl_blkcnt, &p->mpole, &p->local, &p->items, &p->carry,
-                  &p->tot_m2l, &p->tot_p2p, &p->cur_m2l, &p->cur_p2p, &p->m2l_off, &p->m2l_src,
-                  &p->p2p_off, &p->p2p_src};
+                  &p->nq, &p->leaves, &p->lvl_blkcnt, &p->mpole, &p->local, &p->carry,
+                  &p->trm_pool, &p->trp_pool, &p->carry_off, &p->carry_cnt, &p->own_m2l,
+                  &p->own_p2p, &p->tr_cnt_m2l, &p->tr_cnt_p2p, &p->tr_start_m2l,
+                  &p->tr_start_p2p, &p->tr_keys, &p->tr_keys_alt, &p->tr_vals,
+                  &p->tr_vals_alt, &p->m2l_off, &p->m2l_src, &p->p2p_off, &p->p2p_src,
+                  &p->p2p_task, &p->p2p_part, &p->p2p_toff, &p->p2p_poff, &p->tot_m2l,
+                  &p->tot_p2p};
   for (DBuf* b : bufs) release(*b);
   if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);
   for (int i = 0; i < 2 * FMM_N_STAGES; i++)
@@ -384,9 +418,10 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   rec(p, FMM_STAGE_DOWN, 1, st);
 
   rec(p, FMM_STAGE_P2P, 0, st);
-  TRY_HIP(launch_p2p(dt, leaves, p->n_leaves, P<int32_t>(p->nbegin), P<int32_t>(p->ncount),
-                     P<int64_t>(p->p2p_off), P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
-                     P<int32_t>(p->idx), phi, acc, st));
+  TRY_HIP(launch_p2p(dt, p->p2p_task.p, p->n_p2p_tasks, leaves, p->n_leaves,
+                     P<int64_t>(p->p2p_toff), P<int64_t>(p->p2p_poff), P<int32_t>(p->nbegin),
+                     P<int32_t>(p->ncount), P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
+                     P<int32_t>(p->idx), phi, acc, p->p2p_part.p, p->n_p2p_part > 0, st));
   rec(p, FMM_STAGE_P2P, 1, st);
   p->evaluated = true;
   return FMM_OK;

@@ -166,14 +166,25 @@ __global__ void __launch_bounds__(BB_THREADS)
   }
 }
 
-__global__ void k_bbox_final(const double* part, int nblk, RootInfo* root) {
-  if (threadIdx.x != 0) return;
-  double lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
-  for (int b = 0; b < nblk; b++)
+__global__ void __launch_bounds__(BB_THREADS) k_bbox_final(const double* part, int nblk, RootInfo* root) {
+  __shared__ double s[6][BB_THREADS];
+  double l6[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int b = threadIdx.x; b < nblk; b += BB_THREADS)
     for (int a = 0; a < 3; a++) {
-      lo[a] = fmin(lo[a], part[6 * b + a]);
-      hi[a] = fmax(hi[a], part[6 * b + 3 + a]);
+      l6[a] = fmin(l6[a], part[6 * b + a]);
+      l6[3 + a] = fmax(l6[3 + a], part[6 * b + 3 + a]);
     }
+  for (int a = 0; a < 6; a++) s[a][threadIdx.x] = l6[a];
+  __syncthreads();
+  for (int h = BB_THREADS / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h)
+      for (int a = 0; a < 6; a++)
+        s[a][threadIdx.x] = a < 3 ? fmin(s[a][threadIdx.x], s[a][threadIdx.x + h])
+                                  : fmax(s[a][threadIdx.x], s[a][threadIdx.x + h]);
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  double lo[3] = {s[0][0], s[1][0], s[2][0]}, hi[3] = {s[3][0], s[4][0], s[5][0]};
   double ext = 0.0;
   for (int a = 0; a < 3; a++) ext = fmax(ext, __dsub_rn(hi[a], lo[a]));
   // smallest power of two >= ext (1 if ext == 0)
@@ -198,7 +209,7 @@ hipError_t launch_bbox(const void* pos, const void* mass, int64_t n, int dtype, 
   else
     k_bbox_partial<float><<<nblk, BB_THREADS, 0, st>>>((const float*)pos, (const float*)mass, n,
                                                        part, ctrl);
-  k_bbox_final<<<1, 64, 0, st>>>(part, nblk, root);
+  k_bbox_final<<<1, BB_THREADS, 0, st>>>(part, nblk, root);
   return hipGetLastError();
 }
 
@@ -315,12 +326,16 @@ __global__ void __launch_bounds__(RS_THREADS)
   }
 }
 
-hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
-                             int64_t n, int32_t* hist, int32_t* scan_tmp, hipStream_t st) {
+hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
+                                  int32_t* idx_alt, int64_t n, int bits, int32_t* hist,
+                                  int32_t* scan_tmp, bool* in_alt, hipStream_t st) {
+  *in_alt = false;
+  if (n <= 0) return hipSuccess;
   int nblk = (int)((n + RS_TILE - 1) / RS_TILE);
   uint64_t *ka = keys, *kb = keys_alt;
   int32_t *va = idx, *vb = idx_alt;
-  for (int pass = 0; pass < 8; pass++) {
+  const int passes = (bits + 7) / 8;
+  for (int pass = 0; pass < passes; pass++) {
     int shift = 8 * pass;
     k_radix_hist<<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, hist, nblk);
     hipError_t e = scan_excl<int32_t>(hist, hist, (int64_t)256 * nblk, nullptr, scan_tmp, st);
@@ -332,9 +347,16 @@ hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, i
     int32_t* tv = va;
     va = vb;
     vb = tv;
+    *in_alt = !*in_alt;
   }
-  // 8 passes: the result is back in (keys, idx)
   return hipGetLastError();
+}
+
+hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
+                             int64_t n, int32_t* hist, int32_t* scan_tmp, hipStream_t st) {
+  bool alt;
+  // 8 passes of 8 bits over the 63-bit keys: the result is back in (keys, idx)
+  return launch_radix_sort_bits(keys, idx, keys_alt, idx_alt, n, 64, hist, scan_tmp, &alt, st);
 }
 
 // ===================================================================
@@ -451,12 +473,18 @@ __global__ void k_tree_levelinfo(const int64_t* scanned, int nblk, const int64_t
 
 // leaves per level = sum over blocks of the leaf-start counts (the upper half
 // of blkcnt); reduced in a fixed order by one thread per level
-__global__ void k_tree_leaflevels(const int64_t* blkcnt, int nblk, int64_t* out) {
-  int l = threadIdx.x;
-  if (l >= MAX_LEVELS) return;
-  int64_t s = 0;
-  for (int b = 0; b < nblk; b++) s += blkcnt[(int64_t)(MAX_LEVELS + l) * nblk + b];
-  out[l] = s;
+__global__ void __launch_bounds__(256) k_tree_leaflevels(const int64_t* blkcnt, int nblk, int64_t* out) {
+  __shared__ int64_t s[256];
+  const int l = blockIdx.x;  // one block per level
+  int64_t v = 0;
+  for (int b = threadIdx.x; b < nblk; b += 256) v += blkcnt[(int64_t)(MAX_LEVELS + l) * nblk + b];
+  s[threadIdx.x] = v;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) s[threadIdx.x] += s[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[l] = s[0];
 }
 
 hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t* lcp, int8_t* wlev,
@@ -484,7 +512,7 @@ hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t*
   }
   k_tree_leafcount<<<nblk, TR_THREADS, 0, st>>>(lcp, stj, n, S, span2, leaf_level, blkcnt, nblk);
   // leaf counts per level live in the upper half and are not scanned
-  k_tree_leaflevels<<<1, 64, 0, st>>>(blkcnt, nblk, ctrl->leaves_at_level);
+  k_tree_leaflevels<<<MAX_LEVELS, 256, 0, st>>>(blkcnt, nblk, ctrl->leaves_at_level);
   int64_t total_len = (int64_t)MAX_LEVELS * nblk;
   int64_t* total = blkcnt + 2 * total_len;  // the spare slot after both halves
   hipError_t e = scan_excl<int64_t>(blkcnt, blkcnt, total_len, total, scan_tmp, st);

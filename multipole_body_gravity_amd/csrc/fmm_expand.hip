@@ -14,6 +14,8 @@
 // to its parent is Mt_m(P) = sum_{k<=m} Mt_k(child) (-d)^(m-k)/(m-k)!, d =
 // c_child - c_P, and the multipole-to-local step becomes a plain contraction.
 // The local array holds the derivatives L_n = d^n Phi at the cell centre.
+#include <algorithm>
+
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -49,31 +51,70 @@ static hipError_t ensure_table() {
   return e;
 }
 
+__constant__ double c_inv_int[FMM_MAX_ORDER + 2] = {0.0,       1.0,       0.5,
+                                                     1.0 / 3.0, 0.25,      0.2,
+                                                     1.0 / 6.0, 1.0 / 7.0, 0.125, 1.0 / 9.0};
+
+// x^n / n!
 __device__ __forceinline__ double pow_over_fact(double x, int n) {
   double r = 1.0;
-  for (int i = 1; i <= n; i++) r = r * x / (double)i;
+  for (int i = 1; i <= n; i++) r = r * x * c_inv_int[i];
   return r;
 }
 
-// ---------------- P2M: one thread per (leaf, coefficient) ----------------
+constexpr int EX_THREADS = 256;
+constexpr int EX_WAVES = EX_THREADS / WAVE;
+constexpr int PP = FMM_MAX_ORDER + 1;  // entries of a 1-d power table
+constexpr int MAXCH = 8;
+
+// ---------------- P2M: one wave per leaf, lanes over coefficients ----------------
+// Particles are staged 64 at a time: lane j tabulates (-s_j)^a / a! per axis in
+// LDS, then lane m accumulates m_j * ex[a] ey[b] ez[c] over the staged particles
+// in particle order.
 template <typename T>
-__global__ void k_p2m(int K, const P4<T>* pts, const int32_t* leaves, int64_t n_leaves,
-                      const int32_t* begin, const int32_t* count, const double* centre, T* mpole) {
-  int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (gid >= n_leaves * K) return;
-  const int64_t li = gid / K;
-  const int m = (int)(gid - li * K);
-  const int32_t node = leaves[li];
-  const int a = c_mi.a[m], b = c_mi.b[m], c = c_mi.c[m];
-  const double cx = centre[3 * node], cy = centre[3 * node + 1], cz = centre[3 * node + 2];
-  double acc = 0.0;
-  const int32_t j0 = begin[node], j1 = j0 + count[node];
-  for (int32_t j = j0; j < j1; j++) {
-    const P4<T> p = pts[j];
-    const double sx = cx - (double)p.x, sy = cy - (double)p.y, sz = cz - (double)p.z;  // -s
-    acc += (double)p.m * pow_over_fact(sx, a) * pow_over_fact(sy, b) * pow_over_fact(sz, c);
+__global__ void __launch_bounds__(EX_THREADS)
+    k_p2m(int order, int K, const P4<T>* pts, const int32_t* leaves, int64_t n_leaves,
+          const int32_t* begin, const int32_t* count, const double* centre, T* mpole) {
+  __shared__ double tab[EX_WAVES][WAVE][3][PP];
+  __shared__ double ms[EX_WAVES][WAVE];
+  const int lane = __lane_id(), w = threadIdx.x / WAVE;
+  for (int64_t li = (int64_t)blockIdx.x * EX_WAVES + w; li < n_leaves;
+       li += (int64_t)gridDim.x * EX_WAVES) {
+    const int32_t node = leaves[li];
+    const double c[3] = {centre[3 * node], centre[3 * node + 1], centre[3 * node + 2]};
+    double acc[3] = {0.0, 0.0, 0.0};  // coefficients lane, lane+64, lane+128
+    const int32_t j0 = begin[node], j1 = j0 + count[node];
+    for (int32_t jb = j0; jb < j1; jb += WAVE) {
+      const int nj = min(WAVE, j1 - jb);
+      if (lane < nj) {
+        const P4<T> p = pts[jb + lane];
+        const double xs[3] = {c[0] - (double)p.x, c[1] - (double)p.y, c[2] - (double)p.z};
+        for (int ax = 0; ax < 3; ax++) {
+          double v = 1.0;
+          tab[w][lane][ax][0] = 1.0;
+          for (int q = 1; q <= order; q++) {
+            v = v * xs[ax] * c_inv_int[q];
+            tab[w][lane][ax][q] = v;
+          }
+        }
+        ms[w][lane] = (double)p.m;
+      }
+      __builtin_amdgcn_wave_barrier();
+      for (int r = 0; r < 3; r++) {
+        const int m = lane + WAVE * r;
+        if (m >= K) break;
+        const int a = c_mi.a[m], b = c_mi.b[m], cc = c_mi.c[m];
+        double s = acc[r];
+        for (int j = 0; j < nj; j++) s += ms[w][j] * tab[w][j][0][a] * tab[w][j][1][b] * tab[w][j][2][cc];
+        acc[r] = s;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    for (int r = 0; r < 3; r++) {
+      const int m = lane + WAVE * r;
+      if (m < K) mpole[(int64_t)node * K + m] = (T)acc[r];
+    }
   }
-  mpole[(int64_t)node * K + m] = (T)acc;
 }
 
 hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leaves,
@@ -82,48 +123,65 @@ hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leav
   hipError_t e = ensure_table();
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
-  int64_t nt = n_leaves * K;
-  if (nt == 0) return hipSuccess;
-  unsigned g = (unsigned)((nt + 255) / 256);
+  if (n_leaves == 0) return hipSuccess;
+  int64_t blocks = std::min<int64_t>((n_leaves + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
-    k_p2m<double><<<g, 256, 0, st>>>(K, (const P4<double>*)pts, leaves, n_leaves, begin, count,
-                                     centre, (double*)mpole);
+    k_p2m<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, (const P4<double>*)pts, leaves,
+                                                            n_leaves, begin, count, centre,
+                                                            (double*)mpole);
   else
-    k_p2m<float><<<g, 256, 0, st>>>(K, (const P4<float>*)pts, leaves, n_leaves, begin, count,
-                                    centre, (float*)mpole);
+    k_p2m<float><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, (const P4<float>*)pts, leaves,
+                                                           n_leaves, begin, count, centre,
+                                                           (float*)mpole);
   return hipGetLastError();
 }
 
-// ---------------- M2M: one thread per (parent, coefficient) ----------------
+// ---------------- M2M: one wave per parent, lanes over coefficients ----------------
+// Mt_m(P) = sum_children sum_{k<=m} Mt_k(child) (-d)^(m-k) / (m-k)!, d = c_child - c_P;
+// the children's moments and power tables are staged in LDS, children and
+// terms are added in a fixed order.
 template <typename T>
-__global__ void k_m2m(int K, int64_t lvl_begin, int64_t lvl_count, const int32_t* first_child,
-                      const uint8_t* n_child, const double* centre, T* mpole) {
-  int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (gid >= lvl_count * K) return;
-  const int64_t pi = gid / K;
-  const int m = (int)(gid - pi * K);
-  const int64_t P = lvl_begin + pi;
-  const int nc = n_child[P];
-  if (nc == 0) return;  // leaf: moments come from P2M
-  const int ma = c_mi.a[m], mb = c_mi.b[m], mc = c_mi.c[m];
-  double acc = 0.0;
-  const int32_t fc = first_child[P];
-  for (int ci = 0; ci < nc; ci++) {
-    const int64_t ch = fc + ci;
-    // -d = c_P - c_child
-    const double nx = centre[3 * P] - centre[3 * ch], ny = centre[3 * P + 1] - centre[3 * ch + 1],
-                 nz = centre[3 * P + 2] - centre[3 * ch + 2];
-    const T* Mc = mpole + ch * K;
-    for (int i = 0; i <= ma; i++) {
-      const double ex = pow_over_fact(nx, ma - i);
-      for (int j = 0; j <= mb; j++) {
-        const double exy = ex * pow_over_fact(ny, mb - j);
-        for (int k = 0; k <= mc; k++)
-          acc += (double)Mc[mi_index(i, j, k)] * exy * pow_over_fact(nz, mc - k);
+__global__ void __launch_bounds__(EX_THREADS)
+    k_m2m(int order, int K, int64_t lvl_begin, int64_t lvl_count, const int32_t* first_child,
+          const uint8_t* n_child, const double* centre, T* mpole) {
+  __shared__ double mc[EX_WAVES][MAXCH][ncoef(FMM_MAX_ORDER)];
+  __shared__ double tab[EX_WAVES][MAXCH][3][PP];
+  const int lane = __lane_id(), w = threadIdx.x / WAVE;
+  for (int64_t pi = (int64_t)blockIdx.x * EX_WAVES + w; pi < lvl_count;
+       pi += (int64_t)gridDim.x * EX_WAVES) {
+    const int64_t P = lvl_begin + pi;
+    const int nc = n_child[P];
+    if (nc == 0) continue;  // leaf: moments come from P2M
+    const int64_t fc = first_child[P];
+    for (int q = lane; q < nc * K; q += WAVE) {
+      const int ch = q / K, k = q - ch * K;
+      mc[w][ch][k] = (double)mpole[(fc + ch) * K + k];
+    }
+    if (lane < 3 * nc) {
+      const int ch = lane / 3, ax = lane - 3 * ch;
+      const double nd = centre[3 * P + ax] - centre[3 * (fc + ch) + ax];  // -d
+      double v = 1.0;
+      tab[w][ch][ax][0] = 1.0;
+      for (int q = 1; q <= order; q++) {
+        v = v * nd * c_inv_int[q];
+        tab[w][ch][ax][q] = v;
       }
     }
+    __builtin_amdgcn_wave_barrier();
+    for (int m = lane; m < K; m += WAVE) {
+      const int ma = c_mi.a[m], mb = c_mi.b[m], mcc = c_mi.c[m];
+      double acc = 0.0;
+      for (int ch = 0; ch < nc; ch++)
+        for (int i = 0; i <= ma; i++)
+          for (int j = 0; j <= mb; j++) {
+            const double exy = tab[w][ch][0][ma - i] * tab[w][ch][1][mb - j];
+            for (int k = 0; k <= mcc; k++)
+              acc += mc[w][ch][mi_index(i, j, k)] * exy * tab[w][ch][2][mcc - k];
+          }
+      mpole[P * K + m] = (T)acc;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
-  mpole[P * K + m] = (T)acc;
 }
 
 hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
@@ -132,44 +190,57 @@ hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
   hipError_t e = ensure_table();
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
-  int64_t nt = lvl_count * K;
-  if (nt == 0) return hipSuccess;
-  unsigned g = (unsigned)((nt + 255) / 256);
+  if (lvl_count == 0) return hipSuccess;
+  int64_t blocks = std::min<int64_t>((lvl_count + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
-    k_m2m<double><<<g, 256, 0, st>>>(K, lvl_begin, lvl_count, first_child, n_child, centre,
-                                     (double*)mpole);
+    k_m2m<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, lvl_begin, lvl_count,
+                                                            first_child, n_child, centre,
+                                                            (double*)mpole);
   else
-    k_m2m<float><<<g, 256, 0, st>>>(K, lvl_begin, lvl_count, first_child, n_child, centre,
-                                    (float*)mpole);
+    k_m2m<float><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, lvl_begin, lvl_count,
+                                                           first_child, n_child, centre,
+                                                           (float*)mpole);
   return hipGetLastError();
 }
 
-// ---------------- L2L: one thread per (child, coefficient) ----------------
+// ---------------- L2L: one wave per child, lanes over coefficients ----------------
 // L_n(child) += sum_{|n|+|k|<=p} L_(n+k)(parent) d^k / k!, d = c_child - c_parent
 template <typename T>
-__global__ void k_l2l(int order, int K, int64_t lvl_begin, int64_t lvl_count, const int32_t* parent,
-                      const double* centre, T* local) {
-  int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (gid >= lvl_count * K) return;
-  const int64_t ci = gid / K;
-  const int n = (int)(gid - ci * K);
-  const int64_t a = lvl_begin + ci;
-  const int64_t P = parent[a];
-  const int na = c_mi.a[n], nb = c_mi.b[n], nc = c_mi.c[n];
-  const int rem = order - (na + nb + nc);
-  const double dx = centre[3 * a] - centre[3 * P], dy = centre[3 * a + 1] - centre[3 * P + 1],
-               dz = centre[3 * a + 2] - centre[3 * P + 2];
-  const T* Lp = local + P * K;
-  double acc = 0.0;
-  for (int i = 0; i <= rem; i++) {
-    const double ex = pow_over_fact(dx, i);
-    for (int j = 0; i + j <= rem; j++) {
-      const double exy = ex * pow_over_fact(dy, j);
-      for (int k = 0; i + j + k <= rem; k++)
-        acc += (double)Lp[mi_index(na + i, nb + j, nc + k)] * exy * pow_over_fact(dz, k);
+__global__ void __launch_bounds__(EX_THREADS)
+    k_l2l(int order, int K, int64_t lvl_begin, int64_t lvl_count, const int32_t* parent,
+          const double* centre, T* local) {
+  __shared__ double lp[EX_WAVES][ncoef(FMM_MAX_ORDER)];
+  __shared__ double tab[EX_WAVES][3][PP];
+  const int lane = __lane_id(), w = threadIdx.x / WAVE;
+  for (int64_t ci = (int64_t)blockIdx.x * EX_WAVES + w; ci < lvl_count;
+       ci += (int64_t)gridDim.x * EX_WAVES) {
+    const int64_t a = lvl_begin + ci;
+    const int64_t P = parent[a];
+    for (int k = lane; k < K; k += WAVE) lp[w][k] = (double)local[P * K + k];
+    if (lane < 3) {
+      const double d = centre[3 * a + lane] - centre[3 * P + lane];
+      double v = 1.0;
+      tab[w][lane][0] = 1.0;
+      for (int q = 1; q <= order; q++) {
+        v = v * d * c_inv_int[q];
+        tab[w][lane][q] = v;
+      }
     }
+    __builtin_amdgcn_wave_barrier();
+    for (int n = lane; n < K; n += WAVE) {
+      const int na = c_mi.a[n], nb = c_mi.b[n], nc = c_mi.c[n];
+      const int rem = order - (na + nb + nc);
+      double acc = 0.0;
+      for (int i = 0; i <= rem; i++)
+        for (int j = 0; i + j <= rem; j++) {
+          const double exy = tab[w][0][i] * tab[w][1][j];
+          for (int k = 0; i + j + k <= rem; k++)
+            acc += lp[w][mi_index(na + i, nb + j, nc + k)] * exy * tab[w][2][k];
+        }
+      local[a * K + n] = (T)((double)local[a * K + n] + acc);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
-  local[a * K + n] = (T)((double)local[a * K + n] + acc);
 }
 
 hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
@@ -177,15 +248,14 @@ hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
   hipError_t e = ensure_table();
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
-  int64_t nt = lvl_count * K;
-  if (nt == 0) return hipSuccess;
-  unsigned g = (unsigned)((nt + 255) / 256);
+  if (lvl_count == 0) return hipSuccess;
+  int64_t blocks = std::min<int64_t>((lvl_count + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
-    k_l2l<double><<<g, 256, 0, st>>>(order, K, lvl_begin, lvl_count, parent, centre,
-                                     (double*)local);
+    k_l2l<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, lvl_begin, lvl_count, parent,
+                                                            centre, (double*)local);
   else
-    k_l2l<float><<<g, 256, 0, st>>>(order, K, lvl_begin, lvl_count, parent, centre,
-                                    (float*)local);
+    k_l2l<float><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, lvl_begin, lvl_count, parent,
+                                                           centre, (float*)local);
   return hipGetLastError();
 }
 

@@ -35,8 +35,13 @@ struct Control {
   int64_t leaves_at_level[MAX_LEVELS];
   int64_t n_m2l;
   int64_t n_p2p;
-  int32_t nA[MAX_LEVELS + 1];  // walk: type-A (pending leaf) items per step
+  int64_t own_m2l_total, own_p2p_total;  // walk: entries found at the target's own level
+  int64_t n_p2p_tasks, n_p2p_part;        // near-field tasks and partial-sum slots
+  int32_t pool_overflow;                  // a sharded pool ran out of room
+  int32_t max_leaf_count;
+  int64_t pool_used[3][512];              // carry, transposed M2L, transposed P2P shards
 };
+constexpr int POOL_SHARDS = 512;
 
 // Grow-only device buffer.
 struct DBuf {
@@ -65,8 +70,13 @@ struct fmm_plan_s {
   mbg::DBuf leaves, lvl_blkcnt;
   mbg::DBuf mpole, local;
   // walk
-  mbg::DBuf items, carry, tot_m2l, tot_p2p, cur_m2l, cur_p2p;
+  mbg::DBuf carry, trm_pool, trp_pool, carry_off, carry_cnt, own_m2l, own_p2p;
+  mbg::DBuf tr_cnt_m2l, tr_cnt_p2p, tr_start_m2l, tr_start_p2p;
+  mbg::DBuf tr_keys, tr_keys_alt, tr_vals, tr_vals_alt;
   mbg::DBuf m2l_off, m2l_src, p2p_off, p2p_src;
+  // near-field tasks (target leaf x bounded slice of its list)
+  mbg::DBuf p2p_task, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
+  int64_t n_p2p_tasks = 0, n_p2p_part = 0;
 
   // host copies of the last build's sizes
   int64_t n_nodes = 0, n_leaves = 0, n_m2l = 0, n_p2p = 0;
@@ -76,10 +86,7 @@ struct fmm_plan_s {
   int walk_retries = 0;
   mbg::RootInfo root_host{};
 
-  // walk item bookkeeping (host-computed capacities)
-  int64_t item_base[mbg::MAX_LEVELS + 2] = {0};
-  int64_t item_amax[mbg::MAX_LEVELS + 2] = {0};
-  int64_t carry_cap = 0;
+  int64_t shard_cap[3] = {0, 0, 0};  // carry, transposed M2L, transposed P2P
 
   mbg::Control* ctrl_host = nullptr;  // pinned
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
@@ -128,12 +135,12 @@ hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const i
                               hipStream_t st);
 
 // ---- walk ----
-struct WalkItems {  // SoA over the global item index space
-  int32_t* tgt;
-  int64_t* gen_off;
-  int32_t* gen_cnt;
-  int64_t* carry_off;
-  int32_t* carry_cnt;
+// Sharded bump allocator: shard sh owns [sh * shard_cap, (sh+1) * shard_cap).
+template <typename T>
+struct Pool {
+  T* data;
+  int64_t shard_cap;
+  int64_t* used;  // [POOL_SHARDS]
 };
 struct WalkArgs {
   const uint8_t* level;
@@ -143,23 +150,43 @@ struct WalkArgs {
   const int32_t* parent;
   double t2;
   int step;
-  int64_t lvl_begin, lvl_count;      // nodes at level `step`
-  int64_t prev_lvl_begin;            // nodes at level step-1
-  int64_t base, amax;                // this step's item range
-  int64_t prev_base, prev_amax;      // previous step's item range
-  int64_t next_base;                 // next step's item base (type-A writes)
-  int64_t next_amax;
-  WalkItems it;
-  int32_t* carry;
-  int64_t carry_cap;
-  int64_t *tot_m2l, *tot_p2p;
-  int64_t *cur_m2l, *cur_p2p;
+  int64_t lvl_begin, lvl_count;  // nodes at level `step`
+  Pool<int32_t> carry;           // rejected partners of non-leaf nodes
+  Pool<uint64_t> trm, trp;       // transposed entries: (target << key_shift) | source
+  int64_t* carry_off;            // per node: its carry slice
+  int32_t* carry_cnt;
+  int32_t *own_m2l, *own_p2p;    // per node: entries found at its own level
   const int64_t *m2l_off, *p2p_off;
   int32_t *m2l_src, *p2p_src;
+  int key_shift;
   Control* ctrl;
 };
 hipError_t launch_walk_pass1(const WalkArgs& a, hipStream_t st);
 hipError_t launch_walk_pass2(const WalkArgs& a, hipStream_t st);
+hipError_t launch_walk_root(int pass, int root_leaf, const WalkArgs& a, hipStream_t st);
+hipError_t launch_walk_reset(Control* ctrl, hipStream_t st);
+hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
+                                  Control* ctrl, hipStream_t st);
+// dense copy of the transposed pools: M2L keys first (kind bit clear), then P2P (kind bit set)
+hipError_t launch_tr_compact(const WalkArgs& a, int kind_bit, uint64_t* dst, hipStream_t st);
+hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
+                          int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st);
+hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
+                               const int32_t* cnt_m2l, const int32_t* cnt_p2p, int64_t* tot_m2l,
+                               int64_t* tot_p2p, hipStream_t st);
+hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
+                             int64_t n_nodes, const int64_t* m2l_off, const int32_t* own_m2l,
+                             const int64_t* start_m2l, int32_t* m2l_src, const int64_t* p2p_off,
+                             const int32_t* own_p2p, const int64_t* start_p2p, int32_t* p2p_src,
+                             hipStream_t st);
+hipError_t launch_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
+                                   const int64_t* task_total, const int64_t* part_total,
+                                   Control* ctrl, hipStream_t st);
+// LSD radix sort over the low `bits` bits; returns in *in_alt whether the
+// result ended in (keys_alt, idx_alt).
+hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
+                                  int32_t* idx_alt, int64_t n, int bits, int32_t* hist,
+                                  int32_t* scan_tmp, bool* in_alt, hipStream_t st);
 
 // ---- numeric passes ----
 hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leaves,
@@ -175,10 +202,19 @@ hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
                       const int32_t* parent, const double* centre, void* local, hipStream_t st);
 hipError_t launch_l2p(int dtype, int order, int64_t n, const void* pts, const int32_t* leaf_of,
                       const double* centre, const void* local, void* far, hipStream_t st);
-hipError_t launch_p2p(int dtype, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
-                      const int32_t* count, const int64_t* off, const int32_t* src,
-                      const void* pts, const void* far, const int32_t* perm, void* phi,
-                      void* acc, hipStream_t st);
+size_t p2p_task_bytes();
+hipError_t launch_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                                 const int32_t* count, int64_t* ntask, int64_t* npart,
+                                 hipStream_t st);
+hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
+                                const int64_t* task_off, const int64_t* part_off,
+                                const int64_t* off, const int32_t* count, void* tasks,
+                                hipStream_t st);
+hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
+                      int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
+                      const int32_t* begin, const int32_t* count, const int32_t* src,
+                      const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
+                      void* part, bool any_multi, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // expansions in the plan's dtype/convention -> fp64 raw moments / derivatives
 hipError_t launch_export_expansions(int dtype, int order, int64_t n_nodes, const void* mpole,

@@ -7,10 +7,15 @@
 // directly).  The far field computed by L2P is added here and the result is
 // written in the caller's particle order.
 //
-// Work split: one wave per target leaf.  A leaf of tc <= 64 targets is spread
-// over the 64 lanes as tc targets x floor(64/tc) source slices; each lane walks
-// its slice of every source leaf in order, and the slices of one target are
-// summed in a fixed order through LDS.
+// Work split.  A task is one target leaf and a slice of at most TASK_E source
+// leaves of its list (a sparse leaf next to dense clusters can have ~10^5
+// source leaves; slicing keeps every wave's work bounded).  One wave per task:
+// the source particles of up to 64 list entries are enumerated in list order
+// and staged 64 at a time through LDS; the tc <= 64 targets of the leaf occupy
+// the lanes as tc targets x floor(64/tc) source slices, and the slices of one
+// target are summed in a fixed order.  A leaf with one task writes its final
+// result directly; a leaf with several tasks writes per-task partial sums that
+// a second kernel adds in task order.  Every sum has a fixed order.
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -18,70 +23,193 @@ namespace mbg {
 
 constexpr int P2P_THREADS = 256;
 constexpr int P2P_WAVES = P2P_THREADS / WAVE;
+constexpr int TASK_E = 64;  // source leaves per task
+
+struct P2PTask {
+  int64_t e0, e1;  // slice of the target leaf's list
+  int64_t part;    // first partial slot, or -1 when the task is the leaf's only one
+  int32_t leaf;    // target leaf node
+  int32_t pad;
+};
 
 __device__ __forceinline__ double p2p_rsqrt(double x) {
+  // hardware estimate + one cubically convergent correction (see the M2L file)
   double y = __builtin_amdgcn_rsq(x);
   double e = fma(-x * y, y, 1.0);
   return fma(y * e, fma(e, 0.375, 0.5), y);
 }
 __device__ __forceinline__ float p2p_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// ---- task construction (build time) ----
+__global__ void k_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                                 const int32_t* count, int64_t* ntask, int64_t* npart) {
+  int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (li >= n_leaves) return;
+  const int32_t a = leaves[li];
+  const int64_t len = off[a + 1] - off[a];
+  const int64_t nt = len <= TASK_E ? 1 : (len + TASK_E - 1) / TASK_E;
+  ntask[li] = nt;
+  npart[li] = nt > 1 ? nt * (int64_t)count[a] : 0;
+}
+
+// One thread per task: find its leaf by binary search over the task offsets.
+__global__ void k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
+                                const int64_t* task_off, const int64_t* part_off,
+                                const int64_t* off, const int32_t* count, P2PTask* tasks) {
+  int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (k >= n_tasks) return;
+  int64_t lo = 0, hi = n_leaves;  // last li with task_off[li] <= k
+  while (hi - lo > 1) {
+    int64_t mid = (lo + hi) >> 1;
+    if (task_off[mid] <= k)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int64_t li = lo;
+  const int32_t a = leaves[li];
+  const int64_t nt = task_off[li + 1] - task_off[li];
+  const int64_t kk = k - task_off[li];
+  P2PTask t;
+  t.e0 = off[a] + kk * TASK_E;
+  t.e1 = min(off[a + 1], t.e0 + TASK_E);
+  t.part = nt > 1 ? part_off[li] + kk * (int64_t)count[a] : -1;
+  t.leaf = a;
+  t.pad = 0;
+  tasks[k] = t;
+}
+
+// ---- near-field sums ----
 template <typename T>
 __global__ void __launch_bounds__(P2P_THREADS)
-    k_p2p(const int32_t* __restrict__ leaves, int64_t n_leaves, const int32_t* __restrict__ begin,
-          const int32_t* __restrict__ count, const int64_t* __restrict__ off,
-          const int32_t* __restrict__ src, const P4<T>* __restrict__ pts,
-          const P4<T>* __restrict__ far, const int32_t* __restrict__ perm, T* __restrict__ phi,
-          T* __restrict__ acc) {
-  __shared__ T part[P2P_WAVES][4][WAVE];
+    k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
+          const int32_t* __restrict__ count, const int32_t* __restrict__ src,
+          const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
+          const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
+          T* __restrict__ part) {
+  __shared__ P4<T> tile[P2P_WAVES][WAVE];
+  __shared__ int32_t tidx[P2P_WAVES][WAVE];
+  __shared__ T red[P2P_WAVES][4][WAVE];
   const int lane = __lane_id();
   const int w = threadIdx.x / WAVE;
-  for (int64_t li = (int64_t)blockIdx.x * P2P_WAVES + w; li < n_leaves;
-       li += (int64_t)gridDim.x * P2P_WAVES) {
-    const int32_t a = leaves[li];
+  for (int64_t ti = (int64_t)blockIdx.x * P2P_WAVES + w; ti < n_tasks;
+       ti += (int64_t)gridDim.x * P2P_WAVES) {
+    const P2PTask task = tasks[ti];
+    const int32_t a = task.leaf;
     const int32_t tb = begin[a], tn = count[a];
-    const int64_t e0 = off[a], e1 = off[a + 1];
     for (int32_t t0 = 0; t0 < tn; t0 += WAVE) {
       const int tc = min(WAVE, tn - t0);
       const int nsl = WAVE / tc;
       const int t = lane % tc, sl = lane / tc;
-      const bool active = sl < nsl;
       const int32_t i = tb + t0 + t;
       const P4<T> pi = pts[i];
       T fp = 0, fx = 0, fy = 0, fz = 0;
-      if (active) {
-        for (int64_t e = e0; e < e1; e++) {
-          const int32_t b = src[e];
-          const int32_t j1 = begin[b] + count[b];
-          for (int32_t j = begin[b] + sl; j < j1; j += nsl) {
-            const P4<T> pj = pts[j];
-            const T dx = pi.x - pj.x, dy = pi.y - pj.y, dz = pi.z - pj.z;
-            const T r2 = dx * dx + dy * dy + dz * dz;
-            T rinv = p2p_rsqrt(r2);
-            rinv = (j == i) ? (T)0 : rinv;  // self term omitted
-            const T mr = pj.m * rinv;
-            const T mr3 = mr * rinv * rinv;
-            fp -= mr;
-            fx -= mr3 * dx;
-            fy -= mr3 * dy;
-            fz -= mr3 * dz;
+      for (int64_t eg = task.e0; eg < task.e1; eg += WAVE) {
+        int32_t sb = 0, sc = 0;
+        if (eg + lane < task.e1) {
+          const int32_t b = src[eg + lane];
+          sb = begin[b];
+          sc = count[b];
+        }
+        const int incl = wave_incl_scan(sc);
+        const int excl = incl - sc;
+        const int tot = __shfl(incl, WAVE - 1, WAVE);
+        for (int q0 = 0; q0 < tot; q0 += WAVE) {
+          const int q = q0 + lane;
+          int h = 0;
+#pragma unroll
+          for (int step = 32; step >= 1; step >>= 1) {
+            const int v = __shfl(incl, h + step - 1, WAVE);
+            if (v <= q) h += step;
           }
+          h = min(h, WAVE - 1);
+          const int32_t jj = __shfl(sb, h, WAVE) + (q - __shfl(excl, h, WAVE));
+          if (q < tot) {
+            tile[w][lane] = pts[jj];
+            tidx[w][lane] = jj;
+          }
+          __builtin_amdgcn_wave_barrier();
+          const int nv = min(WAVE, tot - q0);
+          if (sl < nsl) {
+            for (int s = sl; s < nv; s += nsl) {
+              const P4<T> pj = tile[w][s];
+              const T dx = pi.x - pj.x, dy = pi.y - pj.y, dz = pi.z - pj.z;
+              const T r2 = dx * dx + dy * dy + dz * dz;
+              T rinv = p2p_rsqrt(r2);
+              rinv = (tidx[w][s] == i) ? (T)0 : rinv;  // self term omitted
+              const T mr = pj.m * rinv;
+              const T mr3 = mr * rinv * rinv;
+              fp -= mr;
+              fx -= mr3 * dx;
+              fy -= mr3 * dy;
+              fz -= mr3 * dz;
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
         }
       }
-      part[w][0][lane] = fp;
-      part[w][1][lane] = fx;
-      part[w][2][lane] = fy;
-      part[w][3][lane] = fz;
+      red[w][0][lane] = fp;
+      red[w][1][lane] = fx;
+      red[w][2][lane] = fy;
+      red[w][3][lane] = fz;
       __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0);
       if (lane < tc) {
         T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
         for (int s = 0; s < nsl; s++) {
-          s0 += part[w][0][s * tc + lane];
-          s1 += part[w][1][s * tc + lane];
-          s2 += part[w][2][s * tc + lane];
-          s3 += part[w][3][s * tc + lane];
+          s0 += red[w][0][s * tc + lane];
+          s1 += red[w][1][s * tc + lane];
+          s2 += red[w][2][s * tc + lane];
+          s3 += red[w][3][s * tc + lane];
         }
+        if (task.part < 0) {
+          const P4<T> f = far[i];
+          const int64_t o = perm[i];
+          phi[o] = f.x + s0;
+          acc[3 * o] = f.y + s1;
+          acc[3 * o + 1] = f.z + s2;
+          acc[3 * o + 2] = f.m + s3;
+        } else {
+          T* pp = part + 4 * (task.part + t0 + lane);
+          pp[0] = s0;
+          pp[1] = s1;
+          pp[2] = s2;
+          pp[3] = s3;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+// Leaves split over several tasks: lane l adds the partials of tasks l, l+64,
+// ... in order, then a fixed butterfly adds the lanes.
+template <typename T>
+__global__ void k_p2p_combine(const int32_t* leaves, int64_t n_leaves, const int64_t* task_off,
+                              const int64_t* part_off, const int32_t* begin, const int32_t* count,
+                              const T* part, const P4<T>* far, const int32_t* perm, T* phi,
+                              T* acc) {
+  const int lane = __lane_id();
+  for (int64_t li = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE; li < n_leaves;
+       li += (int64_t)gridDim.x * (blockDim.x / WAVE)) {
+    const int64_t nt = task_off[li + 1] - task_off[li];
+    if (nt <= 1) continue;
+    const int32_t a = leaves[li];
+    const int32_t tn = count[a], tb = begin[a];
+    for (int32_t t = 0; t < tn; t++) {
+      T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+      for (int64_t k = lane; k < nt; k += WAVE) {
+        const T* pp = part + 4 * (part_off[li] + k * tn + t);
+        s0 += pp[0];
+        s1 += pp[1];
+        s2 += pp[2];
+        s3 += pp[3];
+      }
+      s0 = wave_sum(s0);
+      s1 = wave_sum(s1);
+      s2 = wave_sum(s2);
+      s3 = wave_sum(s3);
+      if (lane == 0) {
+        const int32_t i = tb + t;
         const P4<T> f = far[i];
         const int64_t o = perm[i];
         phi[o] = f.x + s0;
@@ -89,26 +217,58 @@ __global__ void __launch_bounds__(P2P_THREADS)
         acc[3 * o + 1] = f.z + s2;
         acc[3 * o + 2] = f.m + s3;
       }
-      __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
-hipError_t launch_p2p(int dtype, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
-                      const int32_t* count, const int64_t* off, const int32_t* src,
-                      const void* pts, const void* far, const int32_t* perm, void* phi,
-                      void* acc, hipStream_t st) {
+size_t p2p_task_bytes() { return sizeof(P2PTask); }
+
+hipError_t launch_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                                 const int32_t* count, int64_t* ntask, int64_t* npart,
+                                 hipStream_t st) {
   if (n_leaves == 0) return hipSuccess;
-  int64_t blocks = (n_leaves + P2P_WAVES - 1) / P2P_WAVES;
+  k_p2p_task_count<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, off,
+                                                                        count, ntask, npart);
+  return hipGetLastError();
+}
+
+hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
+                                const int64_t* task_off, const int64_t* part_off,
+                                const int64_t* off, const int32_t* count, void* tasks,
+                                hipStream_t st) {
+  if (n_tasks == 0) return hipSuccess;
+  k_p2p_task_fill<<<(unsigned)((n_tasks + 255) / 256), 256, 0, st>>>(
+      leaves, n_leaves, n_tasks, task_off, part_off, off, count, (P2PTask*)tasks);
+  return hipGetLastError();
+}
+
+hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
+                      int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
+                      const int32_t* begin, const int32_t* count, const int32_t* src,
+                      const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
+                      void* part, bool any_multi, hipStream_t st) {
+  if (n_tasks == 0) return hipSuccess;
+  int64_t blocks = (n_tasks + P2P_WAVES - 1) / P2P_WAVES;
   if (blocks > 65535) blocks = 65535;
-  if (dtype == FMM_F64)
+  int64_t cblocks = (n_leaves + P2P_WAVES - 1) / P2P_WAVES;
+  if (cblocks > 65535) cblocks = 65535;
+  if (dtype == FMM_F64) {
     k_p2p<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
-        leaves, n_leaves, begin, count, off, src, (const P4<double>*)pts, (const P4<double>*)far,
-        perm, (double*)phi, (double*)acc);
-  else
+        (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<double>*)pts,
+        (const P4<double>*)far, perm, (double*)phi, (double*)acc, (double*)part);
+    if (any_multi)
+      k_p2p_combine<double><<<(unsigned)cblocks, P2P_THREADS, 0, st>>>(
+          leaves, n_leaves, task_off, part_off, begin, count, (const double*)part,
+          (const P4<double>*)far, perm, (double*)phi, (double*)acc);
+  } else {
     k_p2p<float><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
-        leaves, n_leaves, begin, count, off, src, (const P4<float>*)pts, (const P4<float>*)far,
-        perm, (float*)phi, (float*)acc);
+        (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<float>*)pts,
+        (const P4<float>*)far, perm, (float*)phi, (float*)acc, (float*)part);
+    if (any_multi)
+      k_p2p_combine<float><<<(unsigned)cblocks, P2P_THREADS, 0, st>>>(
+          leaves, n_leaves, task_off, part_off, begin, count, (const float*)part,
+          (const P4<float>*)far, perm, (float*)phi, (float*)acc);
+  }
   return hipGetLastError();
 }
 

@@ -8,22 +8,29 @@
 // equal) -- is evaluated here target by target, one tree level per step:
 //
 //   * at step s every node t of level s receives as candidates the "carry" of
-//     its parent (the parent's rejected partners), each carried leaf kept as
-//     it is and each carried non-leaf replaced by its children;
-//   * a leaf t additionally keeps receiving, at steps s+1, s+2, ..., the
-//     children of the non-leaf partners it rejected at the previous step
-//     (the pair walk splits only the non-leaf side there);
-//   * each candidate c is accepted (M2L t<-c) or rejected; a rejected c goes
-//     to t's carry if t is a non-leaf, to t's P2P list if both are leaves,
-//     and to t's pending carry otherwise.
+//     its parent (the parent's rejected partners): each carried leaf is kept
+//     as it is, each carried non-leaf is replaced by its children;
+//   * each candidate c is accepted (M2L t <- c) or rejected; a rejected c goes
+//     to t's carry if t is a non-leaf, and to t's P2P list if t and c are both
+//     leaves.
 //
-// Candidates are enumerated in ascending node order, so each step appends a
-// sorted run of sources, and runs of later steps hold deeper (larger) ids:
-// every target's lists come out sorted by source without a sort.  Pass 1
-// counts list lengths and materializes the carries; after a scan of the
-// per-target totals, pass 2 re-classifies and writes the lists in place.
-// Carry slices are allocated with an integer atomic counter: their placement
-// varies between runs, their contents and the final lists do not.
+// The pair walk also refines the partners of a leaf t past t's own level
+// (only the non-leaf side can split).  Those pairs are exactly the pairs in
+// which a deeper target sees t as a carried leaf, and the acceptance test is
+// symmetric, so they are emitted from that side: when a target of level s
+// accepts a carried leaf c of a coarser level, the entry (c <- target) is
+// added to c's list as well, and likewise for leaf-leaf rejections.  Such
+// transposed entries are appended in any order and put in place by a radix
+// sort of (target, source) keys; a target's own entries (sources at its level
+// or coarser) come first, its transposed ones (deeper sources) after, so every
+// list ends sorted by source, as the pair walk's canonical order requires.
+//
+// Pass 1 counts each target's own entries and writes its carry and its
+// transposed entries; the transposed entries are then sorted, counted per
+// target, and after a scan of the per-target totals pass 2 re-classifies and
+// writes the own entries in place.  Carry slices and transposed entries are
+// placed by sharded bump allocators (integer atomics spread over 512 counters
+// by target): their placement varies between runs, the final lists do not.
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -67,11 +74,10 @@ __device__ __forceinline__ int classify(const WalkArgs& a, const Target& T, int3
 }
 
 // Visit the candidates of a generator slice in ascending node order, 64 at a
-// time: first the carried leaves (levels < s, kept as they are), then the
-// children of the carried non-leaves (level s).  Each phase follows the sorted
-// generator order, and every id of the first phase is smaller than every id
-// of the second.  f(active, cand) is called by the whole wave (it may use
-// ballots).
+// time: first the carried leaves (levels < s, kept as they are: phase 0), then
+// the children of the carried non-leaves (level s: phase 1).  Each phase
+// follows the sorted generator order, and every id of phase 0 is smaller than
+// every id of phase 1.  f(active, cand, phase) is called by the whole wave.
 template <typename F>
 __device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int64_t g0, int gc, F&& f) {
   const int lane = __lane_id();
@@ -80,7 +86,7 @@ __device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int64_t g0
       const int j = c0 + lane;
       int nc = 0, fc = 0;
       if (j < gc) {
-        const int32_t g = a.carry[g0 + j];
+        const int32_t g = a.carry.data[g0 + j];
         const int k = a.n_child[g];
         if (phase == 0 && k == 0) {
           nc = 1;
@@ -107,109 +113,112 @@ __device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int64_t g0
         h = min(h, WAVE - 1);
         const int fch = __shfl(fc, h, WAVE);
         const int exh = __shfl(excl, h, WAVE);
-        f(active, (int32_t)(fch + (qi - exh)));
+        f(active, (int32_t)(fch + (qi - exh)), phase);
       }
     }
   }
 }
 
-// Item record of step s, index i in [0, amax) (type A) or [amax, amax+lvl_count)
-// (type B: the level-s node lvl_begin + i - amax).
-__device__ __forceinline__ void item_source(const WalkArgs& a, int64_t i, int32_t& t, int64_t& g0,
-                                            int& gc, bool pass1) {
-  const int64_t gi = a.base + i;
-  if (i < a.amax) {
-    t = a.it.tgt[gi];
-    g0 = a.it.gen_off[gi];
-    gc = a.it.gen_cnt[gi];
-    return;
+__device__ __forceinline__ int shard_of(int32_t t) {
+  return (int)(((uint32_t)t * 2654435761u) >> 23) & (POOL_SHARDS - 1);
+}
+
+// Wave-wide allocation of n entries from shard sh (lane 0 bumps the counter).
+// Returns the global offset, or -1 when the shard is full (overflow flagged).
+template <typename T>
+__device__ __forceinline__ int64_t pool_alloc(const Pool<T>& p, int sh, int n, Control* ctrl) {
+  int64_t off = 0;
+  if (__lane_id() == 0)
+    off = (int64_t)atomicAdd((unsigned long long*)&p.used[sh], (unsigned long long)n);
+  off = __shfl(off, 0, WAVE);
+  if (off + n > p.shard_cap) {
+    if (__lane_id() == 0) atomicOr(&ctrl->pool_overflow, 1);
+    return -1;
   }
-  t = (int32_t)(a.lvl_begin + (i - a.amax));
-  if (pass1) {
-    const int64_t pitem = a.prev_base + a.prev_amax + (a.parent[t] - a.prev_lvl_begin);
-    g0 = a.it.carry_off[pitem];
-    gc = a.it.carry_cnt[pitem];
-    a.it.tgt[gi] = t;
-    a.it.gen_off[gi] = g0;
-    a.it.gen_cnt[gi] = gc;
-  } else {
-    g0 = a.it.gen_off[gi];
-    gc = a.it.gen_cnt[gi];
-  }
+  return (int64_t)sh * p.shard_cap + off;
 }
 
 __global__ void __launch_bounds__(WK_THREADS) k_walk_pass1(WalkArgs a) {
-  if (a.ctrl->carry_overflow) return;
+  // after an overflow the parents' carries may be missing: do nothing, the
+  // host regrows the pools and repeats pass 1
+  if (a.ctrl->pool_overflow) return;
   const int lane = __lane_id();
   const uint64_t lt = lanemask_lt();
-  const int64_t nA = a.ctrl->nA[a.step];
-  const int64_t n_items = nA + a.lvl_count;
-  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < n_items;
+  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.lvl_count;
        j += (int64_t)gridDim.x * WK_WAVES) {
-    const int64_t i = (j < nA) ? j : a.amax + (j - nA);
-    int32_t t;
-    int64_t g0;
-    int gc;
-    item_source(a, i, t, g0, gc, true);
+    const int32_t t = (int32_t)(a.lvl_begin + j);
+    const int32_t par = a.parent[t];
+    const int64_t g0 = a.carry_off[par];
+    const int gc = a.carry_cnt[par];
     Target T{t, a.level[t], a.q[t], a.n_child[t] == 0};
-    int n_m2l = 0, n_p2p = 0, n_carry = 0;
-    for_each_candidate(a, g0, gc, [&](bool act, int32_t c) {
+    int n_m2l = 0, n_p2p = 0, n_carry = 0, n_trm = 0, n_trp = 0;
+    for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int phase) {
       const int ty = act ? classify(a, T, c) : CAND_NONE;
-      n_m2l += __popcll(__ballot(ty == CAND_M2L));
-      n_p2p += __popcll(__ballot(ty == CAND_P2P));
-      n_carry += __popcll(__ballot(ty == CAND_CARRY));
-    });
-    int64_t off = 0;
-    if (n_carry > 0) {
-      if (lane == 0) off = (int64_t)atomicAdd((unsigned long long*)&a.ctrl->carry_used,
-                                              (unsigned long long)n_carry);
-      off = __shfl(off, 0, WAVE);
-      if (off + n_carry > a.carry_cap) {
-        if (lane == 0) atomicOr(&a.ctrl->carry_overflow, 1);
-        return;  // results are discarded; the host regrows the pool and retries
+      const bool m = ty == CAND_M2L, p = ty == CAND_P2P, k = ty == CAND_CARRY && !T.leaf;
+      const int cm = __popcll(__ballot(m)), cp = __popcll(__ballot(p));
+      n_m2l += cm;
+      n_p2p += cp;
+      n_carry += __popcll(__ballot(k));
+      if (phase == 0) {  // carried leaves of coarser levels: transposed entries
+        n_trm += cm;
+        n_trp += cp;
       }
-      int64_t cur = off;
-      for_each_candidate(a, g0, gc, [&](bool act, int32_t c) {
+    });
+    const int sh = shard_of(t);
+    int64_t off = 0;
+    bool ok = true;
+    if (n_carry > 0) {
+      off = pool_alloc(a.carry, sh, n_carry, a.ctrl);
+      ok = off >= 0;
+    }
+    int64_t om = 0, op = 0;
+    if (ok && n_trm > 0) {
+      om = pool_alloc(a.trm, sh, n_trm, a.ctrl);
+      ok = om >= 0;
+    }
+    if (ok && n_trp > 0) {
+      op = pool_alloc(a.trp, sh, n_trp, a.ctrl);
+      ok = op >= 0;
+    }
+    if (!ok) continue;  // results are discarded; the host regrows the pools and retries
+    if (n_carry + n_trm + n_trp > 0) {
+      int64_t ck = off, cm = om, cp = op;
+      for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int phase) {
         const int ty = act ? classify(a, T, c) : CAND_NONE;
-        const uint64_t m = __ballot(ty == CAND_CARRY);
-        if (ty == CAND_CARRY) a.carry[cur + __popcll(m & lt)] = c;
-        cur += __popcll(m);
+        const uint64_t bk = __ballot(ty == CAND_CARRY && !T.leaf);
+        if (ty == CAND_CARRY && !T.leaf) a.carry.data[ck + __popcll(bk & lt)] = c;
+        ck += __popcll(bk);
+        if (phase == 0) {
+          const uint64_t key = ((uint64_t)(uint32_t)c << a.key_shift) | (uint32_t)t;
+          const uint64_t bm = __ballot(ty == CAND_M2L), bp = __ballot(ty == CAND_P2P);
+          if (ty == CAND_M2L) a.trm.data[cm + __popcll(bm & lt)] = key;
+          if (ty == CAND_P2P) a.trp.data[cp + __popcll(bp & lt)] = key;
+          cm += __popcll(bm);
+          cp += __popcll(bp);
+        }
       });
     }
     if (lane == 0) {
-      const int64_t gi = a.base + i;
-      a.it.carry_off[gi] = off;
-      a.it.carry_cnt[gi] = n_carry;
-      a.tot_m2l[t] += n_m2l;
-      a.tot_p2p[t] += n_p2p;
-      if (T.leaf && n_carry > 0) {  // the leaf keeps refining its partners next step
-        const int slot = atomicAdd(&a.ctrl->nA[a.step + 1], 1);
-        const int64_t ni = a.next_base + slot;
-        a.it.tgt[ni] = t;
-        a.it.gen_off[ni] = off;
-        a.it.gen_cnt[ni] = n_carry;
-      }
+      a.carry_off[t] = off;
+      a.carry_cnt[t] = n_carry;
+      a.own_m2l[t] = n_m2l;
+      a.own_p2p[t] = n_p2p;
     }
   }
 }
 
 __global__ void __launch_bounds__(WK_THREADS) k_walk_pass2(WalkArgs a) {
-  const int lane = __lane_id();
   const uint64_t lt = lanemask_lt();
-  const int64_t nA = a.ctrl->nA[a.step];
-  const int64_t n_items = nA + a.lvl_count;
-  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < n_items;
+  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.lvl_count;
        j += (int64_t)gridDim.x * WK_WAVES) {
-    const int64_t i = (j < nA) ? j : a.amax + (j - nA);
-    int32_t t;
-    int64_t g0;
-    int gc;
-    item_source(a, i, t, g0, gc, false);
+    const int32_t t = (int32_t)(a.lvl_begin + j);
+    const int32_t par = a.parent[t];
+    const int64_t g0 = a.carry_off[par];
+    const int gc = a.carry_cnt[par];
     Target T{t, a.level[t], a.q[t], a.n_child[t] == 0};
-    const int64_t m0 = a.m2l_off[t] + a.cur_m2l[t];
-    const int64_t p0 = a.p2p_off[t] + a.cur_p2p[t];
+    const int64_t m0 = a.m2l_off[t], p0 = a.p2p_off[t];
     int64_t cm = 0, cp = 0;
-    for_each_candidate(a, g0, gc, [&](bool act, int32_t c) {
+    for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int) {
       const int ty = act ? classify(a, T, c) : CAND_NONE;
       const uint64_t mm = __ballot(ty == CAND_M2L);
       const uint64_t mp = __ballot(ty == CAND_P2P);
@@ -218,10 +227,6 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk_pass2(WalkArgs a) {
       cm += __popcll(mm);
       cp += __popcll(mp);
     });
-    if (lane == 0) {
-      a.cur_m2l[t] += cm;
-      a.cur_p2p[t] += cp;
-    }
   }
 }
 
@@ -230,17 +235,19 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk_pass2(WalkArgs a) {
 __global__ void k_walk_root(int pass, int root_leaf, WalkArgs a) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   if (pass == 1) {
+    a.own_m2l[0] = 0;
+    a.carry_off[0] = 0;
     if (root_leaf) {
-      a.tot_p2p[0] = 1;
+      a.own_p2p[0] = 1;
+      a.carry_cnt[0] = 0;
     } else {
-      a.carry[0] = 0;
-      a.ctrl->carry_used = 1;
-      const int64_t gi = a.base;
-      a.it.tgt[gi] = 0;
-      a.it.gen_off[gi] = 0;
-      a.it.gen_cnt[gi] = 0;
-      a.it.carry_off[gi] = 0;
-      a.it.carry_cnt[gi] = 1;
+      a.own_p2p[0] = 0;
+      const int sh = shard_of(0);
+      const int64_t off = (int64_t)sh * a.carry.shard_cap + a.carry.used[sh];
+      a.carry.data[off] = 0;
+      a.carry.used[sh] += 1;
+      a.carry_off[0] = off;
+      a.carry_cnt[0] = 1;
     }
   } else if (root_leaf) {
     a.p2p_src[a.p2p_off[0]] = 0;
@@ -248,19 +255,117 @@ __global__ void k_walk_root(int pass, int root_leaf, WalkArgs a) {
 }
 
 __global__ void k_walk_reset(Control* c) {
-  const int i = threadIdx.x;
-  if (i <= MAX_LEVELS) c->nA[i] = 0;
-  if (i == 0) {
-    c->carry_overflow = 0;
-    c->carry_used = 0;
+  for (int i = threadIdx.x; i < 3 * POOL_SHARDS; i += blockDim.x) (&c->pool_used[0][0])[i] = 0;
+  if (threadIdx.x == 0) c->pool_overflow = 0;
+}
+
+// Sum of the own counts (list sizes are known before the transposed sort).
+__global__ void k_walk_own_totals(int64_t n, const int32_t* om, const int32_t* op, Control* c) {
+  __shared__ int64_t sm[WK_THREADS], sp[WK_THREADS];
+  int64_t a = 0, b = 0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    a += om[i];
+    b += op[i];
+  }
+  sm[threadIdx.x] = a;
+  sp[threadIdx.x] = b;
+  __syncthreads();
+  for (int s = WK_THREADS / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      sm[threadIdx.x] += sm[threadIdx.x + s];
+      sp[threadIdx.x] += sp[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    c->own_m2l_total = sm[0];
+    c->own_p2p_total = sp[0];
   }
 }
 
-__global__ void k_walk_totals(const int64_t* m2l_total, const int64_t* p2p_total, Control* c) {
+// One block per shard: copy the shard's used entries to the dense array
+// (transposed M2L pool first, then the P2P pool with the kind bit set).
+__global__ void k_tr_compact(Pool<uint64_t> trm, Pool<uint64_t> trp, int kind_bit, uint64_t* dst) {
+  const int sh = blockIdx.x % POOL_SHARDS;
+  const int kind = blockIdx.x / POOL_SHARDS;
+  const Pool<uint64_t>& p = kind ? trp : trm;
+  __shared__ int64_t base;
+  if (threadIdx.x == 0) {
+    int64_t b = 0;
+    if (kind)
+      for (int i = 0; i < POOL_SHARDS; i++) b += trm.used[i];
+    for (int i = 0; i < sh; i++) b += p.used[i];
+    base = b;
+  }
+  __syncthreads();
+  const int64_t n = p.used[sh];
+  const uint64_t kb = (uint64_t)kind << kind_bit;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x)
+    dst[base + i] = p.data[(int64_t)sh * p.shard_cap + i] | kb;
+}
+
+// Runs of equal (kind, target) in the sorted keys: first index and length.
+__global__ void k_tr_runs(const uint64_t* keys, int64_t n, int sh, int kind_bit, int64_t n_nodes,
+                          int64_t* start, int32_t* cnt) {
+  int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const uint64_t g = keys[k] >> sh;  // kind and target
+  const bool first = k == 0 || (keys[k - 1] >> sh) != g;
+  const bool last = k == n - 1 || (keys[k + 1] >> sh) != g;
+  const int kind = (int)(keys[k] >> kind_bit);
+  const int64_t c = (int64_t)(g & ((1ull << (kind_bit - sh)) - 1ull));
+  const int64_t slot = (int64_t)kind * n_nodes + c;
+  if (first) start[slot] = k;
+  if (last) {
+    int64_t s0 = k;
+    // the run start is written by another thread: recompute it by search
+    int64_t lo = 0, hi = k;
+    while (lo < hi) {
+      int64_t mid = (lo + hi) >> 1;
+      if ((keys[mid] >> sh) < g)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    s0 = lo;
+    cnt[slot] = (int32_t)(k - s0 + 1);
+  }
+}
+
+__global__ void k_walk_offsets(int64_t n, const int32_t* om, const int32_t* op, const int32_t* cm,
+                               const int32_t* cp, int64_t* totm, int64_t* totp) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  totm[i] = (int64_t)om[i] + cm[i];
+  totp[i] = (int64_t)op[i] + cp[i];
+}
+
+__global__ void k_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
+                                   const int64_t* task_total, const int64_t* part_total,
+                                   Control* c) {
   if (threadIdx.x == 0) {
     c->n_m2l = *m2l_total;
     c->n_p2p = *p2p_total;
+    c->n_p2p_tasks = *task_total;
+    c->n_p2p_part = *part_total;
   }
+}
+
+// Sorted transposed keys -> after each target's own entries.
+__global__ void k_tr_scatter(const uint64_t* keys, int64_t n, int sh, int kind_bit,
+                             int64_t n_nodes, const int64_t* m2l_off, const int32_t* own_m2l,
+                             const int64_t* start_m2l, int32_t* m2l_src, const int64_t* p2p_off,
+                             const int32_t* own_p2p, const int64_t* start_p2p, int32_t* p2p_src) {
+  int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const uint64_t key = keys[k];
+  const int kind = (int)(key >> kind_bit);
+  const int64_t c = (int64_t)((key >> sh) & ((1ull << (kind_bit - sh)) - 1ull));
+  const int32_t src = (int32_t)(key & ((1ull << sh) - 1ull));
+  if (kind == 0)
+    m2l_src[m2l_off[c] + own_m2l[c] + (k - start_m2l[c])] = src;
+  else
+    p2p_src[p2p_off[c] + own_p2p[c] + (k - start_p2p[c])] = src;
 }
 
 hipError_t launch_walk_root(int pass, int root_leaf, const WalkArgs& a, hipStream_t st) {
@@ -268,19 +373,54 @@ hipError_t launch_walk_root(int pass, int root_leaf, const WalkArgs& a, hipStrea
   return hipGetLastError();
 }
 hipError_t launch_walk_reset(Control* ctrl, hipStream_t st) {
-  k_walk_reset<<<1, 64, 0, st>>>(ctrl);
+  k_walk_reset<<<1, 256, 0, st>>>(ctrl);
   return hipGetLastError();
 }
-hipError_t launch_walk_totals(const int64_t* m2l_total, const int64_t* p2p_total, Control* ctrl,
-                              hipStream_t st) {
-  k_walk_totals<<<1, 64, 0, st>>>(m2l_total, p2p_total, ctrl);
+hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
+                                  Control* ctrl, hipStream_t st) {
+  k_walk_own_totals<<<1, WK_THREADS, 0, st>>>(n_nodes, own_m2l, own_p2p, ctrl);
+  return hipGetLastError();
+}
+hipError_t launch_tr_compact(const WalkArgs& a, int kind_bit, uint64_t* dst, hipStream_t st) {
+  k_tr_compact<<<2 * POOL_SHARDS, 256, 0, st>>>(a.trm, a.trp, kind_bit, dst);
+  return hipGetLastError();
+}
+hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
+                          int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  k_tr_runs<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, key_shift, kind_bit, n_nodes,
+                                                         start, cnt);
+  return hipGetLastError();
+}
+hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
+                               const int32_t* cnt_m2l, const int32_t* cnt_p2p, int64_t* tot_m2l,
+                               int64_t* tot_p2p, hipStream_t st) {
+  k_walk_offsets<<<(unsigned)((n_nodes + 255) / 256), 256, 0, st>>>(n_nodes, own_m2l, own_p2p,
+                                                                    cnt_m2l, cnt_p2p, tot_m2l,
+                                                                    tot_p2p);
+  return hipGetLastError();
+}
+hipError_t launch_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
+                                   const int64_t* task_total, const int64_t* part_total,
+                                   Control* ctrl, hipStream_t st) {
+  k_walk_copy_totals<<<1, 64, 0, st>>>(m2l_total, p2p_total, task_total, part_total, ctrl);
+  return hipGetLastError();
+}
+hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
+                             int64_t n_nodes, const int64_t* m2l_off, const int32_t* own_m2l,
+                             const int64_t* start_m2l, int32_t* m2l_src, const int64_t* p2p_off,
+                             const int32_t* own_p2p, const int64_t* start_p2p, int32_t* p2p_src,
+                             hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  k_tr_scatter<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
+      keys, n, key_shift, kind_bit, n_nodes, m2l_off, own_m2l, start_m2l, m2l_src, p2p_off,
+      own_p2p, start_p2p, p2p_src);
   return hipGetLastError();
 }
 
 static unsigned walk_grid(const WalkArgs& a) {
-  int64_t ub = a.amax + a.lvl_count;
-  int64_t blocks = (ub + WK_WAVES - 1) / WK_WAVES;
-  if (blocks > 8192) blocks = 8192;
+  int64_t blocks = (a.lvl_count + WK_WAVES - 1) / WK_WAVES;
+  if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   return (unsigned)blocks;
 }
