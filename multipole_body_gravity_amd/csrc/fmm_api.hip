@@ -110,8 +110,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     p->shard_cap[k] = std::max<int64_t>(p->shard_cap[k], guess[k] / POOL_SHARDS + 64);
 
   WalkArgs a{};
-  a.level = P<uint8_t>(p->nlevel);
-  a.q = P<uint64_t>(p->nq);
+  a.geo = P<int4>(p->ngeo);
   a.first_child = P<int32_t>(p->nfirst);
   a.n_child = P<uint8_t>(p->nnchild);
   a.parent = P<int32_t>(p->nparent);
@@ -293,7 +292,7 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->lcp, &p->wlev, &p->wtmp, &p->leaf_level, &p->leaf_of, &p->radix_hist,
                   &p->scan_tmp, &p->root, &p->ctrl, &p->bbox_part, &p->nlevel, &p->nprefix,
                   &p->nbegin, &p->ncount, &p->nparent, &p->nfirst, &p->nnchild, &p->ncentre,
-                  &p->nq, &p->leaves, &p->lvl_blkcnt, &p->mpole, &p->local, &p->carry,
+                  &p->nq, &p->ngeo, &p->leaves, &p->lvl_blkcnt, &p->mpole, &p->local, &p->carry,
                   &p->trm_pool, &p->trp_pool, &p->carry_off, &p->carry_cnt, &p->own_m2l,
                   &p->own_p2p, &p->tr_cnt_m2l, &p->tr_cnt_p2p, &p->tr_start_m2l,
                   &p->tr_start_p2p, &p->tr_keys, &p->tr_keys_alt, &p->tr_vals,
@@ -366,13 +365,15 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   TRY(grow(p->nnchild, nn));
   TRY(grow(p->ncentre, 24 * nn));
   TRY(grow(p->nq, 8 * nn));
+  TRY(grow(p->ngeo, 16 * nn));
   TRY(grow(p->leaves, 4 * (3 * nn + 2)));
   TRY(grow(p->mpole, w * p->K * nn));
   TRY(grow(p->local, w * p->K * nn));
   TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
   TreeArrays t{P<uint8_t>(p->nlevel),  P<uint64_t>(p->nprefix), P<int32_t>(p->nbegin),
                P<int32_t>(p->ncount),  P<int32_t>(p->nparent),  P<int32_t>(p->nfirst),
-               P<uint8_t>(p->nnchild), P<double>(p->ncentre),   P<uint64_t>(p->nq)};
+               P<uint8_t>(p->nnchild), P<double>(p->ncentre),   P<uint64_t>(p->nq),
+               P<int4>(p->ngeo)};
   int32_t* leaves = P<int32_t>(p->leaves);
   TRY_HIP(launch_tree_phase2(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
                              P<int8_t>(p->leaf_level), P<int64_t>(p->lvl_blkcnt), nn, p->level_off,

@@ -613,6 +613,15 @@ __global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t n_n
   // integer cell coordinates and geometric centre
   uint32_t qx = compact3(P >> 2), qy = compact3(P >> 1), qz = compact3(P);
   t.q[id] = ((uint64_t)qx << 42) | ((uint64_t)qy << 21) | (uint64_t)qz;
+  {  // exact integer geometry in units of 1/2^22 of the root side
+    const int sh = KEY_BITS - l;
+    int4 g;
+    g.x = (int)((2u * qx + 1u) << sh);
+    g.y = (int)((2u * qy + 1u) << sh);
+    g.z = (int)((2u * qz + 1u) << sh);
+    g.w = (1 << sh) | (leaf ? (1 << 30) : 0);
+    t.geo[id] = g;
+  }
   const double w = ldexp(root->side, -l);
   const uint32_t q[3] = {qx, qy, qz};
 #pragma unroll

@@ -67,6 +67,164 @@ constexpr int EX_WAVES = EX_THREADS / WAVE;
 constexpr int PP = FMM_MAX_ORDER + 1;  // entries of a 1-d power table
 constexpr int MAXCH = 8;
 
+// ---------------- register-resident variants for orders <= 5 ----------------
+// P2M, one thread per leaf: the leaf's particles are read in order and every
+// scaled moment is accumulated in registers.
+template <typename T, int P>
+__global__ void __launch_bounds__(256)
+    k_p2m_reg(const P4<T>* pts, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
+              const int32_t* count, const double* centre, T* mpole) {
+  constexpr int K = Tabs<P>::K;
+  const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (li >= n_leaves) return;
+  const int32_t node = leaves[li];
+  const double cx = centre[3 * node], cy = centre[3 * node + 1], cz = centre[3 * node + 2];
+  double acc[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) acc[k] = 0.0;
+  const int32_t j0 = begin[node], j1 = j0 + count[node];
+  for (int32_t j = j0; j < j1; j++) {
+    const P4<T> p = pts[j];
+    const double sx = cx - (double)p.x, sy = cy - (double)p.y, sz = cz - (double)p.z;  // -s
+    double px[P + 1], py[P + 1], pz[P + 1];
+    px[0] = (double)p.m;  // the mass rides on the x table
+    py[0] = pz[0] = 1.0;
+#pragma unroll
+    for (int q = 1; q <= P; q++) {
+      px[q] = px[q - 1] * sx * (1.0 / q);
+      py[q] = py[q - 1] * sy * (1.0 / q);
+      pz[q] = pz[q - 1] * sz * (1.0 / q);
+    }
+    static_for<0, K>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      acc[k] += px[tabs<P>.a[k]] * py[tabs<P>.b[k]] * pz[tabs<P>.c[k]];
+    });
+  }
+  T* out = mpole + (int64_t)node * K;
+#pragma unroll
+  for (int k = 0; k < K; k++) out[k] = (T)acc[k];
+}
+
+// M2M, eight lanes per parent: lane c translates child c to the parent centre
+// (Mt_m += Mt_k(child) (-d)^(m-k)/(m-k)!, all in registers), then the eight
+// lanes are added by a fixed butterfly and lane c writes coefficients c, c+8, ...
+template <int P>
+struct M2MTab {
+  static constexpr int NT = binom_c(P + 6, 6);
+  int m[NT], k[NT], ea[NT], eb[NT], ec[NT];
+  int nt;
+  constexpr M2MTab() : m(), k(), ea(), eb(), ec(), nt(0) {
+    constexpr int K = (P + 1) * (P + 2) * (P + 3) / 6;
+    int t = 0;
+    for (int mi = 0; mi < K; mi++)
+      for (int ki = 0; ki < K; ki++) {
+        int ma = tabs<P>.a[mi], mb = tabs<P>.b[mi], mc = tabs<P>.c[mi];
+        int ka = tabs<P>.a[ki], kb = tabs<P>.b[ki], kc = tabs<P>.c[ki];
+        if (ka <= ma && kb <= mb && kc <= mc) {
+          m[t] = mi;
+          k[t] = ki;
+          ea[t] = ma - ka;
+          eb[t] = mb - kb;
+          ec[t] = mc - kc;
+          t++;
+        }
+      }
+    nt = t;
+  }
+};
+template <int P>
+inline constexpr M2MTab<P> m2m_tab{};
+
+template <typename T, int P>
+__global__ void __launch_bounds__(256)
+    k_m2m_reg(int64_t lvl_begin, int64_t lvl_count, const int32_t* first_child,
+              const uint8_t* n_child, const double* centre, T* mpole) {
+  constexpr int K = Tabs<P>::K;
+  constexpr int NTM = m2m_tab<P>.nt;
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t pi = g >> 3;
+  const int c = (int)(g & 7);
+  const bool valid_p = pi < lvl_count;
+  const int64_t Pn = lvl_begin + (valid_p ? pi : 0);
+  const int nc = valid_p ? n_child[Pn] : 0;
+  double acc[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) acc[k] = 0.0;
+  if (c < nc) {
+    const int64_t ch = first_child[Pn] + c;
+    const double nx = centre[3 * Pn] - centre[3 * ch], ny = centre[3 * Pn + 1] - centre[3 * ch + 1],
+                 nz = centre[3 * Pn + 2] - centre[3 * ch + 2];  // -d
+    double px[P + 1], py[P + 1], pz[P + 1];
+    px[0] = py[0] = pz[0] = 1.0;
+#pragma unroll
+    for (int q = 1; q <= P; q++) {
+      px[q] = px[q - 1] * nx * (1.0 / q);
+      py[q] = py[q - 1] * ny * (1.0 / q);
+      pz[q] = pz[q - 1] * nz * (1.0 / q);
+    }
+    const T* Mc = mpole + ch * K;
+    double M[K];
+#pragma unroll
+    for (int k = 0; k < K; k++) M[k] = (double)Mc[k];
+    static_for<0, NTM>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      acc[m2m_tab<P>.m[t]] += M[m2m_tab<P>.k[t]] * (px[m2m_tab<P>.ea[t]] * py[m2m_tab<P>.eb[t]] *
+                                                    pz[m2m_tab<P>.ec[t]]);
+    });
+  }
+#pragma unroll
+  for (int k = 0; k < K; k++) {
+    double v = acc[k];
+    v += __shfl_xor(v, 1, WAVE);
+    v += __shfl_xor(v, 2, WAVE);
+    v += __shfl_xor(v, 4, WAVE);
+    acc[k] = v;
+  }
+  if (valid_p && nc > 0) {
+    T* out = mpole + Pn * K;
+    static_for<0, K>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if ((k & 7) == c) out[k] = (T)acc[k];
+    });
+  }
+}
+
+template <typename T>
+static bool p2m_reg_dispatch(int order, const void* pts, const int32_t* leaves, int64_t n_leaves,
+                             const int32_t* begin, const int32_t* count, const double* centre,
+                             void* mpole, hipStream_t st) {
+  unsigned g = (unsigned)((n_leaves + 255) / 256);
+  switch (order) {
+#define P2MR(P)                                                                                  \
+  case P:                                                                                        \
+    k_p2m_reg<T, P><<<g, 256, 0, st>>>((const P4<T>*)pts, leaves, n_leaves, begin, count, centre, \
+                                       (T*)mpole);                                               \
+    return true;
+    P2MR(0) P2MR(1) P2MR(2) P2MR(3) P2MR(4) P2MR(5)
+#undef P2MR
+    default:
+      return false;
+  }
+}
+
+template <typename T>
+static bool m2m_reg_dispatch(int order, int64_t lvl_begin, int64_t lvl_count,
+                             const int32_t* first_child, const uint8_t* n_child,
+                             const double* centre, void* mpole, hipStream_t st) {
+  unsigned g = (unsigned)((lvl_count * 8 + 255) / 256);
+  switch (order) {
+#define M2MR(P)                                                                       \
+  case P:                                                                             \
+    k_m2m_reg<T, P><<<g, 256, 0, st>>>(lvl_begin, lvl_count, first_child, n_child, centre, \
+                                       (T*)mpole);                                    \
+    return true;
+    M2MR(0) M2MR(1) M2MR(2) M2MR(3) M2MR(4) M2MR(5)
+#undef M2MR
+    default:
+      return false;
+  }
+}
+
 // ---------------- P2M: one wave per leaf, lanes over coefficients ----------------
 // Particles are staged 64 at a time: lane j tabulates (-s_j)^a / a! per axis in
 // LDS, then lane m accumulates m_j * ex[a] ey[b] ez[c] over the staged particles
@@ -124,6 +282,11 @@ hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leav
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
   if (n_leaves == 0) return hipSuccess;
+  if (dtype == FMM_F64 ? p2m_reg_dispatch<double>(order, pts, leaves, n_leaves, begin, count,
+                                                  centre, mpole, st)
+                       : p2m_reg_dispatch<float>(order, pts, leaves, n_leaves, begin, count,
+                                                 centre, mpole, st))
+    return hipGetLastError();
   int64_t blocks = std::min<int64_t>((n_leaves + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
     k_p2m<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, (const P4<double>*)pts, leaves,
@@ -191,6 +354,11 @@ hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
   if (lvl_count == 0) return hipSuccess;
+  if (dtype == FMM_F64 ? m2m_reg_dispatch<double>(order, lvl_begin, lvl_count, first_child,
+                                                  n_child, centre, mpole, st)
+                       : m2m_reg_dispatch<float>(order, lvl_begin, lvl_count, first_child,
+                                                 n_child, centre, mpole, st))
+    return hipGetLastError();
   int64_t blocks = std::min<int64_t>((lvl_count + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
     k_m2m<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, lvl_begin, lvl_count,

@@ -66,7 +66,7 @@ struct fmm_plan_s {
   mbg::DBuf radix_hist, scan_tmp;
   mbg::DBuf root, ctrl, bbox_part;
   // node-sized
-  mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq;
+  mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq, ngeo;
   mbg::DBuf leaves, lvl_blkcnt;
   mbg::DBuf mpole, local;
   // walk
@@ -121,6 +121,7 @@ struct TreeArrays {
   uint8_t* n_child;
   double* centre;  // [n_nodes][3]
   uint64_t* q;     // packed integer cell coords qx<<42 | qy<<21 | qz
+  int4* geo;       // centre and half-width in units of 1/2^22 of the root side; leaf flag bit 30
 };
 
 hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t* lcp, int8_t* wlev,
@@ -143,8 +144,7 @@ struct Pool {
   int64_t* used;  // [POOL_SHARDS]
 };
 struct WalkArgs {
-  const uint8_t* level;
-  const uint64_t* q;
+  const int4* geo;
   const int32_t* first_child;
   const uint8_t* n_child;
   const int32_t* parent;

@@ -80,6 +80,22 @@ __global__ void k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t
 }
 
 // ---- near-field sums ----
+constexpr int TILE = 2 * WAVE;  // source particles staged per round
+
+template <typename T>
+__device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp, T& fx, T& fy,
+                                         T& fz) {
+  const T dx = pi.x - pj.x, dy = pi.y - pj.y, dz = pi.z - pj.z;
+  const T r2 = dx * dx + dy * dy + dz * dz;
+  const T rinv = p2p_rsqrt(r2);
+  const T mr = pj.m * rinv;
+  const T mr3 = mr * rinv * rinv;
+  fp -= mr;
+  fx -= mr3 * dx;
+  fy -= mr3 * dy;
+  fz -= mr3 * dz;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(P2P_THREADS)
     k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
@@ -87,8 +103,7 @@ __global__ void __launch_bounds__(P2P_THREADS)
           const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
           const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
           T* __restrict__ part) {
-  __shared__ P4<T> tile[P2P_WAVES][WAVE];
-  __shared__ int32_t tidx[P2P_WAVES][WAVE];
+  __shared__ P4<T> tile[P2P_WAVES][TILE];
   __shared__ T red[P2P_WAVES][4][WAVE];
   const int lane = __lane_id();
   const int w = threadIdx.x / WAVE;
@@ -104,48 +119,46 @@ __global__ void __launch_bounds__(P2P_THREADS)
       const int32_t i = tb + t0 + t;
       const P4<T> pi = pts[i];
       T fp = 0, fx = 0, fy = 0, fz = 0;
+      bool self = false;
       for (int64_t eg = task.e0; eg < task.e1; eg += WAVE) {
         int32_t sb = 0, sc = 0;
         if (eg + lane < task.e1) {
           const int32_t b = src[eg + lane];
-          sb = begin[b];
-          sc = count[b];
+          if (b == a) {
+            self = true;  // the target leaf itself: summed below with the self test
+          } else {
+            sb = begin[b];
+            sc = count[b];
+          }
         }
         const int incl = wave_incl_scan(sc);
         const int excl = incl - sc;
         const int tot = __shfl(incl, WAVE - 1, WAVE);
-        for (int q0 = 0; q0 < tot; q0 += WAVE) {
-          const int q = q0 + lane;
-          int h = 0;
+        for (int q0 = 0; q0 < tot; q0 += TILE) {
 #pragma unroll
-          for (int step = 32; step >= 1; step >>= 1) {
-            const int v = __shfl(incl, h + step - 1, WAVE);
-            if (v <= q) h += step;
-          }
-          h = min(h, WAVE - 1);
-          const int32_t jj = __shfl(sb, h, WAVE) + (q - __shfl(excl, h, WAVE));
-          if (q < tot) {
-            tile[w][lane] = pts[jj];
-            tidx[w][lane] = jj;
-          }
-          __builtin_amdgcn_wave_barrier();
-          const int nv = min(WAVE, tot - q0);
-          if (sl < nsl) {
-            for (int s = sl; s < nv; s += nsl) {
-              const P4<T> pj = tile[w][s];
-              const T dx = pi.x - pj.x, dy = pi.y - pj.y, dz = pi.z - pj.z;
-              const T r2 = dx * dx + dy * dy + dz * dz;
-              T rinv = p2p_rsqrt(r2);
-              rinv = (tidx[w][s] == i) ? (T)0 : rinv;  // self term omitted
-              const T mr = pj.m * rinv;
-              const T mr3 = mr * rinv * rinv;
-              fp -= mr;
-              fx -= mr3 * dx;
-              fy -= mr3 * dy;
-              fz -= mr3 * dz;
+          for (int r = 0; r < TILE / WAVE; r++) {
+            const int q = q0 + r * WAVE + lane;
+            int h = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1) {
+              const int v = __shfl(incl, h + step - 1, WAVE);
+              if (v <= q) h += step;
             }
+            h = min(h, WAVE - 1);
+            const int32_t jj = __shfl(sb, h, WAVE) + (q - __shfl(excl, h, WAVE));
+            if (q < tot) tile[w][r * WAVE + lane] = pts[jj];
           }
           __builtin_amdgcn_wave_barrier();
+          const int nv = min(TILE, tot - q0);
+          if (sl < nsl)
+            for (int s = sl; s < nv; s += nsl) pair_acc(pi, tile[w][s], fp, fx, fy, fz);
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+      if (__ballot(self) != 0ull && sl < nsl) {
+        for (int32_t s = sl; s < tn; s += nsl) {
+          if (tb + s == i) continue;  // self term omitted
+          pair_acc(pi, pts[tb + s], fp, fx, fy, fz);
         }
       }
       red[w][0][lane] = fp;
@@ -181,42 +194,58 @@ __global__ void __launch_bounds__(P2P_THREADS)
   }
 }
 
-// Leaves split over several tasks: lane l adds the partials of tasks l, l+64,
-// ... in order, then a fixed butterfly adds the lanes.
+// Leaves split over several tasks, one block per leaf: thread (t, s) adds the
+// partials of tasks s, s + nsl, ... of target t in order, then the nsl slices
+// of each target are added in slice order.
+constexpr int CB_THREADS = 256;
+
 template <typename T>
-__global__ void k_p2p_combine(const int32_t* leaves, int64_t n_leaves, const int64_t* task_off,
-                              const int64_t* part_off, const int32_t* begin, const int32_t* count,
-                              const T* part, const P4<T>* far, const int32_t* perm, T* phi,
-                              T* acc) {
-  const int lane = __lane_id();
-  for (int64_t li = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE; li < n_leaves;
-       li += (int64_t)gridDim.x * (blockDim.x / WAVE)) {
+__global__ void __launch_bounds__(CB_THREADS)
+    k_p2p_combine(const int32_t* leaves, int64_t n_leaves, const int64_t* task_off,
+                  const int64_t* part_off, const int32_t* begin, const int32_t* count,
+                  const T* part, const P4<T>* far, const int32_t* perm, T* phi, T* acc) {
+  __shared__ T red[4][CB_THREADS];
+  for (int64_t li = blockIdx.x; li < n_leaves; li += gridDim.x) {
     const int64_t nt = task_off[li + 1] - task_off[li];
     if (nt <= 1) continue;
     const int32_t a = leaves[li];
     const int32_t tn = count[a], tb = begin[a];
-    for (int32_t t = 0; t < tn; t++) {
+    for (int32_t t0 = 0; t0 < tn; t0 += CB_THREADS) {
+      const int tc = min(CB_THREADS, tn - t0);
+      const int nsl = CB_THREADS / tc;
+      const int t = threadIdx.x % tc, sl = threadIdx.x / tc;
       T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-      for (int64_t k = lane; k < nt; k += WAVE) {
-        const T* pp = part + 4 * (part_off[li] + k * tn + t);
-        s0 += pp[0];
-        s1 += pp[1];
-        s2 += pp[2];
-        s3 += pp[3];
+      if (sl < nsl) {
+        for (int64_t k = sl; k < nt; k += nsl) {
+          const T* pp = part + 4 * (part_off[li] + k * tn + t0 + t);
+          s0 += pp[0];
+          s1 += pp[1];
+          s2 += pp[2];
+          s3 += pp[3];
+        }
       }
-      s0 = wave_sum(s0);
-      s1 = wave_sum(s1);
-      s2 = wave_sum(s2);
-      s3 = wave_sum(s3);
-      if (lane == 0) {
-        const int32_t i = tb + t;
+      red[0][threadIdx.x] = s0;
+      red[1][threadIdx.x] = s1;
+      red[2][threadIdx.x] = s2;
+      red[3][threadIdx.x] = s3;
+      __syncthreads();
+      if ((int)threadIdx.x < tc) {
+        T r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+        for (int s = 0; s < nsl; s++) {
+          r0 += red[0][s * tc + threadIdx.x];
+          r1 += red[1][s * tc + threadIdx.x];
+          r2 += red[2][s * tc + threadIdx.x];
+          r3 += red[3][s * tc + threadIdx.x];
+        }
+        const int32_t i = tb + t0 + threadIdx.x;
         const P4<T> f = far[i];
         const int64_t o = perm[i];
-        phi[o] = f.x + s0;
-        acc[3 * o] = f.y + s1;
-        acc[3 * o + 1] = f.z + s2;
-        acc[3 * o + 2] = f.m + s3;
+        phi[o] = f.x + r0;
+        acc[3 * o] = f.y + r1;
+        acc[3 * o + 1] = f.z + r2;
+        acc[3 * o + 2] = f.m + r3;
       }
+      __syncthreads();
     }
   }
 }
@@ -250,14 +279,13 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
   if (n_tasks == 0) return hipSuccess;
   int64_t blocks = (n_tasks + P2P_WAVES - 1) / P2P_WAVES;
   if (blocks > 65535) blocks = 65535;
-  int64_t cblocks = (n_leaves + P2P_WAVES - 1) / P2P_WAVES;
-  if (cblocks > 65535) cblocks = 65535;
+  int64_t cblocks = n_leaves < 65535 ? n_leaves : 65535;
   if (dtype == FMM_F64) {
     k_p2p<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
         (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<double>*)pts,
         (const P4<double>*)far, perm, (double*)phi, (double*)acc, (double*)part);
     if (any_multi)
-      k_p2p_combine<double><<<(unsigned)cblocks, P2P_THREADS, 0, st>>>(
+      k_p2p_combine<double><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
           leaves, n_leaves, task_off, part_off, begin, count, (const double*)part,
           (const P4<double>*)far, perm, (double*)phi, (double*)acc);
   } else {
@@ -265,7 +293,7 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
         (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<float>*)pts,
         (const P4<float>*)far, perm, (float*)phi, (float*)acc, (float*)part);
     if (any_multi)
-      k_p2p_combine<float><<<(unsigned)cblocks, P2P_THREADS, 0, st>>>(
+      k_p2p_combine<float><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
           leaves, n_leaves, task_off, part_off, begin, count, (const float*)part,
           (const P4<float>*)far, perm, (float*)phi, (float*)acc);
   }

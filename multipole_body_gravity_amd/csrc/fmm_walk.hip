@@ -40,18 +40,17 @@ constexpr int WK_THREADS = 256;
 constexpr int WK_WAVES = WK_THREADS / WAVE;
 constexpr uint32_t QMASK = 0x1fffffu;
 
-// Opening criterion in units of half the finer cell's side: centres and
-// half-widths become integers, |c_A - c_B|^2 and 3 (h_A + h_B)^2 are exact in
-// fp64 (< 2^46), and the only rounding is the product with fl(theta^2).
-__device__ __forceinline__ bool accept_pair(int la, uint64_t qa, int lb, uint64_t qb, double t2) {
-  const int lm = max(la, lb);
-  const int ha = 1 << (lm - la), hb = 1 << (lm - lb);
-  const int ax = ha * (2 * (int)((qa >> 42) & QMASK) + 1), bx = hb * (2 * (int)((qb >> 42) & QMASK) + 1);
-  const int ay = ha * (2 * (int)((qa >> 21) & QMASK) + 1), by = hb * (2 * (int)((qb >> 21) & QMASK) + 1);
-  const int az = ha * (2 * (int)(qa & QMASK) + 1), bz = hb * (2 * (int)(qb & QMASK) + 1);
-  const double dx = (double)(ax - bx), dy = (double)(ay - by), dz = (double)(az - bz);
+// Opening criterion, theta = |l_A + l_B| / |c_A - c_B| with l = (h, h, h):
+// accept iff 3 (h_A + h_B)^2 < fl(theta^2) |c_A - c_B|^2.  Centres and
+// half-widths are integers in units of 1/2^22 of the root side, so both squares
+// are exact in fp64 (< 2^47) and the only rounding is the product with
+// fl(theta^2); a change of unit by a power of two scales both sides exactly,
+// so the decision equals the one taken in units of the finer cell.
+constexpr int GEO_LEAF = 1 << 30;
+__device__ __forceinline__ bool accept_pair(const int4& A, const int4& B, double t2) {
+  const double dx = (double)(A.x - B.x), dy = (double)(A.y - B.y), dz = (double)(A.z - B.z);
   const double r2 = dx * dx + dy * dy + dz * dz;  // exact
-  const double s = (double)(ha + hb);
+  const double s = (double)((A.w & (GEO_LEAF - 1)) + (B.w & (GEO_LEAF - 1)));
   const double lhs = 3.0 * (s * s);  // exact
   return lhs < t2 * r2;
 }
@@ -60,17 +59,15 @@ enum { CAND_NONE = 0, CAND_M2L = 1, CAND_P2P = 2, CAND_CARRY = 3 };
 
 struct Target {
   int32_t t;
-  int lt;
-  uint64_t qt;
+  int4 g;
   bool leaf;
 };
 
 __device__ __forceinline__ int classify(const WalkArgs& a, const Target& T, int32_t c) {
-  const int lc = a.level[c];
-  const uint64_t qc = a.q[c];
-  if (accept_pair(T.lt, T.qt, lc, qc, a.t2)) return CAND_M2L;
+  const int4 g = a.geo[c];
+  if (accept_pair(T.g, g, a.t2)) return CAND_M2L;
   if (!T.leaf) return CAND_CARRY;
-  return (a.n_child[c] == 0) ? CAND_P2P : CAND_CARRY;
+  return (g.w & GEO_LEAF) ? CAND_P2P : CAND_CARRY;
 }
 
 // Visit the candidates of a generator slice in ascending node order, 64 at a
@@ -150,7 +147,7 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk_pass1(WalkArgs a) {
     const int32_t par = a.parent[t];
     const int64_t g0 = a.carry_off[par];
     const int gc = a.carry_cnt[par];
-    Target T{t, a.level[t], a.q[t], a.n_child[t] == 0};
+    Target T{t, a.geo[t], (a.geo[t].w & GEO_LEAF) != 0};
     int n_m2l = 0, n_p2p = 0, n_carry = 0, n_trm = 0, n_trp = 0;
     for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int phase) {
       const int ty = act ? classify(a, T, c) : CAND_NONE;
@@ -215,7 +212,7 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk_pass2(WalkArgs a) {
     const int32_t par = a.parent[t];
     const int64_t g0 = a.carry_off[par];
     const int gc = a.carry_cnt[par];
-    Target T{t, a.level[t], a.q[t], a.n_child[t] == 0};
+    Target T{t, a.geo[t], (a.geo[t].w & GEO_LEAF) != 0};
     const int64_t m0 = a.m2l_off[t], p0 = a.p2p_off[t];
     int64_t cm = 0, cp = 0;
     for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int) {
@@ -256,14 +253,20 @@ __global__ void k_walk_root(int pass, int root_leaf, WalkArgs a) {
 
 __global__ void k_walk_reset(Control* c) {
   for (int i = threadIdx.x; i < 3 * POOL_SHARDS; i += blockDim.x) (&c->pool_used[0][0])[i] = 0;
-  if (threadIdx.x == 0) c->pool_overflow = 0;
+  if (threadIdx.x == 0) {
+    c->pool_overflow = 0;
+    c->own_m2l_total = 0;
+    c->own_p2p_total = 0;
+  }
 }
 
-// Sum of the own counts (list sizes are known before the transposed sort).
+// Sum of the own counts (list sizes are known before the transposed sort);
+// block partial sums are added with integer atomics (order-independent).
 __global__ void k_walk_own_totals(int64_t n, const int32_t* om, const int32_t* op, Control* c) {
   __shared__ int64_t sm[WK_THREADS], sp[WK_THREADS];
   int64_t a = 0, b = 0;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
     a += om[i];
     b += op[i];
   }
@@ -278,8 +281,8 @@ __global__ void k_walk_own_totals(int64_t n, const int32_t* om, const int32_t* o
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    c->own_m2l_total = sm[0];
-    c->own_p2p_total = sp[0];
+    atomicAdd((unsigned long long*)&c->own_m2l_total, (unsigned long long)sm[0]);
+    atomicAdd((unsigned long long*)&c->own_p2p_total, (unsigned long long)sp[0]);
   }
 }
 
@@ -304,32 +307,23 @@ __global__ void k_tr_compact(Pool<uint64_t> trm, Pool<uint64_t> trp, int kind_bi
     dst[base + i] = p.data[(int64_t)sh * p.shard_cap + i] | kb;
 }
 
-// Runs of equal (kind, target) in the sorted keys: first index and length.
+// Runs of equal (kind, target) in the sorted keys: first index and end index.
 __global__ void k_tr_runs(const uint64_t* keys, int64_t n, int sh, int kind_bit, int64_t n_nodes,
                           int64_t* start, int32_t* cnt) {
   int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (k >= n) return;
   const uint64_t g = keys[k] >> sh;  // kind and target
-  const bool first = k == 0 || (keys[k - 1] >> sh) != g;
-  const bool last = k == n - 1 || (keys[k + 1] >> sh) != g;
   const int kind = (int)(keys[k] >> kind_bit);
   const int64_t c = (int64_t)(g & ((1ull << (kind_bit - sh)) - 1ull));
   const int64_t slot = (int64_t)kind * n_nodes + c;
-  if (first) start[slot] = k;
-  if (last) {
-    int64_t s0 = k;
-    // the run start is written by another thread: recompute it by search
-    int64_t lo = 0, hi = k;
-    while (lo < hi) {
-      int64_t mid = (lo + hi) >> 1;
-      if ((keys[mid] >> sh) < g)
-        lo = mid + 1;
-      else
-        hi = mid;
-    }
-    s0 = lo;
-    cnt[slot] = (int32_t)(k - s0 + 1);
-  }
+  if (k == 0 || (keys[k - 1] >> sh) != g) start[slot] = k;
+  if (k == n - 1 || (keys[k + 1] >> sh) != g) cnt[slot] = (int32_t)(k + 1);  // end, for now
+}
+
+// run ends -> run lengths
+__global__ void k_tr_lengths(int64_t m, const int64_t* start, int32_t* cnt) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < m && cnt[i] > 0) cnt[i] = (int32_t)(cnt[i] - start[i]);
 }
 
 __global__ void k_walk_offsets(int64_t n, const int32_t* om, const int32_t* op, const int32_t* cm,
@@ -378,7 +372,9 @@ hipError_t launch_walk_reset(Control* ctrl, hipStream_t st) {
 }
 hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
                                   Control* ctrl, hipStream_t st) {
-  k_walk_own_totals<<<1, WK_THREADS, 0, st>>>(n_nodes, own_m2l, own_p2p, ctrl);
+  int64_t blocks = (n_nodes + WK_THREADS - 1) / WK_THREADS;
+  if (blocks > 1024) blocks = 1024;
+  k_walk_own_totals<<<(unsigned)blocks, WK_THREADS, 0, st>>>(n_nodes, own_m2l, own_p2p, ctrl);
   return hipGetLastError();
 }
 hipError_t launch_tr_compact(const WalkArgs& a, int kind_bit, uint64_t* dst, hipStream_t st) {
@@ -390,6 +386,7 @@ hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int ki
   if (n <= 0) return hipSuccess;
   k_tr_runs<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, key_shift, kind_bit, n_nodes,
                                                          start, cnt);
+  k_tr_lengths<<<(unsigned)((2 * n_nodes + 255) / 256), 256, 0, st>>>(2 * n_nodes, start, cnt);
   return hipGetLastError();
 }
 hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
