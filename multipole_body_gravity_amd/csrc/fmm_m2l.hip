@@ -16,6 +16,8 @@
 // target's list, accumulates a private partial local expansion, and the 64
 // partials are summed by a fixed butterfly, so the result does not depend on
 // scheduling.  Each target is written once (every level in one launch).
+#include <algorithm>
+
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -86,15 +88,17 @@ __global__ void __launch_bounds__(M2L_THREADS)
     for (int k = 0; k < K; k++) acc[k] = (T)0;
     for (int64_t e = e0 + lane; e < e1; e += WAVE) {
       const int64_t b = src[e];
+      // the source's moments are loaded first; the derivative tensor, which
+      // needs only the centres, is built while they are in flight
+      const T* Mb = mpole + b * K;
+      T M[K];
+#pragma unroll
+      for (int k = 0; k < K; k++) M[k] = Mb[k];
       const T rx = (T)(cax - centre[3 * b]);
       const T ry = (T)(cay - centre[3 * b + 1]);
       const T rz = (T)(caz - centre[3 * b + 2]);
       T D[K];
       dtensor<T, P>(rx, ry, rz, D);
-      const T* Mb = mpole + b * K;
-      T M[K];
-#pragma unroll
-      for (int k = 0; k < K; k++) M[k] = Mb[k];
       static_for<0, NT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         acc[tabs<P>.tn[t]] += M[tabs<P>.tm[t]] * D[tabs<P>.tk[t]];

@@ -82,7 +82,7 @@ def lattice(ngrid: int, seed: int, rms_cells: float = 0.3, slope: float = -2.0) 
     psi = np.empty((3, ngrid, ngrid, ngrid))
     for c in range(3):
         white = rng.standard_normal((ngrid, ngrid, ngrid))
-        psi[c] = np.fft.irfftn(np.fft.rfftn(white) * amp, s=(ngrid, ngrid, ngrid))
+        psi[c] = np.fft.irfftn(np.fft.rfftn(white) * amp, s=(ngrid, ngrid, ngrid), axes=(0, 1, 2))
     rms = np.sqrt(np.mean(np.sum(psi ** 2, axis=0)))
     psi *= (rms_cells / ngrid) / rms
     gx, gy, gz = np.meshgrid(q1, q1, q1, indexing="ij")

@@ -171,8 +171,23 @@ def test_parity_1e5(orc, name):
     plan.close()
 
 
-@pytest.mark.parametrize("name", ["clustered_1e6_p4", "clustered_1e6_f32", "clustered_1e6_p6"])
-def test_parity_1e6_sampled(orc, name):
+@pytest.mark.timeout(300)
+def test_parity_headline_full(orc):
+    """The benchmarked workload (10^6 clustered, fp64, order 4, theta 0.7, leaf
+    32) against the full oracle: every key, node, list entry and particle."""
+    c = W.CONFIGS["clustered_1e6_p4"]
+    pos, mass = inputs(c["dist"], c["n"], c["seed"], c["dtype"])
+    plan, phi, acc = gpu_run(pos, mass, c["order"], c["theta"], c["leaf"], c["dtype"])
+    say("  oracle (full)")
+    ref = orc.fmm(pos, mass, c["order"], c["theta"], c["leaf"])
+    check_structure(plan, ref)
+    check_values(phi, acc, ref, c["dtype"])
+    plan.close()
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name,n_sample", [("clustered_1e6_f32", 512), ("clustered_1e6_p6", 128)])
+def test_parity_1e6_sampled(orc, name, n_sample):
     """Full-size workloads: complete structure check, values on a seeded sample
     of particles (the oracle computes their leaves' exact lists and expansions)."""
     c = W.CONFIGS[name]
@@ -182,7 +197,7 @@ def test_parity_1e6_sampled(orc, name):
     full = orc.fmm(pos, mass, c["order"], c["theta"], c["leaf"], numeric=False)
     check_structure(plan, full)
     del full
-    smp = np.random.default_rng(77).choice(c["n"], 512, replace=False)
+    smp = np.random.default_rng(77).choice(c["n"], n_sample, replace=False)
     ref = orc.fmm(pos, mass, c["order"], c["theta"], c["leaf"], sample=smp)
     check_values(phi, acc, ref, c["dtype"], idx=smp)
     plan.close()
@@ -247,4 +262,23 @@ def test_expansions_match_oracle(orc):
     assert np.max(np.abs(mp - ref.mpole) / scale_m) < 1e-12
     scale_l = np.abs(ref.local).max(axis=1, keepdims=True) + 1e-300
     assert np.max(np.abs(lc - ref.local) / scale_l) < 1e-11
+    plan.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,n_sample", [("lattice_256_f32", 256), ("lattice_256_p8", 24)])
+def test_parity_lattice_sampled(orc, name, n_sample):
+    """256^3 displaced lattice: keys, permutation and tree in full; lists and
+    values for the leaves of a seeded particle sample (the oracle's walk is
+    restricted to those targets)."""
+    c = W.CONFIGS[name]
+    say(f"  case {name}: generating")
+    pos, mass = inputs(c["dist"], c["n"], c["seed"], c["dtype"])
+    say("  gpu")
+    plan, phi, acc = gpu_run(pos, mass, c["order"], c["theta"], c["leaf"], c["dtype"])
+    smp = np.random.default_rng(78).choice(c["n"], n_sample, replace=False)
+    say("  oracle (sampled)")
+    ref = orc.fmm(pos, mass, c["order"], c["theta"], c["leaf"], sample=smp)
+    check_structure(plan, ref, sample_targets=np.nonzero(ref.mark)[0])
+    check_values(phi, acc, ref, c["dtype"], idx=smp)
     plan.close()
