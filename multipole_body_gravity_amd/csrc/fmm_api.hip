@@ -206,15 +206,45 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
                               a.own_m2l, tr_start, a.m2l_src, P<int64_t>(p->p2p_off), a.own_p2p,
                               tr_start + nn, a.p2p_src, st));
 
+  // sibling unions of the children's own M2L sources (counted here, written
+  // once their total is known)
+  const int64_t np = nn - nl;
+  p->n_parents = np;
+  TRY(grow(p->uoff, (size_t)(np + 1) * 8));
+  int64_t* uoff = P<int64_t>(p->uoff);
+  const int32_t* parents = P<int32_t>(p->parents);
+  if (np > 0) {
+    TRY_HIP(launch_union(1, a, parents, np, uoff, nullptr, nullptr, st));
+    TRY_HIP(scan_exclusive_i64(uoff, uoff, np, uoff + np, p->scan_tmp.p, st));
+  } else {
+    TRY_HIP(launch_fill_zero(uoff, 8, st));
+  }
+
   // near-field tasks
   TRY_HIP(launch_p2p_task_count(leaves, nl, P<int64_t>(p->p2p_off), P<int32_t>(p->ncount), toff,
                                 poff, st));
   TRY_HIP(scan_exclusive_i64(toff, toff, nl, toff + nl, p->scan_tmp.p, st));
   TRY_HIP(scan_exclusive_i64(poff, poff, nl, poff + nl, p->scan_tmp.p, st));
+  // transposed-tail M2L tasks
+  TRY(grow(p->tail_toff, (size_t)(nl + 1) * 8));
+  int64_t* ttoff = P<int64_t>(p->tail_toff);
+  TRY_HIP(launch_tail_count(leaves, nl, P<int64_t>(p->m2l_off), a.own_m2l, ttoff, st));
+  TRY_HIP(scan_exclusive_i64(ttoff, ttoff, nl, ttoff + nl, p->scan_tmp.p, st));
   TRY_HIP(launch_walk_copy_totals(P<int64_t>(p->m2l_off) + nn, P<int64_t>(p->p2p_off) + nn,
-                                  toff + nl, poff + nl, dctrl, st));
+                                  toff + nl, poff + nl, uoff + np, ttoff + nl, dctrl, st));
   TRY(sync_ctrl(p, st));
   if (p->ctrl_host->n_m2l != p->n_m2l || p->ctrl_host->n_p2p != p->n_p2p) return FMM_ERR_HIP;
+  p->n_union = p->ctrl_host->n_union;
+  TRY(grow(p->usrc, (size_t)std::max<int64_t>(p->n_union, 1) * 4));
+  TRY(grow(p->umask, (size_t)std::max<int64_t>(p->n_union, 1)));
+  if (np > 0)
+    TRY_HIP(launch_union(2, a, parents, np, uoff, P<int32_t>(p->usrc), P<uint8_t>(p->umask), st));
+  p->n_tail_tasks = p->ctrl_host->n_tail_tasks;
+  TRY(grow(p->tail_task, (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * sizeof(TailTask)));
+  TRY(grow(p->tail_part,
+           (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * p->K * wbytes(p->dtype)));
+  TRY_HIP(launch_tail_fill(leaves, nl, P<int64_t>(p->m2l_off), a.own_m2l, ttoff,
+                           P<TailTask>(p->tail_task), st));
   p->n_p2p_tasks = p->ctrl_host->n_p2p_tasks;
   p->n_p2p_part = p->ctrl_host->n_p2p_part;
   TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
@@ -298,7 +328,8 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->tr_start_p2p, &p->tr_keys, &p->tr_keys_alt, &p->tr_vals,
                   &p->tr_vals_alt, &p->m2l_off, &p->m2l_src, &p->p2p_off, &p->p2p_src,
                   &p->p2p_task, &p->p2p_part, &p->p2p_toff, &p->p2p_poff, &p->tot_m2l,
-                  &p->tot_p2p};
+                  &p->tot_p2p,  &p->parents,  &p->uoff,    &p->usrc,    &p->umask,
+                  &p->tail_toff, &p->tail_task, &p->tail_part};
   for (DBuf* b : bufs) release(*b);
   if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);
   for (int i = 0; i < 2 * FMM_N_STAGES; i++)
@@ -367,7 +398,8 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   TRY(grow(p->nq, 8 * nn));
   TRY(grow(p->ngeo, 16 * nn));
   TRY(grow(p->leaves, 4 * (3 * nn + 2)));
-  TRY(grow(p->mpole, w * p->K * nn));
+  TRY(grow(p->parents, 4 * nn));
+  TRY(grow(p->mpole, (size_t)mrec_bytes(p->K, (int)w) * nn));
   TRY(grow(p->local, w * p->K * nn));
   TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
   TreeArrays t{P<uint8_t>(p->nlevel),  P<uint64_t>(p->nprefix), P<int32_t>(p->nbegin),
@@ -378,7 +410,9 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   TRY_HIP(launch_tree_phase2(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
                              P<int8_t>(p->leaf_level), P<int64_t>(p->lvl_blkcnt), nn, p->level_off,
                              root, t, leaves + nn, leaves + 2 * nn + 1, leaves,
-                             P<int32_t>(p->leaf_of), p->scan_tmp.p, ctrl, st));
+                             P<int32_t>(p->leaf_of), P<int32_t>(p->parents), p->scan_tmp.p, ctrl,
+                             st));
+  TRY_HIP(launch_mrec_centres(p->dtype, p->order, nn, P<double>(p->ncentre), p->mpole.p, st));
   rec(p, FMM_STAGE_TREE, 1, st);
 
   rec(p, FMM_STAGE_WALK, 0, st);
@@ -406,8 +440,26 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   rec(p, FMM_STAGE_UP, 1, st);
 
   rec(p, FMM_STAGE_M2L, 0, st);
-  TRY_HIP(launch_m2l(dt, ord, p->n_nodes, P<int64_t>(p->m2l_off), P<int32_t>(p->m2l_src), centre,
-                     p->mpole.p, p->local.p, st));
+  M2LArgs ma{};
+  ma.n_nodes = p->n_nodes;
+  ma.parents = P<int32_t>(p->parents);
+  ma.n_parents = p->n_parents;
+  ma.first_child = P<int32_t>(p->nfirst);
+  ma.n_child = P<uint8_t>(p->nnchild);
+  ma.uoff = P<int64_t>(p->uoff);
+  ma.usrc = P<int32_t>(p->usrc);
+  ma.umask = P<uint8_t>(p->umask);
+  ma.leaves = leaves;
+  ma.n_leaves = p->n_leaves;
+  ma.tasks = P<TailTask>(p->tail_task);
+  ma.n_tasks = p->n_tail_tasks;
+  ma.toff = P<int64_t>(p->tail_toff);
+  ma.src = P<int32_t>(p->m2l_src);
+  ma.centre = centre;
+  ma.mrec = p->mpole.p;
+  ma.part = p->tail_part.p;
+  ma.local = p->local.p;
+  TRY_HIP(launch_m2l(dt, ord, ma, st));
   rec(p, FMM_STAGE_M2L, 1, st);
 
   rec(p, FMM_STAGE_DOWN, 0, st);

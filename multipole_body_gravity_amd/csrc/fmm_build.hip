@@ -631,9 +631,13 @@ __global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t n_n
 
 __global__ void k_tree_leaves(const int32_t* leaf_flag, const int32_t* scan, int64_t n_nodes,
                               const int32_t* begin, const int32_t* count, int32_t* leaves,
-                              int32_t* leaf_of) {
+                              int32_t* leaf_of, int32_t* parents) {
   int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (id >= n_nodes || !leaf_flag[id]) return;
+  if (id >= n_nodes) return;
+  if (!leaf_flag[id]) {  // non-leaf: its rank among non-leaves is id - (leaves before id)
+    parents[id - scan[id]] = (int32_t)id;
+    return;
+  }
   leaves[scan[id]] = (int32_t)id;
   for (int32_t k = begin[id]; k < begin[id] + count[id]; k++) leaf_of[k] = (int32_t)id;
 }
@@ -642,8 +646,8 @@ hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const i
                               const int8_t* leaf_level, const int64_t* blkcnt_scanned,
                               int64_t n_nodes, const int64_t* level_off_host, const RootInfo* root,
                               const TreeArrays& t, int32_t* leaf_flag, int32_t* leaf_scan,
-                              int32_t* leaves, int32_t* leaf_of, void* scan_tmp, Control* ctrl,
-                              hipStream_t st) {
+                              int32_t* leaves, int32_t* leaf_of, int32_t* parents, void* scan_tmp,
+                              Control* ctrl, hipStream_t st) {
   int nblk = (int)((n + TR_THREADS - 1) / TR_THREADS);
   k_tree_emit<<<nblk, TR_THREADS, 0, st>>>(keys, n, lcp, leaf_level, blkcnt_scanned, nblk,
                                            t.level, t.prefix, t.begin);
@@ -655,7 +659,7 @@ hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const i
   hipError_t e = scan_excl<int32_t>(leaf_flag, leaf_scan, n_nodes, nullptr, scan_tmp, st);
   if (e != hipSuccess) return e;
   k_tree_leaves<<<g, 256, 0, st>>>(leaf_flag, leaf_scan, n_nodes, t.begin, t.count, leaves,
-                                   leaf_of);
+                                   leaf_of, parents);
   (void)ctrl;
   return hipGetLastError();
 }

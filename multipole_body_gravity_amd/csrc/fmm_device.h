@@ -16,6 +16,15 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (1ull << __lane_id()) - 1ull;
 }
 
+// Value of lane 0 in a scalar register (for values known to be wave-uniform).
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Wave-wide sum with a fixed butterfly order: every lane gets the same,
 // bit-reproducible result.
 template <typename T>

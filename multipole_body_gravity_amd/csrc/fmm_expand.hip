@@ -75,6 +75,7 @@ __global__ void __launch_bounds__(256)
     k_p2m_reg(const P4<T>* pts, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
               const int32_t* count, const double* centre, T* mpole) {
   constexpr int K = Tabs<P>::K;
+  constexpr int RS = mrec_stride(K, sizeof(T));
   const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (li >= n_leaves) return;
   const int32_t node = leaves[li];
@@ -100,7 +101,7 @@ __global__ void __launch_bounds__(256)
       acc[k] += px[tabs<P>.a[k]] * py[tabs<P>.b[k]] * pz[tabs<P>.c[k]];
     });
   }
-  T* out = mpole + (int64_t)node * K;
+  T* out = mpole + (int64_t)node * RS;
 #pragma unroll
   for (int k = 0; k < K; k++) out[k] = (T)acc[k];
 }
@@ -140,6 +141,7 @@ __global__ void __launch_bounds__(256)
     k_m2m_reg(int64_t lvl_begin, int64_t lvl_count, const int32_t* first_child,
               const uint8_t* n_child, const double* centre, T* mpole) {
   constexpr int K = Tabs<P>::K;
+  constexpr int RS = mrec_stride(K, sizeof(T));
   constexpr int NTM = m2m_tab<P>.nt;
   const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int64_t pi = g >> 3;
@@ -162,7 +164,7 @@ __global__ void __launch_bounds__(256)
       py[q] = py[q - 1] * ny * (1.0 / q);
       pz[q] = pz[q - 1] * nz * (1.0 / q);
     }
-    const T* Mc = mpole + ch * K;
+    const T* Mc = mpole + ch * RS;
     double M[K];
 #pragma unroll
     for (int k = 0; k < K; k++) M[k] = (double)Mc[k];
@@ -181,11 +183,88 @@ __global__ void __launch_bounds__(256)
     acc[k] = v;
   }
   if (valid_p && nc > 0) {
-    T* out = mpole + Pn * K;
+    T* out = mpole + Pn * RS;
     static_for<0, K>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       if ((k & 7) == c) out[k] = (T)acc[k];
     });
+  }
+}
+
+// L2L, one thread per child: L_n(child) += sum_{|n|+|k|<=p} L_(n+k)(parent) d^k/k!.
+template <int P>
+struct L2LTab {
+  static constexpr int NT = binom_c(P + 6, 6);
+  int n[NT], src[NT], ka[NT], kb[NT], kc[NT];
+  constexpr L2LTab() : n(), src(), ka(), kb(), kc() {
+    constexpr int K = (P + 1) * (P + 2) * (P + 3) / 6;
+    int t = 0;
+    for (int ni = 0; ni < K; ni++)
+      for (int ki = 0; ki < K; ki++)
+        if (tabs<P>.d[ni] + tabs<P>.d[ki] <= P) {
+          n[t] = ni;
+          src[t] = mi_index(tabs<P>.a[ni] + tabs<P>.a[ki], tabs<P>.b[ni] + tabs<P>.b[ki],
+                            tabs<P>.c[ni] + tabs<P>.c[ki]);
+          ka[t] = tabs<P>.a[ki];
+          kb[t] = tabs<P>.b[ki];
+          kc[t] = tabs<P>.c[ki];
+          t++;
+        }
+  }
+};
+template <int P>
+inline constexpr L2LTab<P> l2l_tab{};
+
+template <typename T, int P>
+__global__ void __launch_bounds__(256)
+    k_l2l_reg(int64_t lvl_begin, int64_t lvl_count, const int32_t* parent, const double* centre,
+              T* local) {
+  constexpr int K = Tabs<P>::K;
+  constexpr int NTL = L2LTab<P>::NT;
+  const int64_t ci = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (ci >= lvl_count) return;
+  const int64_t a = lvl_begin + ci;
+  const int64_t Pn = parent[a];
+  const double dx = centre[3 * a] - centre[3 * Pn], dy = centre[3 * a + 1] - centre[3 * Pn + 1],
+               dz = centre[3 * a + 2] - centre[3 * Pn + 2];
+  double px[P + 1], py[P + 1], pz[P + 1];
+  px[0] = py[0] = pz[0] = 1.0;
+#pragma unroll
+  for (int q = 1; q <= P; q++) {
+    px[q] = px[q - 1] * dx * (1.0 / q);
+    py[q] = py[q - 1] * dy * (1.0 / q);
+    pz[q] = pz[q - 1] * dz * (1.0 / q);
+  }
+  const T* Lp = local + Pn * K;
+  T* Lc = local + a * K;
+  double L[K], acc[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) {
+    L[k] = (double)Lp[k];
+    acc[k] = (double)Lc[k];
+  }
+  static_for<0, NTL>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    acc[l2l_tab<P>.n[t]] += L[l2l_tab<P>.src[t]] *
+                            (px[l2l_tab<P>.ka[t]] * py[l2l_tab<P>.kb[t]] * pz[l2l_tab<P>.kc[t]]);
+  });
+#pragma unroll
+  for (int k = 0; k < K; k++) Lc[k] = (T)acc[k];
+}
+
+template <typename T>
+static bool l2l_reg_dispatch(int order, int64_t lvl_begin, int64_t lvl_count, const int32_t* parent,
+                             const double* centre, void* local, hipStream_t st) {
+  unsigned g = (unsigned)((lvl_count + 255) / 256);
+  switch (order) {
+#define L2LR(P)                                                                             \
+  case P:                                                                                   \
+    k_l2l_reg<T, P><<<g, 256, 0, st>>>(lvl_begin, lvl_count, parent, centre, (T*)local); \
+    return true;
+    L2LR(0) L2LR(1) L2LR(2) L2LR(3) L2LR(4) L2LR(5)
+#undef L2LR
+    default:
+      return false;
   }
 }
 
@@ -270,7 +349,7 @@ __global__ void __launch_bounds__(EX_THREADS)
     }
     for (int r = 0; r < 3; r++) {
       const int m = lane + WAVE * r;
-      if (m < K) mpole[(int64_t)node * K + m] = (T)acc[r];
+      if (m < K) mpole[(int64_t)node * mrec_stride(K, sizeof(T)) + m] = (T)acc[r];
     }
   }
 }
@@ -310,6 +389,7 @@ __global__ void __launch_bounds__(EX_THREADS)
   __shared__ double mc[EX_WAVES][MAXCH][ncoef(FMM_MAX_ORDER)];
   __shared__ double tab[EX_WAVES][MAXCH][3][PP];
   const int lane = __lane_id(), w = threadIdx.x / WAVE;
+  const int64_t RS = mrec_stride(K, sizeof(T));
   for (int64_t pi = (int64_t)blockIdx.x * EX_WAVES + w; pi < lvl_count;
        pi += (int64_t)gridDim.x * EX_WAVES) {
     const int64_t P = lvl_begin + pi;
@@ -318,7 +398,7 @@ __global__ void __launch_bounds__(EX_THREADS)
     const int64_t fc = first_child[P];
     for (int q = lane; q < nc * K; q += WAVE) {
       const int ch = q / K, k = q - ch * K;
-      mc[w][ch][k] = (double)mpole[(fc + ch) * K + k];
+      mc[w][ch][k] = (double)mpole[(fc + ch) * RS + k];
     }
     if (lane < 3 * nc) {
       const int ch = lane / 3, ax = lane - 3 * ch;
@@ -341,7 +421,7 @@ __global__ void __launch_bounds__(EX_THREADS)
             for (int k = 0; k <= mcc; k++)
               acc += mc[w][ch][mi_index(i, j, k)] * exy * tab[w][ch][2][mcc - k];
           }
-      mpole[P * K + m] = (T)acc;
+      mpole[P * RS + m] = (T)acc;
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -417,6 +497,11 @@ hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
   if (lvl_count == 0) return hipSuccess;
+  if (dtype == FMM_F64 ? l2l_reg_dispatch<double>(order, lvl_begin, lvl_count, parent, centre,
+                                                  local, st)
+                       : l2l_reg_dispatch<float>(order, lvl_begin, lvl_count, parent, centre,
+                                                 local, st))
+    return hipGetLastError();
   int64_t blocks = std::min<int64_t>((lvl_count + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
     k_l2l<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, lvl_begin, lvl_count, parent,
@@ -511,6 +596,25 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
+__global__ void k_mrec_centres(int64_t n_nodes, int RB, int CB, const double* centre,
+                               unsigned char* mrec) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= 3 * n_nodes) return;
+  const int64_t node = i / 3;
+  double* c = (double*)(mrec + node * RB + CB);
+  c[i - 3 * node] = centre[i];
+}
+
+hipError_t launch_mrec_centres(int dtype, int order, int64_t n_nodes, const double* centre,
+                               void* mpole, hipStream_t st) {
+  if (n_nodes <= 0) return hipSuccess;
+  const int K = ncoef(order), wb = dtype == FMM_F64 ? 8 : 4;
+  const unsigned g = (unsigned)((3 * n_nodes + 255) / 256);
+  k_mrec_centres<<<g, 256, 0, st>>>(n_nodes, mrec_bytes(K, wb), mrec_centre_byte(K, wb),
+                                            centre, (unsigned char*)mpole);
+  return hipGetLastError();
+}
+
 // scaled moments -> raw moments M_m = (-1)^|m| m! Mt_m; locals copied as fp64
 template <typename T>
 __global__ void k_export(int K, int64_t total, const T* mpole, const T* local, double* mp,
@@ -524,7 +628,7 @@ __global__ void k_export(int K, int64_t total, const T* mpole, const T* local, d
   for (int i = 2; i <= b; i++) f *= i;
   for (int i = 2; i <= c; i++) f *= i;
   if ((a + b + c) & 1) f = -f;
-  if (mp) mp[gid] = (double)mpole[gid] * f;
+  if (mp) mp[gid] = (double)mpole[(gid / K) * mrec_stride(K, sizeof(T)) + m] * f;
   if (lc) lc[gid] = (double)local[gid];
 }
 

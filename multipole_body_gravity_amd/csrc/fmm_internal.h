@@ -16,6 +16,12 @@ constexpr int MAX_LEVELS = KEY_BITS + 1;  // levels 0..21
 
 // Number of Cartesian coefficients of total degree <= p: C(p+3, 3).
 constexpr int ncoef(int p) { return (p + 1) * (p + 2) * (p + 3) / 6; }
+// Multipole record of a node: its K scaled moments (element size wb), then its
+// centre as three fp64 words at the next 8-byte boundary, padded to a multiple
+// of 16 bytes so that records can be moved in 16-byte pieces.
+constexpr int mrec_centre_byte(int K, int wb) { return (K * wb + 7) / 8 * 8; }
+constexpr int mrec_bytes(int K, int wb) { return (mrec_centre_byte(K, wb) + 24 + 15) / 16 * 16; }
+constexpr int mrec_stride(int K, int wb) { return mrec_bytes(K, wb) / wb; }  // in elements
 
 // Root cube and key scale, computed on the device.
 struct RootInfo {
@@ -37,6 +43,8 @@ struct Control {
   int64_t n_p2p;
   int64_t own_m2l_total, own_p2p_total;  // walk: entries found at the target's own level
   int64_t n_p2p_tasks, n_p2p_part;        // near-field tasks and partial-sum slots
+  int64_t n_union;                        // sibling-union M2L entries
+  int64_t n_tail_tasks;                   // transposed-tail M2L tasks
   int32_t pool_overflow;                  // a sharded pool ran out of room
   int32_t max_leaf_count;
   int64_t pool_used[3][512];              // carry, transposed M2L, transposed P2P shards
@@ -76,6 +84,12 @@ struct fmm_plan_s {
   mbg::DBuf m2l_off, m2l_src, p2p_off, p2p_src;
   // near-field tasks (target leaf x bounded slice of its list)
   mbg::DBuf p2p_task, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
+  // sibling-union M2L lists: per parent, the sources accepted by any child + child masks
+  mbg::DBuf parents, uoff, usrc, umask;
+  int64_t n_parents = 0, n_union = 0;
+  // transposed-tail M2L tasks: per-leaf task offsets, tasks, partial locals
+  mbg::DBuf tail_toff, tail_task, tail_part;
+  int64_t n_tail_tasks = 0;
   int64_t n_p2p_tasks = 0, n_p2p_part = 0;
 
   // host copies of the last build's sizes
@@ -132,8 +146,8 @@ hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const i
                               const int8_t* leaf_level, const int64_t* blkcnt_scanned,
                               int64_t n_nodes, const int64_t* level_off_host, const RootInfo* root,
                               const TreeArrays& t, int32_t* leaf_flag, int32_t* leaf_scan,
-                              int32_t* leaves, int32_t* leaf_of, void* scan_tmp, Control* ctrl,
-                              hipStream_t st);
+                              int32_t* leaves, int32_t* leaf_of, int32_t* parents, void* scan_tmp,
+                              Control* ctrl, hipStream_t st);
 
 // ---- walk ----
 // Sharded bump allocator: shard sh owns [sh * shard_cap, (sh+1) * shard_cap).
@@ -181,7 +195,11 @@ hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int
                              hipStream_t st);
 hipError_t launch_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
                                    const int64_t* task_total, const int64_t* part_total,
+                                   const int64_t* union_total, const int64_t* tail_total,
                                    Control* ctrl, hipStream_t st);
+// per parent: count / write the union of its children's own M2L sources with masks
+hipError_t launch_union(int pass, const WalkArgs& a, const int32_t* parents, int64_t n_parents,
+                        int64_t* ucount_or_off, int32_t* usrc, uint8_t* umask, hipStream_t st);
 // LSD radix sort over the low `bits` bits; returns in *in_alt whether the
 // result ended in (keys_alt, idx_alt).
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
@@ -195,9 +213,41 @@ hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leav
 hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
                       const int32_t* first_child, const uint8_t* n_child, const double* centre,
                       void* mpole, hipStream_t st);
-hipError_t launch_m2l(int dtype, int order, int64_t n_nodes, const int64_t* off,
-                      const int32_t* src, const double* centre, const void* mpole, void* local,
-                      hipStream_t st);
+// M2L: the root's local is cleared, the sibling blocks write every child's own
+// entries, the leaves' transposed tails [off[t] + own[t], off[t+1]) are
+// evaluated as tasks of at most TAIL_E entries and subtracted per leaf.
+constexpr int TAIL_E = 64;
+struct TailTask {
+  int64_t e0;  // first entry
+  int32_t n;   // entries (1..TAIL_E)
+  int32_t li;  // index into the leaf list
+};
+struct M2LArgs {
+  int64_t n_nodes;
+  const int32_t* parents;
+  int64_t n_parents;
+  const int32_t* first_child;
+  const uint8_t* n_child;
+  const int64_t *uoff;
+  const int32_t* usrc;
+  const uint8_t* umask;
+  const int32_t* leaves;
+  int64_t n_leaves;
+  const TailTask* tasks;
+  int64_t n_tasks;
+  const int64_t* toff;   // per leaf: first task (n_leaves + 1)
+  const int32_t* src;    // M2L list sources
+  const double* centre;
+  const void* mrec;      // multipole records
+  void* part;            // task partials (n_tasks x K)
+  void* local;
+};
+hipError_t launch_m2l(int dtype, int order, const M2LArgs& a, hipStream_t st);
+hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                             const int32_t* own, int64_t* cnt, hipStream_t st);
+hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                            const int32_t* own, const int64_t* toff, TailTask* tasks,
+                            hipStream_t st);
 hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
                       const int32_t* parent, const double* centre, void* local, hipStream_t st);
 hipError_t launch_l2p(int dtype, int order, int64_t n, const void* pts, const int32_t* leaf_of,
@@ -217,6 +267,9 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       void* part, bool any_multi, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // expansions in the plan's dtype/convention -> fp64 raw moments / derivatives
+// copy the node centres into the multipole records
+hipError_t launch_mrec_centres(int dtype, int order, int64_t n_nodes, const double* centre,
+                               void* mpole, hipStream_t st);
 hipError_t launch_export_expansions(int dtype, int order, int64_t n_nodes, const void* mpole,
                                     const void* local, double* mp_out, double* lc_out,
                                     hipStream_t st);

@@ -12,10 +12,8 @@
 //     R^(j)_(k+e_x) = x R^(j+1)_k + k_x R^(j+1)_(k-e_x)   (same for y, z),
 //     R^(j)_0 = F_j = (-1)^j (2j-1)!! / |r|^(2j+1),   D^k = R^(0)_k.
 //
-// Work split: one wave per target cell; lane l takes sources l, l+64, ... of the
-// target's list, accumulates a private partial local expansion, and the 64
-// partials are summed by a fixed butterfly, so the result does not depend on
-// scheduling.  Each target is written once (every level in one launch).
+// Every summation runs in a fixed order (fixed butterflies, no atomics), so
+// results do not depend on scheduling.
 #include <algorithm>
 
 #include "fmm_device.h"
@@ -71,55 +69,278 @@ __device__ __forceinline__ void dtensor(T x, T y, T z, T (&D)[Tabs<P>::K]) {
   });
 }
 
+// ---------------- sibling blocks ----------------
+// The children of one parent receive the same candidates, so their own sources
+// are the union U of the candidates any child accepts (built with the walk,
+// each entry carrying an 8-bit mask of the accepting children).  One wave per
+// parent: lane l = 8 t + j pairs child slot t with source slot j of a chunk of
+// 8 union entries.  The chunk's source records (moments + centre) are copied
+// from HBM straight into LDS by 16-byte global-to-LDS loads, NS chunks ahead in
+// a ring, so no registers hold data in flight and each record is read once for
+// up to 8 children.  Each lane keeps the partial local expansion of child t
+// over its source slot; the 8 slots are summed by a fixed butterfly at the end
+// and the children's locals are written (not added).
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+template <typename T, int P>
+struct SibCfg {
+  static constexpr int K = Tabs<P>::K;
+  static constexpr int RB = mrec_bytes(K, sizeof(T));       // record bytes
+  static constexpr int CB = mrec_centre_byte(K, sizeof(T)); // centre offset in a record
+  static constexpr int PC = RB / 16;                        // 16-byte pieces per record
+  static constexpr int NI = (8 * PC + WAVE - 1) / WAVE;     // copy instructions per chunk
+  static constexpr int SB = NI * WAVE * 16;                 // ring stage bytes
+  static constexpr int NS = NI <= 3 ? 3 : 2;                // ring depth (chunks)
+  static constexpr int WIN = 256;                           // union entries per id window
+  static constexpr int WAIT = (NS - 1) * NI;                // copies allowed in flight
+};
+
 template <typename T, int P>
 __global__ void __launch_bounds__(M2L_THREADS)
-    k_m2l(int64_t n_nodes, const int64_t* __restrict__ off, const int32_t* __restrict__ src,
-          const double* __restrict__ centre, const T* __restrict__ mpole, T* __restrict__ local) {
-  constexpr int K = Tabs<P>::K;
+    k_m2l_sib(int64_t n_parents, const int32_t* __restrict__ parents,
+              const int32_t* __restrict__ first_child, const uint8_t* __restrict__ n_child,
+              const int64_t* __restrict__ uoff, const int32_t* __restrict__ usrc,
+              const uint8_t* __restrict__ umask, const double* __restrict__ centre,
+              const unsigned char* __restrict__ mrec, T* __restrict__ local) {
+  using C = SibCfg<T, P>;
+  constexpr int K = C::K;
   constexpr int NT = Tabs<P>::NT;
-  const int lane = __lane_id();
-  const int64_t wid = (int64_t)blockIdx.x * (M2L_THREADS / WAVE) + threadIdx.x / WAVE;
-  const int64_t nw = (int64_t)gridDim.x * (M2L_THREADS / WAVE);
-  for (int64_t a = wid; a < n_nodes; a += nw) {
-    const int64_t e0 = off[a], e1 = off[a + 1];
-    const double cax = centre[3 * a], cay = centre[3 * a + 1], caz = centre[3 * a + 2];
+  constexpr int WPB = M2L_THREADS / WAVE;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[WPB][C::NS][C::SB];
+  __shared__ int32_t wid[WPB][C::WIN];
+  __shared__ uint8_t wmk[WPB][C::WIN];
+  const int lane = __lane_id(), w = threadIdx.x / WAVE;
+  const int t = lane >> 3, j = lane & 7;
+  // this lane's piece of each copy instruction: record slot ps (8 = padding) and piece pq
+  int ps[C::NI], pq[C::NI];
+#pragma unroll
+  for (int i = 0; i < C::NI; i++) {
+    const int f = WAVE * i + lane;
+    ps[i] = f < 8 * C::PC ? f / C::PC : 8;
+    pq[i] = f < 8 * C::PC ? f - (f / C::PC) * C::PC : 0;
+  }
+  for (int64_t pi = (int64_t)blockIdx.x * WPB + w; pi < n_parents;
+       pi += (int64_t)gridDim.x * WPB) {
+    // wave-uniform values are moved to scalar registers so that the loop
+    // conditions below are uniform branches
+    const int32_t par = uniform(parents[pi]);
+    const int nc = uniform((int)n_child[par]);
+    const int64_t ch = (int64_t)uniform(first_child[par]) + t;
+    double cx = 0.0, cy = 0.0, cz = 0.0;
+    if (t < nc) {
+      cx = centre[3 * ch];
+      cy = centre[3 * ch + 1];
+      cz = centre[3 * ch + 2];
+    }
+    const int64_t u0 = uniform(uoff[pi]), u1 = uniform(uoff[pi + 1]);
     T acc[K];
 #pragma unroll
     for (int k = 0; k < K; k++) acc[k] = (T)0;
-    for (int64_t e = e0 + lane; e < e1; e += WAVE) {
-      const int64_t b = src[e];
-      // the source's moments are loaded first; the derivative tensor, which
-      // needs only the centres, is built while they are in flight
-      const T* Mb = mpole + b * K;
-      T M[K];
+    for (int64_t w0 = u0; w0 < u1; w0 += C::WIN) {
+      const int n = (int)min((int64_t)C::WIN, u1 - w0);
+      const int nch = (n + 7) >> 3;
+      // id window, padded to whole chunks with (node 0, empty mask)
+      for (int e = lane; e < 8 * nch; e += WAVE) {
+        int32_t id = 0;
+        uint8_t mk = 0;
+        if (e < n) {
+          id = usrc[w0 + e];
+          mk = umask[w0 + e];
+        }
+        wid[w][e] = id;
+        wmk[w][e] = mk;
+      }
+      __builtin_amdgcn_wave_barrier();
+      // copy chunk c into ring stage c % NS; chunks past the end copy node 0's
+      // record into the free stage, so every step issues the same NI copies
+      auto issue = [&](int c) {
+        unsigned char* stage = ring[w][c % C::NS];
+        const int cc = min(c, nch - 1);
 #pragma unroll
-      for (int k = 0; k < K; k++) M[k] = Mb[k];
-      const T rx = (T)(cax - centre[3 * b]);
-      const T ry = (T)(cay - centre[3 * b + 1]);
-      const T rz = (T)(caz - centre[3 * b + 2]);
-      T D[K];
-      dtensor<T, P>(rx, ry, rz, D);
-      static_for<0, NT>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        acc[tabs<P>.tn[t]] += M[tabs<P>.tm[t]] * D[tabs<P>.tk[t]];
-      });
+        for (int i = 0; i < C::NI; i++) {
+          int64_t node = 0;
+          if (c < nch && ps[i] < 8) node = wid[w][8 * cc + ps[i]];
+          const unsigned char* g = mrec + node * C::RB + 16 * pq[i];
+          __builtin_amdgcn_global_load_lds((gvoid_t*)g, (lvoid_t*)(stage + i * WAVE * 16), 16, 0,
+                                           0);
+        }
+      };
+#pragma unroll
+      for (int c = 0; c < C::NS - 1; c++) issue(c);
+      for (int c = 0; c < nch; c++) {
+        issue(c + C::NS - 1);
+        // copies complete in issue order: at most WAIT newer ones may remain
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::WAIT) : "memory");
+        const unsigned char* rec = ring[w][c % C::NS] + j * C::RB;
+        const uint32_t m = wmk[w][8 * c + j];
+        if ((m >> t) & 1u) {
+          const double* cs = (const double*)(rec + C::CB);
+          const T rx = (T)(cx - cs[0]), ry = (T)(cy - cs[1]), rz = (T)(cz - cs[2]);
+          T D[K];
+          dtensor<T, P>(rx, ry, rz, D);
+          const T* Ms = (const T*)rec;
+          static_for<0, NT>([&](auto tc) {
+            constexpr int q = decltype(tc)::value;
+            acc[tabs<P>.tn[q]] += Ms[tabs<P>.tm[q]] * D[tabs<P>.tk[q]];
+          });
+        }
+        asm volatile("" ::: "memory");  // this stage is read before it is refilled
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // padding copies land before reuse
     }
-    T* La = local + a * K;
-    static_for<0, K>([&](auto nc) {
-      constexpr int n = decltype(nc)::value;
-      const T v = wave_sum(acc[n]);
-      if (lane == (n & (WAVE - 1))) La[n] = -v;  // G = 1: L = -sum
+    T* Lc = local + ch * K;
+    static_for<0, K>([&](auto nc_) {
+      constexpr int n = decltype(nc_)::value;
+      T x = acc[n];
+      x += __shfl_xor(x, 1, WAVE);
+      x += __shfl_xor(x, 2, WAVE);
+      x += __shfl_xor(x, 4, WAVE);
+      if (t < nc && (n & 7) == j) Lc[n] = -x;  // G = 1: L = -sum
     });
   }
 }
 
+// ---------------- transposed tails ----------------
+// A leaf's entries after its own ones, [off[a] + own[a], off[a + 1]), come from
+// deeper targets that accepted it; their lengths vary widely (0 to thousands),
+// so they are cut into tasks of at most TAIL_E entries.  A wave takes 8
+// consecutive tasks: lane l = 8 t + j walks entries j, j + 8, ... of task t, the
+// 8 lanes of a task are summed by a fixed butterfly and the task's partial
+// local is stored; a second kernel subtracts each leaf's task partials, in task
+// order, from its local.
+template <typename T, int P>
+__global__ void __launch_bounds__(M2L_THREADS)
+    k_m2l_tail(int64_t n_tasks, const TailTask* __restrict__ tasks,
+               const int32_t* __restrict__ leaves, const int32_t* __restrict__ src,
+               const double* __restrict__ centre, const unsigned char* __restrict__ mrec,
+               T* __restrict__ part) {
+  constexpr int K = Tabs<P>::K;
+  constexpr int NT = Tabs<P>::NT;
+  constexpr int RB = mrec_bytes(K, sizeof(T));
+  constexpr int CB = mrec_centre_byte(K, sizeof(T));
+  const int lane = __lane_id();
+  const int t = lane >> 3, j = lane & 7;
+  const int64_t wid = (int64_t)blockIdx.x * (M2L_THREADS / WAVE) + threadIdx.x / WAVE;
+  const int64_t nw = (int64_t)gridDim.x * (M2L_THREADS / WAVE);
+  for (int64_t g = wid; 8 * g < n_tasks; g += nw) {
+    const int64_t ti = 8 * g + t;
+    int n = 0;
+    int64_t e0 = 0, a = 0;
+    if (ti < n_tasks) {
+      const TailTask tk = tasks[ti];
+      n = tk.n;
+      e0 = tk.e0;
+      a = leaves[tk.li];
+    }
+    const double ax = ti < n_tasks ? centre[3 * a] : 0.0;
+    const double ay = ti < n_tasks ? centre[3 * a + 1] : 0.0;
+    const double az = ti < n_tasks ? centre[3 * a + 2] : 0.0;
+    T acc[K];
+#pragma unroll
+    for (int k = 0; k < K; k++) acc[k] = (T)0;
+    for (int e = j; e < n; e += 8) {
+      const int64_t b = src[e0 + e];
+      const unsigned char* rb = mrec + b * RB;
+      const T* Mb = (const T*)rb;
+      T M[K];
+#pragma unroll
+      for (int k = 0; k < K; k++) M[k] = Mb[k];
+      const double* cb = (const double*)(rb + CB);
+      const T rx = (T)(ax - cb[0]), ry = (T)(ay - cb[1]), rz = (T)(az - cb[2]);
+      T D[K];
+      dtensor<T, P>(rx, ry, rz, D);
+      static_for<0, NT>([&](auto tc) {
+        constexpr int q = decltype(tc)::value;
+        acc[tabs<P>.tn[q]] += M[tabs<P>.tm[q]] * D[tabs<P>.tk[q]];
+      });
+    }
+    T* Pt = part + ti * K;
+    static_for<0, K>([&](auto nc) {
+      constexpr int q = decltype(nc)::value;
+      T x = acc[q];
+      x += __shfl_xor(x, 1, WAVE);
+      x += __shfl_xor(x, 2, WAVE);
+      x += __shfl_xor(x, 4, WAVE);
+      if (ti < n_tasks && (q & 7) == j) Pt[q] = x;
+    });
+  }
+}
+
+// thread per (leaf, coefficient): L -= sum of the leaf's task partials, in order
 template <typename T>
-static void m2l_dispatch(int order, unsigned g, hipStream_t st, int64_t n_nodes, const int64_t* off,
-                         const int32_t* src, const double* centre, const T* mpole, T* local) {
+__global__ void k_m2l_tail_combine(int64_t n_leaves, int K, const int32_t* __restrict__ leaves,
+                                   const int64_t* __restrict__ toff, const T* __restrict__ part,
+                                   T* __restrict__ local) {
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (g >= n_leaves * K) return;
+  const int64_t li = g / K;
+  const int n = (int)(g - li * K);
+  const int64_t t0 = toff[li], t1 = toff[li + 1];
+  if (t0 == t1) return;
+  T s = (T)0;
+  for (int64_t q = t0; q < t1; q++) s += part[q * K + n];
+  local[(int64_t)leaves[li] * K + n] -= s;
+}
+
+__global__ void k_tail_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                             const int32_t* own, int64_t* cnt) {
+  const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (li >= n_leaves) return;
+  const int64_t a = leaves[li];
+  const int64_t len = off[a + 1] - off[a] - own[a];
+  cnt[li] = (len + TAIL_E - 1) / TAIL_E;
+}
+
+__global__ void k_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                            const int32_t* own, const int64_t* toff, TailTask* tasks) {
+  const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (li >= n_leaves) return;
+  const int64_t a = leaves[li];
+  const int64_t e0 = off[a] + own[a], e1 = off[a + 1];
+  int64_t q = toff[li];
+  for (int64_t e = e0; e < e1; e += TAIL_E, q++)
+    tasks[q] = TailTask{e, (int32_t)min((int64_t)TAIL_E, e1 - e), (int32_t)li};
+}
+
+hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                             const int32_t* own, int64_t* cnt, hipStream_t st) {
+  if (n_leaves <= 0) return hipSuccess;
+  k_tail_count<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, off, own,
+                                                                    cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                            const int32_t* own, const int64_t* toff, TailTask* tasks,
+                            hipStream_t st) {
+  if (n_leaves <= 0) return hipSuccess;
+  k_tail_fill<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, off, own,
+                                                                   toff, tasks);
+  return hipGetLastError();
+}
+
+static unsigned m2l_grid(int64_t waves) {
+  int64_t blocks = (waves + (M2L_THREADS / WAVE) - 1) / (M2L_THREADS / WAVE);
+  if (blocks > 65535) blocks = 65535;
+  if (blocks < 1) blocks = 1;
+  return (unsigned)blocks;
+}
+
+template <typename T>
+static void m2l_dispatch(int order, hipStream_t st, const M2LArgs& a) {
+  const unsigned gs = m2l_grid(a.n_parents), gt = m2l_grid((a.n_tasks + 7) / 8);
+  const unsigned char* rec = (const unsigned char*)a.mrec;
   switch (order) {
-#define M2L_CASE(P) \
-  case P:           \
-    k_m2l<T, P><<<g, M2L_THREADS, 0, st>>>(n_nodes, off, src, centre, mpole, local); \
+#define M2L_CASE(P)                                                                          \
+  case P:                                                                                    \
+    if (a.n_parents > 0)                                                                     \
+      k_m2l_sib<T, P><<<gs, M2L_THREADS, 0, st>>>(a.n_parents, a.parents, a.first_child,      \
+                                                  a.n_child, a.uoff, a.usrc, a.umask,        \
+                                                  a.centre, rec, (T*)a.local);               \
+    if (a.n_tasks > 0)                                                                       \
+      k_m2l_tail<T, P><<<gt, M2L_THREADS, 0, st>>>(a.n_tasks, a.tasks, a.leaves, a.src,       \
+                                                   a.centre, rec, (T*)a.part);               \
     break;
     M2L_CASE(0) M2L_CASE(1) M2L_CASE(2) M2L_CASE(3) M2L_CASE(4)
     M2L_CASE(5) M2L_CASE(6) M2L_CASE(7) M2L_CASE(8)
@@ -127,21 +348,24 @@ static void m2l_dispatch(int order, unsigned g, hipStream_t st, int64_t n_nodes,
     default:
       break;
   }
+  if (a.n_tasks > 0) {
+    const int K = ncoef(order);
+    const unsigned g = (unsigned)((a.n_leaves * K + 255) / 256);
+    k_m2l_tail_combine<T><<<g, 256, 0, st>>>(a.n_leaves, K, a.leaves, a.toff,
+                                             (const T*)a.part, (T*)a.local);
+  }
 }
 
-hipError_t launch_m2l(int dtype, int order, int64_t n_nodes, const int64_t* off,
-                      const int32_t* src, const double* centre, const void* mpole, void* local,
-                      hipStream_t st) {
-  int64_t blocks = (n_nodes + (M2L_THREADS / WAVE) - 1) / (M2L_THREADS / WAVE);
-  if (blocks > 65535) blocks = 65535;
-  if (blocks < 1) blocks = 1;
-  unsigned g = (unsigned)blocks;
+hipError_t launch_m2l(int dtype, int order, const M2LArgs& a, hipStream_t st) {
+  if (a.n_nodes <= 0) return hipSuccess;
+  // the root is nobody's child: its local (no far-field terms) is cleared
+  const size_t kb = (size_t)ncoef(order) * (dtype == FMM_F64 ? 8 : 4);
+  hipError_t e = launch_fill_zero(a.local, kb, st);
+  if (e != hipSuccess) return e;
   if (dtype == FMM_F64)
-    m2l_dispatch<double>(order, g, st, n_nodes, off, src, centre, (const double*)mpole,
-                         (double*)local);
+    m2l_dispatch<double>(order, st, a);
   else
-    m2l_dispatch<float>(order, g, st, n_nodes, off, src, centre, (const float*)mpole,
-                        (float*)local);
+    m2l_dispatch<float>(order, st, a);
   return hipGetLastError();
 }
 

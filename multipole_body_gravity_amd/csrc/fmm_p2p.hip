@@ -96,6 +96,10 @@ __device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp
   fz -= mr3 * dz;
 }
 
+// Lane layout for a chunk of tc <= 64 targets: lane l serves target l % tc
+// and source slice l / tc; with nsl = ceil(64 / tc) slices the last slice may
+// cover only the first 64 - (nsl-1) tc targets, so a target has ns(t) = nsl
+// or nsl - 1 slices, and slice s of target t takes sources s, s + ns(t), ...
 template <typename T>
 __global__ void __launch_bounds__(P2P_THREADS)
     k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
@@ -114,8 +118,9 @@ __global__ void __launch_bounds__(P2P_THREADS)
     const int32_t tb = begin[a], tn = count[a];
     for (int32_t t0 = 0; t0 < tn; t0 += WAVE) {
       const int tc = min(WAVE, tn - t0);
-      const int nsl = WAVE / tc;
+      const int nsl = (WAVE + tc - 1) / tc;
       const int t = lane % tc, sl = lane / tc;
+      const int ns = (t < WAVE - (nsl - 1) * tc) ? nsl : nsl - 1;  // slices of target t
       const int32_t i = tb + t0 + t;
       const P4<T> pi = pts[i];
       T fp = 0, fx = 0, fy = 0, fz = 0;
@@ -150,13 +155,12 @@ __global__ void __launch_bounds__(P2P_THREADS)
           }
           __builtin_amdgcn_wave_barrier();
           const int nv = min(TILE, tot - q0);
-          if (sl < nsl)
-            for (int s = sl; s < nv; s += nsl) pair_acc(pi, tile[w][s], fp, fx, fy, fz);
+          for (int s = sl; s < nv; s += ns) pair_acc(pi, tile[w][s], fp, fx, fy, fz);
           __builtin_amdgcn_wave_barrier();
         }
       }
-      if (__ballot(self) != 0ull && sl < nsl) {
-        for (int32_t s = sl; s < tn; s += nsl) {
+      if (__ballot(self) != 0ull) {
+        for (int32_t s = sl; s < tn; s += ns) {
           if (tb + s == i) continue;  // self term omitted
           pair_acc(pi, pts[tb + s], fp, fx, fy, fz);
         }
@@ -168,11 +172,11 @@ __global__ void __launch_bounds__(P2P_THREADS)
       __builtin_amdgcn_wave_barrier();
       if (lane < tc) {
         T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-        for (int s = 0; s < nsl; s++) {
-          s0 += red[w][0][s * tc + lane];
-          s1 += red[w][1][s * tc + lane];
-          s2 += red[w][2][s * tc + lane];
-          s3 += red[w][3][s * tc + lane];
+        for (int q = 0; q < ns; q++) {
+          s0 += red[w][0][q * tc + lane];
+          s1 += red[w][1][q * tc + lane];
+          s2 += red[w][2][q * tc + lane];
+          s3 += red[w][3][q * tc + lane];
         }
         if (task.part < 0) {
           const P4<T> f = far[i];

@@ -336,13 +336,74 @@ __global__ void k_walk_offsets(int64_t n, const int32_t* om, const int32_t* op, 
 
 __global__ void k_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
                                    const int64_t* task_total, const int64_t* part_total,
+                                   const int64_t* union_total, const int64_t* tail_total,
                                    Control* c) {
   if (threadIdx.x == 0) {
     c->n_m2l = *m2l_total;
     c->n_p2p = *p2p_total;
     c->n_p2p_tasks = *task_total;
     c->n_p2p_part = *part_total;
+    c->n_union = *union_total;
+    c->n_tail_tasks = *tail_total;
   }
+}
+
+// The children of a non-leaf P all receive the same candidates (P's carry,
+// expanded), so their own M2L sources are the candidates accepted by at least
+// one child.  One wave per parent enumerates them once, in ascending order,
+// and keeps each accepted candidate with a mask of the accepting children.
+__global__ void __launch_bounds__(WK_THREADS)
+    k_union(int pass, WalkArgs a, const int32_t* parents, int64_t n_parents, int64_t* cnt_off,
+            int32_t* usrc, uint8_t* umask) {
+  const uint64_t lt = lanemask_lt();
+  const int lane = __lane_id();
+  for (int64_t pi = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; pi < n_parents;
+       pi += (int64_t)gridDim.x * WK_WAVES) {
+    const int32_t P = parents[pi];
+    const int nc = a.n_child[P];
+    const int32_t fc = a.first_child[P];
+    int4 mine = make_int4(0, 0, 0, 0);
+    if (lane < nc) mine = a.geo[fc + lane];
+    int4 cg[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      cg[t].x = __shfl(mine.x, t, WAVE);
+      cg[t].y = __shfl(mine.y, t, WAVE);
+      cg[t].z = __shfl(mine.z, t, WAVE);
+      cg[t].w = __shfl(mine.w, t, WAVE);
+    }
+    const int64_t g0 = a.carry_off[P];
+    const int gc = a.carry_cnt[P];
+    int64_t base = pass == 2 ? cnt_off[pi] : 0;
+    int64_t n = 0;
+    for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int) {
+      uint32_t m = 0;
+      if (act) {
+        const int4 g = a.geo[c];
+#pragma unroll
+        for (int t = 0; t < 8; t++)
+          if (t < nc && accept_pair(cg[t], g, a.t2)) m |= 1u << t;
+      }
+      const uint64_t b = __ballot(m != 0);
+      if (pass == 2 && m != 0) {
+        const int64_t o = base + n + __popcll(b & lt);
+        usrc[o] = c;
+        umask[o] = (uint8_t)m;
+      }
+      n += __popcll(b);
+    });
+    if (pass == 1 && lane == 0) cnt_off[pi] = n;
+  }
+}
+
+hipError_t launch_union(int pass, const WalkArgs& a, const int32_t* parents, int64_t n_parents,
+                        int64_t* ucount_or_off, int32_t* usrc, uint8_t* umask, hipStream_t st) {
+  if (n_parents <= 0) return hipSuccess;
+  int64_t blocks = (n_parents + WK_WAVES - 1) / WK_WAVES;
+  if (blocks > 16384) blocks = 16384;
+  k_union<<<(unsigned)blocks, WK_THREADS, 0, st>>>(pass, a, parents, n_parents, ucount_or_off,
+                                                  usrc, umask);
+  return hipGetLastError();
 }
 
 // Sorted transposed keys -> after each target's own entries.
@@ -399,8 +460,10 @@ hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own_m2l, const in
 }
 hipError_t launch_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
                                    const int64_t* task_total, const int64_t* part_total,
+                                   const int64_t* union_total, const int64_t* tail_total,
                                    Control* ctrl, hipStream_t st) {
-  k_walk_copy_totals<<<1, 64, 0, st>>>(m2l_total, p2p_total, task_total, part_total, ctrl);
+  k_walk_copy_totals<<<1, 64, 0, st>>>(m2l_total, p2p_total, task_total, part_total, union_total,
+                                       tail_total, ctrl);
   return hipGetLastError();
 }
 hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
