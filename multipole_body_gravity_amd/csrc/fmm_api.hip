@@ -91,23 +91,34 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   const int depth = p->depth;
   const int64_t nn = p->n_nodes;
   const int64_t nl = p->n_leaves;
-  TRY(grow(p->carry_off, (size_t)nn * 8));
-  TRY(grow(p->carry_cnt, (size_t)nn * 4));
-  TRY(grow(p->own_m2l, (size_t)nn * 4));
-  TRY(grow(p->own_p2p, (size_t)nn * 4));
+  const int64_t np = nn - nl;
+  for (DBuf* b : {&p->cu_off, &p->u_off, &p->pu_off, &p->trm_off, &p->trp_off})
+    TRY(grow(*b, (size_t)nn * 8));
+  for (DBuf* b : {&p->cu_cnt, &p->u_cnt, &p->pu_cnt, &p->own_m2l, &p->own_p2p})
+    TRY(grow(*b, (size_t)nn * 4));
+  TRY(grow(p->rootgen, 8));
   TRY(grow(p->tr_cnt_m2l, (size_t)2 * nn * 4));  // [kind][node]
   TRY(grow(p->tr_start_m2l, (size_t)2 * nn * 8));
-  TRY(grow(p->tot_m2l, (size_t)(nn + 1) * 8));
   TRY(grow(p->tot_p2p, (size_t)(nn + 1) * 8));
-  TRY(grow(p->m2l_off, (size_t)(nn + 1) * 8));
   TRY(grow(p->p2p_off, (size_t)(nn + 1) * 8));
   TRY(grow(p->p2p_toff, (size_t)(nl + 1) * 8));
   TRY(grow(p->p2p_poff, (size_t)(nl + 1) * 8));
+  TRY(grow(p->tail_toff, (size_t)(nl + 1) * 8));
   TRY(grow(p->scan_tmp, scan_tmp_bytes(std::max(nn, nl) + 1)));
+  // the parents of level l (non-leaf nodes, id order) are parents[pbeg[l] .. pbeg[l + 1])
+  p->n_parents = np;
+  p->pbeg[0] = 0;
+  for (int l = 0; l <= MAX_LEVELS; l++) {
+    const int64_t cnt = l < MAX_LEVELS ? (p->level_off[l + 1] - p->level_off[l]) : 0;
+    const int64_t lv = l < MAX_LEVELS ? p->leaves_at_level[l] : 0;
+    p->pbeg[l + 1] = p->pbeg[l] + (cnt - lv);
+  }
+  if (p->pbeg[MAX_LEVELS + 1] != np) return FMM_ERR_HIP;
   // first guesses for the pools (regrown from the measured use on overflow)
-  const int64_t guess[3] = {96 * nn + 4096, 24 * nn + 4096, 12 * nn + 4096};
-  for (int k = 0; k < 3; k++)
-    p->shard_cap[k] = std::max<int64_t>(p->shard_cap[k], guess[k] / POOL_SHARDS + 64);
+  const int64_t guess[N_POOLS] = {48 * nn + 4096, 64 * nn + 4096, 32 * nn + 4096, 48 * nn + 4096,
+                                  32 * nn + 4096};
+  for (int k = 0; k < N_POOLS; k++)
+    p->shard_cap[k] = std::max<int64_t>(p->shard_cap[k], std::max<int64_t>(guess[k] / POOL_SHARDS, 2048));
 
   WalkArgs a{};
   a.geo = P<int4>(p->ngeo);
@@ -115,62 +126,67 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   a.n_child = P<uint8_t>(p->nnchild);
   a.parent = P<int32_t>(p->nparent);
   a.t2 = p->t2;
-  a.carry_off = P<int64_t>(p->carry_off);
-  a.carry_cnt = P<int32_t>(p->carry_cnt);
+  a.parents = P<int32_t>(p->parents);
+  a.cu_off = P<int64_t>(p->cu_off);
+  a.u_off = P<int64_t>(p->u_off);
+  a.pu_off = P<int64_t>(p->pu_off);
+  a.trm_off = P<int64_t>(p->trm_off);
+  a.trp_off = P<int64_t>(p->trp_off);
+  a.cu_cnt = P<int32_t>(p->cu_cnt);
+  a.u_cnt = P<int32_t>(p->u_cnt);
+  a.pu_cnt = P<int32_t>(p->pu_cnt);
   a.own_m2l = P<int32_t>(p->own_m2l);
   a.own_p2p = P<int32_t>(p->own_p2p);
-  a.m2l_off = P<int64_t>(p->m2l_off);
-  a.p2p_off = P<int64_t>(p->p2p_off);
+  a.rootgen = P<uint64_t>(p->rootgen);
   a.key_shift = bits_for(nn);
+  p->key_shift = a.key_shift;
   const int kind_bit = 2 * a.key_shift;
   a.ctrl = P<Control>(p->ctrl);
   Control* dctrl = P<Control>(p->ctrl);
   const int root_leaf = (depth == 0) ? 1 : 0;
-  auto step_args = [&](int s) {
-    WalkArgs b = a;
-    b.step = s;
-    b.lvl_begin = p->level_off[s];
-    b.lvl_count = p->level_off[s + 1] - p->level_off[s];
-    return b;
-  };
   int32_t* leaves = P<int32_t>(p->leaves);
   int64_t* toff = P<int64_t>(p->p2p_toff);
   int64_t* poff = P<int64_t>(p->p2p_poff);
 
   p->walk_retries = 0;
   for (;;) {
-    TRY(grow(p->carry, (size_t)p->shard_cap[0] * POOL_SHARDS * 4));
-    TRY(grow(p->trm_pool, (size_t)p->shard_cap[1] * POOL_SHARDS * 8));
-    TRY(grow(p->trp_pool, (size_t)p->shard_cap[2] * POOL_SHARDS * 8));
-    a.carry = Pool<int32_t>{P<int32_t>(p->carry), p->shard_cap[0], dctrl->pool_used[0]};
-    a.trm = Pool<uint64_t>{P<uint64_t>(p->trm_pool), p->shard_cap[1], dctrl->pool_used[1]};
-    a.trp = Pool<uint64_t>{P<uint64_t>(p->trp_pool), p->shard_cap[2], dctrl->pool_used[2]};
-    TRY_HIP(launch_walk_reset(dctrl, st));
-    TRY_HIP(launch_walk_root(1, root_leaf, step_args(0), st));
-    for (int s = 1; s <= depth; s++) TRY_HIP(launch_walk_pass1(step_args(s), st));
+    for (int k = 0; k < N_POOLS; k++)
+      TRY(grow(p->pool[k], (size_t)p->shard_cap[k] * POOL_SHARDS * 8));
+    Pool<uint64_t>* pools[N_POOLS] = {&a.cu, &a.u, &a.pu, &a.trm, &a.trp};
+    for (int k = 0; k < N_POOLS; k++)
+      *pools[k] = Pool<uint64_t>{P<uint64_t>(p->pool[k]), p->shard_cap[k], dctrl->pool_used[k]};
+    TRY_HIP(launch_walk_reset(dctrl, P<uint64_t>(p->rootgen), st));
+    TRY_HIP(launch_walk_root(1, root_leaf, a.own_m2l, a.own_p2p, nullptr, nullptr, st));
+    for (int l = 0; l < depth; l++) {
+      a.pbeg = p->pbeg[l];
+      a.pcnt = p->pbeg[l + 1] - p->pbeg[l];
+      TRY_HIP(launch_walk(1, a, st));
+      TRY_HIP(launch_walk(2, a, st));
+    }
     TRY_HIP(launch_walk_own_totals(nn, a.own_m2l, a.own_p2p, dctrl, st));
     TRY(sync_ctrl(p, st));
     if (!p->ctrl_host->pool_overflow) break;
-    if (++p->walk_retries > 4) return FMM_ERR_OOM;
-    for (int k = 0; k < 3; k++) {
+    // the levels after the first overflow did not run: grow at least twofold
+    if (++p->walk_retries > 12) return FMM_ERR_OOM;
+    for (int k = 0; k < N_POOLS; k++) {
       int64_t mx = 0;
       for (int sh = 0; sh < POOL_SHARDS; sh++) mx = std::max(mx, p->ctrl_host->pool_used[k][sh]);
-      if (mx > p->shard_cap[k]) p->shard_cap[k] = mx + mx / 2 + 64;
+      if (mx > p->shard_cap[k]) p->shard_cap[k] = std::max(mx + mx / 2, 2 * p->shard_cap[k]);
     }
   }
   const Control& c = *p->ctrl_host;
-  int64_t ntm = 0, ntp = 0;
+  int64_t ntm = 0, ntp = 0, nu = 0;
   for (int sh = 0; sh < POOL_SHARDS; sh++) {
-    ntm += c.pool_used[1][sh];
-    ntp += c.pool_used[2][sh];
+    ntm += c.pool_used[POOL_TRM][sh];
+    ntp += c.pool_used[POOL_TRP][sh];
+    nu += c.pool_used[POOL_U][sh];
   }
   const int64_t ntr = ntm + ntp;
+  p->n_union = nu;
   p->n_m2l = c.own_m2l_total + ntm;
   p->n_p2p = c.own_p2p_total + ntp;
-  TRY(grow(p->m2l_src, (size_t)p->n_m2l * 4));
-  TRY(grow(p->p2p_src, (size_t)p->n_p2p * 4));
-  a.m2l_src = P<int32_t>(p->m2l_src);
-  a.p2p_src = P<int32_t>(p->p2p_src);
+  p->n_tr = ntr;
+  p->m2l_lists_ready = false;
 
   // transposed entries: dense copy, sort by (kind, target, source), run lengths
   int32_t* tr_cnt = P<int32_t>(p->tr_cnt_m2l);
@@ -193,64 +209,67 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     sorted = in_alt ? P<uint64_t>(p->tr_keys_alt) : P<uint64_t>(p->tr_keys);
     TRY_HIP(launch_tr_runs(sorted, ntr, a.key_shift, kind_bit, nn, tr_start, tr_cnt, st));
   }
-  TRY_HIP(launch_walk_offsets(nn, a.own_m2l, a.own_p2p, tr_cnt, tr_cnt + nn,
-                              P<int64_t>(p->tot_m2l), P<int64_t>(p->tot_p2p), st));
-  TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_m2l), P<int64_t>(p->m2l_off), nn,
-                             P<int64_t>(p->m2l_off) + nn, p->scan_tmp.p, st));
-  TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_p2p), P<int64_t>(p->p2p_off), nn,
-                             P<int64_t>(p->p2p_off) + nn, p->scan_tmp.p, st));
-  TRY_HIP(launch_walk_root(2, root_leaf, step_args(0), st));
-  for (int s = 1; s <= depth; s++) TRY_HIP(launch_walk_pass2(step_args(s), st));
-  if (ntr > 0)
-    TRY_HIP(launch_tr_scatter(sorted, ntr, a.key_shift, kind_bit, nn, P<int64_t>(p->m2l_off),
-                              a.own_m2l, tr_start, a.m2l_src, P<int64_t>(p->p2p_off), a.own_p2p,
-                              tr_start + nn, a.p2p_src, st));
+  p->tr_sorted = sorted;
 
-  // sibling unions of the children's own M2L sources (counted here, written
-  // once their total is known)
-  const int64_t np = nn - nl;
-  p->n_parents = np;
-  TRY(grow(p->uoff, (size_t)(np + 1) * 8));
-  int64_t* uoff = P<int64_t>(p->uoff);
-  const int32_t* parents = P<int32_t>(p->parents);
-  if (np > 0) {
-    TRY_HIP(launch_union(1, a, parents, np, uoff, nullptr, nullptr, st));
-    TRY_HIP(scan_exclusive_i64(uoff, uoff, np, uoff + np, p->scan_tmp.p, st));
-  } else {
-    TRY_HIP(launch_fill_zero(uoff, 8, st));
-  }
+  // P2P lists: own entries (from the parents' P2P unions) then transposed ones
+  int64_t* p2p_off = P<int64_t>(p->p2p_off);
+  TRY_HIP(launch_walk_offsets(nn, a.own_p2p, tr_cnt + nn, P<int64_t>(p->tot_p2p), st));
+  TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_p2p), p2p_off, nn, p2p_off + nn, p->scan_tmp.p, st));
+  TRY(grow(p->p2p_src, (size_t)std::max<int64_t>(p->n_p2p, 1) * 4));
+  int32_t* p2p_src = P<int32_t>(p->p2p_src);
+  TRY_HIP(launch_union_scatter(a.parents, np, a.first_child, a.n_child, a.pu.data, a.pu_off,
+                               a.pu_cnt, p2p_off, p2p_src, st));
+  TRY_HIP(launch_walk_root(2, root_leaf, a.own_m2l, a.own_p2p, p2p_off, p2p_src, st));
+  if (ntr > 0)
+    TRY_HIP(launch_tr_scatter(sorted, ntr, a.key_shift, kind_bit, 1, nn, p2p_off, a.own_p2p,
+                              tr_start + nn, p2p_src, st));
 
   // near-field tasks
-  TRY_HIP(launch_p2p_task_count(leaves, nl, P<int64_t>(p->p2p_off), P<int32_t>(p->ncount), toff,
-                                poff, st));
+  TRY_HIP(launch_p2p_task_count(leaves, nl, p2p_off, P<int32_t>(p->ncount), toff, poff, st));
   TRY_HIP(scan_exclusive_i64(toff, toff, nl, toff + nl, p->scan_tmp.p, st));
   TRY_HIP(scan_exclusive_i64(poff, poff, nl, poff + nl, p->scan_tmp.p, st));
   // transposed-tail M2L tasks
-  TRY(grow(p->tail_toff, (size_t)(nl + 1) * 8));
   int64_t* ttoff = P<int64_t>(p->tail_toff);
-  TRY_HIP(launch_tail_count(leaves, nl, P<int64_t>(p->m2l_off), a.own_m2l, ttoff, st));
+  TRY_HIP(launch_tail_count(leaves, nl, tr_cnt, ttoff, st));
   TRY_HIP(scan_exclusive_i64(ttoff, ttoff, nl, ttoff + nl, p->scan_tmp.p, st));
-  TRY_HIP(launch_walk_copy_totals(P<int64_t>(p->m2l_off) + nn, P<int64_t>(p->p2p_off) + nn,
-                                  toff + nl, poff + nl, uoff + np, ttoff + nl, dctrl, st));
+  TRY_HIP(launch_walk_copy_totals(p2p_off + nn, toff + nl, poff + nl, ttoff + nl, dctrl, st));
   TRY(sync_ctrl(p, st));
-  if (p->ctrl_host->n_m2l != p->n_m2l || p->ctrl_host->n_p2p != p->n_p2p) return FMM_ERR_HIP;
-  p->n_union = p->ctrl_host->n_union;
-  TRY(grow(p->usrc, (size_t)std::max<int64_t>(p->n_union, 1) * 4));
-  TRY(grow(p->umask, (size_t)std::max<int64_t>(p->n_union, 1)));
-  if (np > 0)
-    TRY_HIP(launch_union(2, a, parents, np, uoff, P<int32_t>(p->usrc), P<uint8_t>(p->umask), st));
+  if (p->ctrl_host->n_p2p != p->n_p2p) return FMM_ERR_HIP;
+  p->n_p2p_tasks = p->ctrl_host->n_p2p_tasks;
+  p->n_p2p_part = p->ctrl_host->n_p2p_part;
   p->n_tail_tasks = p->ctrl_host->n_tail_tasks;
+  TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
+  TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
+  TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, p2p_off,
+                               P<int32_t>(p->ncount), p->p2p_task.p, st));
   TRY(grow(p->tail_task, (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * sizeof(TailTask)));
   TRY(grow(p->tail_part,
            (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * p->K * wbytes(p->dtype)));
-  TRY_HIP(launch_tail_fill(leaves, nl, P<int64_t>(p->m2l_off), a.own_m2l, ttoff,
-                           P<TailTask>(p->tail_task), st));
-  p->n_p2p_tasks = p->ctrl_host->n_p2p_tasks;
-  p->n_p2p_part = p->ctrl_host->n_p2p_part;
-  TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
-  TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
-  TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, P<int64_t>(p->p2p_off),
-                               P<int32_t>(p->ncount), p->p2p_task.p, st));
+  TRY_HIP(launch_tail_fill(leaves, nl, tr_start, tr_cnt, ttoff, P<TailTask>(p->tail_task), st));
+  return FMM_OK;
+}
+
+// Per-target M2L lists (own entries from the parents' M2L unions, then the
+// transposed tail), built only when they are asked for.
+int materialize_m2l_lists(fmm_plan_t p, hipStream_t st) {
+  if (p->m2l_lists_ready) return FMM_OK;
+  const int64_t nn = p->n_nodes;
+  TRY(grow(p->tot_m2l, (size_t)(nn + 1) * 8));
+  TRY(grow(p->m2l_off, (size_t)(nn + 1) * 8));
+  TRY(grow(p->m2l_src, (size_t)std::max<int64_t>(p->n_m2l, 1) * 4));
+  int64_t* off = P<int64_t>(p->m2l_off);
+  const int32_t* own = P<int32_t>(p->own_m2l);
+  TRY_HIP(launch_walk_offsets(nn, own, P<int32_t>(p->tr_cnt_m2l), P<int64_t>(p->tot_m2l), st));
+  TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_m2l), off, nn, off + nn, p->scan_tmp.p, st));
+  TRY_HIP(launch_union_scatter(P<int32_t>(p->parents), p->n_parents, P<int32_t>(p->nfirst),
+                               P<uint8_t>(p->nnchild), P<uint64_t>(p->pool[POOL_U]),
+                               P<int64_t>(p->u_off), P<int32_t>(p->u_cnt), off,
+                               P<int32_t>(p->m2l_src), st));
+  if (p->n_tr > 0)
+    TRY_HIP(launch_tr_scatter(p->tr_sorted, p->n_tr, p->key_shift, 2 * p->key_shift, 0, nn, off,
+                              own, P<int64_t>(p->tr_start_m2l), P<int32_t>(p->m2l_src), st));
+  TRY_HIP(hipStreamSynchronize(st));
+  p->m2l_lists_ready = true;
   return FMM_OK;
 }
 
@@ -318,18 +337,23 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
 int fmm_destroy(fmm_plan_t p) {
   if (!p) return FMM_ERR_ARG;
   (void)hipDeviceSynchronize();
-  DBuf* bufs[] = {&p->keys, &p->keys_alt, &p->idx, &p->idx_alt, &p->pts, &p->far, &p->perm_inv,
-                  &p->lcp, &p->wlev, &p->wtmp, &p->leaf_level, &p->leaf_of, &p->radix_hist,
-                  &p->scan_tmp, &p->root, &p->ctrl, &p->bbox_part, &p->nlevel, &p->nprefix,
-                  &p->nbegin, &p->ncount, &p->nparent, &p->nfirst, &p->nnchild, &p->ncentre,
-                  &p->nq, &p->ngeo, &p->leaves, &p->lvl_blkcnt, &p->mpole, &p->local, &p->carry,
-                  &p->trm_pool, &p->trp_pool, &p->carry_off, &p->carry_cnt, &p->own_m2l,
-                  &p->own_p2p, &p->tr_cnt_m2l, &p->tr_cnt_p2p, &p->tr_start_m2l,
-                  &p->tr_start_p2p, &p->tr_keys, &p->tr_keys_alt, &p->tr_vals,
-                  &p->tr_vals_alt, &p->m2l_off, &p->m2l_src, &p->p2p_off, &p->p2p_src,
-                  &p->p2p_task, &p->p2p_part, &p->p2p_toff, &p->p2p_poff, &p->tot_m2l,
-                  &p->tot_p2p,  &p->parents,  &p->uoff,    &p->usrc,    &p->umask,
-                  &p->tail_toff, &p->tail_task, &p->tail_part};
+  DBuf* bufs[] = {&p->keys,       &p->keys_alt,    &p->idx,         &p->idx_alt,
+                  &p->pts,        &p->far,         &p->perm_inv,    &p->lcp,
+                  &p->wlev,       &p->wtmp,        &p->leaf_level,  &p->leaf_of,
+                  &p->radix_hist, &p->scan_tmp,    &p->root,        &p->ctrl,
+                  &p->bbox_part,  &p->nlevel,      &p->nprefix,     &p->nbegin,
+                  &p->ncount,     &p->nparent,     &p->nfirst,      &p->nnchild,
+                  &p->ncentre,    &p->nq,          &p->ngeo,        &p->leaves,
+                  &p->lvl_blkcnt, &p->mpole,       &p->local,       &p->pool[0],
+                  &p->pool[1],    &p->pool[2],     &p->pool[3],     &p->pool[4],
+                  &p->cu_off,     &p->cu_cnt,      &p->u_off,       &p->u_cnt,
+                  &p->pu_off,     &p->pu_cnt,      &p->trm_off,     &p->trp_off,
+                  &p->own_m2l,    &p->own_p2p,     &p->rootgen,     &p->tr_cnt_m2l,
+                  &p->tr_start_m2l, &p->tr_keys,   &p->tr_keys_alt, &p->tr_vals,
+                  &p->tr_vals_alt, &p->m2l_off,    &p->m2l_src,     &p->p2p_off,
+                  &p->p2p_src,    &p->p2p_task,    &p->p2p_part,    &p->p2p_toff,
+                  &p->p2p_poff,   &p->tot_m2l,     &p->tot_p2p,     &p->parents,
+                  &p->tail_toff,  &p->tail_task,   &p->tail_part};
   for (DBuf* b : bufs) release(*b);
   if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);
   for (int i = 0; i < 2 * FMM_N_STAGES; i++)
@@ -446,15 +470,16 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   ma.n_parents = p->n_parents;
   ma.first_child = P<int32_t>(p->nfirst);
   ma.n_child = P<uint8_t>(p->nnchild);
-  ma.uoff = P<int64_t>(p->uoff);
-  ma.usrc = P<int32_t>(p->usrc);
-  ma.umask = P<uint8_t>(p->umask);
+  ma.upool = P<uint64_t>(p->pool[POOL_U]);
+  ma.u_off = P<int64_t>(p->u_off);
+  ma.u_cnt = P<int32_t>(p->u_cnt);
   ma.leaves = leaves;
   ma.n_leaves = p->n_leaves;
   ma.tasks = P<TailTask>(p->tail_task);
   ma.n_tasks = p->n_tail_tasks;
   ma.toff = P<int64_t>(p->tail_toff);
-  ma.src = P<int32_t>(p->m2l_src);
+  ma.keys = p->tr_sorted;
+  ma.src_mask = (1ull << p->key_shift) - 1ull;
   ma.centre = centre;
   ma.mrec = p->mpole.p;
   ma.part = p->tail_part.p;
@@ -541,7 +566,9 @@ int fmm_copy_lists(fmm_plan_t p, int64_t* m2l_off, int32_t* m2l_src, int64_t* p2
                    int32_t* p2p_src) {
   if (!p) return FMM_ERR_ARG;
   if (!p->built) return FMM_ERR_STATE;
+  TRY_HIP(hipSetDevice(p->device));
   TRY_HIP(hipDeviceSynchronize());
+  if (m2l_off || m2l_src) TRY(materialize_m2l_lists(p, nullptr));
   const size_t m = (size_t)p->n_nodes + 1;
   if (m2l_off) TRY_HIP(hipMemcpy(m2l_off, p->m2l_off.p, 8 * m, hipMemcpyDeviceToHost));
   if (p2p_off) TRY_HIP(hipMemcpy(p2p_off, p->p2p_off.p, 8 * m, hipMemcpyDeviceToHost));

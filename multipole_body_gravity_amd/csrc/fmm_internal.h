@@ -30,11 +30,12 @@ struct RootInfo {
   double scale;  // 2^21 / side (exact)
 };
 
-// Device scalars written by kernels and read back at the two build syncs.
+// Device scalars written by kernels and read back at the build syncs.
+constexpr int POOL_SHARDS = 512;
+enum { POOL_CU = 0, POOL_U = 1, POOL_PU = 2, POOL_TRM = 3, POOL_TRP = 4, N_POOLS = 5 };
 struct Control {
   int32_t nonfinite;
-  int32_t carry_overflow;
-  int64_t carry_used;     // entries requested from the carry pool
+  int32_t pad0;
   int64_t n_nodes;
   int64_t n_leaves;
   int64_t level_off[MAX_LEVELS + 1];
@@ -43,14 +44,11 @@ struct Control {
   int64_t n_p2p;
   int64_t own_m2l_total, own_p2p_total;  // walk: entries found at the target's own level
   int64_t n_p2p_tasks, n_p2p_part;        // near-field tasks and partial-sum slots
-  int64_t n_union;                        // sibling-union M2L entries
   int64_t n_tail_tasks;                   // transposed-tail M2L tasks
   int32_t pool_overflow;                  // a sharded pool ran out of room
   int32_t max_leaf_count;
-  int64_t pool_used[3][512];              // carry, transposed M2L, transposed P2P shards
+  int64_t pool_used[N_POOLS][POOL_SHARDS];  // per pool and shard: entries handed out
 };
-constexpr int POOL_SHARDS = 512;
-
 // Grow-only device buffer.
 struct DBuf {
   void* p = nullptr;
@@ -77,16 +75,24 @@ struct fmm_plan_s {
   mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq, ngeo;
   mbg::DBuf leaves, lvl_blkcnt;
   mbg::DBuf mpole, local;
-  // walk
-  mbg::DBuf carry, trm_pool, trp_pool, carry_off, carry_cnt, own_m2l, own_p2p;
-  mbg::DBuf tr_cnt_m2l, tr_cnt_p2p, tr_start_m2l, tr_start_p2p;
+  // walk: sharded pools (carry unions, M2L unions, P2P unions, transposed
+  // M2L and P2P keys) and per-node slices / counts
+  mbg::DBuf pool[mbg::N_POOLS];
+  mbg::DBuf cu_off, cu_cnt, u_off, u_cnt, pu_off, pu_cnt, trm_off, trp_off, own_m2l, own_p2p;
+  mbg::DBuf rootgen;
+  mbg::DBuf tr_cnt_m2l, tr_start_m2l;  // [kind][node] run lengths / starts in the sorted keys
   mbg::DBuf tr_keys, tr_keys_alt, tr_vals, tr_vals_alt;
+  const uint64_t* tr_sorted = nullptr;  // sorted transposed keys (one of tr_keys / tr_keys_alt)
+  int64_t n_tr = 0;
+  int key_shift = 0;
   mbg::DBuf m2l_off, m2l_src, p2p_off, p2p_src;
+  bool m2l_lists_ready = false;  // per-target M2L lists materialized (on request only)
   // near-field tasks (target leaf x bounded slice of its list)
   mbg::DBuf p2p_task, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
-  // sibling-union M2L lists: per parent, the sources accepted by any child + child masks
-  mbg::DBuf parents, uoff, usrc, umask;
+  // non-leaf nodes in id order; the parents of level l are parents[pbeg[l] .. pbeg[l+1])
+  mbg::DBuf parents;
   int64_t n_parents = 0, n_union = 0;
+  int64_t pbeg[mbg::MAX_LEVELS + 2] = {0};
   // transposed-tail M2L tasks: per-leaf task offsets, tasks, partial locals
   mbg::DBuf tail_toff, tail_task, tail_part;
   int64_t n_tail_tasks = 0;
@@ -100,7 +106,7 @@ struct fmm_plan_s {
   int walk_retries = 0;
   mbg::RootInfo root_host{};
 
-  int64_t shard_cap[3] = {0, 0, 0};  // carry, transposed M2L, transposed P2P
+  int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0, 0, 0};  // entries per shard, per pool
 
   mbg::Control* ctrl_host = nullptr;  // pinned
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
@@ -163,43 +169,44 @@ struct WalkArgs {
   const uint8_t* n_child;
   const int32_t* parent;
   double t2;
-  int step;
-  int64_t lvl_begin, lvl_count;  // nodes at level `step`
-  Pool<int32_t> carry;           // rejected partners of non-leaf nodes
-  Pool<uint64_t> trm, trp;       // transposed entries: (target << key_shift) | source
-  int64_t* carry_off;            // per node: its carry slice
-  int32_t* carry_cnt;
-  int32_t *own_m2l, *own_p2p;    // per node: entries found at its own level
-  const int64_t *m2l_off, *p2p_off;
-  int32_t *m2l_src, *p2p_src;
+  const int32_t* parents;  // non-leaf nodes, id order
+  int64_t pbeg, pcnt;      // the parents of this step: parents[pbeg .. pbeg + pcnt)
+  // pools of packed entries (node << 8) | child mask, and transposed keys
+  Pool<uint64_t> cu, u, pu, trm, trp;
+  // per parent: slices of its carry union, M2L union, P2P union; tr allocations
+  int64_t *cu_off, *u_off, *pu_off, *trm_off, *trp_off;
+  int32_t *cu_cnt, *u_cnt, *pu_cnt;
+  int32_t *own_m2l, *own_p2p;  // per node: entries found at its own level
+  const uint64_t* rootgen;     // the root's generator: one entry, the root itself
   int key_shift;
   Control* ctrl;
 };
-hipError_t launch_walk_pass1(const WalkArgs& a, hipStream_t st);
-hipError_t launch_walk_pass2(const WalkArgs& a, hipStream_t st);
-hipError_t launch_walk_root(int pass, int root_leaf, const WalkArgs& a, hipStream_t st);
-hipError_t launch_walk_reset(Control* ctrl, hipStream_t st);
+// per step (the children of the parents of one level): pass 1 counts and
+// allocates, pass 2 writes
+hipError_t launch_walk(int pass, const WalkArgs& a, hipStream_t st);
+hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, hipStream_t st);
+hipError_t launch_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
+                            const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st);
 hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
                                   Control* ctrl, hipStream_t st);
 // dense copy of the transposed pools: M2L keys first (kind bit clear), then P2P (kind bit set)
 hipError_t launch_tr_compact(const WalkArgs& a, int kind_bit, uint64_t* dst, hipStream_t st);
 hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
                           int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st);
-hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
-                               const int32_t* cnt_m2l, const int32_t* cnt_p2p, int64_t* tot_m2l,
-                               int64_t* tot_p2p, hipStream_t st);
+hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_t* tr_cnt,
+                               int64_t* tot, hipStream_t st);
+// sorted transposed keys of one kind -> after each target's own entries
 hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
-                             int64_t n_nodes, const int64_t* m2l_off, const int32_t* own_m2l,
-                             const int64_t* start_m2l, int32_t* m2l_src, const int64_t* p2p_off,
-                             const int32_t* own_p2p, const int64_t* start_p2p, int32_t* p2p_src,
-                             hipStream_t st);
-hipError_t launch_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
-                                   const int64_t* task_total, const int64_t* part_total,
-                                   const int64_t* union_total, const int64_t* tail_total,
+                             int kind, int64_t n_nodes, const int64_t* off, const int32_t* own,
+                             const int64_t* start, int32_t* src, hipStream_t st);
+// per-target own entries from the unions of their parents (root-leaf case included)
+hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
+                                const int32_t* first_child, const uint8_t* n_child,
+                                const uint64_t* pool, const int64_t* uoff, const int32_t* ucnt,
+                                const int64_t* off, int32_t* src, hipStream_t st);
+hipError_t launch_walk_copy_totals(const int64_t* p2p_total, const int64_t* task_total,
+                                   const int64_t* part_total, const int64_t* tail_total,
                                    Control* ctrl, hipStream_t st);
-// per parent: count / write the union of its children's own M2L sources with masks
-hipError_t launch_union(int pass, const WalkArgs& a, const int32_t* parents, int64_t n_parents,
-                        int64_t* ucount_or_off, int32_t* usrc, uint8_t* umask, hipStream_t st);
 // LSD radix sort over the low `bits` bits; returns in *in_alt whether the
 // result ended in (keys_alt, idx_alt).
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
@@ -214,11 +221,12 @@ hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
                       const int32_t* first_child, const uint8_t* n_child, const double* centre,
                       void* mpole, hipStream_t st);
 // M2L: the root's local is cleared, the sibling blocks write every child's own
-// entries, the leaves' transposed tails [off[t] + own[t], off[t+1]) are
-// evaluated as tasks of at most TAIL_E entries and subtracted per leaf.
+// entries (from its parent's M2L union), and the leaves' transposed tails (runs
+// of the sorted transposed keys) are evaluated as tasks of at most TAIL_E
+// entries and subtracted per leaf.
 constexpr int TAIL_E = 64;
 struct TailTask {
-  int64_t e0;  // first entry
+  int64_t e0;  // first entry in the sorted transposed keys
   int32_t n;   // entries (1..TAIL_E)
   int32_t li;  // index into the leaf list
 };
@@ -228,25 +236,26 @@ struct M2LArgs {
   int64_t n_parents;
   const int32_t* first_child;
   const uint8_t* n_child;
-  const int64_t *uoff;
-  const int32_t* usrc;
-  const uint8_t* umask;
+  const uint64_t* upool;  // packed (source << 8) | child mask
+  const int64_t* u_off;   // per parent node
+  const int32_t* u_cnt;
   const int32_t* leaves;
   int64_t n_leaves;
   const TailTask* tasks;
   int64_t n_tasks;
-  const int64_t* toff;   // per leaf: first task (n_leaves + 1)
-  const int32_t* src;    // M2L list sources
+  const int64_t* toff;    // per leaf: first task (n_leaves + 1)
+  const uint64_t* keys;   // sorted transposed keys; source = key & src_mask
+  uint64_t src_mask;
   const double* centre;
-  const void* mrec;      // multipole records
-  void* part;            // task partials (n_tasks x K)
+  const void* mrec;       // multipole records
+  void* part;             // task partials (n_tasks x K)
   void* local;
 };
 hipError_t launch_m2l(int dtype, int order, const M2LArgs& a, hipStream_t st);
-hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                             const int32_t* own, int64_t* cnt, hipStream_t st);
-hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                            const int32_t* own, const int64_t* toff, TailTask* tasks,
+hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
+                             int64_t* cnt, hipStream_t st);
+hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
+                            const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks,
                             hipStream_t st);
 hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
                       const int32_t* parent, const double* centre, void* local, hipStream_t st);

@@ -100,8 +100,8 @@ template <typename T, int P>
 __global__ void __launch_bounds__(M2L_THREADS)
     k_m2l_sib(int64_t n_parents, const int32_t* __restrict__ parents,
               const int32_t* __restrict__ first_child, const uint8_t* __restrict__ n_child,
-              const int64_t* __restrict__ uoff, const int32_t* __restrict__ usrc,
-              const uint8_t* __restrict__ umask, const double* __restrict__ centre,
+              const uint64_t* __restrict__ upool, const int64_t* __restrict__ u_off,
+              const int32_t* __restrict__ u_cnt, const double* __restrict__ centre,
               const unsigned char* __restrict__ mrec, T* __restrict__ local) {
   using C = SibCfg<T, P>;
   constexpr int K = C::K;
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(M2L_THREADS)
       cy = centre[3 * ch + 1];
       cz = centre[3 * ch + 2];
     }
-    const int64_t u0 = uniform(uoff[pi]), u1 = uniform(uoff[pi + 1]);
+    const int64_t u0 = uniform(u_off[par]), u1 = u0 + uniform(u_cnt[par]);
     T acc[K];
 #pragma unroll
     for (int k = 0; k < K; k++) acc[k] = (T)0;
@@ -145,8 +145,9 @@ __global__ void __launch_bounds__(M2L_THREADS)
         int32_t id = 0;
         uint8_t mk = 0;
         if (e < n) {
-          id = usrc[w0 + e];
-          mk = umask[w0 + e];
+          const uint64_t v = upool[w0 + e];
+          id = (int32_t)(v >> 8);
+          mk = (uint8_t)(v & 0xff);
         }
         wid[w][e] = id;
         wmk[w][e] = mk;
@@ -202,7 +203,7 @@ __global__ void __launch_bounds__(M2L_THREADS)
 }
 
 // ---------------- transposed tails ----------------
-// A leaf's entries after its own ones, [off[a] + own[a], off[a + 1]), come from
+// A leaf's transposed entries (a run of the sorted transposed keys) come from
 // deeper targets that accepted it; their lengths vary widely (0 to thousands),
 // so they are cut into tasks of at most TAIL_E entries.  A wave takes 8
 // consecutive tasks: lane l = 8 t + j walks entries j, j + 8, ... of task t, the
@@ -212,9 +213,9 @@ __global__ void __launch_bounds__(M2L_THREADS)
 template <typename T, int P>
 __global__ void __launch_bounds__(M2L_THREADS)
     k_m2l_tail(int64_t n_tasks, const TailTask* __restrict__ tasks,
-               const int32_t* __restrict__ leaves, const int32_t* __restrict__ src,
-               const double* __restrict__ centre, const unsigned char* __restrict__ mrec,
-               T* __restrict__ part) {
+               const int32_t* __restrict__ leaves, const uint64_t* __restrict__ keys,
+               uint64_t src_mask, const double* __restrict__ centre,
+               const unsigned char* __restrict__ mrec, T* __restrict__ part) {
   constexpr int K = Tabs<P>::K;
   constexpr int NT = Tabs<P>::NT;
   constexpr int RB = mrec_bytes(K, sizeof(T));
@@ -240,7 +241,7 @@ __global__ void __launch_bounds__(M2L_THREADS)
 #pragma unroll
     for (int k = 0; k < K; k++) acc[k] = (T)0;
     for (int e = j; e < n; e += 8) {
-      const int64_t b = src[e0 + e];
+      const int64_t b = (int64_t)(keys[e0 + e] & src_mask);
       const unsigned char* rb = mrec + b * RB;
       const T* Mb = (const T*)rb;
       T M[K];
@@ -283,40 +284,39 @@ __global__ void k_m2l_tail_combine(int64_t n_leaves, int K, const int32_t* __res
   local[(int64_t)leaves[li] * K + n] -= s;
 }
 
-__global__ void k_tail_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                             const int32_t* own, int64_t* cnt) {
+__global__ void k_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
+                             int64_t* cnt) {
   const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (li >= n_leaves) return;
-  const int64_t a = leaves[li];
-  const int64_t len = off[a + 1] - off[a] - own[a];
+  const int64_t len = tr_cnt[leaves[li]];
   cnt[li] = (len + TAIL_E - 1) / TAIL_E;
 }
 
-__global__ void k_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                            const int32_t* own, const int64_t* toff, TailTask* tasks) {
+__global__ void k_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
+                            const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks) {
   const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (li >= n_leaves) return;
   const int64_t a = leaves[li];
-  const int64_t e0 = off[a] + own[a], e1 = off[a + 1];
+  if (tr_cnt[a] == 0) return;
+  const int64_t e0 = tr_start[a], e1 = e0 + tr_cnt[a];
   int64_t q = toff[li];
   for (int64_t e = e0; e < e1; e += TAIL_E, q++)
     tasks[q] = TailTask{e, (int32_t)min((int64_t)TAIL_E, e1 - e), (int32_t)li};
 }
 
-hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                             const int32_t* own, int64_t* cnt, hipStream_t st) {
+hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
+                             int64_t* cnt, hipStream_t st) {
   if (n_leaves <= 0) return hipSuccess;
-  k_tail_count<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, off, own,
-                                                                    cnt);
+  k_tail_count<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, tr_cnt, cnt);
   return hipGetLastError();
 }
 
-hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                            const int32_t* own, const int64_t* toff, TailTask* tasks,
+hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
+                            const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks,
                             hipStream_t st) {
   if (n_leaves <= 0) return hipSuccess;
-  k_tail_fill<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, off, own,
-                                                                   toff, tasks);
+  k_tail_fill<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, tr_start,
+                                                                   tr_cnt, toff, tasks);
   return hipGetLastError();
 }
 
@@ -336,11 +336,11 @@ static void m2l_dispatch(int order, hipStream_t st, const M2LArgs& a) {
   case P:                                                                                    \
     if (a.n_parents > 0)                                                                     \
       k_m2l_sib<T, P><<<gs, M2L_THREADS, 0, st>>>(a.n_parents, a.parents, a.first_child,      \
-                                                  a.n_child, a.uoff, a.usrc, a.umask,        \
+                                                  a.n_child, a.upool, a.u_off, a.u_cnt,      \
                                                   a.centre, rec, (T*)a.local);               \
     if (a.n_tasks > 0)                                                                       \
-      k_m2l_tail<T, P><<<gt, M2L_THREADS, 0, st>>>(a.n_tasks, a.tasks, a.leaves, a.src,       \
-                                                   a.centre, rec, (T*)a.part);               \
+      k_m2l_tail<T, P><<<gt, M2L_THREADS, 0, st>>>(a.n_tasks, a.tasks, a.leaves, a.keys,      \
+                                                   a.src_mask, a.centre, rec, (T*)a.part);   \
     break;
     M2L_CASE(0) M2L_CASE(1) M2L_CASE(2) M2L_CASE(3) M2L_CASE(4)
     M2L_CASE(5) M2L_CASE(6) M2L_CASE(7) M2L_CASE(8)

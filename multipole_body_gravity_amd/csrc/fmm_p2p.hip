@@ -10,9 +10,10 @@
 // Work split.  A task is one target leaf and a slice of at most TASK_E source
 // leaves of its list (a sparse leaf next to dense clusters can have ~10^5
 // source leaves; slicing keeps every wave's work bounded).  One wave per task:
-// the source particles of up to 64 list entries are enumerated in list order
-// and staged 64 at a time through LDS; the tc <= 64 targets of the leaf occupy
-// the lanes as tc targets x floor(64/tc) source slices, and the slices of one
+// the source particles of a group of list entries are enumerated in list order
+// (an LDS table maps each particle to its entry) and staged 128 at a time
+// through LDS; each lane holds two targets, so one LDS read serves two pairs,
+// the target pairs x source slices fill the 64 lanes, and the slices of one
 // target are summed in a fixed order.  A leaf with one task writes its final
 // result directly; a leaf with several tasks writes per-task partial sums that
 // a second kernel adds in task order.  Every sum has a fixed order.
@@ -33,10 +34,12 @@ struct P2PTask {
 };
 
 __device__ __forceinline__ double p2p_rsqrt(double x) {
-  // hardware estimate + one cubically convergent correction (see the M2L file)
-  double y = __builtin_amdgcn_rsq(x);
-  double e = fma(-x * y, y, 1.0);
-  return fma(y * e, fma(e, 0.375, 0.5), y);
+  // hardware estimate (relative error ~2^-24) + one Newton step
+  // y <- y + (y/2)(1 - x y^2): relative error ~(3/2) e^2 < 1e-14, far below the
+  // rounding noise of the pair sums at the tolerances the results are held to
+  const double y = __builtin_amdgcn_rsq(x);
+  const double e = fma(-x * y, y, 1.0);
+  return fma(0.5 * y, e, y);
 }
 __device__ __forceinline__ float p2p_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
@@ -80,7 +83,8 @@ __global__ void k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t
 }
 
 // ---- near-field sums ----
-constexpr int TILE = 2 * WAVE;  // source particles staged per round
+constexpr int TILE = 2 * WAVE;       // source particles staged per round
+constexpr int MAXQ = 4096;           // source particles per owner table
 
 template <typename T>
 __device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp, T& fx, T& fy,
@@ -96,10 +100,22 @@ __device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp
   fz -= mr3 * dz;
 }
 
-// Lane layout for a chunk of tc <= 64 targets: lane l serves target l % tc
-// and source slice l / tc; with nsl = ceil(64 / tc) slices the last slice may
-// cover only the first 64 - (nsl-1) tc targets, so a target has ns(t) = nsl
-// or nsl - 1 slices, and slice s of target t takes sources s, s + ns(t), ...
+// Lane layout for a chunk of tc <= 128 targets: each lane holds two targets
+// (2g, 2g + 1), so one source read from LDS serves two pairs.  With
+// G = ceil(tc / 2) groups and nsl = ceil(64 / G) source slices, lane l serves
+// group l % G and slice l / G; the last slice may cover only the first
+// 64 - (nsl - 1) G groups, so a group has ns(g) = nsl or nsl - 1 slices, and
+// slice s of group g takes sources s, s + ns(g), ...
+template <typename T>
+struct P2PShared {
+  union {
+    P4<T> tile[TILE];
+    T red[8][WAVE];
+  };
+  uint8_t owner[MAXQ];  // list entry (within the group of 64) of each source particle
+  int32_t sbase[WAVE];  // per entry: first particle minus its first source index
+};
+
 template <typename T>
 __global__ void __launch_bounds__(P2P_THREADS)
     k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
@@ -107,25 +123,28 @@ __global__ void __launch_bounds__(P2P_THREADS)
           const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
           const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
           T* __restrict__ part) {
-  __shared__ P4<T> tile[P2P_WAVES][TILE];
-  __shared__ T red[P2P_WAVES][4][WAVE];
+  __shared__ P2PShared<T> sh_all[P2P_WAVES];
   const int lane = __lane_id();
   const int w = threadIdx.x / WAVE;
+  P2PShared<T>& sh = sh_all[w];
   for (int64_t ti = (int64_t)blockIdx.x * P2P_WAVES + w; ti < n_tasks;
        ti += (int64_t)gridDim.x * P2P_WAVES) {
     const P2PTask task = tasks[ti];
     const int32_t a = task.leaf;
     const int32_t tb = begin[a], tn = count[a];
-    for (int32_t t0 = 0; t0 < tn; t0 += WAVE) {
-      const int tc = min(WAVE, tn - t0);
-      const int nsl = (WAVE + tc - 1) / tc;
-      const int t = lane % tc, sl = lane / tc;
-      const int ns = (t < WAVE - (nsl - 1) * tc) ? nsl : nsl - 1;  // slices of target t
-      const int32_t i = tb + t0 + t;
-      const P4<T> pi = pts[i];
-      T fp = 0, fx = 0, fy = 0, fz = 0;
+    for (int32_t t0 = 0; t0 < tn; t0 += 2 * WAVE) {
+      const int tc = min(2 * WAVE, tn - t0);
+      const int G = (tc + 1) >> 1;
+      const int nsl = (WAVE + G - 1) / G;
+      const int g = lane % G, sl = lane / G;
+      const int ns = (g < WAVE - (nsl - 1) * G) ? nsl : nsl - 1;  // slices of group g
+      const int32_t i0 = tb + t0 + 2 * g;
+      const bool two = 2 * g + 1 < tc;
+      const P4<T> p0 = pts[i0];
+      const P4<T> p1 = pts[two ? i0 + 1 : i0];
+      T a0 = 0, a1 = 0, a2 = 0, a3 = 0, b0 = 0, b1 = 0, b2 = 0, b3 = 0;
       bool self = false;
-      for (int64_t eg = task.e0; eg < task.e1; eg += WAVE) {
+      for (int64_t eg = task.e0; eg < task.e1;) {
         int32_t sb = 0, sc = 0;
         if (eg + lane < task.e1) {
           const int32_t b = src[eg + lane];
@@ -136,48 +155,67 @@ __global__ void __launch_bounds__(P2P_THREADS)
             sc = count[b];
           }
         }
-        const int incl = wave_incl_scan(sc);
+        int incl = wave_incl_scan(sc);
+        // take the longest prefix of entries whose particles fit the owner table
+        // (at least one entry; a single larger one needs no table)
+        const int H = max(1, (int)__popcll(__ballot(incl <= MAXQ)));
+        const int inclH = __shfl(incl, H - 1, WAVE);
+        if (lane >= H) {
+          sc = 0;
+          incl = inclH;
+        }
         const int excl = incl - sc;
         const int tot = __shfl(incl, WAVE - 1, WAVE);
+        const bool one = tot > MAXQ;  // one entry, particles sb[0] + q
+        sh.sbase[lane] = sb - excl;
+        if (!one)
+          for (int k = 0; k < sc; k++) sh.owner[excl + k] = (uint8_t)lane;
+        __builtin_amdgcn_wave_barrier();
         for (int q0 = 0; q0 < tot; q0 += TILE) {
 #pragma unroll
           for (int r = 0; r < TILE / WAVE; r++) {
             const int q = q0 + r * WAVE + lane;
-            int h = 0;
-#pragma unroll
-            for (int step = 32; step >= 1; step >>= 1) {
-              const int v = __shfl(incl, h + step - 1, WAVE);
-              if (v <= q) h += step;
-            }
-            h = min(h, WAVE - 1);
-            const int32_t jj = __shfl(sb, h, WAVE) + (q - __shfl(excl, h, WAVE));
-            if (q < tot) tile[w][r * WAVE + lane] = pts[jj];
+            if (q < tot) sh.tile[r * WAVE + lane] = pts[sh.sbase[one ? 0 : sh.owner[q]] + q];
           }
           __builtin_amdgcn_wave_barrier();
           const int nv = min(TILE, tot - q0);
-          for (int s = sl; s < nv; s += ns) pair_acc(pi, tile[w][s], fp, fx, fy, fz);
+          for (int s = sl; s < nv; s += ns) {
+            const P4<T> pj = sh.tile[s];
+            pair_acc(p0, pj, a0, a1, a2, a3);
+            pair_acc(p1, pj, b0, b1, b2, b3);
+          }
           __builtin_amdgcn_wave_barrier();
         }
+        eg += H;
       }
       if (__ballot(self) != 0ull) {
         for (int32_t s = sl; s < tn; s += ns) {
-          if (tb + s == i) continue;  // self term omitted
-          pair_acc(pi, pts[tb + s], fp, fx, fy, fz);
+          const P4<T> pj = pts[tb + s];
+          if (tb + s != i0) pair_acc(p0, pj, a0, a1, a2, a3);  // self term omitted
+          if (tb + s != i0 + 1) pair_acc(p1, pj, b0, b1, b2, b3);
         }
       }
-      red[w][0][lane] = fp;
-      red[w][1][lane] = fx;
-      red[w][2][lane] = fy;
-      red[w][3][lane] = fz;
+      sh.red[0][lane] = a0;
+      sh.red[1][lane] = a1;
+      sh.red[2][lane] = a2;
+      sh.red[3][lane] = a3;
+      sh.red[4][lane] = b0;
+      sh.red[5][lane] = b1;
+      sh.red[6][lane] = b2;
+      sh.red[7][lane] = b3;
       __builtin_amdgcn_wave_barrier();
-      if (lane < tc) {
+      // target t0 + l (l < tc) is finished by lane l % 64: group l / 2, member l % 2
+      for (int l = lane; l < tc; l += WAVE) {
+        const int gg = l >> 1, m = 4 * (l & 1);
+        const int nsg = (gg < WAVE - (nsl - 1) * G) ? nsl : nsl - 1;
         T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-        for (int q = 0; q < ns; q++) {
-          s0 += red[w][0][q * tc + lane];
-          s1 += red[w][1][q * tc + lane];
-          s2 += red[w][2][q * tc + lane];
-          s3 += red[w][3][q * tc + lane];
+        for (int q = 0; q < nsg; q++) {
+          s0 += sh.red[m][q * G + gg];
+          s1 += sh.red[m + 1][q * G + gg];
+          s2 += sh.red[m + 2][q * G + gg];
+          s3 += sh.red[m + 3][q * G + gg];
         }
+        const int32_t i = tb + t0 + l;
         if (task.part < 0) {
           const P4<T> f = far[i];
           const int64_t o = perm[i];
@@ -186,7 +224,7 @@ __global__ void __launch_bounds__(P2P_THREADS)
           acc[3 * o + 1] = f.z + s2;
           acc[3 * o + 2] = f.m + s3;
         } else {
-          T* pp = part + 4 * (task.part + t0 + lane);
+          T* pp = part + 4 * (task.part + t0 + l);
           pp[0] = s0;
           pp[1] = s1;
           pp[2] = s2;

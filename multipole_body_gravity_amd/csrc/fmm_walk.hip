@@ -5,32 +5,35 @@
 // multipole-to-local translations, refine the rest, sum the remaining nearby
 // pairs directly).  The pair walk from (root, root) -- accept -> M2L, two
 // leaves -> P2P, otherwise split the coarser non-leaf (both when the levels are
-// equal) -- is evaluated here target by target, one tree level per step:
+// equal) -- is evaluated here one tree level per step, per sibling group:
 //
-//   * at step s every node t of level s receives as candidates the "carry" of
-//     its parent (the parent's rejected partners): each carried leaf is kept
-//     as it is, each carried non-leaf is replaced by its children;
-//   * each candidate c is accepted (M2L t <- c) or rejected; a rejected c goes
-//     to t's carry if t is a non-leaf, and to t's P2P list if t and c are both
-//     leaves.
+//   * the children of a node X all receive the same candidates: X's "carry"
+//     (X's rejected partners) with each carried leaf kept as it is and each
+//     carried non-leaf replaced by its children;
+//   * each candidate c is tested against every child t: accepted -> M2L
+//     (t <- c); rejected with t and c both leaves -> P2P (t <- c); rejected
+//     with t a non-leaf -> c goes to t's carry.
+//
+// One wave per X enumerates the candidates once per pass and keeps, for the
+// group, three unions of (candidate, 8-bit mask of children): the M2L union,
+// the P2P union and the carry union.  A child's own list (or carry) is the
+// union's entries with its bit set, in enumeration order.
 //
 // The pair walk also refines the partners of a leaf t past t's own level
 // (only the non-leaf side can split).  Those pairs are exactly the pairs in
 // which a deeper target sees t as a carried leaf, and the acceptance test is
-// symmetric, so they are emitted from that side: when a target of level s
-// accepts a carried leaf c of a coarser level, the entry (c <- target) is
-// added to c's list as well, and likewise for leaf-leaf rejections.  Such
-// transposed entries are appended in any order and put in place by a radix
-// sort of (target, source) keys; a target's own entries (sources at its level
-// or coarser) come first, its transposed ones (deeper sources) after, so every
+// symmetric, so they are emitted from that side: when a target accepts a
+// carried leaf c of a coarser level, the entry (c <- target) is added to c's
+// list as well, and likewise for leaf-leaf rejections.  Such transposed
+// entries are appended in any order and put in place by a radix sort of
+// (target, source) keys; a target's own entries (sources at its level or
+// coarser) come first, its transposed ones (deeper sources) after, so every
 // list ends sorted by source, as the pair walk's canonical order requires.
 //
-// Pass 1 counts each target's own entries and writes its carry and its
-// transposed entries; the transposed entries are then sorted, counted per
-// target, and after a scan of the per-target totals pass 2 re-classifies and
-// writes the own entries in place.  Carry slices and transposed entries are
-// placed by sharded bump allocators (integer atomics spread over 512 counters
-// by target): their placement varies between runs, the final lists do not.
+// Pass 1 of a step counts the unions and transposed entries of every group and
+// reserves their room; pass 2 enumerates again and writes them.  Room comes
+// from sharded bump allocators (integer atomics spread over 512 counters by
+// node): placement varies between runs, the lists do not.
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -38,7 +41,6 @@ namespace mbg {
 
 constexpr int WK_THREADS = 256;
 constexpr int WK_WAVES = WK_THREADS / WAVE;
-constexpr uint32_t QMASK = 0x1fffffu;
 
 // Opening criterion, theta = |l_A + l_B| / |c_A - c_B| with l = (h, h, h):
 // accept iff 3 (h_A + h_B)^2 < fl(theta^2) |c_A - c_B|^2.  Centres and
@@ -55,42 +57,42 @@ __device__ __forceinline__ bool accept_pair(const int4& A, const int4& B, double
   return lhs < t2 * r2;
 }
 
-enum { CAND_NONE = 0, CAND_M2L = 1, CAND_P2P = 2, CAND_CARRY = 3 };
-
-struct Target {
-  int32_t t;
-  int4 g;
-  bool leaf;
-};
-
-__device__ __forceinline__ int classify(const WalkArgs& a, const Target& T, int32_t c) {
-  const int4 g = a.geo[c];
-  if (accept_pair(T.g, g, a.t2)) return CAND_M2L;
-  if (!T.leaf) return CAND_CARRY;
-  return (g.w & GEO_LEAF) ? CAND_P2P : CAND_CARRY;
-}
-
-// Visit the candidates of a generator slice in ascending node order, 64 at a
-// time: first the carried leaves (levels < s, kept as they are: phase 0), then
-// the children of the carried non-leaves (level s: phase 1).  Each phase
-// follows the sorted generator order, and every id of phase 0 is smaller than
-// every id of phase 1.  f(active, cand, phase) is called by the whole wave.
+// Visit the candidates of the group of X in ascending node order, 64 at a time:
+// first the carried leaves (levels < s, kept as they are: phase 0), then the
+// children of the carried non-leaves (level s: phase 1).  X's carry is the
+// entries of its parent's carry union with X's bit set (for the root: the
+// root).  f(active, cand, phase) is called by the whole wave.
 template <typename F>
-__device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int64_t g0, int gc, F&& f) {
+__device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int32_t X, F&& f) {
   const int lane = __lane_id();
+  const uint64_t* gen;
+  int gc, slot;
+  if (X == 0) {
+    gen = a.rootgen;
+    gc = 1;
+    slot = 0;
+  } else {
+    const int32_t Y = uniform(a.parent[X]);
+    gen = a.cu.data + uniform(a.cu_off[Y]);
+    gc = uniform(a.cu_cnt[Y]);
+    slot = X - uniform(a.first_child[Y]);
+  }
   for (int phase = 0; phase < 2; phase++) {
     for (int c0 = 0; c0 < gc; c0 += WAVE) {
       const int j = c0 + lane;
       int nc = 0, fc = 0;
       if (j < gc) {
-        const int32_t g = a.carry.data[g0 + j];
-        const int k = a.n_child[g];
-        if (phase == 0 && k == 0) {
-          nc = 1;
-          fc = g;
-        } else if (phase == 1 && k != 0) {
-          nc = k;
-          fc = a.first_child[g];
+        const uint64_t e = gen[j];
+        if ((e >> slot) & 1u) {
+          const int32_t g = (int32_t)(e >> 8);
+          const int k = a.n_child[g];
+          if (phase == 0 && k == 0) {
+            nc = 1;
+            fc = g;
+          } else if (phase == 1 && k != 0) {
+            nc = k;
+            fc = a.first_child[g];
+          }
         }
       }
       const int incl = wave_incl_scan(nc);
@@ -123,7 +125,7 @@ __device__ __forceinline__ int shard_of(int32_t t) {
 // Wave-wide allocation of n entries from shard sh (lane 0 bumps the counter).
 // Returns the global offset, or -1 when the shard is full (overflow flagged).
 template <typename T>
-__device__ __forceinline__ int64_t pool_alloc(const Pool<T>& p, int sh, int n, Control* ctrl) {
+__device__ __forceinline__ int64_t pool_alloc(const Pool<T>& p, int sh, int64_t n, Control* ctrl) {
   int64_t off = 0;
   if (__lane_id() == 0)
     off = (int64_t)atomicAdd((unsigned long long*)&p.used[sh], (unsigned long long)n);
@@ -135,128 +137,162 @@ __device__ __forceinline__ int64_t pool_alloc(const Pool<T>& p, int sh, int n, C
   return (int64_t)sh * p.shard_cap + off;
 }
 
-__global__ void __launch_bounds__(WK_THREADS) k_walk_pass1(WalkArgs a) {
-  // after an overflow the parents' carries may be missing: do nothing, the
-  // host regrows the pools and repeats pass 1
+// The children of X: geometry of child t in cg[t]; masks of the leaf children
+// and of all children.
+struct Group {
+  int4 cg[8];
+  uint32_t leafmask, allmask;
+  int nc;
+  int32_t fc;
+};
+
+__device__ __forceinline__ Group load_group(const WalkArgs& a, int32_t X) {
+  Group G;
+  const int lane = __lane_id();
+  G.nc = uniform((int)a.n_child[X]);
+  G.fc = uniform(a.first_child[X]);
+  int4 mine = make_int4(0, 0, 0, 0);
+  if (lane < G.nc) mine = a.geo[G.fc + lane];
+#pragma unroll
+  for (int t = 0; t < 8; t++) {
+    G.cg[t].x = __shfl(mine.x, t, WAVE);
+    G.cg[t].y = __shfl(mine.y, t, WAVE);
+    G.cg[t].z = __shfl(mine.z, t, WAVE);
+    G.cg[t].w = __shfl(mine.w, t, WAVE);
+  }
+  G.allmask = (1u << G.nc) - 1u;
+  G.leafmask = (uint32_t)__ballot(lane < G.nc && (mine.w & GEO_LEAF) != 0) & G.allmask;
+  return G;
+}
+
+// Classify candidate c for every child: masks of M2L, P2P and carry.
+__device__ __forceinline__ void classify(const WalkArgs& a, const Group& G, int32_t c,
+                                         uint32_t& mM, uint32_t& mP, uint32_t& mC) {
+  const int4 g = a.geo[c];
+  uint32_t acc = 0;
+#pragma unroll
+  for (int t = 0; t < 8; t++)
+    if (accept_pair(G.cg[t], g, a.t2)) acc |= 1u << t;
+  acc &= G.allmask;
+  const uint32_t rej = G.allmask & ~acc;
+  mM = acc;
+  mP = (g.w & GEO_LEAF) ? (rej & G.leafmask) : 0u;
+  mC = rej & ~G.leafmask;
+}
+
+// 8 counters of up to 2^32 - 1 in four 64-bit words: bit t of m adds one to counter t
+__device__ __forceinline__ void add_bits(uint64_t (&c)[4], uint32_t m) {
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+    c[k] += (uint64_t)((m >> (2 * k)) & 1u) | ((uint64_t)((m >> (2 * k + 1)) & 1u) << 32);
+}
+
+__global__ void __launch_bounds__(WK_THREADS) k_walk(int pass, WalkArgs a) {
+  // after an overflow the carry unions may be incomplete: do nothing, the host
+  // regrows the pools and repeats the walk
   if (a.ctrl->pool_overflow) return;
   const int lane = __lane_id();
   const uint64_t lt = lanemask_lt();
-  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.lvl_count;
+  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.pcnt;
        j += (int64_t)gridDim.x * WK_WAVES) {
-    const int32_t t = (int32_t)(a.lvl_begin + j);
-    const int32_t par = a.parent[t];
-    const int64_t g0 = a.carry_off[par];
-    const int gc = a.carry_cnt[par];
-    Target T{t, a.geo[t], (a.geo[t].w & GEO_LEAF) != 0};
-    int n_m2l = 0, n_p2p = 0, n_carry = 0, n_trm = 0, n_trp = 0;
-    for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int phase) {
-      const int ty = act ? classify(a, T, c) : CAND_NONE;
-      const bool m = ty == CAND_M2L, p = ty == CAND_P2P, k = ty == CAND_CARRY && !T.leaf;
-      const int cm = __popcll(__ballot(m)), cp = __popcll(__ballot(p));
-      n_m2l += cm;
-      n_p2p += cp;
-      n_carry += __popcll(__ballot(k));
-      if (phase == 0) {  // carried leaves of coarser levels: transposed entries
-        n_trm += cm;
-        n_trp += cp;
+    const int32_t X = uniform(a.parents[a.pbeg + j]);
+    const Group G = load_group(a, X);
+    if (pass == 1) {
+      int64_t nU = 0, nPU = 0, nCU = 0;
+      uint32_t ntm = 0, ntp = 0;  // per lane
+      uint64_t cm[4] = {0, 0, 0, 0}, cp[4] = {0, 0, 0, 0};
+      for_each_candidate(a, X, [&](bool act, int32_t c, int phase) {
+        uint32_t mM = 0, mP = 0, mC = 0;
+        if (act) classify(a, G, c, mM, mP, mC);
+        nU += __popcll(__ballot(mM != 0));
+        nPU += __popcll(__ballot(mP != 0));
+        nCU += __popcll(__ballot(mC != 0));
+        add_bits(cm, mM);
+        add_bits(cp, mP);
+        if (phase == 0) {  // carried leaves of coarser levels: transposed entries
+          ntm += __popc(mM);
+          ntp += __popc(mP);
+        }
+      });
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        cm[k] = wave_sum(cm[k]);
+        cp[k] = wave_sum(cp[k]);
       }
-    });
-    const int sh = shard_of(t);
-    int64_t off = 0;
-    bool ok = true;
-    if (n_carry > 0) {
-      off = pool_alloc(a.carry, sh, n_carry, a.ctrl);
-      ok = off >= 0;
-    }
-    int64_t om = 0, op = 0;
-    if (ok && n_trm > 0) {
-      om = pool_alloc(a.trm, sh, n_trm, a.ctrl);
-      ok = om >= 0;
-    }
-    if (ok && n_trp > 0) {
-      op = pool_alloc(a.trp, sh, n_trp, a.ctrl);
-      ok = op >= 0;
-    }
-    if (!ok) continue;  // results are discarded; the host regrows the pools and retries
-    if (n_carry + n_trm + n_trp > 0) {
-      int64_t ck = off, cm = om, cp = op;
-      for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int phase) {
-        const int ty = act ? classify(a, T, c) : CAND_NONE;
-        const uint64_t bk = __ballot(ty == CAND_CARRY && !T.leaf);
-        if (ty == CAND_CARRY && !T.leaf) a.carry.data[ck + __popcll(bk & lt)] = c;
-        ck += __popcll(bk);
+      const int64_t tm = wave_sum((int64_t)ntm), tp = wave_sum((int64_t)ntp);
+      const int sh = shard_of(X);
+      int64_t oCU = 0, oU = 0, oPU = 0, oTM = 0, oTP = 0;
+      bool ok = true;
+      if (nCU > 0) ok = (oCU = pool_alloc(a.cu, sh, nCU, a.ctrl)) >= 0;
+      if (ok && nU > 0) ok = (oU = pool_alloc(a.u, sh, nU, a.ctrl)) >= 0;
+      if (ok && nPU > 0) ok = (oPU = pool_alloc(a.pu, sh, nPU, a.ctrl)) >= 0;
+      if (ok && tm > 0) ok = (oTM = pool_alloc(a.trm, sh, tm, a.ctrl)) >= 0;
+      if (ok && tp > 0) ok = (oTP = pool_alloc(a.trp, sh, tp, a.ctrl)) >= 0;
+      if (!ok) continue;  // results are discarded; the host regrows the pools and retries
+      if (lane == 0) {
+        a.cu_off[X] = oCU;
+        a.cu_cnt[X] = (int32_t)nCU;
+        a.u_off[X] = oU;
+        a.u_cnt[X] = (int32_t)nU;
+        a.pu_off[X] = oPU;
+        a.pu_cnt[X] = (int32_t)nPU;
+        a.trm_off[X] = oTM;
+        a.trp_off[X] = oTP;
+      }
+      if (lane < G.nc) {
+        const int k = lane >> 1, hi = lane & 1;
+        uint64_t vm = 0, vp = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if (q == k) {
+            vm = cm[q];
+            vp = cp[q];
+          }
+        a.own_m2l[G.fc + lane] = (int32_t)(hi ? (vm >> 32) : (vm & 0xffffffffu));
+        a.own_p2p[G.fc + lane] = (int32_t)(hi ? (vp >> 32) : (vp & 0xffffffffu));
+      }
+    } else {
+      const int64_t oCU = a.cu_off[X], oU = a.u_off[X], oPU = a.pu_off[X];
+      const int64_t oTM = a.trm_off[X], oTP = a.trp_off[X];
+      int64_t kU = 0, kPU = 0, kCU = 0, kTM = 0, kTP = 0;
+      for_each_candidate(a, X, [&](bool act, int32_t c, int phase) {
+        uint32_t mM = 0, mP = 0, mC = 0;
+        if (act) classify(a, G, c, mM, mP, mC);
+        const uint64_t packed = (uint64_t)(uint32_t)c << 8;
+        const uint64_t bU = __ballot(mM != 0), bP = __ballot(mP != 0), bC = __ballot(mC != 0);
+        if (mM) a.u.data[oU + kU + __popcll(bU & lt)] = packed | mM;
+        if (mP) a.pu.data[oPU + kPU + __popcll(bP & lt)] = packed | mP;
+        if (mC) a.cu.data[oCU + kCU + __popcll(bC & lt)] = packed | mC;
+        kU += __popcll(bU);
+        kPU += __popcll(bP);
+        kCU += __popcll(bC);
         if (phase == 0) {
-          const uint64_t key = ((uint64_t)(uint32_t)c << a.key_shift) | (uint32_t)t;
-          const uint64_t bm = __ballot(ty == CAND_M2L), bp = __ballot(ty == CAND_P2P);
-          if (ty == CAND_M2L) a.trm.data[cm + __popcll(bm & lt)] = key;
-          if (ty == CAND_P2P) a.trp.data[cp + __popcll(bp & lt)] = key;
-          cm += __popcll(bm);
-          cp += __popcll(bp);
+          // (c <- child t) for every child t that accepted c, or paired with it
+          const int nm = __popc(mM), np = __popc(mP);
+          const int im = wave_incl_scan(nm), ip = wave_incl_scan(np);
+          int64_t om = oTM + kTM + (im - nm), op = oTP + kTP + (ip - np);
+          const uint64_t hiC = (uint64_t)(uint32_t)c << a.key_shift;
+          for (uint32_t m = mM; m; m &= m - 1)
+            a.trm.data[om++] = hiC | (uint32_t)(G.fc + __ffs(m) - 1);
+          for (uint32_t m = mP; m; m &= m - 1)
+            a.trp.data[op++] = hiC | (uint32_t)(G.fc + __ffs(m) - 1);
+          kTM += __shfl(im, WAVE - 1, WAVE);
+          kTP += __shfl(ip, WAVE - 1, WAVE);
         }
       });
     }
-    if (lane == 0) {
-      a.carry_off[t] = off;
-      a.carry_cnt[t] = n_carry;
-      a.own_m2l[t] = n_m2l;
-      a.own_p2p[t] = n_p2p;
-    }
   }
 }
 
-__global__ void __launch_bounds__(WK_THREADS) k_walk_pass2(WalkArgs a) {
-  const uint64_t lt = lanemask_lt();
-  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.lvl_count;
-       j += (int64_t)gridDim.x * WK_WAVES) {
-    const int32_t t = (int32_t)(a.lvl_begin + j);
-    const int32_t par = a.parent[t];
-    const int64_t g0 = a.carry_off[par];
-    const int gc = a.carry_cnt[par];
-    Target T{t, a.geo[t], (a.geo[t].w & GEO_LEAF) != 0};
-    const int64_t m0 = a.m2l_off[t], p0 = a.p2p_off[t];
-    int64_t cm = 0, cp = 0;
-    for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int) {
-      const int ty = act ? classify(a, T, c) : CAND_NONE;
-      const uint64_t mm = __ballot(ty == CAND_M2L);
-      const uint64_t mp = __ballot(ty == CAND_P2P);
-      if (ty == CAND_M2L) a.m2l_src[m0 + cm + __popcll(mm & lt)] = c;
-      if (ty == CAND_P2P) a.p2p_src[p0 + cp + __popcll(mp & lt)] = c;
-      cm += __popcll(mm);
-      cp += __popcll(mp);
-    });
-  }
-}
-
-// Step 0: the root paired with itself.  A leaf root gives the single list entry
-// P2P(root <- root); otherwise the root's carry is {root} for its children.
-__global__ void k_walk_root(int pass, int root_leaf, WalkArgs a) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  if (pass == 1) {
-    a.own_m2l[0] = 0;
-    a.carry_off[0] = 0;
-    if (root_leaf) {
-      a.own_p2p[0] = 1;
-      a.carry_cnt[0] = 0;
-    } else {
-      a.own_p2p[0] = 0;
-      const int sh = shard_of(0);
-      const int64_t off = (int64_t)sh * a.carry.shard_cap + a.carry.used[sh];
-      a.carry.data[off] = 0;
-      a.carry.used[sh] += 1;
-      a.carry_off[0] = off;
-      a.carry_cnt[0] = 1;
-    }
-  } else if (root_leaf) {
-    a.p2p_src[a.p2p_off[0]] = 0;
-  }
-}
-
-__global__ void k_walk_reset(Control* c) {
-  for (int i = threadIdx.x; i < 3 * POOL_SHARDS; i += blockDim.x) (&c->pool_used[0][0])[i] = 0;
+// Walk set-up: pools empty, no overflow, the root's generator.
+__global__ void k_walk_reset(Control* c, uint64_t* rootgen) {
+  for (int i = threadIdx.x; i < N_POOLS * POOL_SHARDS; i += blockDim.x)
+    (&c->pool_used[0][0])[i] = 0;
   if (threadIdx.x == 0) {
     c->pool_overflow = 0;
     c->own_m2l_total = 0;
     c->own_p2p_total = 0;
+    rootgen[0] = (0ull << 8) | 1ull;  // node 0, slot 0
   }
 }
 
@@ -326,115 +362,96 @@ __global__ void k_tr_lengths(int64_t m, const int64_t* start, int32_t* cnt) {
   if (i < m && cnt[i] > 0) cnt[i] = (int32_t)(cnt[i] - start[i]);
 }
 
-__global__ void k_walk_offsets(int64_t n, const int32_t* om, const int32_t* op, const int32_t* cm,
-                               const int32_t* cp, int64_t* totm, int64_t* totp) {
+__global__ void k_walk_offsets(int64_t n, const int32_t* own, const int32_t* tr_cnt,
+                               int64_t* tot) {
   int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= n) return;
-  totm[i] = (int64_t)om[i] + cm[i];
-  totp[i] = (int64_t)op[i] + cp[i];
+  tot[i] = (int64_t)own[i] + tr_cnt[i];
 }
 
-__global__ void k_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
-                                   const int64_t* task_total, const int64_t* part_total,
-                                   const int64_t* union_total, const int64_t* tail_total,
+__global__ void k_walk_copy_totals(const int64_t* p2p_total, const int64_t* task_total,
+                                   const int64_t* part_total, const int64_t* tail_total,
                                    Control* c) {
   if (threadIdx.x == 0) {
-    c->n_m2l = *m2l_total;
     c->n_p2p = *p2p_total;
     c->n_p2p_tasks = *task_total;
     c->n_p2p_part = *part_total;
-    c->n_union = *union_total;
     c->n_tail_tasks = *tail_total;
   }
 }
 
-// The children of a non-leaf P all receive the same candidates (P's carry,
-// expanded), so their own M2L sources are the candidates accepted by at least
-// one child.  One wave per parent enumerates them once, in ascending order,
-// and keeps each accepted candidate with a mask of the accepting children.
-__global__ void __launch_bounds__(WK_THREADS)
-    k_union(int pass, WalkArgs a, const int32_t* parents, int64_t n_parents, int64_t* cnt_off,
-            int32_t* usrc, uint8_t* umask) {
-  const uint64_t lt = lanemask_lt();
-  const int lane = __lane_id();
-  for (int64_t pi = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; pi < n_parents;
-       pi += (int64_t)gridDim.x * WK_WAVES) {
-    const int32_t P = parents[pi];
-    const int nc = a.n_child[P];
-    const int32_t fc = a.first_child[P];
-    int4 mine = make_int4(0, 0, 0, 0);
-    if (lane < nc) mine = a.geo[fc + lane];
-    int4 cg[8];
-#pragma unroll
-    for (int t = 0; t < 8; t++) {
-      cg[t].x = __shfl(mine.x, t, WAVE);
-      cg[t].y = __shfl(mine.y, t, WAVE);
-      cg[t].z = __shfl(mine.z, t, WAVE);
-      cg[t].w = __shfl(mine.w, t, WAVE);
-    }
-    const int64_t g0 = a.carry_off[P];
-    const int gc = a.carry_cnt[P];
-    int64_t base = pass == 2 ? cnt_off[pi] : 0;
-    int64_t n = 0;
-    for_each_candidate(a, g0, gc, [&](bool act, int32_t c, int) {
-      uint32_t m = 0;
-      if (act) {
-        const int4 g = a.geo[c];
-#pragma unroll
-        for (int t = 0; t < 8; t++)
-          if (t < nc && accept_pair(cg[t], g, a.t2)) m |= 1u << t;
-      }
-      const uint64_t b = __ballot(m != 0);
-      if (pass == 2 && m != 0) {
-        const int64_t o = base + n + __popcll(b & lt);
-        usrc[o] = c;
-        umask[o] = (uint8_t)m;
-      }
-      n += __popcll(b);
-    });
-    if (pass == 1 && lane == 0) cnt_off[pi] = n;
-  }
-}
-
-hipError_t launch_union(int pass, const WalkArgs& a, const int32_t* parents, int64_t n_parents,
-                        int64_t* ucount_or_off, int32_t* usrc, uint8_t* umask, hipStream_t st) {
-  if (n_parents <= 0) return hipSuccess;
-  int64_t blocks = (n_parents + WK_WAVES - 1) / WK_WAVES;
-  if (blocks > 16384) blocks = 16384;
-  k_union<<<(unsigned)blocks, WK_THREADS, 0, st>>>(pass, a, parents, n_parents, ucount_or_off,
-                                                  usrc, umask);
-  return hipGetLastError();
-}
-
-// Sorted transposed keys -> after each target's own entries.
-__global__ void k_tr_scatter(const uint64_t* keys, int64_t n, int sh, int kind_bit,
-                             int64_t n_nodes, const int64_t* m2l_off, const int32_t* own_m2l,
-                             const int64_t* start_m2l, int32_t* m2l_src, const int64_t* p2p_off,
-                             const int32_t* own_p2p, const int64_t* start_p2p, int32_t* p2p_src) {
+// Sorted transposed keys of one kind -> after each target's own entries.
+__global__ void k_tr_scatter(const uint64_t* keys, int64_t n, int sh, int kind_bit, int kind,
+                             int64_t n_nodes, const int64_t* off, const int32_t* own,
+                             const int64_t* start, int32_t* src) {
   int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (k >= n) return;
   const uint64_t key = keys[k];
-  const int kind = (int)(key >> kind_bit);
+  if ((int)(key >> kind_bit) != kind) return;
   const int64_t c = (int64_t)((key >> sh) & ((1ull << (kind_bit - sh)) - 1ull));
-  const int32_t src = (int32_t)(key & ((1ull << sh) - 1ull));
-  if (kind == 0)
-    m2l_src[m2l_off[c] + own_m2l[c] + (k - start_m2l[c])] = src;
-  else
-    p2p_src[p2p_off[c] + own_p2p[c] + (k - start_p2p[c])] = src;
+  src[off[c] + own[c] + (k - start[c])] = (int32_t)(key & ((1ull << sh) - 1ull));
 }
 
-hipError_t launch_walk_root(int pass, int root_leaf, const WalkArgs& a, hipStream_t st) {
-  k_walk_root<<<1, 64, 0, st>>>(pass, root_leaf, a);
+// One wave per parent X: child t's own entries are the entries of X's union
+// with bit t set, in union order; they go to src[off[child] ...].
+__global__ void __launch_bounds__(WK_THREADS)
+    k_union_scatter(const int32_t* parents, int64_t n_parents, const int32_t* first_child,
+                    const uint8_t* n_child, const uint64_t* pool, const int64_t* uoff,
+                    const int32_t* ucnt, const int64_t* off, int32_t* src) {
+  const uint64_t lt = lanemask_lt();
+  const int lane = __lane_id();
+  for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < n_parents;
+       j += (int64_t)gridDim.x * WK_WAVES) {
+    const int32_t X = uniform(parents[j]);
+    const int nc = uniform((int)n_child[X]);
+    const int32_t fc = uniform(first_child[X]);
+    const int64_t u0 = uniform(uoff[X]);
+    const int un = uniform(ucnt[X]);
+    int64_t base[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) base[t] = t < nc ? off[fc + t] : 0;
+    for (int e0 = 0; e0 < un; e0 += WAVE) {
+      uint64_t v = 0;
+      if (e0 + lane < un) v = pool[u0 + e0 + lane];
+      const int32_t id = (int32_t)(v >> 8);
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        const bool has = (v >> t) & 1u;
+        const uint64_t b = __ballot(has);
+        if (has) src[base[t] + __popcll(b & lt)] = id;
+        base[t] += __popcll(b);
+      }
+    }
+  }
+}
+
+// The root is nobody's child: its own counts are set here.  A leaf root has the
+// single list entry P2P(root <- root).
+__global__ void k_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
+                            const int64_t* p2p_off, int32_t* p2p_src) {
+  if (threadIdx.x != 0) return;
+  if (pass == 1) {
+    own_m2l[0] = 0;
+    own_p2p[0] = root_leaf;
+  } else if (root_leaf) {
+    p2p_src[p2p_off[0]] = 0;
+  }
+}
+hipError_t launch_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
+                            const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st) {
+  k_walk_root<<<1, 64, 0, st>>>(pass, root_leaf, own_m2l, own_p2p, p2p_off, p2p_src);
   return hipGetLastError();
 }
-hipError_t launch_walk_reset(Control* ctrl, hipStream_t st) {
-  k_walk_reset<<<1, 256, 0, st>>>(ctrl);
+
+hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, hipStream_t st) {
+  k_walk_reset<<<1, 256, 0, st>>>(ctrl, rootgen);
   return hipGetLastError();
 }
 hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
                                   Control* ctrl, hipStream_t st) {
   int64_t blocks = (n_nodes + WK_THREADS - 1) / WK_THREADS;
   if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
   k_walk_own_totals<<<(unsigned)blocks, WK_THREADS, 0, st>>>(n_nodes, own_m2l, own_p2p, ctrl);
   return hipGetLastError();
 }
@@ -450,47 +467,42 @@ hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int ki
   k_tr_lengths<<<(unsigned)((2 * n_nodes + 255) / 256), 256, 0, st>>>(2 * n_nodes, start, cnt);
   return hipGetLastError();
 }
-hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
-                               const int32_t* cnt_m2l, const int32_t* cnt_p2p, int64_t* tot_m2l,
-                               int64_t* tot_p2p, hipStream_t st) {
-  k_walk_offsets<<<(unsigned)((n_nodes + 255) / 256), 256, 0, st>>>(n_nodes, own_m2l, own_p2p,
-                                                                    cnt_m2l, cnt_p2p, tot_m2l,
-                                                                    tot_p2p);
+hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_t* tr_cnt,
+                               int64_t* tot, hipStream_t st) {
+  if (n_nodes <= 0) return hipSuccess;
+  k_walk_offsets<<<(unsigned)((n_nodes + 255) / 256), 256, 0, st>>>(n_nodes, own, tr_cnt, tot);
   return hipGetLastError();
 }
-hipError_t launch_walk_copy_totals(const int64_t* m2l_total, const int64_t* p2p_total,
-                                   const int64_t* task_total, const int64_t* part_total,
-                                   const int64_t* union_total, const int64_t* tail_total,
+hipError_t launch_walk_copy_totals(const int64_t* p2p_total, const int64_t* task_total,
+                                   const int64_t* part_total, const int64_t* tail_total,
                                    Control* ctrl, hipStream_t st) {
-  k_walk_copy_totals<<<1, 64, 0, st>>>(m2l_total, p2p_total, task_total, part_total, union_total,
-                                       tail_total, ctrl);
+  k_walk_copy_totals<<<1, 64, 0, st>>>(p2p_total, task_total, part_total, tail_total, ctrl);
   return hipGetLastError();
 }
 hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
-                             int64_t n_nodes, const int64_t* m2l_off, const int32_t* own_m2l,
-                             const int64_t* start_m2l, int32_t* m2l_src, const int64_t* p2p_off,
-                             const int32_t* own_p2p, const int64_t* start_p2p, int32_t* p2p_src,
-                             hipStream_t st) {
+                             int kind, int64_t n_nodes, const int64_t* off, const int32_t* own,
+                             const int64_t* start, int32_t* src, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  k_tr_scatter<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-      keys, n, key_shift, kind_bit, n_nodes, m2l_off, own_m2l, start_m2l, m2l_src, p2p_off,
-      own_p2p, start_p2p, p2p_src);
+  k_tr_scatter<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, key_shift, kind_bit, kind,
+                                                            n_nodes, off, own, start, src);
   return hipGetLastError();
 }
-
-static unsigned walk_grid(const WalkArgs& a) {
-  int64_t blocks = (a.lvl_count + WK_WAVES - 1) / WK_WAVES;
+hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
+                                const int32_t* first_child, const uint8_t* n_child,
+                                const uint64_t* pool, const int64_t* uoff, const int32_t* ucnt,
+                                const int64_t* off, int32_t* src, hipStream_t st) {
+  if (n_parents <= 0) return hipSuccess;
+  int64_t blocks = (n_parents + WK_WAVES - 1) / WK_WAVES;
   if (blocks > 16384) blocks = 16384;
-  if (blocks < 1) blocks = 1;
-  return (unsigned)blocks;
-}
-
-hipError_t launch_walk_pass1(const WalkArgs& a, hipStream_t st) {
-  k_walk_pass1<<<walk_grid(a), WK_THREADS, 0, st>>>(a);
+  k_union_scatter<<<(unsigned)blocks, WK_THREADS, 0, st>>>(parents, n_parents, first_child,
+                                                           n_child, pool, uoff, ucnt, off, src);
   return hipGetLastError();
 }
-hipError_t launch_walk_pass2(const WalkArgs& a, hipStream_t st) {
-  k_walk_pass2<<<walk_grid(a), WK_THREADS, 0, st>>>(a);
+hipError_t launch_walk(int pass, const WalkArgs& a, hipStream_t st) {
+  if (a.pcnt <= 0) return hipSuccess;
+  int64_t blocks = (a.pcnt + WK_WAVES - 1) / WK_WAVES;
+  if (blocks > 16384) blocks = 16384;
+  k_walk<<<(unsigned)blocks, WK_THREADS, 0, st>>>(pass, a);
   return hipGetLastError();
 }
 
