@@ -61,6 +61,54 @@ def roofline_obj(flops_per_launch, ms, dtype_peak, traffic=None):
             "frac": round(achieved / dtype_peak, 4), "traffic": traffic}
 
 
+# kernel -> (source file whose text the traffic figure is tied to, profile summary)
+KERNEL_SOURCES = {
+    "p2p": "multipole_body_gravity_amd/csrc/fmm_p2p.hip",
+    "m2l_sib": "multipole_body_gravity_amd/csrc/fmm_m2l.hip",
+    "m2l_tail": "multipole_body_gravity_amd/csrc/fmm_m2l.hip",
+}
+
+
+def source_sha(kernel):
+    import hashlib
+    path = os.path.join(ROOT, KERNEL_SOURCES[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None.
+
+    The summary (profiles/traffic_<kernel>_<workload>.md) holds one line
+    'traffic_json: {...}' with the calibrated FETCH_SIZE + WRITE_SIZE bytes and
+    the hash of the kernel's source file when the counters were taken; a
+    different hash means the kernel changed since, and no figure is reported.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic_json:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("source_sha") == source_sha(kernel):
+                    return rec["bytes_per_launch"]
+    return None
+
+
+def copy_probe(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for calibrating HBM byte counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                      "reps": reps}))
+
+
 def cpu_baseline(pos, mass, cfg):
     from oracle import oracle as orc
     cores = len(os.sched_getaffinity(0))
@@ -79,11 +127,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
 
@@ -113,28 +167,42 @@ def main():
     tgt = np.repeat(np.arange(st["n_nodes"]), np.diff(lists["p2p_off"]))
     p2p_pairs = int(np.sum(cnt[tgt] * cnt[lists["p2p_src"]]) - cfg["n"])  # minus self terms
     n_m2l = st["n_m2l"]
+    # own M2L entries (source at the target's level or coarser: the sibling kernel)
+    # and transposed ones (deeper sources: the tail kernel)
+    lvl = tree["level"].astype(np.int64)
+    mt = np.repeat(np.arange(st["n_nodes"]), np.diff(lists["m2l_off"]))
+    n_m2l_tr = int(np.sum(lvl[lists["m2l_src"]] > lvl[mt]))
+    n_m2l_own = n_m2l - n_m2l_tr
+    del lists, tgt, mt
 
     plan.set_timing(True)
     stage_sum = {k: 0.0 for k in st["stage_ms"]}
+    kern_sum = {k: 0.0 for k in st["kernel_ms"]}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         plan.build(tpos, tmass)
         plan.eval(phi, acc)
-        s = plan.stats()  # reads the step's HIP-event stage times (synchronizes)
+        s = plan.stats()  # reads the step's HIP-event stage and kernel times (synchronizes)
         for k, v in s["stage_ms"].items():
             stage_sum[k] += v
+        for k, v in s["kernel_ms"].items():
+            kern_sum[k] += v
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_avg = {k: v / args.steps for k, v in stage_sum.items()}
+    kern_avg = {k: v / args.steps for k, v in kern_sum.items()}
     ms_step = wall / args.steps * 1e3
 
-    m2l_flops = n_m2l * m2l_flops_per_pair(cfg["order"])
-    p2p_flops = p2p_pairs * P2P_FLOPS_PER_PAIR
+    # algorithmic flops per launch of each compute kernel, over its measured
+    # average launch time (HIP events recorded on the launch stream)
+    fpp = m2l_flops_per_pair(cfg["order"])
+    flops = {"m2l_sib": n_m2l_own * fpp, "m2l_tail": n_m2l_tr * fpp,
+             "p2p": p2p_pairs * P2P_FLOPS_PER_PAIR}
     peak = FP64_VECTOR_PEAK_TFLOPS if cfg["dtype"] == "f64" else FP32_VECTOR_PEAK_TFLOPS
-    rl = {"m2l": roofline_obj(m2l_flops, stage_avg["m2l"], peak),
-          "p2p": roofline_obj(p2p_flops, stage_avg["p2p"], peak)}
-    dominant = "m2l" if stage_avg["m2l"] >= stage_avg["p2p"] else "p2p"
+    rl = {k: roofline_obj(flops[k], kern_avg[k], peak, measured_traffic(k, args.workload))
+          for k in flops if kern_avg[k] > 0}
+    dominant = max(rl, key=lambda k: kern_avg[k])
     roof = dict(rl[dominant])
     roof["kernel"] = dominant
 
@@ -155,12 +223,13 @@ def main():
                    "order": cfg["order"], "theta": cfg["theta"], "leaf_size": cfg["leaf"],
                    "seed": cfg["seed"]},
         "roofline": roof,
-        "roofline_other": rl["p2p" if dominant == "m2l" else "m2l"] | {
-            "kernel": "p2p" if dominant == "m2l" else "m2l"},
+        "roofline_other": {k: v for k, v in rl.items() if k != dominant},
         "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()},
-        "work": {"n_m2l": n_m2l, "p2p_pairs": p2p_pairs, "n_nodes": st["n_nodes"],
+        "kernel_ms": {k: round(v, 4) for k, v in kern_avg.items()},
+        "work": {"n_m2l": n_m2l, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,
+                 "p2p_pairs": p2p_pairs, "n_nodes": st["n_nodes"],
                  "n_leaves": st["n_leaves"], "depth": st["depth"],
-                 "m2l_flops_per_pair": m2l_flops_per_pair(cfg["order"])},
+                 "m2l_flops_per_pair": fpp, "p2p_flops_per_pair": P2P_FLOPS_PER_PAIR},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pos, mass, cfg)

@@ -77,6 +77,17 @@ enum fmm_stage {
   FMM_N_STAGES = 8
 };
 
+/* Kernel indices of fmm_stats_t.kernel_ms: single launches inside the M2L
+ * and P2P stages (filled when timing is enabled, -1 when the kernel did not
+ * run in the last eval). */
+enum fmm_kernel {
+  FMM_KERNEL_M2L_SIB = 0,     /* M2L over the sibling unions (own entries) */
+  FMM_KERNEL_M2L_TAIL = 1,    /* M2L over the transposed tails            */
+  FMM_KERNEL_P2P = 2,         /* near-field pair sums                     */
+  FMM_KERNEL_P2P_COMBINE = 3, /* ordered sum of split leaves' partials    */
+  FMM_N_KERNELS = 4
+};
+
 typedef struct {
   int64_t n, n_nodes, n_leaves, n_m2l, n_p2p;
   int32_t depth, order, leaf_size, dtype;
@@ -84,7 +95,8 @@ typedef struct {
   double lo[3], side;    /* root cube */
   float stage_ms[FMM_N_STAGES]; /* last build/eval, when timing is on */
   int32_t walk_retries;  /* workspace regrowths during the last walk */
-  int32_t reserved[7];
+  float kernel_ms[FMM_N_KERNELS]; /* last eval, when timing is on */
+  int32_t reserved[3];
 } fmm_stats_t;
 
 /* Create a plan for N particles.  N in [1, 2^31), order in [0, FMM_MAX_ORDER],

@@ -330,6 +330,8 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
     return fail(FMM_ERR_OOM);
   for (int i = 0; i < 2 * FMM_N_STAGES; i++)
     if (hipEventCreate(&p->ev[i]) != hipSuccess) return fail(FMM_ERR_HIP);
+  for (int i = 0; i < 2 * FMM_N_KERNELS; i++)
+    if (hipEventCreate(&p->kev[i]) != hipSuccess) return fail(FMM_ERR_HIP);
   *out = p;
   return FMM_OK;
 }
@@ -358,6 +360,8 @@ int fmm_destroy(fmm_plan_t p) {
   if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);
   for (int i = 0; i < 2 * FMM_N_STAGES; i++)
     if (p->ev[i]) (void)hipEventDestroy(p->ev[i]);
+  for (int i = 0; i < 2 * FMM_N_KERNELS; i++)
+    if (p->kev[i]) (void)hipEventDestroy(p->kev[i]);
   delete p;
   return FMM_OK;
 }
@@ -484,6 +488,9 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   ma.mrec = p->mpole.p;
   ma.part = p->tail_part.p;
   ma.local = p->local.p;
+  for (int k = 0; k < FMM_N_KERNELS; k++) p->kran[k] = false;
+  ma.ev = p->timing ? p->kev : nullptr;
+  ma.ran = p->kran;
   TRY_HIP(launch_m2l(dt, ord, ma, st));
   rec(p, FMM_STAGE_M2L, 1, st);
 
@@ -499,7 +506,9 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   TRY_HIP(launch_p2p(dt, p->p2p_task.p, p->n_p2p_tasks, leaves, p->n_leaves,
                      P<int64_t>(p->p2p_toff), P<int64_t>(p->p2p_poff), P<int32_t>(p->nbegin),
                      P<int32_t>(p->ncount), P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
-                     P<int32_t>(p->idx), phi, acc, p->p2p_part.p, p->n_p2p_part > 0, st));
+                     P<int32_t>(p->idx), phi, acc, p->p2p_part.p, p->n_p2p_part > 0,
+                     p->timing ? p->kev + 2 * FMM_KERNEL_P2P : nullptr,
+                     p->kran + FMM_KERNEL_P2P, st));
   rec(p, FMM_STAGE_P2P, 1, st);
   p->evaluated = true;
   return FMM_OK;
@@ -531,6 +540,13 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
         out->stage_ms[s] = ms;
       else
         out->stage_ms[s] = -1.f;
+    }
+    for (int k = 0; k < FMM_N_KERNELS; k++) {
+      float ms = -1.f;
+      if (!p->kran[k] ||
+          hipEventElapsedTime(&ms, p->kev[2 * k], p->kev[2 * k + 1]) != hipSuccess)
+        ms = -1.f;
+      out->kernel_ms[k] = ms;
     }
     (void)hipGetLastError();
   }

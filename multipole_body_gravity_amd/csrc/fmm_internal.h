@@ -110,6 +110,8 @@ struct fmm_plan_s {
 
   mbg::Control* ctrl_host = nullptr;  // pinned
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
+  hipEvent_t kev[2 * FMM_N_KERNELS] = {};  // begin/end of single kernel launches
+  bool kran[FMM_N_KERNELS] = {};          // the kernel ran in the last eval
   float stage_ms[FMM_N_STAGES] = {0};
 };
 
@@ -250,6 +252,8 @@ struct M2LArgs {
   const void* mrec;       // multipole records
   void* part;             // task partials (n_tasks x K)
   void* local;
+  hipEvent_t* ev;         // null, or begin/end events of the sibling and tail kernels
+  bool* ran;              // with ev: set when the kernel was launched
 };
 hipError_t launch_m2l(int dtype, int order, const M2LArgs& a, hipStream_t st);
 hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
@@ -273,7 +277,7 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                       const int32_t* begin, const int32_t* count, const int32_t* src,
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
-                      void* part, bool any_multi, hipStream_t st);
+                      void* part, bool any_multi, hipEvent_t* ev, bool* ran, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // expansions in the plan's dtype/convention -> fp64 raw moments / derivatives
 // copy the node centres into the multipole records

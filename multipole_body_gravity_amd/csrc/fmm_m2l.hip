@@ -331,16 +331,27 @@ template <typename T>
 static void m2l_dispatch(int order, hipStream_t st, const M2LArgs& a) {
   const unsigned gs = m2l_grid(a.n_parents), gt = m2l_grid((a.n_tasks + 7) / 8);
   const unsigned char* rec = (const unsigned char*)a.mrec;
+  // a.ev (optional): begin/end of the sibling kernel, then of the tail kernel
+  auto mark = [&](int k) {
+    if (a.ev) (void)hipEventRecord(a.ev[k], st);
+    if (a.ev && (k & 1)) a.ran[k >> 1] = true;
+  };
   switch (order) {
 #define M2L_CASE(P)                                                                          \
   case P:                                                                                    \
-    if (a.n_parents > 0)                                                                     \
+    if (a.n_parents > 0) {                                                                   \
+      mark(0);                                                                               \
       k_m2l_sib<T, P><<<gs, M2L_THREADS, 0, st>>>(a.n_parents, a.parents, a.first_child,      \
                                                   a.n_child, a.upool, a.u_off, a.u_cnt,      \
                                                   a.centre, rec, (T*)a.local);               \
-    if (a.n_tasks > 0)                                                                       \
+      mark(1);                                                                               \
+    }                                                                                        \
+    if (a.n_tasks > 0) {                                                                     \
+      mark(2);                                                                               \
       k_m2l_tail<T, P><<<gt, M2L_THREADS, 0, st>>>(a.n_tasks, a.tasks, a.leaves, a.keys,      \
                                                    a.src_mask, a.centre, rec, (T*)a.part);   \
+      mark(3);                                                                               \
+    }                                                                                        \
     break;
     M2L_CASE(0) M2L_CASE(1) M2L_CASE(2) M2L_CASE(3) M2L_CASE(4)
     M2L_CASE(5) M2L_CASE(6) M2L_CASE(7) M2L_CASE(8)

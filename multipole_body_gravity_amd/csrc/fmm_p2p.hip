@@ -24,7 +24,7 @@ namespace mbg {
 
 constexpr int P2P_THREADS = 256;
 constexpr int P2P_WAVES = P2P_THREADS / WAVE;
-constexpr int TASK_E = 64;  // source leaves per task
+constexpr int TASK_E = 256;  // source leaves per task
 
 struct P2PTask {
   int64_t e0, e1;  // slice of the target leaf's list
@@ -84,7 +84,7 @@ __global__ void k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t
 
 // ---- near-field sums ----
 constexpr int TILE = 2 * WAVE;       // source particles staged per round
-constexpr int MAXQ = 4096;           // source particles per owner table
+constexpr int MAXQ = 2048;           // source particles per owner table
 
 template <typename T>
 __device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp, T& fx, T& fy,
@@ -117,7 +117,7 @@ struct P2PShared {
 };
 
 template <typename T>
-__global__ void __launch_bounds__(P2P_THREADS)
+__global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_eu(5, 8)))
     k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
           const int32_t* __restrict__ count, const int32_t* __restrict__ src,
           const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
@@ -179,7 +179,15 @@ __global__ void __launch_bounds__(P2P_THREADS)
           }
           __builtin_amdgcn_wave_barrier();
           const int nv = min(TILE, tot - q0);
-          for (int s = sl; s < nv; s += ns) {
+          int s = sl;
+          for (; s + ns < nv; s += 2 * ns) {  // two sources per step: four independent pairs
+            const P4<T> pj = sh.tile[s], pk = sh.tile[s + ns];
+            pair_acc(p0, pj, a0, a1, a2, a3);
+            pair_acc(p1, pj, b0, b1, b2, b3);
+            pair_acc(p0, pk, a0, a1, a2, a3);
+            pair_acc(p1, pk, b0, b1, b2, b3);
+          }
+          if (s < nv) {
             const P4<T> pj = sh.tile[s];
             pair_acc(p0, pj, a0, a1, a2, a3);
             pair_acc(p1, pj, b0, b1, b2, b3);
@@ -317,27 +325,39 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                       const int32_t* begin, const int32_t* count, const int32_t* src,
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
-                      void* part, bool any_multi, hipStream_t st) {
+                      void* part, bool any_multi, hipEvent_t* ev, bool* ran, hipStream_t st) {
+  // ev (optional): begin/end of the pair kernel, then of the combine
   if (n_tasks == 0) return hipSuccess;
   int64_t blocks = (n_tasks + P2P_WAVES - 1) / P2P_WAVES;
   if (blocks > 65535) blocks = 65535;
   int64_t cblocks = n_leaves < 65535 ? n_leaves : 65535;
-  if (dtype == FMM_F64) {
+  if (ev) (void)hipEventRecord(ev[0], st);
+  if (dtype == FMM_F64)
     k_p2p<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
         (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<double>*)pts,
         (const P4<double>*)far, perm, (double*)phi, (double*)acc, (double*)part);
-    if (any_multi)
-      k_p2p_combine<double><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
-          leaves, n_leaves, task_off, part_off, begin, count, (const double*)part,
-          (const P4<double>*)far, perm, (double*)phi, (double*)acc);
-  } else {
+  else
     k_p2p<float><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
         (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<float>*)pts,
         (const P4<float>*)far, perm, (float*)phi, (float*)acc, (float*)part);
-    if (any_multi)
+  if (ev) {
+    (void)hipEventRecord(ev[1], st);
+    ran[0] = true;
+  }
+  if (any_multi) {
+    if (ev) (void)hipEventRecord(ev[2], st);
+    if (dtype == FMM_F64)
+      k_p2p_combine<double><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
+          leaves, n_leaves, task_off, part_off, begin, count, (const double*)part,
+          (const P4<double>*)far, perm, (double*)phi, (double*)acc);
+    else
       k_p2p_combine<float><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
           leaves, n_leaves, task_off, part_off, begin, count, (const float*)part,
           (const P4<float>*)far, perm, (float*)phi, (float*)acc);
+    if (ev) {
+      (void)hipEventRecord(ev[3], st);
+      ran[1] = true;
+    }
   }
   return hipGetLastError();
 }

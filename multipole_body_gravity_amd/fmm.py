@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libmbg_fmm.so")
 FMM_F32, FMM_F64 = 0, 1
 MAX_ORDER = 8
 STAGES = ["keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p"]
+KERNELS = ["m2l_sib", "m2l_tail", "p2p", "p2p_combine"]  # fmm_stats_t.kernel_ms order
 _ERR = {0: "ok", -1: "invalid argument", -2: "plan not built", -3: "device out of memory",
         -4: "HIP runtime error", -5: "non-finite position or mass", -6: "no HIP device"}
 
@@ -35,7 +36,7 @@ class _Stats(ctypes.Structure):
                 ("order", ctypes.c_int32), ("leaf_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("theta", ctypes.c_double), ("lo", ctypes.c_double * 3), ("side", ctypes.c_double),
                 ("stage_ms", ctypes.c_float * 8), ("walk_retries", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 7)]
+                ("kernel_ms", ctypes.c_float * 4), ("reserved", ctypes.c_int32 * 3)]
 
 
 _lib = None
@@ -141,7 +142,8 @@ class Plan:
         return {"n": s.n, "n_nodes": s.n_nodes, "n_leaves": s.n_leaves, "n_m2l": s.n_m2l,
                 "n_p2p": s.n_p2p, "depth": s.depth, "order": s.order, "leaf_size": s.leaf_size,
                 "theta": s.theta, "lo": list(s.lo), "side": s.side, "walk_retries": s.walk_retries,
-                "stage_ms": {k: float(v) for k, v in zip(STAGES, s.stage_ms)}}
+                "stage_ms": {k: float(v) for k, v in zip(STAGES, s.stage_ms)},
+                "kernel_ms": {k: float(v) for k, v in zip(KERNELS, s.kernel_ms)}}
 
     def copy_keys(self):
         keys = np.zeros(self.n, dtype=np.uint64)
