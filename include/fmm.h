@@ -78,8 +78,8 @@ enum fmm_stage {
 };
 
 /* Kernel indices of fmm_stats_t.kernel_ms: single launches inside the M2L
- * and P2P stages (filled when timing is enabled, -1 when the kernel did not
- * run in the last eval). */
+ * and P2P stages (filled when timing is enabled; 0 for a kernel that did not
+ * run). */
 enum fmm_kernel {
   FMM_KERNEL_M2L_SIB = 0,     /* M2L over the sibling unions (own entries) */
   FMM_KERNEL_M2L_TAIL = 1,    /* M2L over the transposed tails            */
@@ -93,10 +93,12 @@ typedef struct {
   int32_t depth, order, leaf_size, dtype;
   double theta;
   double lo[3], side;    /* root cube */
-  float stage_ms[FMM_N_STAGES]; /* last build/eval, when timing is on */
+  float stage_ms[FMM_N_STAGES]; /* mean over the timed steps, see fmm_set_timing */
   int32_t walk_retries;  /* workspace regrowths during the last walk */
-  float kernel_ms[FMM_N_KERNELS]; /* last eval, when timing is on */
-  int32_t reserved[3];
+  float kernel_ms[FMM_N_KERNELS]; /* mean over the timed evals */
+  int32_t timed_builds;  /* builds and evals the means are taken over */
+  int32_t timed_evals;
+  int32_t reserved[1];
 } fmm_stats_t;
 
 /* Create a plan for N particles.  N in [1, 2^31), order in [0, FMM_MAX_ORDER],
@@ -124,10 +126,15 @@ int fmm_destroy(fmm_plan_t plan);
 /* Static string for a status code. */
 const char* fmm_strerror(int code);
 
-/* Turn per-stage HIP-event timing on (1) or off (0); read via fmm_stats. */
+/* Turn HIP-event timing of the stages and of the main kernels on (1) or off
+ * (0).  Events are recorded on the caller's stream, between launches; their
+ * times are collected at the next synchronization the library makes anyway
+ * (the first one of the next build) or by fmm_stats, so timing adds no
+ * synchronization.  Enabling resets the means. */
 int fmm_set_timing(fmm_plan_t plan, int enable);
 
-/* Sizes of the last build and, with timing on, stage times (synchronizes). */
+/* Sizes of the last build and, with timing on, the mean stage and kernel times
+ * since timing was enabled (synchronizes the device). */
 int fmm_stats(fmm_plan_t plan, fmm_stats_t* out);
 
 /* ---- introspection (host copies for parity checks; each synchronizes) ---- */

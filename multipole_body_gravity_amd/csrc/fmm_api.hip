@@ -74,6 +74,41 @@ int bbox_blocks(int64_t n) {
   return (int)std::min<int64_t>(std::max<int64_t>(b, 1), 1024);
 }
 
+// Timing: events are read only after a synchronization that follows them.
+// The first three build stages are collected at the end of their build (after
+// its last synchronization); the walk stage and the eval's stages and kernels
+// at the first synchronization of the next build, or by fmm_stats.
+double elapsed(hipEvent_t a, hipEvent_t b) {
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, a, b) != hipSuccess) {
+    (void)hipGetLastError();
+    ms = 0.f;
+  }
+  return (double)ms;
+}
+void collect_early_build(fmm_plan_t p) {
+  if (!p->timing) return;
+  for (int s = FMM_STAGE_KEYS; s <= FMM_STAGE_TREE; s++)
+    p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
+  p->pend_build = true;  // the walk stage is still pending
+}
+void collect_pending(fmm_plan_t p) {
+  if (p->pend_build) {
+    p->stage_sum[FMM_STAGE_WALK] +=
+        elapsed(p->ev[2 * FMM_STAGE_WALK], p->ev[2 * FMM_STAGE_WALK + 1]);
+    p->n_timed_builds++;
+    p->pend_build = false;
+  }
+  if (p->pend_eval) {
+    for (int s = FMM_STAGE_UP; s <= FMM_STAGE_P2P; s++)
+      p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
+    for (int k = 0; k < FMM_N_KERNELS; k++)
+      if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
+    p->n_timed_evals++;
+    p->pend_eval = false;
+  }
+}
+
 int sync_ctrl(fmm_plan_t p, hipStream_t st) {
   TRY_HIP(hipMemcpyAsync(p->ctrl_host, p->ctrl.p, sizeof(Control), hipMemcpyDeviceToHost, st));
   TRY_HIP(hipStreamSynchronize(st));
@@ -369,6 +404,14 @@ int fmm_destroy(fmm_plan_t p) {
 int fmm_set_timing(fmm_plan_t p, int enable) {
   if (!p) return FMM_ERR_ARG;
   p->timing = enable != 0;
+  if (p->timing) {
+    TRY_HIP(hipSetDevice(p->device));
+    TRY_HIP(hipDeviceSynchronize());
+    p->pend_build = p->pend_eval = false;
+    for (double& x : p->stage_sum) x = 0.0;
+    for (double& x : p->kernel_sum) x = 0.0;
+    p->n_timed_builds = p->n_timed_evals = 0;
+  }
   return FMM_OK;
 }
 
@@ -402,6 +445,7 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
                              P<int64_t>(p->lvl_blkcnt), p->scan_tmp.p, ctrl, st));
   TRY_HIP(hipMemcpyAsync(&p->root_host, root, sizeof(RootInfo), hipMemcpyDeviceToHost, st));
   TRY(sync_ctrl(p, st));
+  collect_pending(p);  // the previous step's events have completed
   if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;
   const Control& c = *p->ctrl_host;
   const int64_t nn = c.level_off[MAX_LEVELS];
@@ -446,6 +490,7 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   rec(p, FMM_STAGE_WALK, 0, st);
   TRY(run_walk(p, st));
   rec(p, FMM_STAGE_WALK, 1, st);
+  collect_early_build(p);  // keys, sort and tree ended before the walk's last sync
   p->built = true;
   return FMM_OK;
 }
@@ -510,6 +555,7 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
                      p->timing ? p->kev + 2 * FMM_KERNEL_P2P : nullptr,
                      p->kran + FMM_KERNEL_P2P, st));
   rec(p, FMM_STAGE_P2P, 1, st);
+  p->pend_eval = p->timing;
   p->evaluated = true;
   return FMM_OK;
 }
@@ -533,22 +579,15 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
     out->side = p->root_host.side;
   }
   if (p->timing) {
+    TRY_HIP(hipSetDevice(p->device));
     TRY_HIP(hipDeviceSynchronize());
-    for (int s = 0; s < FMM_N_STAGES; s++) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, p->ev[2 * s], p->ev[2 * s + 1]) == hipSuccess)
-        out->stage_ms[s] = ms;
-      else
-        out->stage_ms[s] = -1.f;
-    }
-    for (int k = 0; k < FMM_N_KERNELS; k++) {
-      float ms = -1.f;
-      if (!p->kran[k] ||
-          hipEventElapsedTime(&ms, p->kev[2 * k], p->kev[2 * k + 1]) != hipSuccess)
-        ms = -1.f;
-      out->kernel_ms[k] = ms;
-    }
-    (void)hipGetLastError();
+    collect_pending(p);
+    const double nb = std::max(1, p->n_timed_builds), ne = std::max(1, p->n_timed_evals);
+    for (int s = 0; s < FMM_N_STAGES; s++)
+      out->stage_ms[s] = (float)(p->stage_sum[s] / (s <= FMM_STAGE_WALK ? nb : ne));
+    for (int k = 0; k < FMM_N_KERNELS; k++) out->kernel_ms[k] = (float)(p->kernel_sum[k] / ne);
+    out->timed_builds = p->n_timed_builds;
+    out->timed_evals = p->n_timed_evals;
   }
   return FMM_OK;
 }

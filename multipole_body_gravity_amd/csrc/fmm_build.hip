@@ -263,66 +263,123 @@ __global__ void __launch_bounds__(RS_THREADS)
   h[threadIdx.x] = 0;
   __syncthreads();
   int64_t base = (int64_t)blockIdx.x * RS_TILE;
-#pragma unroll 4
+  int dg[RS_ROUNDS];  // all loads issued before the first use
+#pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
     int64_t i = base + r * RS_THREADS + threadIdx.x;
-    if (i < n) atomicAdd(&h[(keys[i] >> shift) & 255u], 1);
+    dg[r] = i < n ? (int)((keys[i] >> shift) & 255u) : -1;
+  }
+  // one LDS atomic per distinct digit of a wave and round (equal digits found
+  // by ballots): few distinct digits do not serialize on one counter
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; r++) {
+    const int d = dg[r];
+    uint64_t mask = __ballot(d >= 0);
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+      const uint64_t bb = __ballot((d >> b) & 1);
+      mask &= ((d >> b) & 1) ? bb : ~bb;
+    }
+    if (d >= 0 && (mask & lt) == 0) atomicAdd(&h[d], __popcll(mask));
   }
   __syncthreads();
   hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
 }
 
-// Elements of a tile are visited in input order (round-major, then thread):
-// within a round, ranks among equal digits come from wave ballots (lower
-// lanes first) and per-wave counts (lower waves first), so the scatter is
-// stable.
+// Scatter of one tile, stable.  Wave w ranks the w-th quarter of the tile on
+// its own, 64 elements per round in input order: ranks among equal digits
+// come from wave ballots (lower lanes first) added to the wave's running count
+// of the digit.  The per-wave counts are then combined in wave order (earlier
+// quarters first) and over digits, the tile is reordered by digit in LDS and
+// written out in that order, so each digit's run goes to consecutive addresses.
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
                     int64_t n, int shift, const int32_t* hist_scan, int nblk) {
-  __shared__ int bin_base[256];
-  __shared__ int wcnt[RS_THREADS / WAVE][256];
-  const int tid = threadIdx.x, w = tid / WAVE;
-  bin_base[tid] = hist_scan[(int64_t)tid * nblk + blockIdx.x];
+  constexpr int NW = RS_THREADS / WAVE;
+  constexpr int WTILE = RS_TILE / NW;  // elements per wave
+  __shared__ uint64_t skey[RS_TILE];
+  __shared__ int32_t sval[RS_TILE];
+  __shared__ int wcnt[NW][256];  // per-wave digit counts; then per-wave starts
+  __shared__ int dstart[256];    // tile-local start of each digit's run
+  __shared__ int gbase[256];     // global start of this tile's part of each digit
+  __shared__ int wsum[NW];
+  const int tid = threadIdx.x, w = tid / WAVE, lane = __lane_id();
+  gbase[tid] = hist_scan[(int64_t)tid * nblk + blockIdx.x];
 #pragma unroll
-  for (int i = 0; i < RS_THREADS / WAVE; i++) wcnt[i][tid] = 0;
+  for (int q = 0; q < NW; q++) wcnt[q][tid] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * RS_TILE;
+  const int64_t wbase = (int64_t)blockIdx.x * RS_TILE + (int64_t)w * WTILE;
   const uint64_t lt = lanemask_lt();
+  int rk[RS_ROUNDS];  // rank of this lane's element of each round among its digit in the wave
+  uint64_t kk[RS_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; r++) {  // all loads issued before the first use
+    const int64_t i = wbase + r * WAVE + lane;
+    kk[r] = i < n ? kin[i] : 0ull;
+  }
+#pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
-    int64_t i = base + r * RS_THREADS + tid;
-    bool valid = i < n;
-    uint64_t key = valid ? kin[i] : 0ull;
-    int32_t val = valid ? vin[i] : 0;
-    int d = (int)((key >> shift) & 255u);
+    const int64_t i = wbase + r * WAVE + lane;
+    const bool valid = i < n;
+    const int d = (int)((kk[r] >> shift) & 255u);
     uint64_t mask = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; b++) {
-      uint64_t bb = __ballot((d >> b) & 1);
+      const uint64_t bb = __ballot((d >> b) & 1);
       mask &= ((d >> b) & 1) ? bb : ~bb;
     }
-    int rank = __popcll(mask & lt);
-    if (valid && rank == 0) wcnt[w][d] = __popcll(mask);
-    __syncthreads();
-    int pos = 0;
-    if (valid) {
-      pos = bin_base[d] + rank;
-      for (int j = 0; j < w; j++) pos += wcnt[j][d];
-    }
-    __syncthreads();
-    {
-      int s = 0;
+    const int rank = __popcll(mask & lt);
+    const int before = valid ? wcnt[w][d] : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) wcnt[w][d] = before + __popcll(mask);
+    __builtin_amdgcn_wave_barrier();
+    rk[r] = before + rank;
+  }
+  __syncthreads();
+  // thread d: starts of digit d in each wave's quarter, and its tile total
+  int tot = 0;
 #pragma unroll
-      for (int j = 0; j < RS_THREADS / WAVE; j++) {
-        s += wcnt[j][tid];
-        wcnt[j][tid] = 0;
-      }
-      bin_base[tid] += s;
-    }
+  for (int q = 0; q < NW; q++) {
+    const int c = wcnt[q][tid];
+    wcnt[q][tid] = tot;
+    tot += c;
+  }
+  {
+    const int incl = wave_incl_scan(tot);
+    if (lane == WAVE - 1) wsum[w] = incl;
     __syncthreads();
-    if (valid) {
-      kout[pos] = key;
-      vout[pos] = val;
+    int off = 0;
+    for (int q = 0; q < w; q++) off += wsum[q];
+    dstart[tid] = off + incl - tot;
+  }
+  __syncthreads();
+  int32_t vv[RS_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; r++) {
+    const int64_t i = wbase + r * WAVE + lane;
+    vv[r] = i < n ? vin[i] : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; r++) {
+    const int64_t i = wbase + r * WAVE + lane;
+    if (i < n) {
+      const uint64_t key = kk[r];
+      const int d = (int)((key >> shift) & 255u);
+      const int lp = dstart[d] + wcnt[w][d] + rk[r];
+      skey[lp] = key;
+      sval[lp] = vv[r];
     }
+  }
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RS_TILE;
+  const int tn = (int)min((int64_t)RS_TILE, n - base);
+  for (int j = tid; j < tn; j += RS_THREADS) {
+    const uint64_t key = skey[j];
+    const int d = (int)((key >> shift) & 255u);
+    const int64_t o = (int64_t)gbase[d] + (j - dstart[d]);
+    kout[o] = key;
+    vout[o] = sval[j];
   }
 }
 

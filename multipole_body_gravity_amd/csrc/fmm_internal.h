@@ -112,7 +112,9 @@ struct fmm_plan_s {
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
   hipEvent_t kev[2 * FMM_N_KERNELS] = {};  // begin/end of single kernel launches
   bool kran[FMM_N_KERNELS] = {};          // the kernel ran in the last eval
-  float stage_ms[FMM_N_STAGES] = {0};
+  bool pend_build = false, pend_eval = false;  // events recorded, not yet collected
+  double stage_sum[FMM_N_STAGES] = {0}, kernel_sum[FMM_N_KERNELS] = {0};
+  int32_t n_timed_builds = 0, n_timed_evals = 0;
 };
 
 namespace mbg {

@@ -36,7 +36,8 @@ class _Stats(ctypes.Structure):
                 ("order", ctypes.c_int32), ("leaf_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("theta", ctypes.c_double), ("lo", ctypes.c_double * 3), ("side", ctypes.c_double),
                 ("stage_ms", ctypes.c_float * 8), ("walk_retries", ctypes.c_int32),
-                ("kernel_ms", ctypes.c_float * 4), ("reserved", ctypes.c_int32 * 3)]
+                ("kernel_ms", ctypes.c_float * 4), ("timed_builds", ctypes.c_int32),
+                ("timed_evals", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 _lib = None
@@ -143,7 +144,8 @@ class Plan:
                 "n_p2p": s.n_p2p, "depth": s.depth, "order": s.order, "leaf_size": s.leaf_size,
                 "theta": s.theta, "lo": list(s.lo), "side": s.side, "walk_retries": s.walk_retries,
                 "stage_ms": {k: float(v) for k, v in zip(STAGES, s.stage_ms)},
-                "kernel_ms": {k: float(v) for k, v in zip(KERNELS, s.kernel_ms)}}
+                "kernel_ms": {k: float(v) for k, v in zip(KERNELS, s.kernel_ms)},
+                "timed_builds": s.timed_builds, "timed_evals": s.timed_evals}
 
     def copy_keys(self):
         keys = np.zeros(self.n, dtype=np.uint64)
