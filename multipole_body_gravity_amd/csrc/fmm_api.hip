@@ -246,6 +246,12 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   }
   p->tr_sorted = sorted;
 
+  // launch order of the M2L sibling blocks
+  TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
+  TRY(grow(p->ord_hist, 256 * sizeof(int)));
+  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, P<int>(p->ord_hist), P<int32_t>(p->m2l_order),
+                           st));
+
   // P2P lists: own entries (from the parents' P2P unions) then transposed ones
   int64_t* p2p_off = P<int64_t>(p->p2p_off);
   TRY_HIP(launch_walk_offsets(nn, a.own_p2p, tr_cnt + nn, P<int64_t>(p->tot_p2p), st));
@@ -274,9 +280,11 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   p->n_p2p_part = p->ctrl_host->n_p2p_part;
   p->n_tail_tasks = p->ctrl_host->n_tail_tasks;
   TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
+  TRY(grow(p->p2p_task_tmp, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
   TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
   TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, p2p_off,
-                               P<int32_t>(p->ncount), p->p2p_task.p, st));
+                               P<int32_t>(p->ncount), p->p2p_task.p, p->p2p_task_tmp.p,
+                               P<int>(p->ord_hist), st));
   TRY(grow(p->tail_task, (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * sizeof(TailTask)));
   TRY(grow(p->tail_part,
            (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * p->K * wbytes(p->dtype)));
@@ -390,6 +398,7 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->tr_vals_alt, &p->m2l_off,    &p->m2l_src,     &p->p2p_off,
                   &p->p2p_src,    &p->p2p_task,    &p->p2p_part,    &p->p2p_toff,
                   &p->p2p_poff,   &p->tot_m2l,     &p->tot_p2p,     &p->parents,
+                  &p->m2l_order,  &p->ord_hist,    &p->p2p_task_tmp,
                   &p->tail_toff,  &p->tail_task,   &p->tail_part};
   for (DBuf* b : bufs) release(*b);
   if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);
@@ -515,7 +524,7 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   rec(p, FMM_STAGE_M2L, 0, st);
   M2LArgs ma{};
   ma.n_nodes = p->n_nodes;
-  ma.parents = P<int32_t>(p->parents);
+  ma.parents = P<int32_t>(p->m2l_order);
   ma.n_parents = p->n_parents;
   ma.first_child = P<int32_t>(p->nfirst);
   ma.n_child = P<uint8_t>(p->nnchild);

@@ -82,6 +82,55 @@ __global__ void k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t
   tasks[k] = t;
 }
 
+// Launch order of the tasks: most pairs first (buckets of 1/8 octave of
+// targets x source leaves), so the longest waves do not start last.  Every
+// task's sums are independent of when it runs, so the order within a bucket
+// (set by integer atomics) does not change any result.
+__device__ __forceinline__ int task_bucket(const P2PTask& t, const int32_t* count) {
+  const double w = (double)count[t.leaf] * (double)(t.e1 - t.e0);
+  return 255 - min(255, (int)(8.0 * log2(w + 1.0)));
+}
+// block-local counts in LDS, one global atomic per (block, bucket)
+__global__ void k_task_hist(const P2PTask* tasks, int64_t n, const int32_t* count, int* hist) {
+  __shared__ int lc[256];
+  lc[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) atomicAdd(&lc[task_bucket(tasks[i], count)], 1);
+  __syncthreads();
+  if (lc[threadIdx.x] > 0) atomicAdd(&hist[threadIdx.x], lc[threadIdx.x]);
+}
+__global__ void k_task_scan(int* hist) {  // one block of 256: exclusive scan in place
+  __shared__ int ws[4];
+  const int t = threadIdx.x, lane = __lane_id(), w = t / WAVE;
+  const int c = hist[t];
+  const int incl = wave_incl_scan(c);
+  if (lane == WAVE - 1) ws[w] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int q = 0; q < w; q++) off += ws[q];
+  hist[t] = off + incl - c;
+}
+// rank within the block in LDS, one global atomic per (block, bucket) for the base
+__global__ void k_task_place(const P2PTask* in, int64_t n, const int32_t* count, int* pos,
+                             P2PTask* out) {
+  __shared__ int lc[256], lbase[256];
+  lc[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  int b = 0, r = 0;
+  P2PTask t{};
+  if (i < n) {
+    t = in[i];
+    b = task_bucket(t, count);
+    r = atomicAdd(&lc[b], 1);
+  }
+  __syncthreads();
+  if (lc[threadIdx.x] > 0) lbase[threadIdx.x] = atomicAdd(&pos[threadIdx.x], lc[threadIdx.x]);
+  __syncthreads();
+  if (i < n) out[lbase[b] + r] = t;
+}
+
 // ---- near-field sums ----
 constexpr int TILE = 2 * WAVE;       // source particles staged per round
 constexpr int MAXQ = 2048;           // source particles per owner table
@@ -314,10 +363,16 @@ hipError_t launch_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const 
 hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
                                 const int64_t* task_off, const int64_t* part_off,
                                 const int64_t* off, const int32_t* count, void* tasks,
-                                hipStream_t st) {
+                                void* tmp, int* hist, hipStream_t st) {
   if (n_tasks == 0) return hipSuccess;
-  k_p2p_task_fill<<<(unsigned)((n_tasks + 255) / 256), 256, 0, st>>>(
-      leaves, n_leaves, n_tasks, task_off, part_off, off, count, (P2PTask*)tasks);
+  const unsigned g = (unsigned)((n_tasks + 255) / 256);
+  k_p2p_task_fill<<<g, 256, 0, st>>>(leaves, n_leaves, n_tasks, task_off, part_off, off, count,
+                                     (P2PTask*)tmp);
+  hipError_t e = launch_fill_zero(hist, 256 * sizeof(int), st);
+  if (e != hipSuccess) return e;
+  k_task_hist<<<g, 256, 0, st>>>((const P2PTask*)tmp, n_tasks, count, hist);
+  k_task_scan<<<1, 256, 0, st>>>(hist);
+  k_task_place<<<g, 256, 0, st>>>((const P2PTask*)tmp, n_tasks, count, hist, (P2PTask*)tasks);
   return hipGetLastError();
 }
 
