@@ -127,8 +127,10 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   const int64_t nn = p->n_nodes;
   const int64_t nl = p->n_leaves;
   const int64_t np = nn - nl;
-  for (DBuf* b : {&p->cu_off, &p->u_off, &p->pu_off, &p->trm_off, &p->trp_off})
-    TRY(grow(*b, (size_t)nn * 8));
+  for (DBuf* b : {&p->cu_off, &p->u_off, &p->pu_off}) TRY(grow(*b, (size_t)nn * 8));
+  for (DBuf* b : {&p->trm_cnt, &p->trp_cnt}) TRY(grow(*b, (size_t)std::max<int64_t>(np, 1) * 8));
+  for (DBuf* b : {&p->trm_base, &p->trp_base})
+    TRY(grow(*b, (size_t)(std::max<int64_t>(np, 1) + 1) * 8));
   for (DBuf* b : {&p->cu_cnt, &p->u_cnt, &p->pu_cnt, &p->own_m2l, &p->own_p2p})
     TRY(grow(*b, (size_t)nn * 4));
   TRY(grow(p->rootgen, 8));
@@ -150,8 +152,8 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   }
   if (p->pbeg[MAX_LEVELS + 1] != np) return FMM_ERR_HIP;
   // first guesses for the pools (regrown from the measured use on overflow)
-  const int64_t guess[N_POOLS] = {48 * nn + 4096, 64 * nn + 4096, 32 * nn + 4096, 48 * nn + 4096,
-                                  32 * nn + 4096};
+  // (a group reserves its candidate count in each of the three unions)
+  const int64_t guess[N_POOLS] = {128 * nn + 4096, 128 * nn + 4096, 128 * nn + 4096};
   for (int k = 0; k < N_POOLS; k++)
     p->shard_cap[k] = std::max<int64_t>(p->shard_cap[k], std::max<int64_t>(guess[k] / POOL_SHARDS, 2048));
 
@@ -165,8 +167,10 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   a.cu_off = P<int64_t>(p->cu_off);
   a.u_off = P<int64_t>(p->u_off);
   a.pu_off = P<int64_t>(p->pu_off);
-  a.trm_off = P<int64_t>(p->trm_off);
-  a.trp_off = P<int64_t>(p->trp_off);
+  a.trm_cnt = P<int64_t>(p->trm_cnt);
+  a.trp_cnt = P<int64_t>(p->trp_cnt);
+  a.trm_base = P<int64_t>(p->trm_base);
+  a.trp_base = P<int64_t>(p->trp_base);
   a.cu_cnt = P<int32_t>(p->cu_cnt);
   a.u_cnt = P<int32_t>(p->u_cnt);
   a.pu_cnt = P<int32_t>(p->pu_cnt);
@@ -187,7 +191,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   for (;;) {
     for (int k = 0; k < N_POOLS; k++)
       TRY(grow(p->pool[k], (size_t)p->shard_cap[k] * POOL_SHARDS * 8));
-    Pool<uint64_t>* pools[N_POOLS] = {&a.cu, &a.u, &a.pu, &a.trm, &a.trp};
+    Pool<uint64_t>* pools[N_POOLS] = {&a.cu, &a.u, &a.pu};
     for (int k = 0; k < N_POOLS; k++)
       *pools[k] = Pool<uint64_t>{P<uint64_t>(p->pool[k]), p->shard_cap[k], dctrl->pool_used[k]};
     TRY_HIP(launch_walk_reset(dctrl, P<uint64_t>(p->rootgen), st));
@@ -195,10 +199,19 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     for (int l = 0; l < depth; l++) {
       a.pbeg = p->pbeg[l];
       a.pcnt = p->pbeg[l + 1] - p->pbeg[l];
-      TRY_HIP(launch_walk(1, a, st));
-      TRY_HIP(launch_walk(2, a, st));
+      TRY_HIP(launch_walk(a, st));
     }
     TRY_HIP(launch_walk_own_totals(nn, a.own_m2l, a.own_p2p, dctrl, st));
+    if (np > 0) {  // offsets of every group's transposed keys, in group order
+      TRY_HIP(scan_exclusive_i64(a.trm_cnt, P<int64_t>(p->trm_base), np,
+                                        P<int64_t>(p->trm_base) + np, p->scan_tmp.p, st));
+      TRY_HIP(scan_exclusive_i64(a.trp_cnt, P<int64_t>(p->trp_base), np,
+                                        P<int64_t>(p->trp_base) + np, p->scan_tmp.p, st));
+      TRY_HIP(launch_tr_totals(P<int64_t>(p->trm_base) + np, P<int64_t>(p->trp_base) + np, dctrl,
+                               st));
+    } else {
+      TRY_HIP(launch_fill_zero(&dctrl->n_trm, 16, st));
+    }
     TRY(sync_ctrl(p, st));
     if (!p->ctrl_host->pool_overflow) break;
     // the levels after the first overflow did not run: grow at least twofold
@@ -210,20 +223,18 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     }
   }
   const Control& c = *p->ctrl_host;
-  int64_t ntm = 0, ntp = 0, nu = 0;
-  for (int sh = 0; sh < POOL_SHARDS; sh++) {
-    ntm += c.pool_used[POOL_TRM][sh];
-    ntp += c.pool_used[POOL_TRP][sh];
-    nu += c.pool_used[POOL_U][sh];
-  }
+  int64_t nu = 0;
+  for (int sh = 0; sh < POOL_SHARDS; sh++) nu += c.pool_used[POOL_U][sh];
+  const int64_t ntm = c.n_trm, ntp = c.n_trp;
   const int64_t ntr = ntm + ntp;
-  p->n_union = nu;
+  p->n_union = nu;  // room reserved for the M2L unions (an upper bound)
   p->n_m2l = c.own_m2l_total + ntm;
   p->n_p2p = c.own_p2p_total + ntp;
   p->n_tr = ntr;
   p->m2l_lists_ready = false;
 
-  // transposed entries: dense copy, sort by (kind, target, source), run lengths
+  // transposed entries: emitted in group order (ascending source for each
+  // target), then stably sorted on (kind, target); run lengths per target
   int32_t* tr_cnt = P<int32_t>(p->tr_cnt_m2l);
   int64_t* tr_start = P<int64_t>(p->tr_start_m2l);
   TRY_HIP(launch_fill_zero(tr_cnt, (size_t)2 * nn * 4, st));
@@ -231,16 +242,18 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   if (ntr > 0) {
     TRY(grow(p->tr_keys, (size_t)ntr * 8));
     TRY(grow(p->tr_keys_alt, (size_t)ntr * 8));
-    TRY(grow(p->tr_vals, (size_t)ntr * 4));
-    TRY(grow(p->tr_vals_alt, (size_t)ntr * 4));
     TRY(grow(p->radix_hist, 4 * radix_hist_ints(ntr)));
     TRY(grow(p->scan_tmp, scan_tmp_bytes((int64_t)radix_hist_ints(ntr))));
-    TRY_HIP(launch_tr_compact(a, kind_bit, P<uint64_t>(p->tr_keys), st));
+    a.tr_keys = P<uint64_t>(p->tr_keys);
+    a.n_trm = &dctrl->n_trm;
+    a.pbeg = 0;
+    a.pcnt = np;
+    TRY_HIP(launch_tr_emit(a, st));
     bool in_alt = false;
-    TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), P<int32_t>(p->tr_vals),
-                                   P<uint64_t>(p->tr_keys_alt), P<int32_t>(p->tr_vals_alt), ntr,
-                                   kind_bit + 1, P<int32_t>(p->radix_hist),
-                                   P<int32_t>(p->scan_tmp), &in_alt, st));
+    TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), nullptr, P<uint64_t>(p->tr_keys_alt),
+                                   nullptr, ntr, a.key_shift, a.key_shift + 1,
+                                   P<int32_t>(p->radix_hist), P<int32_t>(p->scan_tmp), &in_alt,
+                                   st));
     sorted = in_alt ? P<uint64_t>(p->tr_keys_alt) : P<uint64_t>(p->tr_keys);
     TRY_HIP(launch_tr_runs(sorted, ntr, a.key_shift, kind_bit, nn, tr_start, tr_cnt, st));
   }
@@ -390,9 +403,10 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->ncount,     &p->nparent,     &p->nfirst,      &p->nnchild,
                   &p->ncentre,    &p->nq,          &p->ngeo,        &p->leaves,
                   &p->lvl_blkcnt, &p->mpole,       &p->local,       &p->pool[0],
-                  &p->pool[1],    &p->pool[2],     &p->pool[3],     &p->pool[4],
+                  &p->pool[1],    &p->pool[2],
                   &p->cu_off,     &p->cu_cnt,      &p->u_off,       &p->u_cnt,
-                  &p->pu_off,     &p->pu_cnt,      &p->trm_off,     &p->trp_off,
+                  &p->pu_off,     &p->pu_cnt,      &p->trm_cnt,     &p->trp_cnt,
+                  &p->trm_base,   &p->trp_base,
                   &p->own_m2l,    &p->own_p2p,     &p->rootgen,     &p->tr_cnt_m2l,
                   &p->tr_start_m2l, &p->tr_keys,   &p->tr_keys_alt, &p->tr_vals,
                   &p->tr_vals_alt, &p->m2l_off,    &p->m2l_src,     &p->p2p_off,

@@ -358,7 +358,7 @@ __global__ void __launch_bounds__(RS_THREADS)
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
     const int64_t i = wbase + r * WAVE + lane;
-    vv[r] = i < n ? vin[i] : 0;
+    vv[r] = (vin && i < n) ? vin[i] : 0;
   }
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
@@ -379,21 +379,22 @@ __global__ void __launch_bounds__(RS_THREADS)
     const int d = (int)((key >> shift) & 255u);
     const int64_t o = (int64_t)gbase[d] + (j - dstart[d]);
     kout[o] = key;
-    vout[o] = sval[j];
+    if (vout) vout[o] = sval[j];
   }
 }
 
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
-                                  int32_t* idx_alt, int64_t n, int bits, int32_t* hist,
-                                  int32_t* scan_tmp, bool* in_alt, hipStream_t st) {
+                                  int32_t* idx_alt, int64_t n, int lo_bit, int bits,
+                                  int32_t* hist, int32_t* scan_tmp, bool* in_alt,
+                                  hipStream_t st) {
   *in_alt = false;
   if (n <= 0) return hipSuccess;
   int nblk = (int)((n + RS_TILE - 1) / RS_TILE);
   uint64_t *ka = keys, *kb = keys_alt;
-  int32_t *va = idx, *vb = idx_alt;
+  int32_t *va = idx, *vb = idx_alt;  // both null: keys only
   const int passes = (bits + 7) / 8;
   for (int pass = 0; pass < passes; pass++) {
-    int shift = 8 * pass;
+    int shift = lo_bit + 8 * pass;
     k_radix_hist<<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, hist, nblk);
     hipError_t e = scan_excl<int32_t>(hist, hist, (int64_t)256 * nblk, nullptr, scan_tmp, st);
     if (e != hipSuccess) return e;
@@ -413,7 +414,7 @@ hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, i
                              int64_t n, int32_t* hist, int32_t* scan_tmp, hipStream_t st) {
   bool alt;
   // 8 passes of 8 bits over the 63-bit keys: the result is back in (keys, idx)
-  return launch_radix_sort_bits(keys, idx, keys_alt, idx_alt, n, 64, hist, scan_tmp, &alt, st);
+  return launch_radix_sort_bits(keys, idx, keys_alt, idx_alt, n, 0, 64, hist, scan_tmp, &alt, st);
 }
 
 // ===================================================================

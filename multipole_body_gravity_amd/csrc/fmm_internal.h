@@ -32,7 +32,7 @@ struct RootInfo {
 
 // Device scalars written by kernels and read back at the build syncs.
 constexpr int POOL_SHARDS = 512;
-enum { POOL_CU = 0, POOL_U = 1, POOL_PU = 2, POOL_TRM = 3, POOL_TRP = 4, N_POOLS = 5 };
+enum { POOL_CU = 0, POOL_U = 1, POOL_PU = 2, N_POOLS = 3 };
 struct Control {
   int32_t nonfinite;
   int32_t pad0;
@@ -43,6 +43,7 @@ struct Control {
   int64_t n_m2l;
   int64_t n_p2p;
   int64_t own_m2l_total, own_p2p_total;  // walk: entries found at the target's own level
+  int64_t n_trm, n_trp;                   // walk: transposed M2L and P2P entries
   int64_t n_p2p_tasks, n_p2p_part;        // near-field tasks and partial-sum slots
   int64_t n_tail_tasks;                   // transposed-tail M2L tasks
   int32_t pool_overflow;                  // a sharded pool ran out of room
@@ -78,7 +79,8 @@ struct fmm_plan_s {
   // walk: sharded pools (carry unions, M2L unions, P2P unions, transposed
   // M2L and P2P keys) and per-node slices / counts
   mbg::DBuf pool[mbg::N_POOLS];
-  mbg::DBuf cu_off, cu_cnt, u_off, u_cnt, pu_off, pu_cnt, trm_off, trp_off, own_m2l, own_p2p;
+  mbg::DBuf cu_off, cu_cnt, u_off, u_cnt, pu_off, pu_cnt, own_m2l, own_p2p;
+  mbg::DBuf trm_cnt, trp_cnt, trm_base, trp_base;  // per parent index: transposed entries
   mbg::DBuf rootgen;
   mbg::DBuf tr_cnt_m2l, tr_start_m2l;  // [kind][node] run lengths / starts in the sorted keys
   mbg::DBuf tr_keys, tr_keys_alt, tr_vals, tr_vals_alt;
@@ -106,7 +108,7 @@ struct fmm_plan_s {
   int walk_retries = 0;
   mbg::RootInfo root_host{};
 
-  int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0, 0, 0};  // entries per shard, per pool
+  int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0};  // entries per shard, per pool
 
   mbg::Control* ctrl_host = nullptr;  // pinned
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
@@ -175,26 +177,29 @@ struct WalkArgs {
   double t2;
   const int32_t* parents;  // non-leaf nodes, id order
   int64_t pbeg, pcnt;      // the parents of this step: parents[pbeg .. pbeg + pcnt)
-  // pools of packed entries (node << 8) | child mask, and transposed keys
-  Pool<uint64_t> cu, u, pu, trm, trp;
-  // per parent: slices of its carry union, M2L union, P2P union; tr allocations
-  int64_t *cu_off, *u_off, *pu_off, *trm_off, *trp_off;
+  // pools of packed entries (node << 8) | child mask
+  Pool<uint64_t> cu, u, pu;
+  // per parent node: slices of its carry union, M2L union, P2P union
+  int64_t *cu_off, *u_off, *pu_off;
   int32_t *cu_cnt, *u_cnt, *pu_cnt;
   int32_t *own_m2l, *own_p2p;  // per node: entries found at its own level
+  int64_t *trm_cnt, *trp_cnt;  // per parent index: transposed entries it emits
+  const int64_t *trm_base, *trp_base;  // their exclusive scans (emission pass)
+  uint64_t* tr_keys;           // transposed keys, M2L then P2P (emission pass)
+  const int64_t* n_trm;        // device total of the M2L ones
   const uint64_t* rootgen;     // the root's generator: one entry, the root itself
   int key_shift;
   Control* ctrl;
 };
-// per step (the children of the parents of one level): pass 1 counts and
-// allocates, pass 2 writes
-hipError_t launch_walk(int pass, const WalkArgs& a, hipStream_t st);
+// one step: the children of the parents of one level, counted and written
+hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
+// after the walk, every parent at once: the transposed keys (a.pbeg = 0, a.pcnt = all)
+hipError_t launch_tr_emit(const WalkArgs& a, hipStream_t st);
 hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, hipStream_t st);
 hipError_t launch_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
                             const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st);
 hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
                                   Control* ctrl, hipStream_t st);
-// dense copy of the transposed pools: M2L keys first (kind bit clear), then P2P (kind bit set)
-hipError_t launch_tr_compact(const WalkArgs& a, int kind_bit, uint64_t* dst, hipStream_t st);
 hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
                           int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st);
 hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_t* tr_cnt,
@@ -211,11 +216,17 @@ hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
 hipError_t launch_walk_copy_totals(const int64_t* p2p_total, const int64_t* task_total,
                                    const int64_t* part_total, const int64_t* tail_total,
                                    Control* ctrl, hipStream_t st);
+// transposed totals (ends of the two scans) into the control block
+hipError_t launch_tr_totals(const int64_t* trm_total, const int64_t* trp_total, Control* ctrl,
+                            hipStream_t st);
 // LSD radix sort over the low `bits` bits; returns in *in_alt whether the
 // result ended in (keys_alt, idx_alt).
+// stable LSD sort of keys by bits [lo_bit, lo_bit + bits) (idx/idx_alt may be
+// null for keys only); *in_alt tells which buffer holds the result
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
-                                  int32_t* idx_alt, int64_t n, int bits, int32_t* hist,
-                                  int32_t* scan_tmp, bool* in_alt, hipStream_t st);
+                                  int32_t* idx_alt, int64_t n, int lo_bit, int bits,
+                                  int32_t* hist, int32_t* scan_tmp, bool* in_alt,
+                                  hipStream_t st);
 
 // ---- numeric passes ----
 hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leaves,

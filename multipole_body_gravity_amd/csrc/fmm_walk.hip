@@ -30,10 +30,14 @@
 // coarser) come first, its transposed ones (deeper sources) after, so every
 // list ends sorted by source, as the pair walk's canonical order requires.
 //
-// Pass 1 of a step counts the unions and transposed entries of every group and
-// reserves their room; pass 2 enumerates again and writes them.  Room comes
-// from sharded bump allocators (integer atomics spread over 512 counters by
-// node): placement varies between runs, the lists do not.
+// A step enumerates each group's candidates once: their number, known from the
+// carry alone, reserves room for the three unions (sharded bump allocators,
+// integer atomics spread over 512 counters by node: placement varies between
+// runs, the lists do not), and the transposed entries are only counted.  After
+// the last step one launch over every group re-tests the carried leaves only
+// and writes the transposed keys at offsets from a scan over the groups in id
+// order: for a fixed target the keys come out with ascending sources, so a
+// stable sort on (kind, target) alone puts every transposed list in order.
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -122,21 +126,6 @@ __device__ __forceinline__ int shard_of(int32_t t) {
   return (int)(((uint32_t)t * 2654435761u) >> 23) & (POOL_SHARDS - 1);
 }
 
-// Wave-wide allocation of n entries from shard sh (lane 0 bumps the counter).
-// Returns the global offset, or -1 when the shard is full (overflow flagged).
-template <typename T>
-__device__ __forceinline__ int64_t pool_alloc(const Pool<T>& p, int sh, int64_t n, Control* ctrl) {
-  int64_t off = 0;
-  if (__lane_id() == 0)
-    off = (int64_t)atomicAdd((unsigned long long*)&p.used[sh], (unsigned long long)n);
-  off = __shfl(off, 0, WAVE);
-  if (off + n > p.shard_cap) {
-    if (__lane_id() == 0) atomicOr(&ctrl->pool_overflow, 1);
-    return -1;
-  }
-  return (int64_t)sh * p.shard_cap + off;
-}
-
 // The children of X: geometry of child t in cg[t]; masks of the leaf children
 // and of all children.
 struct Group {
@@ -187,7 +176,20 @@ __device__ __forceinline__ void add_bits(uint64_t (&c)[4], uint32_t m) {
     c[k] += (uint64_t)((m >> (2 * k)) & 1u) | ((uint64_t)((m >> (2 * k + 1)) & 1u) << 32);
 }
 
-__global__ void __launch_bounds__(WK_THREADS) k_walk(int pass, WalkArgs a) {
+// The generator of X (its carry): the entries of its parent's carry union with
+// X's bit set; for the root, the root.
+struct Gen {
+  const uint64_t* e;
+  int n, slot;
+};
+__device__ __forceinline__ Gen generator(const WalkArgs& a, int32_t X) {
+  if (X == 0) return Gen{a.rootgen, 1, 0};
+  const int32_t Y = uniform(a.parent[X]);
+  return Gen{a.cu.data + uniform(a.cu_off[Y]), uniform(a.cu_cnt[Y]),
+             X - uniform(a.first_child[Y])};
+}
+
+__global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
   // after an overflow the carry unions may be incomplete: do nothing, the host
   // regrows the pools and repeats the walk
   if (a.ctrl->pool_overflow) return;
@@ -195,92 +197,134 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(int pass, WalkArgs a) {
   const uint64_t lt = lanemask_lt();
   for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.pcnt;
        j += (int64_t)gridDim.x * WK_WAVES) {
-    const int32_t X = uniform(a.parents[a.pbeg + j]);
+    const int64_t pi = a.pbeg + j;
+    const int32_t X = uniform(a.parents[pi]);
     const Group G = load_group(a, X);
-    if (pass == 1) {
-      int64_t nU = 0, nPU = 0, nCU = 0;
-      uint32_t ntm = 0, ntp = 0;  // per lane
-      uint64_t cm[4] = {0, 0, 0, 0}, cp[4] = {0, 0, 0, 0};
-      for_each_candidate(a, X, [&](bool act, int32_t c, int phase) {
-        uint32_t mM = 0, mP = 0, mC = 0;
-        if (act) classify(a, G, c, mM, mP, mC);
-        nU += __popcll(__ballot(mM != 0));
-        nPU += __popcll(__ballot(mP != 0));
-        nCU += __popcll(__ballot(mC != 0));
-        add_bits(cm, mM);
-        add_bits(cp, mP);
-        if (phase == 0) {  // carried leaves of coarser levels: transposed entries
-          ntm += __popc(mM);
-          ntp += __popc(mP);
-        }
-      });
-#pragma unroll
-      for (int k = 0; k < 4; k++) {
-        cm[k] = wave_sum(cm[k]);
-        cp[k] = wave_sum(cp[k]);
+    // number of candidates: carried leaves count 1, carried non-leaves their children
+    const Gen gen = generator(a, X);
+    int nc_lane = 0;
+    for (int c0 = lane; c0 < gen.n; c0 += WAVE) {
+      const uint64_t e = gen.e[c0];
+      if ((e >> gen.slot) & 1u) {
+        const int k = a.n_child[(int32_t)(e >> 8)];
+        nc_lane += k == 0 ? 1 : k;
       }
-      const int64_t tm = wave_sum((int64_t)ntm), tp = wave_sum((int64_t)ntp);
-      const int sh = shard_of(X);
-      int64_t oCU = 0, oU = 0, oPU = 0, oTM = 0, oTP = 0;
-      bool ok = true;
-      if (nCU > 0) ok = (oCU = pool_alloc(a.cu, sh, nCU, a.ctrl)) >= 0;
-      if (ok && nU > 0) ok = (oU = pool_alloc(a.u, sh, nU, a.ctrl)) >= 0;
-      if (ok && nPU > 0) ok = (oPU = pool_alloc(a.pu, sh, nPU, a.ctrl)) >= 0;
-      if (ok && tm > 0) ok = (oTM = pool_alloc(a.trm, sh, tm, a.ctrl)) >= 0;
-      if (ok && tp > 0) ok = (oTP = pool_alloc(a.trp, sh, tp, a.ctrl)) >= 0;
-      if (!ok) continue;  // results are discarded; the host regrows the pools and retries
-      if (lane == 0) {
-        a.cu_off[X] = oCU;
-        a.cu_cnt[X] = (int32_t)nCU;
-        a.u_off[X] = oU;
-        a.u_cnt[X] = (int32_t)nU;
-        a.pu_off[X] = oPU;
-        a.pu_cnt[X] = (int32_t)nPU;
-        a.trm_off[X] = oTM;
-        a.trp_off[X] = oTP;
-      }
-      if (lane < G.nc) {
-        const int k = lane >> 1, hi = lane & 1;
-        uint64_t vm = 0, vp = 0;
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          if (q == k) {
-            vm = cm[q];
-            vp = cp[q];
-          }
-        a.own_m2l[G.fc + lane] = (int32_t)(hi ? (vm >> 32) : (vm & 0xffffffffu));
-        a.own_p2p[G.fc + lane] = (int32_t)(hi ? (vp >> 32) : (vp & 0xffffffffu));
-      }
-    } else {
-      const int64_t oCU = a.cu_off[X], oU = a.u_off[X], oPU = a.pu_off[X];
-      const int64_t oTM = a.trm_off[X], oTP = a.trp_off[X];
-      int64_t kU = 0, kPU = 0, kCU = 0, kTM = 0, kTP = 0;
-      for_each_candidate(a, X, [&](bool act, int32_t c, int phase) {
-        uint32_t mM = 0, mP = 0, mC = 0;
-        if (act) classify(a, G, c, mM, mP, mC);
-        const uint64_t packed = (uint64_t)(uint32_t)c << 8;
-        const uint64_t bU = __ballot(mM != 0), bP = __ballot(mP != 0), bC = __ballot(mC != 0);
-        if (mM) a.u.data[oU + kU + __popcll(bU & lt)] = packed | mM;
-        if (mP) a.pu.data[oPU + kPU + __popcll(bP & lt)] = packed | mP;
-        if (mC) a.cu.data[oCU + kCU + __popcll(bC & lt)] = packed | mC;
-        kU += __popcll(bU);
-        kPU += __popcll(bP);
-        kCU += __popcll(bC);
-        if (phase == 0) {
-          // (c <- child t) for every child t that accepted c, or paired with it
-          const int nm = __popc(mM), np = __popc(mP);
-          const int im = wave_incl_scan(nm), ip = wave_incl_scan(np);
-          int64_t om = oTM + kTM + (im - nm), op = oTP + kTP + (ip - np);
-          const uint64_t hiC = (uint64_t)(uint32_t)c << a.key_shift;
-          for (uint32_t m = mM; m; m &= m - 1)
-            a.trm.data[om++] = hiC | (uint32_t)(G.fc + __ffs(m) - 1);
-          for (uint32_t m = mP; m; m &= m - 1)
-            a.trp.data[op++] = hiC | (uint32_t)(G.fc + __ffs(m) - 1);
-          kTM += __shfl(im, WAVE - 1, WAVE);
-          kTP += __shfl(ip, WAVE - 1, WAVE);
-        }
-      });
     }
+    const int64_t ncand = wave_sum((int64_t)nc_lane);
+    // room for up to ncand entries in each union; one atomic per pool, issued together
+    const int sh = shard_of(X);
+    int64_t o[3] = {0, 0, 0};
+    if (lane == 0 && ncand > 0) {
+      o[0] = (int64_t)atomicAdd((unsigned long long*)&a.cu.used[sh], (unsigned long long)ncand);
+      o[1] = (int64_t)atomicAdd((unsigned long long*)&a.u.used[sh], (unsigned long long)ncand);
+      o[2] = (int64_t)atomicAdd((unsigned long long*)&a.pu.used[sh], (unsigned long long)ncand);
+    }
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+      o[k] = __shfl(o[k], 0, WAVE);
+      const Pool<uint64_t>& P = k == 0 ? a.cu : (k == 1 ? a.u : a.pu);
+      ok = ok && o[k] + ncand <= P.shard_cap;
+      o[k] += (int64_t)sh * P.shard_cap;
+    }
+    if (!ok) {  // results are discarded; the host regrows the pools and retries
+      if (lane == 0) atomicOr(&a.ctrl->pool_overflow, 1);
+      continue;
+    }
+    int64_t kU = 0, kPU = 0, kCU = 0;
+    uint32_t ntm = 0, ntp = 0;  // per lane
+    uint64_t cm[4] = {0, 0, 0, 0}, cp[4] = {0, 0, 0, 0};
+    for_each_candidate(a, X, [&](bool act, int32_t c, int phase) {
+      uint32_t mM = 0, mP = 0, mC = 0;
+      if (act) classify(a, G, c, mM, mP, mC);
+      const uint64_t packed = (uint64_t)(uint32_t)c << 8;
+      const uint64_t bU = __ballot(mM != 0), bP = __ballot(mP != 0), bC = __ballot(mC != 0);
+      if (mM) a.u.data[o[1] + kU + __popcll(bU & lt)] = packed | mM;
+      if (mP) a.pu.data[o[2] + kPU + __popcll(bP & lt)] = packed | mP;
+      if (mC) a.cu.data[o[0] + kCU + __popcll(bC & lt)] = packed | mC;
+      kU += __popcll(bU);
+      kPU += __popcll(bP);
+      kCU += __popcll(bC);
+      add_bits(cm, mM);
+      add_bits(cp, mP);
+      if (phase == 0) {  // carried leaves of coarser levels: transposed entries
+        ntm += __popc(mM);
+        ntp += __popc(mP);
+      }
+    });
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      cm[k] = wave_sum(cm[k]);
+      cp[k] = wave_sum(cp[k]);
+    }
+    const int64_t tm = wave_sum((int64_t)ntm), tp = wave_sum((int64_t)ntp);
+    if (lane == 0) {
+      a.cu_off[X] = o[0];
+      a.cu_cnt[X] = (int32_t)kCU;
+      a.u_off[X] = o[1];
+      a.u_cnt[X] = (int32_t)kU;
+      a.pu_off[X] = o[2];
+      a.pu_cnt[X] = (int32_t)kPU;
+      a.trm_cnt[pi] = tm;
+      a.trp_cnt[pi] = tp;
+    }
+    if (lane < G.nc) {
+      const int k = lane >> 1, hi = lane & 1;
+      uint64_t vm = 0, vp = 0;
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        if (q == k) {
+          vm = cm[q];
+          vp = cp[q];
+        }
+      a.own_m2l[G.fc + lane] = (int32_t)(hi ? (vm >> 32) : (vm & 0xffffffffu));
+      a.own_p2p[G.fc + lane] = (int32_t)(hi ? (vp >> 32) : (vp & 0xffffffffu));
+    }
+  }
+}
+
+// Transposed keys, every group at once: the carried leaves of X's generator are
+// tested again against X's children; (c <- child) keys go to the group's slot of
+// the M2L part (accepted) or the P2P part (leaf-leaf rejected), candidate by
+// candidate, children in order.
+__global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a) {
+  const uint64_t lt = lanemask_lt();
+  const int lane = __lane_id();
+  const int64_t ntm_all = *a.n_trm;
+  for (int64_t pi = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; pi < a.pcnt;
+       pi += (int64_t)gridDim.x * WK_WAVES) {
+    if (uniform(a.trm_cnt[pi]) + uniform(a.trp_cnt[pi]) == 0) continue;
+    const int32_t X = uniform(a.parents[pi]);
+    const Group G = load_group(a, X);
+    const Gen gen = generator(a, X);
+    int64_t om = a.trm_base[pi], op = ntm_all + a.trp_base[pi];
+    for (int c0 = 0; c0 < gen.n; c0 += WAVE) {
+      uint32_t mM = 0, mP = 0, mC = 0;
+      int32_t c = 0;
+      if (c0 + lane < gen.n) {
+        const uint64_t e = gen.e[c0 + lane];
+        c = (int32_t)(e >> 8);
+        if (((e >> gen.slot) & 1u) && a.n_child[c] == 0) classify(a, G, c, mM, mP, mC);
+      }
+      const int nm = __popc(mM), np = __popc(mP);
+      const int im = wave_incl_scan(nm), ip = wave_incl_scan(np);
+      int64_t wm = om + (im - nm), wp = op + (ip - np);
+      const uint64_t hiC = (uint64_t)(uint32_t)c << a.key_shift;
+      const uint64_t kind = 1ull << (2 * a.key_shift);
+      for (uint32_t m = mM; m; m &= m - 1) a.tr_keys[wm++] = hiC | (uint32_t)(G.fc + __ffs(m) - 1);
+      for (uint32_t m = mP; m; m &= m - 1)
+        a.tr_keys[wp++] = kind | hiC | (uint32_t)(G.fc + __ffs(m) - 1);
+      om += __shfl(im, WAVE - 1, WAVE);
+      op += __shfl(ip, WAVE - 1, WAVE);
+    }
+    (void)lt;
+  }
+}
+
+__global__ void k_tr_totals(const int64_t* trm_total, const int64_t* trp_total, Control* c) {
+  if (threadIdx.x == 0) {
+    c->n_trm = *trm_total;
+    c->n_trp = *trp_total;
   }
 }
 
@@ -320,27 +364,6 @@ __global__ void k_walk_own_totals(int64_t n, const int32_t* om, const int32_t* o
     atomicAdd((unsigned long long*)&c->own_m2l_total, (unsigned long long)sm[0]);
     atomicAdd((unsigned long long*)&c->own_p2p_total, (unsigned long long)sp[0]);
   }
-}
-
-// One block per shard: copy the shard's used entries to the dense array
-// (transposed M2L pool first, then the P2P pool with the kind bit set).
-__global__ void k_tr_compact(Pool<uint64_t> trm, Pool<uint64_t> trp, int kind_bit, uint64_t* dst) {
-  const int sh = blockIdx.x % POOL_SHARDS;
-  const int kind = blockIdx.x / POOL_SHARDS;
-  const Pool<uint64_t>& p = kind ? trp : trm;
-  __shared__ int64_t base;
-  if (threadIdx.x == 0) {
-    int64_t b = 0;
-    if (kind)
-      for (int i = 0; i < POOL_SHARDS; i++) b += trm.used[i];
-    for (int i = 0; i < sh; i++) b += p.used[i];
-    base = b;
-  }
-  __syncthreads();
-  const int64_t n = p.used[sh];
-  const uint64_t kb = (uint64_t)kind << kind_bit;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x)
-    dst[base + i] = p.data[(int64_t)sh * p.shard_cap + i] | kb;
 }
 
 // Runs of equal (kind, target) in the sorted keys: first index and end index.
@@ -455,10 +478,6 @@ hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const
   k_walk_own_totals<<<(unsigned)blocks, WK_THREADS, 0, st>>>(n_nodes, own_m2l, own_p2p, ctrl);
   return hipGetLastError();
 }
-hipError_t launch_tr_compact(const WalkArgs& a, int kind_bit, uint64_t* dst, hipStream_t st) {
-  k_tr_compact<<<2 * POOL_SHARDS, 256, 0, st>>>(a.trm, a.trp, kind_bit, dst);
-  return hipGetLastError();
-}
 hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
                           int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st) {
   if (n <= 0) return hipSuccess;
@@ -498,11 +517,23 @@ hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
                                                            n_child, pool, uoff, ucnt, off, src);
   return hipGetLastError();
 }
-hipError_t launch_walk(int pass, const WalkArgs& a, hipStream_t st) {
+hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {
   if (a.pcnt <= 0) return hipSuccess;
   int64_t blocks = (a.pcnt + WK_WAVES - 1) / WK_WAVES;
   if (blocks > 16384) blocks = 16384;
-  k_walk<<<(unsigned)blocks, WK_THREADS, 0, st>>>(pass, a);
+  k_walk<<<(unsigned)blocks, WK_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+hipError_t launch_tr_emit(const WalkArgs& a, hipStream_t st) {
+  if (a.pcnt <= 0) return hipSuccess;
+  int64_t blocks = (a.pcnt + WK_WAVES - 1) / WK_WAVES;
+  if (blocks > 16384) blocks = 16384;
+  k_tr_emit<<<(unsigned)blocks, WK_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+hipError_t launch_tr_totals(const int64_t* trm_total, const int64_t* trp_total, Control* ctrl,
+                            hipStream_t st) {
+  k_tr_totals<<<1, 64, 0, st>>>(trm_total, trp_total, ctrl);
   return hipGetLastError();
 }
 
