@@ -402,7 +402,8 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->bbox_part,  &p->nlevel,      &p->nprefix,     &p->nbegin,
                   &p->ncount,     &p->nparent,     &p->nfirst,      &p->nnchild,
                   &p->ncentre,    &p->nq,          &p->ngeo,        &p->leaves,
-                  &p->lvl_blkcnt, &p->mpole,       &p->local,       &p->pool[0],
+                  &p->lvl_blkcnt, &p->mpole,       &p->mred,        &p->local,
+                  &p->pool[0],
                   &p->pool[1],    &p->pool[2],
                   &p->cu_off,     &p->cu_cnt,      &p->u_off,       &p->u_cnt,
                   &p->pu_off,     &p->pu_cnt,      &p->trm_cnt,     &p->trp_cnt,
@@ -494,7 +495,8 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   TRY(grow(p->ngeo, 16 * nn));
   TRY(grow(p->leaves, 4 * (3 * nn + 2)));
   TRY(grow(p->parents, 4 * nn));
-  TRY(grow(p->mpole, (size_t)mrec_bytes(p->K, (int)w) * nn));
+  TRY(grow(p->mpole, w * p->K * nn));
+  TRY(grow(p->mred, (size_t)mrec_bytes((p->order + 1) * (p->order + 1), (int)w) * nn));
   TRY(grow(p->local, w * p->K * nn));
   TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
   TreeArrays t{P<uint8_t>(p->nlevel),  P<uint64_t>(p->nprefix), P<int32_t>(p->nbegin),
@@ -507,7 +509,6 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
                              root, t, leaves + nn, leaves + 2 * nn + 1, leaves,
                              P<int32_t>(p->leaf_of), P<int32_t>(p->parents), p->scan_tmp.p, ctrl,
                              st));
-  TRY_HIP(launch_mrec_centres(p->dtype, p->order, nn, P<double>(p->ncentre), p->mpole.p, st));
   rec(p, FMM_STAGE_TREE, 1, st);
 
   rec(p, FMM_STAGE_WALK, 0, st);
@@ -536,6 +537,7 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   rec(p, FMM_STAGE_UP, 1, st);
 
   rec(p, FMM_STAGE_M2L, 0, st);
+  TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, st));
   M2LArgs ma{};
   ma.n_nodes = p->n_nodes;
   ma.parents = P<int32_t>(p->m2l_order);
@@ -553,7 +555,7 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   ma.keys = p->tr_sorted;
   ma.src_mask = (1ull << p->key_shift) - 1ull;
   ma.centre = centre;
-  ma.mrec = p->mpole.p;
+  ma.mrec = p->mred.p;
   ma.part = p->tail_part.p;
   ma.local = p->local.p;
   for (int k = 0; k < FMM_N_KERNELS; k++) p->kran[k] = false;

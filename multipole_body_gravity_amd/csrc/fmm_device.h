@@ -200,6 +200,94 @@ struct Tabs {
 template <int P>
 inline constexpr Tabs<P> tabs{};
 
+// Tables for the traceless form of the translation.  The derivatives of 1/r
+// are harmonic: D_(k+2x) + D_(k+2y) + D_(k+2z) = 0.  So a moment component
+// with m_z >= 2 can be folded onto m - 2z + 2x and m - 2z + 2y (with sign -1)
+// without changing any sum_m Mt_m D_(n+m) -- the degree |m| is kept, so the
+// truncation |n| + |m| <= P is kept too -- and a local coefficient with
+// n_z >= 2 follows from two with one less z:  L_n = -L_(n-2z+2x) - L_(n-2z+2y).
+// The translation then runs over n, m with n_z, m_z <= 1 only: (P+1)^2
+// components each instead of C(P+3,3).
+//   rfull[r]          full index of reduced component r (graded order kept)
+//   tn, tm, tk        contraction terms: reduced n, reduced m, full n+m
+//   fold (dst, src)   moment folding, in an order that finishes every source
+//   rec (dst, s1, s2) local reconstruction, in increasing n_z
+template <int P>
+struct HTabs {
+  static constexpr int K = (P + 1) * (P + 2) * (P + 3) / 6;
+  static constexpr int KR = (P + 1) * (P + 1);
+  static constexpr int NF = 2 * (K - KR);
+  static constexpr int NRC = K - KR;
+  static constexpr int count_terms() {
+    int t = 0;
+    for (int dn = 0; dn <= P; dn++)
+      for (int dm = 0; dm + dn <= P; dm++) t += (2 * dn + 1) * (2 * dm + 1);
+    return t;
+  }
+  static constexpr int NT = count_terms();
+  int rfull[KR];
+  int tn[NT], tm[NT], tk[NT];
+  int fd[NF], fs[NF];
+  int rd[NRC], r1[NRC], r2[NRC];
+  constexpr HTabs() : rfull(), tn(), tm(), tk(), fd(), fs(), rd(), r1(), r2() {
+    int a[K] = {}, b[K] = {}, c[K] = {}, d[K] = {};
+    int k = 0;
+    for (int dd = 0; dd <= P; dd++)
+      for (int aa = dd; aa >= 0; aa--)
+        for (int bb = dd - aa; bb >= 0; bb--) {
+          a[k] = aa;
+          b[k] = bb;
+          c[k] = dd - aa - bb;
+          d[k] = dd;
+          k++;
+        }
+    int red[K] = {};
+    int r = 0;
+    for (int q = 0; q < K; q++) {
+      red[q] = -1;
+      if (c[q] <= 1) {
+        rfull[r] = q;
+        red[q] = r;
+        r++;
+      }
+    }
+    int t = 0;
+    for (int n = 0; n < K; n++)
+      for (int m = 0; m < K; m++)
+        if (c[n] <= 1 && c[m] <= 1 && d[n] + d[m] <= P) {
+          tn[t] = red[n];
+          tm[t] = red[m];
+          tk[t] = mi_index(a[n] + a[m], b[n] + b[m], c[n] + c[m]);
+          t++;
+        }
+    // folding: sources with the largest z first (their targets have z - 2)
+    int f = 0;
+    for (int cz = P; cz >= 2; cz--)
+      for (int q = 0; q < K; q++)
+        if (c[q] == cz) {
+          fd[f] = mi_index(a[q] + 2, b[q], c[q] - 2);
+          fs[f] = q;
+          f++;
+          fd[f] = mi_index(a[q], b[q] + 2, c[q] - 2);
+          fs[f] = q;
+          f++;
+        }
+    // reconstruction: increasing z, so both sources are known
+    int e = 0;
+    for (int cz = 2; cz <= P; cz++)
+      for (int q = 0; q < K; q++)
+        if (c[q] == cz) {
+          rd[e] = q;
+          r1[e] = mi_index(a[q] + 2, b[q], c[q] - 2);
+          r2[e] = mi_index(a[q], b[q] + 2, c[q] - 2);
+          e++;
+        }
+  }
+};
+
+template <int P>
+inline constexpr HTabs<P> htabs{};
+
 template <typename T>
 struct alignas(4 * sizeof(T)) P4 {
   T x, y, z, m;

@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256)
     k_p2m_reg(const P4<T>* pts, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
               const int32_t* count, const double* centre, T* mpole) {
   constexpr int K = Tabs<P>::K;
-  constexpr int RS = mrec_stride(K, sizeof(T));
+  constexpr int RS = K;  // moments stored densely
   const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (li >= n_leaves) return;
   const int32_t node = leaves[li];
@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(256)
     k_m2m_reg(int64_t lvl_begin, int64_t lvl_count, const int32_t* first_child,
               const uint8_t* n_child, const double* centre, T* mpole) {
   constexpr int K = Tabs<P>::K;
-  constexpr int RS = mrec_stride(K, sizeof(T));
+  constexpr int RS = K;  // moments stored densely
   constexpr int NTM = m2m_tab<P>.nt;
   const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   const int64_t pi = g >> 3;
@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(EX_THREADS)
     }
     for (int r = 0; r < 3; r++) {
       const int m = lane + WAVE * r;
-      if (m < K) mpole[(int64_t)node * mrec_stride(K, sizeof(T)) + m] = (T)acc[r];
+      if (m < K) mpole[(int64_t)node * K + m] = (T)acc[r];
     }
   }
 }
@@ -389,7 +389,7 @@ __global__ void __launch_bounds__(EX_THREADS)
   __shared__ double mc[EX_WAVES][MAXCH][ncoef(FMM_MAX_ORDER)];
   __shared__ double tab[EX_WAVES][MAXCH][3][PP];
   const int lane = __lane_id(), w = threadIdx.x / WAVE;
-  const int64_t RS = mrec_stride(K, sizeof(T));
+  const int64_t RS = K;
   for (int64_t pi = (int64_t)blockIdx.x * EX_WAVES + w; pi < lvl_count;
        pi += (int64_t)gridDim.x * EX_WAVES) {
     const int64_t P = lvl_begin + pi;
@@ -596,25 +596,6 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
-__global__ void k_mrec_centres(int64_t n_nodes, int RB, int CB, const double* centre,
-                               unsigned char* mrec) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= 3 * n_nodes) return;
-  const int64_t node = i / 3;
-  double* c = (double*)(mrec + node * RB + CB);
-  c[i - 3 * node] = centre[i];
-}
-
-hipError_t launch_mrec_centres(int dtype, int order, int64_t n_nodes, const double* centre,
-                               void* mpole, hipStream_t st) {
-  if (n_nodes <= 0) return hipSuccess;
-  const int K = ncoef(order), wb = dtype == FMM_F64 ? 8 : 4;
-  const unsigned g = (unsigned)((3 * n_nodes + 255) / 256);
-  k_mrec_centres<<<g, 256, 0, st>>>(n_nodes, mrec_bytes(K, wb), mrec_centre_byte(K, wb),
-                                            centre, (unsigned char*)mpole);
-  return hipGetLastError();
-}
-
 // scaled moments -> raw moments M_m = (-1)^|m| m! Mt_m; locals copied as fp64
 template <typename T>
 __global__ void k_export(int K, int64_t total, const T* mpole, const T* local, double* mp,
@@ -628,7 +609,7 @@ __global__ void k_export(int K, int64_t total, const T* mpole, const T* local, d
   for (int i = 2; i <= b; i++) f *= i;
   for (int i = 2; i <= c; i++) f *= i;
   if ((a + b + c) & 1) f = -f;
-  if (mp) mp[gid] = (double)mpole[(gid / K) * mrec_stride(K, sizeof(T)) + m] * f;
+  if (mp) mp[gid] = (double)mpole[gid] * f;
   if (lc) lc[gid] = (double)local[gid];
 }
 

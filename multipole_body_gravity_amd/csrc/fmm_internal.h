@@ -16,9 +16,10 @@ constexpr int MAX_LEVELS = KEY_BITS + 1;  // levels 0..21
 
 // Number of Cartesian coefficients of total degree <= p: C(p+3, 3).
 constexpr int ncoef(int p) { return (p + 1) * (p + 2) * (p + 3) / 6; }
-// Multipole record of a node: its K scaled moments (element size wb), then its
-// centre as three fp64 words at the next 8-byte boundary, padded to a multiple
-// of 16 bytes so that records can be moved in 16-byte pieces.
+// Source record of a node for the M2L: its KR folded (traceless-form)
+// moments (element size wb), then its centre as three fp64 words at the next
+// 8-byte boundary, padded to a multiple of 16 bytes so that records can be
+// moved in 16-byte pieces.
 constexpr int mrec_centre_byte(int K, int wb) { return (K * wb + 7) / 8 * 8; }
 constexpr int mrec_bytes(int K, int wb) { return (mrec_centre_byte(K, wb) + 24 + 15) / 16 * 16; }
 constexpr int mrec_stride(int K, int wb) { return mrec_bytes(K, wb) / wb; }  // in elements
@@ -75,7 +76,7 @@ struct fmm_plan_s {
   // node-sized
   mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq, ngeo;
   mbg::DBuf leaves, lvl_blkcnt;
-  mbg::DBuf mpole, local;
+  mbg::DBuf mpole, mred, local;
   // walk: sharded pools (carry unions, M2L unions, P2P unions, transposed
   // M2L and P2P keys) and per-node slices / counts
   mbg::DBuf pool[mbg::N_POOLS];
@@ -262,7 +263,7 @@ struct M2LArgs {
   const uint64_t* keys;   // sorted transposed keys; source = key & src_mask
   uint64_t src_mask;
   const double* centre;
-  const void* mrec;       // multipole records
+  const void* mrec;       // source records (folded moments + centre)
   void* part;             // task partials (n_tasks x K)
   void* local;
   hipEvent_t* ev;         // null, or begin/end events of the sibling and tail kernels
@@ -296,9 +297,9 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       void* part, bool any_multi, hipEvent_t* ev, bool* ran, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // expansions in the plan's dtype/convention -> fp64 raw moments / derivatives
-// copy the node centres into the multipole records
-hipError_t launch_mrec_centres(int dtype, int order, int64_t n_nodes, const double* centre,
-                               void* mpole, hipStream_t st);
+// traceless source records for the M2L: folded moments + centre, per node
+hipError_t launch_m2l_records(int dtype, int order, int64_t n_nodes, const double* centre,
+                              const void* mpole, void* mred, hipStream_t st);
 hipError_t launch_export_expansions(int dtype, int order, int64_t n_nodes, const void* mpole,
                                     const void* local, double* mp_out, double* lc_out,
                                     hipStream_t st);

@@ -12,6 +12,14 @@
 //     R^(j)_(k+e_x) = x R^(j+1)_k + k_x R^(j+1)_(k-e_x)   (same for y, z),
 //     R^(j)_0 = F_j = (-1)^j (2j-1)!! / |r|^(2j+1),   D^k = R^(0)_k.
 //
+// The translation runs in its traceless form: since D is harmonic
+// (D_(k+2x) + D_(k+2y) + D_(k+2z) = 0), the moment components with m_z >= 2
+// are folded once per node onto m_z <= 1 (same degree, so the truncation is
+// unchanged), the pair loop forms L_n for n_z <= 1 only, and the L_n with
+// n_z >= 2 follow from L_n = -L_(n-2z+2x) - L_(n-2z+2y).  At order 4 that is
+// 155 terms per pair instead of 210 (1365 instead of 3003 at order 8); the
+// result equals the full sum up to rounding.
+//
 // Every summation runs in a fixed order (fixed butterflies, no atomics), so
 // results do not depend on scheduling.
 #include <algorithm>
@@ -69,6 +77,47 @@ __device__ __forceinline__ void dtensor(T x, T y, T z, T (&D)[Tabs<P>::K]) {
   });
 }
 
+// ---------------- source records ----------------
+// Thread per node: fold the moments (components with m_z >= 2 onto m_z - 2,
+// largest z first) and store the (P+1)^2 remaining ones with the centre.
+template <typename T, int P>
+__global__ void k_m2l_records(int64_t n_nodes, const double* __restrict__ centre,
+                              const T* __restrict__ mpole, unsigned char* __restrict__ mred) {
+  constexpr int K = Tabs<P>::K, KR = HTabs<P>::KR;
+  constexpr int RB = mrec_bytes(KR, sizeof(T)), CB = mrec_centre_byte(KR, sizeof(T));
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n_nodes) return;
+  T M[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) M[k] = mpole[i * K + k];
+  static_for<0, HTabs<P>::NF>([&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    M[htabs<P>.fd[f]] -= M[htabs<P>.fs[f]];
+  });
+  T* out = (T*)(mred + i * RB);
+  static_for<0, KR>([&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    out[r] = M[htabs<P>.rfull[r]];
+  });
+  double* c = (double*)(mred + i * RB + CB);
+  c[0] = centre[3 * i];
+  c[1] = centre[3 * i + 1];
+  c[2] = centre[3 * i + 2];
+}
+
+// reduced accumulators (n_z <= 1) -> all K coefficients, by the harmonic relation
+template <typename T, int P>
+__device__ __forceinline__ void unfold_locals(const T (&acc)[HTabs<P>::KR], T (&L)[Tabs<P>::K]) {
+  static_for<0, HTabs<P>::KR>([&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    L[htabs<P>.rfull[r]] = acc[r];
+  });
+  static_for<0, HTabs<P>::NRC>([&](auto ec) {
+    constexpr int e = decltype(ec)::value;
+    L[htabs<P>.rd[e]] = -L[htabs<P>.r1[e]] - L[htabs<P>.r2[e]];
+  });
+}
+
 // ---------------- sibling blocks ----------------
 // The children of one parent receive the same candidates, so their own sources
 // are the union U of the candidates any child accepts (built with the walk,
@@ -85,9 +134,9 @@ typedef __attribute__((address_space(3))) void lvoid_t;
 
 template <typename T, int P>
 struct SibCfg {
-  static constexpr int K = Tabs<P>::K;
-  static constexpr int RB = mrec_bytes(K, sizeof(T));       // record bytes
-  static constexpr int CB = mrec_centre_byte(K, sizeof(T)); // centre offset in a record
+  static constexpr int KR = HTabs<P>::KR;
+  static constexpr int RB = mrec_bytes(KR, sizeof(T));       // record bytes
+  static constexpr int CB = mrec_centre_byte(KR, sizeof(T)); // centre offset in a record
   static constexpr int PC = RB / 16;                        // 16-byte pieces per record
   static constexpr int NI = (8 * PC + WAVE - 1) / WAVE;     // copy instructions per chunk
   static constexpr int SB = NI * WAVE * 16;                 // ring stage bytes
@@ -104,8 +153,8 @@ __global__ void __launch_bounds__(M2L_THREADS)
               const int32_t* __restrict__ u_cnt, const double* __restrict__ centre,
               const unsigned char* __restrict__ mrec, T* __restrict__ local) {
   using C = SibCfg<T, P>;
-  constexpr int K = C::K;
-  constexpr int NT = Tabs<P>::NT;
+  constexpr int K = Tabs<P>::K, KR = C::KR;
+  constexpr int NT = HTabs<P>::NT;
   constexpr int WPB = M2L_THREADS / WAVE;
   __shared__ __attribute__((aligned(16))) unsigned char ring[WPB][C::NS][C::SB];
   __shared__ int32_t wid[WPB][C::WIN];
@@ -134,9 +183,9 @@ __global__ void __launch_bounds__(M2L_THREADS)
       cz = centre[3 * ch + 2];
     }
     const int64_t u0 = uniform(u_off[par]), u1 = u0 + uniform(u_cnt[par]);
-    T acc[K];
+    T acc[KR];
 #pragma unroll
-    for (int k = 0; k < K; k++) acc[k] = (T)0;
+    for (int k = 0; k < KR; k++) acc[k] = (T)0;
     for (int64_t w0 = u0; w0 < u1; w0 += C::WIN) {
       const int n = (int)min((int64_t)C::WIN, u1 - w0);
       const int nch = (n + 7) >> 3;
@@ -183,21 +232,27 @@ __global__ void __launch_bounds__(M2L_THREADS)
           const T* Ms = (const T*)rec;
           static_for<0, NT>([&](auto tc) {
             constexpr int q = decltype(tc)::value;
-            acc[tabs<P>.tn[q]] += Ms[tabs<P>.tm[q]] * D[tabs<P>.tk[q]];
+            acc[htabs<P>.tn[q]] += Ms[htabs<P>.tm[q]] * D[htabs<P>.tk[q]];
           });
         }
         asm volatile("" ::: "memory");  // this stage is read before it is refilled
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // padding copies land before reuse
     }
-    T* Lc = local + ch * K;
-    static_for<0, K>([&](auto nc_) {
-      constexpr int n = decltype(nc_)::value;
-      T x = acc[n];
+#pragma unroll
+    for (int r = 0; r < KR; r++) {
+      T x = acc[r];
       x += __shfl_xor(x, 1, WAVE);
       x += __shfl_xor(x, 2, WAVE);
       x += __shfl_xor(x, 4, WAVE);
-      if (t < nc && (n & 7) == j) Lc[n] = -x;  // G = 1: L = -sum
+      acc[r] = -x;  // G = 1: L = -sum
+    }
+    T L[K];
+    unfold_locals<T, P>(acc, L);
+    T* Lc = local + ch * K;
+    static_for<0, K>([&](auto nc_) {
+      constexpr int n = decltype(nc_)::value;
+      if (t < nc && (n & 7) == j) Lc[n] = L[n];
     });
   }
 }
@@ -216,10 +271,10 @@ __global__ void __launch_bounds__(M2L_THREADS)
                const int32_t* __restrict__ leaves, const uint64_t* __restrict__ keys,
                uint64_t src_mask, const double* __restrict__ centre,
                const unsigned char* __restrict__ mrec, T* __restrict__ part) {
-  constexpr int K = Tabs<P>::K;
-  constexpr int NT = Tabs<P>::NT;
-  constexpr int RB = mrec_bytes(K, sizeof(T));
-  constexpr int CB = mrec_centre_byte(K, sizeof(T));
+  constexpr int K = Tabs<P>::K, KR = HTabs<P>::KR;
+  constexpr int NT = HTabs<P>::NT;
+  constexpr int RB = mrec_bytes(KR, sizeof(T));
+  constexpr int CB = mrec_centre_byte(KR, sizeof(T));
   const int lane = __lane_id();
   const int t = lane >> 3, j = lane & 7;
   const int64_t wid = (int64_t)blockIdx.x * (M2L_THREADS / WAVE) + threadIdx.x / WAVE;
@@ -237,33 +292,39 @@ __global__ void __launch_bounds__(M2L_THREADS)
     const double ax = ti < n_tasks ? centre[3 * a] : 0.0;
     const double ay = ti < n_tasks ? centre[3 * a + 1] : 0.0;
     const double az = ti < n_tasks ? centre[3 * a + 2] : 0.0;
-    T acc[K];
+    T acc[KR];
 #pragma unroll
-    for (int k = 0; k < K; k++) acc[k] = (T)0;
+    for (int k = 0; k < KR; k++) acc[k] = (T)0;
     for (int e = j; e < n; e += 8) {
       const int64_t b = (int64_t)(keys[e0 + e] & src_mask);
       const unsigned char* rb = mrec + b * RB;
       const T* Mb = (const T*)rb;
-      T M[K];
+      T M[KR];
 #pragma unroll
-      for (int k = 0; k < K; k++) M[k] = Mb[k];
+      for (int k = 0; k < KR; k++) M[k] = Mb[k];
       const double* cb = (const double*)(rb + CB);
       const T rx = (T)(ax - cb[0]), ry = (T)(ay - cb[1]), rz = (T)(az - cb[2]);
       T D[K];
       dtensor<T, P>(rx, ry, rz, D);
       static_for<0, NT>([&](auto tc) {
         constexpr int q = decltype(tc)::value;
-        acc[tabs<P>.tn[q]] += M[tabs<P>.tm[q]] * D[tabs<P>.tk[q]];
+        acc[htabs<P>.tn[q]] += M[htabs<P>.tm[q]] * D[htabs<P>.tk[q]];
       });
     }
-    T* Pt = part + ti * K;
-    static_for<0, K>([&](auto nc) {
-      constexpr int q = decltype(nc)::value;
-      T x = acc[q];
+#pragma unroll
+    for (int r = 0; r < KR; r++) {
+      T x = acc[r];
       x += __shfl_xor(x, 1, WAVE);
       x += __shfl_xor(x, 2, WAVE);
       x += __shfl_xor(x, 4, WAVE);
-      if (ti < n_tasks && (q & 7) == j) Pt[q] = x;
+      acc[r] = x;
+    }
+    T S[K];
+    unfold_locals<T, P>(acc, S);  // the relation is linear: it holds for partial sums too
+    T* Pt = part + ti * K;
+    static_for<0, K>([&](auto nc) {
+      constexpr int q = decltype(nc)::value;
+      if (ti < n_tasks && (q & 7) == j) Pt[q] = S[q];
     });
   }
 }
@@ -373,6 +434,35 @@ hipError_t launch_m2l_order(const int32_t* parents, int64_t np, const int32_t* u
   k_ord_count<<<g, 256, 0, st>>>(parents, np, u_cnt, hist);
   k_ord_scan<<<1, 256, 0, st>>>(hist);
   k_ord_scatter<<<g, 256, 0, st>>>(parents, np, u_cnt, hist, order);
+  return hipGetLastError();
+}
+
+template <typename T>
+static void records_dispatch(int order, unsigned g, hipStream_t st, int64_t n, const double* c,
+                             const T* m, unsigned char* r) {
+  switch (order) {
+#define REC_CASE(P) \
+  case P:           \
+    k_m2l_records<T, P><<<g, 256, 0, st>>>(n, c, m, r); \
+    break;
+    REC_CASE(0) REC_CASE(1) REC_CASE(2) REC_CASE(3) REC_CASE(4)
+    REC_CASE(5) REC_CASE(6) REC_CASE(7) REC_CASE(8)
+#undef REC_CASE
+    default:
+      break;
+  }
+}
+
+hipError_t launch_m2l_records(int dtype, int order, int64_t n_nodes, const double* centre,
+                              const void* mpole, void* mred, hipStream_t st) {
+  if (n_nodes <= 0) return hipSuccess;
+  const unsigned g = (unsigned)((n_nodes + 255) / 256);
+  if (dtype == FMM_F64)
+    records_dispatch<double>(order, g, st, n_nodes, centre, (const double*)mpole,
+                             (unsigned char*)mred);
+  else
+    records_dispatch<float>(order, g, st, n_nodes, centre, (const float*)mpole,
+                            (unsigned char*)mred);
   return hipGetLastError();
 }
 
