@@ -31,25 +31,40 @@ def binom(n, k):
     return math.comb(n, k)
 
 
-def m2l_flops_per_pair(p: int) -> int:
-    """Algorithmic flops of one multipole-to-local translation at order p.
-
-    Contraction: |n|+|m| <= p terms, one multiply-add each: 2 C(p+6, 6).
-    Derivative tensor of 1/R by the recurrence over levels j = p..0: every entry
-    of multi-index k != 0 costs a multiply (one source) or a multiply plus a
+def _dtensor_flops(p: int, max_kz: int) -> int:
+    """Derivative tensor of 1/R by the recurrence over levels j = p..0, for the
+    entries with k_z <= max_kz: a multiply (one source) or a multiply plus a
     multiply-add (two sources, when the split axis index is >= 2); plus the
-    offset (3), |R|^2 (5), the inverse square root (1) and the g_j chain (2p).
-    """
-    contraction = 2 * binom(p + 6, 6)
+    offset (3), |R|^2 (5), the inverse square root (1) and the g_j chain (2p)."""
     d = 3 + 5 + 1 + 1 + 2 * p
     for j in range(p, -1, -1):
         for deg in range(1, p - j + 1):
             for a in range(deg, -1, -1):
                 for b in range(deg - a, -1, -1):
                     c = deg - a - b
+                    if c > max_kz:
+                        continue
                     kk = a if a > 0 else (b if b > 0 else c)
                     d += 3 if kk >= 2 else 1
-    return contraction + d
+    return d
+
+
+def m2l_flops_per_pair(p: int) -> int:
+    """Algorithmic flops of one multipole-to-local translation at order p, in the
+    traceless form the kernels evaluate (the same result as the plain Cartesian
+    sum: D is harmonic, so moments are folded onto m_z <= 1 once per node and
+    locals with n_z >= 2 are rebuilt once per target): one multiply-add for
+    every n, m with n_z, m_z <= 1 and |n| + |m| <= p, i.e.
+    2 sum_(dn+dm<=p) (2dn+1)(2dm+1), plus the derivative entries with k_z <= 2.
+    """
+    contraction = 2 * sum((2 * dn + 1) * (2 * dm + 1)
+                          for dn in range(p + 1) for dm in range(p + 1 - dn))
+    return contraction + _dtensor_flops(p, 2)
+
+
+def m2l_flops_per_pair_plain(p: int) -> int:
+    """The same translation as the plain Cartesian sum over |n| + |m| <= p."""
+    return 2 * binom(p + 6, 6) + _dtensor_flops(p, p)
 
 
 P2P_FLOPS_PER_PAIR = 19  # 3 sub, |r|^2 5, rsqrt 1, 3 mul, 1 add, 3 FMA (6)
@@ -227,7 +242,8 @@ def main():
         "work": {"n_m2l": n_m2l, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,
                  "p2p_pairs": p2p_pairs, "n_nodes": st["n_nodes"],
                  "n_leaves": st["n_leaves"], "depth": st["depth"],
-                 "m2l_flops_per_pair": fpp, "p2p_flops_per_pair": P2P_FLOPS_PER_PAIR},
+                 "m2l_flops_per_pair": fpp, "p2p_flops_per_pair": P2P_FLOPS_PER_PAIR,
+                 "m2l_flops_per_pair_plain_cartesian": m2l_flops_per_pair_plain(cfg["order"])},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pos, mass, cfg)

@@ -115,6 +115,23 @@ int sync_ctrl(fmm_plan_t p, hipStream_t st) {
   return FMM_OK;
 }
 
+// scratch of the launch-order sorts (grow-only)
+int grow_order_bufs(fmm_plan_t p, int64_t n) {
+  n = std::max<int64_t>(n, 1);
+  TRY(grow(p->ord_key, (size_t)n * 8));
+  TRY(grow(p->ord_key_alt, (size_t)n * 8));
+  TRY(grow(p->ord_val, (size_t)n * 4));
+  TRY(grow(p->ord_val_alt, (size_t)n * 4));
+  TRY(grow(p->radix_hist, 4 * radix_hist_ints(n)));
+  TRY(grow(p->scan_tmp, scan_tmp_bytes((int64_t)radix_hist_ints(n))));
+  return FMM_OK;
+}
+OrderBufs order_bufs(fmm_plan_t p) {
+  return OrderBufs{P<uint64_t>(p->ord_key), P<uint64_t>(p->ord_key_alt), P<int32_t>(p->ord_val),
+                   P<int32_t>(p->ord_val_alt), P<int32_t>(p->radix_hist),
+                   P<int32_t>(p->scan_tmp)};
+}
+
 // ---------------- walk ----------------
 int bits_for(int64_t v) {  // bits to hold 0..v
   int b = 1;
@@ -261,9 +278,11 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
 
   // launch order of the M2L sibling blocks
   TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
-  TRY(grow(p->ord_hist, 256 * sizeof(int)));
-  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, P<int>(p->ord_hist), P<int32_t>(p->m2l_order),
-                           st));
+  TRY(grow_order_bufs(p, np));
+  int32_t* ord = nullptr;
+  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, order_bufs(p), &ord, st));
+  if (np > 0)
+    TRY_HIP(hipMemcpyAsync(p->m2l_order.p, ord, (size_t)np * 4, hipMemcpyDeviceToDevice, st));
 
   // P2P lists: own entries (from the parents' P2P unions) then transposed ones
   int64_t* p2p_off = P<int64_t>(p->p2p_off);
@@ -294,10 +313,11 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   p->n_tail_tasks = p->ctrl_host->n_tail_tasks;
   TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
   TRY(grow(p->p2p_task_tmp, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
+  TRY(grow_order_bufs(p, p->n_p2p_tasks));
   TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
   TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, p2p_off,
                                P<int32_t>(p->ncount), p->p2p_task.p, p->p2p_task_tmp.p,
-                               P<int>(p->ord_hist), st));
+                               order_bufs(p), st));
   TRY(grow(p->tail_task, (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * sizeof(TailTask)));
   TRY(grow(p->tail_part,
            (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * p->K * wbytes(p->dtype)));
@@ -413,7 +433,8 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->tr_vals_alt, &p->m2l_off,    &p->m2l_src,     &p->p2p_off,
                   &p->p2p_src,    &p->p2p_task,    &p->p2p_part,    &p->p2p_toff,
                   &p->p2p_poff,   &p->tot_m2l,     &p->tot_p2p,     &p->parents,
-                  &p->m2l_order,  &p->ord_hist,    &p->p2p_task_tmp,
+                  &p->m2l_order,  &p->ord_key,     &p->ord_key_alt, &p->ord_val,
+                  &p->ord_val_alt, &p->p2p_task_tmp,
                   &p->tail_toff,  &p->tail_task,   &p->tail_part};
   for (DBuf* b : bufs) release(*b);
   if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);

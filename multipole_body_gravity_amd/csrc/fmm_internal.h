@@ -93,7 +93,7 @@ struct fmm_plan_s {
   // near-field tasks (target leaf x bounded slice of its list)
   mbg::DBuf p2p_task, p2p_task_tmp, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
   // non-leaf nodes in id order; the parents of level l are parents[pbeg[l] .. pbeg[l+1])
-  mbg::DBuf parents, m2l_order, ord_hist;
+  mbg::DBuf parents, m2l_order, ord_key, ord_key_alt, ord_val, ord_val_alt;
   int64_t n_parents = 0, n_union = 0;
   int64_t pbeg[mbg::MAX_LEVELS + 2] = {0};
   // transposed-tail M2L tasks: per-leaf task offsets, tasks, partial locals
@@ -270,9 +270,16 @@ struct M2LArgs {
   bool* ran;              // with ev: set when the kernel was launched
 };
 hipError_t launch_m2l(int dtype, int order, const M2LArgs& a, hipStream_t st);
-// parents in launch order for the sibling blocks (longest unions first)
-hipError_t launch_m2l_order(const int32_t* parents, int64_t np, const int32_t* u_cnt, int* hist,
-                            int32_t* order, hipStream_t st);
+// scratch of a one-pass (8-bit key) stable sort used to order launches
+struct OrderBufs {
+  uint64_t *key, *key_alt;
+  int32_t *val, *val_alt;
+  int32_t *hist, *scan_tmp;
+};
+// parents in launch order for the sibling blocks (longer unions first);
+// *order points into ob
+hipError_t launch_m2l_order(const int32_t* parents, int64_t np, const int32_t* u_cnt,
+                            const OrderBufs& ob, int32_t** order, hipStream_t st);
 hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
                              int64_t* cnt, hipStream_t st);
 hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
@@ -289,7 +296,7 @@ hipError_t launch_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const 
 hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
                                 const int64_t* task_off, const int64_t* part_off,
                                 const int64_t* off, const int32_t* count, void* tasks,
-                                void* tmp, int* hist, hipStream_t st);
+                                void* tmp, const OrderBufs& ob, hipStream_t st);
 hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                       const int32_t* begin, const int32_t* count, const int32_t* src,

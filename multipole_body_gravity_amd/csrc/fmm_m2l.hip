@@ -381,59 +381,30 @@ hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64
   return hipGetLastError();
 }
 
-// Launch order of the sibling blocks: longest unions first (buckets of chunk
-// counts), so that the longest waves do not start last.  Each parent's result
-// does not depend on when it runs, so the order within a bucket is free.
-// block-local counts in LDS, one global atomic per (block, bucket)
-__global__ void k_ord_count(const int32_t* parents, int64_t np, const int32_t* u_cnt, int* hist) {
-  __shared__ int lc[256];
-  lc[threadIdx.x] = 0;
-  __syncthreads();
+// Launch order of the sibling blocks: longer unions (by octave) first, so that
+// the longest waves do not start last; a stable sort keeps id order inside an
+// octave, so that blocks running together mostly share source records in L2.
+// Each parent's result does not depend on when it runs.
+__global__ void k_ord_keys(const int32_t* parents, int64_t np, const int32_t* u_cnt,
+                           uint64_t* key, int32_t* val) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i < np) atomicAdd(&lc[255 - min(255, (u_cnt[parents[i]] + 7) >> 3)], 1);
-  __syncthreads();
-  if (lc[threadIdx.x] > 0) atomicAdd(&hist[threadIdx.x], lc[threadIdx.x]);
-}
-__global__ void k_ord_scan(int* hist) {  // one block of 256: exclusive scan in place
-  __shared__ int ws[4];
-  const int t = threadIdx.x, lane = __lane_id(), w = t / WAVE;
-  const int c = hist[t];
-  const int incl = wave_incl_scan(c);
-  if (lane == WAVE - 1) ws[w] = incl;
-  __syncthreads();
-  int off = 0;
-  for (int q = 0; q < w; q++) off += ws[q];
-  hist[t] = off + incl - c;
-}
-// rank within the block in LDS, one global atomic per (block, bucket) for the base
-__global__ void k_ord_scatter(const int32_t* parents, int64_t np, const int32_t* u_cnt, int* pos,
-                              int32_t* order) {
-  __shared__ int lc[256], lbase[256];
-  lc[threadIdx.x] = 0;
-  __syncthreads();
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  int32_t X = 0;
-  int b = 0, r = 0;
-  if (i < np) {
-    X = parents[i];
-    b = 255 - min(255, (u_cnt[X] + 7) >> 3);
-    r = atomicAdd(&lc[b], 1);
-  }
-  __syncthreads();
-  if (lc[threadIdx.x] > 0) lbase[threadIdx.x] = atomicAdd(&pos[threadIdx.x], lc[threadIdx.x]);
-  __syncthreads();
-  if (i < np) order[lbase[b] + r] = X;
+  if (i >= np) return;
+  const uint32_t u = (uint32_t)u_cnt[parents[i]];
+  key[i] = (uint64_t)(31 - (u ? 31 - __clz(u) : 0));  // descending octave
+  val[i] = parents[i];
 }
 
-hipError_t launch_m2l_order(const int32_t* parents, int64_t np, const int32_t* u_cnt, int* hist,
-                            int32_t* order, hipStream_t st) {
+hipError_t launch_m2l_order(const int32_t* parents, int64_t np, const int32_t* u_cnt,
+                            const OrderBufs& ob, int32_t** order, hipStream_t st) {
+  *order = nullptr;
   if (np <= 0) return hipSuccess;
-  hipError_t e = launch_fill_zero(hist, 256 * sizeof(int), st);
-  if (e != hipSuccess) return e;
   const unsigned g = (unsigned)((np + 255) / 256);
-  k_ord_count<<<g, 256, 0, st>>>(parents, np, u_cnt, hist);
-  k_ord_scan<<<1, 256, 0, st>>>(hist);
-  k_ord_scatter<<<g, 256, 0, st>>>(parents, np, u_cnt, hist, order);
+  k_ord_keys<<<g, 256, 0, st>>>(parents, np, u_cnt, ob.key, ob.val);
+  bool alt = false;
+  hipError_t e = launch_radix_sort_bits(ob.key, ob.val, ob.key_alt, ob.val_alt, np, 0, 8, ob.hist,
+                                        ob.scan_tmp, &alt, st);
+  *order = alt ? ob.val_alt : ob.val;
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -82,53 +82,22 @@ __global__ void k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t
   tasks[k] = t;
 }
 
-// Launch order of the tasks: most pairs first (buckets of 1/8 octave of
-// targets x source leaves), so the longest waves do not start last.  Every
-// task's sums are independent of when it runs, so the order within a bucket
-// (set by integer atomics) does not change any result.
-__device__ __forceinline__ int task_bucket(const P2PTask& t, const int32_t* count) {
-  const double w = (double)count[t.leaf] * (double)(t.e1 - t.e0);
-  return 255 - min(255, (int)(8.0 * log2(w + 1.0)));
-}
-// block-local counts in LDS, one global atomic per (block, bucket)
-__global__ void k_task_hist(const P2PTask* tasks, int64_t n, const int32_t* count, int* hist) {
-  __shared__ int lc[256];
-  lc[threadIdx.x] = 0;
-  __syncthreads();
+// Launch order of the tasks: heavier octaves of work (targets x source leaves)
+// first, so the longest waves do not start last; a stable sort keeps leaf order
+// inside an octave, so that tasks running together mostly share their sources
+// in L2.  Every task's sums are independent of when it runs.
+__global__ void k_task_keys(const P2PTask* tasks, int64_t n, const int32_t* count, uint64_t* key,
+                            int32_t* val) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i < n) atomicAdd(&lc[task_bucket(tasks[i], count)], 1);
-  __syncthreads();
-  if (lc[threadIdx.x] > 0) atomicAdd(&hist[threadIdx.x], lc[threadIdx.x]);
+  if (i >= n) return;
+  const P2PTask t = tasks[i];
+  const uint64_t w = (uint64_t)count[t.leaf] * (uint64_t)(t.e1 - t.e0);
+  key[i] = (uint64_t)(63 - (w ? 63 - __clzll(w) : 0));  // descending octave
+  val[i] = (int32_t)i;
 }
-__global__ void k_task_scan(int* hist) {  // one block of 256: exclusive scan in place
-  __shared__ int ws[4];
-  const int t = threadIdx.x, lane = __lane_id(), w = t / WAVE;
-  const int c = hist[t];
-  const int incl = wave_incl_scan(c);
-  if (lane == WAVE - 1) ws[w] = incl;
-  __syncthreads();
-  int off = 0;
-  for (int q = 0; q < w; q++) off += ws[q];
-  hist[t] = off + incl - c;
-}
-// rank within the block in LDS, one global atomic per (block, bucket) for the base
-__global__ void k_task_place(const P2PTask* in, int64_t n, const int32_t* count, int* pos,
-                             P2PTask* out) {
-  __shared__ int lc[256], lbase[256];
-  lc[threadIdx.x] = 0;
-  __syncthreads();
+__global__ void k_task_gather(const P2PTask* in, const int32_t* idx, int64_t n, P2PTask* out) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  int b = 0, r = 0;
-  P2PTask t{};
-  if (i < n) {
-    t = in[i];
-    b = task_bucket(t, count);
-    r = atomicAdd(&lc[b], 1);
-  }
-  __syncthreads();
-  if (lc[threadIdx.x] > 0) lbase[threadIdx.x] = atomicAdd(&pos[threadIdx.x], lc[threadIdx.x]);
-  __syncthreads();
-  if (i < n) out[lbase[b] + r] = t;
+  if (i < n) out[i] = in[idx[i]];
 }
 
 // ---- near-field sums ----
@@ -228,15 +197,7 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
           }
           __builtin_amdgcn_wave_barrier();
           const int nv = min(TILE, tot - q0);
-          int s = sl;
-          for (; s + ns < nv; s += 2 * ns) {  // two sources per step: four independent pairs
-            const P4<T> pj = sh.tile[s], pk = sh.tile[s + ns];
-            pair_acc(p0, pj, a0, a1, a2, a3);
-            pair_acc(p1, pj, b0, b1, b2, b3);
-            pair_acc(p0, pk, a0, a1, a2, a3);
-            pair_acc(p1, pk, b0, b1, b2, b3);
-          }
-          if (s < nv) {
+          for (int s = sl; s < nv; s += ns) {
             const P4<T> pj = sh.tile[s];
             pair_acc(p0, pj, a0, a1, a2, a3);
             pair_acc(p1, pj, b0, b1, b2, b3);
@@ -363,16 +324,18 @@ hipError_t launch_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const 
 hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
                                 const int64_t* task_off, const int64_t* part_off,
                                 const int64_t* off, const int32_t* count, void* tasks,
-                                void* tmp, int* hist, hipStream_t st) {
+                                void* tmp, const OrderBufs& ob, hipStream_t st) {
   if (n_tasks == 0) return hipSuccess;
   const unsigned g = (unsigned)((n_tasks + 255) / 256);
   k_p2p_task_fill<<<g, 256, 0, st>>>(leaves, n_leaves, n_tasks, task_off, part_off, off, count,
                                      (P2PTask*)tmp);
-  hipError_t e = launch_fill_zero(hist, 256 * sizeof(int), st);
+  k_task_keys<<<g, 256, 0, st>>>((const P2PTask*)tmp, n_tasks, count, ob.key, ob.val);
+  bool alt = false;
+  hipError_t e = launch_radix_sort_bits(ob.key, ob.val, ob.key_alt, ob.val_alt, n_tasks, 0, 8,
+                                        ob.hist, ob.scan_tmp, &alt, st);
   if (e != hipSuccess) return e;
-  k_task_hist<<<g, 256, 0, st>>>((const P2PTask*)tmp, n_tasks, count, hist);
-  k_task_scan<<<1, 256, 0, st>>>(hist);
-  k_task_place<<<g, 256, 0, st>>>((const P2PTask*)tmp, n_tasks, count, hist, (P2PTask*)tasks);
+  k_task_gather<<<g, 256, 0, st>>>((const P2PTask*)tmp, alt ? ob.val_alt : ob.val, n_tasks,
+                                   (P2PTask*)tasks);
   return hipGetLastError();
 }
 
