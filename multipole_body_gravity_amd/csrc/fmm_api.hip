@@ -586,9 +586,15 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   rec(p, FMM_STAGE_M2L, 1, st);
 
   rec(p, FMM_STAGE_DOWN, 0, st);
-  for (int l = 1; l <= p->depth; l++)
-    TRY_HIP(launch_l2l(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
-                       P<int32_t>(p->nparent), centre, p->local.p, st));
+  p->l2l_pulled = launch_l2l_pull(dt, ord, leaves, p->n_leaves, P<int32_t>(p->nparent), centre,
+                                  p->local.p, st);
+  if (p->l2l_pulled) {
+    TRY_HIP(hipGetLastError());
+  } else {
+    for (int l = 1; l <= p->depth; l++)
+      TRY_HIP(launch_l2l(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                         P<int32_t>(p->nparent), centre, p->local.p, nullptr, st));
+  }
   TRY_HIP(launch_l2p(dt, ord, p->n, p->pts.p, P<int32_t>(p->leaf_of), centre, p->local.p,
                      p->far.p, st));
   rec(p, FMM_STAGE_DOWN, 1, st);
@@ -691,13 +697,32 @@ int fmm_copy_expansions(fmm_plan_t p, double* mpole, double* local) {
     (void)hipFree(dm);
     return FMM_ERR_OOM;
   }
-  int rc = status_of(launch_export_expansions(p->dtype, p->order, p->n_nodes, p->mpole.p,
-                                              p->local.p, dm, dl, nullptr));
+  // With the one-launch downward pass, internal nodes keep only their M2L
+  // part; their full locals (parent's shifted in, level by level) are rebuilt
+  // here on a copy, leaves being complete already.
+  void* lsrc = p->local.p;
+  void* tmp = nullptr;
+  const size_t lbytes = m * wbytes(p->dtype);
+  int rc = FMM_OK;
+  if (p->l2l_pulled) {
+    if (hipMalloc(&tmp, lbytes) != hipSuccess) rc = FMM_ERR_OOM;
+    if (rc == FMM_OK)
+      rc = status_of(hipMemcpy(tmp, p->local.p, lbytes, hipMemcpyDeviceToDevice));
+    for (int l = 1; rc == FMM_OK && l <= p->depth; l++)
+      rc = status_of(launch_l2l(p->dtype, p->order, p->level_off[l],
+                                p->level_off[l + 1] - p->level_off[l], P<int32_t>(p->nparent),
+                                P<double>(p->ncentre), tmp, P<uint8_t>(p->nnchild), nullptr));
+    lsrc = tmp;
+  }
+  if (rc == FMM_OK)
+    rc = status_of(launch_export_expansions(p->dtype, p->order, p->n_nodes, p->mpole.p, lsrc, dm,
+                                            dl, nullptr));
   if (rc == FMM_OK) rc = status_of(hipDeviceSynchronize());
   if (rc == FMM_OK && mpole) rc = status_of(hipMemcpy(mpole, dm, 8 * m, hipMemcpyDeviceToHost));
   if (rc == FMM_OK && local) rc = status_of(hipMemcpy(local, dl, 8 * m, hipMemcpyDeviceToHost));
   (void)hipFree(dm);
   (void)hipFree(dl);
+  if (tmp) (void)hipFree(tmp);
   return rc;
 }
 

@@ -218,12 +218,13 @@ inline constexpr L2LTab<P> l2l_tab{};
 template <typename T, int P>
 __global__ void __launch_bounds__(256)
     k_l2l_reg(int64_t lvl_begin, int64_t lvl_count, const int32_t* parent, const double* centre,
-              T* local) {
+              T* local, const uint8_t* skip_leaves) {
   constexpr int K = Tabs<P>::K;
   constexpr int NTL = L2LTab<P>::NT;
   const int64_t ci = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (ci >= lvl_count) return;
   const int64_t a = lvl_begin + ci;
+  if (skip_leaves && skip_leaves[a] == 0) return;  // (n_child given: leaves are complete)
   const int64_t Pn = parent[a];
   const double dx = centre[3 * a] - centre[3 * Pn], dy = centre[3 * a + 1] - centre[3 * Pn + 1],
                dz = centre[3 * a + 2] - centre[3 * Pn + 2];
@@ -252,14 +253,85 @@ __global__ void __launch_bounds__(256)
   for (int k = 0; k < K; k++) Lc[k] = (T)acc[k];
 }
 
+// Downward pass for orders <= 5, one thread per leaf: Taylor shifts of a
+// degree-p polynomial are exact and compose, so the leaf's local is the sum of
+// its own M2L local and of every ancestor's M2L local shifted straight to the
+// leaf centre (leaf first, then up to the root; the same sums as the
+// level-by-level pass in another association).  Internal nodes' locals are
+// only read, so one launch replaces one launch per level.
+template <typename T, int P>
+__global__ void __launch_bounds__(256)
+    k_l2l_pull(const int32_t* leaves, int64_t n_leaves, const int32_t* parent,
+               const double* centre, T* local) {
+  constexpr int K = Tabs<P>::K;
+  constexpr int NTL = L2LTab<P>::NT;
+  const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (li >= n_leaves) return;
+  const int64_t a = leaves[li];
+  T* La = local + a * K;
+  double acc[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) acc[k] = (double)La[k];
+  const double cx = centre[3 * a], cy = centre[3 * a + 1], cz = centre[3 * a + 2];
+  for (int64_t q = parent[a]; q >= 0; q = parent[q]) {
+    const double dx = cx - centre[3 * q], dy = cy - centre[3 * q + 1], dz = cz - centre[3 * q + 2];
+    double px[P + 1], py[P + 1], pz[P + 1];
+    px[0] = py[0] = pz[0] = 1.0;
+#pragma unroll
+    for (int r = 1; r <= P; r++) {
+      px[r] = px[r - 1] * dx * (1.0 / r);
+      py[r] = py[r - 1] * dy * (1.0 / r);
+      pz[r] = pz[r - 1] * dz * (1.0 / r);
+    }
+    const T* Lq = local + q * K;
+    double L[K];
+#pragma unroll
+    for (int k = 0; k < K; k++) L[k] = (double)Lq[k];
+    static_for<0, NTL>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      acc[l2l_tab<P>.n[t]] += L[l2l_tab<P>.src[t]] *
+                              (px[l2l_tab<P>.ka[t]] * py[l2l_tab<P>.kb[t]] * pz[l2l_tab<P>.kc[t]]);
+    });
+  }
+#pragma unroll
+  for (int k = 0; k < K; k++) La[k] = (T)acc[k];
+}
+
+template <typename T>
+static bool l2l_pull_dispatch(int order, const int32_t* leaves, int64_t n_leaves,
+                              const int32_t* parent, const double* centre, void* local,
+                              hipStream_t st) {
+  const unsigned g = (unsigned)((n_leaves + 255) / 256);
+  switch (order) {
+#define L2LP(P)                                                                              \
+  case P:                                                                                    \
+    k_l2l_pull<T, P><<<g, 256, 0, st>>>(leaves, n_leaves, parent, centre, (T*)local);        \
+    return true;
+    L2LP(0) L2LP(1) L2LP(2) L2LP(3) L2LP(4) L2LP(5)
+#undef L2LP
+    default:
+      return false;
+  }
+}
+
+bool launch_l2l_pull(int dtype, int order, const int32_t* leaves, int64_t n_leaves,
+                     const int32_t* parent, const double* centre, void* local, hipStream_t st) {
+  if (n_leaves <= 0) return true;
+  return dtype == FMM_F64
+             ? l2l_pull_dispatch<double>(order, leaves, n_leaves, parent, centre, local, st)
+             : l2l_pull_dispatch<float>(order, leaves, n_leaves, parent, centre, local, st);
+}
+
 template <typename T>
 static bool l2l_reg_dispatch(int order, int64_t lvl_begin, int64_t lvl_count, const int32_t* parent,
-                             const double* centre, void* local, hipStream_t st) {
+                             const double* centre, void* local, const uint8_t* skip_leaves,
+                             hipStream_t st) {
   unsigned g = (unsigned)((lvl_count + 255) / 256);
   switch (order) {
 #define L2LR(P)                                                                             \
   case P:                                                                                   \
-    k_l2l_reg<T, P><<<g, 256, 0, st>>>(lvl_begin, lvl_count, parent, centre, (T*)local); \
+    k_l2l_reg<T, P><<<g, 256, 0, st>>>(lvl_begin, lvl_count, parent, centre, (T*)local,     \
+                                       skip_leaves);                                        \
     return true;
     L2LR(0) L2LR(1) L2LR(2) L2LR(3) L2LR(4) L2LR(5)
 #undef L2LR
@@ -492,16 +564,18 @@ __global__ void __launch_bounds__(EX_THREADS)
 }
 
 hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
-                      const int32_t* parent, const double* centre, void* local, hipStream_t st) {
+                      const int32_t* parent, const double* centre, void* local,
+                      const uint8_t* skip_leaves, hipStream_t st) {
   hipError_t e = ensure_table();
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
   if (lvl_count == 0) return hipSuccess;
   if (dtype == FMM_F64 ? l2l_reg_dispatch<double>(order, lvl_begin, lvl_count, parent, centre,
-                                                  local, st)
+                                                  local, skip_leaves, st)
                        : l2l_reg_dispatch<float>(order, lvl_begin, lvl_count, parent, centre,
-                                                 local, st))
+                                                 local, skip_leaves, st))
     return hipGetLastError();
+  if (skip_leaves) return hipErrorInvalidValue;  // only with the register kernels
   int64_t blocks = std::min<int64_t>((lvl_count + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
     k_l2l<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(order, K, lvl_begin, lvl_count, parent,

@@ -67,6 +67,7 @@ struct fmm_plan_s {
   double theta, t2;
   int device;
   bool built = false, evaluated = false, timing = false;
+  bool l2l_pulled = false;  // last eval used the one-launch downward pass
 
   // N-sized
   mbg::DBuf keys, keys_alt, idx, idx_alt, pts, far, perm_inv;
@@ -285,8 +286,15 @@ hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int3
 hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
                             const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks,
                             hipStream_t st);
+// downward pass in one launch (orders with register kernels; false: not
+// available, use the per-level L2L)
+bool launch_l2l_pull(int dtype, int order, const int32_t* leaves, int64_t n_leaves,
+                     const int32_t* parent, const double* centre, void* local, hipStream_t st);
+// one level of the level-by-level L2L (skip_leaves: the n_child array, to leave
+// leaves untouched; register kernels only)
 hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
-                      const int32_t* parent, const double* centre, void* local, hipStream_t st);
+                      const int32_t* parent, const double* centre, void* local,
+                      const uint8_t* skip_leaves, hipStream_t st);
 hipError_t launch_l2p(int dtype, int order, int64_t n, const void* pts, const int32_t* leaf_of,
                       const double* centre, const void* local, void* far, hipStream_t st);
 size_t p2p_task_bytes();
