@@ -227,9 +227,12 @@ struct HTabs {
   static constexpr int NT = count_terms();
   int rfull[KR];
   int tn[NT], tm[NT], tk[NT];
+  int ko[K + 1];        // the terms grouped by derivative index: terms of k are
+  int kn[NT], km[NT];   //   (kn, km)[ko[k] .. ko[k+1])
   int fd[NF], fs[NF];
   int rd[NRC], r1[NRC], r2[NRC];
-  constexpr HTabs() : rfull(), tn(), tm(), tk(), fd(), fs(), rd(), r1(), r2() {
+  constexpr HTabs()
+      : rfull(), tn(), tm(), tk(), ko(), kn(), km(), fd(), fs(), rd(), r1(), r2() {
     int a[K] = {}, b[K] = {}, c[K] = {}, d[K] = {};
     int k = 0;
     for (int dd = 0; dd <= P; dd++)
@@ -260,6 +263,17 @@ struct HTabs {
           tk[t] = mi_index(a[n] + a[m], b[n] + b[m], c[n] + c[m]);
           t++;
         }
+    int o = 0;
+    for (int kk = 0; kk < K; kk++) {
+      ko[kk] = o;
+      for (int q = 0; q < t; q++)
+        if (tk[q] == kk) {
+          kn[o] = tn[q];
+          km[o] = tm[q];
+          o++;
+        }
+    }
+    ko[K] = o;
     // folding: sources with the largest z first (their targets have z - 2)
     int f = 0;
     for (int cz = P; cz >= 2; cz--)

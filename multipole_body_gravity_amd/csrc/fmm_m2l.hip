@@ -42,41 +42,6 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
 __device__ __forceinline__ float rsqrt_any(float x) { return __builtin_amdgcn_rsqf(x); }
 __device__ __forceinline__ double rsqrt_any(double x) { return rsqrt_f64(x); }
 
-// Derivatives of 1/|r| up to total degree P, graded layout.  Every index is a
-// compile-time constant, so the whole table lives in registers.
-template <typename T, int P>
-__device__ __forceinline__ void dtensor(T x, T y, T z, T (&D)[Tabs<P>::K]) {
-  constexpr int NR = Tabs<P>::NR;
-  const T r2 = x * x + y * y + z * z;
-  const T rinv = rsqrt_any(r2);
-  const T rinv2 = rinv * rinv;
-  T g[P + 1];
-  g[0] = rinv;
-#pragma unroll
-  for (int j = 0; j < P; j++) g[j + 1] = (T)(-(2 * j + 1)) * g[j] * rinv2;
-  T R[NR];
-  static_for<0, NR>([&](auto ec) {
-    constexpr int e = decltype(ec)::value;
-    constexpr int ax = tabs<P>.raxis[e];
-    if constexpr (ax < 0) {
-      R[e] = g[tabs<P>.rlev[e]];
-    } else {
-      const T u = ax == 0 ? x : (ax == 1 ? y : z);
-      constexpr int s1 = tabs<P>.rs1[e];
-      constexpr int s2 = tabs<P>.rs2[e];
-      if constexpr (s2 >= 0) {
-        R[e] = u * R[s1] + (T)tabs<P>.rc2[e] * R[s2];
-      } else {
-        R[e] = u * R[s1];
-      }
-    }
-  });
-  static_for<0, Tabs<P>::K>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    D[k] = R[tabs<P>.roff[0] + k];
-  });
-}
-
 // ---------------- source records ----------------
 // Thread per node: fold the moments (components with m_z >= 2 onto m_z - 2,
 // largest z first) and store the (P+1)^2 remaining ones with the centre.
@@ -145,6 +110,51 @@ struct SibCfg {
   static constexpr int WAIT = (NS - 1) * NI;                // copies allowed in flight
 };
 
+// Derivatives D_k of 1/|r| up to total degree P (graded layout) and the
+// traceless contraction acc[n] += Mt[m] D[n+m] together: the recurrence levels
+// j = P .. 1 first, then every final derivative (level 0) is formed and used at
+// once by the terms that read it, so the D table is never live as a whole.
+// Every index is a compile-time constant: all of it stays in registers, and
+// derivatives no term reads (k_z > 2) are never formed.
+template <typename T, int P>
+__device__ __forceinline__ void dtensor_contract(T x, T y, T z, const T* Ms,
+                                                 T (&acc)[HTabs<P>::KR]) {
+  constexpr int NR = Tabs<P>::NR;
+  constexpr int R0 = tabs<P>.roff[0];  // level 0: the final derivatives
+  const T r2 = x * x + y * y + z * z;
+  const T rinv = rsqrt_any(r2);
+  const T rinv2 = rinv * rinv;
+  T g[P + 1];
+  g[0] = rinv;
+#pragma unroll
+  for (int j = 0; j < P; j++) g[j + 1] = (T)(-(2 * j + 1)) * g[j] * rinv2;
+  T R[NR];
+  static_for<0, NR>([&](auto ec) {
+    constexpr int e = decltype(ec)::value;
+    constexpr int ax = tabs<P>.raxis[e];
+    T v;
+    if constexpr (ax < 0) {
+      v = g[tabs<P>.rlev[e]];
+    } else {
+      const T u = ax == 0 ? x : (ax == 1 ? y : z);
+      constexpr int s1 = tabs<P>.rs1[e];
+      constexpr int s2 = tabs<P>.rs2[e];
+      if constexpr (s2 >= 0)
+        v = u * R[s1] + (T)tabs<P>.rc2[e] * R[s2];
+      else
+        v = u * R[s1];
+    }
+    R[e] = v;
+    if constexpr (e >= R0) {  // a final derivative: its terms now
+      constexpr int k = e - R0;
+      static_for<htabs<P>.ko[k], htabs<P>.ko[k + 1]>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        acc[htabs<P>.kn[q]] += Ms[htabs<P>.km[q]] * v;
+      });
+    }
+  });
+}
+
 template <typename T, int P>
 __global__ void __launch_bounds__(M2L_THREADS)
     k_m2l_sib(int64_t n_parents, const int32_t* __restrict__ parents,
@@ -154,7 +164,6 @@ __global__ void __launch_bounds__(M2L_THREADS)
               const unsigned char* __restrict__ mrec, T* __restrict__ local) {
   using C = SibCfg<T, P>;
   constexpr int K = Tabs<P>::K, KR = C::KR;
-  constexpr int NT = HTabs<P>::NT;
   constexpr int WPB = M2L_THREADS / WAVE;
   __shared__ __attribute__((aligned(16))) unsigned char ring[WPB][C::NS][C::SB];
   __shared__ int32_t wid[WPB][C::WIN];
@@ -227,13 +236,7 @@ __global__ void __launch_bounds__(M2L_THREADS)
         if ((m >> t) & 1u) {
           const double* cs = (const double*)(rec + C::CB);
           const T rx = (T)(cx - cs[0]), ry = (T)(cy - cs[1]), rz = (T)(cz - cs[2]);
-          T D[K];
-          dtensor<T, P>(rx, ry, rz, D);
-          const T* Ms = (const T*)rec;
-          static_for<0, NT>([&](auto tc) {
-            constexpr int q = decltype(tc)::value;
-            acc[htabs<P>.tn[q]] += Ms[htabs<P>.tm[q]] * D[htabs<P>.tk[q]];
-          });
+          dtensor_contract<T, P>(rx, ry, rz, (const T*)rec, acc);
         }
         asm volatile("" ::: "memory");  // this stage is read before it is refilled
       }
@@ -272,7 +275,6 @@ __global__ void __launch_bounds__(M2L_THREADS)
                uint64_t src_mask, const double* __restrict__ centre,
                const unsigned char* __restrict__ mrec, T* __restrict__ part) {
   constexpr int K = Tabs<P>::K, KR = HTabs<P>::KR;
-  constexpr int NT = HTabs<P>::NT;
   constexpr int RB = mrec_bytes(KR, sizeof(T));
   constexpr int CB = mrec_centre_byte(KR, sizeof(T));
   const int lane = __lane_id();
@@ -304,12 +306,7 @@ __global__ void __launch_bounds__(M2L_THREADS)
       for (int k = 0; k < KR; k++) M[k] = Mb[k];
       const double* cb = (const double*)(rb + CB);
       const T rx = (T)(ax - cb[0]), ry = (T)(ay - cb[1]), rz = (T)(az - cb[2]);
-      T D[K];
-      dtensor<T, P>(rx, ry, rz, D);
-      static_for<0, NT>([&](auto tc) {
-        constexpr int q = decltype(tc)::value;
-        acc[htabs<P>.tn[q]] += M[htabs<P>.tm[q]] * D[htabs<P>.tk[q]];
-      });
+      dtensor_contract<T, P>(rx, ry, rz, M, acc);
     }
 #pragma unroll
     for (int r = 0; r < KR; r++) {
