@@ -120,10 +120,11 @@ __device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp
 
 // Lane layout for a chunk of tc <= 128 targets: each lane holds two targets
 // (2g, 2g + 1), so one source read from LDS serves two pairs.  With
-// G = ceil(tc / 2) groups and nsl = ceil(64 / G) source slices, lane l serves
-// group l % G and slice l / G; the last slice may cover only the first
-// 64 - (nsl - 1) G groups, so a group has ns(g) = nsl or nsl - 1 slices, and
-// slice s of group g takes sources s, s + ns(g), ...
+// G = ceil(tc / 2) target pairs and ns = floor(64 / G) source slices, lane
+// l < G ns serves pair g = l % G and slice sl = l / G, taking sources sl,
+// sl + ns, ...; the few remaining lanes repeat slice 0 of their pair and their
+// sums are dropped.  Sources are staged TT = ns floor(128 / ns) at a time, so
+// in every full stage each lane takes exactly TT / ns sources.
 template <typename T>
 struct P2PShared {
   union {
@@ -153,9 +154,15 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
     for (int32_t t0 = 0; t0 < tn; t0 += 2 * WAVE) {
       const int tc = min(2 * WAVE, tn - t0);
       const int G = (tc + 1) >> 1;
-      const int nsl = (WAVE + G - 1) / G;
-      const int g = lane % G, sl = lane / G;
-      const int ns = (g < WAVE - (nsl - 1) * G) ? nsl : nsl - 1;  // slices of group g
+      // small quotients through the hardware reciprocal: each true quotient is
+      // at least 0.5 / 64 away from an integer, far above the estimate's error
+      const float rg = __builtin_amdgcn_rcpf((float)G);
+      const int ns = uniform((int)(((float)WAVE + 0.5f) * rg));  // floor(64 / G)
+      const int sl0 = (int)(((float)lane + 0.5f) * rg);          // floor(lane / G)
+      const int g = lane - sl0 * G;
+      const int sl = sl0 < ns ? sl0 : 0;
+      const int per = uniform((int)(((float)TILE + 0.5f) * __builtin_amdgcn_rcpf((float)ns)));
+      const int TT = ns * per;
       const int32_t i0 = tb + t0 + 2 * g;
       const bool two = 2 * g + 1 < tc;
       const P4<T> p0 = pts[i0];
@@ -189,18 +196,29 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
         if (!one)
           for (int k = 0; k < sc; k++) sh.owner[excl + k] = (uint8_t)lane;
         __builtin_amdgcn_wave_barrier();
-        for (int q0 = 0; q0 < tot; q0 += TILE) {
+        for (int q0 = 0; q0 < tot; q0 += TT) {
 #pragma unroll
           for (int r = 0; r < TILE / WAVE; r++) {
-            const int q = q0 + r * WAVE + lane;
-            if (q < tot) sh.tile[r * WAVE + lane] = pts[sh.sbase[one ? 0 : sh.owner[q]] + q];
+            const int k = r * WAVE + lane;
+            const int q = q0 + k;
+            if (k < TT && q < tot) sh.tile[k] = pts[sh.sbase[one ? 0 : sh.owner[q]] + q];
           }
           __builtin_amdgcn_wave_barrier();
-          const int nv = min(TILE, tot - q0);
-          for (int s = sl; s < nv; s += ns) {
-            const P4<T> pj = sh.tile[s];
-            pair_acc(p0, pj, a0, a1, a2, a3);
-            pair_acc(p1, pj, b0, b1, b2, b3);
+          const int nv = min(TT, tot - q0);
+          if (nv == TT) {
+            // a full stage: the same number of sources on every lane
+            const P4<T>* sp = sh.tile + sl;
+            for (int k = 0; k < per; k++) {
+              const P4<T> pj = sp[k * ns];
+              pair_acc(p0, pj, a0, a1, a2, a3);
+              pair_acc(p1, pj, b0, b1, b2, b3);
+            }
+          } else {
+            for (int s = sl; s < nv; s += ns) {
+              const P4<T> pj = sh.tile[s];
+              pair_acc(p0, pj, a0, a1, a2, a3);
+              pair_acc(p1, pj, b0, b1, b2, b3);
+            }
           }
           __builtin_amdgcn_wave_barrier();
         }
@@ -222,12 +240,11 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
       sh.red[6][lane] = b2;
       sh.red[7][lane] = b3;
       __builtin_amdgcn_wave_barrier();
-      // target t0 + l (l < tc) is finished by lane l % 64: group l / 2, member l % 2
+      // target t0 + l (l < tc) is finished by lane l % 64: pair l / 2, member l % 2
       for (int l = lane; l < tc; l += WAVE) {
         const int gg = l >> 1, m = 4 * (l & 1);
-        const int nsg = (gg < WAVE - (nsl - 1) * G) ? nsl : nsl - 1;
         T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-        for (int q = 0; q < nsg; q++) {
+        for (int q = 0; q < ns; q++) {
           s0 += sh.red[m][q * G + gg];
           s1 += sh.red[m + 1][q * G + gg];
           s2 += sh.red[m + 2][q * G + gg];
