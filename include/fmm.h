@@ -70,7 +70,7 @@ enum fmm_stage {
   FMM_STAGE_SORT = 1,  /* radix sort + gather into sorted order */
   FMM_STAGE_TREE = 2,  /* octree build                          */
   FMM_STAGE_WALK = 3,  /* dual-tree walk, M2L and P2P lists     */
-  FMM_STAGE_UP = 4,    /* P2M + M2M                             */
+  FMM_STAGE_UP = 4,    /* P2M + M2M + M2L source records (build) */
   FMM_STAGE_M2L = 5,   /* the single M2L launch                 */
   FMM_STAGE_DOWN = 6,  /* L2L + L2P                             */
   FMM_STAGE_P2P = 7,   /* the single P2P (+ combine) launch     */
@@ -107,15 +107,19 @@ typedef struct {
  * on demand during builds (grow-only, freed by fmm_destroy). */
 int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size, int dtype);
 
-/* Sort the particles, build the octree and the interaction lists.  pos [N][3]
- * and mass [N] are device arrays in the plan's dtype; they are copied into the
- * plan's sorted layout, so the caller may reuse them once `stream` has passed
- * this call.  Synchronizes `stream` twice (tree size, list sizes).  Returns
- * FMM_ERR_NONFINITE (and leaves the plan un-built) if any input is NaN/Inf. */
+/* Sort the particles, build the octree and the interaction lists, and form the
+ * multipoles (P2M, M2M).  pos [N][3] and mass [N] are device arrays in the
+ * plan's dtype; they are copied into the plan's sorted layout, so the caller
+ * may reuse them once `stream` has passed this call.  The multipoles depend on
+ * the tree only: they are formed on a second stream owned by the plan, which
+ * starts after the tree and overlaps the walk; the next fmm_eval or fmm_build
+ * on any stream waits for it.  Synchronizes `stream` three times (tree size,
+ * list sizes twice).  Returns FMM_ERR_NONFINITE (and leaves the plan un-built)
+ * if any input is NaN/Inf. */
 int fmm_build(fmm_plan_t plan, const void* pos, const void* mass, void* stream);
 
-/* Evaluate potential and acceleration of every particle: P2M, M2M, M2L, L2L,
- * L2P, P2P, written in the caller's order.  phi [N] and acc [N][3] are device
+/* Evaluate potential and acceleration of every particle: M2L, L2L, L2P, P2P
+ * (after the build's multipoles), written in the caller's order.  phi [N] and acc [N][3] are device
  * arrays in the plan's dtype.  Asynchronous on `stream`; may be repeated after
  * one build. */
 int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
@@ -127,7 +131,8 @@ int fmm_destroy(fmm_plan_t plan);
 const char* fmm_strerror(int code);
 
 /* Turn HIP-event timing of the stages and of the main kernels on (1) or off
- * (0).  Events are recorded on the caller's stream, between launches; their
+ * (0).  Events are recorded between launches on the stream that runs them
+ * (the caller's; the plan's second stream for the upward stage); their
  * times are collected at the next synchronization the library makes anyway
  * (the first one of the next build) or by fmm_stats, so timing adds no
  * synchronization.  Enabling resets the means. */

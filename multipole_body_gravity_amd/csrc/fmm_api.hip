@@ -76,8 +76,10 @@ int bbox_blocks(int64_t n) {
 
 // Timing: events are read only after a synchronization that follows them.
 // The first three build stages are collected at the end of their build (after
-// its last synchronization); the walk stage and the eval's stages and kernels
-// at the first synchronization of the next build, or by fmm_stats.
+// its last synchronization); the walk and upward stages (the latter on the
+// second stream, which the next build's stream waits for before its first
+// synchronization) and the eval's stages and kernels at the first
+// synchronization of the next build, or by fmm_stats.
 double elapsed(hipEvent_t a, hipEvent_t b) {
   float ms = 0.f;
   if (hipEventElapsedTime(&ms, a, b) != hipSuccess) {
@@ -94,13 +96,13 @@ void collect_early_build(fmm_plan_t p) {
 }
 void collect_pending(fmm_plan_t p) {
   if (p->pend_build) {
-    p->stage_sum[FMM_STAGE_WALK] +=
-        elapsed(p->ev[2 * FMM_STAGE_WALK], p->ev[2 * FMM_STAGE_WALK + 1]);
+    for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP})
+      p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
     p->n_timed_builds++;
     p->pend_build = false;
   }
   if (p->pend_eval) {
-    for (int s = FMM_STAGE_UP; s <= FMM_STAGE_P2P; s++)
+    for (int s = FMM_STAGE_M2L; s <= FMM_STAGE_P2P; s++)
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
     for (int k = 0; k < FMM_N_KERNELS; k++)
       if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
@@ -408,6 +410,11 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
     if (hipEventCreate(&p->ev[i]) != hipSuccess) return fail(FMM_ERR_HIP);
   for (int i = 0; i < 2 * FMM_N_KERNELS; i++)
     if (hipEventCreate(&p->kev[i]) != hipSuccess) return fail(FMM_ERR_HIP);
+  // default priority, like every stream of the library
+  if (hipStreamCreateWithFlags(&p->up_stream, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_tree, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_up, hipEventDisableTiming) != hipSuccess)
+    return fail(FMM_ERR_HIP);
   *out = p;
   return FMM_OK;
 }
@@ -442,6 +449,9 @@ int fmm_destroy(fmm_plan_t p) {
     if (p->ev[i]) (void)hipEventDestroy(p->ev[i]);
   for (int i = 0; i < 2 * FMM_N_KERNELS; i++)
     if (p->kev[i]) (void)hipEventDestroy(p->kev[i]);
+  if (p->ev_tree) (void)hipEventDestroy(p->ev_tree);
+  if (p->ev_up) (void)hipEventDestroy(p->ev_up);
+  if (p->up_stream) (void)hipStreamDestroy(p->up_stream);
   delete p;
   return FMM_OK;
 }
@@ -469,6 +479,8 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   const int64_t n = p->n;
   Control* ctrl = P<Control>(p->ctrl);
   RootInfo* root = P<RootInfo>(p->root);
+  // the previous build's upward pass reads the sorted particles and the tree
+  if (p->up_issued) TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
 
   rec(p, FMM_STAGE_KEYS, 0, st);
   TRY_HIP(launch_fill_zero(ctrl, sizeof(Control), st));
@@ -532,6 +544,25 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
                              st));
   rec(p, FMM_STAGE_TREE, 1, st);
 
+  // upward pass on the second stream, overlapping the walk
+  hipStream_t us = p->up_stream;
+  TRY_HIP(hipEventRecord(p->ev_tree, st));
+  TRY_HIP(hipStreamWaitEvent(us, p->ev_tree, 0));
+  {
+    const int dt = p->dtype, ord = p->order;
+    const double* centre = P<double>(p->ncentre);
+    rec(p, FMM_STAGE_UP, 0, us);
+    TRY_HIP(launch_p2m(dt, ord, p->pts.p, leaves, p->n_leaves, P<int32_t>(p->nbegin),
+                       P<int32_t>(p->ncount), centre, p->mpole.p, us));
+    for (int l = p->depth - 1; l >= 0; l--)
+      TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                         P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, us));
+    TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, us));
+    rec(p, FMM_STAGE_UP, 1, us);
+  }
+  TRY_HIP(hipEventRecord(p->ev_up, us));
+  p->up_issued = true;
+
   rec(p, FMM_STAGE_WALK, 0, st);
   TRY(run_walk(p, st));
   rec(p, FMM_STAGE_WALK, 1, st);
@@ -549,16 +580,10 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   const double* centre = P<double>(p->ncentre);
   int32_t* leaves = P<int32_t>(p->leaves);
 
-  rec(p, FMM_STAGE_UP, 0, st);
-  TRY_HIP(launch_p2m(dt, ord, p->pts.p, leaves, p->n_leaves, P<int32_t>(p->nbegin),
-                     P<int32_t>(p->ncount), centre, p->mpole.p, st));
-  for (int l = p->depth - 1; l >= 0; l--)
-    TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
-                       P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, st));
-  rec(p, FMM_STAGE_UP, 1, st);
+  // multipoles and source records come from the build's upward pass
+  TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
 
   rec(p, FMM_STAGE_M2L, 0, st);
-  TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, st));
   M2LArgs ma{};
   ma.n_nodes = p->n_nodes;
   ma.parents = P<int32_t>(p->m2l_order);
@@ -636,7 +661,8 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
     collect_pending(p);
     const double nb = std::max(1, p->n_timed_builds), ne = std::max(1, p->n_timed_evals);
     for (int s = 0; s < FMM_N_STAGES; s++)
-      out->stage_ms[s] = (float)(p->stage_sum[s] / (s <= FMM_STAGE_WALK ? nb : ne));
+      out->stage_ms[s] =
+          (float)(p->stage_sum[s] / (s <= FMM_STAGE_WALK || s == FMM_STAGE_UP ? nb : ne));
     for (int k = 0; k < FMM_N_KERNELS; k++) out->kernel_ms[k] = (float)(p->kernel_sum[k] / ne);
     out->timed_builds = p->n_timed_builds;
     out->timed_evals = p->n_timed_evals;

@@ -113,6 +113,12 @@ struct fmm_plan_s {
   int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0};  // entries per shard, per pool
 
   mbg::Control* ctrl_host = nullptr;  // pinned
+  // The upward pass (P2M, M2M, M2L source records) depends only on the tree, so
+  // a build issues it on a second stream of its own, where it overlaps the
+  // walk; the eval's stream, and the next build's, wait for ev_up.
+  hipStream_t up_stream = nullptr;
+  hipEvent_t ev_tree = nullptr, ev_up = nullptr;
+  bool up_issued = false;
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
   hipEvent_t kev[2 * FMM_N_KERNELS] = {};  // begin/end of single kernel launches
   bool kran[FMM_N_KERNELS] = {};          // the kernel ran in the last eval
