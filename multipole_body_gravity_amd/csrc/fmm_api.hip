@@ -490,9 +490,14 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   rec(p, FMM_STAGE_KEYS, 1, st);
 
   rec(p, FMM_STAGE_SORT, 0, st);
+  bool sorted_alt = false;
   TRY_HIP(launch_radix_sort(P<uint64_t>(p->keys), P<int32_t>(p->idx), P<uint64_t>(p->keys_alt),
                             P<int32_t>(p->idx_alt), n, P<int32_t>(p->radix_hist),
-                            P<int32_t>(p->scan_tmp), st));
+                            P<int32_t>(p->scan_tmp), &sorted_alt, st));
+  if (sorted_alt) {  // the sorted keys and permutation are the plan's from here on
+    std::swap(p->keys, p->keys_alt);
+    std::swap(p->idx, p->idx_alt);
+  }
   TRY_HIP(launch_gather(pos, mass, P<int32_t>(p->idx), n, p->dtype, p->pts.p, st));
   rec(p, FMM_STAGE_SORT, 1, st);
 

@@ -16,6 +16,7 @@ namespace mbg {
 constexpr int SCAN_THREADS = 256;
 constexpr int SCAN_ITEMS = 8;
 constexpr int SCAN_TILE = SCAN_THREADS * SCAN_ITEMS;
+constexpr int64_t SCAN_DIRECT_BLOCKS = 2048;  // up to here blocks sum their offsets themselves
 
 template <typename I>
 __device__ I block_excl_scan(I v, I* total) {
@@ -86,6 +87,35 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply(const I* in, I* out
   }
 }
 
+// Apply with the block offsets summed in place: block b adds sums[0 .. b-1]
+// itself (a few thousand block sums at most), so no separate pass scans them;
+// sums == null means a single block.  The last block writes the total.
+template <typename I>
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply_direct(const I* in, I* out, int64_t n,
+                                                                    const I* sums, I* total) {
+  I part = 0;
+  if (sums)
+    for (int64_t i = threadIdx.x; i < (int64_t)blockIdx.x; i += SCAN_THREADS) part += sums[i];
+  I boff;
+  block_excl_scan(part, &boff);
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+  I v[SCAN_ITEMS];
+  I s = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; i++) {
+    v[i] = (base + i < n) ? in[base + i] : 0;
+    s += v[i];
+  }
+  I tot;
+  I ex = block_excl_scan(s, &tot) + boff;
+#pragma unroll
+  for (int i = 0; i < SCAN_ITEMS; i++) {
+    if (base + i < n) out[base + i] = ex;
+    ex += v[i];
+  }
+  if (total && blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *total = boff + tot;
+}
+
 size_t scan_tmp_bytes(int64_t n) {
   int64_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
   return (size_t)(nb + 1) * sizeof(int64_t);
@@ -104,9 +134,17 @@ static hipError_t scan_excl(const I* in, I* out, int64_t n, I* total, void* tmp,
   }
   int64_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
   I* sums = (I*)tmp;
+  if (nb == 1) {
+    k_scan_apply_direct<I><<<1, SCAN_THREADS, 0, st>>>(in, out, n, nullptr, total);
+    return hipGetLastError();
+  }
   k_scan_reduce<I><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(in, n, sums);
-  k_scan_top<I><<<1, SCAN_THREADS, 0, st>>>(sums, nb, total);
-  k_scan_apply<I><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(in, out, n, sums);
+  if (nb <= SCAN_DIRECT_BLOCKS) {
+    k_scan_apply_direct<I><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(in, out, n, sums, total);
+  } else {
+    k_scan_top<I><<<1, SCAN_THREADS, 0, st>>>(sums, nb, total);
+    k_scan_apply<I><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(in, out, n, sums);
+  }
   return hipGetLastError();
 }
 
@@ -246,28 +284,45 @@ hipError_t launch_keys(const void* pos, int64_t n, int dtype, const RootInfo* ro
 }
 
 // ===================================================================
-// LSD radix sort of (u64 key, i32 index), 8-bit digits, stable
+// LSD radix sort of (u64 key, i32 index), stable, digits of 8 or 9 bits
 // ===================================================================
 constexpr int RS_THREADS = 256;
 constexpr int RS_ROUNDS = 16;
 constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
+constexpr int RS_MAX_RADIX = 512;
 
 size_t radix_hist_ints(int64_t n) {
   int64_t nb = (n + RS_TILE - 1) / RS_TILE;
-  return (size_t)(256 * nb);
+  return (size_t)(RS_MAX_RADIX * nb);
 }
 
+// digit of key at `shift` (dmask: the pass's digit mask) and the lanes of the
+// wave holding the same digit, from RB ballots
+template <int RB>
+__device__ __forceinline__ uint64_t same_digit(int d, bool valid) {
+  uint64_t mask = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < RB; b++) {
+    const uint64_t bb = __ballot((d >> b) & 1);
+    mask &= ((d >> b) & 1) ? bb : ~bb;
+  }
+  return mask;
+}
+
+template <int RB>
 __global__ void __launch_bounds__(RS_THREADS)
-    k_radix_hist(const uint64_t* keys, int64_t n, int shift, int32_t* hist, int nblk) {
-  __shared__ int h[256];
-  h[threadIdx.x] = 0;
+    k_radix_hist(const uint64_t* keys, int64_t n, int shift, uint32_t dmask, int32_t* hist,
+                 int nblk) {
+  constexpr int R = 1 << RB;
+  __shared__ int h[R];
+  for (int d = threadIdx.x; d < R; d += RS_THREADS) h[d] = 0;
   __syncthreads();
   int64_t base = (int64_t)blockIdx.x * RS_TILE;
   int dg[RS_ROUNDS];  // all loads issued before the first use
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
     int64_t i = base + r * RS_THREADS + threadIdx.x;
-    dg[r] = i < n ? (int)((keys[i] >> shift) & 255u) : -1;
+    dg[r] = i < n ? (int)((keys[i] >> shift) & dmask) : -1;
   }
   // one LDS atomic per distinct digit of a wave and round (equal digits found
   // by ballots): few distinct digits do not serialize on one counter
@@ -275,16 +330,12 @@ __global__ void __launch_bounds__(RS_THREADS)
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
     const int d = dg[r];
-    uint64_t mask = __ballot(d >= 0);
-#pragma unroll
-    for (int b = 0; b < 8; b++) {
-      const uint64_t bb = __ballot((d >> b) & 1);
-      mask &= ((d >> b) & 1) ? bb : ~bb;
-    }
+    const uint64_t mask = same_digit<RB>(d, d >= 0);
     if (d >= 0 && (mask & lt) == 0) atomicAdd(&h[d], __popcll(mask));
   }
   __syncthreads();
-  hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+  for (int d = threadIdx.x; d < R; d += RS_THREADS)
+    hist[(int64_t)d * nblk + blockIdx.x] = h[d];
 }
 
 // Scatter of one tile, stable.  Wave w ranks the w-th quarter of the tile on
@@ -293,21 +344,26 @@ __global__ void __launch_bounds__(RS_THREADS)
 // of the digit.  The per-wave counts are then combined in wave order (earlier
 // quarters first) and over digits, the tile is reordered by digit in LDS and
 // written out in that order, so each digit's run goes to consecutive addresses.
+template <int RB>
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
-                    int64_t n, int shift, const int32_t* hist_scan, int nblk) {
+                    int64_t n, int shift, uint32_t dmask, const int32_t* hist_scan, int nblk) {
+  constexpr int R = 1 << RB;
+  constexpr int DPT = R / RS_THREADS;  // digits per thread in the digit scan (1 or 2)
   constexpr int NW = RS_THREADS / WAVE;
   constexpr int WTILE = RS_TILE / NW;  // elements per wave
   __shared__ uint64_t skey[RS_TILE];
   __shared__ int32_t sval[RS_TILE];
-  __shared__ int wcnt[NW][256];  // per-wave digit counts; then per-wave starts
-  __shared__ int dstart[256];    // tile-local start of each digit's run
-  __shared__ int gbase[256];     // global start of this tile's part of each digit
+  __shared__ int wcnt[NW][R];  // per-wave digit counts; then per-wave starts
+  __shared__ int dstart[R];    // tile-local start of each digit's run
+  __shared__ int gbase[R];     // global start of this tile's part of each digit
   __shared__ int wsum[NW];
   const int tid = threadIdx.x, w = tid / WAVE, lane = __lane_id();
-  gbase[tid] = hist_scan[(int64_t)tid * nblk + blockIdx.x];
+  for (int d = tid; d < R; d += RS_THREADS) {
+    gbase[d] = hist_scan[(int64_t)d * nblk + blockIdx.x];
 #pragma unroll
-  for (int q = 0; q < NW; q++) wcnt[q][tid] = 0;
+    for (int q = 0; q < NW; q++) wcnt[q][d] = 0;
+  }
   __syncthreads();
   const int64_t wbase = (int64_t)blockIdx.x * RS_TILE + (int64_t)w * WTILE;
   const uint64_t lt = lanemask_lt();
@@ -322,13 +378,8 @@ __global__ void __launch_bounds__(RS_THREADS)
   for (int r = 0; r < RS_ROUNDS; r++) {
     const int64_t i = wbase + r * WAVE + lane;
     const bool valid = i < n;
-    const int d = (int)((kk[r] >> shift) & 255u);
-    uint64_t mask = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; b++) {
-      const uint64_t bb = __ballot((d >> b) & 1);
-      mask &= ((d >> b) & 1) ? bb : ~bb;
-    }
+    const int d = (int)((kk[r] >> shift) & dmask);
+    const uint64_t mask = same_digit<RB>(d, valid);
     const int rank = __popcll(mask & lt);
     const int before = valid ? wcnt[w][d] : 0;
     __builtin_amdgcn_wave_barrier();
@@ -337,21 +388,33 @@ __global__ void __launch_bounds__(RS_THREADS)
     rk[r] = before + rank;
   }
   __syncthreads();
-  // thread d: starts of digit d in each wave's quarter, and its tile total
-  int tot = 0;
+  // thread t: digits DPT t .. DPT t + DPT - 1: starts in each wave's quarter,
+  // and the tile totals
+  int tot[DPT], tsum = 0;
 #pragma unroll
-  for (int q = 0; q < NW; q++) {
-    const int c = wcnt[q][tid];
-    wcnt[q][tid] = tot;
-    tot += c;
+  for (int k = 0; k < DPT; k++) {
+    const int d = DPT * tid + k;
+    tot[k] = 0;
+#pragma unroll
+    for (int q = 0; q < NW; q++) {
+      const int c = wcnt[q][d];
+      wcnt[q][d] = tot[k];
+      tot[k] += c;
+    }
+    tsum += tot[k];
   }
   {
-    const int incl = wave_incl_scan(tot);
+    const int incl = wave_incl_scan(tsum);
     if (lane == WAVE - 1) wsum[w] = incl;
     __syncthreads();
     int off = 0;
     for (int q = 0; q < w; q++) off += wsum[q];
-    dstart[tid] = off + incl - tot;
+    int e = off + incl - tsum;
+#pragma unroll
+    for (int k = 0; k < DPT; k++) {
+      dstart[DPT * tid + k] = e;
+      e += tot[k];
+    }
   }
   __syncthreads();
   int32_t vv[RS_ROUNDS];
@@ -365,7 +428,7 @@ __global__ void __launch_bounds__(RS_THREADS)
     const int64_t i = wbase + r * WAVE + lane;
     if (i < n) {
       const uint64_t key = kk[r];
-      const int d = (int)((key >> shift) & 255u);
+      const int d = (int)((key >> shift) & dmask);
       const int lp = dstart[d] + wcnt[w][d] + rk[r];
       skey[lp] = key;
       sval[lp] = vv[r];
@@ -376,29 +439,42 @@ __global__ void __launch_bounds__(RS_THREADS)
   const int tn = (int)min((int64_t)RS_TILE, n - base);
   for (int j = tid; j < tn; j += RS_THREADS) {
     const uint64_t key = skey[j];
-    const int d = (int)((key >> shift) & 255u);
+    const int d = (int)((key >> shift) & dmask);
     const int64_t o = (int64_t)gbase[d] + (j - dstart[d]);
     kout[o] = key;
     if (vout) vout[o] = sval[j];
   }
 }
 
+// Sorts on bits [lo_bit, lo_bit + bits): 9-bit digits when that saves a pass
+// (63-bit Morton keys: 7 passes instead of 8), else 8-bit ones; the last
+// digit is masked to the remaining bits.
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
                                   int32_t* idx_alt, int64_t n, int lo_bit, int bits,
                                   int32_t* hist, int32_t* scan_tmp, bool* in_alt,
                                   hipStream_t st) {
   *in_alt = false;
-  if (n <= 0) return hipSuccess;
-  int nblk = (int)((n + RS_TILE - 1) / RS_TILE);
+  if (n <= 0 || bits <= 0) return hipSuccess;
+  const int nblk = (int)((n + RS_TILE - 1) / RS_TILE);
+  const int rb = (bits + 8) / 9 < (bits + 7) / 8 ? 9 : 8;
+  const int passes = (bits + rb - 1) / rb;
   uint64_t *ka = keys, *kb = keys_alt;
   int32_t *va = idx, *vb = idx_alt;  // both null: keys only
-  const int passes = (bits + 7) / 8;
   for (int pass = 0; pass < passes; pass++) {
-    int shift = lo_bit + 8 * pass;
-    k_radix_hist<<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, hist, nblk);
-    hipError_t e = scan_excl<int32_t>(hist, hist, (int64_t)256 * nblk, nullptr, scan_tmp, st);
+    const int shift = lo_bit + rb * pass;
+    const int db = std::min(rb, lo_bit + bits - shift);
+    const uint32_t dmask = (1u << db) - 1u;
+    const int64_t nh = ((int64_t)1 << rb) * nblk;
+    if (rb == 9)
+      k_radix_hist<9><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+    else
+      k_radix_hist<8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+    hipError_t e = scan_excl<int32_t>(hist, hist, nh, nullptr, scan_tmp, st);
     if (e != hipSuccess) return e;
-    k_radix_scatter<<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, hist, nblk);
+    if (rb == 9)
+      k_radix_scatter<9><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist, nblk);
+    else
+      k_radix_scatter<8><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist, nblk);
     uint64_t* tk = ka;
     ka = kb;
     kb = tk;
@@ -411,10 +487,11 @@ hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_a
 }
 
 hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
-                             int64_t n, int32_t* hist, int32_t* scan_tmp, hipStream_t st) {
-  bool alt;
-  // 8 passes of 8 bits over the 63-bit keys: the result is back in (keys, idx)
-  return launch_radix_sort_bits(keys, idx, keys_alt, idx_alt, n, 0, 64, hist, scan_tmp, &alt, st);
+                             int64_t n, int32_t* hist, int32_t* scan_tmp, bool* in_alt,
+                             hipStream_t st) {
+  // 7 passes of 9 bits over the 63-bit keys: the result is in (keys_alt, idx_alt)
+  return launch_radix_sort_bits(keys, idx, keys_alt, idx_alt, n, 0, 63, hist, scan_tmp, in_alt,
+                                st);
 }
 
 // ===================================================================

@@ -135,7 +135,8 @@ hipError_t launch_bbox(const void* pos, const void* mass, int64_t n, int dtype, 
 hipError_t launch_keys(const void* pos, int64_t n, int dtype, const RootInfo* root,
                        uint64_t* keys, int32_t* idx, hipStream_t st);
 hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
-                             int64_t n, int32_t* hist, int32_t* scan_tmp, hipStream_t st);
+                             int64_t n, int32_t* hist, int32_t* scan_tmp, bool* in_alt,
+                             hipStream_t st);
 hipError_t launch_gather(const void* pos, const void* mass, const int32_t* perm, int64_t n,
                          int dtype, void* pts, hipStream_t st);
 size_t radix_hist_ints(int64_t n);
