@@ -25,24 +25,78 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Wave-wide sum with a fixed butterfly order: every lane gets the same,
-// bit-reproducible result.
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+// ---- cross-lane moves inside rows of 16 lanes (DPP), no LDS round trip ----
+// DPP controls: quad_perm, row_shr:n, row_mirror, row_half_mirror.  A lane
+// whose source lies outside its row receives 0.
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int dpp_row_shr(int n) { return 0x110 + n; }
+
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_move(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp_move(int64_t v) {
+  const uint32_t lo = (uint32_t)dpp_move<CTRL>((int32_t)(uint32_t)(uint64_t)v);
+  const uint32_t hi = (uint32_t)dpp_move<CTRL>((int32_t)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t v) {
+  return (uint64_t)dpp_move<CTRL>((int64_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+  return (uint32_t)dpp_move<CTRL>((int32_t)v);
+}
+__device__ __forceinline__ int32_t read_lane(int32_t v, int l) {
+  return __builtin_amdgcn_readlane(v, l);
+}
+__device__ __forceinline__ uint32_t read_lane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int32_t)v, l);
+}
+__device__ __forceinline__ int64_t read_lane(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)(uint64_t)v, l);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint64_t read_lane(uint64_t v, int l) {
+  return (uint64_t)read_lane((int64_t)v, l);
 }
 
+// Wave-wide sum of an integer type (all 64 lanes active): butterflies inside
+// each row, then the four row sums; every lane gets the same value.
+template <typename I>
+__device__ __forceinline__ I wave_sum(I v) {
+  static_assert(std::is_integral<I>::value, "integer sums only");
+  v += dpp_move<DPP_QUAD_XOR1>(v);
+  v += dpp_move<DPP_QUAD_XOR2>(v);
+  v += dpp_move<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_move<DPP_ROW_MIRROR>(v);
+  return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
+}
+
+// Inclusive prefix sum over the wave (integer types, all 64 lanes active):
+// shifts by 1, 2, 4, 8 inside each row of 16, then each row adds the totals
+// of the rows before it.
 template <typename I>
 __device__ __forceinline__ I wave_incl_scan(I v) {
-  const int l = __lane_id();
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    I t = __shfl_up(v, o, WAVE);
-    if (l >= o) v += t;
-  }
-  return v;
+  static_assert(std::is_integral<I>::value, "integer scans only");
+  v += dpp_move<dpp_row_shr(1)>(v);
+  v += dpp_move<dpp_row_shr(2)>(v);
+  v += dpp_move<dpp_row_shr(4)>(v);
+  v += dpp_move<dpp_row_shr(8)>(v);
+  const I r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+  const int row = __lane_id() >> 4;
+  I add = 0;
+  if (row >= 1) add += r0;
+  if (row >= 2) add += r1;
+  if (row >= 3) add += r2;
+  return v + add;
 }
 
 // Spread the low 21 bits of v to every third bit (bit b -> bit 3b).

@@ -45,6 +45,7 @@ namespace mbg {
 
 constexpr int WK_THREADS = 256;
 constexpr int WK_WAVES = WK_THREADS / WAVE;
+constexpr int WALK_TAB = 8 * WAVE;  // candidates of 64 carried entries (<= 8 children each)
 
 // Opening criterion, theta = |l_A + l_B| / |c_A - c_B| with l = (h, h, h):
 // accept iff 3 (h_A + h_B)^2 < fl(theta^2) |c_A - c_B|^2.  Centres and
@@ -65,9 +66,13 @@ __device__ __forceinline__ bool accept_pair(const int4& A, const int4& B, double
 // first the carried leaves (levels < s, kept as they are: phase 0), then the
 // children of the carried non-leaves (level s: phase 1).  X's carry is the
 // entries of its parent's carry union with X's bit set (for the root: the
-// root).  f(active, cand, phase) is called by the whole wave.
+// root).  f(active, cand, geo of cand, phase) is called by the whole wave; the
+// geometry of the next 64 candidates is loaded before f runs on the current
+// ones, so its latency overlaps their classification.  tab: the wave's LDS
+// table of WALK_TAB candidates.
 template <typename F>
-__device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int32_t X, F&& f) {
+__device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int32_t X, int32_t* tab,
+                                                   F&& f) {
   const int lane = __lane_id();
   const uint64_t* gen;
   int gc, slot;
@@ -99,25 +104,30 @@ __device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int32_t X,
           }
         }
       }
+      // the (at most 8 x 64) candidates of these entries, in order, in the
+      // wave's LDS table
       const int incl = wave_incl_scan(nc);
       const int excl = incl - nc;
-      const int tot = __shfl(incl, WAVE - 1, WAVE);
-      for (int b = 0; b < tot; b += WAVE) {
-        const int qi = b + lane;
-        const bool active = qi < tot;
-        // smallest lane h with incl[h] > qi
-        int h = 0;
-#pragma unroll
-        for (int step = 32; step >= 1; step >>= 1) {
-          const int probe = h + step - 1;
-          const int v = __shfl(incl, probe, WAVE);
-          if (v <= qi) h += step;
-        }
-        h = min(h, WAVE - 1);
-        const int fch = __shfl(fc, h, WAVE);
-        const int exh = __shfl(excl, h, WAVE);
-        f(active, (int32_t)(fch + (qi - exh)), phase);
+      const int tot = read_lane(incl, WAVE - 1);
+      for (int k = 0; k < nc; k++) tab[excl + k] = fc + k;
+      __builtin_amdgcn_wave_barrier();
+      int32_t cn = 0;
+      int4 gn = make_int4(0, 0, 0, 0);
+      if (lane < tot) {
+        cn = tab[lane];
+        gn = a.geo[cn];
       }
+      for (int b = 0; b < tot; b += WAVE) {
+        const bool active = b + lane < tot;
+        const int32_t c = cn;
+        const int4 g = gn;
+        if (b + WAVE + lane < tot) {
+          cn = tab[b + WAVE + lane];
+          gn = a.geo[cn];
+        }
+        f(active, c, g, phase);
+      }
+      __builtin_amdgcn_wave_barrier();  // the table is read before it is refilled
     }
   }
 }
@@ -154,10 +164,9 @@ __device__ __forceinline__ Group load_group(const WalkArgs& a, int32_t X) {
   return G;
 }
 
-// Classify candidate c for every child: masks of M2L, P2P and carry.
-__device__ __forceinline__ void classify(const WalkArgs& a, const Group& G, int32_t c,
+// Classify a candidate of geometry g for every child: masks of M2L, P2P and carry.
+__device__ __forceinline__ void classify(const WalkArgs& a, const Group& G, const int4& g,
                                          uint32_t& mM, uint32_t& mP, uint32_t& mC) {
-  const int4 g = a.geo[c];
   uint32_t acc = 0;
 #pragma unroll
   for (int t = 0; t < 8; t++)
@@ -193,6 +202,8 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
   // after an overflow the carry unions may be incomplete: do nothing, the host
   // regrows the pools and repeats the walk
   if (a.ctrl->pool_overflow) return;
+  __shared__ int32_t tab_all[WK_WAVES][WALK_TAB];
+  int32_t* tab = tab_all[threadIdx.x / WAVE];
   const int lane = __lane_id();
   const uint64_t lt = lanemask_lt();
   for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.pcnt;
@@ -234,9 +245,9 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
     int64_t kU = 0, kPU = 0, kCU = 0;
     uint32_t ntm = 0, ntp = 0;  // per lane
     uint64_t cm[4] = {0, 0, 0, 0}, cp[4] = {0, 0, 0, 0};
-    for_each_candidate(a, X, [&](bool act, int32_t c, int phase) {
+    for_each_candidate(a, X, tab, [&](bool act, int32_t c, const int4& g, int phase) {
       uint32_t mM = 0, mP = 0, mC = 0;
-      if (act) classify(a, G, c, mM, mP, mC);
+      if (act) classify(a, G, g, mM, mP, mC);
       const uint64_t packed = (uint64_t)(uint32_t)c << 8;
       const uint64_t bU = __ballot(mM != 0), bP = __ballot(mP != 0), bC = __ballot(mC != 0);
       if (mM) a.u.data[o[1] + kU + __popcll(bU & lt)] = packed | mM;
@@ -304,7 +315,7 @@ __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a) {
       if (c0 + lane < gen.n) {
         const uint64_t e = gen.e[c0 + lane];
         c = (int32_t)(e >> 8);
-        if (((e >> gen.slot) & 1u) && a.n_child[c] == 0) classify(a, G, c, mM, mP, mC);
+        if (((e >> gen.slot) & 1u) && a.n_child[c] == 0) classify(a, G, a.geo[c], mM, mP, mC);
       }
       const int nm = __popc(mM), np = __popc(mP);
       const int im = wave_incl_scan(nm), ip = wave_incl_scan(np);
