@@ -52,6 +52,14 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
   return (uint32_t)dpp_move<CTRL>((int32_t)v);
 }
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+  return __longlong_as_double((long long)dpp_move<CTRL>((int64_t)__double_as_longlong(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(dpp_move<CTRL>((int32_t)__float_as_int(v)));
+}
 __device__ __forceinline__ int32_t read_lane(int32_t v, int l) {
   return __builtin_amdgcn_readlane(v, l);
 }

@@ -42,6 +42,16 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
 __device__ __forceinline__ float rsqrt_any(float x) { return __builtin_amdgcn_rsqf(x); }
 __device__ __forceinline__ double rsqrt_any(double x) { return rsqrt_f64(x); }
 
+// Sum over the 8 lanes 8t .. 8t + 7 by DPP moves inside the row: pairs, then
+// quads, then the two quads (half mirror); all 8 lanes get the same value.
+template <typename T>
+__device__ __forceinline__ T sum8(T x) {
+  x += dpp_move<DPP_QUAD_XOR1>(x);
+  x += dpp_move<DPP_QUAD_XOR2>(x);
+  x += dpp_move<DPP_ROW_HALF_MIRROR>(x);
+  return x;
+}
+
 // ---------------- source records ----------------
 // Thread per node: fold the moments (components with m_z >= 2 onto m_z - 2,
 // largest z first) and store the (P+1)^2 remaining ones with the centre.
@@ -245,9 +255,7 @@ __global__ void __launch_bounds__(M2L_THREADS)
 #pragma unroll
     for (int r = 0; r < KR; r++) {
       T x = acc[r];
-      x += __shfl_xor(x, 1, WAVE);
-      x += __shfl_xor(x, 2, WAVE);
-      x += __shfl_xor(x, 4, WAVE);
+      x = sum8(x);
       acc[r] = -x;  // G = 1: L = -sum
     }
     T L[K];
@@ -297,23 +305,45 @@ __global__ void __launch_bounds__(M2L_THREADS)
     T acc[KR];
 #pragma unroll
     for (int k = 0; k < KR; k++) acc[k] = (T)0;
-    for (int e = j; e < n; e += 8) {
-      const int64_t b = (int64_t)(keys[e0 + e] & src_mask);
-      const unsigned char* rb = mrec + b * RB;
+    // software pipeline (when the registers allow: low orders): the next
+    // entry's record is loaded while the current one is used, and the key
+    // after it one step earlier still
+    constexpr bool PIPE = KR * sizeof(T) <= 200;
+    T Mn[KR];
+    double cn[3];
+    auto load_rec = [&](uint64_t key) {
+      const unsigned char* rb = mrec + (int64_t)(key & src_mask) * RB;
       const T* Mb = (const T*)rb;
-      T M[KR];
 #pragma unroll
-      for (int k = 0; k < KR; k++) M[k] = Mb[k];
+      for (int k = 0; k < KR; k++) Mn[k] = Mb[k];
       const double* cb = (const double*)(rb + CB);
-      const T rx = (T)(ax - cb[0]), ry = (T)(ay - cb[1]), rz = (T)(az - cb[2]);
-      dtensor_contract<T, P>(rx, ry, rz, M, acc);
+      cn[0] = cb[0];
+      cn[1] = cb[1];
+      cn[2] = cb[2];
+    };
+    if constexpr (PIPE) {
+      uint64_t knext = j + 8 < n ? keys[e0 + j + 8] : 0ull;
+      if (j < n) load_rec(keys[e0 + j]);
+      for (int e = j; e < n; e += 8) {
+        T M[KR];
+#pragma unroll
+        for (int k = 0; k < KR; k++) M[k] = Mn[k];
+        const T rx = (T)(ax - cn[0]), ry = (T)(ay - cn[1]), rz = (T)(az - cn[2]);
+        if (e + 8 < n) load_rec(knext);
+        if (e + 16 < n) knext = keys[e0 + e + 16];
+        dtensor_contract<T, P>(rx, ry, rz, M, acc);
+      }
+    } else {
+      for (int e = j; e < n; e += 8) {
+        load_rec(keys[e0 + e]);
+        const T rx = (T)(ax - cn[0]), ry = (T)(ay - cn[1]), rz = (T)(az - cn[2]);
+        dtensor_contract<T, P>(rx, ry, rz, Mn, acc);
+      }
     }
 #pragma unroll
     for (int r = 0; r < KR; r++) {
       T x = acc[r];
-      x += __shfl_xor(x, 1, WAVE);
-      x += __shfl_xor(x, 2, WAVE);
-      x += __shfl_xor(x, 4, WAVE);
+      x = sum8(x);
       acc[r] = x;
     }
     T S[K];
