@@ -70,11 +70,12 @@ enum fmm_stage {
   FMM_STAGE_SORT = 1,  /* radix sort + gather into sorted order */
   FMM_STAGE_TREE = 2,  /* octree build                          */
   FMM_STAGE_WALK = 3,  /* dual-tree walk, M2L and P2P lists     */
-  FMM_STAGE_UP = 4,    /* P2M + M2M + M2L source records (build) */
-  FMM_STAGE_M2L = 5,   /* the single M2L launch                 */
+  FMM_STAGE_UP = 4,    /* P2M + M2M + M2L source records (build, second stream) */
+  FMM_STAGE_M2L = 5,   /* M2L of the own entries, sibling kernel (build, second stream) */
   FMM_STAGE_DOWN = 6,  /* L2L + L2P                             */
   FMM_STAGE_P2P = 7,   /* the single P2P (+ combine) launch     */
-  FMM_N_STAGES = 8
+  FMM_STAGE_TAIL = 8,  /* M2L of the transposed tails (eval)    */
+  FMM_N_STAGES = 9
 };
 
 /* Kernel indices of fmm_stats_t.kernel_ms: single launches inside the M2L
@@ -95,7 +96,7 @@ typedef struct {
   double lo[3], side;    /* root cube */
   float stage_ms[FMM_N_STAGES]; /* mean over the timed steps, see fmm_set_timing */
   int32_t walk_retries;  /* workspace regrowths during the last walk */
-  float kernel_ms[FMM_N_KERNELS]; /* mean over the timed evals */
+  float kernel_ms[FMM_N_KERNELS]; /* mean over the timed builds (sibling M2L) or evals */
   int32_t timed_builds;  /* builds and evals the means are taken over */
   int32_t timed_evals;
   int32_t reserved[1];
@@ -107,21 +108,24 @@ typedef struct {
  * on demand during builds (grow-only, freed by fmm_destroy). */
 int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size, int dtype);
 
-/* Sort the particles, build the octree and the interaction lists, and form the
- * multipoles (P2M, M2M).  pos [N][3] and mass [N] are device arrays in the
- * plan's dtype; they are copied into the plan's sorted layout, so the caller
- * may reuse them once `stream` has passed this call.  The multipoles depend on
- * the tree only: they are formed on a second stream owned by the plan, which
+/* Sort the particles, build the octree and the interaction lists, form the
+ * multipoles (P2M, M2M) and translate them along the own M2L entries (every
+ * pair whose source is at the target's level or coarser).  pos [N][3] and
+ * mass [N] are device arrays in the plan's dtype; they are copied into the
+ * plan's sorted layout, so the caller may reuse them once `stream` has passed
+ * this call.  The multipoles need the tree only and the own-entry M2L the
+ * walk's unions only: both run on a second stream owned by the plan, which
  * starts after the tree and overlaps the walk; the next fmm_eval or fmm_build
  * on any stream waits for it.  Synchronizes `stream` three times (tree size,
  * list sizes twice).  Returns FMM_ERR_NONFINITE (and leaves the plan un-built)
  * if any input is NaN/Inf. */
 int fmm_build(fmm_plan_t plan, const void* pos, const void* mass, void* stream);
 
-/* Evaluate potential and acceleration of every particle: M2L, L2L, L2P, P2P
- * (after the build's multipoles), written in the caller's order.  phi [N] and acc [N][3] are device
- * arrays in the plan's dtype.  Asynchronous on `stream`; may be repeated after
- * one build. */
+/* Evaluate potential and acceleration of every particle: the M2L of the
+ * transposed entries, L2L, L2P and P2P on top of the build's far-field work,
+ * written in the caller's order.  phi [N] and acc [N][3] are device arrays in
+ * the plan's dtype.  Asynchronous on `stream`; may be repeated after one
+ * build (the build's results are only read). */
 int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
 
 /* Free the plan and its workspace (synchronizes the device). */

@@ -96,16 +96,20 @@ void collect_early_build(fmm_plan_t p) {
 }
 void collect_pending(fmm_plan_t p) {
   if (p->pend_build) {
-    for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP})
+    for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP, FMM_STAGE_M2L})
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
+    if (p->kran[FMM_KERNEL_M2L_SIB])
+      p->kernel_sum[FMM_KERNEL_M2L_SIB] +=
+          elapsed(p->kev[2 * FMM_KERNEL_M2L_SIB], p->kev[2 * FMM_KERNEL_M2L_SIB + 1]);
     p->n_timed_builds++;
     p->pend_build = false;
   }
   if (p->pend_eval) {
-    for (int s = FMM_STAGE_M2L; s <= FMM_STAGE_P2P; s++)
+    for (int s : {FMM_STAGE_TAIL, FMM_STAGE_DOWN, FMM_STAGE_P2P})
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
     for (int k = 0; k < FMM_N_KERNELS; k++)
-      if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
+      if (k != FMM_KERNEL_M2L_SIB && p->kran[k])
+        p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_evals++;
     p->pend_eval = false;
   }
@@ -139,6 +143,47 @@ int bits_for(int64_t v) {  // bits to hold 0..v
   int b = 1;
   while (b < 62 && ((int64_t)1 << b) <= v) b++;
   return b;
+}
+
+// Arguments of the M2L kernels for the current build.
+M2LArgs m2l_args(fmm_plan_t p) {
+  M2LArgs ma{};
+  ma.n_nodes = p->n_nodes;
+  ma.parents = P<int32_t>(p->m2l_order);
+  ma.n_parents = p->n_parents;
+  ma.first_child = P<int32_t>(p->nfirst);
+  ma.n_child = P<uint8_t>(p->nnchild);
+  ma.upool = P<uint64_t>(p->pool[POOL_U]);
+  ma.u_off = P<int64_t>(p->u_off);
+  ma.u_cnt = P<int32_t>(p->u_cnt);
+  ma.leaves = P<int32_t>(p->leaves);
+  ma.n_leaves = p->n_leaves;
+  ma.tasks = P<TailTask>(p->tail_task);
+  ma.n_tasks = p->n_tail_tasks;
+  ma.toff = P<int64_t>(p->tail_toff);
+  ma.keys = p->tr_sorted;
+  ma.src_mask = (1ull << p->key_shift) - 1ull;
+  ma.centre = P<double>(p->ncentre);
+  ma.mrec = p->mred.p;
+  ma.part = p->tail_part.p;
+  ma.local = p->local.p;
+  return ma;
+}
+
+// The sibling M2L on the second stream: after the upward pass (same stream)
+// and the launch order (ev_order on the walk's stream).  ev_up marks its end.
+int issue_sibling_m2l(fmm_plan_t p, hipStream_t st) {
+  hipStream_t us = p->up_stream;
+  TRY_HIP(hipEventRecord(p->ev_order, st));
+  TRY_HIP(hipStreamWaitEvent(us, p->ev_order, 0));
+  M2LArgs ma = m2l_args(p);
+  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_SIB : nullptr;
+  ma.ran = p->kran + FMM_KERNEL_M2L_SIB;
+  rec(p, FMM_STAGE_M2L, 0, us);
+  TRY_HIP(launch_m2l_sib(p->dtype, p->order, ma, us));
+  rec(p, FMM_STAGE_M2L, 1, us);
+  TRY_HIP(hipEventRecord(p->ev_up, us));
+  return FMM_OK;
 }
 
 int run_walk(fmm_plan_t p, hipStream_t st) {
@@ -252,6 +297,16 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   p->n_tr = ntr;
   p->m2l_lists_ready = false;
 
+  // launch order of the M2L sibling blocks; then the sibling M2L itself on the
+  // second stream, where it overlaps the rest of the walk
+  TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
+  TRY(grow_order_bufs(p, np));
+  int32_t* ord = nullptr;
+  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, order_bufs(p), &ord, st));
+  if (np > 0)
+    TRY_HIP(hipMemcpyAsync(p->m2l_order.p, ord, (size_t)np * 4, hipMemcpyDeviceToDevice, st));
+  TRY(issue_sibling_m2l(p, st));
+
   // transposed entries: emitted in group order (ascending source for each
   // target), then stably sorted on (kind, target); run lengths per target
   int32_t* tr_cnt = P<int32_t>(p->tr_cnt_m2l);
@@ -277,14 +332,6 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     TRY_HIP(launch_tr_runs(sorted, ntr, a.key_shift, kind_bit, nn, tr_start, tr_cnt, st));
   }
   p->tr_sorted = sorted;
-
-  // launch order of the M2L sibling blocks
-  TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
-  TRY(grow_order_bufs(p, np));
-  int32_t* ord = nullptr;
-  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, order_bufs(p), &ord, st));
-  if (np > 0)
-    TRY_HIP(hipMemcpyAsync(p->m2l_order.p, ord, (size_t)np * 4, hipMemcpyDeviceToDevice, st));
 
   // P2P lists: own entries (from the parents' P2P unions) then transposed ones
   int64_t* p2p_off = P<int64_t>(p->p2p_off);
@@ -413,6 +460,7 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
   // default priority, like every stream of the library
   if (hipStreamCreateWithFlags(&p->up_stream, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_tree, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_order, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_up, hipEventDisableTiming) != hipSuccess)
     return fail(FMM_ERR_HIP);
   *out = p;
@@ -429,7 +477,7 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->bbox_part,  &p->nlevel,      &p->nprefix,     &p->nbegin,
                   &p->ncount,     &p->nparent,     &p->nfirst,      &p->nnchild,
                   &p->ncentre,    &p->nq,          &p->ngeo,        &p->leaves,
-                  &p->lvl_blkcnt, &p->mpole,       &p->mred,        &p->local,
+                  &p->lvl_blkcnt, &p->mpole,       &p->mred,        &p->local,       &p->lfin,
                   &p->pool[0],
                   &p->pool[1],    &p->pool[2],
                   &p->cu_off,     &p->cu_cnt,      &p->u_off,       &p->u_cnt,
@@ -450,6 +498,7 @@ int fmm_destroy(fmm_plan_t p) {
   for (int i = 0; i < 2 * FMM_N_KERNELS; i++)
     if (p->kev[i]) (void)hipEventDestroy(p->kev[i]);
   if (p->ev_tree) (void)hipEventDestroy(p->ev_tree);
+  if (p->ev_order) (void)hipEventDestroy(p->ev_order);
   if (p->ev_up) (void)hipEventDestroy(p->ev_up);
   if (p->up_stream) (void)hipStreamDestroy(p->up_stream);
   delete p;
@@ -479,7 +528,8 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   const int64_t n = p->n;
   Control* ctrl = P<Control>(p->ctrl);
   RootInfo* root = P<RootInfo>(p->root);
-  // the previous build's upward pass reads the sorted particles and the tree
+  // the previous build's second stream reads the sorted particles, the tree
+  // and the walk's unions
   if (p->up_issued) TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
 
   rec(p, FMM_STAGE_KEYS, 0, st);
@@ -508,6 +558,7 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   TRY_HIP(hipMemcpyAsync(&p->root_host, root, sizeof(RootInfo), hipMemcpyDeviceToHost, st));
   TRY(sync_ctrl(p, st));
   collect_pending(p);  // the previous step's events have completed
+  for (int k = 0; k < FMM_N_KERNELS; k++) p->kran[k] = false;
   if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;
   const Control& c = *p->ctrl_host;
   const int64_t nn = c.level_off[MAX_LEVELS];
@@ -536,6 +587,7 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   TRY(grow(p->mpole, w * p->K * nn));
   TRY(grow(p->mred, (size_t)mrec_bytes((p->order + 1) * (p->order + 1), (int)w) * nn));
   TRY(grow(p->local, w * p->K * nn));
+  TRY(grow(p->lfin, w * p->K * nn));
   TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
   TreeArrays t{P<uint8_t>(p->nlevel),  P<uint64_t>(p->nprefix), P<int32_t>(p->nbegin),
                P<int32_t>(p->ncount),  P<int32_t>(p->nparent),  P<int32_t>(p->nfirst),
@@ -565,11 +617,14 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
     TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, us));
     rec(p, FMM_STAGE_UP, 1, us);
   }
-  TRY_HIP(hipEventRecord(p->ev_up, us));
-  p->up_issued = true;
+  p->up_issued = true;  // ev_up is recorded by the walk, after the sibling M2L
 
   rec(p, FMM_STAGE_WALK, 0, st);
-  TRY(run_walk(p, st));
+  const int wrc = run_walk(p, st);
+  if (wrc != FMM_OK) {
+    (void)hipEventRecord(p->ev_up, us);  // the next call still waits for this stream
+    return wrc;
+  }
   rec(p, FMM_STAGE_WALK, 1, st);
   collect_early_build(p);  // keys, sort and tree ended before the walk's last sync
   p->built = true;
@@ -585,47 +640,38 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   const double* centre = P<double>(p->ncentre);
   int32_t* leaves = P<int32_t>(p->leaves);
 
-  // multipoles and source records come from the build's upward pass
+  // multipoles, source records and the own-entry locals come from the build's
+  // second stream; `local` is only read from here on
   TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
+  const int64_t nn = p->n_nodes;
+  const size_t lbytes = (size_t)nn * p->K * wbytes(dt);
+  const bool pull = ord <= 5;  // the one-launch downward pass
 
-  rec(p, FMM_STAGE_M2L, 0, st);
-  M2LArgs ma{};
-  ma.n_nodes = p->n_nodes;
-  ma.parents = P<int32_t>(p->m2l_order);
-  ma.n_parents = p->n_parents;
-  ma.first_child = P<int32_t>(p->nfirst);
-  ma.n_child = P<uint8_t>(p->nnchild);
-  ma.upool = P<uint64_t>(p->pool[POOL_U]);
-  ma.u_off = P<int64_t>(p->u_off);
-  ma.u_cnt = P<int32_t>(p->u_cnt);
-  ma.leaves = leaves;
-  ma.n_leaves = p->n_leaves;
-  ma.tasks = P<TailTask>(p->tail_task);
-  ma.n_tasks = p->n_tail_tasks;
-  ma.toff = P<int64_t>(p->tail_toff);
-  ma.keys = p->tr_sorted;
-  ma.src_mask = (1ull << p->key_shift) - 1ull;
-  ma.centre = centre;
-  ma.mrec = p->mred.p;
-  ma.part = p->tail_part.p;
-  ma.local = p->local.p;
-  for (int k = 0; k < FMM_N_KERNELS; k++) p->kran[k] = false;
-  ma.ev = p->timing ? p->kev : nullptr;
-  ma.ran = p->kran;
-  TRY_HIP(launch_m2l(dt, ord, ma, st));
-  rec(p, FMM_STAGE_M2L, 1, st);
+  rec(p, FMM_STAGE_TAIL, 0, st);
+  M2LArgs ma = m2l_args(p);
+  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_TAIL : nullptr;
+  ma.ran = p->kran + FMM_KERNEL_M2L_TAIL;
+  if (!pull) {  // the level-by-level pass works on a copy
+    TRY_HIP(hipMemcpyAsync(p->lfin.p, p->local.p, lbytes, hipMemcpyDeviceToDevice, st));
+    ma.local = p->lfin.p;
+  }
+  TRY_HIP(launch_m2l_tails(dt, ord, ma, !pull, st));
+  rec(p, FMM_STAGE_TAIL, 1, st);
 
   rec(p, FMM_STAGE_DOWN, 0, st);
-  p->l2l_pulled = launch_l2l_pull(dt, ord, leaves, p->n_leaves, P<int32_t>(p->nparent), centre,
-                                  p->local.p, st);
+  p->l2l_pulled = pull && launch_l2l_pull(dt, ord, leaves, p->n_leaves, P<int32_t>(p->nparent),
+                                          centre, p->local.p,
+                                          p->n_tail_tasks > 0 ? P<int64_t>(p->tail_toff) : nullptr,
+                                          p->tail_part.p, p->lfin.p, st);
+  if (pull && !p->l2l_pulled) return FMM_ERR_HIP;
   if (p->l2l_pulled) {
     TRY_HIP(hipGetLastError());
   } else {
     for (int l = 1; l <= p->depth; l++)
       TRY_HIP(launch_l2l(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
-                         P<int32_t>(p->nparent), centre, p->local.p, nullptr, st));
+                         P<int32_t>(p->nparent), centre, p->lfin.p, nullptr, st));
   }
-  TRY_HIP(launch_l2p(dt, ord, p->n, p->pts.p, P<int32_t>(p->leaf_of), centre, p->local.p,
+  TRY_HIP(launch_l2p(dt, ord, p->n, p->pts.p, P<int32_t>(p->leaf_of), centre, p->lfin.p,
                      p->far.p, st));
   rec(p, FMM_STAGE_DOWN, 1, st);
 
@@ -666,9 +712,12 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
     collect_pending(p);
     const double nb = std::max(1, p->n_timed_builds), ne = std::max(1, p->n_timed_evals);
     for (int s = 0; s < FMM_N_STAGES; s++)
-      out->stage_ms[s] =
-          (float)(p->stage_sum[s] / (s <= FMM_STAGE_WALK || s == FMM_STAGE_UP ? nb : ne));
-    for (int k = 0; k < FMM_N_KERNELS; k++) out->kernel_ms[k] = (float)(p->kernel_sum[k] / ne);
+      out->stage_ms[s] = (float)(p->stage_sum[s] / (s <= FMM_STAGE_WALK || s == FMM_STAGE_UP ||
+                                                             s == FMM_STAGE_M2L
+                                                         ? nb
+                                                         : ne));
+    for (int k = 0; k < FMM_N_KERNELS; k++)
+      out->kernel_ms[k] = (float)(p->kernel_sum[k] / (k == FMM_KERNEL_M2L_SIB ? nb : ne));
     out->timed_builds = p->n_timed_builds;
     out->timed_evals = p->n_timed_evals;
   }
@@ -728,10 +777,12 @@ int fmm_copy_expansions(fmm_plan_t p, double* mpole, double* local) {
     (void)hipFree(dm);
     return FMM_ERR_OOM;
   }
-  // With the one-launch downward pass, internal nodes keep only their M2L
-  // part; their full locals (parent's shifted in, level by level) are rebuilt
-  // here on a copy, leaves being complete already.
-  void* lsrc = p->local.p;
+  // The eval's complete locals are in lfin: every node's with the
+  // level-by-level pass, the leaves' only with the one-launch pass.  There
+  // the internal nodes' full locals (own M2L part in `local`, parent's shifted
+  // in, level by level) are rebuilt on a copy, and the leaves' rows taken from
+  // lfin.
+  void* lsrc = p->lfin.p;
   void* tmp = nullptr;
   const size_t lbytes = m * wbytes(p->dtype);
   int rc = FMM_OK;
@@ -743,6 +794,10 @@ int fmm_copy_expansions(fmm_plan_t p, double* mpole, double* local) {
       rc = status_of(launch_l2l(p->dtype, p->order, p->level_off[l],
                                 p->level_off[l + 1] - p->level_off[l], P<int32_t>(p->nparent),
                                 P<double>(p->ncentre), tmp, P<uint8_t>(p->nnchild), nullptr));
+    if (rc == FMM_OK)
+      rc = status_of(launch_copy_rows(P<int32_t>(p->leaves), p->n_leaves,
+                                      (int64_t)p->K * (int64_t)wbytes(p->dtype), p->lfin.p, tmp,
+                                      nullptr));
     lsrc = tmp;
   }
   if (rc == FMM_OK)

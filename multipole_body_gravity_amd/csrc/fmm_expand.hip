@@ -255,23 +255,37 @@ __global__ void __launch_bounds__(256)
 
 // Downward pass for orders <= 5, one thread per leaf: Taylor shifts of a
 // degree-p polynomial are exact and compose, so the leaf's local is the sum of
-// its own M2L local and of every ancestor's M2L local shifted straight to the
-// leaf centre (leaf first, then up to the root; the same sums as the
-// level-by-level pass in another association).  Internal nodes' locals are
-// only read, so one launch replaces one launch per level.
+// its own M2L local (own entries, minus the sum of its transposed-tail task
+// partials in task order) and of every ancestor's M2L local shifted straight
+// to the leaf centre (leaf first, then up to the root; the same sums as the
+// level-by-level pass in another association).  `local` is only read; the
+// result goes to out[leaf], so one launch replaces one launch per level.
 template <typename T, int P>
 __global__ void __launch_bounds__(256)
     k_l2l_pull(const int32_t* leaves, int64_t n_leaves, const int32_t* parent,
-               const double* centre, T* local) {
+               const double* centre, const T* local, const int64_t* toff, const T* part,
+               T* out) {
   constexpr int K = Tabs<P>::K;
   constexpr int NTL = L2LTab<P>::NT;
   const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (li >= n_leaves) return;
   const int64_t a = leaves[li];
-  T* La = local + a * K;
+  const T* La = local + a * K;
   double acc[K];
+  if (toff && toff[li + 1] > toff[li]) {
+    T s[K];
 #pragma unroll
-  for (int k = 0; k < K; k++) acc[k] = (double)La[k];
+    for (int k = 0; k < K; k++) s[k] = (T)0;
+    for (int64_t q = toff[li]; q < toff[li + 1]; q++) {
+#pragma unroll
+      for (int k = 0; k < K; k++) s[k] += part[q * K + k];
+    }
+#pragma unroll
+    for (int k = 0; k < K; k++) acc[k] = (double)(La[k] - s[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; k++) acc[k] = (double)La[k];
+  }
   const double cx = centre[3 * a], cy = centre[3 * a + 1], cz = centre[3 * a + 2];
   for (int64_t q = parent[a]; q >= 0; q = parent[q]) {
     const double dx = cx - centre[3 * q], dy = cy - centre[3 * q + 1], dz = cz - centre[3 * q + 2];
@@ -293,19 +307,41 @@ __global__ void __launch_bounds__(256)
                               (px[l2l_tab<P>.ka[t]] * py[l2l_tab<P>.kb[t]] * pz[l2l_tab<P>.kc[t]]);
     });
   }
+  T* Oa = out + a * K;
 #pragma unroll
-  for (int k = 0; k < K; k++) La[k] = (T)acc[k];
+  for (int k = 0; k < K; k++) Oa[k] = (T)acc[k];
+}
+
+// dst row r = src row r for the listed rows (row_bytes a multiple of 4)
+__global__ void k_copy_rows(const int32_t* rows, int64_t n, int64_t words, const uint32_t* src,
+                            uint32_t* dst) {
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (g >= n * words) return;
+  const int64_t i = g / words, w = g - i * words;
+  const int64_t r = rows[i];
+  dst[r * words + w] = src[r * words + w];
+}
+
+hipError_t launch_copy_rows(const int32_t* rows, int64_t n, int64_t row_bytes, const void* src,
+                            void* dst, hipStream_t st) {
+  const int64_t words = row_bytes / 4;
+  if (n <= 0 || words <= 0) return hipSuccess;
+  const int64_t tot = n * words;
+  k_copy_rows<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(rows, n, words,
+                                                             (const uint32_t*)src, (uint32_t*)dst);
+  return hipGetLastError();
 }
 
 template <typename T>
 static bool l2l_pull_dispatch(int order, const int32_t* leaves, int64_t n_leaves,
-                              const int32_t* parent, const double* centre, void* local,
-                              hipStream_t st) {
+                              const int32_t* parent, const double* centre, const void* local,
+                              const int64_t* toff, const void* part, void* out, hipStream_t st) {
   const unsigned g = (unsigned)((n_leaves + 255) / 256);
   switch (order) {
 #define L2LP(P)                                                                              \
   case P:                                                                                    \
-    k_l2l_pull<T, P><<<g, 256, 0, st>>>(leaves, n_leaves, parent, centre, (T*)local);        \
+    k_l2l_pull<T, P><<<g, 256, 0, st>>>(leaves, n_leaves, parent, centre, (const T*)local,    \
+                                        toff, (const T*)part, (T*)out);                      \
     return true;
     L2LP(0) L2LP(1) L2LP(2) L2LP(3) L2LP(4) L2LP(5)
 #undef L2LP
@@ -315,11 +351,14 @@ static bool l2l_pull_dispatch(int order, const int32_t* leaves, int64_t n_leaves
 }
 
 bool launch_l2l_pull(int dtype, int order, const int32_t* leaves, int64_t n_leaves,
-                     const int32_t* parent, const double* centre, void* local, hipStream_t st) {
+                     const int32_t* parent, const double* centre, const void* local,
+                     const int64_t* toff, const void* part, void* out, hipStream_t st) {
+  if (order > 5) return false;
   if (n_leaves <= 0) return true;
-  return dtype == FMM_F64
-             ? l2l_pull_dispatch<double>(order, leaves, n_leaves, parent, centre, local, st)
-             : l2l_pull_dispatch<float>(order, leaves, n_leaves, parent, centre, local, st);
+  return dtype == FMM_F64 ? l2l_pull_dispatch<double>(order, leaves, n_leaves, parent, centre,
+                                                      local, toff, part, out, st)
+                          : l2l_pull_dispatch<float>(order, leaves, n_leaves, parent, centre,
+                                                     local, toff, part, out, st);
 }
 
 template <typename T>

@@ -77,7 +77,7 @@ struct fmm_plan_s {
   // node-sized
   mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq, ngeo;
   mbg::DBuf leaves, lvl_blkcnt;
-  mbg::DBuf mpole, mred, local;
+  mbg::DBuf mpole, mred, local, lfin;
   // walk: sharded pools (carry unions, M2L unions, P2P unions, transposed
   // M2L and P2P keys) and per-node slices / counts
   mbg::DBuf pool[mbg::N_POOLS];
@@ -116,8 +116,13 @@ struct fmm_plan_s {
   // The upward pass (P2M, M2M, M2L source records) depends only on the tree, so
   // a build issues it on a second stream of its own, where it overlaps the
   // walk; the eval's stream, and the next build's, wait for ev_up.
+  // The sibling M2L (own entries) needs the unions and their launch order
+  // only: the build issues it on the same stream after the upward pass, once
+  // the walk has ordered the groups (ev_order), so it overlaps the rest of the
+  // walk.  It writes `local`; the eval leaves `local` as it is and writes the
+  // leaves' complete locals into `lfin`, so evals can repeat.
   hipStream_t up_stream = nullptr;
-  hipEvent_t ev_tree = nullptr, ev_up = nullptr;
+  hipEvent_t ev_tree = nullptr, ev_order = nullptr, ev_up = nullptr;
   bool up_issued = false;
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
   hipEvent_t kev[2 * FMM_N_KERNELS] = {};  // begin/end of single kernel launches
@@ -277,7 +282,13 @@ struct M2LArgs {
   hipEvent_t* ev;         // null, or begin/end events of the sibling and tail kernels
   bool* ran;              // with ev: set when the kernel was launched
 };
-hipError_t launch_m2l(int dtype, int order, const M2LArgs& a, hipStream_t st);
+// own entries: clears the root's local, then the sibling kernel writes the
+// local of every other node (a.local)
+hipError_t launch_m2l_sib(int dtype, int order, const M2LArgs& a, hipStream_t st);
+// transposed tails: task partials into a.part; with combine, also subtracts
+// each leaf's partials, in task order, from a.local
+hipError_t launch_m2l_tails(int dtype, int order, const M2LArgs& a, bool combine,
+                            hipStream_t st);
 // scratch of a one-pass (8-bit key) stable sort used to order launches
 struct OrderBufs {
   uint64_t *key, *key_alt;
@@ -294,9 +305,14 @@ hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64
                             const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks,
                             hipStream_t st);
 // downward pass in one launch (orders with register kernels; false: not
-// available, use the per-level L2L)
+// available, use the per-level L2L): out[leaf] = local[leaf] - its tail
+// partials (toff / part, may be null) + every ancestor's local shifted to it
 bool launch_l2l_pull(int dtype, int order, const int32_t* leaves, int64_t n_leaves,
-                     const int32_t* parent, const double* centre, void* local, hipStream_t st);
+                     const int32_t* parent, const double* centre, const void* local,
+                     const int64_t* toff, const void* part, void* out, hipStream_t st);
+// dst row r = src row r for the n listed rows of row_bytes bytes each
+hipError_t launch_copy_rows(const int32_t* rows, int64_t n, int64_t row_bytes, const void* src,
+                            void* dst, hipStream_t st);
 // one level of the level-by-level L2L (skip_leaves: the n_child array, to leave
 // leaves untouched; register kernels only)
 hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,

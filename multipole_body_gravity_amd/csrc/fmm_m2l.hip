@@ -472,38 +472,55 @@ static unsigned m2l_grid(int64_t waves) {
 }
 
 template <typename T>
-static void m2l_dispatch(int order, hipStream_t st, const M2LArgs& a) {
-  const unsigned gs = m2l_grid(a.n_parents), gt = m2l_grid((a.n_tasks + 7) / 8);
+static void m2l_sib_dispatch(int order, hipStream_t st, const M2LArgs& a) {
+  const unsigned gs = m2l_grid(a.n_parents);
   const unsigned char* rec = (const unsigned char*)a.mrec;
-  // a.ev (optional): begin/end of the sibling kernel, then of the tail kernel
-  auto mark = [&](int k) {
-    if (a.ev) (void)hipEventRecord(a.ev[k], st);
-    if (a.ev && (k & 1)) a.ran[k >> 1] = true;
-  };
+  if (a.n_parents <= 0) return;
+  // a.ev (optional): begin/end events of the sibling kernel
+  if (a.ev) (void)hipEventRecord(a.ev[0], st);
   switch (order) {
-#define M2L_CASE(P)                                                                          \
+#define M2L_SIB(P)                                                                           \
   case P:                                                                                    \
-    if (a.n_parents > 0) {                                                                   \
-      mark(0);                                                                               \
-      k_m2l_sib<T, P><<<gs, M2L_THREADS, 0, st>>>(a.n_parents, a.parents, a.first_child,      \
-                                                  a.n_child, a.upool, a.u_off, a.u_cnt,      \
-                                                  a.centre, rec, (T*)a.local);               \
-      mark(1);                                                                               \
-    }                                                                                        \
-    if (a.n_tasks > 0) {                                                                     \
-      mark(2);                                                                               \
-      k_m2l_tail<T, P><<<gt, M2L_THREADS, 0, st>>>(a.n_tasks, a.tasks, a.leaves, a.keys,      \
-                                                   a.src_mask, a.centre, rec, (T*)a.part);   \
-      mark(3);                                                                               \
-    }                                                                                        \
+    k_m2l_sib<T, P><<<gs, M2L_THREADS, 0, st>>>(a.n_parents, a.parents, a.first_child,        \
+                                                a.n_child, a.upool, a.u_off, a.u_cnt,        \
+                                                a.centre, rec, (T*)a.local);                 \
     break;
-    M2L_CASE(0) M2L_CASE(1) M2L_CASE(2) M2L_CASE(3) M2L_CASE(4)
-    M2L_CASE(5) M2L_CASE(6) M2L_CASE(7) M2L_CASE(8)
-#undef M2L_CASE
+    M2L_SIB(0) M2L_SIB(1) M2L_SIB(2) M2L_SIB(3) M2L_SIB(4)
+    M2L_SIB(5) M2L_SIB(6) M2L_SIB(7) M2L_SIB(8)
+#undef M2L_SIB
     default:
       break;
   }
-  if (a.n_tasks > 0) {
+  if (a.ev) {
+    (void)hipEventRecord(a.ev[1], st);
+    a.ran[0] = true;
+  }
+}
+
+template <typename T>
+static void m2l_tail_dispatch(int order, hipStream_t st, const M2LArgs& a, bool combine) {
+  if (a.n_tasks <= 0) return;
+  const unsigned gt = m2l_grid((a.n_tasks + 7) / 8);
+  const unsigned char* rec = (const unsigned char*)a.mrec;
+  // a.ev (optional): begin/end events of the tail kernel
+  if (a.ev) (void)hipEventRecord(a.ev[0], st);
+  switch (order) {
+#define M2L_TAIL(P)                                                                          \
+  case P:                                                                                    \
+    k_m2l_tail<T, P><<<gt, M2L_THREADS, 0, st>>>(a.n_tasks, a.tasks, a.leaves, a.keys,        \
+                                                 a.src_mask, a.centre, rec, (T*)a.part);     \
+    break;
+    M2L_TAIL(0) M2L_TAIL(1) M2L_TAIL(2) M2L_TAIL(3) M2L_TAIL(4)
+    M2L_TAIL(5) M2L_TAIL(6) M2L_TAIL(7) M2L_TAIL(8)
+#undef M2L_TAIL
+    default:
+      break;
+  }
+  if (a.ev) {
+    (void)hipEventRecord(a.ev[1], st);
+    a.ran[0] = true;
+  }
+  if (combine) {
     const int K = ncoef(order);
     const unsigned g = (unsigned)((a.n_leaves * K + 255) / 256);
     k_m2l_tail_combine<T><<<g, 256, 0, st>>>(a.n_leaves, K, a.leaves, a.toff,
@@ -511,16 +528,25 @@ static void m2l_dispatch(int order, hipStream_t st, const M2LArgs& a) {
   }
 }
 
-hipError_t launch_m2l(int dtype, int order, const M2LArgs& a, hipStream_t st) {
+hipError_t launch_m2l_sib(int dtype, int order, const M2LArgs& a, hipStream_t st) {
   if (a.n_nodes <= 0) return hipSuccess;
   // the root is nobody's child: its local (no far-field terms) is cleared
   const size_t kb = (size_t)ncoef(order) * (dtype == FMM_F64 ? 8 : 4);
   hipError_t e = launch_fill_zero(a.local, kb, st);
   if (e != hipSuccess) return e;
   if (dtype == FMM_F64)
-    m2l_dispatch<double>(order, st, a);
+    m2l_sib_dispatch<double>(order, st, a);
   else
-    m2l_dispatch<float>(order, st, a);
+    m2l_sib_dispatch<float>(order, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_m2l_tails(int dtype, int order, const M2LArgs& a, bool combine,
+                            hipStream_t st) {
+  if (dtype == FMM_F64)
+    m2l_tail_dispatch<double>(order, st, a, combine);
+  else
+    m2l_tail_dispatch<float>(order, st, a, combine);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmbg_fmm.so")
 
 FMM_F32, FMM_F64 = 0, 1
 MAX_ORDER = 8
-STAGES = ["keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p"]
+STAGES = ["keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p", "tail"]  # stage_ms order
 KERNELS = ["m2l_sib", "m2l_tail", "p2p", "p2p_combine"]  # fmm_stats_t.kernel_ms order
 _ERR = {0: "ok", -1: "invalid argument", -2: "plan not built", -3: "device out of memory",
         -4: "HIP runtime error", -5: "non-finite position or mass", -6: "no HIP device"}
@@ -35,7 +35,7 @@ class _Stats(ctypes.Structure):
                 ("n_m2l", ctypes.c_int64), ("n_p2p", ctypes.c_int64), ("depth", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("leaf_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("theta", ctypes.c_double), ("lo", ctypes.c_double * 3), ("side", ctypes.c_double),
-                ("stage_ms", ctypes.c_float * 8), ("walk_retries", ctypes.c_int32),
+                ("stage_ms", ctypes.c_float * len(STAGES)), ("walk_retries", ctypes.c_int32),
                 ("kernel_ms", ctypes.c_float * 4), ("timed_builds", ctypes.c_int32),
                 ("timed_evals", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
