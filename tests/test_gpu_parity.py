@@ -282,3 +282,37 @@ def test_parity_lattice_sampled(orc, name, n_sample):
     check_structure(plan, ref, sample_targets=np.nonzero(ref.mark)[0])
     check_values(phi, acc, ref, c["dtype"], idx=smp)
     plan.close()
+
+
+def test_streams_and_timing(orc):
+    """Build on one stream and evaluate on another (the plan's second stream is
+    ordered against both); with timing on, every stage and kernel is counted
+    once per step and the means are positive."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    dev = torch.device("cuda:0")
+    pos, mass = W.make("plummer", 30000, 71)
+    tp, tm = torch.from_numpy(pos).to(dev), torch.from_numpy(mass).to(dev)
+    plan = Plan(30000, order=4, theta=0.7, leaf_size=16, dtype=torch.float64, device=dev)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())  # the inputs were copied on the default stream
+    plan.set_timing(True)
+    steps = 3
+    for _ in range(steps):
+        with torch.cuda.stream(s1):
+            plan.build(tp, tm, stream=s1)
+        s2.wait_stream(s1)
+        with torch.cuda.stream(s2):
+            phi, acc = plan.eval(stream=s2)
+    torch.cuda.synchronize()
+    st = plan.stats()
+    assert st["timed_builds"] == steps and st["timed_evals"] == steps, st
+    for k, v in st["stage_ms"].items():
+        assert v >= 0.0, (k, st["stage_ms"])
+    for k in ("keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p"):
+        assert st["stage_ms"][k] > 0.0, (k, st["stage_ms"])
+    for k in ("m2l_sib", "m2l_tail", "p2p"):
+        assert st["kernel_ms"][k] > 0.0, (k, st["kernel_ms"])
+    ref = orc.fmm(pos, mass, 4, 0.7, 16)
+    check_values(phi.cpu().numpy(), acc.cpu().numpy(), ref, "f64")
+    plan.close()
