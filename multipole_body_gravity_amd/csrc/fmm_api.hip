@@ -170,6 +170,23 @@ M2LArgs m2l_args(fmm_plan_t p) {
   return ma;
 }
 
+// P2M, M2M (deepest level first) and the M2L source records on the second
+// stream (ordered after the tree by ev_tree).
+int issue_upward(fmm_plan_t p) {
+  hipStream_t us = p->up_stream;
+  const int dt = p->dtype, ord = p->order;
+  const double* centre = P<double>(p->ncentre);
+  rec(p, FMM_STAGE_UP, 0, us);
+  TRY_HIP(launch_p2m(dt, ord, p->pts.p, P<int32_t>(p->leaves), p->n_leaves,
+                     P<int32_t>(p->nbegin), P<int32_t>(p->ncount), centre, p->mpole.p, us));
+  for (int l = p->depth - 1; l >= 0; l--)
+    TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                       P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, us));
+  TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, us));
+  rec(p, FMM_STAGE_UP, 1, us);
+  return FMM_OK;
+}
+
 // The sibling M2L on the second stream: after the upward pass (same stream)
 // and the launch order (ev_order on the walk's stream).  ev_up marks its end.
 int issue_sibling_m2l(fmm_plan_t p, hipStream_t st) {
@@ -265,6 +282,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
       a.pcnt = p->pbeg[l + 1] - p->pbeg[l];
       TRY_HIP(launch_walk(a, st));
     }
+    if (p->walk_retries == 0) TRY(issue_upward(p));
     TRY_HIP(launch_walk_own_totals(nn, a.own_m2l, a.own_p2p, dctrl, st));
     if (np > 0) {  // offsets of every group's transposed keys, in group order
       TRY_HIP(scan_exclusive_i64(a.trm_cnt, P<int64_t>(p->trm_base), np,
@@ -601,22 +619,12 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
                              st));
   rec(p, FMM_STAGE_TREE, 1, st);
 
-  // upward pass on the second stream, overlapping the walk
+  // the upward pass goes on the second stream after the tree; it is issued
+  // by the walk once its level launches are queued (host launch time then
+  // overlaps the walk's execution instead of delaying it)
   hipStream_t us = p->up_stream;
   TRY_HIP(hipEventRecord(p->ev_tree, st));
   TRY_HIP(hipStreamWaitEvent(us, p->ev_tree, 0));
-  {
-    const int dt = p->dtype, ord = p->order;
-    const double* centre = P<double>(p->ncentre);
-    rec(p, FMM_STAGE_UP, 0, us);
-    TRY_HIP(launch_p2m(dt, ord, p->pts.p, leaves, p->n_leaves, P<int32_t>(p->nbegin),
-                       P<int32_t>(p->ncount), centre, p->mpole.p, us));
-    for (int l = p->depth - 1; l >= 0; l--)
-      TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
-                         P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, us));
-    TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, us));
-    rec(p, FMM_STAGE_UP, 1, us);
-  }
   p->up_issued = true;  // ev_up is recorded by the walk, after the sibling M2L
 
   rec(p, FMM_STAGE_WALK, 0, st);
