@@ -323,7 +323,6 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, order_bufs(p), &ord, st));
   if (np > 0)
     TRY_HIP(hipMemcpyAsync(p->m2l_order.p, ord, (size_t)np * 4, hipMemcpyDeviceToDevice, st));
-  TRY(issue_sibling_m2l(p, st));
 
   // transposed entries: emitted in group order (ascending source for each
   // target), then stably sorted on (kind, target); run lengths per target
@@ -350,6 +349,9 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     TRY_HIP(launch_tr_runs(sorted, ntr, a.key_shift, kind_bit, nn, tr_start, tr_cnt, st));
   }
   p->tr_sorted = sorted;
+  // the sibling M2L beside the rest of the walk (after the transposed sort:
+  // beside that sort it was slower, the sort's kernels being starved)
+  TRY(issue_sibling_m2l(p, st));
 
   // P2P lists: own entries (from the parents' P2P unions) then transposed ones
   int64_t* p2p_off = P<int64_t>(p->p2p_off);
