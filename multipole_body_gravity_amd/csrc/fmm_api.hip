@@ -121,22 +121,6 @@ int sync_ctrl(fmm_plan_t p, hipStream_t st) {
   return FMM_OK;
 }
 
-// scratch of the launch-order sorts (grow-only)
-int grow_order_bufs(fmm_plan_t p, int64_t n) {
-  n = std::max<int64_t>(n, 1);
-  TRY(grow(p->ord_key, (size_t)n * 8));
-  TRY(grow(p->ord_key_alt, (size_t)n * 8));
-  TRY(grow(p->ord_val, (size_t)n * 4));
-  TRY(grow(p->ord_val_alt, (size_t)n * 4));
-  TRY(grow(p->radix_hist, 4 * radix_hist_ints(n)));
-  TRY(grow(p->scan_tmp, scan_tmp_bytes((int64_t)radix_hist_ints(n))));
-  return FMM_OK;
-}
-OrderBufs order_bufs(fmm_plan_t p) {
-  return OrderBufs{P<uint64_t>(p->ord_key), P<uint64_t>(p->ord_key_alt), P<int32_t>(p->ord_val),
-                   P<int32_t>(p->ord_val_alt), P<int32_t>(p->radix_hist),
-                   P<int32_t>(p->scan_tmp)};
-}
 
 // ---------------- walk ----------------
 int bits_for(int64_t v) {  // bits to hold 0..v
@@ -222,7 +206,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   TRY(grow(p->p2p_toff, (size_t)(nl + 1) * 8));
   TRY(grow(p->p2p_poff, (size_t)(nl + 1) * 8));
   TRY(grow(p->tail_toff, (size_t)(nl + 1) * 8));
-  TRY(grow(p->scan_tmp, scan_tmp_bytes(std::max(nn, nl) + 1)));
+  TRY(grow(p->scan_tmp, 3 * scan_tmp_bytes(std::max(nn, nl) + 1)));
   // the parents of level l (non-leaf nodes, id order) are parents[pbeg[l] .. pbeg[l + 1])
   p->n_parents = np;
   p->pbeg[0] = 0;
@@ -275,7 +259,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     Pool<uint64_t>* pools[N_POOLS] = {&a.cu, &a.u, &a.pu};
     for (int k = 0; k < N_POOLS; k++)
       *pools[k] = Pool<uint64_t>{P<uint64_t>(p->pool[k]), p->shard_cap[k], dctrl->pool_used[k]};
-    TRY_HIP(launch_walk_reset(dctrl, P<uint64_t>(p->rootgen), st));
+    TRY_HIP(launch_walk_reset(dctrl, P<uint64_t>(p->rootgen), root_leaf, st));
     TRY_HIP(launch_walk_root(1, root_leaf, a.own_m2l, a.own_p2p, nullptr, nullptr, st));
     for (int l = 0; l < depth; l++) {
       a.pbeg = p->pbeg[l];
@@ -283,16 +267,11 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
       TRY_HIP(launch_walk(a, st));
     }
     if (p->walk_retries == 0) TRY(issue_upward(p));
-    TRY_HIP(launch_walk_own_totals(nn, a.own_m2l, a.own_p2p, dctrl, st));
-    if (np > 0) {  // offsets of every group's transposed keys, in group order
-      TRY_HIP(scan_exclusive_i64(a.trm_cnt, P<int64_t>(p->trm_base), np,
-                                        P<int64_t>(p->trm_base) + np, p->scan_tmp.p, st));
-      TRY_HIP(scan_exclusive_i64(a.trp_cnt, P<int64_t>(p->trp_base), np,
-                                        P<int64_t>(p->trp_base) + np, p->scan_tmp.p, st));
-      TRY_HIP(launch_tr_totals(P<int64_t>(p->trm_base) + np, P<int64_t>(p->trp_base) + np, dctrl,
-                               st));
-    } else {
-      TRY_HIP(launch_fill_zero(&dctrl->n_trm, 16, st));
+    {  // offsets of every group's transposed keys, in group order; totals to the control block
+      const int64_t* in[2] = {a.trm_cnt, a.trp_cnt};
+      int64_t* out[2] = {P<int64_t>(p->trm_base), P<int64_t>(p->trp_base)};
+      int64_t* dst[2] = {&dctrl->n_trm, &dctrl->n_trp};
+      TRY_HIP(scan_exclusive_multi_i64(2, in, out, dst, np, p->scan_tmp.p, st));
     }
     TRY(sync_ctrl(p, st));
     if (!p->ctrl_host->pool_overflow) break;
@@ -305,24 +284,24 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     }
   }
   const Control& c = *p->ctrl_host;
-  int64_t nu = 0;
-  for (int sh = 0; sh < POOL_SHARDS; sh++) nu += c.pool_used[POOL_U][sh];
+  int64_t nu = 0, own_m = 0, own_p = c.own_p2p_total;  // the root's, when it is a leaf
+  for (int sh = 0; sh < POOL_SHARDS; sh++) {
+    nu += c.pool_used[POOL_U][sh];
+    own_m += c.own_used[0][sh];
+    own_p += c.own_used[1][sh];
+  }
   const int64_t ntm = c.n_trm, ntp = c.n_trp;
   const int64_t ntr = ntm + ntp;
   p->n_union = nu;  // room reserved for the M2L unions (an upper bound)
-  p->n_m2l = c.own_m2l_total + ntm;
-  p->n_p2p = c.own_p2p_total + ntp;
+  p->n_m2l = own_m + ntm;
+  p->n_p2p = own_p + ntp;
   p->n_tr = ntr;
   p->m2l_lists_ready = false;
 
   // launch order of the M2L sibling blocks; then the sibling M2L itself on the
   // second stream, where it overlaps the rest of the walk
   TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
-  TRY(grow_order_bufs(p, np));
-  int32_t* ord = nullptr;
-  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, order_bufs(p), &ord, st));
-  if (np > 0)
-    TRY_HIP(hipMemcpyAsync(p->m2l_order.p, ord, (size_t)np * 4, hipMemcpyDeviceToDevice, st));
+  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, dctrl, P<int32_t>(p->m2l_order), st));
 
   // transposed entries: emitted in group order (ascending source for each
   // target), then stably sorted on (kind, target); run lengths per target
@@ -356,7 +335,12 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   // P2P lists: own entries (from the parents' P2P unions) then transposed ones
   int64_t* p2p_off = P<int64_t>(p->p2p_off);
   TRY_HIP(launch_walk_offsets(nn, a.own_p2p, tr_cnt + nn, P<int64_t>(p->tot_p2p), st));
-  TRY_HIP(scan_exclusive_i64(P<int64_t>(p->tot_p2p), p2p_off, nn, p2p_off + nn, p->scan_tmp.p, st));
+  {
+    const int64_t* in[1] = {P<int64_t>(p->tot_p2p)};
+    int64_t* out[1] = {p2p_off};
+    int64_t* dst[1] = {&dctrl->n_p2p};
+    TRY_HIP(scan_exclusive_multi_i64(1, in, out, dst, nn, p->scan_tmp.p, st));
+  }
   TRY(grow(p->p2p_src, (size_t)std::max<int64_t>(p->n_p2p, 1) * 4));
   int32_t* p2p_src = P<int32_t>(p->p2p_src);
   TRY_HIP(launch_union_scatter(a.parents, np, a.first_child, a.n_child, a.pu.data, a.pu_off,
@@ -366,27 +350,26 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     TRY_HIP(launch_tr_scatter(sorted, ntr, a.key_shift, kind_bit, 1, nn, p2p_off, a.own_p2p,
                               tr_start + nn, p2p_src, st));
 
-  // near-field tasks
-  TRY_HIP(launch_p2p_task_count(leaves, nl, p2p_off, P<int32_t>(p->ncount), toff, poff, st));
-  TRY_HIP(scan_exclusive_i64(toff, toff, nl, toff + nl, p->scan_tmp.p, st));
-  TRY_HIP(scan_exclusive_i64(poff, poff, nl, poff + nl, p->scan_tmp.p, st));
-  // transposed-tail M2L tasks
+  // near-field tasks, their partial slots and the transposed-tail M2L tasks,
+  // per leaf; offsets and totals (to the control block) in one scan
   int64_t* ttoff = P<int64_t>(p->tail_toff);
-  TRY_HIP(launch_tail_count(leaves, nl, tr_cnt, ttoff, st));
-  TRY_HIP(scan_exclusive_i64(ttoff, ttoff, nl, ttoff + nl, p->scan_tmp.p, st));
-  TRY_HIP(launch_walk_copy_totals(p2p_off + nn, toff + nl, poff + nl, ttoff + nl, dctrl, st));
+  TRY_HIP(launch_leaf_task_counts(leaves, nl, p2p_off, P<int32_t>(p->ncount), tr_cnt, toff, poff,
+                                  ttoff, dctrl, st));
+  {
+    const int64_t* in[3] = {toff, poff, ttoff};
+    int64_t* out[3] = {toff, poff, ttoff};
+    int64_t* dst[3] = {&dctrl->n_p2p_tasks, &dctrl->n_p2p_part, &dctrl->n_tail_tasks};
+    TRY_HIP(scan_exclusive_multi_i64(3, in, out, dst, nl, p->scan_tmp.p, st));
+  }
   TRY(sync_ctrl(p, st));
   if (p->ctrl_host->n_p2p != p->n_p2p) return FMM_ERR_HIP;
   p->n_p2p_tasks = p->ctrl_host->n_p2p_tasks;
   p->n_p2p_part = p->ctrl_host->n_p2p_part;
   p->n_tail_tasks = p->ctrl_host->n_tail_tasks;
   TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
-  TRY(grow(p->p2p_task_tmp, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
-  TRY(grow_order_bufs(p, p->n_p2p_tasks));
   TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
   TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, p2p_off,
-                               P<int32_t>(p->ncount), p->p2p_task.p, p->p2p_task_tmp.p,
-                               order_bufs(p), st));
+                               P<int32_t>(p->ncount), dctrl, p->p2p_task.p, st));
   TRY(grow(p->tail_task, (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * sizeof(TailTask)));
   TRY(grow(p->tail_part,
            (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * p->K * wbytes(p->dtype)));
@@ -508,8 +491,7 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->tr_vals_alt, &p->m2l_off,    &p->m2l_src,     &p->p2p_off,
                   &p->p2p_src,    &p->p2p_task,    &p->p2p_part,    &p->p2p_toff,
                   &p->p2p_poff,   &p->tot_m2l,     &p->tot_p2p,     &p->parents,
-                  &p->m2l_order,  &p->ord_key,     &p->ord_key_alt, &p->ord_val,
-                  &p->ord_val_alt, &p->p2p_task_tmp,
+                  &p->m2l_order,
                   &p->tail_toff,  &p->tail_task,   &p->tail_part};
   for (DBuf* b : bufs) release(*b);
   if (p->ctrl_host) (void)hipHostFree(p->ctrl_host);

@@ -148,6 +148,108 @@ static hipError_t scan_excl(const I* in, I* out, int64_t n, I* total, void* tmp,
   return hipGetLastError();
 }
 
+// ---- up to 3 int64 arrays of one length scanned together ----
+// Exclusive scans of in[r] into out[r] (in place allowed), total of array r at
+// out[r][n] and, when given, also at dst[r] (a control-block field).
+template <int R>
+struct ScanMulti {
+  const int64_t* in[R];
+  int64_t* out[R];
+  int64_t* dst[R];
+};
+
+template <int R>
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_multi_reduce(ScanMulti<R> a, int64_t n,
+                                                                    int64_t* sums) {
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    int64_t s = 0;
+#pragma unroll
+    for (int i = 0; i < SCAN_ITEMS; i++)
+      if (base + i < n) s += a.in[r][base + i];
+    int64_t tot;
+    block_excl_scan(s, &tot);
+    if (threadIdx.x == 0) sums[(int64_t)r * gridDim.x + blockIdx.x] = tot;
+  }
+}
+
+// each block sums the block totals before it itself (at most a few thousand)
+template <int R>
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_multi_apply(ScanMulti<R> a, int64_t n,
+                                                                   const int64_t* sums) {
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    int64_t part = 0;
+    if (sums)
+      for (int64_t i = threadIdx.x; i < (int64_t)blockIdx.x; i += SCAN_THREADS)
+        part += sums[(int64_t)r * gridDim.x + i];
+    int64_t boff;
+    block_excl_scan(part, &boff);
+    int64_t v[SCAN_ITEMS];
+    int64_t s = 0;
+#pragma unroll
+    for (int i = 0; i < SCAN_ITEMS; i++) {
+      v[i] = (base + i < n) ? a.in[r][base + i] : 0;
+      s += v[i];
+    }
+    int64_t tot;
+    int64_t ex = block_excl_scan(s, &tot) + boff;
+#pragma unroll
+    for (int i = 0; i < SCAN_ITEMS; i++) {
+      if (base + i < n) a.out[r][base + i] = ex;
+      ex += v[i];
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+      a.out[r][n] = boff + tot;
+      if (a.dst[r]) *a.dst[r] = boff + tot;
+    }
+  }
+}
+
+template <int R>
+static hipError_t scan_multi(const ScanMulti<R>& a, int64_t n, void* tmp, hipStream_t st) {
+  const int64_t nb = std::max<int64_t>((n + SCAN_TILE - 1) / SCAN_TILE, 1);
+  if (nb > SCAN_DIRECT_BLOCKS) {  // long arrays: one classic scan per array
+    for (int r = 0; r < R; r++) {
+      hipError_t e = scan_excl<int64_t>(a.in[r], a.out[r], n, a.out[r] + n, tmp, st);
+      if (e != hipSuccess) return e;
+      if (a.dst[r]) {
+        e = hipMemcpyAsync(a.dst[r], a.out[r] + n, 8, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return e;
+      }
+    }
+    return hipSuccess;
+  }
+  int64_t* sums = (int64_t*)tmp;
+  if (nb > 1) k_scan_multi_reduce<R><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(a, n, sums);
+  k_scan_multi_apply<R><<<(unsigned)nb, SCAN_THREADS, 0, st>>>(a, n, nb > 1 ? sums : nullptr);
+  return hipGetLastError();
+}
+
+hipError_t scan_exclusive_multi_i64(int r, const int64_t* const* in, int64_t* const* out,
+                                    int64_t* const* dst, int64_t n, void* tmp, hipStream_t st) {
+  switch (r) {
+    case 1: {
+      ScanMulti<1> a{{in[0]}, {out[0]}, {dst ? dst[0] : nullptr}};
+      return scan_multi<1>(a, n, tmp, st);
+    }
+    case 2: {
+      ScanMulti<2> a{{in[0], in[1]}, {out[0], out[1]},
+                     {dst ? dst[0] : nullptr, dst ? dst[1] : nullptr}};
+      return scan_multi<2>(a, n, tmp, st);
+    }
+    case 3: {
+      ScanMulti<3> a{{in[0], in[1], in[2]}, {out[0], out[1], out[2]},
+                     {dst ? dst[0] : nullptr, dst ? dst[1] : nullptr, dst ? dst[2] : nullptr}};
+      return scan_multi<3>(a, n, tmp, st);
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 hipError_t scan_exclusive_i64(const int64_t* in, int64_t* out, int64_t n, int64_t* total,
                               void* tmp, hipStream_t st) {
   return scan_excl<int64_t>(in, out, n, total, tmp, st);

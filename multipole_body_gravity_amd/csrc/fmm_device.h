@@ -107,6 +107,34 @@ __device__ __forceinline__ I wave_incl_scan(I v) {
   return v + add;
 }
 
+// Launch-order octave of a work estimate w: 63 - floor(log2 w), 63 for w = 0
+// (so ascending octaves are descending work).
+__device__ __forceinline__ int work_octave(uint64_t w) {
+  return 63 - (w ? 63 - __clzll(w) : 0);
+}
+
+// Block-wide placement into octave buckets (blockDim.x threads, all calling):
+// returns this thread's slot for octave o (o < 0: none).  oct[] holds the
+// bucket sizes of the whole launch, cur[] global cursors (zero at the start);
+// a block takes one contiguous range per bucket, so items of one block stay
+// together, in an order that depends on timing only inside the block.
+template <int NB>
+__device__ __forceinline__ int64_t octave_slot(int o, const int32_t* oct, int32_t* cur) {
+  __shared__ int cnt[NB];
+  __shared__ int64_t base[NB];
+  for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
+  __syncthreads();
+  const int r = o >= 0 ? atomicAdd(&cnt[o], 1) : 0;
+  __syncthreads();
+  for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+    int64_t start = 0;
+    for (int q = 0; q < b; q++) start += oct[q];
+    base[b] = cnt[b] ? start + atomicAdd(&cur[b], cnt[b]) : 0;
+  }
+  __syncthreads();
+  return o >= 0 ? base[o] + r : -1;
+}
+
 // Spread the low 21 bits of v to every third bit (bit b -> bit 3b).
 __device__ __forceinline__ uint64_t spread3(uint32_t v) {
   uint64_t x = v & 0x1fffffull;

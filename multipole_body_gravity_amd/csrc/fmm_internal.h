@@ -31,6 +31,9 @@ struct RootInfo {
   double scale;  // 2^21 / side (exact)
 };
 
+// Work octaves in the launch orders (descending: octave 63 - floor(log2 w)).
+constexpr int ORDER_OCT = 64;
+
 // Device scalars written by kernels and read back at the build syncs.
 constexpr int POOL_SHARDS = 512;
 enum { POOL_CU = 0, POOL_U = 1, POOL_PU = 2, N_POOLS = 3 };
@@ -44,12 +47,19 @@ struct Control {
   int64_t n_m2l;
   int64_t n_p2p;
   int64_t own_m2l_total, own_p2p_total;  // walk: entries found at the target's own level
+  // (summed on the host from per-shard counts, so that the groups' additions
+  // spread over many addresses)
   int64_t n_trm, n_trp;                   // walk: transposed M2L and P2P entries
   int64_t n_p2p_tasks, n_p2p_part;        // near-field tasks and partial-sum slots
   int64_t n_tail_tasks;                   // transposed-tail M2L tasks
   int32_t pool_overflow;                  // a sharded pool ran out of room
   int32_t max_leaf_count;
   int64_t pool_used[N_POOLS][POOL_SHARDS];  // per pool and shard: entries handed out
+  int64_t own_used[2][POOL_SHARDS];          // per shard: own M2L / P2P entries found
+  // launch orders (work octaves, heaviest first) of the near-field tasks and
+  // of the sibling M2L groups: per-octave counts and placement cursors
+  int32_t task_oct[ORDER_OCT], task_cur[ORDER_OCT];
+  int32_t group_oct[ORDER_OCT], group_cur[ORDER_OCT];
 };
 // Grow-only device buffer.
 struct DBuf {
@@ -92,9 +102,9 @@ struct fmm_plan_s {
   mbg::DBuf m2l_off, m2l_src, p2p_off, p2p_src;
   bool m2l_lists_ready = false;  // per-target M2L lists materialized (on request only)
   // near-field tasks (target leaf x bounded slice of its list)
-  mbg::DBuf p2p_task, p2p_task_tmp, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
+  mbg::DBuf p2p_task, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
   // non-leaf nodes in id order; the parents of level l are parents[pbeg[l] .. pbeg[l+1])
-  mbg::DBuf parents, m2l_order, ord_key, ord_key_alt, ord_val, ord_val_alt;
+  mbg::DBuf parents, m2l_order;
   int64_t n_parents = 0, n_union = 0;
   int64_t pbeg[mbg::MAX_LEVELS + 2] = {0};
   // transposed-tail M2L tasks: per-leaf task offsets, tasks, partial locals
@@ -149,6 +159,11 @@ size_t scan_tmp_bytes(int64_t n);
 
 // Exclusive scan of int64 (in may alias out).  If total != nullptr the grand
 // total is written there.
+// r (1 to 3) int64 arrays of length n scanned together: exclusive scan of
+// in[i] into out[i] (in place allowed), the total at out[i][n] and, if dst and
+// dst[i] are given, at dst[i]; tmp: scan_tmp_bytes(n) * r bytes
+hipError_t scan_exclusive_multi_i64(int r, const int64_t* const* in, int64_t* const* out,
+                                    int64_t* const* dst, int64_t n, void* tmp, hipStream_t st);
 hipError_t scan_exclusive_i64(const int64_t* in, int64_t* out, int64_t n, int64_t* total,
                               void* tmp, hipStream_t st);
 hipError_t scan_exclusive_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total,
@@ -209,11 +224,10 @@ struct WalkArgs {
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
 // after the walk, every parent at once: the transposed keys (a.pbeg = 0, a.pcnt = all)
 hipError_t launch_tr_emit(const WalkArgs& a, hipStream_t st);
-hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, hipStream_t st);
+hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, hipStream_t st);
 hipError_t launch_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
                             const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st);
-hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
-                                  Control* ctrl, hipStream_t st);
+
 hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
                           int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st);
 hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_t* tr_cnt,
@@ -227,12 +241,8 @@ hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
                                 const int32_t* first_child, const uint8_t* n_child,
                                 const uint64_t* pool, const int64_t* uoff, const int32_t* ucnt,
                                 const int64_t* off, int32_t* src, hipStream_t st);
-hipError_t launch_walk_copy_totals(const int64_t* p2p_total, const int64_t* task_total,
-                                   const int64_t* part_total, const int64_t* tail_total,
-                                   Control* ctrl, hipStream_t st);
-// transposed totals (ends of the two scans) into the control block
-hipError_t launch_tr_totals(const int64_t* trm_total, const int64_t* trp_total, Control* ctrl,
-                            hipStream_t st);
+
+
 // LSD radix sort over the low `bits` bits; returns in *in_alt whether the
 // result ended in (keys_alt, idx_alt).
 // stable LSD sort of keys by bits [lo_bit, lo_bit + bits) (idx/idx_alt may be
@@ -289,18 +299,12 @@ hipError_t launch_m2l_sib(int dtype, int order, const M2LArgs& a, hipStream_t st
 // each leaf's partials, in task order, from a.local
 hipError_t launch_m2l_tails(int dtype, int order, const M2LArgs& a, bool combine,
                             hipStream_t st);
-// scratch of a one-pass (8-bit key) stable sort used to order launches
-struct OrderBufs {
-  uint64_t *key, *key_alt;
-  int32_t *val, *val_alt;
-  int32_t *hist, *scan_tmp;
-};
-// parents in launch order for the sibling blocks (longer unions first);
-// *order points into ob
+// launch order of the sibling M2L groups (parents with longer unions first),
+// written to order[0 .. np) (counts in ctrl->group_oct, cursors group_cur,
+// both zero at the start)
 hipError_t launch_m2l_order(const int32_t* parents, int64_t np, const int32_t* u_cnt,
-                            const OrderBufs& ob, int32_t** order, hipStream_t st);
-hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
-                             int64_t* cnt, hipStream_t st);
+                            Control* ctrl, int32_t* order, hipStream_t st);
+
 hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
                             const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks,
                             hipStream_t st);
@@ -321,13 +325,17 @@ hipError_t launch_l2l(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
 hipError_t launch_l2p(int dtype, int order, int64_t n, const void* pts, const int32_t* leaf_of,
                       const double* centre, const void* local, void* far, hipStream_t st);
 size_t p2p_task_bytes();
-hipError_t launch_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                                 const int32_t* count, int64_t* ntask, int64_t* npart,
-                                 hipStream_t st);
+// per leaf: near-field tasks, their partial-sum slots (0 for one task) and
+// transposed-tail M2L tasks (tr_cnt: the leaves' transposed M2L run lengths)
+hipError_t launch_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                                   const int32_t* count, const int32_t* tr_cnt, int64_t* ntask,
+                                   int64_t* npart, int64_t* ntail, Control* ctrl, hipStream_t st);
+// the tasks in launch order (heavier octaves of work first; ctrl->task_oct
+// counted by launch_leaf_task_counts, task_cur zero at the start)
 hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
                                 const int64_t* task_off, const int64_t* part_off,
-                                const int64_t* off, const int32_t* count, void* tasks,
-                                void* tmp, const OrderBufs& ob, hipStream_t st);
+                                const int64_t* off, const int32_t* count, Control* ctrl,
+                                void* tasks, hipStream_t st);
 hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                       const int32_t* begin, const int32_t* count, const int32_t* src,

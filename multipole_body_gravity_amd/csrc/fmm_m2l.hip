@@ -372,13 +372,6 @@ __global__ void k_m2l_tail_combine(int64_t n_leaves, int K, const int32_t* __res
   local[(int64_t)leaves[li] * K + n] -= s;
 }
 
-__global__ void k_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
-                             int64_t* cnt) {
-  const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (li >= n_leaves) return;
-  const int64_t len = tr_cnt[leaves[li]];
-  cnt[li] = (len + TAIL_E - 1) / TAIL_E;
-}
 
 __global__ void k_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
                             const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks) {
@@ -392,12 +385,6 @@ __global__ void k_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64
     tasks[q] = TailTask{e, (int32_t)min((int64_t)TAIL_E, e1 - e), (int32_t)li};
 }
 
-hipError_t launch_tail_count(const int32_t* leaves, int64_t n_leaves, const int32_t* tr_cnt,
-                             int64_t* cnt, hipStream_t st) {
-  if (n_leaves <= 0) return hipSuccess;
-  k_tail_count<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, tr_cnt, cnt);
-  return hipGetLastError();
-}
 
 hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
                             const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks,
@@ -412,26 +399,34 @@ hipError_t launch_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64
 // the longest waves do not start last; a stable sort keeps id order inside an
 // octave, so that blocks running together mostly share source records in L2.
 // Each parent's result does not depend on when it runs.
-__global__ void k_ord_keys(const int32_t* parents, int64_t np, const int32_t* u_cnt,
-                           uint64_t* key, int32_t* val) {
+// Launch order of the sibling M2L groups: longer unions first (octaves of the
+// union length), each block's groups of one octave together.
+__global__ void __launch_bounds__(256) k_group_octaves(const int32_t* parents, int64_t np,
+                                                       const int32_t* u_cnt, Control* ctrl) {
+  __shared__ int oct[ORDER_OCT];
+  for (int b = threadIdx.x; b < ORDER_OCT; b += blockDim.x) oct[b] = 0;
+  __syncthreads();
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= np) return;
-  const uint32_t u = (uint32_t)u_cnt[parents[i]];
-  key[i] = (uint64_t)(31 - (u ? 31 - __clz(u) : 0));  // descending octave
-  val[i] = parents[i];
+  if (i < np) atomicAdd(&oct[work_octave((uint64_t)(uint32_t)u_cnt[parents[i]])], 1);
+  __syncthreads();
+  for (int b = threadIdx.x; b < ORDER_OCT; b += blockDim.x)
+    if (oct[b]) atomicAdd(&ctrl->group_oct[b], oct[b]);
+}
+__global__ void __launch_bounds__(256) k_group_place(const int32_t* parents, int64_t np,
+                                                     const int32_t* u_cnt, Control* ctrl,
+                                                     int32_t* order) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int o = i < np ? work_octave((uint64_t)(uint32_t)u_cnt[parents[i]]) : -1;
+  const int64_t slot = octave_slot<ORDER_OCT>(o, ctrl->group_oct, ctrl->group_cur);
+  if (i < np && slot >= 0 && slot < np) order[slot] = parents[i];
 }
 
 hipError_t launch_m2l_order(const int32_t* parents, int64_t np, const int32_t* u_cnt,
-                            const OrderBufs& ob, int32_t** order, hipStream_t st) {
-  *order = nullptr;
+                            Control* ctrl, int32_t* order, hipStream_t st) {
   if (np <= 0) return hipSuccess;
   const unsigned g = (unsigned)((np + 255) / 256);
-  k_ord_keys<<<g, 256, 0, st>>>(parents, np, u_cnt, ob.key, ob.val);
-  bool alt = false;
-  hipError_t e = launch_radix_sort_bits(ob.key, ob.val, ob.key_alt, ob.val_alt, np, 0, 8, ob.hist,
-                                        ob.scan_tmp, &alt, st);
-  *order = alt ? ob.val_alt : ob.val;
-  if (e != hipSuccess) return e;
+  k_group_octaves<<<g, 256, 0, st>>>(parents, np, u_cnt, ctrl);
+  k_group_place<<<g, 256, 0, st>>>(parents, np, u_cnt, ctrl, order);
   return hipGetLastError();
 }
 

@@ -44,61 +44,67 @@ __device__ __forceinline__ double p2p_rsqrt(double x) {
 __device__ __forceinline__ float p2p_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // ---- task construction (build time) ----
-__global__ void k_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                                 const int32_t* count, int64_t* ntask, int64_t* npart) {
+__global__ void k_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                                   const int32_t* count, const int32_t* tr_cnt, int64_t* ntask,
+                                   int64_t* npart, int64_t* ntail, Control* ctrl) {
+  __shared__ int oct[ORDER_OCT];
+  for (int b = threadIdx.x; b < ORDER_OCT; b += blockDim.x) oct[b] = 0;
+  __syncthreads();
   int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (li >= n_leaves) return;
-  const int32_t a = leaves[li];
-  const int64_t len = off[a + 1] - off[a];
-  const int64_t nt = len <= TASK_E ? 1 : (len + TASK_E - 1) / TASK_E;
-  ntask[li] = nt;
-  npart[li] = nt > 1 ? nt * (int64_t)count[a] : 0;
+  if (li < n_leaves) {
+    const int32_t a = leaves[li];
+    const int64_t len = off[a + 1] - off[a];
+    const int64_t nt = len <= TASK_E ? 1 : (len + TASK_E - 1) / TASK_E;
+    ntask[li] = nt;
+    npart[li] = nt > 1 ? nt * (int64_t)count[a] : 0;
+    ntail[li] = ((int64_t)tr_cnt[a] + TAIL_E - 1) / TAIL_E;
+    // launch-order octaves of the leaf's tasks: nt - 1 full ones and the last
+    const uint64_t c = (uint64_t)count[a];
+    if (nt > 1) atomicAdd(&oct[work_octave(c * TASK_E)], (int)(nt - 1));
+    atomicAdd(&oct[work_octave(c * (uint64_t)(len - (nt - 1) * TASK_E))], 1);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < ORDER_OCT; b += blockDim.x)
+    if (oct[b]) atomicAdd(&ctrl->task_oct[b], oct[b]);
 }
 
 // One thread per task: find its leaf by binary search over the task offsets.
-__global__ void k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
-                                const int64_t* task_off, const int64_t* part_off,
-                                const int64_t* off, const int32_t* count, P2PTask* tasks) {
-  int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (k >= n_tasks) return;
-  int64_t lo = 0, hi = n_leaves;  // last li with task_off[li] <= k
-  while (hi - lo > 1) {
-    int64_t mid = (lo + hi) >> 1;
-    if (task_off[mid] <= k)
-      lo = mid;
-    else
-      hi = mid;
+// Task k (leaf order) is built and placed in launch order: heavier octaves of
+// work (targets x source leaves) first, so the longest waves do not start
+// last; a block's tasks of one octave stay together, so that tasks running
+// together mostly share their sources in L2.  Every task's sums (and its
+// partial slots) are independent of where and when it runs.
+__global__ void __launch_bounds__(256)
+    k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
+                    const int64_t* task_off, const int64_t* part_off, const int64_t* off,
+                    const int32_t* count, Control* ctrl, P2PTask* tasks) {
+  const int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  P2PTask t{};
+  int o = -1;
+  if (k < n_tasks) {
+    int64_t lo = 0, hi = n_leaves;  // last li with task_off[li] <= k
+    while (hi - lo > 1) {
+      int64_t mid = (lo + hi) >> 1;
+      if (task_off[mid] <= k)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int64_t li = lo;
+    const int32_t a = leaves[li];
+    const int64_t nt = task_off[li + 1] - task_off[li];
+    const int64_t kk = k - task_off[li];
+    t.e0 = off[a] + kk * TASK_E;
+    t.e1 = min(off[a + 1], t.e0 + TASK_E);
+    t.part = nt > 1 ? part_off[li] + kk * (int64_t)count[a] : -1;
+    t.leaf = a;
+    t.pad = 0;
+    o = work_octave((uint64_t)count[a] * (uint64_t)(t.e1 - t.e0));
   }
-  const int64_t li = lo;
-  const int32_t a = leaves[li];
-  const int64_t nt = task_off[li + 1] - task_off[li];
-  const int64_t kk = k - task_off[li];
-  P2PTask t;
-  t.e0 = off[a] + kk * TASK_E;
-  t.e1 = min(off[a + 1], t.e0 + TASK_E);
-  t.part = nt > 1 ? part_off[li] + kk * (int64_t)count[a] : -1;
-  t.leaf = a;
-  t.pad = 0;
-  tasks[k] = t;
+  const int64_t slot = octave_slot<ORDER_OCT>(o, ctrl->task_oct, ctrl->task_cur);
+  if (k < n_tasks && slot >= 0 && slot < n_tasks) tasks[slot] = t;
 }
 
-// Launch order of the tasks: heavier octaves of work (targets x source leaves)
-// first, so the longest waves do not start last; a stable sort keeps leaf order
-// inside an octave, so that tasks running together mostly share their sources
-// in L2.  Every task's sums are independent of when it runs.
-__global__ void k_task_keys(const P2PTask* tasks, int64_t n, const int32_t* count, uint64_t* key,
-                            int32_t* val) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const P2PTask t = tasks[i];
-  const uint64_t w = (uint64_t)count[t.leaf] * (uint64_t)(t.e1 - t.e0);
-  key[i] = (uint64_t)(63 - (w ? 63 - __clzll(w) : 0));  // descending octave
-  val[i] = (int32_t)i;
-}
-__global__ void k_task_gather(const P2PTask* in, const int32_t* idx, int64_t n, P2PTask* out) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i < n) out[i] = in[idx[i]];
-}
 
 // ---- near-field sums ----
 constexpr int TILE = 2 * WAVE;       // source particles staged per round
@@ -329,30 +335,23 @@ __global__ void __launch_bounds__(CB_THREADS)
 
 size_t p2p_task_bytes() { return sizeof(P2PTask); }
 
-hipError_t launch_p2p_task_count(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
-                                 const int32_t* count, int64_t* ntask, int64_t* npart,
-                                 hipStream_t st) {
+hipError_t launch_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
+                                   const int32_t* count, const int32_t* tr_cnt, int64_t* ntask,
+                                   int64_t* npart, int64_t* ntail, Control* ctrl, hipStream_t st) {
   if (n_leaves == 0) return hipSuccess;
-  k_p2p_task_count<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(leaves, n_leaves, off,
-                                                                        count, ntask, npart);
+  k_leaf_task_counts<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(
+      leaves, n_leaves, off, count, tr_cnt, ntask, npart, ntail, ctrl);
   return hipGetLastError();
 }
 
 hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
                                 const int64_t* task_off, const int64_t* part_off,
-                                const int64_t* off, const int32_t* count, void* tasks,
-                                void* tmp, const OrderBufs& ob, hipStream_t st) {
+                                const int64_t* off, const int32_t* count, Control* ctrl,
+                                void* tasks, hipStream_t st) {
   if (n_tasks == 0) return hipSuccess;
   const unsigned g = (unsigned)((n_tasks + 255) / 256);
   k_p2p_task_fill<<<g, 256, 0, st>>>(leaves, n_leaves, n_tasks, task_off, part_off, off, count,
-                                     (P2PTask*)tmp);
-  k_task_keys<<<g, 256, 0, st>>>((const P2PTask*)tmp, n_tasks, count, ob.key, ob.val);
-  bool alt = false;
-  hipError_t e = launch_radix_sort_bits(ob.key, ob.val, ob.key_alt, ob.val_alt, n_tasks, 0, 8,
-                                        ob.hist, ob.scan_tmp, &alt, st);
-  if (e != hipSuccess) return e;
-  k_task_gather<<<g, 256, 0, st>>>((const P2PTask*)tmp, alt ? ob.val_alt : ob.val, n_tasks,
-                                   (P2PTask*)tasks);
+                                     ctrl, (P2PTask*)tasks);
   return hipGetLastError();
 }
 

@@ -269,7 +269,15 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
       cp[k] = wave_sum(cp[k]);
     }
     const int64_t tm = wave_sum((int64_t)ntm), tp = wave_sum((int64_t)ntp);
+    int64_t om = 0, op = 0;  // the group's own entries, for the list totals
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      om += (int64_t)(cm[k] & 0xffffffffu) + (int64_t)(cm[k] >> 32);
+      op += (int64_t)(cp[k] & 0xffffffffu) + (int64_t)(cp[k] >> 32);
+    }
     if (lane == 0) {
+      if (om) atomicAdd((unsigned long long*)&a.ctrl->own_used[0][sh], (unsigned long long)om);
+      if (op) atomicAdd((unsigned long long*)&a.ctrl->own_used[1][sh], (unsigned long long)op);
       a.cu_off[X] = o[0];
       a.cu_cnt[X] = (int32_t)kCU;
       a.u_off[X] = o[1];
@@ -332,50 +340,27 @@ __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a) {
   }
 }
 
-__global__ void k_tr_totals(const int64_t* trm_total, const int64_t* trp_total, Control* c) {
-  if (threadIdx.x == 0) {
-    c->n_trm = *trm_total;
-    c->n_trp = *trp_total;
-  }
-}
 
-// Walk set-up: pools empty, no overflow, the root's generator.
-__global__ void k_walk_reset(Control* c, uint64_t* rootgen) {
+// Walk set-up: pools empty, no overflow, the root's generator; the own-entry
+// totals start with the root's (itself as its only P2P entry when it is a leaf).
+__global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf) {
   for (int i = threadIdx.x; i < N_POOLS * POOL_SHARDS; i += blockDim.x)
     (&c->pool_used[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 2 * POOL_SHARDS; i += blockDim.x) (&c->own_used[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < ORDER_OCT; i += blockDim.x) {
+    c->task_oct[i] = c->task_cur[i] = 0;
+    c->group_oct[i] = c->group_cur[i] = 0;
+  }
   if (threadIdx.x == 0) {
     c->pool_overflow = 0;
     c->own_m2l_total = 0;
-    c->own_p2p_total = 0;
+    c->own_p2p_total = root_leaf;
     rootgen[0] = (0ull << 8) | 1ull;  // node 0, slot 0
   }
 }
 
 // Sum of the own counts (list sizes are known before the transposed sort);
 // block partial sums are added with integer atomics (order-independent).
-__global__ void k_walk_own_totals(int64_t n, const int32_t* om, const int32_t* op, Control* c) {
-  __shared__ int64_t sm[WK_THREADS], sp[WK_THREADS];
-  int64_t a = 0, b = 0;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    a += om[i];
-    b += op[i];
-  }
-  sm[threadIdx.x] = a;
-  sp[threadIdx.x] = b;
-  __syncthreads();
-  for (int s = WK_THREADS / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      sm[threadIdx.x] += sm[threadIdx.x + s];
-      sp[threadIdx.x] += sp[threadIdx.x + s];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    atomicAdd((unsigned long long*)&c->own_m2l_total, (unsigned long long)sm[0]);
-    atomicAdd((unsigned long long*)&c->own_p2p_total, (unsigned long long)sp[0]);
-  }
-}
 
 // Runs of equal (kind, target) in the sorted keys: first index and end index.
 __global__ void k_tr_runs(const uint64_t* keys, int64_t n, int sh, int kind_bit, int64_t n_nodes,
@@ -403,16 +388,6 @@ __global__ void k_walk_offsets(int64_t n, const int32_t* own, const int32_t* tr_
   tot[i] = (int64_t)own[i] + tr_cnt[i];
 }
 
-__global__ void k_walk_copy_totals(const int64_t* p2p_total, const int64_t* task_total,
-                                   const int64_t* part_total, const int64_t* tail_total,
-                                   Control* c) {
-  if (threadIdx.x == 0) {
-    c->n_p2p = *p2p_total;
-    c->n_p2p_tasks = *task_total;
-    c->n_p2p_part = *part_total;
-    c->n_tail_tasks = *tail_total;
-  }
-}
 
 // Sorted transposed keys of one kind -> after each target's own entries.
 __global__ void k_tr_scatter(const uint64_t* keys, int64_t n, int sh, int kind_bit, int kind,
@@ -477,16 +452,8 @@ hipError_t launch_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, hipStream_t st) {
-  k_walk_reset<<<1, 256, 0, st>>>(ctrl, rootgen);
-  return hipGetLastError();
-}
-hipError_t launch_walk_own_totals(int64_t n_nodes, const int32_t* own_m2l, const int32_t* own_p2p,
-                                  Control* ctrl, hipStream_t st) {
-  int64_t blocks = (n_nodes + WK_THREADS - 1) / WK_THREADS;
-  if (blocks > 1024) blocks = 1024;
-  if (blocks < 1) blocks = 1;
-  k_walk_own_totals<<<(unsigned)blocks, WK_THREADS, 0, st>>>(n_nodes, own_m2l, own_p2p, ctrl);
+hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, hipStream_t st) {
+  k_walk_reset<<<1, 256, 0, st>>>(ctrl, rootgen, root_leaf);
   return hipGetLastError();
 }
 hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
@@ -501,12 +468,6 @@ hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_
                                int64_t* tot, hipStream_t st) {
   if (n_nodes <= 0) return hipSuccess;
   k_walk_offsets<<<(unsigned)((n_nodes + 255) / 256), 256, 0, st>>>(n_nodes, own, tr_cnt, tot);
-  return hipGetLastError();
-}
-hipError_t launch_walk_copy_totals(const int64_t* p2p_total, const int64_t* task_total,
-                                   const int64_t* part_total, const int64_t* tail_total,
-                                   Control* ctrl, hipStream_t st) {
-  k_walk_copy_totals<<<1, 64, 0, st>>>(p2p_total, task_total, part_total, tail_total, ctrl);
   return hipGetLastError();
 }
 hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
@@ -540,11 +501,6 @@ hipError_t launch_tr_emit(const WalkArgs& a, hipStream_t st) {
   int64_t blocks = (a.pcnt + WK_WAVES - 1) / WK_WAVES;
   if (blocks > 16384) blocks = 16384;
   k_tr_emit<<<(unsigned)blocks, WK_THREADS, 0, st>>>(a);
-  return hipGetLastError();
-}
-hipError_t launch_tr_totals(const int64_t* trm_total, const int64_t* trp_total, Control* ctrl,
-                            hipStream_t st) {
-  k_tr_totals<<<1, 64, 0, st>>>(trm_total, trp_total, ctrl);
   return hipGetLastError();
 }
 
