@@ -259,8 +259,8 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     Pool<uint64_t>* pools[N_POOLS] = {&a.cu, &a.u, &a.pu};
     for (int k = 0; k < N_POOLS; k++)
       *pools[k] = Pool<uint64_t>{P<uint64_t>(p->pool[k]), p->shard_cap[k], dctrl->pool_used[k]};
-    TRY_HIP(launch_walk_reset(dctrl, P<uint64_t>(p->rootgen), root_leaf, st));
-    TRY_HIP(launch_walk_root(1, root_leaf, a.own_m2l, a.own_p2p, nullptr, nullptr, st));
+    TRY_HIP(launch_walk_reset(dctrl, P<uint64_t>(p->rootgen), root_leaf, a.own_m2l, a.own_p2p,
+                              st));
     for (int l = 0; l < depth; l++) {
       a.pbeg = p->pbeg[l];
       a.pcnt = p->pbeg[l + 1] - p->pbeg[l];
@@ -307,8 +307,8 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   // target), then stably sorted on (kind, target); run lengths per target
   int32_t* tr_cnt = P<int32_t>(p->tr_cnt_m2l);
   int64_t* tr_start = P<int64_t>(p->tr_start_m2l);
-  TRY_HIP(launch_fill_zero(tr_cnt, (size_t)2 * nn * 4, st));
   const uint64_t* sorted = nullptr;
+  if (ntr == 0) TRY_HIP(launch_fill_zero(tr_cnt, (size_t)2 * nn * 4, st));
   if (ntr > 0) {
     TRY(grow(p->tr_keys, (size_t)ntr * 8));
     TRY(grow(p->tr_keys_alt, (size_t)ntr * 8));
@@ -318,7 +318,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     a.n_trm = &dctrl->n_trm;
     a.pbeg = 0;
     a.pcnt = np;
-    TRY_HIP(launch_tr_emit(a, st));
+    TRY_HIP(launch_tr_emit(a, tr_cnt, 2 * nn, st));  // also clears tr_cnt
     bool in_alt = false;
     TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), nullptr, P<uint64_t>(p->tr_keys_alt),
                                    nullptr, ntr, a.key_shift, a.key_shift + 1,
@@ -345,7 +345,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   int32_t* p2p_src = P<int32_t>(p->p2p_src);
   TRY_HIP(launch_union_scatter(a.parents, np, a.first_child, a.n_child, a.pu.data, a.pu_off,
                                a.pu_cnt, p2p_off, p2p_src, st));
-  TRY_HIP(launch_walk_root(2, root_leaf, a.own_m2l, a.own_p2p, p2p_off, p2p_src, st));
+  if (root_leaf) TRY_HIP(launch_walk_root_leaf(p2p_off, p2p_src, st));
   if (ntr > 0)
     TRY_HIP(launch_tr_scatter(sorted, ntr, a.key_shift, kind_bit, 1, nn, p2p_off, a.own_p2p,
                               tr_start + nn, p2p_src, st));

@@ -222,11 +222,12 @@ struct WalkArgs {
 };
 // one step: the children of the parents of one level, counted and written
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
-// after the walk, every parent at once: the transposed keys (a.pbeg = 0, a.pcnt = all)
-hipError_t launch_tr_emit(const WalkArgs& a, hipStream_t st);
-hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, hipStream_t st);
-hipError_t launch_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
-                            const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st);
+// after the walk, every parent at once: the transposed keys (a.pbeg = 0,
+// a.pcnt = all); also clears run_cnt[0 .. run_n) for the run step
+hipError_t launch_tr_emit(const WalkArgs& a, int32_t* run_cnt, int64_t run_n, hipStream_t st);
+hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, int32_t* own_m2l,
+                             int32_t* own_p2p, hipStream_t st);
+hipError_t launch_walk_root_leaf(const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st);
 
 hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
                           int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st);

@@ -306,7 +306,12 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
 // tested again against X's children; (c <- child) keys go to the group's slot of
 // the M2L part (accepted) or the P2P part (leaf-leaf rejected), candidate by
 // candidate, children in order.
-__global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a) {
+__global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a, int32_t* run_cnt,
+                                                         int64_t run_n) {
+  // the run lengths of the next step start at zero (targets without a run)
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < run_n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    run_cnt[i] = 0;
   const uint64_t lt = lanemask_lt();
   const int lane = __lane_id();
   const int64_t ntm_all = *a.n_trm;
@@ -343,7 +348,8 @@ __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a) {
 
 // Walk set-up: pools empty, no overflow, the root's generator; the own-entry
 // totals start with the root's (itself as its only P2P entry when it is a leaf).
-__global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf) {
+__global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf, int32_t* own_m2l,
+                             int32_t* own_p2p) {
   for (int i = threadIdx.x; i < N_POOLS * POOL_SHARDS; i += blockDim.x)
     (&c->pool_used[0][0])[i] = 0;
   for (int i = threadIdx.x; i < 2 * POOL_SHARDS; i += blockDim.x) (&c->own_used[0][0])[i] = 0;
@@ -352,6 +358,8 @@ __global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf) {
     c->group_oct[i] = c->group_cur[i] = 0;
   }
   if (threadIdx.x == 0) {
+    own_m2l[0] = 0;  // the root is nobody's child: its own counts are set here
+    own_p2p[0] = root_leaf;
     c->pool_overflow = 0;
     c->own_m2l_total = 0;
     c->own_p2p_total = root_leaf;
@@ -436,24 +444,18 @@ __global__ void __launch_bounds__(WK_THREADS)
 
 // The root is nobody's child: its own counts are set here.  A leaf root has the
 // single list entry P2P(root <- root).
-__global__ void k_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
-                            const int64_t* p2p_off, int32_t* p2p_src) {
-  if (threadIdx.x != 0) return;
-  if (pass == 1) {
-    own_m2l[0] = 0;
-    own_p2p[0] = root_leaf;
-  } else if (root_leaf) {
-    p2p_src[p2p_off[0]] = 0;
-  }
+// A root that is a leaf: its only P2P entry is itself.
+__global__ void k_walk_root_leaf(const int64_t* p2p_off, int32_t* p2p_src) {
+  if (threadIdx.x == 0) p2p_src[p2p_off[0]] = 0;
 }
-hipError_t launch_walk_root(int pass, int root_leaf, int32_t* own_m2l, int32_t* own_p2p,
-                            const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st) {
-  k_walk_root<<<1, 64, 0, st>>>(pass, root_leaf, own_m2l, own_p2p, p2p_off, p2p_src);
+hipError_t launch_walk_root_leaf(const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st) {
+  k_walk_root_leaf<<<1, 64, 0, st>>>(p2p_off, p2p_src);
   return hipGetLastError();
 }
 
-hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, hipStream_t st) {
-  k_walk_reset<<<1, 256, 0, st>>>(ctrl, rootgen, root_leaf);
+hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, int32_t* own_m2l,
+                             int32_t* own_p2p, hipStream_t st) {
+  k_walk_reset<<<1, 256, 0, st>>>(ctrl, rootgen, root_leaf, own_m2l, own_p2p);
   return hipGetLastError();
 }
 hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
@@ -496,11 +498,10 @@ hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {
   k_walk<<<(unsigned)blocks, WK_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
-hipError_t launch_tr_emit(const WalkArgs& a, hipStream_t st) {
-  if (a.pcnt <= 0) return hipSuccess;
-  int64_t blocks = (a.pcnt + WK_WAVES - 1) / WK_WAVES;
+hipError_t launch_tr_emit(const WalkArgs& a, int32_t* run_cnt, int64_t run_n, hipStream_t st) {
+  int64_t blocks = (std::max<int64_t>(a.pcnt, 1) + WK_WAVES - 1) / WK_WAVES;
   if (blocks > 16384) blocks = 16384;
-  k_tr_emit<<<(unsigned)blocks, WK_THREADS, 0, st>>>(a);
+  k_tr_emit<<<(unsigned)blocks, WK_THREADS, 0, st>>>(a, run_cnt, run_n);
   return hipGetLastError();
 }
 
