@@ -266,13 +266,15 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
       a.pcnt = p->pbeg[l + 1] - p->pbeg[l];
       TRY_HIP(launch_walk(a, st));
     }
-    if (p->walk_retries == 0) TRY(issue_upward(p));
     {  // offsets of every group's transposed keys, in group order; totals to the control block
       const int64_t* in[2] = {a.trm_cnt, a.trp_cnt};
       int64_t* out[2] = {P<int64_t>(p->trm_base), P<int64_t>(p->trp_base)};
       int64_t* dst[2] = {&dctrl->n_trm, &dctrl->n_trp};
       TRY_HIP(scan_exclusive_multi_i64(2, in, out, dst, np, p->scan_tmp.p, st));
     }
+    // the upward pass, once this attempt's walk launches are all queued (its
+    // host launch time then overlaps the walk instead of delaying it)
+    if (p->walk_retries == 0) TRY(issue_upward(p));
     TRY(sync_ctrl(p, st));
     if (!p->ctrl_host->pool_overflow) break;
     // the levels after the first overflow did not run: grow at least twofold
