@@ -559,8 +559,8 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   TRY_HIP(launch_tree_phase1(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
                              P<int8_t>(p->wlev), P<int8_t>(p->wtmp), P<int8_t>(p->leaf_level),
                              P<int64_t>(p->lvl_blkcnt), p->scan_tmp.p, ctrl, st));
-  TRY_HIP(hipMemcpyAsync(&p->root_host, root, sizeof(RootInfo), hipMemcpyDeviceToHost, st));
   TRY(sync_ctrl(p, st));
+  p->root_host = p->ctrl_host->root;
   collect_pending(p);  // the previous step's events have completed
   for (int k = 0; k < FMM_N_KERNELS; k++) p->kran[k] = false;
   if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;

@@ -306,7 +306,8 @@ __global__ void __launch_bounds__(BB_THREADS)
   }
 }
 
-__global__ void __launch_bounds__(BB_THREADS) k_bbox_final(const double* part, int nblk, RootInfo* root) {
+__global__ void __launch_bounds__(BB_THREADS) k_bbox_final(const double* part, int nblk, RootInfo* root,
+                                                          Control* ctrl) {
   __shared__ double s[6][BB_THREADS];
   double l6[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
   for (int b = threadIdx.x; b < nblk; b += BB_THREADS)
@@ -336,9 +337,12 @@ __global__ void __launch_bounds__(BB_THREADS) k_bbox_final(const double* part, i
   }
   int e2;
   frexp(side, &e2);
-  for (int a = 0; a < 3; a++) root->lo[a] = isfinite(lo[a]) ? lo[a] : 0.0;
-  root->side = side;
-  root->scale = ldexp(1.0, KEY_BITS - (e2 - 1));
+  RootInfo r;
+  for (int a = 0; a < 3; a++) r.lo[a] = isfinite(lo[a]) ? lo[a] : 0.0;
+  r.side = side;
+  r.scale = ldexp(1.0, KEY_BITS - (e2 - 1));
+  *root = r;
+  ctrl->root = r;  // the host's copy comes with the control block
 }
 
 hipError_t launch_bbox(const void* pos, const void* mass, int64_t n, int dtype, double* part,
@@ -349,7 +353,7 @@ hipError_t launch_bbox(const void* pos, const void* mass, int64_t n, int dtype, 
   else
     k_bbox_partial<float><<<nblk, BB_THREADS, 0, st>>>((const float*)pos, (const float*)mass, n,
                                                        part, ctrl);
-  k_bbox_final<<<1, BB_THREADS, 0, st>>>(part, nblk, root);
+  k_bbox_final<<<1, BB_THREADS, 0, st>>>(part, nblk, root, ctrl);
   return hipGetLastError();
 }
 

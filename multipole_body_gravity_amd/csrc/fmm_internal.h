@@ -38,6 +38,7 @@ constexpr int ORDER_OCT = 64;
 constexpr int POOL_SHARDS = 512;
 enum { POOL_CU = 0, POOL_U = 1, POOL_PU = 2, N_POOLS = 3 };
 struct Control {
+  RootInfo root;  // the root cell, for the host
   int32_t nonfinite;
   int32_t pad0;
   int64_t n_nodes;
