@@ -6,6 +6,7 @@ N = 10^6 particles, 64-Plummer clustered set (seed 1005), fp64, order 4,
 theta 0.7, leaf 32, inputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --sweep [--sweep-n N] [--sweep-orders 2,4,6,8] [--sweep-thetas ...]
 """
 from __future__ import annotations
 
@@ -135,6 +136,62 @@ def cpu_baseline(pos, mass, cfg):
             "sample": f"the full workload ({cfg['n']} particles, one oracle build+eval, {dt:.1f} s)"}
 
 
+def sweep(args):
+    """Accuracy-runtime sweep over order and opening angle on a Hernquist sphere
+    (the jz-fmm page's accuracy-runtime comparison, replayed on one GPU): per
+    (p, theta) the build+eval time and the acceleration and potential errors
+    against direct summation (fmm_direct) at seeded sample particles.  One JSON
+    line per configuration."""
+    import torch
+
+    from multipole_body_gravity_amd import Plan, direct, workloads
+    dev = torch.device("cuda:0")
+    n = args.sweep_n
+    pos, mass = workloads.make("hernquist", n, 1007)
+    tpos = torch.from_numpy(pos).to(dev)
+    tmass = torch.from_numpy(mass).to(dev)
+    del pos, mass
+    smp = np.random.default_rng(77).choice(n, min(args.sweep_targets, n), replace=False)
+    tsmp = torch.from_numpy(smp).to(dev)
+    rphi, racc = direct(tpos, tmass, tsmp)
+    rphi, racc = rphi.cpu().numpy(), racc.cpu().numpy()
+
+    def rel(got, ref):
+        nref = np.linalg.norm(ref, axis=-1) if ref.ndim == 2 else np.abs(ref)
+        d = np.linalg.norm(got - ref, axis=-1) if ref.ndim == 2 else np.abs(got - ref)
+        return d / nref
+
+    for order in [int(x) for x in args.sweep_orders.split(",")]:
+        for theta in [float(x) for x in args.sweep_thetas.split(",")]:
+            plan = Plan(n, order=order, theta=theta, leaf_size=32, dtype=torch.float64, device=dev)
+            phi = torch.empty(n, dtype=torch.float64, device=dev)
+            acc = torch.empty(n, 3, dtype=torch.float64, device=dev)
+            plan.build(tpos, tmass)
+            plan.eval(phi, acc)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                plan.build(tpos, tmass)
+                plan.eval(phi, acc)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / args.steps
+            st = plan.stats()
+            ea = rel(acc[tsmp].cpu().numpy(), racc)
+            ep = rel(phi[tsmp].cpu().numpy(), rphi)
+            print(json.dumps({"sweep": "hernquist", "n": n, "order": order, "theta": theta,
+                              "leaf_size": 32, "dtype": "f64", "steps": args.steps,
+                              "ms_per_step": round(dt * 1e3, 3),
+                              "value": round(n / dt, 1), "unit": "particles/s",
+                              "acc_rel_err_p99": float(np.percentile(ea, 99)),
+                              "acc_rel_err_max": float(ea.max()),
+                              "phi_rel_err_p99": float(np.percentile(ep, 99)),
+                              "targets": int(smp.size), "n_nodes": st["n_nodes"],
+                              "n_m2l": st["n_m2l"], "n_p2p": st["n_p2p"]}), flush=True)
+            plan.close()
+            del phi, acc
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +201,12 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="accuracy-runtime sweep on a Hernquist sphere instead of the headline line")
+    ap.add_argument("--sweep-n", type=int, default=40_000_000)
+    ap.add_argument("--sweep-orders", default="2,4,6,8")
+    ap.add_argument("--sweep-thetas", default="0.4,0.5,0.6,0.7")
+    ap.add_argument("--sweep-targets", type=int, default=2048)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
@@ -152,6 +215,11 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.sweep:
+        if args.steps == ap.get_default("steps"):
+            args.steps = 3
+        sweep(args)
         return
 
     import torch

@@ -168,6 +168,21 @@ int fmm_copy_lists(fmm_plan_t plan, int64_t* m2l_off, int32_t* m2l_src, int64_t*
  * contribution translated in).  NULL skips one. */
 int fmm_copy_expansions(fmm_plan_t plan, double* mpole, double* local);
 
+/* ---- reference ---- */
+
+/* Direct summation at chosen targets (jz-fmm page, "From particle pairs to node
+ * pairs": the direct sum with the self term omitted), for accuracy
+ * measurements: for t < n_targets, phi[t] and acc[3t..3t+2] of particle
+ * targets[t] (caller indices in [0, n)) from all n particles.  pos [n][3],
+ * mass [n], phi [n_targets] and acc [n_targets][3] are device arrays in the
+ * dtype; targets [n_targets] is a device int64 array.  Sums run in fp64 in a
+ * fixed order (bitwise reproducible).  Independent of any plan; allocates a
+ * temporary workspace of 2 KiB per target and synchronizes `stream`.  Returns
+ * FMM_ERR_ARG for null pointers, n < 1, n_targets < 0 or a bad dtype; a
+ * target index outside [0, n) gets NaN results. */
+int fmm_direct(const void* pos, const void* mass, int64_t n, const int64_t* targets,
+               int64_t n_targets, int dtype, void* phi, void* acc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

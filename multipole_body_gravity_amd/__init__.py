@@ -7,11 +7,11 @@ lazily so that input generation works without the GPU library.
 """
 from __future__ import annotations
 
-__all__ = ["Plan", "FmmError", "workloads"]
+__all__ = ["Plan", "FmmError", "direct", "workloads"]
 
 
 def __getattr__(name):
-    if name in ("Plan", "FmmError"):
+    if name in ("Plan", "FmmError", "direct"):
         from . import fmm
         return getattr(fmm, name)
     raise AttributeError(name)

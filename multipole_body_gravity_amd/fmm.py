@@ -64,6 +64,7 @@ def load_library():
     lib.fmm_copy_tree.argtypes = [P] * 8
     lib.fmm_copy_lists.argtypes = [P] * 5
     lib.fmm_copy_expansions.argtypes = [P, P, P]
+    lib.fmm_direct.argtypes = [P, P, i64, P, i64, i32, P, P, P]
     _lib = lib
     return lib
 
@@ -193,3 +194,28 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def direct(pos: torch.Tensor, mass: torch.Tensor, targets: torch.Tensor, stream=None):
+    """Direct-sum potential and acceleration of particles `targets` (int64 device
+    tensor of indices) from all particles (fp64 sums; fmm_direct)."""
+    if pos.dim() != 2 or pos.shape[1] != 3 or mass.shape != (pos.shape[0],):
+        raise FmmError(-1, "fmm_direct: pos must be [N,3] and mass [N]")
+    if pos.dtype not in (torch.float32, torch.float64) or mass.dtype != pos.dtype:
+        raise FmmError(-1, "fmm_direct: pos and mass of one float dtype")
+    if targets.dtype != torch.int64 or not (pos.is_cuda and mass.is_cuda and targets.is_cuda):
+        raise FmmError(-1, "fmm_direct: device tensors, int64 targets")
+    pos, mass, targets = pos.contiguous(), mass.contiguous(), targets.contiguous()
+    nt = targets.shape[0]
+    phi = torch.empty(nt, dtype=pos.dtype, device=pos.device)
+    acc = torch.empty(nt, 3, dtype=pos.dtype, device=pos.device)
+    lib = load_library()
+    with torch.cuda.device(pos.device):
+        rc = lib.fmm_direct(ctypes.c_void_p(pos.data_ptr()), ctypes.c_void_p(mass.data_ptr()),
+                            pos.shape[0], ctypes.c_void_p(targets.data_ptr()), nt,
+                            FMM_F64 if pos.dtype == torch.float64 else FMM_F32,
+                            ctypes.c_void_p(phi.data_ptr()), ctypes.c_void_p(acc.data_ptr()),
+                            _stream_handle(stream))
+    if rc:
+        raise FmmError(rc, "fmm_direct")
+    return phi, acc

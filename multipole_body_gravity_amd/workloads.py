@@ -14,18 +14,22 @@ Distributions:
   clustered  -- 64 Plummer spheres, centres uniform in the unit cube, scale
                 radii log-uniform in [0.002, 0.05], occupancies from a
                 multinomial draw with Dirichlet(1) weights, shuffled.
+  hernquist  -- Hernquist sphere (scale a = 1): radii from the inverse of the
+                cumulative mass profile M(<r)/M = r^2 / (r + a)^2, truncated
+                at 100 a (98 % of the mass), isotropic directions.
   lattice    -- 256^3 cell-centred lattice of the unit cube displaced by a
                 Gaussian random field with power spectrum P(k) ~ k^-2 per
                 component (rms displacement 0.3 lattice spacings), wrapped
                 periodically into [0, 1).
-The jz-fmm page measures a 40-million-particle Hernquist sphere and jaccpot a
-distribution it does not state; these sets stand in for them.
+The jz-fmm page measures a 40-million-particle Hernquist sphere (its
+accuracy-runtime figure) and jaccpot a distribution it does not state; the
+hernquist set replays the former's shape, the others stand in for the rest.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["uniform", "plummer", "clustered", "lattice", "CONFIGS", "make"]
+__all__ = ["uniform", "plummer", "clustered", "hernquist", "lattice", "CONFIGS", "make"]
 
 
 def uniform(n: int, seed: int) -> np.ndarray:
@@ -70,6 +74,15 @@ def clustered(n: int, seed: int, n_clusters: int = 64, a_min: float = 0.002,
     return pos[rng.permutation(n)]
 
 
+def hernquist(n: int, seed: int, a: float = 1.0, trunc: float = 100.0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    frac = (trunc / (1.0 + trunc)) ** 2  # mass fraction inside trunc*a
+    u = 1.0 - rng.random(n)  # (0, 1]
+    s = np.sqrt(frac * u)  # r / (r + a)
+    r = a * s / (1.0 - s)
+    return r[:, None] * _directions(rng, n)
+
+
 def lattice(ngrid: int, seed: int, rms_cells: float = 0.3, slope: float = -2.0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     q1 = (np.arange(ngrid) + 0.5) / ngrid
@@ -102,6 +115,9 @@ CONFIGS = {
     "clustered_1e6_p4": dict(dist="clustered", n=1_000_000, seed=1005, dtype="f64", order=4, theta=0.7, leaf=32),
     "clustered_1e6_p6": dict(dist="clustered", n=1_000_000, seed=1005, dtype="f64", order=6, theta=0.5, leaf=32),
     "clustered_1e6_f32": dict(dist="clustered", n=1_000_000, seed=1005, dtype="f32", order=4, theta=0.7, leaf=32),
+    "hernquist_1e5": dict(dist="hernquist", n=100_000, seed=1007, dtype="f64", order=4, theta=0.7, leaf=32),
+    "hernquist_4e7": dict(dist="hernquist", n=40_000_000, seed=1007, dtype="f64", order=4, theta=0.7,
+                          leaf=32),
     "lattice_256_f32": dict(dist="lattice", n=256 ** 3, seed=1006, dtype="f32", order=4, theta=0.7, leaf=64),
     "lattice_256_p8": dict(dist="lattice", n=256 ** 3, seed=1006, dtype="f64", order=8, theta=0.5, leaf=64),
 }
@@ -115,6 +131,8 @@ def make(dist: str, n: int, seed: int):
         pos = plummer(n, seed)
     elif dist == "clustered":
         pos = clustered(n, seed)
+    elif dist == "hernquist":
+        pos = hernquist(n, seed)
     elif dist == "lattice":
         g = round(n ** (1.0 / 3.0))
         if g ** 3 != n:

@@ -159,7 +159,7 @@ def test_degenerate_inputs(orc, kind):
     plan.close()
 
 
-@pytest.mark.parametrize("name", ["plummer_1e5", "uniform_1e5"])
+@pytest.mark.parametrize("name", ["plummer_1e5", "uniform_1e5", "hernquist_1e5"])
 def test_parity_1e5(orc, name):
     c = W.CONFIGS[name]
     say(f"  case {name}")
@@ -266,11 +266,12 @@ def test_expansions_match_oracle(orc):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,n_sample", [("lattice_256_f32", 256), ("lattice_256_p8", 24)])
-def test_parity_lattice_sampled(orc, name, n_sample):
-    """256^3 displaced lattice: keys, permutation and tree in full; lists and
-    values for the leaves of a seeded particle sample (the oracle's walk is
-    restricted to those targets)."""
+@pytest.mark.parametrize("name,n_sample", [("lattice_256_f32", 256), ("lattice_256_p8", 24),
+                                           ("hernquist_4e7", 64)])
+def test_parity_large_sampled(orc, name, n_sample):
+    """256^3 displaced lattice and the 4e7-particle Hernquist sphere: keys,
+    permutation and tree in full; lists and values for the leaves of a seeded
+    particle sample (the oracle's walk is restricted to those targets)."""
     c = W.CONFIGS[name]
     say(f"  case {name}: generating")
     pos, mass = inputs(c["dist"], c["n"], c["seed"], c["dtype"])
@@ -282,6 +283,25 @@ def test_parity_lattice_sampled(orc, name, n_sample):
     check_structure(plan, ref, sample_targets=np.nonzero(ref.mark)[0])
     check_values(phi, acc, ref, c["dtype"], idx=smp)
     plan.close()
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_direct_matches_oracle(orc, dt):
+    """fmm_direct (the accuracy reference) against the oracle's direct sum on
+    the same values, targets including the first and last particle."""
+    torch = _torch()
+    from multipole_body_gravity_amd import direct
+    pos, mass = inputs("plummer", 20000, 81, dt)
+    tdt = torch.float64 if dt == "f64" else torch.float32
+    dev = torch.device("cuda:0")
+    tg = np.concatenate([[0, 19999], np.random.default_rng(5).choice(20000, 700, replace=False)])
+    phi, acc = direct(torch.from_numpy(pos).to(dev, tdt), torch.from_numpy(mass).to(dev, tdt),
+                      torch.from_numpy(tg).to(dev))
+    rphi, racc = orc.direct(pos, mass, tg)
+    ea, _ = rel_err(acc.double().cpu().numpy(), racc)
+    ep, _ = rel_err(phi.double().cpu().numpy(), rphi)
+    tol = 1e-12 if dt == "f64" else 2e-7  # fp64 sums; fp32 only in the output
+    assert ea.max() <= tol and ep.max() <= tol, (ea.max(), ep.max())
 
 
 def test_streams_and_timing(orc):

@@ -495,3 +495,24 @@ def test_argument_errors(orc):
     with pytest.raises(orc.OracleError) as ei:
         orc.fmm(pos, m2, 4, 0.5, 8)
     assert ei.value.code == orc.ERR_NONFINITE
+
+
+@pytest.mark.parametrize("name", ["plummer", "hernquist"])
+def test_generator_radial_profiles(name):
+    """The sphere generators follow their cumulative mass profiles (truncated):
+    Kolmogorov-Smirnov distance of 2e5 radii to the analytic CDF, and isotropy."""
+    n = 200_000
+    if name == "plummer":
+        pos = W.plummer(n, 5)
+        cdf = lambda r: (r ** 3 / (1 + r ** 2) ** 1.5) / (20.0 ** 3 / (1 + 20.0 ** 2) ** 1.5)
+        rmax = 20.0
+    else:
+        pos = W.hernquist(n, 5)
+        cdf = lambda r: (r / (1 + r)) ** 2 / (100.0 / 101.0) ** 2
+        rmax = 100.0
+    r = np.sort(np.linalg.norm(pos, axis=1))
+    assert r[-1] <= rmax * (1 + 1e-12)
+    emp = np.arange(1, n + 1) / n
+    ks = np.max(np.abs(emp - cdf(r)))
+    assert ks < 1.63 / np.sqrt(n) * 1.5, ks  # well inside the 1 % KS level
+    assert np.all(np.abs(pos.mean(axis=0)) < 5 * r.mean() / np.sqrt(n))
