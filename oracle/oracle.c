@@ -17,7 +17,12 @@
  *   - the opening criterion theta = |l_A + l_B| / |c_A - c_B|, open iff
  *     theta >= theta_max (same section, the criterion equation);
  *   - upward pass, interaction stage, downward pass ("Combining near and far
- *     interactions").
+ *     interactions");
+ *   - the vector-Jacobian product of the force calculation ("Following
+ *     sensitivities backwards"): exactly, by the chain rule, for the direct
+ *     sum, and in the page's fast multipole form (the next higher derivative
+ *     of the original evaluation plus an FMM whose sources are the
+ *     sensitivities as monopoles and dipoles).
  *
  * Readings taken where the page is silent (each repeated at its code):
  *   R1  "order p": every expansion keeps total degree <= p; the translation
@@ -251,6 +256,68 @@ static void l2p_one(const mtab* t, const double* L, const double* dx, double* ph
   acc[2] += a[2];
 }
 
+/* Moments of monopoles q_j and point dipoles d_j about c.  A point dipole d
+ * at x has the potential d . grad_y G(y - x), G = -1/|r| (the field of a
+ * monopole, differentiated with respect to its position and negated), so with
+ * s = x - c its raw moments are the negated derivative of s^m along d:
+ *   M_m += q s^m - sum_a d_a m_a s^(m - e_a).
+ * These are the sources of the FMM inside the VJP (jz-fmm page, "Following
+ * sensitivities backwards": the force sensitivities act as dipole moments). */
+static void p2m_dip_set(const mtab* t, int64_t n, const double* pos, const double* q,
+                        const double* dip, const double* c, double* M) {
+  for (int64_t j = 0; j < n; j++) {
+    double s[3] = {pos[3 * j] - c[0], pos[3 * j + 1] - c[1], pos[3 * j + 2] - c[2]};
+    for (int k = 0; k < t->K; k++) {
+      const int* m = t->e[k];
+      double v = q[j] * ipow(s[0], m[0]) * ipow(s[1], m[1]) * ipow(s[2], m[2]);
+      for (int a = 0; a < 3; a++) {
+        if (m[a] == 0) continue;
+        int e[3] = {m[0], m[1], m[2]};
+        e[a] -= 1;
+        v -= dip[3 * j + a] * (double)m[a] * ipow(s[0], e[0]) * ipow(s[1], e[1]) *
+             ipow(s[2], e[2]);
+      }
+      M[k] += v;
+    }
+  }
+}
+
+/* Second derivatives of the local Taylor polynomial at offset dx (the "next
+ * higher derivative" of the original evaluation that the VJP needs):
+ *   H_ab = sum_n L_(n + e_a + e_b) dx^n / n!,   order xx, yy, zz, xy, xz, yz. */
+static void l2p_hess_one(const mtab* t, const double* L, const double* dx, double* H6) {
+  static const int pa[6] = {0, 1, 2, 0, 0, 1}, pb[6] = {0, 1, 2, 1, 2, 2};
+  for (int i = 0; i < t->K; i++) {
+    const int* n = t->e[i];
+    if (n[0] + n[1] + n[2] + 2 > t->p) continue;
+    double w = ipow(dx[0], n[0]) * ipow(dx[1], n[1]) * ipow(dx[2], n[2]) /
+               (fact(n[0]) * fact(n[1]) * fact(n[2]));
+    for (int h = 0; h < 6; h++) {
+      int e[3] = {n[0], n[1], n[2]};
+      e[pa[h]] += 1;
+      e[pb[h]] += 1;
+      H6[h] += L[t->idx[e[0]][e[1]][e[2]]] * w;
+    }
+  }
+}
+
+int oracle_p2m_dipole(int order, int64_t n, const double* pos, const double* q,
+                      const double* dip, const double* centre, double* mpole) {
+  if (order < 0 || order > MAXP || n < 0) return ORACLE_ERR_ARG;
+  mtab t;
+  mtab_init(&t, order);
+  memset(mpole, 0, sizeof(double) * (size_t)t.K);
+  p2m_dip_set(&t, n, pos, q, dip, centre, mpole);
+  return ORACLE_OK;
+}
+int oracle_l2p_hessian(int order, const double* L, const double* dx, double* H6) {
+  if (order < 0 || order > MAXP) return ORACLE_ERR_ARG;
+  mtab t;
+  mtab_init(&t, order);
+  for (int h = 0; h < 6; h++) H6[h] = 0.0;
+  l2p_hess_one(&t, L, dx, H6);
+  return ORACLE_OK;
+}
 int oracle_p2m(int order, int64_t n, const double* pos, const double* mass,
                const double* centre, double* mpole) {
   if (order < 0 || order > MAXP || n < 0) return ORACLE_ERR_ARG;
@@ -321,6 +388,66 @@ int oracle_direct(int64_t n, const double* pos, const double* mass, int64_t nt,
     acc[3 * q] = a0;
     acc[3 * q + 1] = a1;
     acc[3 * q + 2] = a2;
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* vector-Jacobian product, direct sum                                 */
+/* ------------------------------------------------------------------ */
+/* The VJP carries the sensitivities pb_i = dS/dphi_i and ab_i = dS/da_i of a
+ * scalar S back to the positions and masses ("Following sensitivities
+ * backwards" on the jz-fmm page).  Here it is the exact gradient of
+ * S = sum_i pb_i phi_i + ab_i . a_i for the direct sum, by the plain chain
+ * rule over ordered pairs.  With r = x_i - x_j and f(r) = -1/|r|:
+ *   grad f = r/|r|^3,   Hess f = I/|r|^3 - 3 r r^T/|r|^5,
+ *   phi_i = sum_j m_j f(r),   a_i = -sum_j m_j grad f(r),
+ * so pair (i, j) adds  l_ij = m_j (pb_i f(r) - ab_i . grad f(r))  to S, and
+ *   dl_ij/dm_j = pb_i f - ab_i . grad f,
+ *   dl_ij/dr   = m_j (pb_i grad f - Hess f ab_i),
+ * which goes to x_i with a plus and to x_j with a minus sign.  Each particle
+ * gathers the terms of the pairs it is part of, so the loop runs over i
+ * without shared writes. */
+static void pair_vjp_grad(const double* r, double mj, double pbi, const double* abi,
+                          double* g) { /* g = dl_ij/dr */
+  double rr = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+  double r3 = rr * rr * rr, r5 = r3 * rr * rr;
+  double ra = r[0] * abi[0] + r[1] * abi[1] + r[2] * abi[2];
+  for (int a = 0; a < 3; a++) {
+    double gradf = r[a] / r3;
+    double hab = abi[a] / r3 - 3.0 * r[a] * ra / r5; /* (Hess f) ab */
+    g[a] = mj * (pbi * gradf - hab);
+  }
+}
+static double pair_vjp_mass(const double* r, double pbi, const double* abi) {
+  double rr = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+  double r3 = rr * rr * rr;
+  double f = -1.0 / rr;
+  double ag = (r[0] * abi[0] + r[1] * abi[1] + r[2] * abi[2]) / r3; /* ab . grad f */
+  return pbi * f - ag;
+}
+
+int oracle_direct_vjp(int64_t n, const double* pos, const double* mass, const double* pb,
+                      const double* ab, double* xbar, double* mbar) {
+  if (n < 0) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t i = 0; i < n; i++) {
+    double gx[3] = {0.0, 0.0, 0.0}, gm = 0.0, g[3];
+    for (int64_t j = 0; j < n; j++) {
+      if (j == i) continue;
+      double r[3] = {pos[3 * i] - pos[3 * j], pos[3 * i + 1] - pos[3 * j + 1],
+                     pos[3 * i + 2] - pos[3 * j + 2]};
+      /* pair (i, j): i is the target, r = x_i - x_j */
+      pair_vjp_grad(r, mass[j], pb[i], ab + 3 * i, g);
+      for (int a = 0; a < 3; a++) gx[a] += g[a];
+      /* pair (j, i): i is the source, r' = x_j - x_i = -r */
+      double rn[3] = {-r[0], -r[1], -r[2]};
+      pair_vjp_grad(rn, mass[i], pb[j], ab + 3 * j, g);
+      for (int a = 0; a < 3; a++) gx[a] -= g[a];
+      gm += pair_vjp_mass(rn, pb[j], ab + 3 * j);
+    }
+    for (int a = 0; a < 3; a++) xbar[3 * i + a] = gx[a];
+    mbar[i] = gm;
   }
   return ORACLE_OK;
 }
@@ -956,6 +1083,176 @@ int oracle_fmm(int64_t n, const double* pos, const double* mass, int order, doub
   r->times[7] = tot;
   *out = r;
   return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* vector-Jacobian product, fast multipole form                        */
+/* ------------------------------------------------------------------ */
+/* The jz-fmm page ("Following sensitivities backwards") evaluates the VJP of
+ * the FMM with two contributions.  Written out for S = sum_i pb_i phi_i +
+ * ab_i . a_i, with Phi the potential of the masses and
+ *   Psi(y) = sum_k [ pb_k G(y - x_k) + ab_k . grad_y G(y - x_k) ],  G = -1/|r|,
+ * the potential of monopoles pb_k and dipoles ab_k (self term omitted):
+ *   dS/dx_i = -pb_i a_i - Hess Phi(x_i) ab_i + m_i grad Psi(x_i),
+ *   dS/dm_i = Psi(x_i).
+ * The first two terms are the "next higher derivative in the original
+ * evaluation" (Hess Phi from the forward's leaf locals plus the near field),
+ * the last ones "an FMM with the force sensitivities acting as dipole
+ * moments": the same tree, lists and translations, with the moments of the
+ * monopoles and dipoles.  Every sum runs over the same near and far split as
+ * the forward.  Requires a full (not sampled) numeric result. */
+static int fmm_vjp_on(const oracle_result* r, const double* pb, const double* ab,
+                      double* xbar, double* mbar) {
+  const int64_t n = r->n, nn = r->n_nodes;
+  const int K = r->K;
+  mtab tab;
+  mtab_init(&tab, r->p);
+  double* pbs = (double*)malloc(sizeof(double) * (size_t)n);
+  double* abs_ = (double*)malloc(sizeof(double) * 3 * (size_t)n);
+  double* Mb = (double*)calloc((size_t)(nn * K), sizeof(double));
+  double* Lb = (double*)calloc((size_t)(nn * K), sizeof(double));
+  double* H = (double*)calloc((size_t)(6 * n), sizeof(double));
+  double* psi = (double*)calloc((size_t)n, sizeof(double));
+  double* mg = (double*)calloc((size_t)(3 * n), sizeof(double)); /* -grad Psi */
+  if (!pbs || !abs_ || !Mb || !Lb || !H || !psi || !mg) {
+    free(pbs);
+    free(abs_);
+    free(Mb);
+    free(Lb);
+    free(H);
+    free(psi);
+    free(mg);
+    return ORACLE_ERR_OOM;
+  }
+  for (int64_t k = 0; k < n; k++) {
+    int64_t i = r->perm[k];
+    pbs[k] = pb[i];
+    for (int a = 0; a < 3; a++) abs_[3 * k + a] = ab[3 * i + a];
+  }
+
+  /* upward pass of the sensitivity sources */
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < nn; i++)
+    if (r->n_child[i] == 0)
+      p2m_dip_set(&tab, r->count[i], r->xs + 3 * (int64_t)r->begin[i], pbs + r->begin[i],
+                  abs_ + 3 * (int64_t)r->begin[i], r->centre + 3 * i, Mb + i * K);
+  for (int lev = r->depth - 1; lev >= 0; lev--) {
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < nn; i++) {
+      if (r->level[i] != lev || r->n_child[i] == 0) continue;
+      for (int c = 0; c < r->n_child[i]; c++) {
+        int64_t ch = r->first_child[i] + c;
+        double d[3] = {r->centre[3 * ch] - r->centre[3 * i],
+                       r->centre[3 * ch + 1] - r->centre[3 * i + 1],
+                       r->centre[3 * ch + 2] - r->centre[3 * i + 2]};
+        m2m_one(&tab, Mb + ch * K, d, Mb + i * K);
+      }
+    }
+  }
+  /* interaction stage over the forward's accepted pairs */
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t a = 0; a < nn; a++) {
+    for (int64_t e = r->m2l_off[a]; e < r->m2l_off[a + 1]; e++) {
+      int64_t b = r->m2l_src[e];
+      double R[3] = {r->centre[3 * a] - r->centre[3 * b],
+                     r->centre[3 * a + 1] - r->centre[3 * b + 1],
+                     r->centre[3 * a + 2] - r->centre[3 * b + 2]};
+      m2l_one(&tab, Mb + b * K, R, Lb + a * K);
+    }
+  }
+  /* downward pass */
+  for (int lev = 1; lev <= r->depth; lev++) {
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < nn; i++) {
+      if (r->level[i] != lev) continue;
+      int64_t pa = r->parent[i];
+      double d[3] = {r->centre[3 * i] - r->centre[3 * pa],
+                     r->centre[3 * i + 1] - r->centre[3 * pa + 1],
+                     r->centre[3 * i + 2] - r->centre[3 * pa + 2]};
+      l2l_one(&tab, Lb + pa * K, d, Lb + i * K);
+    }
+  }
+  /* far parts at the particles: Hess Phi from the forward's locals, Psi and
+   * -grad Psi from the sensitivity locals */
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < nn; i++) {
+    if (r->n_child[i] != 0) continue;
+    for (int32_t k = r->begin[i]; k < r->begin[i] + r->count[i]; k++) {
+      double dx[3] = {r->xs[3 * k] - r->centre[3 * i], r->xs[3 * k + 1] - r->centre[3 * i + 1],
+                      r->xs[3 * k + 2] - r->centre[3 * i + 2]};
+      l2p_hess_one(&tab, r->L + i * K, dx, H + 6 * (int64_t)k);
+      l2p_one(&tab, Lb + i * K, dx, psi + k, mg + 3 * (int64_t)k);
+    }
+  }
+  /* near field, self term omitted by index */
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t a = 0; a < nn; a++) {
+    if (r->n_child[a] != 0) continue;
+    for (int32_t i = r->begin[a]; i < r->begin[a] + r->count[a]; i++) {
+      double h[6] = {0, 0, 0, 0, 0, 0}, ps = 0.0, gp[3] = {0, 0, 0};
+      for (int64_t e = r->p2p_off[a]; e < r->p2p_off[a + 1]; e++) {
+        int32_t b = r->p2p_src[e];
+        for (int32_t j = r->begin[b]; j < r->begin[b] + r->count[b]; j++) {
+          if (j == i) continue;
+          double d[3] = {r->xs[3 * i] - r->xs[3 * j], r->xs[3 * i + 1] - r->xs[3 * j + 1],
+                         r->xs[3 * i + 2] - r->xs[3 * j + 2]};
+          double rr = sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+          double r3 = rr * rr * rr, r5 = r3 * rr * rr;
+          double mj = r->ms[j];
+          /* Hess Phi: m_j (I/r^3 - 3 d d^T/r^5) */
+          h[0] += mj * (1.0 / r3 - 3.0 * d[0] * d[0] / r5);
+          h[1] += mj * (1.0 / r3 - 3.0 * d[1] * d[1] / r5);
+          h[2] += mj * (1.0 / r3 - 3.0 * d[2] * d[2] / r5);
+          h[3] -= mj * 3.0 * d[0] * d[1] / r5;
+          h[4] -= mj * 3.0 * d[0] * d[2] / r5;
+          h[5] -= mj * 3.0 * d[1] * d[2] / r5;
+          /* Psi and grad Psi of monopole pb_j and dipole ab_j at x_j */
+          const double* aj = abs_ + 3 * (int64_t)j;
+          double ad = aj[0] * d[0] + aj[1] * d[1] + aj[2] * d[2];
+          ps += -pbs[j] / rr + ad / r3;
+          for (int c = 0; c < 3; c++) gp[c] += pbs[j] * d[c] / r3 + aj[c] / r3 - 3.0 * d[c] * ad / r5;
+        }
+      }
+      for (int c = 0; c < 6; c++) H[6 * (int64_t)i + c] += h[c];
+      psi[i] += ps;
+      for (int c = 0; c < 3; c++) mg[3 * (int64_t)i + c] -= gp[c];
+    }
+  }
+  /* combine in the caller's order */
+  for (int64_t k = 0; k < n; k++) {
+    int64_t i = r->perm[k];
+    const double* h = H + 6 * k;
+    const double* b = abs_ + 3 * k;
+    double hb[3] = {h[0] * b[0] + h[3] * b[1] + h[4] * b[2],
+                    h[3] * b[0] + h[1] * b[1] + h[5] * b[2],
+                    h[4] * b[0] + h[5] * b[1] + h[2] * b[2]};
+    for (int a = 0; a < 3; a++)
+      xbar[3 * i + a] = -pbs[k] * r->acc[3 * i + a] - hb[a] - r->ms[k] * mg[3 * k + a];
+    mbar[i] = psi[k];
+  }
+  free(pbs);
+  free(abs_);
+  free(Mb);
+  free(Lb);
+  free(H);
+  free(psi);
+  free(mg);
+  return ORACLE_OK;
+}
+
+int oracle_fmm_vjp(int64_t n, const double* pos, const double* mass, int order, double theta,
+                   int leaf_size, const double* pb, const double* ab, double* xbar,
+                   double* mbar) {
+  for (int64_t i = 0; i < n; i++)
+    if (!isfinite(pb[i]) || !isfinite(ab[3 * i]) || !isfinite(ab[3 * i + 1]) ||
+        !isfinite(ab[3 * i + 2]))
+      return ORACLE_ERR_NONFINITE;
+  oracle_result* r = NULL;
+  int rc = oracle_fmm(n, pos, mass, order, theta, leaf_size, 0, NULL, 1, &r);
+  if (rc) return rc;
+  rc = fmm_vjp_on(r, pb, ab, xbar, mbar);
+  oracle_free(r);
+  return rc;
 }
 
 /* ------------------------------------------------------------------ */

@@ -92,6 +92,22 @@ int oracle_l2p(int order, const double* local, const double* delta,
 int oracle_morton(int64_t n, const double* pos, double* lo, double* side,
                   uint64_t* keys);
 
+/* Vector-Jacobian products for S = sum_i pb_i phi_i + ab_i . a_i (pb [n],
+ * ab [n][3], caller's order): xbar [n][3] = dS/dpos, mbar [n] = dS/dmass.
+ * oracle_direct_vjp is the exact gradient of the direct sum (O(N^2));
+ * oracle_fmm_vjp is the fast multipole form of the jz-fmm page on the tree and
+ * lists of oracle_fmm with the same order, theta and leaf size. */
+int oracle_direct_vjp(int64_t n, const double* pos, const double* mass,
+                      const double* pb, const double* ab, double* xbar, double* mbar);
+int oracle_fmm_vjp(int64_t n, const double* pos, const double* mass, int order,
+                   double theta, int leaf_size, const double* pb, const double* ab,
+                   double* xbar, double* mbar);
+/* Moments of monopoles q [n] and point dipoles dip [n][3] about centre. */
+int oracle_p2m_dipole(int order, int64_t n, const double* pos, const double* q,
+                      const double* dip, const double* centre, double* mpole);
+/* Hessian of the local polynomial at offset delta: H6 = xx, yy, zz, xy, xz, yz. */
+int oracle_l2p_hessian(int order, const double* local, const double* delta, double* H6);
+
 #ifdef __cplusplus
 }
 #endif

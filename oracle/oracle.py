@@ -73,6 +73,10 @@ def _load():
     lib.oracle_l2l.argtypes = [i32, P, P, P]
     lib.oracle_l2p.argtypes = [i32, P, P, P, P]
     lib.oracle_morton.argtypes = [i64, P, P, P, P]
+    lib.oracle_direct_vjp.argtypes = [i64, P, P, P, P, P, P]
+    lib.oracle_fmm_vjp.argtypes = [i64, P, P, i32, dbl, i32, P, P, P, P]
+    lib.oracle_p2m_dipole.argtypes = [i32, i64, P, P, P, P, P]
+    lib.oracle_l2p_hessian.argtypes = [i32, P, P, P]
     _lib = lib
     return lib
 
@@ -285,3 +289,59 @@ def l2p(order, local, delta):
     if rc:
         raise OracleError(rc)
     return float(phi[0]), acc
+
+
+# ---- vector-Jacobian products ----------------------------------------------
+
+def direct_vjp(pos, mass, phi_bar, acc_bar):
+    """Exact gradient of S = sum pb.phi + ab.a of the direct sum: (xbar[n,3], mbar[n])."""
+    lib = _load()
+    pos = _f64(pos, (-1, 3))
+    mass = _f64(mass)
+    pb = _f64(phi_bar)
+    ab = _f64(acc_bar, (-1, 3))
+    n = pos.shape[0]
+    xbar = np.zeros((n, 3))
+    mbar = np.zeros(n)
+    rc = lib.oracle_direct_vjp(n, _p(pos), _p(mass), _p(pb), _p(ab), _p(xbar), _p(mbar))
+    if rc:
+        raise OracleError(rc)
+    return xbar, mbar
+
+
+def fmm_vjp(pos, mass, phi_bar, acc_bar, order=4, theta=0.7, leaf_size=32):
+    """Fast multipole VJP on the oracle's own tree and lists: (xbar[n,3], mbar[n])."""
+    lib = _load()
+    pos = _f64(pos, (-1, 3))
+    mass = _f64(mass)
+    pb = _f64(phi_bar)
+    ab = _f64(acc_bar, (-1, 3))
+    n = pos.shape[0]
+    xbar = np.zeros((n, 3))
+    mbar = np.zeros(n)
+    rc = lib.oracle_fmm_vjp(n, _p(pos), _p(mass), int(order), float(theta), int(leaf_size),
+                            _p(pb), _p(ab), _p(xbar), _p(mbar))
+    if rc:
+        raise OracleError(rc)
+    return xbar, mbar
+
+
+def p2m_dipole(order, pos, q, dip, centre):
+    lib = _load()
+    pos = _f64(pos, (-1, 3))
+    out = np.zeros(ncoef(order))
+    rc = lib.oracle_p2m_dipole(order, pos.shape[0], _p(pos), _p(_f64(q)), _p(_f64(dip, (-1, 3))),
+                               _p(_f64(centre)), _p(out))
+    if rc:
+        raise OracleError(rc)
+    return out
+
+
+def l2p_hessian(order, local, delta):
+    """Second derivatives of the local polynomial at delta, as a symmetric 3x3 matrix."""
+    lib = _load()
+    h = np.zeros(6)
+    rc = lib.oracle_l2p_hessian(order, _p(_f64(local)), _p(_f64(delta)), _p(h))
+    if rc:
+        raise OracleError(rc)
+    return np.array([[h[0], h[3], h[4]], [h[3], h[1], h[5]], [h[4], h[5], h[2]]])

@@ -516,3 +516,161 @@ def test_generator_radial_profiles(name):
     ks = np.max(np.abs(emp - cdf(r)))
     assert ks < 1.63 / np.sqrt(n) * 1.5, ks  # well inside the 1 % KS level
     assert np.all(np.abs(pos.mean(axis=0)) < 5 * r.mean() / np.sqrt(n))
+
+
+# --------------------------------------------------------------------------
+# vector-Jacobian product (jz-fmm page, "Following sensitivities backwards")
+# --------------------------------------------------------------------------
+
+def _direct_S_torch(pos, mass, pb, ab):
+    """S = sum pb.phi + ab.a of the direct sum, as a torch graph (CPU, fp64)."""
+    import torch
+    X = torch.tensor(pos, requires_grad=True)
+    M = torch.tensor(mass, requires_grad=True)
+    n = pos.shape[0]
+    eye = torch.eye(n, dtype=torch.float64)
+    d = X[:, None, :] - X[None, :, :]
+    r = torch.sqrt((d ** 2).sum(-1) + eye)  # the diagonal is masked below
+    off = 1.0 - eye
+    phi = -(off * M[None, :] / r).sum(1)
+    acc = -(off[..., None] * M[None, :, None] * d / r[..., None] ** 3).sum(1)
+    S = (torch.tensor(pb) * phi).sum() + (torch.tensor(ab) * acc).sum()
+    S.backward()
+    return X.grad.numpy(), M.grad.numpy()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_direct_vjp_equals_autograd(orc, seed):
+    rng = np.random.default_rng(seed)
+    n = 80
+    pos = rng.random((n, 3))
+    mass = rng.random(n) + 0.1
+    pb = rng.standard_normal(n)
+    ab = rng.standard_normal((n, 3))
+    xb, mb = orc.direct_vjp(pos, mass, pb, ab)
+    xt, mt = _direct_S_torch(pos, mass, pb, ab)
+    assert np.abs(xb - xt).max() <= 1e-12 * np.abs(xt).max()
+    assert np.abs(mb - mt).max() <= 1e-12 * np.abs(mt).max()
+
+
+def test_direct_vjp_finite_differences(orc):
+    """Central differences of S through the oracle's direct sum (no torch)."""
+    rng = np.random.default_rng(7)
+    n = 24
+    pos = rng.random((n, 3))
+    mass = rng.random(n) + 0.1
+    pb = rng.standard_normal(n)
+    ab = rng.standard_normal((n, 3))
+    xb, mb = orc.direct_vjp(pos, mass, pb, ab)
+
+    def S(p, m):
+        phi, acc = orc.direct(p, m)
+        return float(pb @ phi + np.sum(ab * acc))
+
+    h = 1e-5
+    for i, a in [(0, 0), (5, 1), (17, 2), (23, 0)]:
+        pp, pm = pos.copy(), pos.copy()
+        pp[i, a] += h
+        pm[i, a] -= h
+        fd = (S(pp, mass) - S(pm, mass)) / (2 * h)
+        assert abs(fd - xb[i, a]) <= 1e-6 * max(1.0, abs(xb[i, a]))
+    for i in [3, 11]:
+        mp, mm = mass.copy(), mass.copy()
+        mp[i] += h
+        mm[i] -= h
+        fd = (S(pos, mp) - S(pos, mm)) / (2 * h)  # S is linear in each mass
+        assert abs(fd - mb[i]) <= 1e-8 * max(1.0, abs(mb[i]))
+
+
+def test_p2m_dipole(orc):
+    """A point dipole is the limit of a monopole differentiated along its
+    position; with no dipoles the moments are the mass moments."""
+    rng = np.random.default_rng(11)
+    p = 6
+    c = np.array([0.1, -0.2, 0.3])
+    x = c + 0.3 * rng.standard_normal((1, 3))
+    q = np.array([0.7])
+    d = rng.standard_normal((1, 3))
+    mono = orc.p2m_dipole(p, x, q, np.zeros((1, 3)), c)
+    assert np.allclose(mono, orc.p2m(p, x, q, c), rtol=0, atol=1e-15)
+    dip = orc.p2m_dipole(p, x, np.zeros(1), d, c)
+    h = 1e-5
+    fd = np.zeros_like(dip)
+    for a in range(3):
+        xp, xm = x.copy(), x.copy()
+        xp[0, a] += h
+        xm[0, a] -= h
+        fd -= d[0, a] * (orc.p2m(p, xp, [1.0], c) - orc.p2m(p, xm, [1.0], c)) / (2 * h)
+    assert np.abs(dip - fd).max() <= 1e-8 * np.abs(dip).max()
+    # a dipole at the centre has only the first moments, M_(e_a) = -d_a
+    at = orc.p2m_dipole(p, c[None, :], np.zeros(1), d, c)
+    mi = orc.multi_indices(p)
+    for k, m in enumerate(mi):
+        want = -d[0, m.index(1)] if sum(m) == 1 else 0.0
+        assert at[k] == pytest.approx(want, abs=1e-15)
+
+
+def test_l2p_hessian(orc):
+    """Hessian of the local polynomial: traceless for harmonic locals, equal to
+    minus the Jacobian of the L2P acceleration, and converging to the exact
+    tidal tensor of a point mass."""
+    rng = np.random.default_rng(5)
+    src = np.array([2.0, -1.5, 1.0])
+    m = 0.8
+    c = np.zeros(3)
+    dx = np.array([0.12, -0.05, 0.09])
+    p = 8
+    L = -m * orc.dtensor(p, c - src)  # derivatives of -m/|x - src| at c: harmonic
+    H = orc.l2p_hessian(p, L, dx)
+    assert np.allclose(H, H.T)
+    assert abs(np.trace(H)) <= 1e-12 * np.abs(H).max()
+    h = 1e-5
+    J = np.zeros((3, 3))
+    for b in range(3):
+        e = np.zeros(3)
+        e[b] = h
+        J[:, b] = (orc.l2p(p, L, dx + e)[1] - orc.l2p(p, L, dx - e)[1]) / (2 * h)
+    assert np.abs(H + J).max() <= 1e-7 * np.abs(H).max()
+    r = c + dx - src
+    rn = np.linalg.norm(r)
+    exact = m * (np.eye(3) / rn ** 3 - 3 * np.outer(r, r) / rn ** 5)
+    errs = [np.abs(orc.l2p_hessian(q, -m * orc.dtensor(q, c - src), dx) - exact).max()
+            for q in (2, 4, 6, 8)]
+    assert all(b < a for a, b in zip(errs, errs[1:]))
+    assert errs[-1] <= 1e-5 * np.abs(exact).max()
+    del rng
+
+
+def _vjp_case(n, seed):
+    rng = np.random.default_rng(seed)
+    pos = W.plummer(n, seed)
+    mass = np.full(n, 1.0 / n)
+    pb = rng.standard_normal(n)
+    ab = rng.standard_normal((n, 3))
+    return pos, mass, pb, ab
+
+
+def test_fmm_vjp_all_near_equals_direct(orc):
+    pos, mass, pb, ab = _vjp_case(1500, 21)
+    xd, md = orc.direct_vjp(pos, mass, pb, ab)
+    for kw in (dict(leaf_size=1500, theta=0.7), dict(leaf_size=8, theta=1e-3)):
+        xf, mf = orc.fmm_vjp(pos, mass, pb, ab, order=4, **kw)
+        assert np.abs(xf - xd).max() <= 1e-13 * np.abs(xd).max()
+        assert np.abs(mf - md).max() <= 1e-13 * np.abs(md).max()
+
+
+def test_fmm_vjp_converges_with_order(orc):
+    """The far-field terms (Hessian from the locals, the dipole-source FMM) are
+    approximations; a dropped term or a wrong sign would stop the error
+    falling with the order."""
+    pos, mass, pb, ab = _vjp_case(3000, 22)
+    xd, md = orc.direct_vjp(pos, mass, pb, ab)
+    nx = np.linalg.norm(xd, axis=1)
+    e_x, e_m = [], []
+    for p in (2, 4, 6, 8):
+        xf, mf = orc.fmm_vjp(pos, mass, pb, ab, order=p, theta=0.5, leaf_size=16)
+        e_x.append(np.percentile(np.linalg.norm(xf - xd, axis=1) / nx, 99))
+        e_m.append(np.abs(mf - md).max() / np.abs(md).max())
+    assert all(b < 0.5 * a for a, b in zip(e_x, e_x[1:])), e_x
+    assert all(b < 0.5 * a for a, b in zip(e_m, e_m[1:])), e_m
+    assert e_x[-1] < 1e-3 and e_m[-1] < 1e-5, (e_x, e_m)
