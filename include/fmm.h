@@ -75,7 +75,8 @@ enum fmm_stage {
   FMM_STAGE_DOWN = 6,  /* L2L + L2P                             */
   FMM_STAGE_P2P = 7,   /* the single P2P (+ combine) launch     */
   FMM_STAGE_TAIL = 8,  /* M2L of the transposed tails (eval)    */
-  FMM_N_STAGES = 9
+  FMM_STAGE_VJP = 9,   /* the whole fmm_vjp call                */
+  FMM_N_STAGES = 10
 };
 
 /* Kernel indices of fmm_stats_t.kernel_ms: single launches inside the M2L
@@ -86,7 +87,9 @@ enum fmm_kernel {
   FMM_KERNEL_M2L_TAIL = 1,    /* M2L over the transposed tails            */
   FMM_KERNEL_P2P = 2,         /* near-field pair sums                     */
   FMM_KERNEL_P2P_COMBINE = 3, /* ordered sum of split leaves' partials    */
-  FMM_N_KERNELS = 4
+  FMM_KERNEL_VJP_M2L_SIB = 4, /* fmm_vjp: sibling M2L of the sensitivity moments */
+  FMM_KERNEL_VJP_P2P = 5,     /* fmm_vjp: near-field pair sums            */
+  FMM_N_KERNELS = 6
 };
 
 typedef struct {
@@ -96,10 +99,10 @@ typedef struct {
   double lo[3], side;    /* root cube */
   float stage_ms[FMM_N_STAGES]; /* mean over the timed steps, see fmm_set_timing */
   int32_t walk_retries;  /* workspace regrowths during the last walk */
-  float kernel_ms[FMM_N_KERNELS]; /* mean over the timed builds (sibling M2L) or evals */
-  int32_t timed_builds;  /* builds and evals the means are taken over */
+  float kernel_ms[FMM_N_KERNELS]; /* mean over the timed builds (sibling M2L), evals or VJPs */
+  int32_t timed_builds;  /* builds, evals and VJPs the means are taken over */
   int32_t timed_evals;
-  int32_t reserved[1];
+  int32_t timed_vjps;
 } fmm_stats_t;
 
 /* Create a plan for N particles.  N in [1, 2^31), order in [0, FMM_MAX_ORDER],
@@ -127,6 +130,27 @@ int fmm_build(fmm_plan_t plan, const void* pos, const void* mass, void* stream);
  * the plan's dtype.  Asynchronous on `stream`; may be repeated after one
  * build (the build's results are only read). */
 int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
+
+/* Vector-Jacobian product of the evaluation (jz-fmm page, "Following
+ * sensitivities backwards"): given the sensitivities phi_bar = dS/dphi [N] and
+ * acc_bar = dS/da [N][3] of a scalar S, writes
+ *   pos_bar [N][3] = dS/dpos = -phi_bar_i a_i - (Hess phi)(x_i) acc_bar_i
+ *                              + m_i grad Psi(x_i),
+ *   mass_bar [N]   = dS/dmass = Psi(x_i),
+ * Psi being the potential of monopoles phi_bar and point dipoles acc_bar at the
+ * particles (self term omitted).  The page's two contributions: the next
+ * higher derivative (the Hessian) of the original evaluation, and an FMM whose
+ * sources are the sensitivities acting as dipole moments.  Both use the plan's
+ * tree, lists and order: the Hessian comes from the leaf locals of order p (one
+ * degree below the acceleration), so build the plan one order higher than the
+ * forward evaluation to keep the accuracy of that evaluation.  All arrays are
+ * device arrays in the plan's dtype, in the caller's order.  Requires a built
+ * plan (FMM_ERR_STATE otherwise); runs the forward's leaf locals itself if no
+ * fmm_eval followed the build.  Asynchronous on `stream`; repeatable; must not
+ * overlap an fmm_eval of the same plan on another stream (they share the
+ * split-task partial buffers). */
+int fmm_vjp(fmm_plan_t plan, const void* phi_bar, const void* acc_bar, void* pos_bar,
+            void* mass_bar, void* stream);
 
 /* Free the plan and its workspace (synchronizes the device). */
 int fmm_destroy(fmm_plan_t plan);

@@ -107,11 +107,18 @@ void collect_pending(fmm_plan_t p) {
   if (p->pend_eval) {
     for (int s : {FMM_STAGE_TAIL, FMM_STAGE_DOWN, FMM_STAGE_P2P})
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
-    for (int k = 0; k < FMM_N_KERNELS; k++)
-      if (k != FMM_KERNEL_M2L_SIB && p->kran[k])
-        p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
+    for (int k = FMM_KERNEL_M2L_TAIL; k <= FMM_KERNEL_P2P_COMBINE; k++)
+      if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_evals++;
     p->pend_eval = false;
+  }
+  if (p->pend_vjp) {
+    p->stage_sum[FMM_STAGE_VJP] +=
+        elapsed(p->ev[2 * FMM_STAGE_VJP], p->ev[2 * FMM_STAGE_VJP + 1]);
+    for (int k : {FMM_KERNEL_VJP_M2L_SIB, FMM_KERNEL_VJP_P2P})
+      if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
+    p->n_timed_vjps++;
+    p->pend_vjp = false;
   }
 }
 
@@ -403,6 +410,45 @@ int materialize_m2l_lists(fmm_plan_t p, hipStream_t st) {
   return FMM_OK;
 }
 
+// The leaves' complete forward locals in lfin: the M2L of the transposed
+// tails, then the downward pass (one launch at orders <= 5, else level by
+// level on a copy of `local`).  Records the tail stage and the start of the
+// downward stage.
+int leaf_locals(fmm_plan_t p, hipStream_t st) {
+  const int dt = p->dtype, ord = p->order;
+  const double* centre = P<double>(p->ncentre);
+  int32_t* leaves = P<int32_t>(p->leaves);
+  const int64_t nn = p->n_nodes;
+  const size_t lbytes = (size_t)nn * p->K * wbytes(dt);
+  const bool pull = ord <= 5;  // the one-launch downward pass
+
+  rec(p, FMM_STAGE_TAIL, 0, st);
+  M2LArgs ma = m2l_args(p);
+  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_TAIL : nullptr;
+  ma.ran = p->kran + FMM_KERNEL_M2L_TAIL;
+  if (!pull) {  // the level-by-level pass works on a copy
+    TRY_HIP(hipMemcpyAsync(p->lfin.p, p->local.p, lbytes, hipMemcpyDeviceToDevice, st));
+    ma.local = p->lfin.p;
+  }
+  TRY_HIP(launch_m2l_tails(dt, ord, ma, !pull, st));
+  rec(p, FMM_STAGE_TAIL, 1, st);
+
+  rec(p, FMM_STAGE_DOWN, 0, st);
+  p->l2l_pulled = pull && launch_l2l_pull(dt, ord, leaves, p->n_leaves, P<int32_t>(p->nparent),
+                                          centre, p->local.p,
+                                          p->n_tail_tasks > 0 ? P<int64_t>(p->tail_toff) : nullptr,
+                                          p->tail_part.p, p->lfin.p, st);
+  if (pull && !p->l2l_pulled) return FMM_ERR_HIP;
+  if (p->l2l_pulled) {
+    TRY_HIP(hipGetLastError());
+  } else {
+    for (int l = 1; l <= p->depth; l++)
+      TRY_HIP(launch_l2l(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                         P<int32_t>(p->nparent), centre, p->lfin.p, nullptr, st));
+  }
+  return FMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -483,6 +529,8 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->ncount,     &p->nparent,     &p->nfirst,      &p->nnchild,
                   &p->ncentre,    &p->nq,          &p->ngeo,        &p->leaves,
                   &p->lvl_blkcnt, &p->mpole,       &p->mred,        &p->local,       &p->lfin,
+                  &p->vrec,       &p->vfar,        &p->vmpole,      &p->vmred,
+                  &p->vlocal,     &p->vlfin,
                   &p->pool[0],
                   &p->pool[1],    &p->pool[2],
                   &p->cu_off,     &p->cu_cnt,      &p->u_off,       &p->u_cnt,
@@ -515,10 +563,10 @@ int fmm_set_timing(fmm_plan_t p, int enable) {
   if (p->timing) {
     TRY_HIP(hipSetDevice(p->device));
     TRY_HIP(hipDeviceSynchronize());
-    p->pend_build = p->pend_eval = false;
+    p->pend_build = p->pend_eval = p->pend_vjp = false;
     for (double& x : p->stage_sum) x = 0.0;
     for (double& x : p->kernel_sum) x = 0.0;
-    p->n_timed_builds = p->n_timed_evals = 0;
+    p->n_timed_builds = p->n_timed_evals = p->n_timed_vjps = 0;
   }
   return FMM_OK;
 }
@@ -630,47 +678,17 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   if (!p->built) return FMM_ERR_STATE;
   hipStream_t st = (hipStream_t)stream;
   TRY_HIP(hipSetDevice(p->device));
-  const int dt = p->dtype, ord = p->order;
-  const double* centre = P<double>(p->ncentre);
-  int32_t* leaves = P<int32_t>(p->leaves);
-
   // multipoles, source records and the own-entry locals come from the build's
   // second stream; `local` is only read from here on
   TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
-  const int64_t nn = p->n_nodes;
-  const size_t lbytes = (size_t)nn * p->K * wbytes(dt);
-  const bool pull = ord <= 5;  // the one-launch downward pass
-
-  rec(p, FMM_STAGE_TAIL, 0, st);
-  M2LArgs ma = m2l_args(p);
-  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_TAIL : nullptr;
-  ma.ran = p->kran + FMM_KERNEL_M2L_TAIL;
-  if (!pull) {  // the level-by-level pass works on a copy
-    TRY_HIP(hipMemcpyAsync(p->lfin.p, p->local.p, lbytes, hipMemcpyDeviceToDevice, st));
-    ma.local = p->lfin.p;
-  }
-  TRY_HIP(launch_m2l_tails(dt, ord, ma, !pull, st));
-  rec(p, FMM_STAGE_TAIL, 1, st);
-
-  rec(p, FMM_STAGE_DOWN, 0, st);
-  p->l2l_pulled = pull && launch_l2l_pull(dt, ord, leaves, p->n_leaves, P<int32_t>(p->nparent),
-                                          centre, p->local.p,
-                                          p->n_tail_tasks > 0 ? P<int64_t>(p->tail_toff) : nullptr,
-                                          p->tail_part.p, p->lfin.p, st);
-  if (pull && !p->l2l_pulled) return FMM_ERR_HIP;
-  if (p->l2l_pulled) {
-    TRY_HIP(hipGetLastError());
-  } else {
-    for (int l = 1; l <= p->depth; l++)
-      TRY_HIP(launch_l2l(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
-                         P<int32_t>(p->nparent), centre, p->lfin.p, nullptr, st));
-  }
-  TRY_HIP(launch_l2p(dt, ord, p->n, p->pts.p, P<int32_t>(p->leaf_of), centre, p->lfin.p,
-                     p->far.p, st));
+  TRY(leaf_locals(p, st));
+  TRY_HIP(launch_l2p(p->dtype, p->order, p->n, p->pts.p, P<int32_t>(p->leaf_of),
+                     P<double>(p->ncentre), p->lfin.p, p->far.p, st));
   rec(p, FMM_STAGE_DOWN, 1, st);
 
   rec(p, FMM_STAGE_P2P, 0, st);
-  TRY_HIP(launch_p2p(dt, p->p2p_task.p, p->n_p2p_tasks, leaves, p->n_leaves,
+  int32_t* leaves = P<int32_t>(p->leaves);
+  TRY_HIP(launch_p2p(p->dtype, p->p2p_task.p, p->n_p2p_tasks, leaves, p->n_leaves,
                      P<int64_t>(p->p2p_toff), P<int64_t>(p->p2p_poff), P<int32_t>(p->nbegin),
                      P<int32_t>(p->ncount), P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
                      P<int32_t>(p->idx), phi, acc, p->p2p_part.p, p->n_p2p_part > 0,
@@ -679,6 +697,79 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   rec(p, FMM_STAGE_P2P, 1, st);
   p->pend_eval = p->timing;
   p->evaluated = true;
+  return FMM_OK;
+}
+
+int fmm_vjp(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_bar,
+            void* mass_bar, void* stream) {
+  if (!p || !phi_bar || !acc_bar || !pos_bar || !mass_bar) return FMM_ERR_ARG;
+  if (!p->built) return FMM_ERR_STATE;
+  hipStream_t st = (hipStream_t)stream;
+  TRY_HIP(hipSetDevice(p->device));
+  const int dt = p->dtype, ord = p->order;
+  const int64_t n = p->n, nn = p->n_nodes;
+  const size_t w = wbytes(dt);
+  TRY(grow(p->vrec, 8 * w * n));
+  TRY(grow(p->vfar, 4 * w * n));
+  TRY(grow(p->vmpole, w * p->K * nn));
+  TRY(grow(p->vmred, (size_t)mrec_bytes((ord + 1) * (ord + 1), (int)w) * nn));
+  TRY(grow(p->vlocal, w * p->K * nn));
+  TRY(grow(p->vlfin, w * p->K * nn));
+  TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
+  // the forward's leaf locals (lfin) give the Hessian term
+  if (!p->evaluated) {
+    TRY(leaf_locals(p, st));
+    p->evaluated = true;
+  }
+  rec(p, FMM_STAGE_VJP, 0, st);
+  const double* centre = P<double>(p->ncentre);
+  int32_t* leaves = P<int32_t>(p->leaves);
+  // sensitivity sources: monopoles pb and dipoles ab at the particles, on the
+  // forward's tree and lists
+  TRY_HIP(launch_vjp_gather(dt, n, p->pts.p, P<int32_t>(p->idx), phi_bar, acc_bar, p->vrec.p, st));
+  TRY_HIP(launch_p2m_dip(dt, ord, p->vrec.p, leaves, p->n_leaves, P<int32_t>(p->nbegin),
+                         P<int32_t>(p->ncount), centre, p->vmpole.p, st));
+  for (int l = p->depth - 1; l >= 0; l--)
+    TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                       P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->vmpole.p, st));
+  TRY_HIP(launch_m2l_records(dt, ord, nn, centre, p->vmpole.p, p->vmred.p, st));
+  M2LArgs ma = m2l_args(p);
+  ma.mrec = p->vmred.p;
+  ma.local = p->vlocal.p;
+  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_VJP_M2L_SIB : nullptr;
+  ma.ran = p->kran + FMM_KERNEL_VJP_M2L_SIB;
+  TRY_HIP(launch_m2l_sib(dt, ord, ma, st));
+  ma.ev = nullptr;
+  ma.ran = nullptr;
+  const bool pull = ord <= 5;
+  if (!pull) {
+    TRY_HIP(hipMemcpyAsync(p->vlfin.p, p->vlocal.p, (size_t)nn * p->K * w,
+                           hipMemcpyDeviceToDevice, st));
+    ma.local = p->vlfin.p;
+  }
+  TRY_HIP(launch_m2l_tails(dt, ord, ma, !pull, st));
+  if (pull) {
+    if (!launch_l2l_pull(dt, ord, leaves, p->n_leaves, P<int32_t>(p->nparent), centre,
+                         p->vlocal.p, p->n_tail_tasks > 0 ? P<int64_t>(p->tail_toff) : nullptr,
+                         p->tail_part.p, p->vlfin.p, st))
+      return FMM_ERR_HIP;
+    TRY_HIP(hipGetLastError());
+  } else {
+    for (int l = 1; l <= p->depth; l++)
+      TRY_HIP(launch_l2l(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
+                         P<int32_t>(p->nparent), centre, p->vlfin.p, nullptr, st));
+  }
+  TRY_HIP(launch_l2p_vjp(dt, ord, n, p->vrec.p, P<int32_t>(p->leaf_of), centre, p->lfin.p,
+                         p->vlfin.p, p->vfar.p, st));
+  TRY_HIP(launch_p2p_vjp(dt, p->p2p_task.p, p->n_p2p_tasks, leaves, p->n_leaves,
+                         P<int64_t>(p->p2p_toff), P<int64_t>(p->p2p_poff), P<int32_t>(p->nbegin),
+                         P<int32_t>(p->ncount), P<int32_t>(p->p2p_src), p->vrec.p, p->vfar.p,
+                         P<int32_t>(p->idx), mass_bar, pos_bar, p->p2p_part.p,
+                         p->n_p2p_part > 0,
+                         p->timing ? p->kev + 2 * FMM_KERNEL_VJP_P2P : nullptr,
+                         p->kran + FMM_KERNEL_VJP_P2P, st));
+  rec(p, FMM_STAGE_VJP, 1, st);
+  p->pend_vjp = p->timing;
   return FMM_OK;
 }
 
@@ -704,16 +795,21 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
     TRY_HIP(hipSetDevice(p->device));
     TRY_HIP(hipDeviceSynchronize());
     collect_pending(p);
-    const double nb = std::max(1, p->n_timed_builds), ne = std::max(1, p->n_timed_evals);
+    const double nb = std::max(1, p->n_timed_builds), ne = std::max(1, p->n_timed_evals),
+                 nv = std::max(1, p->n_timed_vjps);
     for (int s = 0; s < FMM_N_STAGES; s++)
       out->stage_ms[s] = (float)(p->stage_sum[s] / (s <= FMM_STAGE_WALK || s == FMM_STAGE_UP ||
                                                              s == FMM_STAGE_M2L
                                                          ? nb
-                                                         : ne));
+                                                     : s == FMM_STAGE_VJP ? nv
+                                                                          : ne));
     for (int k = 0; k < FMM_N_KERNELS; k++)
-      out->kernel_ms[k] = (float)(p->kernel_sum[k] / (k == FMM_KERNEL_M2L_SIB ? nb : ne));
+      out->kernel_ms[k] = (float)(p->kernel_sum[k] / (k == FMM_KERNEL_M2L_SIB   ? nb
+                                                      : k >= FMM_KERNEL_VJP_M2L_SIB ? nv
+                                                                                    : ne));
     out->timed_builds = p->n_timed_builds;
     out->timed_evals = p->n_timed_evals;
+    out->timed_vjps = p->n_timed_vjps;
   }
   return FMM_OK;
 }

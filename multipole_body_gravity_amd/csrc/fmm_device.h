@@ -396,5 +396,12 @@ template <typename T>
 struct alignas(4 * sizeof(T)) P4 {
   T x, y, z, m;
 };
+// A particle with its VJP sensitivities: position and mass, then pb = dS/dphi
+// and ab = dS/da.
+template <typename T>
+struct alignas(8 * sizeof(T)) P8 {
+  P4<T> p;  // x, y, z, m
+  P4<T> c;  // pb, abx, aby, abz
+};
 
 }  // namespace mbg

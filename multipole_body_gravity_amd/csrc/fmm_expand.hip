@@ -693,6 +693,207 @@ hipError_t launch_l2p(int dtype, int order, int64_t n, const void* pts, const in
   return hipGetLastError();
 }
 
+// ---------------- VJP: sensitivity records, their moments, far-field parts ----------------
+// rec[k] = (sorted particle k, its sensitivities pb, ab from the caller's order)
+template <typename T>
+__global__ void k_vjp_gather(int64_t n, const P4<T>* pts, const int32_t* perm, const T* pb,
+                             const T* ab, P8<T>* rec) {
+  const int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const int64_t i = perm[k];
+  P8<T> r;
+  r.p = pts[k];
+  r.c.x = pb[i];
+  r.c.y = ab[3 * i];
+  r.c.z = ab[3 * i + 1];
+  r.c.m = ab[3 * i + 2];
+  rec[k] = r;
+}
+
+hipError_t launch_vjp_gather(int dtype, int64_t n, const void* pts, const int32_t* perm,
+                             const void* pb, const void* ab, void* rec, hipStream_t st) {
+  const unsigned g = (unsigned)((n + 255) / 256);
+  if (dtype == FMM_F64)
+    k_vjp_gather<double><<<g, 256, 0, st>>>(n, (const P4<double>*)pts, perm, (const double*)pb,
+                                            (const double*)ab, (P8<double>*)rec);
+  else
+    k_vjp_gather<float><<<g, 256, 0, st>>>(n, (const P4<float>*)pts, perm, (const float*)pb,
+                                           (const float*)ab, (P8<float>*)rec);
+  return hipGetLastError();
+}
+
+// Moments of the sensitivity sources, one wave per leaf, lanes over
+// coefficients.  A monopole pb and a point dipole ab at x = c + s (the
+// dipole's potential is ab . grad_y G(y - x), G = -1/r) have the scaled
+// moments
+//   Mt_m = pb (-s)^m / m! + sum_a ab_a (-s)^(m - e_a) / (m - e_a)!,
+// so with the staged tables tab[a][q] = (-s_a)^q / q! every term is a product
+// of three table entries.
+template <typename T>
+__global__ void __launch_bounds__(EX_THREADS)
+    k_p2m_dip(int order, int K, const P8<T>* rec, const int32_t* leaves, int64_t n_leaves,
+              const int32_t* begin, const int32_t* count, const double* centre, T* mpole) {
+  __shared__ double tab[EX_WAVES][WAVE][3][PP];
+  __shared__ double wq[EX_WAVES][WAVE][4];  // pb, abx, aby, abz
+  const int lane = __lane_id(), w = threadIdx.x / WAVE;
+  for (int64_t li = (int64_t)blockIdx.x * EX_WAVES + w; li < n_leaves;
+       li += (int64_t)gridDim.x * EX_WAVES) {
+    const int32_t node = leaves[li];
+    const double c[3] = {centre[3 * node], centre[3 * node + 1], centre[3 * node + 2]};
+    double acc[3] = {0.0, 0.0, 0.0};  // coefficients lane, lane+64, lane+128
+    const int32_t j0 = begin[node], j1 = j0 + count[node];
+    for (int32_t jb = j0; jb < j1; jb += WAVE) {
+      const int nj = min(WAVE, j1 - jb);
+      if (lane < nj) {
+        const P8<T> r = rec[jb + lane];
+        const double xs[3] = {c[0] - (double)r.p.x, c[1] - (double)r.p.y, c[2] - (double)r.p.z};
+        for (int ax = 0; ax < 3; ax++) {
+          double v = 1.0;
+          tab[w][lane][ax][0] = 1.0;
+          for (int q = 1; q <= order; q++) {
+            v = v * xs[ax] * c_inv_int[q];
+            tab[w][lane][ax][q] = v;
+          }
+        }
+        wq[w][lane][0] = (double)r.c.x;
+        wq[w][lane][1] = (double)r.c.y;
+        wq[w][lane][2] = (double)r.c.z;
+        wq[w][lane][3] = (double)r.c.m;
+      }
+      __builtin_amdgcn_wave_barrier();
+      for (int rr = 0; rr < 3; rr++) {
+        const int m = lane + WAVE * rr;
+        if (m >= K) break;
+        const int a = c_mi.a[m], b = c_mi.b[m], cc = c_mi.c[m];
+        double s = acc[rr];
+        for (int j = 0; j < nj; j++) {
+          const double tx = tab[w][j][0][a], ty = tab[w][j][1][b], tz = tab[w][j][2][cc];
+          double v = wq[w][j][0] * tx * ty * tz;
+          if (a > 0) v += wq[w][j][1] * tab[w][j][0][a - 1] * ty * tz;
+          if (b > 0) v += wq[w][j][2] * tx * tab[w][j][1][b - 1] * tz;
+          if (cc > 0) v += wq[w][j][3] * tx * ty * tab[w][j][2][cc - 1];
+          s += v;
+        }
+        acc[rr] = s;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    for (int rr = 0; rr < 3; rr++) {
+      const int m = lane + WAVE * rr;
+      if (m < K) mpole[(int64_t)node * K + m] = (T)acc[rr];
+    }
+  }
+}
+
+hipError_t launch_p2m_dip(int dtype, int order, const void* rec, const int32_t* leaves,
+                          int64_t n_leaves, const int32_t* begin, const int32_t* count,
+                          const double* centre, void* mpole, hipStream_t st) {
+  hipError_t e = ensure_table();
+  if (e != hipSuccess) return e;
+  const int K = ncoef(order);
+  if (n_leaves == 0) return hipSuccess;
+  int64_t blocks = std::min<int64_t>((n_leaves + EX_WAVES - 1) / EX_WAVES, 65535);
+  if (dtype == FMM_F64)
+    k_p2m_dip<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(
+        order, K, (const P8<double>*)rec, leaves, n_leaves, begin, count, centre, (double*)mpole);
+  else
+    k_p2m_dip<float><<<(unsigned)blocks, EX_THREADS, 0, st>>>(
+        order, K, (const P8<float>*)rec, leaves, n_leaves, begin, count, centre, (float*)mpole);
+  return hipGetLastError();
+}
+
+// Far-field parts of the VJP at the particles, one thread per particle:
+//   from the forward's leaf locals L:   a = -grad phi,  H = Hess phi
+//     (H_ab = sum_n L_(n + e_a + e_b) dx^n / n!, the next higher derivative);
+//   from the sensitivity locals B:      Psi and grad Psi;
+// out[k] = (Psi, -pb a - H ab + m grad Psi) in sorted order.
+template <typename T, int P>
+__global__ void k_l2p_vjp(int64_t n, const P8<T>* rec, const int32_t* leaf_of,
+                          const double* centre, const T* local, const T* blocal, P4<T>* out) {
+  constexpr int K = Tabs<P>::K;
+  int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const int32_t leaf = leaf_of[k];
+  const P8<T> r = rec[k];
+  const T dx = (T)((double)r.p.x - centre[3 * leaf]);
+  const T dy = (T)((double)r.p.y - centre[3 * leaf + 1]);
+  const T dz = (T)((double)r.p.z - centre[3 * leaf + 2]);
+  T px[P + 1], py[P + 1], pz[P + 1];  // x^i / i!
+  px[0] = py[0] = pz[0] = (T)1;
+#pragma unroll
+  for (int i = 1; i <= P; i++) {
+    px[i] = px[i - 1] * dx * (T)(1.0 / i);
+    py[i] = py[i - 1] * dy * (T)(1.0 / i);
+    pz[i] = pz[i - 1] * dz * (T)(1.0 / i);
+  }
+  const T* L = local + (int64_t)leaf * K;
+  const T* B = blocal + (int64_t)leaf * K;
+  T ax = 0, ay = 0, az = 0;
+  T hxx = 0, hyy = 0, hzz = 0, hxy = 0, hxz = 0, hyz = 0;
+  T ps = 0, gx = 0, gy = 0, gz = 0;
+  static_for<0, K>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int a = tabs<P>.a[i], b = tabs<P>.b[i], c = tabs<P>.c[i];
+    const T l = L[i], q = B[i];
+    ps += q * px[a] * py[b] * pz[c];
+    if constexpr (a > 0) {
+      ax -= l * px[a - 1] * py[b] * pz[c];
+      gx += q * px[a - 1] * py[b] * pz[c];
+    }
+    if constexpr (b > 0) {
+      ay -= l * px[a] * py[b - 1] * pz[c];
+      gy += q * px[a] * py[b - 1] * pz[c];
+    }
+    if constexpr (c > 0) {
+      az -= l * px[a] * py[b] * pz[c - 1];
+      gz += q * px[a] * py[b] * pz[c - 1];
+    }
+    if constexpr (a > 1) hxx += l * px[a - 2] * py[b] * pz[c];
+    if constexpr (b > 1) hyy += l * px[a] * py[b - 2] * pz[c];
+    if constexpr (c > 1) hzz += l * px[a] * py[b] * pz[c - 2];
+    if constexpr (a > 0 && b > 0) hxy += l * px[a - 1] * py[b - 1] * pz[c];
+    if constexpr (a > 0 && c > 0) hxz += l * px[a - 1] * py[b] * pz[c - 1];
+    if constexpr (b > 0 && c > 0) hyz += l * px[a] * py[b - 1] * pz[c - 1];
+  });
+  const T pb = r.c.x, bx = r.c.y, by = r.c.z, bz = r.c.m, m = r.p.m;
+  P4<T> o;
+  o.x = ps;
+  o.y = -pb * ax - (hxx * bx + hxy * by + hxz * bz) + m * gx;
+  o.z = -pb * ay - (hxy * bx + hyy * by + hyz * bz) + m * gy;
+  o.m = -pb * az - (hxz * bx + hyz * by + hzz * bz) + m * gz;
+  out[k] = o;
+}
+
+template <typename T>
+static void l2p_vjp_dispatch(int order, unsigned g, hipStream_t st, int64_t n, const P8<T>* rec,
+                             const int32_t* leaf_of, const double* centre, const T* local,
+                             const T* blocal, P4<T>* out) {
+  switch (order) {
+#define L2PV_CASE(P) \
+  case P:            \
+    k_l2p_vjp<T, P><<<g, 256, 0, st>>>(n, rec, leaf_of, centre, local, blocal, out); \
+    break;
+    L2PV_CASE(0) L2PV_CASE(1) L2PV_CASE(2) L2PV_CASE(3) L2PV_CASE(4)
+    L2PV_CASE(5) L2PV_CASE(6) L2PV_CASE(7) L2PV_CASE(8)
+#undef L2PV_CASE
+    default:
+      break;
+  }
+}
+
+hipError_t launch_l2p_vjp(int dtype, int order, int64_t n, const void* rec, const int32_t* leaf_of,
+                          const double* centre, const void* local, const void* blocal, void* out,
+                          hipStream_t st) {
+  unsigned g = (unsigned)((n + 255) / 256);
+  if (dtype == FMM_F64)
+    l2p_vjp_dispatch<double>(order, g, st, n, (const P8<double>*)rec, leaf_of, centre,
+                             (const double*)local, (const double*)blocal, (P4<double>*)out);
+  else
+    l2p_vjp_dispatch<float>(order, g, st, n, (const P8<float>*)rec, leaf_of, centre,
+                            (const float*)local, (const float*)blocal, (P4<float>*)out);
+  return hipGetLastError();
+}
+
 // ---------------- helpers ----------------
 __global__ void k_fill_zero(uint32_t* p, size_t n_words) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_words;

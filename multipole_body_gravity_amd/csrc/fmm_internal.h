@@ -89,6 +89,10 @@ struct fmm_plan_s {
   mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq, ngeo;
   mbg::DBuf leaves, lvl_blkcnt;
   mbg::DBuf mpole, mred, local, lfin;
+  // VJP: sensitivity records (N), far parts (N), and the sensitivity
+  // expansions (node-sized), apart from the forward's so that evals and VJPs
+  // of one build can alternate
+  mbg::DBuf vrec, vfar, vmpole, vmred, vlocal, vlfin;
   // walk: sharded pools (carry unions, M2L unions, P2P unions, transposed
   // M2L and P2P keys) and per-node slices / counts
   mbg::DBuf pool[mbg::N_POOLS];
@@ -138,9 +142,9 @@ struct fmm_plan_s {
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
   hipEvent_t kev[2 * FMM_N_KERNELS] = {};  // begin/end of single kernel launches
   bool kran[FMM_N_KERNELS] = {};          // the kernel ran in the last eval
-  bool pend_build = false, pend_eval = false;  // events recorded, not yet collected
+  bool pend_build = false, pend_eval = false, pend_vjp = false;  // events not yet collected
   double stage_sum[FMM_N_STAGES] = {0}, kernel_sum[FMM_N_KERNELS] = {0};
-  int32_t n_timed_builds = 0, n_timed_evals = 0;
+  int32_t n_timed_builds = 0, n_timed_evals = 0, n_timed_vjps = 0;
 };
 
 namespace mbg {
@@ -344,6 +348,28 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
                       void* part, bool any_multi, hipEvent_t* ev, bool* ran, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// ---- vector-Jacobian product ----
+// rec[k] = P8 (sorted particle k, pb and ab of caller index perm[k])
+hipError_t launch_vjp_gather(int dtype, int64_t n, const void* pts, const int32_t* perm,
+                             const void* pb, const void* ab, void* rec, hipStream_t st);
+// leaf moments of the monopoles pb and dipoles ab held in the records
+hipError_t launch_p2m_dip(int dtype, int order, const void* rec, const int32_t* leaves,
+                          int64_t n_leaves, const int32_t* begin, const int32_t* count,
+                          const double* centre, void* mpole, hipStream_t st);
+// far-field parts per sorted particle: (Psi, -pb a - (Hess phi) ab + m grad Psi),
+// from the forward's leaf locals and the sensitivity leaf locals
+hipError_t launch_l2p_vjp(int dtype, int order, int64_t n, const void* rec, const int32_t* leaf_of,
+                          const double* centre, const void* local, const void* blocal, void* out,
+                          hipStream_t st);
+// near field of the VJP on the forward's tasks; writes mbar [N] and xbar [N][3]
+// in the caller's order (far parts from `far`)
+hipError_t launch_p2p_vjp(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
+                          int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
+                          const int32_t* begin, const int32_t* count, const int32_t* src,
+                          const void* recs, const void* far, const int32_t* perm, void* mbar,
+                          void* xbar, void* part, bool any_multi, hipEvent_t* ev, bool* ran,
+                          hipStream_t st);
 // expansions in the plan's dtype/convention -> fp64 raw moments / derivatives
 // traceless source records for the M2L: folded moments + centre, per node
 hipError_t launch_m2l_records(int dtype, int order, int64_t n_nodes, const double* centre,

@@ -110,19 +110,58 @@ __global__ void __launch_bounds__(256)
 constexpr int TILE = 2 * WAVE;       // source particles staged per round
 constexpr int MAXQ = 2048;           // source particles per owner table
 
+// Pair interactions.  Each adds one source's contribution to the four
+// per-target sums that the task writes.
+//
+// Forward: potential and acceleration of target i from source j.
 template <typename T>
-__device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp, T& fx, T& fy,
-                                         T& fz) {
-  const T dx = pi.x - pj.x, dy = pi.y - pj.y, dz = pi.z - pj.z;
-  const T r2 = dx * dx + dy * dy + dz * dz;
-  const T rinv = p2p_rsqrt(r2);
-  const T mr = pj.m * rinv;
-  const T mr3 = mr * rinv * rinv;
-  fp -= mr;
-  fx -= mr3 * dx;
-  fy -= mr3 * dy;
-  fz -= mr3 * dz;
-}
+struct ForcePair {
+  using Rec = P4<T>;  // x, y, z, m
+  static __device__ __forceinline__ void add(const Rec& pi, const Rec& pj, T& fp, T& fx, T& fy,
+                                             T& fz) {
+    const T dx = pi.x - pj.x, dy = pi.y - pj.y, dz = pi.z - pj.z;
+    const T r2 = dx * dx + dy * dy + dz * dz;
+    const T rinv = p2p_rsqrt(r2);
+    const T mr = pj.m * rinv;
+    const T mr3 = mr * rinv * rinv;
+    fp -= mr;
+    fx -= mr3 * dx;
+    fy -= mr3 * dy;
+    fz -= mr3 * dz;
+  }
+};
+
+// VJP: the record of a particle is its position and mass, then the
+// sensitivities pb = dS/dphi and ab = dS/da of its outputs.  With r = x_i - x_j
+// the pair contributes to
+//   Psi(x_i)  = sum_j -pb_j/|r| + ab_j . r/|r|^3                 (dS/dm_i)
+//   xbar_i    = sum_j [ s r + w - 3 (r . w) r/|r|^2 ] / |r|^3,
+//   s = pb_i m_j + m_i pb_j,   w = m_i ab_j - m_j ab_i,
+// which is -pb_i a_i - (Hess Phi) ab_i + m_i grad Psi restricted to the pair:
+// the near-field part of the VJP's position gradient.
+template <typename T>
+struct VjpPair {
+  using Rec = P8<T>;
+  static __device__ __forceinline__ void add(const Rec& ti, const Rec& sj, T& ps, T& gx, T& gy,
+                                             T& gz) {
+    const T dx = ti.p.x - sj.p.x, dy = ti.p.y - sj.p.y, dz = ti.p.z - sj.p.z;
+    const T r2 = dx * dx + dy * dy + dz * dz;
+    const T rinv = p2p_rsqrt(r2);
+    const T rinv2 = rinv * rinv;
+    const T rinv3 = rinv * rinv2;
+    const T s = ti.c.x * sj.p.m + ti.p.m * sj.c.x;
+    const T wx = ti.p.m * sj.c.y - sj.p.m * ti.c.y;
+    const T wy = ti.p.m * sj.c.z - sj.p.m * ti.c.z;
+    const T wz = ti.p.m * sj.c.m - sj.p.m * ti.c.m;
+    const T rw = dx * wx + dy * wy + dz * wz;
+    const T coef = s - (T)3 * rw * rinv2;
+    gx += rinv3 * (coef * dx + wx);
+    gy += rinv3 * (coef * dy + wy);
+    gz += rinv3 * (coef * dz + wz);
+    const T ad = sj.c.y * dx + sj.c.z * dy + sj.c.m * dz;
+    ps += rinv3 * ad - sj.c.x * rinv;
+  }
+};
 
 // Lane layout for a chunk of tc <= 128 targets: each lane holds two targets
 // (2g, 2g + 1), so one source read from LDS serves two pairs.  With
@@ -131,27 +170,32 @@ __device__ __forceinline__ void pair_acc(const P4<T>& pi, const P4<T>& pj, T& fp
 // sl + ns, ...; the few remaining lanes repeat slice 0 of their pair and their
 // sums are dropped.  Sources are staged TT = ns floor(128 / ns) at a time, so
 // in every full stage each lane takes exactly TT / ns sources.
-template <typename T>
+template <typename T, typename Rec>
 struct P2PShared {
   union {
-    P4<T> tile[TILE];
+    Rec tile[TILE];
     T red[8][WAVE];
   };
   uint8_t owner[MAXQ];  // list entry (within the group of 64) of each source particle
   int32_t sbase[WAVE];  // per entry: first particle minus its first source index
 };
 
-template <typename T>
-__global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_eu(5, 8)))
-    k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
-          const int32_t* __restrict__ count, const int32_t* __restrict__ src,
-          const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
-          const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
-          T* __restrict__ part) {
-  __shared__ P2PShared<T> sh_all[P2P_WAVES];
+// The tasks of one wave.  Per target, out1[perm] = far.x + sum0 and
+// out3[3 perm + a] = far.(y, z, m)[a] + sum(a + 1); a split leaf writes its
+// four sums per task into `part` instead.
+template <typename T, class Pair>
+__device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int64_t n_tasks,
+                                          const int32_t* __restrict__ begin,
+                                          const int32_t* __restrict__ count,
+                                          const int32_t* __restrict__ src,
+                                          const typename Pair::Rec* __restrict__ pts,
+                                          const P4<T>* __restrict__ far,
+                                          const int32_t* __restrict__ perm, T* __restrict__ out1,
+                                          T* __restrict__ out3, T* __restrict__ part,
+                                          P2PShared<T, typename Pair::Rec>& sh) {
+  using Rec = typename Pair::Rec;
   const int lane = __lane_id();
   const int w = threadIdx.x / WAVE;
-  P2PShared<T>& sh = sh_all[w];
   for (int64_t ti = (int64_t)blockIdx.x * P2P_WAVES + w; ti < n_tasks;
        ti += (int64_t)gridDim.x * P2P_WAVES) {
     const P2PTask task = tasks[ti];
@@ -171,8 +215,8 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
       const int TT = ns * per;
       const int32_t i0 = tb + t0 + 2 * g;
       const bool two = 2 * g + 1 < tc;
-      const P4<T> p0 = pts[i0];
-      const P4<T> p1 = pts[two ? i0 + 1 : i0];
+      const Rec p0 = pts[i0];
+      const Rec p1 = pts[two ? i0 + 1 : i0];
       T a0 = 0, a1 = 0, a2 = 0, a3 = 0, b0 = 0, b1 = 0, b2 = 0, b3 = 0;
       bool self = false;
       for (int64_t eg = task.e0; eg < task.e1;) {
@@ -213,17 +257,17 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
           const int nv = min(TT, tot - q0);
           if (nv == TT) {
             // a full stage: the same number of sources on every lane
-            const P4<T>* sp = sh.tile + sl;
+            const Rec* sp = sh.tile + sl;
             for (int k = 0; k < per; k++) {
-              const P4<T> pj = sp[k * ns];
-              pair_acc(p0, pj, a0, a1, a2, a3);
-              pair_acc(p1, pj, b0, b1, b2, b3);
+              const Rec pj = sp[k * ns];
+              Pair::add(p0, pj, a0, a1, a2, a3);
+              Pair::add(p1, pj, b0, b1, b2, b3);
             }
           } else {
             for (int s = sl; s < nv; s += ns) {
-              const P4<T> pj = sh.tile[s];
-              pair_acc(p0, pj, a0, a1, a2, a3);
-              pair_acc(p1, pj, b0, b1, b2, b3);
+              const Rec pj = sh.tile[s];
+              Pair::add(p0, pj, a0, a1, a2, a3);
+              Pair::add(p1, pj, b0, b1, b2, b3);
             }
           }
           __builtin_amdgcn_wave_barrier();
@@ -232,9 +276,9 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
       }
       if (__ballot(self) != 0ull) {
         for (int32_t s = sl; s < tn; s += ns) {
-          const P4<T> pj = pts[tb + s];
-          if (tb + s != i0) pair_acc(p0, pj, a0, a1, a2, a3);  // self term omitted
-          if (tb + s != i0 + 1) pair_acc(p1, pj, b0, b1, b2, b3);
+          const Rec pj = pts[tb + s];
+          if (tb + s != i0) Pair::add(p0, pj, a0, a1, a2, a3);  // self term omitted
+          if (tb + s != i0 + 1) Pair::add(p1, pj, b0, b1, b2, b3);
         }
       }
       sh.red[0][lane] = a0;
@@ -260,10 +304,10 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
         if (task.part < 0) {
           const P4<T> f = far[i];
           const int64_t o = perm[i];
-          phi[o] = f.x + s0;
-          acc[3 * o] = f.y + s1;
-          acc[3 * o + 1] = f.z + s2;
-          acc[3 * o + 2] = f.m + s3;
+          out1[o] = f.x + s0;
+          out3[3 * o] = f.y + s1;
+          out3[3 * o + 1] = f.z + s2;
+          out3[3 * o + 2] = f.m + s3;
         } else {
           T* pp = part + 4 * (task.part + t0 + l);
           pp[0] = s0;
@@ -275,6 +319,32 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
       __builtin_amdgcn_wave_barrier();
     }
   }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_eu(5, 8)))
+    k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
+          const int32_t* __restrict__ count, const int32_t* __restrict__ src,
+          const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
+          const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
+          T* __restrict__ part) {
+  __shared__ P2PShared<T, P4<T>> sh_all[P2P_WAVES];
+  p2p_tasks<T, ForcePair<T>>(tasks, n_tasks, begin, count, src, pts, far, perm, phi, acc, part,
+                             sh_all[threadIdx.x / WAVE]);
+}
+
+// VJP near field: out1 = dS/dm, out3 = dS/dx, with `far` holding the far-field
+// parts of both (Psi and the position gradient) in sorted order.
+template <typename T>
+__global__ void __launch_bounds__(P2P_THREADS)
+    k_p2p_vjp(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
+              const int32_t* __restrict__ count, const int32_t* __restrict__ src,
+              const P8<T>* __restrict__ recs, const P4<T>* __restrict__ far,
+              const int32_t* __restrict__ perm, T* __restrict__ mbar, T* __restrict__ xbar,
+              T* __restrict__ part) {
+  __shared__ P2PShared<T, P8<T>> sh_all[P2P_WAVES];
+  p2p_tasks<T, VjpPair<T>>(tasks, n_tasks, begin, count, src, recs, far, perm, mbar, xbar, part,
+                           sh_all[threadIdx.x / WAVE]);
 }
 
 // Leaves split over several tasks, one block per leaf: thread (t, s) adds the
@@ -392,6 +462,44 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
       (void)hipEventRecord(ev[3], st);
       ran[1] = true;
     }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_p2p_vjp(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
+                          int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
+                          const int32_t* begin, const int32_t* count, const int32_t* src,
+                          const void* recs, const void* far, const int32_t* perm, void* mbar,
+                          void* xbar, void* part, bool any_multi, hipEvent_t* ev, bool* ran,
+                          hipStream_t st) {
+  // ev (optional): begin/end of the pair kernel
+  if (n_tasks == 0) return hipSuccess;
+  int64_t blocks = (n_tasks + P2P_WAVES - 1) / P2P_WAVES;
+  if (blocks > 65535) blocks = 65535;
+  int64_t cblocks = n_leaves < 65535 ? n_leaves : 65535;
+  if (ev) (void)hipEventRecord(ev[0], st);
+  if (dtype == FMM_F64)
+    k_p2p_vjp<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
+        (const P2PTask*)tasks, n_tasks, begin, count, src, (const P8<double>*)recs,
+        (const P4<double>*)far, perm, (double*)mbar, (double*)xbar, (double*)part);
+  else
+    k_p2p_vjp<float><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
+        (const P2PTask*)tasks, n_tasks, begin, count, src, (const P8<float>*)recs,
+        (const P4<float>*)far, perm, (float*)mbar, (float*)xbar, (float*)part);
+  if (ev) {
+    (void)hipEventRecord(ev[1], st);
+    ran[0] = true;
+  }
+  if (any_multi) {
+    // the split leaves' partials: the same ordered combine as the forward
+    if (dtype == FMM_F64)
+      k_p2p_combine<double><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
+          leaves, n_leaves, task_off, part_off, begin, count, (const double*)part,
+          (const P4<double>*)far, perm, (double*)mbar, (double*)xbar);
+    else
+      k_p2p_combine<float><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
+          leaves, n_leaves, task_off, part_off, begin, count, (const float*)part,
+          (const P4<float>*)far, perm, (float*)mbar, (float*)xbar);
   }
   return hipGetLastError();
 }

@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(HERE, "libmbg_fmm.so")
 
 FMM_F32, FMM_F64 = 0, 1
 MAX_ORDER = 8
-STAGES = ["keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p", "tail"]  # stage_ms order
-KERNELS = ["m2l_sib", "m2l_tail", "p2p", "p2p_combine"]  # fmm_stats_t.kernel_ms order
+STAGES = ["keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p", "tail", "vjp"]  # stage_ms order
+KERNELS = ["m2l_sib", "m2l_tail", "p2p", "p2p_combine", "vjp_m2l_sib", "vjp_p2p"]  # kernel_ms order
 _ERR = {0: "ok", -1: "invalid argument", -2: "plan not built", -3: "device out of memory",
         -4: "HIP runtime error", -5: "non-finite position or mass", -6: "no HIP device"}
 
@@ -36,8 +36,8 @@ class _Stats(ctypes.Structure):
                 ("order", ctypes.c_int32), ("leaf_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("theta", ctypes.c_double), ("lo", ctypes.c_double * 3), ("side", ctypes.c_double),
                 ("stage_ms", ctypes.c_float * len(STAGES)), ("walk_retries", ctypes.c_int32),
-                ("kernel_ms", ctypes.c_float * 4), ("timed_builds", ctypes.c_int32),
-                ("timed_evals", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
+                ("kernel_ms", ctypes.c_float * len(KERNELS)), ("timed_builds", ctypes.c_int32),
+                ("timed_evals", ctypes.c_int32), ("timed_vjps", ctypes.c_int32)]
 
 
 _lib = None
@@ -55,6 +55,7 @@ def load_library():
     lib.fmm_plan.argtypes = [ctypes.POINTER(P), i64, i32, dbl, i32, i32]
     lib.fmm_build.argtypes = [P, P, P, P]
     lib.fmm_eval.argtypes = [P, P, P, P]
+    lib.fmm_vjp.argtypes = [P, P, P, P, P, P]
     lib.fmm_destroy.argtypes = [P]
     lib.fmm_strerror.argtypes = [i32]
     lib.fmm_strerror.restype = ctypes.c_char_p
@@ -135,6 +136,29 @@ class Plan:
         self._check(rc, "fmm_eval")
         return phi, acc
 
+    def vjp(self, phi_bar: torch.Tensor, acc_bar: torch.Tensor, pos_bar: torch.Tensor | None = None,
+            mass_bar: torch.Tensor | None = None, stream=None):
+        """Sensitivities of S back to the built positions and masses, given
+        phi_bar = dS/dphi [N] and acc_bar = dS/da [N,3] (fmm_vjp).  Returns
+        (pos_bar [N,3], mass_bar [N])."""
+        for t, shp in ((phi_bar, (self.n,)), (acc_bar, (self.n, 3))):
+            if t.shape != shp or t.dtype != self.dtype or not t.is_cuda:
+                raise FmmError(-1, "fmm_vjp: phi_bar [N] and acc_bar [N,3] device tensors, plan dtype")
+        phi_bar, acc_bar = phi_bar.contiguous(), acc_bar.contiguous()
+        if pos_bar is None:
+            pos_bar = torch.empty(self.n, 3, dtype=self.dtype, device=self.device)
+        if mass_bar is None:
+            mass_bar = torch.empty(self.n, dtype=self.dtype, device=self.device)
+        if pos_bar.shape != (self.n, 3) or mass_bar.shape != (self.n,) or not pos_bar.is_contiguous() \
+                or not mass_bar.is_contiguous() or pos_bar.dtype != self.dtype or mass_bar.dtype != self.dtype:
+            raise FmmError(-1, "fmm_vjp: pos_bar [N,3] and mass_bar [N] contiguous, plan dtype")
+        with torch.cuda.device(self.device):
+            rc = self.lib.fmm_vjp(self._h, ctypes.c_void_p(phi_bar.data_ptr()),
+                                  ctypes.c_void_p(acc_bar.data_ptr()), ctypes.c_void_p(pos_bar.data_ptr()),
+                                  ctypes.c_void_p(mass_bar.data_ptr()), _stream_handle(stream))
+        self._check(rc, "fmm_vjp")
+        return pos_bar, mass_bar
+
     def set_timing(self, enable: bool = True) -> None:
         self._check(self.lib.fmm_set_timing(self._h, 1 if enable else 0), "fmm_set_timing")
 
@@ -146,7 +170,8 @@ class Plan:
                 "theta": s.theta, "lo": list(s.lo), "side": s.side, "walk_retries": s.walk_retries,
                 "stage_ms": {k: float(v) for k, v in zip(STAGES, s.stage_ms)},
                 "kernel_ms": {k: float(v) for k, v in zip(KERNELS, s.kernel_ms)},
-                "timed_builds": s.timed_builds, "timed_evals": s.timed_evals}
+                "timed_builds": s.timed_builds, "timed_evals": s.timed_evals,
+                "timed_vjps": s.timed_vjps}
 
     def copy_keys(self):
         keys = np.zeros(self.n, dtype=np.uint64)

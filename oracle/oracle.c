@@ -1100,7 +1100,8 @@ int oracle_fmm(int64_t n, const double* pos, const double* mass, int order, doub
  * the last ones "an FMM with the force sensitivities acting as dipole
  * moments": the same tree, lists and translations, with the moments of the
  * monopoles and dipoles.  Every sum runs over the same near and far split as
- * the forward.  Requires a full (not sampled) numeric result. */
+ * the forward.  In sampled mode only the marked leaves are targets (the
+ * others get NaN), exactly as in the forward. */
 static int fmm_vjp_on(const oracle_result* r, const double* pb, const double* ab,
                       double* xbar, double* mbar) {
   const int64_t n = r->n, nn = r->n_nodes;
@@ -1165,6 +1166,7 @@ static int fmm_vjp_on(const oracle_result* r, const double* pb, const double* ab
 #pragma omp parallel for schedule(dynamic, 64)
     for (int64_t i = 0; i < nn; i++) {
       if (r->level[i] != lev) continue;
+      if (r->mark && !r->mark[i]) continue;
       int64_t pa = r->parent[i];
       double d[3] = {r->centre[3 * i] - r->centre[3 * pa],
                      r->centre[3 * i + 1] - r->centre[3 * pa + 1],
@@ -1176,7 +1178,7 @@ static int fmm_vjp_on(const oracle_result* r, const double* pb, const double* ab
    * -grad Psi from the sensitivity locals */
 #pragma omp parallel for schedule(dynamic, 64)
   for (int64_t i = 0; i < nn; i++) {
-    if (r->n_child[i] != 0) continue;
+    if (r->n_child[i] != 0 || (r->mark && !r->mark[i])) continue;
     for (int32_t k = r->begin[i]; k < r->begin[i] + r->count[i]; k++) {
       double dx[3] = {r->xs[3 * k] - r->centre[3 * i], r->xs[3 * k + 1] - r->centre[3 * i + 1],
                       r->xs[3 * k + 2] - r->centre[3 * i + 2]};
@@ -1187,7 +1189,7 @@ static int fmm_vjp_on(const oracle_result* r, const double* pb, const double* ab
   /* near field, self term omitted by index */
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t a = 0; a < nn; a++) {
-    if (r->n_child[a] != 0) continue;
+    if (r->n_child[a] != 0 || (r->mark && !r->mark[a])) continue;
     for (int32_t i = r->begin[a]; i < r->begin[a] + r->count[a]; i++) {
       double h[6] = {0, 0, 0, 0, 0, 0}, ps = 0.0, gp[3] = {0, 0, 0};
       for (int64_t e = r->p2p_off[a]; e < r->p2p_off[a + 1]; e++) {
@@ -1230,6 +1232,16 @@ static int fmm_vjp_on(const oracle_result* r, const double* pb, const double* ab
       xbar[3 * i + a] = -pbs[k] * r->acc[3 * i + a] - hb[a] - r->ms[k] * mg[3 * k + a];
     mbar[i] = psi[k];
   }
+  if (r->mark) {
+    for (int64_t i = 0; i < nn; i++) {
+      if (r->n_child[i] != 0 || r->mark[i]) continue;
+      for (int32_t k = r->begin[i]; k < r->begin[i] + r->count[i]; k++) {
+        int64_t q = r->perm[k];
+        mbar[q] = NAN;
+        xbar[3 * q] = xbar[3 * q + 1] = xbar[3 * q + 2] = NAN;
+      }
+    }
+  }
   free(pbs);
   free(abs_);
   free(Mb);
@@ -1241,14 +1253,14 @@ static int fmm_vjp_on(const oracle_result* r, const double* pb, const double* ab
 }
 
 int oracle_fmm_vjp(int64_t n, const double* pos, const double* mass, int order, double theta,
-                   int leaf_size, const double* pb, const double* ab, double* xbar,
-                   double* mbar) {
+                   int leaf_size, int64_t n_sample, const int64_t* sample, const double* pb,
+                   const double* ab, double* xbar, double* mbar) {
   for (int64_t i = 0; i < n; i++)
     if (!isfinite(pb[i]) || !isfinite(ab[3 * i]) || !isfinite(ab[3 * i + 1]) ||
         !isfinite(ab[3 * i + 2]))
       return ORACLE_ERR_NONFINITE;
   oracle_result* r = NULL;
-  int rc = oracle_fmm(n, pos, mass, order, theta, leaf_size, 0, NULL, 1, &r);
+  int rc = oracle_fmm(n, pos, mass, order, theta, leaf_size, n_sample, sample, 1, &r);
   if (rc) return rc;
   rc = fmm_vjp_on(r, pb, ab, xbar, mbar);
   oracle_free(r);

@@ -96,12 +96,13 @@ int oracle_morton(int64_t n, const double* pos, double* lo, double* side,
  * ab [n][3], caller's order): xbar [n][3] = dS/dpos, mbar [n] = dS/dmass.
  * oracle_direct_vjp is the exact gradient of the direct sum (O(N^2));
  * oracle_fmm_vjp is the fast multipole form of the jz-fmm page on the tree and
- * lists of oracle_fmm with the same order, theta and leaf size. */
+ * lists of oracle_fmm with the same order, theta and leaf size (and the same
+ * sampled mode: n_sample > 0 restricts the targets, NaN elsewhere). */
 int oracle_direct_vjp(int64_t n, const double* pos, const double* mass,
                       const double* pb, const double* ab, double* xbar, double* mbar);
 int oracle_fmm_vjp(int64_t n, const double* pos, const double* mass, int order,
-                   double theta, int leaf_size, const double* pb, const double* ab,
-                   double* xbar, double* mbar);
+                   double theta, int leaf_size, int64_t n_sample, const int64_t* sample,
+                   const double* pb, const double* ab, double* xbar, double* mbar);
 /* Moments of monopoles q [n] and point dipoles dip [n][3] about centre. */
 int oracle_p2m_dipole(int order, int64_t n, const double* pos, const double* q,
                       const double* dip, const double* centre, double* mpole);

@@ -74,7 +74,7 @@ def _load():
     lib.oracle_l2p.argtypes = [i32, P, P, P, P]
     lib.oracle_morton.argtypes = [i64, P, P, P, P]
     lib.oracle_direct_vjp.argtypes = [i64, P, P, P, P, P, P]
-    lib.oracle_fmm_vjp.argtypes = [i64, P, P, i32, dbl, i32, P, P, P, P]
+    lib.oracle_fmm_vjp.argtypes = [i64, P, P, i32, dbl, i32, i64, P, P, P, P, P]
     lib.oracle_p2m_dipole.argtypes = [i32, i64, P, P, P, P, P]
     lib.oracle_l2p_hessian.argtypes = [i32, P, P, P]
     _lib = lib
@@ -309,8 +309,9 @@ def direct_vjp(pos, mass, phi_bar, acc_bar):
     return xbar, mbar
 
 
-def fmm_vjp(pos, mass, phi_bar, acc_bar, order=4, theta=0.7, leaf_size=32):
-    """Fast multipole VJP on the oracle's own tree and lists: (xbar[n,3], mbar[n])."""
+def fmm_vjp(pos, mass, phi_bar, acc_bar, order=4, theta=0.7, leaf_size=32, sample=None):
+    """Fast multipole VJP on the oracle's own tree and lists: (xbar[n,3], mbar[n]).
+    `sample` restricts the targets to the leaves holding those particles (NaN elsewhere)."""
     lib = _load()
     pos = _f64(pos, (-1, 3))
     mass = _f64(mass)
@@ -319,7 +320,9 @@ def fmm_vjp(pos, mass, phi_bar, acc_bar, order=4, theta=0.7, leaf_size=32):
     n = pos.shape[0]
     xbar = np.zeros((n, 3))
     mbar = np.zeros(n)
+    smp = np.zeros(0, dtype=np.int64) if sample is None else np.ascontiguousarray(sample, dtype=np.int64)
     rc = lib.oracle_fmm_vjp(n, _p(pos), _p(mass), int(order), float(theta), int(leaf_size),
+                            smp.shape[0], _p(smp) if smp.shape[0] else None,
                             _p(pb), _p(ab), _p(xbar), _p(mbar))
     if rc:
         raise OracleError(rc)

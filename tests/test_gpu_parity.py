@@ -304,6 +304,155 @@ def test_direct_matches_oracle(orc, dt):
     assert ea.max() <= tol and ep.max() <= tol, (ea.max(), ep.max())
 
 
+# --------------------------------------------------------------------------
+# VJP (fmm_vjp) against the oracle's fast multipole VJP on the same tree and
+# lists: dS/dpos and dS/dmass per particle, same tolerances as the forward
+# --------------------------------------------------------------------------
+
+def sensitivities(n, seed, dt):
+    rng = np.random.default_rng(seed)
+    pb = rng.standard_normal(n)
+    ab = rng.standard_normal((n, 3))
+    if dt == "f32":  # the oracle sees exactly the values the GPU gets
+        pb = pb.astype(np.float32).astype(np.float64)
+        ab = ab.astype(np.float32).astype(np.float64)
+    return pb, ab
+
+
+def gpu_vjp(plan, pb, ab, dt):
+    torch = _torch()
+    tdt = torch.float64 if dt == "f64" else torch.float32
+    dev = torch.device("cuda:0")
+    xb, mb = plan.vjp(torch.from_numpy(pb).to(dev, tdt), torch.from_numpy(ab).to(dev, tdt))
+    torch.cuda.synchronize()
+    return xb.double().cpu().numpy(), mb.double().cpu().numpy()
+
+
+def abs_scales(pos, mass, pb, ab, idx):
+    """Per target, the sums of the absolute values of the pair terms of
+    dS/dmass (|pb_j|/r + |ab_j . r|/r^3) and of dS/dpos (|s|/r^2 + 4 |w|/r^3,
+    s = pb_i m_j + m_i pb_j, w = m_i ab_j - m_j ab_i), by brute force."""
+    am = np.zeros(idx.size)
+    ax = np.zeros(idx.size)
+    step = max(1, int(2e7 // pos.shape[0]))
+    for c0 in range(0, idx.size, step):
+        t = idx[c0:c0 + step]
+        d = pos[t, None, :] - pos[None, :, :]
+        r = np.sqrt((d ** 2).sum(-1))
+        r[np.arange(t.size), t] = np.inf  # self term omitted
+        am[c0:c0 + step] = (np.abs(pb)[None, :] / r + np.abs((ab[None] * d).sum(-1)) / r ** 3).sum(1)
+        sabs = np.abs(pb[t, None] * mass[None, :] + mass[t, None] * pb[None, :])
+        w = mass[t, None, None] * ab[None] - mass[None, :, None] * ab[t, None, :]
+        ax[c0:c0 + step] = (sabs / r ** 2 + 4.0 * np.linalg.norm(w, axis=-1) / r ** 3).sum(1)
+    return ax, am
+
+
+def check_vjp(xb, mb, rx, rm, dt, idx=None, inputs=None):
+    """The sensitivities have both signs, so dS/dmass and dS/dpos are sums with
+    cancellation: their rounding error scales with the sum of the absolute pair
+    terms A_i >= |result_i|, not with the result.  The bar is the forward's
+    tolerance relative to A_i (which is the plain relative error where the
+    terms do not cancel); A_i is formed, by brute force, only for the
+    particles whose plain relative error is above the bar."""
+    if idx is None:
+        idx = np.arange(mb.shape[0])
+    tol = TOL[dt]
+    dx = np.linalg.norm(xb[idx] - rx[idx], axis=-1)
+    dm = np.abs(mb[idx] - rm[idx])
+    ex = dx / np.linalg.norm(rx[idx], axis=-1)
+    em = dm / np.abs(rm[idx])
+    bad = ~((ex <= tol) & (em <= tol))
+    say(f"    max rel err pos_bar {ex.max():.3g} mass_bar {em.max():.3g}; {int(bad.sum())} above {tol:g}")
+    if bad.any():
+        pos, mass, pb, ab = inputs
+        ax, am = abs_scales(pos, mass, pb, ab, idx[bad])
+        ex_a, em_a = dx[bad] / ax, dm[bad] / am
+        say(f"    of those, max err / sum|terms| pos_bar {ex_a.max():.3g} mass_bar {em_a.max():.3g}")
+        assert ex_a.max() <= tol, f"pos_bar err {ex_a.max():.3g}"
+        assert em_a.max() <= tol, f"mass_bar err {em_a.max():.3g}"
+
+
+VJP_CASES = [
+    # dist, n, seed, order, theta, leaf, dtype
+    ("uniform", 4096, 1001, 4, 0.7, 32, "f64"),
+    ("plummer", 10000, 1002, 5, 0.7, 32, "f64"),
+    ("clustered", 20000, 31, 4, 0.7, 32, "f32"),
+    ("plummer", 6000, 32, 6, 0.5, 16, "f64"),
+    ("uniform", 1037, 33, 3, 0.6, 7, "f64"),
+    ("plummer", 777, 34, 2, 0.4, 1, "f64"),
+    ("uniform", 3000, 36, 0, 0.7, 20, "f64"),
+    ("plummer", 3000, 37, 8, 0.5, 40, "f64"),
+    ("plummer", 3000, 37, 8, 0.5, 40, "f32"),
+]
+
+
+@pytest.mark.parametrize("dist,n,seed,order,theta,leaf,dt", VJP_CASES)
+def test_vjp_parity(orc, dist, n, seed, order, theta, leaf, dt):
+    say(f"  vjp case {dist} n={n} p={order} theta={theta} leaf={leaf} {dt}")
+    pos, mass = inputs(dist, n, seed, dt)
+    pb, ab = sensitivities(n, seed + 100, dt)
+    plan, _, _ = gpu_run(pos, mass, order, theta, leaf, dt)
+    xb, mb = gpu_vjp(plan, pb, ab, dt)
+    rx, rm = orc.fmm_vjp(pos, mass, pb, ab, order, theta, leaf)
+    check_vjp(xb, mb, rx, rm, dt, inputs=(pos, mass, pb, ab))
+    plan.close()
+
+
+def test_vjp_repeatable(orc):
+    """A VJP right after the build (no eval) equals one after an eval bit for
+    bit, a repeated VJP too, and an eval after a VJP still gives the forward's
+    results bit for bit."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    dev = torch.device("cuda:0")
+    pos, mass = W.make("clustered", 30000, 91)
+    pb, ab = sensitivities(30000, 92, "f64")
+    tp, tm = torch.from_numpy(pos).to(dev), torch.from_numpy(mass).to(dev)
+    tpb, tab = torch.from_numpy(pb).to(dev), torch.from_numpy(ab).to(dev)
+    plan = Plan(30000, order=4, theta=0.6, leaf_size=24, dtype=torch.float64, device=dev)
+    plan.build(tp, tm)
+    x0, m0 = (t.clone() for t in plan.vjp(tpb, tab))
+    phi1, acc1 = (t.clone() for t in plan.eval())
+    x1, m1 = (t.clone() for t in plan.vjp(tpb, tab))
+    x2, m2 = plan.vjp(tpb, tab)
+    phi2, acc2 = plan.eval()
+    torch.cuda.synchronize()
+    assert torch.equal(x0, x1) and torch.equal(m0, m1)
+    assert torch.equal(x1, x2) and torch.equal(m1, m2)
+    assert torch.equal(phi1, phi2) and torch.equal(acc1, acc2)
+    rx, rm = orc.fmm_vjp(pos, mass, pb, ab, 4, 0.6, 24)
+    check_vjp(x2.cpu().numpy(), m2.cpu().numpy(), rx, rm, "f64", inputs=(pos, mass, pb, ab))
+    plan.close()
+
+
+@pytest.mark.timeout(300)
+def test_vjp_parity_1e5(orc):
+    c = W.CONFIGS["plummer_1e5"]
+    pos, mass = inputs(c["dist"], c["n"], c["seed"], c["dtype"])
+    pb, ab = sensitivities(c["n"], 93, c["dtype"])
+    plan, _, _ = gpu_run(pos, mass, c["order"], c["theta"], c["leaf"], c["dtype"])
+    xb, mb = gpu_vjp(plan, pb, ab, c["dtype"])
+    rx, rm = orc.fmm_vjp(pos, mass, pb, ab, c["order"], c["theta"], c["leaf"])
+    check_vjp(xb, mb, rx, rm, c["dtype"], inputs=(pos, mass, pb, ab))
+    plan.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,n_sample", [("clustered_1e6_p4", 256), ("clustered_1e6_f32", 256)])
+def test_vjp_1e6_sampled(orc, name, n_sample):
+    """The VJP at the 10^6-particle clustered workload, in the launch
+    configuration the benchmark times, on the leaves of a seeded sample."""
+    c = W.CONFIGS[name]
+    pos, mass = inputs(c["dist"], c["n"], c["seed"], c["dtype"])
+    pb, ab = sensitivities(c["n"], 94, c["dtype"])
+    plan, _, _ = gpu_run(pos, mass, c["order"], c["theta"], c["leaf"], c["dtype"])
+    xb, mb = gpu_vjp(plan, pb, ab, c["dtype"])
+    smp = np.random.default_rng(95).choice(c["n"], n_sample, replace=False)
+    rx, rm = orc.fmm_vjp(pos, mass, pb, ab, c["order"], c["theta"], c["leaf"], sample=smp)
+    check_vjp(xb, mb, rx, rm, c["dtype"], idx=smp, inputs=(pos, mass, pb, ab))
+    plan.close()
+
+
 def test_streams_and_timing(orc):
     """Build on one stream and evaluate on another (the plan's second stream is
     ordered against both); with timing on, every stage and kernel is counted
@@ -312,7 +461,9 @@ def test_streams_and_timing(orc):
     from multipole_body_gravity_amd import Plan
     dev = torch.device("cuda:0")
     pos, mass = W.make("plummer", 30000, 71)
+    pb, ab = sensitivities(30000, 72, "f64")
     tp, tm = torch.from_numpy(pos).to(dev), torch.from_numpy(mass).to(dev)
+    tpb, tab = torch.from_numpy(pb).to(dev), torch.from_numpy(ab).to(dev)
     plan = Plan(30000, order=4, theta=0.7, leaf_size=16, dtype=torch.float64, device=dev)
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     s1.wait_stream(torch.cuda.current_stream())  # the inputs were copied on the default stream
@@ -324,15 +475,19 @@ def test_streams_and_timing(orc):
         s2.wait_stream(s1)
         with torch.cuda.stream(s2):
             phi, acc = plan.eval(stream=s2)
+            xb, mb = plan.vjp(tpb, tab, stream=s2)
     torch.cuda.synchronize()
     st = plan.stats()
     assert st["timed_builds"] == steps and st["timed_evals"] == steps, st
+    assert st["timed_vjps"] == steps, st
     for k, v in st["stage_ms"].items():
         assert v >= 0.0, (k, st["stage_ms"])
-    for k in ("keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p"):
+    for k in ("keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p", "vjp"):
         assert st["stage_ms"][k] > 0.0, (k, st["stage_ms"])
-    for k in ("m2l_sib", "m2l_tail", "p2p"):
+    for k in ("m2l_sib", "m2l_tail", "p2p", "vjp_m2l_sib", "vjp_p2p"):
         assert st["kernel_ms"][k] > 0.0, (k, st["kernel_ms"])
     ref = orc.fmm(pos, mass, 4, 0.7, 16)
     check_values(phi.cpu().numpy(), acc.cpu().numpy(), ref, "f64")
+    rx, rm = orc.fmm_vjp(pos, mass, pb, ab, 4, 0.7, 16)
+    check_vjp(xb.cpu().numpy(), mb.cpu().numpy(), rx, rm, "f64", inputs=(pos, mass, pb, ab))
     plan.close()

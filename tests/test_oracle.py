@@ -674,3 +674,13 @@ def test_fmm_vjp_converges_with_order(orc):
     assert all(b < 0.5 * a for a, b in zip(e_x, e_x[1:])), e_x
     assert all(b < 0.5 * a for a, b in zip(e_m, e_m[1:])), e_m
     assert e_x[-1] < 1e-3 and e_m[-1] < 1e-5, (e_x, e_m)
+
+
+def test_fmm_vjp_sampled_equals_full(orc):
+    pos, mass, pb, ab = _vjp_case(4000, 23)
+    xf, mf = orc.fmm_vjp(pos, mass, pb, ab, order=4, theta=0.6, leaf_size=16)
+    smp = np.array([0, 17, 999, 2500, 3999])
+    xs, ms = orc.fmm_vjp(pos, mass, pb, ab, order=4, theta=0.6, leaf_size=16, sample=smp)
+    ok = ~np.isnan(ms)
+    assert ok[smp].all() and (~ok).sum() > 0
+    assert np.array_equal(xs[ok], xf[ok]) and np.array_equal(ms[ok], mf[ok])
