@@ -7,6 +7,7 @@ theta 0.7, leaf 32, inputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --sweep [--sweep-n N] [--sweep-orders 2,4,6,8] [--sweep-thetas ...]
+    python bench.py --vjp [--steps K] [--warmup W]   (forward + VJP steps, same workload)
 """
 from __future__ import annotations
 
@@ -69,6 +70,9 @@ def m2l_flops_per_pair_plain(p: int) -> int:
 
 
 P2P_FLOPS_PER_PAIR = 19  # 3 sub, |r|^2 5, rsqrt 1, 3 mul, 1 add, 3 FMA (6)
+# VJP pair: 3 sub, |r|^2 5, rsqrt 1, 1/r^2 and 1/r^3 2, s 3, w 9, r.w 5,
+# coefficient 3, coef r + w 6, accumulate 6, ab_j . r 5, Psi 4
+P2P_VJP_FLOPS_PER_PAIR = 52
 
 
 def roofline_obj(flops_per_launch, ms, dtype_peak, traffic=None):
@@ -192,6 +196,116 @@ def sweep(args):
             torch.cuda.empty_cache()
 
 
+def work_counts(plan, n):
+    """Near-field particle pairs and own / transposed M2L entries of the built plan."""
+    st = plan.stats()
+    lists = plan.copy_lists()
+    tree = plan.copy_tree()
+    cnt = tree["count"].astype(np.int64)
+    tgt = np.repeat(np.arange(st["n_nodes"]), np.diff(lists["p2p_off"]))
+    p2p_pairs = int(np.sum(cnt[tgt] * cnt[lists["p2p_src"]]) - n)  # minus self terms
+    # own M2L entries (source at the target's level or coarser: the sibling kernel)
+    # and transposed ones (deeper sources: the tail kernel)
+    lvl = tree["level"].astype(np.int64)
+    mt = np.repeat(np.arange(st["n_nodes"]), np.diff(lists["m2l_off"]))
+    n_m2l_tr = int(np.sum(lvl[lists["m2l_src"]] > lvl[mt]))
+    return st, p2p_pairs, st["n_m2l"] - n_m2l_tr, n_m2l_tr
+
+
+def vjp_bench(args):
+    """Forward and backward on the headline workload: a step is fmm_build +
+    fmm_eval + fmm_vjp (the VJP with seeded standard-normal sensitivities), K
+    timed steps after W warm-up steps, HIP events around every stage and main
+    kernel of each step (collected at the next build's first synchronization,
+    so the loop carries no extra synchronization).  One JSON line."""
+    import torch
+
+    from multipole_body_gravity_amd import Plan, workloads
+    cfg = workloads.CONFIGS[args.workload]
+    n = cfg["n"]
+    pos, mass = workloads.make(cfg["dist"], n, cfg["seed"])
+    rng = np.random.default_rng(2024)
+    pb = rng.standard_normal(n)
+    ab = rng.standard_normal((n, 3))
+    tdt = torch.float64 if cfg["dtype"] == "f64" else torch.float32
+    dev = torch.device("cuda:0")
+    tpos, tmass = torch.from_numpy(pos).to(dev, tdt), torch.from_numpy(mass).to(dev, tdt)
+    tpb, tab = torch.from_numpy(pb).to(dev, tdt), torch.from_numpy(ab).to(dev, tdt)
+    plan = Plan(n, order=cfg["order"], theta=cfg["theta"], leaf_size=cfg["leaf"], dtype=tdt,
+                device=dev)
+    phi = torch.empty(n, dtype=tdt, device=dev)
+    acc = torch.empty(n, 3, dtype=tdt, device=dev)
+    xb = torch.empty(n, 3, dtype=tdt, device=dev)
+    mb = torch.empty(n, dtype=tdt, device=dev)
+    for _ in range(args.warmup):
+        plan.build(tpos, tmass)
+        plan.eval(phi, acc)
+        plan.vjp(tpb, tab, xb, mb)
+    torch.cuda.synchronize()
+    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
+
+    plan.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        plan.build(tpos, tmass)
+        plan.eval(phi, acc)
+        plan.vjp(tpb, tab, xb, mb)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s = plan.stats()
+    assert s["timed_vjps"] == args.steps and s["timed_evals"] == args.steps, s
+    kern = s["kernel_ms"]
+
+    fpp = m2l_flops_per_pair(cfg["order"])
+    peak = FP64_VECTOR_PEAK_TFLOPS if cfg["dtype"] == "f64" else FP32_VECTOR_PEAK_TFLOPS
+    flops = {"vjp_p2p": p2p_pairs * P2P_VJP_FLOPS_PER_PAIR, "vjp_m2l_sib": n_m2l_own * fpp,
+             "p2p": p2p_pairs * P2P_FLOPS_PER_PAIR, "m2l_sib": n_m2l_own * fpp,
+             "m2l_tail": n_m2l_tr * fpp}
+    rl = {k: roofline_obj(f, kern[k], peak) for k, f in flops.items() if kern[k] > 0}
+    dominant = max(rl, key=lambda k: kern[k])
+    roof = dict(rl[dominant])
+    roof["kernel"] = dominant
+    out = {
+        "metric": "FMM forward + VJP step particles/s at N=10^6 fp64 order 4",
+        "value": round(n * args.steps / wall, 1),
+        "unit": "particles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_vjp": round(s["stage_ms"]["vjp"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "distribution": cfg["dist"], "n": n,
+                   "order": cfg["order"], "theta": cfg["theta"], "leaf_size": cfg["leaf"],
+                   "seed": cfg["seed"], "sensitivities": "standard normal, seed 2024"},
+        "roofline": roof,
+        "roofline_other": {k: v for k, v in rl.items() if k != dominant},
+        "stage_ms": {k: round(v, 4) for k, v in s["stage_ms"].items()},
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "work": {"p2p_pairs": p2p_pairs, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,
+                 "p2p_vjp_flops_per_pair": P2P_VJP_FLOPS_PER_PAIR,
+                 "p2p_flops_per_pair": P2P_FLOPS_PER_PAIR, "m2l_flops_per_pair": fpp},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        cores = len(os.sched_getaffinity(0))
+        orc.set_threads(cores)
+        t2 = time.perf_counter()
+        orc.fmm_vjp(pos, mass, pb, ab, cfg["order"], cfg["theta"], cfg["leaf"])
+        dt = time.perf_counter() - t2
+        out["cpu_baseline"] = {"value": round(n / dt, 1), "unit": "particles/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"the full workload ({n} particles, one oracle forward "
+                                         f"and VJP, {dt:.1f} s)"}
+    plan.close()
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +321,8 @@ def main():
     ap.add_argument("--sweep-orders", default="2,4,6,8")
     ap.add_argument("--sweep-thetas", default="0.4,0.5,0.6,0.7")
     ap.add_argument("--sweep-targets", type=int, default=2048)
+    ap.add_argument("--vjp", action="store_true",
+                    help="time forward + VJP steps (build, eval, fmm_vjp) instead of the forward step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
@@ -220,6 +336,9 @@ def main():
         if args.steps == ap.get_default("steps"):
             args.steps = 3
         sweep(args)
+        return
+    if args.vjp:
+        vjp_bench(args)
         return
 
     import torch
@@ -243,20 +362,8 @@ def main():
     torch.cuda.synchronize()
 
     # work counts of this workload (outside the timed region)
-    st = plan.stats()
-    lists = plan.copy_lists()
-    tree = plan.copy_tree()
-    cnt = tree["count"].astype(np.int64)
-    tgt = np.repeat(np.arange(st["n_nodes"]), np.diff(lists["p2p_off"]))
-    p2p_pairs = int(np.sum(cnt[tgt] * cnt[lists["p2p_src"]]) - cfg["n"])  # minus self terms
+    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, cfg["n"])
     n_m2l = st["n_m2l"]
-    # own M2L entries (source at the target's level or coarser: the sibling kernel)
-    # and transposed ones (deeper sources: the tail kernel)
-    lvl = tree["level"].astype(np.int64)
-    mt = np.repeat(np.arange(st["n_nodes"]), np.diff(lists["m2l_off"]))
-    n_m2l_tr = int(np.sum(lvl[lists["m2l_src"]] > lvl[mt]))
-    n_m2l_own = n_m2l - n_m2l_tr
-    del lists, tgt, mt
 
     # HIP events around every stage and main kernel of each step, on the launch
     # stream; the library reads them at the synchronizations a build makes
@@ -305,8 +412,8 @@ def main():
                    "seed": cfg["seed"]},
         "roofline": roof,
         "roofline_other": {k: v for k, v in rl.items() if k != dominant},
-        "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()},
-        "kernel_ms": {k: round(v, 4) for k, v in kern_avg.items()},
+        "stage_ms": {k: round(v, 4) for k, v in stage_avg.items() if k != "vjp"},
+        "kernel_ms": {k: round(v, 4) for k, v in kern_avg.items() if not k.startswith("vjp")},
         "work": {"n_m2l": n_m2l, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,
                  "p2p_pairs": p2p_pairs, "n_nodes": st["n_nodes"],
                  "n_leaves": st["n_leaves"], "depth": st["depth"],
