@@ -785,6 +785,65 @@ __global__ void __launch_bounds__(EX_THREADS)
   }
 }
 
+// The same moments for orders <= 5, one thread per leaf, all in registers.
+template <typename T, int P>
+__global__ void __launch_bounds__(256)
+    k_p2m_dip_reg(const P8<T>* rec, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
+                  const int32_t* count, const double* centre, T* mpole) {
+  constexpr int K = Tabs<P>::K;
+  const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (li >= n_leaves) return;
+  const int32_t node = leaves[li];
+  const double cx = centre[3 * node], cy = centre[3 * node + 1], cz = centre[3 * node + 2];
+  double acc[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) acc[k] = 0.0;
+  const int32_t j0 = begin[node], j1 = j0 + count[node];
+  for (int32_t j = j0; j < j1; j++) {
+    const P8<T> r = rec[j];
+    const double sx = cx - (double)r.p.x, sy = cy - (double)r.p.y, sz = cz - (double)r.p.z;  // -s
+    const double q = (double)r.c.x, bx = (double)r.c.y, by = (double)r.c.z, bz = (double)r.c.m;
+    double px[P + 1], py[P + 1], pz[P + 1];
+    px[0] = py[0] = pz[0] = 1.0;
+#pragma unroll
+    for (int t = 1; t <= P; t++) {
+      px[t] = px[t - 1] * sx * (1.0 / t);
+      py[t] = py[t - 1] * sy * (1.0 / t);
+      pz[t] = pz[t - 1] * sz * (1.0 / t);
+    }
+    static_for<0, K>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int a = tabs<P>.a[k], b = tabs<P>.b[k], c = tabs<P>.c[k];
+      double v = q * px[a] * py[b] * pz[c];
+      if constexpr (a > 0) v += bx * px[a - 1] * py[b] * pz[c];
+      if constexpr (b > 0) v += by * px[a] * py[b - 1] * pz[c];
+      if constexpr (c > 0) v += bz * px[a] * py[b] * pz[c - 1];
+      acc[k] += v;
+    });
+  }
+  T* out = mpole + (int64_t)node * K;
+#pragma unroll
+  for (int k = 0; k < K; k++) out[k] = (T)acc[k];
+}
+
+template <typename T>
+static bool p2m_dip_reg_dispatch(int order, const void* rec, const int32_t* leaves,
+                                 int64_t n_leaves, const int32_t* begin, const int32_t* count,
+                                 const double* centre, void* mpole, hipStream_t st) {
+  unsigned g = (unsigned)((n_leaves + 255) / 256);
+  switch (order) {
+#define P2MDR(P)                                                                          \
+  case P:                                                                                 \
+    k_p2m_dip_reg<T, P><<<g, 256, 0, st>>>((const P8<T>*)rec, leaves, n_leaves, begin, count, \
+                                           centre, (T*)mpole);                            \
+    return true;
+    P2MDR(0) P2MDR(1) P2MDR(2) P2MDR(3) P2MDR(4) P2MDR(5)
+#undef P2MDR
+    default:
+      return false;
+  }
+}
+
 hipError_t launch_p2m_dip(int dtype, int order, const void* rec, const int32_t* leaves,
                           int64_t n_leaves, const int32_t* begin, const int32_t* count,
                           const double* centre, void* mpole, hipStream_t st) {
@@ -792,6 +851,11 @@ hipError_t launch_p2m_dip(int dtype, int order, const void* rec, const int32_t* 
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
   if (n_leaves == 0) return hipSuccess;
+  if (dtype == FMM_F64 ? p2m_dip_reg_dispatch<double>(order, rec, leaves, n_leaves, begin, count,
+                                                      centre, mpole, st)
+                       : p2m_dip_reg_dispatch<float>(order, rec, leaves, n_leaves, begin, count,
+                                                     centre, mpole, st))
+    return hipGetLastError();
   int64_t blocks = std::min<int64_t>((n_leaves + EX_WAVES - 1) / EX_WAVES, 65535);
   if (dtype == FMM_F64)
     k_p2m_dip<double><<<(unsigned)blocks, EX_THREADS, 0, st>>>(

@@ -108,7 +108,6 @@ __global__ void __launch_bounds__(256)
 
 // ---- near-field sums ----
 constexpr int TILE = 2 * WAVE;       // source particles staged per round
-constexpr int MAXQ = 2048;           // source particles per owner table
 
 // Pair interactions.  Each adds one source's contribution to the four
 // per-target sums that the task writes.
@@ -117,6 +116,7 @@ constexpr int MAXQ = 2048;           // source particles per owner table
 template <typename T>
 struct ForcePair {
   using Rec = P4<T>;  // x, y, z, m
+  static constexpr int MAXQ = 2048;  // source particles per owner table
   static __device__ __forceinline__ void add(const Rec& pi, const Rec& pj, T& fp, T& fx, T& fy,
                                              T& fz) {
     const T dx = pi.x - pj.x, dy = pi.y - pj.y, dz = pi.z - pj.z;
@@ -142,6 +142,9 @@ struct ForcePair {
 template <typename T>
 struct VjpPair {
   using Rec = P8<T>;
+  // a smaller owner table keeps a block of four waves under 40 KB of LDS,
+  // so that four blocks fit a compute unit
+  static constexpr int MAXQ = 1024;
   static __device__ __forceinline__ void add(const Rec& ti, const Rec& sj, T& ps, T& gx, T& gy,
                                              T& gz) {
     const T dx = ti.p.x - sj.p.x, dy = ti.p.y - sj.p.y, dz = ti.p.z - sj.p.z;
@@ -170,7 +173,7 @@ struct VjpPair {
 // sl + ns, ...; the few remaining lanes repeat slice 0 of their pair and their
 // sums are dropped.  Sources are staged TT = ns floor(128 / ns) at a time, so
 // in every full stage each lane takes exactly TT / ns sources.
-template <typename T, typename Rec>
+template <typename T, typename Rec, int MAXQ>
 struct P2PShared {
   union {
     Rec tile[TILE];
@@ -192,8 +195,9 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
                                           const P4<T>* __restrict__ far,
                                           const int32_t* __restrict__ perm, T* __restrict__ out1,
                                           T* __restrict__ out3, T* __restrict__ part,
-                                          P2PShared<T, typename Pair::Rec>& sh) {
+                                          P2PShared<T, typename Pair::Rec, Pair::MAXQ>& sh) {
   using Rec = typename Pair::Rec;
+  constexpr int MAXQ = Pair::MAXQ;
   const int lane = __lane_id();
   const int w = threadIdx.x / WAVE;
   for (int64_t ti = (int64_t)blockIdx.x * P2P_WAVES + w; ti < n_tasks;
@@ -328,7 +332,7 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
           const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
           const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
           T* __restrict__ part) {
-  __shared__ P2PShared<T, P4<T>> sh_all[P2P_WAVES];
+  __shared__ P2PShared<T, P4<T>, ForcePair<T>::MAXQ> sh_all[P2P_WAVES];
   p2p_tasks<T, ForcePair<T>>(tasks, n_tasks, begin, count, src, pts, far, perm, phi, acc, part,
                              sh_all[threadIdx.x / WAVE]);
 }
@@ -336,13 +340,13 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
 // VJP near field: out1 = dS/dm, out3 = dS/dx, with `far` holding the far-field
 // parts of both (Psi and the position gradient) in sorted order.
 template <typename T>
-__global__ void __launch_bounds__(P2P_THREADS)
+__global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8)))
     k_p2p_vjp(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
               const int32_t* __restrict__ count, const int32_t* __restrict__ src,
               const P8<T>* __restrict__ recs, const P4<T>* __restrict__ far,
               const int32_t* __restrict__ perm, T* __restrict__ mbar, T* __restrict__ xbar,
               T* __restrict__ part) {
-  __shared__ P2PShared<T, P8<T>> sh_all[P2P_WAVES];
+  __shared__ P2PShared<T, P8<T>, VjpPair<T>::MAXQ> sh_all[P2P_WAVES];
   p2p_tasks<T, VjpPair<T>>(tasks, n_tasks, begin, count, src, recs, far, perm, mbar, xbar, part,
                            sh_all[threadIdx.x / WAVE]);
 }
