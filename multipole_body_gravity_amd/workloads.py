@@ -29,7 +29,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["uniform", "plummer", "clustered", "hernquist", "lattice", "CONFIGS", "make"]
+__all__ = ["uniform", "plummer", "clustered", "hernquist", "lattice", "CONFIGS", "make",
+           "lattice_state", "LATTICE_DX", "LATTICE_DV"]
 
 
 def uniform(n: int, seed: int) -> np.ndarray:
@@ -141,3 +142,19 @@ def make(dist: str, n: int, seed: int):
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return pos, np.full(n, 1.0 / n)
+
+
+# Integer-lattice state for the reversible integrator: positions x = q dx and
+# velocities v = u dv with q, u int64.  Powers of two, so that q dx is exact in
+# fp64 for |q| < 2^53.
+LATTICE_DX = 2.0 ** -32
+LATTICE_DV = 2.0 ** -32
+
+
+def lattice_state(pos: np.ndarray, seed: int, sigma_v: float = 0.1, dx: float = LATTICE_DX,
+                  dv: float = LATTICE_DV):
+    """q = round(pos / dx) and u = round(v / dv) with v ~ N(0, sigma_v) per component."""
+    rng = np.random.default_rng(seed)
+    q = np.rint(np.asarray(pos, dtype=np.float64) / dx).astype(np.int64)
+    u = np.rint(sigma_v * rng.standard_normal(q.shape) / dv).astype(np.int64)
+    return q, u

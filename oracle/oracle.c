@@ -18,6 +18,8 @@
  *     theta >= theta_max (same section, the criterion equation);
  *   - upward pass, interaction stage, downward pass ("Combining near and far
  *     interactions");
+ *   - the reversible integer-lattice kick-drift-kick step ("Why
+ *     reversibility matters");
  *   - the vector-Jacobian product of the force calculation ("Following
  *     sensitivities backwards"): exactly, by the chain rule, for the direct
  *     sum, and in the page's fast multipole form (the next higher derivative
@@ -1264,6 +1266,69 @@ int oracle_fmm_vjp(int64_t n, const double* pos, const double* mass, int order, 
   if (rc) return rc;
   rc = fmm_vjp_on(r, pb, ab, xbar, mbar);
   oracle_free(r);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* reversible integer-lattice kick-drift-kick step                     */
+/* ------------------------------------------------------------------ */
+/* The jz-fmm page ("Why reversibility matters") keeps positions and velocities
+ * on an integer lattice while the force stays floating point; undoing an
+ * update subtracts the increment the forward update added.  Readings: the
+ * time-symmetric scheme is kick-drift-kick leapfrog; x = q dx and v = u dv
+ * with q, u integer; increments are rounded half to even in fp64:
+ *   kick:  u += s rint(a(q) (dt/2) / dv),    drift: q += s rint(u (dt dv / dx)),
+ * with s = +1 forward and -1 backward.  A backward step runs kick, drift, kick
+ * with s = -1, starting from the force at its starting state, so it undoes a
+ * forward step exactly.  Forces come from oracle_fmm (G = 1).  *min_margin
+ * receives the smallest distance of a kick's rounded quantity to a rounding
+ * boundary (x.5), relative to max(1, |quantity|), over all kicks. */
+static int lattice_force(int64_t n, const int64_t* q, const double* mass, double dx, int order,
+                         double theta, int leaf, double* pos, double* acc) {
+  for (int64_t i = 0; i < 3 * n; i++) pos[i] = (double)q[i] * dx;
+  oracle_result* r = NULL;
+  int rc = oracle_fmm(n, pos, mass, order, theta, leaf, 0, NULL, 1, &r);
+  if (rc) return rc;
+  memcpy(acc, r->acc, sizeof(double) * 3 * (size_t)n);
+  oracle_free(r);
+  return ORACLE_OK;
+}
+
+static void lattice_kick(int64_t n, int64_t* u, const double* acc, double c, int s,
+                         double* min_margin) {
+  for (int64_t i = 0; i < 3 * n; i++) {
+    double k = acc[i] * c;
+    double m = fabs(k - floor(k) - 0.5) / fmax(1.0, fabs(k));
+    if (m < *min_margin) *min_margin = m;
+    u[i] += (int64_t)s * (int64_t)rint(k);
+  }
+}
+
+int oracle_lattice_steps(int64_t n, int64_t* q, int64_t* u, const double* mass, double dx,
+                         double dv, double dt, int n_steps, int direction, int order,
+                         double theta, int leaf_size, double* min_margin) {
+  if (n < 1 || n_steps < 0 || (direction != 1 && direction != -1) || !(dx > 0.0) ||
+      !(dv > 0.0) || !isfinite(dt))
+    return ORACLE_ERR_ARG;
+  double* pos = (double*)malloc(sizeof(double) * 3 * (size_t)n);
+  double* acc = (double*)malloc(sizeof(double) * 3 * (size_t)n);
+  if (!pos || !acc) {
+    free(pos);
+    free(acc);
+    return ORACLE_ERR_OOM;
+  }
+  const double ck = 0.5 * dt / dv, cd = dt * dv / dx;
+  *min_margin = INFINITY;
+  int rc = n_steps > 0 ? lattice_force(n, q, mass, dx, order, theta, leaf_size, pos, acc) : 0;
+  for (int st = 0; st < n_steps && !rc; st++) {
+    lattice_kick(n, u, acc, ck, direction, min_margin);
+    for (int64_t i = 0; i < 3 * n; i++)
+      q[i] += (int64_t)direction * (int64_t)rint((double)u[i] * cd);
+    rc = lattice_force(n, q, mass, dx, order, theta, leaf_size, pos, acc);
+    if (!rc) lattice_kick(n, u, acc, ck, direction, min_margin);
+  }
+  free(pos);
+  free(acc);
   return rc;
 }
 

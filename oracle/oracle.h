@@ -106,6 +106,13 @@ int oracle_fmm_vjp(int64_t n, const double* pos, const double* mass, int order,
 /* Moments of monopoles q [n] and point dipoles dip [n][3] about centre. */
 int oracle_p2m_dipole(int order, int64_t n, const double* pos, const double* q,
                       const double* dip, const double* centre, double* mpole);
+/* n_steps kick-drift-kick steps on the integer lattice x = q dx, v = u dv,
+ * forward (direction +1) or backward (-1), updating q [n][3] and u [n][3] in
+ * place; forces from oracle_fmm with the given order, theta and leaf size.
+ * *min_margin: the closest any kick came to a rounding boundary (relative). */
+int oracle_lattice_steps(int64_t n, int64_t* q, int64_t* u, const double* mass, double dx,
+                         double dv, double dt, int n_steps, int direction, int order,
+                         double theta, int leaf_size, double* min_margin);
 /* Hessian of the local polynomial at offset delta: H6 = xx, yy, zz, xy, xz, yz. */
 int oracle_l2p_hessian(int order, const double* local, const double* delta, double* H6);
 

@@ -77,6 +77,7 @@ def _load():
     lib.oracle_fmm_vjp.argtypes = [i64, P, P, i32, dbl, i32, i64, P, P, P, P, P]
     lib.oracle_p2m_dipole.argtypes = [i32, i64, P, P, P, P, P]
     lib.oracle_l2p_hessian.argtypes = [i32, P, P, P]
+    lib.oracle_lattice_steps.argtypes = [i64, P, P, P, dbl, dbl, dbl, i32, i32, i32, dbl, i32, P]
     _lib = lib
     return lib
 
@@ -348,3 +349,20 @@ def l2p_hessian(order, local, delta):
     if rc:
         raise OracleError(rc)
     return np.array([[h[0], h[3], h[4]], [h[3], h[1], h[5]], [h[4], h[5], h[2]]])
+
+
+# ---- reversible lattice integrator -------------------------------------------
+
+def lattice_steps(q, u, mass, dx, dv, dt, n_steps, direction=1, order=4, theta=0.7, leaf_size=32):
+    """Kick-drift-kick steps on the integer lattice: returns (q, u, min_margin)."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int64).reshape(-1, 3).copy()
+    u = np.ascontiguousarray(u, dtype=np.int64).reshape(-1, 3).copy()
+    mass = _f64(mass)
+    mm = np.zeros(1)
+    rc = lib.oracle_lattice_steps(q.shape[0], _p(q), _p(u), _p(mass), float(dx), float(dv),
+                                  float(dt), int(n_steps), int(direction), int(order),
+                                  float(theta), int(leaf_size), _p(mm))
+    if rc:
+        raise OracleError(rc)
+    return q, u, float(mm[0])
