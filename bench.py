@@ -8,6 +8,7 @@ theta 0.7, leaf 32, inputs resident in HBM.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --sweep [--sweep-n N] [--sweep-orders 2,4,6,8] [--sweep-thetas ...]
     python bench.py --vjp [--steps K] [--warmup W]   (forward + VJP steps, same workload)
+    python bench.py --lattice [--steps K] [--warmup W] (reversible lattice steps, same workload)
 """
 from __future__ import annotations
 
@@ -306,6 +307,78 @@ def vjp_bench(args):
     print(json.dumps(out))
 
 
+def lattice_bench(args):
+    """Reversible integer-lattice kick-drift-kick steps (fmm_lattice_steps) on
+    the headline workload's positions with velocities N(0, 0.1), dt = 1e-3,
+    dx = dv = 2^-32: one call of K steps timed (K + 1 force evaluations, two
+    kicks and a drift per step), then K backward steps outside the timed region
+    that must restore the state bit for bit.  One JSON line."""
+    import torch
+
+    from multipole_body_gravity_amd import Plan, workloads
+    cfg = workloads.CONFIGS[args.workload]
+    n = cfg["n"]
+    pos, mass = workloads.make(cfg["dist"], n, cfg["seed"])
+    q0, u0 = workloads.lattice_state(pos, 301)
+    tdt = torch.float64 if cfg["dtype"] == "f64" else torch.float32
+    dev = torch.device("cuda:0")
+    tq, tu = torch.from_numpy(q0).to(dev), torch.from_numpy(u0).to(dev)
+    tmass = torch.from_numpy(mass).to(dev, tdt)
+    plan = Plan(n, order=cfg["order"], theta=cfg["theta"], leaf_size=cfg["leaf"], dtype=tdt,
+                device=dev)
+    dx, dv, dt = workloads.LATTICE_DX, workloads.LATTICE_DV, 1e-3
+    if args.warmup:
+        plan.lattice_steps(tq, tu, tmass, dx, dv, dt, args.warmup, +1)
+    torch.cuda.synchronize()
+    qs, us = tq.clone(), tu.clone()
+    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
+    plan.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    plan.lattice_steps(tq, tu, tmass, dx, dv, dt, args.steps, +1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s = plan.stats()
+    plan.set_timing(False)
+    plan.lattice_steps(tq, tu, tmass, dx, dv, dt, args.steps, -1)
+    torch.cuda.synchronize()
+    reversible = bool(torch.equal(tq, qs) and torch.equal(tu, us))
+    kern = s["kernel_ms"]
+    fpp = m2l_flops_per_pair(cfg["order"])
+    peak = FP64_VECTOR_PEAK_TFLOPS if cfg["dtype"] == "f64" else FP32_VECTOR_PEAK_TFLOPS
+    flops = {"m2l_sib": n_m2l_own * fpp, "m2l_tail": n_m2l_tr * fpp,
+             "p2p": p2p_pairs * P2P_FLOPS_PER_PAIR}
+    rl = {k: roofline_obj(flops[k], kern[k], peak) for k in flops if kern[k] > 0}
+    dominant = max(rl, key=lambda k: kern[k])
+    roof = dict(rl[dominant])
+    roof["kernel"] = dominant
+    out = {
+        "metric": "reversible lattice KDK step particles/s at N=10^6 fp64 order 4",
+        "value": round(n * args.steps / wall, 1),
+        "unit": "particles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_force_eval": round(wall / (args.steps + 1) * 1e3, 4),
+        "reversible": reversible,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "distribution": cfg["dist"], "n": n,
+                   "order": cfg["order"], "theta": cfg["theta"], "leaf_size": cfg["leaf"],
+                   "seed": cfg["seed"], "dt": dt, "dx": dx, "dv": dv,
+                   "velocities": "N(0, 0.1) per component, seed 301"},
+        "roofline": roof,
+        "stage_ms": {k: round(v, 4) for k, v in s["stage_ms"].items() if k != "vjp"},
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items() if not k.startswith("vjp")},
+    }
+    plan.close()
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +394,8 @@ def main():
     ap.add_argument("--sweep-orders", default="2,4,6,8")
     ap.add_argument("--sweep-thetas", default="0.4,0.5,0.6,0.7")
     ap.add_argument("--sweep-targets", type=int, default=2048)
+    ap.add_argument("--lattice", action="store_true",
+                    help="time reversible integer-lattice steps instead of the forward step")
     ap.add_argument("--vjp", action="store_true",
                     help="time forward + VJP steps (build, eval, fmm_vjp) instead of the forward step")
     args = ap.parse_args()
@@ -339,6 +414,9 @@ def main():
         return
     if args.vjp:
         vjp_bench(args)
+        return
+    if args.lattice:
+        lattice_bench(args)
         return
 
     import torch

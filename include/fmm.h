@@ -152,6 +152,25 @@ int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
 int fmm_vjp(fmm_plan_t plan, const void* phi_bar, const void* acc_bar, void* pos_bar,
             void* mass_bar, void* stream);
 
+/* Reversible integer-lattice kick-drift-kick steps (jz-fmm page, "Why
+ * reversibility matters": positions and velocities on an integer lattice, the
+ * force in floating point, an update undone by subtracting the same integer
+ * increment).  State: q [N][3] and u [N][3], device int64 arrays, updated in
+ * place; x = q dx, v = u dv.  Each step, with s = direction (+1 forward, -1
+ * backward) and a the acceleration of the plan at the current x:
+ *   u += s rint(a (dt/2)/dv);  q += s rint(u dt dv/dx);  u += s rint(a' (dt/2)/dv)
+ * where a' is the acceleration at the new positions; every increment is one
+ * fp64 product rounded half to even.  Because the evaluation is bitwise
+ * reproducible, n steps backward undo n steps forward exactly.  mass [N] is a
+ * device array in the plan's dtype.  Each call evaluates the force n_steps + 1
+ * times (fmm_build + fmm_eval on the plan, whose previous build it replaces)
+ * and synchronizes `stream` at the end.  FMM_ERR_ARG for a null pointer,
+ * n_steps < 0, direction not +-1, dx or dv not positive or a non-finite
+ * dt; FMM_ERR_NONFINITE if positions or masses are not finite, or an increment
+ * is not finite or exceeds 2^62 in magnitude (the state is then unspecified). */
+int fmm_lattice_steps(fmm_plan_t plan, int64_t* q, int64_t* u, const void* mass, double dx,
+                      double dv, double dt, int n_steps, int direction, void* stream);
+
 /* Free the plan and its workspace (synchronizes the device). */
 int fmm_destroy(fmm_plan_t plan);
 

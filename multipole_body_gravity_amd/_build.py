@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmbg_fmm.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["fmm_api.hip", "fmm_build.hip", "fmm_walk.hip", "fmm_expand.hip", "fmm_m2l.hip",
-           "fmm_p2p.hip", "fmm_direct.hip"]
+           "fmm_p2p.hip", "fmm_direct.hip", "fmm_lattice.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-function",
          # keep the compiler from forming packed fp32 operations

@@ -2,6 +2,7 @@
 // management, stage sequencing, the two build synchronizations, timing and
 // introspection copies.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -531,6 +532,7 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->lvl_blkcnt, &p->mpole,       &p->mred,        &p->local,       &p->lfin,
                   &p->vrec,       &p->vfar,        &p->vmpole,      &p->vmred,
                   &p->vlocal,     &p->vlfin,
+                  &p->lat_pos,    &p->lat_phi,     &p->lat_acc,     &p->lat_flag,
                   &p->pool[0],
                   &p->pool[1],    &p->pool[2],
                   &p->cu_off,     &p->cu_cnt,      &p->u_off,       &p->u_cnt,
@@ -771,6 +773,43 @@ int fmm_vjp(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_ba
   rec(p, FMM_STAGE_VJP, 1, st);
   p->pend_vjp = p->timing;
   return FMM_OK;
+}
+
+int fmm_lattice_steps(fmm_plan_t p, int64_t* q, int64_t* u, const void* mass, double dx,
+                      double dv, double dt, int n_steps, int direction, void* stream) {
+  if (!p || !q || !u || !mass || n_steps < 0 || (direction != 1 && direction != -1) ||
+      !(dx > 0.0) || !(dv > 0.0) || !std::isfinite(dx) || !std::isfinite(dv) ||
+      !std::isfinite(dt))
+    return FMM_ERR_ARG;
+  if (n_steps == 0) return FMM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  TRY_HIP(hipSetDevice(p->device));
+  const int dt_ = p->dtype;
+  const int64_t n = p->n;
+  const size_t w = wbytes(dt_);
+  TRY(grow(p->lat_pos, 3 * w * n));
+  TRY(grow(p->lat_phi, w * n));
+  TRY(grow(p->lat_acc, 3 * w * n));
+  TRY(grow(p->lat_flag, sizeof(int)));
+  int* flag = P<int>(p->lat_flag);
+  TRY_HIP(launch_fill_zero(flag, sizeof(int), st));
+  const double ck = 0.5 * dt / dv, cd = dt * dv / dx;
+  auto force = [&]() -> int {  // acceleration of the current lattice positions
+    TRY_HIP(launch_lat_pos(dt_, n, q, dx, p->lat_pos.p, st));
+    TRY(fmm_build(p, p->lat_pos.p, mass, stream));
+    return fmm_eval(p, p->lat_phi.p, p->lat_acc.p, stream);
+  };
+  TRY(force());
+  for (int s = 0; s < n_steps; s++) {
+    TRY_HIP(launch_lat_kick(dt_, n, u, p->lat_acc.p, ck, direction, flag, st));
+    TRY_HIP(launch_lat_drift(n, q, u, cd, direction, flag, st));
+    TRY(force());
+    TRY_HIP(launch_lat_kick(dt_, n, u, p->lat_acc.p, ck, direction, flag, st));
+  }
+  int h = 0;
+  TRY_HIP(hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, st));
+  TRY_HIP(hipStreamSynchronize(st));
+  return h ? FMM_ERR_NONFINITE : FMM_OK;
 }
 
 int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {

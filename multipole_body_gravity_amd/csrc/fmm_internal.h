@@ -93,6 +93,9 @@ struct fmm_plan_s {
   // expansions (node-sized), apart from the forward's so that evals and VJPs
   // of one build can alternate
   mbg::DBuf vrec, vfar, vmpole, vmred, vlocal, vlfin;
+  // lattice integrator: positions, potential and acceleration of the current
+  // lattice state, and the overflow flag
+  mbg::DBuf lat_pos, lat_phi, lat_acc, lat_flag;
   // walk: sharded pools (carry unions, M2L unions, P2P unions, transposed
   // M2L and P2P keys) and per-node slices / counts
   mbg::DBuf pool[mbg::N_POOLS];
@@ -348,6 +351,17 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
                       void* part, bool any_multi, hipEvent_t* ev, bool* ran, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// ---- integer-lattice kick-drift-kick ----
+// pos [N][3] = q dx in the dtype
+hipError_t launch_lat_pos(int dtype, int64_t n, const int64_t* q, double dx, void* pos,
+                          hipStream_t st);
+// u += s rint(acc c); q += s rint(u c); *flag |= 1 on an increment that does
+// not fit (or is not finite)
+hipError_t launch_lat_kick(int dtype, int64_t n, int64_t* u, const void* acc, double c, int s,
+                           int* flag, hipStream_t st);
+hipError_t launch_lat_drift(int64_t n, int64_t* q, const int64_t* u, double c, int s, int* flag,
+                            hipStream_t st);
 
 // ---- vector-Jacobian product ----
 // rec[k] = P8 (sorted particle k, pb and ab of caller index perm[k])

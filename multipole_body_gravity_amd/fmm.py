@@ -56,6 +56,7 @@ def load_library():
     lib.fmm_build.argtypes = [P, P, P, P]
     lib.fmm_eval.argtypes = [P, P, P, P]
     lib.fmm_vjp.argtypes = [P, P, P, P, P, P]
+    lib.fmm_lattice_steps.argtypes = [P, P, P, P, dbl, dbl, dbl, i32, i32, P]
     lib.fmm_destroy.argtypes = [P]
     lib.fmm_strerror.argtypes = [i32]
     lib.fmm_strerror.restype = ctypes.c_char_p
@@ -158,6 +159,26 @@ class Plan:
                                   ctypes.c_void_p(mass_bar.data_ptr()), _stream_handle(stream))
         self._check(rc, "fmm_vjp")
         return pos_bar, mass_bar
+
+    def lattice_steps(self, q: torch.Tensor, u: torch.Tensor, mass: torch.Tensor, dx: float,
+                      dv: float, dt: float, n_steps: int = 1, direction: int = 1, stream=None):
+        """Reversible kick-drift-kick steps on the integer lattice x = q dx,
+        v = u dv (fmm_lattice_steps); q and u are int64 [N,3] device tensors,
+        updated in place.  direction -1 undoes direction +1 exactly."""
+        for t in (q, u):
+            if t.shape != (self.n, 3) or t.dtype != torch.int64 or not t.is_cuda or not t.is_contiguous():
+                raise FmmError(-1, "fmm_lattice_steps: q and u contiguous int64 [N,3] device tensors")
+        if mass.shape != (self.n,) or mass.dtype != self.dtype or not mass.is_cuda:
+            raise FmmError(-1, "fmm_lattice_steps: mass [N] device tensor of the plan dtype")
+        mass = mass.contiguous()
+        with torch.cuda.device(self.device):
+            rc = self.lib.fmm_lattice_steps(self._h, ctypes.c_void_p(q.data_ptr()),
+                                            ctypes.c_void_p(u.data_ptr()),
+                                            ctypes.c_void_p(mass.data_ptr()), float(dx), float(dv),
+                                            float(dt), int(n_steps), int(direction),
+                                            _stream_handle(stream))
+        self._check(rc, "fmm_lattice_steps")
+        return q, u
 
     def set_timing(self, enable: bool = True) -> None:
         self._check(self.lib.fmm_set_timing(self._h, 1 if enable else 0), "fmm_set_timing")

@@ -26,7 +26,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for want in ["fmm_plan", "fmm_build", "fmm_eval", "fmm_destroy", "fmm_strerror",
                  "fmm_set_timing", "fmm_stats", "fmm_copy_keys", "fmm_copy_tree",
-                 "fmm_copy_lists", "fmm_copy_expansions", "fmm_direct", "fmm_vjp"]:
+                 "fmm_copy_lists", "fmm_copy_expansions", "fmm_direct", "fmm_vjp", "fmm_lattice_steps"]:
         assert want in names
 
 
@@ -58,6 +58,8 @@ def test_null_plan_calls(lib):
     assert lib.fmm_build(None, P(1), P(1), None) == -1
     assert lib.fmm_eval(None, P(1), P(1), None) == -1
     assert lib.fmm_vjp(None, P(1), P(1), P(1), P(1), None) == -1
+    D = ctypes.c_double
+    assert lib.fmm_lattice_steps(None, P(1), P(1), P(1), D(1.0), D(1.0), D(0.1), 1, 1, None) == -1
     assert lib.fmm_destroy(None) == -1
     # the direct-sum reference checks its arguments before any device call
     assert lib.fmm_direct(None, P(1), 10, P(1), 1, 1, P(1), P(1), None) == -1

@@ -453,6 +453,86 @@ def test_vjp_1e6_sampled(orc, name, n_sample):
     plan.close()
 
 
+# --------------------------------------------------------------------------
+# reversible integer-lattice steps (fmm_lattice_steps)
+# --------------------------------------------------------------------------
+
+def gpu_lattice(plan, q, u, mass, dt, n_steps, direction, tdt, dv=W.LATTICE_DV):
+    torch = _torch()
+    dev = torch.device("cuda:0")
+    tq = torch.from_numpy(q).to(dev)
+    tu = torch.from_numpy(u).to(dev)
+    plan.lattice_steps(tq, tu, torch.from_numpy(mass).to(dev, tdt), W.LATTICE_DX, dv,
+                       dt, n_steps, direction)
+    torch.cuda.synchronize()
+    return tq.cpu().numpy(), tu.cpu().numpy()
+
+
+@pytest.mark.parametrize("dist,n,seed,order,theta,leaf", [
+    ("plummer", 4096, 201, 4, 0.7, 32), ("clustered", 10000, 202, 5, 0.6, 16),
+    ("uniform", 777, 203, 2, 0.5, 3)])
+def test_lattice_parity(orc, dist, n, seed, order, theta, leaf):
+    """Three steps from the same integer state give the same integers as the
+    oracle.  The drift is exact.  A kick rounds a * dt/2 / dv, and the two
+    accelerations agree only to the evaluation's tolerance (1e-11), so a kick
+    whose quantity lies within 1e-11 |a dt/2/dv| of a rounding boundary could
+    go either way: the velocity lattice here is dv = 2^-16 (kicks of tens of
+    units, rather than the 2^-32 of the reversibility runs, where a kick of
+    ~10^9 units is uncertain in its last digit), and the test checks that no
+    kick of the seeded cases comes within 1e-10 (relative) of a boundary, so
+    every integer must agree."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    pos, mass = W.make(dist, n, seed)
+    dv = 2.0 ** -16
+    q0, u0 = W.lattice_state(pos, seed + 1, dv=dv)
+    dt = 1e-3
+    plan = Plan(n, order=order, theta=theta, leaf_size=leaf, dtype=torch.float64,
+                device=torch.device("cuda:0"))
+    qg, ug = gpu_lattice(plan, q0, u0, mass, dt, 3, +1, torch.float64, dv=dv)
+    qr, ur, margin = orc.lattice_steps(q0, u0, mass, W.LATTICE_DX, dv, dt, 3, +1,
+                                       order, theta, leaf)
+    say(f"    smallest rounding margin {margin:.3g}")
+    assert margin > 1e-10
+    assert np.array_equal(qg, qr) and np.array_equal(ug, ur)
+    plan.close()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,steps", [("clustered_1e6_p4", 4), ("clustered_1e6_f32", 4),
+                                        ("plummer_1e5", 10)])
+def test_lattice_reversible(name, steps):
+    """Forward steps then as many backward steps return the exact initial
+    integer state, at the benchmark's workload in fp64 and fp32."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    c = W.CONFIGS[name]
+    pos, mass = W.make(c["dist"], c["n"], c["seed"])
+    q0, u0 = W.lattice_state(pos, 301)
+    tdt = torch.float64 if c["dtype"] == "f64" else torch.float32
+    plan = Plan(c["n"], order=c["order"], theta=c["theta"], leaf_size=c["leaf"], dtype=tdt,
+                device=torch.device("cuda:0"))
+    q1, u1 = gpu_lattice(plan, q0, u0, mass, 1e-3, steps, +1, tdt)
+    assert (q1 != q0).mean() > 0.9 and (u1 != u0).mean() > 0.9
+    q2, u2 = gpu_lattice(plan, q1, u1, mass, 1e-3, steps, -1, tdt)
+    assert np.array_equal(q2, q0) and np.array_equal(u2, u0)
+    plan.close()
+
+
+def test_lattice_overflow_reported():
+    """An increment beyond 2^62 (here a huge time step) is an error, not a wrap."""
+    torch = _torch()
+    from multipole_body_gravity_amd import FmmError, Plan
+    pos, mass = W.make("plummer", 2000, 204)
+    q0, u0 = W.lattice_state(pos, 205)
+    plan = Plan(2000, order=3, theta=0.7, leaf_size=16, dtype=torch.float64,
+                device=torch.device("cuda:0"))
+    with pytest.raises(FmmError) as e:
+        gpu_lattice(plan, q0, u0, mass, 1e12, 1, +1, torch.float64)
+    assert e.value.code == -5
+    plan.close()
+
+
 def test_streams_and_timing(orc):
     """Build on one stream and evaluate on another (the plan's second stream is
     ordered against both); with timing on, every stage and kernel is counted
