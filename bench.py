@@ -87,6 +87,8 @@ KERNEL_SOURCES = {
     "p2p": "multipole_body_gravity_amd/csrc/fmm_p2p.hip",
     "m2l_sib": "multipole_body_gravity_amd/csrc/fmm_m2l.hip",
     "m2l_tail": "multipole_body_gravity_amd/csrc/fmm_m2l.hip",
+    "vjp_p2p": "multipole_body_gravity_amd/csrc/fmm_p2p.hip",
+    "vjp_m2l_sib": "multipole_body_gravity_amd/csrc/fmm_m2l.hip",
 }
 
 
@@ -263,7 +265,8 @@ def vjp_bench(args):
     flops = {"vjp_p2p": p2p_pairs * P2P_VJP_FLOPS_PER_PAIR, "vjp_m2l_sib": n_m2l_own * fpp,
              "p2p": p2p_pairs * P2P_FLOPS_PER_PAIR, "m2l_sib": n_m2l_own * fpp,
              "m2l_tail": n_m2l_tr * fpp}
-    rl = {k: roofline_obj(f, kern[k], peak) for k, f in flops.items() if kern[k] > 0}
+    rl = {k: roofline_obj(f, kern[k], peak, measured_traffic(k, args.workload))
+          for k, f in flops.items() if kern[k] > 0}
     dominant = max(rl, key=lambda k: kern[k])
     roof = dict(rl[dominant])
     roof["kernel"] = dominant
