@@ -453,6 +453,54 @@ def test_vjp_1e6_sampled(orc, name, n_sample):
     plan.close()
 
 
+@pytest.mark.parametrize("kind", ["single", "two_body", "all_near", "order0"])
+def test_vjp_degenerate(orc, kind):
+    """One particle (no sensitivity reaches anything), two bodies, a single
+    leaf holding everything (all pairs direct: equal to the exact chain-rule
+    gradient of the direct sum) and order 0."""
+    pos, mass = W.make("plummer", 3000, 96)
+    order, theta, leaf = 4, 0.7, 32
+    if kind == "single":
+        pos, mass = pos[:1], mass[:1]
+    elif kind == "two_body":
+        pos, mass = pos[:2], mass[:2]
+    elif kind == "all_near":
+        pos, mass, leaf = pos[:700], mass[:700], 700
+    else:
+        order = 0
+    n = pos.shape[0]
+    pb, ab = sensitivities(n, 97, "f64")
+    plan, _, _ = gpu_run(pos, mass, order, theta, leaf, "f64")
+    xb, mb = gpu_vjp(plan, pb, ab, "f64")
+    plan.close()
+    if kind == "single":
+        assert np.all(xb == 0.0) and np.all(mb == 0.0)
+        return
+    rx, rm = orc.fmm_vjp(pos, mass, pb, ab, order, theta, leaf)
+    check_vjp(xb, mb, rx, rm, "f64", inputs=(pos, mass, pb, ab))
+    if kind in ("two_body", "all_near"):
+        dx, dm = orc.direct_vjp(pos, mass, pb, ab)
+        assert np.abs(xb - dx).max() <= 1e-12 * np.abs(dx).max()
+        assert np.abs(mb - dm).max() <= 1e-12 * np.abs(dm).max()
+
+
+def test_vjp_rejects_bad_arguments():
+    torch = _torch()
+    from multipole_body_gravity_amd import FmmError, Plan
+    dev = torch.device("cuda:0")
+    plan = Plan(100, order=3, dtype=torch.float64, device=dev)
+    pb = torch.zeros(100, dtype=torch.float64, device=dev)
+    ab = torch.zeros(100, 3, dtype=torch.float64, device=dev)
+    with pytest.raises(FmmError) as e:  # not built
+        plan.vjp(pb, ab)
+    assert e.value.code == -2
+    with pytest.raises(FmmError):
+        plan.vjp(pb[:50], ab)
+    with pytest.raises(FmmError):
+        plan.vjp(pb.float(), ab)
+    plan.close()
+
+
 # --------------------------------------------------------------------------
 # reversible integer-lattice steps (fmm_lattice_steps)
 # --------------------------------------------------------------------------
@@ -517,6 +565,29 @@ def test_lattice_reversible(name, steps):
     q2, u2 = gpu_lattice(plan, q1, u1, mass, 1e-3, steps, -1, tdt)
     assert np.array_equal(q2, q0) and np.array_equal(u2, u0)
     plan.close()
+
+
+def test_lattice_edge_cases(orc):
+    """No steps leaves the state alone; a lone particle drifts by exactly
+    round(u dt dv / dx) per step (as the oracle); a bad direction is an
+    argument error."""
+    torch = _torch()
+    from multipole_body_gravity_amd import FmmError, Plan
+    dev = torch.device("cuda:0")
+    pos, mass = W.make("uniform", 500, 206)
+    q0, u0 = W.lattice_state(pos, 207)
+    plan = Plan(500, order=3, theta=0.7, leaf_size=16, dtype=torch.float64, device=dev)
+    q, u = gpu_lattice(plan, q0, u0, mass, 1e-3, 0, +1, torch.float64)
+    assert np.array_equal(q, q0) and np.array_equal(u, u0)
+    with pytest.raises(FmmError) as e:
+        gpu_lattice(plan, q0, u0, mass, 1e-3, 1, 0, torch.float64)
+    assert e.value.code == -1
+    plan.close()
+    one = Plan(1, order=4, dtype=torch.float64, device=dev)
+    q1, u1 = gpu_lattice(one, q0[:1], u0[:1], mass[:1], 0.37, 3, +1, torch.float64)
+    qr, ur, _ = orc.lattice_steps(q0[:1], u0[:1], mass[:1], W.LATTICE_DX, W.LATTICE_DV, 0.37, 3, +1)
+    assert np.array_equal(q1, qr) and np.array_equal(u1, ur) and np.array_equal(u1, u0[:1])
+    one.close()
 
 
 def test_lattice_overflow_reported():
