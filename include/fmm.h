@@ -148,7 +148,9 @@ int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
  * plan (FMM_ERR_STATE otherwise); runs the forward's leaf locals itself if no
  * fmm_eval followed the build.  Asynchronous on `stream`; repeatable; must not
  * overlap an fmm_eval of the same plan on another stream (they share the
- * split-task partial buffers). */
+ * split-task partial buffers).  Its own workspace (sensitivity records and
+ * expansions, about 2 N + 3 n_nodes K values of the dtype) is allocated by the
+ * first call after a build that needs more, grow-only like the plan's. */
 int fmm_vjp(fmm_plan_t plan, const void* phi_bar, const void* acc_bar, void* pos_bar,
             void* mass_bar, void* stream);
 
