@@ -109,6 +109,13 @@ __global__ void __launch_bounds__(256)
 // ---- near-field sums ----
 constexpr int TILE = 2 * WAVE;       // source particles staged per round
 
+typedef __attribute__((address_space(1))) void p2p_gvoid_t;
+typedef __attribute__((address_space(3))) void p2p_lvoid_t;
+// one 16-byte piece of a source record in LDS
+struct alignas(16) Piece16 {
+  uint64_t a, b;
+};
+
 // Pair interactions.  Each adds one source's contribution to the four
 // per-target sums that the task writes.
 //
@@ -173,10 +180,15 @@ struct VjpPair {
 // sl + ns, ...; the few remaining lanes repeat slice 0 of their pair and their
 // sums are dropped.  Sources are staged TT = ns floor(128 / ns) at a time, so
 // in every full stage each lane takes exactly TT / ns sources.
+// The staged source records are kept as NH planes of 16-byte pieces (plane
+// h holds bytes 16h .. 16h + 15 of every record): global-to-LDS copies fill
+// a plane 64 records at a time, and the lanes reading consecutive records of
+// one plane touch consecutive 16-byte slots.
 template <typename T, typename Rec, int MAXQ>
 struct P2PShared {
+  static constexpr int NH = (int)(sizeof(Rec) / 16);
   union {
-    Rec tile[TILE];
+    Piece16 tile[NH][TILE];
     T red[8][WAVE];
   };
   uint8_t owner[MAXQ];  // list entry (within the group of 64) of each source particle
@@ -198,6 +210,17 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
                                           P2PShared<T, typename Pair::Rec, Pair::MAXQ>& sh) {
   using Rec = typename Pair::Rec;
   constexpr int MAXQ = Pair::MAXQ;
+  constexpr int NH = P2PShared<T, Rec, MAXQ>::NH;
+  static_assert(sizeof(Rec) == 16 * NH, "records are whole 16-byte pieces");
+  auto staged = [&](int s) -> Rec {  // record s of the current stage
+    union {
+      Rec r;
+      Piece16 q[NH];
+    } u;
+#pragma unroll
+    for (int h = 0; h < NH; h++) u.q[h] = sh.tile[h][s];
+    return u.r;
+  };
   const int lane = __lane_id();
   const int w = threadIdx.x / WAVE;
   for (int64_t ti = (int64_t)blockIdx.x * P2P_WAVES + w; ti < n_tasks;
@@ -255,21 +278,29 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
           for (int r = 0; r < TILE / WAVE; r++) {
             const int k = r * WAVE + lane;
             const int q = q0 + k;
-            if (k < TT && q < tot) sh.tile[k] = pts[sh.sbase[one ? 0 : sh.owner[q]] + q];
+            if (k < TT && q < tot) {
+              // record k of the stage straight into LDS, piece h into plane h
+              const unsigned char* g =
+                  (const unsigned char*)(pts + sh.sbase[one ? 0 : sh.owner[q]] + q);
+#pragma unroll
+              for (int h = 0; h < NH; h++)
+                __builtin_amdgcn_global_load_lds((p2p_gvoid_t*)(g + 16 * h),
+                                                 (p2p_lvoid_t*)&sh.tile[h][r * WAVE], 16, 0, 0);
+            }
           }
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the stage has landed in LDS
           __builtin_amdgcn_wave_barrier();
           const int nv = min(TT, tot - q0);
           if (nv == TT) {
             // a full stage: the same number of sources on every lane
-            const Rec* sp = sh.tile + sl;
             for (int k = 0; k < per; k++) {
-              const Rec pj = sp[k * ns];
+              const Rec pj = staged(sl + k * ns);
               Pair::add(p0, pj, a0, a1, a2, a3);
               Pair::add(p1, pj, b0, b1, b2, b3);
             }
           } else {
             for (int s = sl; s < nv; s += ns) {
-              const Rec pj = sh.tile[s];
+              const Rec pj = staged(s);
               Pair::add(p0, pj, a0, a1, a2, a3);
               Pair::add(p1, pj, b0, b1, b2, b3);
             }
