@@ -175,6 +175,7 @@ int issue_upward(fmm_plan_t p) {
     TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
                        P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, us));
   TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, us));
+  TRY_HIP(hipEventRecord(p->ev_rec, us));  // the M2L source records are written
   rec(p, FMM_STAGE_UP, 1, us);
   return FMM_OK;
 }
@@ -414,7 +415,10 @@ int materialize_m2l_lists(fmm_plan_t p, hipStream_t st) {
 // The leaves' complete forward locals in lfin: the M2L of the transposed
 // tails, then the downward pass (one launch at orders <= 5, else level by
 // level on a copy of `local`).  Records the tail stage and the start of the
-// downward stage.
+// downward stage.  With the one-launch pass the tails only write their
+// partials and need only the source records, so they start before the
+// own-entry M2L on the second stream has finished (in its shadow); the pass
+// itself waits for that M2L.
 int leaf_locals(fmm_plan_t p, hipStream_t st) {
   const int dt = p->dtype, ord = p->order;
   const double* centre = P<double>(p->ncentre);
@@ -423,6 +427,7 @@ int leaf_locals(fmm_plan_t p, hipStream_t st) {
   const size_t lbytes = (size_t)nn * p->K * wbytes(dt);
   const bool pull = ord <= 5;  // the one-launch downward pass
 
+  TRY_HIP(hipStreamWaitEvent(st, pull ? p->ev_rec : p->ev_up, 0));
   rec(p, FMM_STAGE_TAIL, 0, st);
   M2LArgs ma = m2l_args(p);
   ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_TAIL : nullptr;
@@ -433,6 +438,7 @@ int leaf_locals(fmm_plan_t p, hipStream_t st) {
   }
   TRY_HIP(launch_m2l_tails(dt, ord, ma, !pull, st));
   rec(p, FMM_STAGE_TAIL, 1, st);
+  if (pull) TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));  // the own-entry locals
 
   rec(p, FMM_STAGE_DOWN, 0, st);
   p->l2l_pulled = pull && launch_l2l_pull(dt, ord, leaves, p->n_leaves, P<int32_t>(p->nparent),
@@ -513,7 +519,8 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
   if (hipStreamCreateWithFlags(&p->up_stream, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_tree, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_order, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&p->ev_up, hipEventDisableTiming) != hipSuccess)
+      hipEventCreateWithFlags(&p->ev_up, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_rec, hipEventDisableTiming) != hipSuccess)
     return fail(FMM_ERR_HIP);
   *out = p;
   return FMM_OK;
@@ -554,6 +561,7 @@ int fmm_destroy(fmm_plan_t p) {
   if (p->ev_tree) (void)hipEventDestroy(p->ev_tree);
   if (p->ev_order) (void)hipEventDestroy(p->ev_order);
   if (p->ev_up) (void)hipEventDestroy(p->ev_up);
+  if (p->ev_rec) (void)hipEventDestroy(p->ev_rec);
   if (p->up_stream) (void)hipStreamDestroy(p->up_stream);
   delete p;
   return FMM_OK;
@@ -680,9 +688,8 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   if (!p->built) return FMM_ERR_STATE;
   hipStream_t st = (hipStream_t)stream;
   TRY_HIP(hipSetDevice(p->device));
-  // multipoles, source records and the own-entry locals come from the build's
-  // second stream; `local` is only read from here on
-  TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
+  // source records and the own-entry locals come from the build's second
+  // stream (leaf_locals waits for each); `local` is only read from here on
   TRY(leaf_locals(p, st));
   TRY_HIP(launch_l2p(p->dtype, p->order, p->n, p->pts.p, P<int32_t>(p->leaf_of),
                      P<double>(p->ncentre), p->lfin.p, p->far.p, st));

@@ -141,6 +141,7 @@ struct fmm_plan_s {
   // leaves' complete locals into `lfin`, so evals can repeat.
   hipStream_t up_stream = nullptr;
   hipEvent_t ev_tree = nullptr, ev_order = nullptr, ev_up = nullptr;
+  hipEvent_t ev_rec = nullptr;  // the M2L source records are written (second stream)
   bool up_issued = false;
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
   hipEvent_t kev[2 * FMM_N_KERNELS] = {};  // begin/end of single kernel launches
