@@ -121,14 +121,18 @@ __device__ __forceinline__ int work_octave(uint64_t w) {
 template <int NB>
 __device__ __forceinline__ int64_t octave_slot(int o, const int32_t* oct, int32_t* cur) {
   __shared__ int cnt[NB];
+  __shared__ int tot[NB];  // the buckets' totals, staged once per block
   __shared__ int64_t base[NB];
-  for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
+  for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+    cnt[b] = 0;
+    tot[b] = oct[b];
+  }
   __syncthreads();
   const int r = o >= 0 ? atomicAdd(&cnt[o], 1) : 0;
   __syncthreads();
   for (int b = threadIdx.x; b < NB; b += blockDim.x) {
     int64_t start = 0;
-    for (int q = 0; q < b; q++) start += oct[q];
+    for (int q = 0; q < b; q++) start += tot[q];
     base[b] = cnt[b] ? start + atomicAdd(&cur[b], cnt[b]) : 0;
   }
   __syncthreads();
