@@ -76,6 +76,40 @@ P2P_FLOPS_PER_PAIR = 19  # 3 sub, |r|^2 5, rsqrt 1, 3 mul, 1 add, 3 FMA (6)
 P2P_VJP_FLOPS_PER_PAIR = 52
 
 
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def hbm_stages(cfg, st, stage_ms, kernel_ms):
+    """Algorithmic HBM bytes of the memory-bound steps over their measured
+    times: the keys stage (bounding box + keys) and the sort stage (seven 9-bit
+    radix passes + gather into sorted records) from the stage events, P2M and
+    L2P from their kernel events.  Bytes count each array element once: per
+    particle, the box reads x, y, z, m and the keys kernel reads x, y, z and
+    writes key + index; a radix pass reads the key (histogram) and the key and
+    index (scatter) and writes both; the gather reads the index and the input
+    and writes the record; P2M reads the records and writes K moments per
+    leaf; L2P reads the record, the leaf index, and per leaf the centre and K
+    locals, and writes four results."""
+    n, nl = cfg["n"], st["n_leaves"]
+    w = 8 if cfg["dtype"] == "f64" else 4
+    K = (cfg["order"] + 1) * (cfg["order"] + 2) * (cfg["order"] + 3) // 6
+    passes = 7
+    items = {
+        "keys": (n * (4 * w + 3 * w + 8 + 4), stage_ms["keys"], "stage"),
+        "sort": (n * (passes * (8 + 12 + 12) + 4 + 4 * w + 4 * w), stage_ms["sort"], "stage"),
+        "p2m": (n * 4 * w + nl * (12 + 24 + K * w), kernel_ms["p2m"], "kernel"),
+        "l2p": (n * (4 * w + 4 + 4 * w) + nl * (24 + K * w), kernel_ms["l2p"], "kernel"),
+    }
+    out = {}
+    for k, (b, ms, how) in items.items():
+        if ms > 0:
+            gbs = b / (ms * 1e-3) / 1e9
+            out[k] = {"bound": "hbm", "bytes": int(b), "ms": round(ms, 4), "achieved": round(gbs, 1),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "timed": how}
+    return out
+
+
 def roofline_obj(flops_per_launch, ms, dtype_peak, traffic=None):
     achieved = flops_per_launch / (ms * 1e-3) / 1e12
     return {"bound": "alu", "achieved": round(achieved, 3), "peak": dtype_peak, "unit": "TFLOP/s",
@@ -493,6 +527,7 @@ def main():
                    "seed": cfg["seed"]},
         "roofline": roof,
         "roofline_other": {k: v for k, v in rl.items() if k != dominant},
+        "hbm": hbm_stages(cfg, st, stage_avg, kern_avg),
         "stage_ms": {k: round(v, 4) for k, v in stage_avg.items() if k != "vjp"},
         "kernel_ms": {k: round(v, 4) for k, v in kern_avg.items() if not k.startswith("vjp")},
         "work": {"n_m2l": n_m2l, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,

@@ -89,7 +89,9 @@ enum fmm_kernel {
   FMM_KERNEL_P2P_COMBINE = 3, /* ordered sum of split leaves' partials    */
   FMM_KERNEL_VJP_M2L_SIB = 4, /* fmm_vjp: sibling M2L of the sensitivity moments */
   FMM_KERNEL_VJP_P2P = 5,     /* fmm_vjp: near-field pair sums            */
-  FMM_N_KERNELS = 6
+  FMM_KERNEL_P2M = 6,         /* leaf moments (build, second stream)      */
+  FMM_KERNEL_L2P = 7,         /* far field at the particles (eval)        */
+  FMM_N_KERNELS = 8
 };
 
 typedef struct {
@@ -99,7 +101,7 @@ typedef struct {
   double lo[3], side;    /* root cube */
   float stage_ms[FMM_N_STAGES]; /* mean over the timed steps, see fmm_set_timing */
   int32_t walk_retries;  /* workspace regrowths during the last walk */
-  float kernel_ms[FMM_N_KERNELS]; /* mean over the timed builds (sibling M2L), evals or VJPs */
+  float kernel_ms[FMM_N_KERNELS]; /* mean over the timed builds (sibling M2L, P2M), evals or VJPs */
   int32_t timed_builds;  /* builds, evals and VJPs the means are taken over */
   int32_t timed_evals;
   int32_t timed_vjps;

@@ -99,16 +99,15 @@ void collect_pending(fmm_plan_t p) {
   if (p->pend_build) {
     for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP, FMM_STAGE_M2L})
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
-    if (p->kran[FMM_KERNEL_M2L_SIB])
-      p->kernel_sum[FMM_KERNEL_M2L_SIB] +=
-          elapsed(p->kev[2 * FMM_KERNEL_M2L_SIB], p->kev[2 * FMM_KERNEL_M2L_SIB + 1]);
+    for (int k : {FMM_KERNEL_M2L_SIB, FMM_KERNEL_P2M})
+      if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_builds++;
     p->pend_build = false;
   }
   if (p->pend_eval) {
     for (int s : {FMM_STAGE_TAIL, FMM_STAGE_DOWN, FMM_STAGE_P2P})
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
-    for (int k = FMM_KERNEL_M2L_TAIL; k <= FMM_KERNEL_P2P_COMBINE; k++)
+    for (int k : {FMM_KERNEL_M2L_TAIL, FMM_KERNEL_P2P, FMM_KERNEL_P2P_COMBINE, FMM_KERNEL_L2P})
       if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_evals++;
     p->pend_eval = false;
@@ -169,8 +168,13 @@ int issue_upward(fmm_plan_t p) {
   const int dt = p->dtype, ord = p->order;
   const double* centre = P<double>(p->ncentre);
   rec(p, FMM_STAGE_UP, 0, us);
+  if (p->timing) TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_P2M], us));
   TRY_HIP(launch_p2m(dt, ord, p->pts.p, P<int32_t>(p->leaves), p->n_leaves,
                      P<int32_t>(p->nbegin), P<int32_t>(p->ncount), centre, p->mpole.p, us));
+  if (p->timing) {
+    TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_P2M + 1], us));
+    p->kran[FMM_KERNEL_P2M] = true;
+  }
   for (int l = p->depth - 1; l >= 0; l--)
     TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
                        P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, us));
@@ -691,8 +695,13 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   // source records and the own-entry locals come from the build's second
   // stream (leaf_locals waits for each); `local` is only read from here on
   TRY(leaf_locals(p, st));
+  if (p->timing) TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_L2P], st));
   TRY_HIP(launch_l2p(p->dtype, p->order, p->n, p->pts.p, P<int32_t>(p->leaf_of),
                      P<double>(p->ncentre), p->lfin.p, p->far.p, st));
+  if (p->timing) {
+    TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_L2P + 1], st));
+    p->kran[FMM_KERNEL_L2P] = true;
+  }
   rec(p, FMM_STAGE_DOWN, 1, st);
 
   rec(p, FMM_STAGE_P2P, 0, st);
@@ -850,9 +859,11 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
                                                      : s == FMM_STAGE_VJP ? nv
                                                                           : ne));
     for (int k = 0; k < FMM_N_KERNELS; k++)
-      out->kernel_ms[k] = (float)(p->kernel_sum[k] / (k == FMM_KERNEL_M2L_SIB   ? nb
-                                                      : k >= FMM_KERNEL_VJP_M2L_SIB ? nv
-                                                                                    : ne));
+      out->kernel_ms[k] = (float)(p->kernel_sum[k] /
+                                  (k == FMM_KERNEL_M2L_SIB || k == FMM_KERNEL_P2M ? nb
+                                   : k == FMM_KERNEL_VJP_M2L_SIB || k == FMM_KERNEL_VJP_P2P
+                                       ? nv
+                                       : ne));
     out->timed_builds = p->n_timed_builds;
     out->timed_evals = p->n_timed_evals;
     out->timed_vjps = p->n_timed_vjps;

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libmbg_fmm.so")
 FMM_F32, FMM_F64 = 0, 1
 MAX_ORDER = 8
 STAGES = ["keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p", "tail", "vjp"]  # stage_ms order
-KERNELS = ["m2l_sib", "m2l_tail", "p2p", "p2p_combine", "vjp_m2l_sib", "vjp_p2p"]  # kernel_ms order
+KERNELS = ["m2l_sib", "m2l_tail", "p2p", "p2p_combine", "vjp_m2l_sib", "vjp_p2p", "p2m",
+           "l2p"]  # kernel_ms order
 _ERR = {0: "ok", -1: "invalid argument", -2: "plan not built", -3: "device out of memory",
         -4: "HIP runtime error", -5: "non-finite position or mass", -6: "no HIP device"}
 
