@@ -417,7 +417,7 @@ int materialize_m2l_lists(fmm_plan_t p, hipStream_t st) {
 }
 
 // The leaves' complete forward locals in lfin: the M2L of the transposed
-// tails, then the downward pass (one launch at orders <= 5, else level by
+// tails, then the downward pass (one launch at orders <= 6, else level by
 // level on a copy of `local`).  Records the tail stage and the start of the
 // downward stage.  With the one-launch pass the tails only write their
 // partials and need only the source records, so they start before the
@@ -429,7 +429,7 @@ int leaf_locals(fmm_plan_t p, hipStream_t st) {
   int32_t* leaves = P<int32_t>(p->leaves);
   const int64_t nn = p->n_nodes;
   const size_t lbytes = (size_t)nn * p->K * wbytes(dt);
-  const bool pull = ord <= 5;  // the one-launch downward pass
+  const bool pull = ord <= 6;  // the one-launch downward pass
 
   TRY_HIP(hipStreamWaitEvent(st, pull ? p->ev_rec : p->ev_up, 0));
   rec(p, FMM_STAGE_TAIL, 0, st);
@@ -759,7 +759,7 @@ int fmm_vjp(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_ba
   TRY_HIP(launch_m2l_sib(dt, ord, ma, st));
   ma.ev = nullptr;
   ma.ran = nullptr;
-  const bool pull = ord <= 5;
+  const bool pull = ord <= 6;
   if (!pull) {
     TRY_HIP(hipMemcpyAsync(p->vlfin.p, p->vlocal.p, (size_t)nn * p->K * w,
                            hipMemcpyDeviceToDevice, st));

@@ -15,6 +15,7 @@
 // c_child - c_P, and the multipole-to-local step becomes a plain contraction.
 // The local array holds the derivatives L_n = d^n Phi at the cell centre.
 #include <algorithm>
+#include <type_traits>
 
 #include "fmm_device.h"
 #include "fmm_internal.h"
@@ -67,7 +68,12 @@ constexpr int EX_WAVES = EX_THREADS / WAVE;
 constexpr int PP = FMM_MAX_ORDER + 1;  // entries of a 1-d power table
 constexpr int MAXCH = 8;
 
-// ---------------- register-resident variants for orders <= 5 ----------------
+// ---------------- register-resident variants ----------------
+// Used wherever they beat the wave-per-node kernels further down: P2M, M2M
+// and L2L up to order 8 in fp64 (at order 8 M2M and L2L spill some registers
+// and are still 3.4x and 2.2x faster, measured on the 256^3 lattice), up to 6
+// in fp32 (the fp32 instances spill from 7 on), the one-launch downward pass
+// and the dipole P2M up to 6.
 // P2M, one thread per leaf: the leaf's particles are read in order and every
 // scaled moment is accumulated in registers.
 template <typename T, int P>
@@ -253,7 +259,7 @@ __global__ void __launch_bounds__(256)
   for (int k = 0; k < K; k++) Lc[k] = (T)acc[k];
 }
 
-// Downward pass for orders <= 5, one thread per leaf: Taylor shifts of a
+// Downward pass for orders <= 6, one thread per leaf: Taylor shifts of a
 // degree-p polynomial are exact and compose, so the leaf's local is the sum of
 // its own M2L local (own entries, minus the sum of its transposed-tail task
 // partials in task order) and of every ancestor's M2L local shifted straight
@@ -343,7 +349,7 @@ static bool l2l_pull_dispatch(int order, const int32_t* leaves, int64_t n_leaves
     k_l2l_pull<T, P><<<g, 256, 0, st>>>(leaves, n_leaves, parent, centre, (const T*)local,    \
                                         toff, (const T*)part, (T*)out);                      \
     return true;
-    L2LP(0) L2LP(1) L2LP(2) L2LP(3) L2LP(4) L2LP(5)
+    L2LP(0) L2LP(1) L2LP(2) L2LP(3) L2LP(4) L2LP(5) L2LP(6)
 #undef L2LP
     default:
       return false;
@@ -353,7 +359,7 @@ static bool l2l_pull_dispatch(int order, const int32_t* leaves, int64_t n_leaves
 bool launch_l2l_pull(int dtype, int order, const int32_t* leaves, int64_t n_leaves,
                      const int32_t* parent, const double* centre, const void* local,
                      const int64_t* toff, const void* part, void* out, hipStream_t st) {
-  if (order > 5) return false;
+  if (order > 6) return false;
   if (n_leaves <= 0) return true;
   return dtype == FMM_F64 ? l2l_pull_dispatch<double>(order, leaves, n_leaves, parent, centre,
                                                       local, toff, part, out, st)
@@ -372,8 +378,20 @@ static bool l2l_reg_dispatch(int order, int64_t lvl_begin, int64_t lvl_count, co
     k_l2l_reg<T, P><<<g, 256, 0, st>>>(lvl_begin, lvl_count, parent, centre, (T*)local,     \
                                        skip_leaves);                                        \
     return true;
-    L2LR(0) L2LR(1) L2LR(2) L2LR(3) L2LR(4) L2LR(5)
+    L2LR(0) L2LR(1) L2LR(2) L2LR(3) L2LR(4) L2LR(5) L2LR(6)
 #undef L2LR
+    case 7:  // fp64 only
+    case 8:
+      if constexpr (std::is_same<T, double>::value) {
+        if (order == 7)
+          k_l2l_reg<T, 7><<<g, 256, 0, st>>>(lvl_begin, lvl_count, parent, centre, (T*)local,
+                                             skip_leaves);
+        else
+          k_l2l_reg<T, 8><<<g, 256, 0, st>>>(lvl_begin, lvl_count, parent, centre, (T*)local,
+                                             skip_leaves);
+        return true;
+      }
+      return false;
     default:
       return false;
   }
@@ -390,8 +408,20 @@ static bool p2m_reg_dispatch(int order, const void* pts, const int32_t* leaves, 
     k_p2m_reg<T, P><<<g, 256, 0, st>>>((const P4<T>*)pts, leaves, n_leaves, begin, count, centre, \
                                        (T*)mpole);                                               \
     return true;
-    P2MR(0) P2MR(1) P2MR(2) P2MR(3) P2MR(4) P2MR(5)
+    P2MR(0) P2MR(1) P2MR(2) P2MR(3) P2MR(4) P2MR(5) P2MR(6)
 #undef P2MR
+    case 7:
+    case 8:  // fp64 only
+      if constexpr (std::is_same<T, double>::value) {
+        if (order == 7)
+          k_p2m_reg<T, 7><<<g, 256, 0, st>>>((const P4<T>*)pts, leaves, n_leaves, begin, count,
+                                             centre, (T*)mpole);
+        else
+          k_p2m_reg<T, 8><<<g, 256, 0, st>>>((const P4<T>*)pts, leaves, n_leaves, begin, count,
+                                             centre, (T*)mpole);
+        return true;
+      }
+      return false;
     default:
       return false;
   }
@@ -408,8 +438,20 @@ static bool m2m_reg_dispatch(int order, int64_t lvl_begin, int64_t lvl_count,
     k_m2m_reg<T, P><<<g, 256, 0, st>>>(lvl_begin, lvl_count, first_child, n_child, centre, \
                                        (T*)mpole);                                    \
     return true;
-    M2MR(0) M2MR(1) M2MR(2) M2MR(3) M2MR(4) M2MR(5)
+    M2MR(0) M2MR(1) M2MR(2) M2MR(3) M2MR(4) M2MR(5) M2MR(6)
 #undef M2MR
+    case 7:  // fp64 only
+    case 8:
+      if constexpr (std::is_same<T, double>::value) {
+        if (order == 7)
+          k_m2m_reg<T, 7><<<g, 256, 0, st>>>(lvl_begin, lvl_count, first_child, n_child, centre,
+                                             (T*)mpole);
+        else
+          k_m2m_reg<T, 8><<<g, 256, 0, st>>>(lvl_begin, lvl_count, first_child, n_child, centre,
+                                             (T*)mpole);
+        return true;
+      }
+      return false;
     default:
       return false;
   }
@@ -785,7 +827,7 @@ __global__ void __launch_bounds__(EX_THREADS)
   }
 }
 
-// The same moments for orders <= 5, one thread per leaf, all in registers.
+// The same moments for orders <= 6, one thread per leaf, all in registers.
 template <typename T, int P>
 __global__ void __launch_bounds__(256)
     k_p2m_dip_reg(const P8<T>* rec, const int32_t* leaves, int64_t n_leaves, const int32_t* begin,
@@ -837,7 +879,7 @@ static bool p2m_dip_reg_dispatch(int order, const void* rec, const int32_t* leav
     k_p2m_dip_reg<T, P><<<g, 256, 0, st>>>((const P8<T>*)rec, leaves, n_leaves, begin, count, \
                                            centre, (T*)mpole);                            \
     return true;
-    P2MDR(0) P2MDR(1) P2MDR(2) P2MDR(3) P2MDR(4) P2MDR(5)
+    P2MDR(0) P2MDR(1) P2MDR(2) P2MDR(3) P2MDR(4) P2MDR(5) P2MDR(6)
 #undef P2MDR
     default:
       return false;
