@@ -109,6 +109,9 @@ typedef __attribute__((address_space(3))) void lvoid_t;
 
 template <typename T, int P>
 struct SibCfg {
+  // waves per SIMD the register budget is cut for: two at order 6 (256
+  // registers, a few spilled, instead of 284 and one wave)
+  static constexpr int WPE = P == 6 && sizeof(T) == 8 ? 2 : 1;
   static constexpr int KR = HTabs<P>::KR;
   static constexpr int RB = mrec_bytes(KR, sizeof(T));       // record bytes
   static constexpr int CB = mrec_centre_byte(KR, sizeof(T)); // centre offset in a record
@@ -166,7 +169,7 @@ __device__ __forceinline__ void dtensor_contract(T x, T y, T z, const T* Ms,
 }
 
 template <typename T, int P>
-__global__ void __launch_bounds__(M2L_THREADS)
+__global__ void __launch_bounds__(M2L_THREADS) __attribute__((amdgpu_waves_per_eu(SibCfg<T, P>::WPE, 8)))
     k_m2l_sib(int64_t n_parents, const int32_t* __restrict__ parents,
               const int32_t* __restrict__ first_child, const uint8_t* __restrict__ n_child,
               const uint64_t* __restrict__ upool, const int64_t* __restrict__ u_off,
