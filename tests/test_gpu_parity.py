@@ -252,12 +252,15 @@ def test_nonfinite_input_rejected():
     plan.close()
 
 
-def test_expansions_match_oracle(orc):
-    """Moments and locals of every cell (after the downward pass)."""
+@pytest.mark.parametrize("order", [5, 6, 7])
+def test_expansions_match_oracle(orc, order):
+    """Moments and locals of every cell (after the downward pass): orders 5
+    and 6 take the one-launch downward pass (internal locals rebuilt on a
+    copy), order 7 the level-by-level one."""
     pos, mass = W.make("plummer", 4000, 61)
-    plan, phi, acc = gpu_run(pos, mass, 5, 0.6, 16, "f64")
+    plan, phi, acc = gpu_run(pos, mass, order, 0.6, 16, "f64")
     mp, lc = plan.copy_expansions()
-    ref = orc.fmm(pos, mass, 5, 0.6, 16, expansions=True)
+    ref = orc.fmm(pos, mass, order, 0.6, 16, expansions=True)
     scale_m = np.abs(ref.mpole).max(axis=1, keepdims=True)
     assert np.max(np.abs(mp - ref.mpole) / scale_m) < 1e-12
     scale_l = np.abs(ref.local).max(axis=1, keepdims=True) + 1e-300
