@@ -487,6 +487,64 @@ def test_vjp_degenerate(orc, kind):
         assert np.abs(mb - dm).max() <= 1e-12 * np.abs(dm).max()
 
 
+def test_vjp_matches_forward_differences():
+    """The VJP against central differences of the GPU's own forward
+    evaluation, S = sum pb.phi + ab.a: masses (S is linear in each, so the
+    difference is exact up to rounding) and positions of particles whose keys
+    and lists do not change under the step.  At order 8, theta 0.3 the two
+    differ only by the expansions' truncation."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    dev = torch.device("cuda:0")
+    n, order, theta, leaf = 2000, 8, 0.3, 16
+    pos, mass = W.make("plummer", n, 98)
+    pb, ab = sensitivities(n, 99, "f64")
+    plan = Plan(n, order=order, theta=theta, leaf_size=leaf, dtype=torch.float64, device=dev)
+    tpb, tab = torch.from_numpy(pb).to(dev), torch.from_numpy(ab).to(dev)
+
+    def S(p, m):
+        plan.build(torch.from_numpy(p).to(dev), torch.from_numpy(m).to(dev))
+        phi, acc = plan.eval()
+        torch.cuda.synchronize()
+        return float((tpb * phi).sum() + (tab * acc).sum())
+
+    S(pos, mass)
+    keys0, _ = plan.copy_keys()
+    lists0 = plan.copy_lists()
+    xb, mb = plan.vjp(tpb, tab)
+    xb, mb = xb.cpu().numpy(), mb.cpu().numpy()
+    gscale = np.abs(xb).max()
+    for i in (3, 500, 1999):
+        h = 1e-3 * mass[i]
+        mp, mm = mass.copy(), mass.copy()
+        mp[i] += h
+        mm[i] -= h
+        fd = (S(pos, mp) - S(pos, mm)) / (2 * h)
+        assert abs(fd - mb[i]) <= 1e-6 * np.abs(mb).max(), (i, fd, mb[i])
+    checked = 0
+    for i in range(0, n, 97):
+        for a in range(3):
+            h = 1e-7
+            pp, pm = pos.copy(), pos.copy()
+            pp[i, a] += h
+            pm[i, a] -= h
+            sp = S(pp, mass)
+            same = np.array_equal(plan.copy_keys()[0], keys0) and \
+                np.array_equal(plan.copy_lists()["p2p_src"], lists0["p2p_src"])
+            sm = S(pm, mass)
+            same = same and np.array_equal(plan.copy_keys()[0], keys0) and \
+                np.array_equal(plan.copy_lists()["p2p_src"], lists0["p2p_src"])
+            if not same:
+                continue
+            fd = (sp - sm) / (2 * h)
+            assert abs(fd - xb[i, a]) <= 1e-5 * gscale, (i, a, fd, xb[i, a])
+            checked += 1
+        if checked >= 12:
+            break
+    assert checked >= 6
+    plan.close()
+
+
 def test_vjp_rejects_bad_arguments():
     torch = _torch()
     from multipole_body_gravity_amd import FmmError, Plan
