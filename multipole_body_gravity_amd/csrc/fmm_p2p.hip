@@ -293,7 +293,10 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
           const int nv = min(TT, tot - q0);
           if (nv == TT) {
             // a full stage: the same number of sources on every lane
-            for (int k = 0; k < per; k++) {
+            // the trip count is uniform: the counter is kept in a scalar
+            // register, so the loop control costs no vector instructions
+            const int per_s = __builtin_amdgcn_readfirstlane(per);
+            for (int k = 0; k < per_s; k = __builtin_amdgcn_readfirstlane(k + 1)) {
               const Rec pj = staged(sl + k * ns);
               Pair::add(p0, pj, a0, a1, a2, a3);
               Pair::add(p1, pj, b0, b1, b2, b3);
