@@ -222,7 +222,7 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
     return u.r;
   };
   const int lane = __lane_id();
-  const int w = threadIdx.x / WAVE;
+  const int w = uniform((int)(threadIdx.x / WAVE));
   for (int64_t ti = (int64_t)blockIdx.x * P2P_WAVES + w; ti < n_tasks;
        ti += (int64_t)gridDim.x * P2P_WAVES) {
     const P2PTask task = tasks[ti];
@@ -280,8 +280,9 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
             const int q = q0 + k;
             if (k < TT && q < tot) {
               // record k of the stage straight into LDS, piece h into plane h
+              // (the record index in 32 bits: particle indices fit an int)
               const unsigned char* g =
-                  (const unsigned char*)(pts + sh.sbase[one ? 0 : sh.owner[q]] + q);
+                  (const unsigned char*)(pts + (sh.sbase[one ? 0 : sh.owner[q]] + q));
 #pragma unroll
               for (int h = 0; h < NH; h++)
                 __builtin_amdgcn_global_load_lds((p2p_gvoid_t*)(g + 16 * h),
@@ -368,7 +369,7 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
           T* __restrict__ part) {
   __shared__ P2PShared<T, P4<T>, ForcePair<T>::MAXQ> sh_all[P2P_WAVES];
   p2p_tasks<T, ForcePair<T>>(tasks, n_tasks, begin, count, src, pts, far, perm, phi, acc, part,
-                             sh_all[threadIdx.x / WAVE]);
+                             sh_all[uniform((int)(threadIdx.x / WAVE))]);
 }
 
 // VJP near field: out1 = dS/dm, out3 = dS/dx, with `far` holding the far-field
@@ -382,7 +383,7 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
               T* __restrict__ part) {
   __shared__ P2PShared<T, P8<T>, VjpPair<T>::MAXQ> sh_all[P2P_WAVES];
   p2p_tasks<T, VjpPair<T>>(tasks, n_tasks, begin, count, src, recs, far, perm, mbar, xbar, part,
-                           sh_all[threadIdx.x / WAVE]);
+                           sh_all[uniform((int)(threadIdx.x / WAVE))]);
 }
 
 // Leaves split over several tasks, one block per leaf: thread (t, s) adds the
