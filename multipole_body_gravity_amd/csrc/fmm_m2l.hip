@@ -181,7 +181,10 @@ __global__ void __launch_bounds__(M2L_THREADS) __attribute__((amdgpu_waves_per_e
   __shared__ __attribute__((aligned(16))) unsigned char ring[WPB][C::NS][C::SB];
   __shared__ int32_t wid[WPB][C::WIN];
   __shared__ uint8_t wmk[WPB][C::WIN];
-  const int lane = __lane_id(), w = threadIdx.x / WAVE;
+  // the wave index in a scalar register (fewer vector registers and
+  // instructions), except at orders 7 and 8, where it raised the spills
+  const int lane = __lane_id(),
+            w = P <= 6 ? uniform((int)(threadIdx.x / WAVE)) : (int)(threadIdx.x / WAVE);
   const int t = lane >> 3, j = lane & 7;
   // this lane's piece of each copy instruction: record slot ps (8 = padding) and piece pq
   int ps[C::NI], pq[C::NI];
