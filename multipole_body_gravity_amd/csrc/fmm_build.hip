@@ -393,12 +393,18 @@ hipError_t launch_keys(const void* pos, int64_t n, int dtype, const RootInfo* ro
 // LSD radix sort of (u64 key, i32 index), stable, digits of 8 or 9 bits
 // ===================================================================
 constexpr int RS_THREADS = 256;
-constexpr int RS_ROUNDS = 16;
-constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
 constexpr int RS_MAX_RADIX = 512;
+// Keys per thread of a tile: 8 up to 2^23 keys, 16 above.  Each tile is one
+// dependent chain (load, rank, reorder, write); with the shorter tiles a sort
+// of 10^6 keys has two per compute unit instead of one, whose chains overlap
+// (7 % off the 10^6-key sort); at 1.7*10^7 keys and more the longer tiles win
+// (half the per-tile histograms to scan).
+constexpr int64_t RS_SHORT_TILES_MAX = (int64_t)1 << 23;
+static int64_t rs_tile(int64_t n) { return RS_THREADS * (n <= RS_SHORT_TILES_MAX ? 8 : 16); }
 
 size_t radix_hist_ints(int64_t n) {
-  int64_t nb = (n + RS_TILE - 1) / RS_TILE;
+  const int64_t tile = rs_tile(n);
+  int64_t nb = (n + tile - 1) / tile;
   return (size_t)(RS_MAX_RADIX * nb);
 }
 
@@ -415,11 +421,12 @@ __device__ __forceinline__ uint64_t same_digit(int d, bool valid) {
   return mask;
 }
 
-template <int RB>
+template <int RB, int RS_ROUNDS>
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_hist(const uint64_t* keys, int64_t n, int shift, uint32_t dmask, int32_t* hist,
                  int nblk) {
   constexpr int R = 1 << RB;
+  constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
   __shared__ int h[R];
   for (int d = threadIdx.x; d < R; d += RS_THREADS) h[d] = 0;
   __syncthreads();
@@ -450,11 +457,12 @@ __global__ void __launch_bounds__(RS_THREADS)
 // of the digit.  The per-wave counts are then combined in wave order (earlier
 // quarters first) and over digits, the tile is reordered by digit in LDS and
 // written out in that order, so each digit's run goes to consecutive addresses.
-template <int RB>
+template <int RB, int RS_ROUNDS>
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
                     int64_t n, int shift, uint32_t dmask, const int32_t* hist_scan, int nblk) {
   constexpr int R = 1 << RB;
+  constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
   constexpr int DPT = R / RS_THREADS;  // digits per thread in the digit scan (1 or 2)
   constexpr int NW = RS_THREADS / WAVE;
   constexpr int WTILE = RS_TILE / NW;  // elements per wave
@@ -475,10 +483,12 @@ __global__ void __launch_bounds__(RS_THREADS)
   const uint64_t lt = lanemask_lt();
   int rk[RS_ROUNDS];  // rank of this lane's element of each round among its digit in the wave
   uint64_t kk[RS_ROUNDS];
+  int32_t vv[RS_ROUNDS];
 #pragma unroll
-  for (int r = 0; r < RS_ROUNDS; r++) {  // all loads issued before the first use
+  for (int r = 0; r < RS_ROUNDS; r++) {  // all loads (keys and values) issued before the first use
     const int64_t i = wbase + r * WAVE + lane;
     kk[r] = i < n ? kin[i] : 0ull;
+    vv[r] = (vin && i < n) ? vin[i] : 0;
   }
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
@@ -523,12 +533,6 @@ __global__ void __launch_bounds__(RS_THREADS)
     }
   }
   __syncthreads();
-  int32_t vv[RS_ROUNDS];
-#pragma unroll
-  for (int r = 0; r < RS_ROUNDS; r++) {
-    const int64_t i = wbase + r * WAVE + lane;
-    vv[r] = (vin && i < n) ? vin[i] : 0;
-  }
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; r++) {
     const int64_t i = wbase + r * WAVE + lane;
@@ -561,7 +565,9 @@ hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_a
                                   hipStream_t st) {
   *in_alt = false;
   if (n <= 0 || bits <= 0) return hipSuccess;
-  const int nblk = (int)((n + RS_TILE - 1) / RS_TILE);
+  const int64_t tile = rs_tile(n);
+  const bool shortt = tile == RS_THREADS * 8;
+  const int nblk = (int)((n + tile - 1) / tile);
   const int rb = (bits + 8) / 9 < (bits + 7) / 8 ? 9 : 8;
   const int passes = (bits + rb - 1) / rb;
   uint64_t *ka = keys, *kb = keys_alt;
@@ -571,16 +577,28 @@ hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_a
     const int db = std::min(rb, lo_bit + bits - shift);
     const uint32_t dmask = (1u << db) - 1u;
     const int64_t nh = ((int64_t)1 << rb) * nblk;
-    if (rb == 9)
-      k_radix_hist<9><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+    if (rb == 9 && shortt)
+      k_radix_hist<9, 8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+    else if (rb == 9)
+      k_radix_hist<9, 16><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+    else if (shortt)
+      k_radix_hist<8, 8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
     else
-      k_radix_hist<8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+      k_radix_hist<8, 16><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
     hipError_t e = scan_excl<int32_t>(hist, hist, nh, nullptr, scan_tmp, st);
     if (e != hipSuccess) return e;
-    if (rb == 9)
-      k_radix_scatter<9><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist, nblk);
+    if (rb == 9 && shortt)
+      k_radix_scatter<9, 8><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
+                                                           nblk);
+    else if (rb == 9)
+      k_radix_scatter<9, 16><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
+                                                            nblk);
+    else if (shortt)
+      k_radix_scatter<8, 8><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
+                                                           nblk);
     else
-      k_radix_scatter<8><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist, nblk);
+      k_radix_scatter<8, 16><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
+                                                            nblk);
     uint64_t* tk = ka;
     ka = kb;
     kb = tk;
