@@ -679,6 +679,42 @@ __global__ void k_tree_lcp(const uint64_t* keys, int64_t n, int S, int8_t* lcp, 
   }
 }
 
+// The same window maxima in one launch when the span fits a block's LDS:
+// each block forms wpad[x] for x in [i0, i0 + TW_OUT + span2 - 1) (-1 past
+// the end, the identity of the maximum), doubles the span in LDS up to span2,
+// and writes stj[i] = max of wpad[i .. i + span2 - 1] for its outputs; it
+// also writes lcp for its indices below n.
+constexpr int TW_OUT = 1024;       // outputs per block
+constexpr int TW_SPAN_MAX = 1024;  // largest span taken in one launch
+__global__ void __launch_bounds__(256)
+    k_tree_window(const uint64_t* keys, int64_t n, int S, int span2, int8_t* lcp, int8_t* stj,
+                  int64_t wlen) {
+  __shared__ int8_t buf[2][TW_OUT + TW_SPAN_MAX];
+  const int64_t i0 = (int64_t)blockIdx.x * TW_OUT;
+  int len = TW_OUT + span2 - 1;
+  for (int x = threadIdx.x; x < len; x += blockDim.x) {
+    const int64_t i = i0 + x;
+    buf[0][x] = (int8_t)((i >= S && i < n) ? shared_level(keys[i - S], keys[i]) : -1);
+  }
+  for (int x = threadIdx.x; x < TW_OUT; x += blockDim.x) {
+    const int64_t i = i0 + x;
+    if (i < n) lcp[i] = (int8_t)(i == 0 ? -1 : shared_level(keys[i - 1], keys[i]));
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int h = 1; h < span2; h *= 2) {  // spans h -> 2h
+    len -= h;
+    for (int x = threadIdx.x; x < len; x += blockDim.x)
+      buf[cur ^ 1][x] = max(buf[cur][x], buf[cur][x + h]);
+    __syncthreads();
+    cur ^= 1;
+  }
+  for (int x = threadIdx.x; x < TW_OUT; x += blockDim.x) {
+    const int64_t i = i0 + x;
+    if (i < wlen) stj[i] = buf[cur][x];
+  }
+}
+
 __global__ void k_tree_stmax(const int8_t* in, int8_t* out, int64_t len, int64_t half) {
   int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= len) return;
@@ -755,17 +791,26 @@ hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t*
   int64_t span2 = 1;
   if ((int64_t)S < n) {
     int64_t wlen = n + S;
-    k_tree_lcp<<<(unsigned)((wlen + 255) / 256), 256, 0, st>>>(keys, n, S, lcp, wlev, wlen);
-    // sparse-table levels until the span 2^J <= S + 1 < 2^(J+1)
-    int8_t *a = wlev, *b = wtmp;
-    while (span2 * 2 <= (int64_t)S + 1) {
-      k_tree_stmax<<<(unsigned)((wlen + 255) / 256), 256, 0, st>>>(a, b, wlen, span2);
-      int8_t* t = a;
-      a = b;
-      b = t;
-      span2 *= 2;
+    int64_t want = 1;  // the span 2^J <= S + 1 < 2^(J+1)
+    while (want * 2 <= (int64_t)S + 1) want *= 2;
+    if (want <= TW_SPAN_MAX) {
+      k_tree_window<<<(unsigned)((wlen + TW_OUT - 1) / TW_OUT), 256, 0, st>>>(keys, n, S, (int)want,
+                                                                              lcp, wlev, wlen);
+      span2 = want;
+      stj = wlev;
+    } else {
+      k_tree_lcp<<<(unsigned)((wlen + 255) / 256), 256, 0, st>>>(keys, n, S, lcp, wlev, wlen);
+      // sparse-table levels, one launch per doubling of the span
+      int8_t *a = wlev, *b = wtmp;
+      while (span2 < want) {
+        k_tree_stmax<<<(unsigned)((wlen + 255) / 256), 256, 0, st>>>(a, b, wlen, span2);
+        int8_t* t = a;
+        a = b;
+        b = t;
+        span2 *= 2;
+      }
+      stj = a;
     }
-    stj = a;
   } else {
     k_tree_lcp<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, S, lcp, nullptr, 0);
   }

@@ -130,7 +130,7 @@ def test_two_body_and_single(orc):
 
 
 @pytest.mark.parametrize("kind", ["line", "plane", "tight_cluster", "leaf_eq_n", "leaf_n_plus_1",
-                                  "root_leaf_big"])
+                                  "root_leaf_big", "leaf_1500", "leaf_2500"])
 def test_degenerate_inputs(orc, kind):
     rng = np.random.default_rng(41)
     leaf = 8
@@ -147,6 +147,11 @@ def test_degenerate_inputs(orc, kind):
         pos = rng.random((8, 3))
     elif kind == "leaf_n_plus_1":
         pos = rng.random((9, 3))
+    elif kind in ("leaf_1500", "leaf_2500"):
+        # leaf windows of 1501 and 2501 keys: the widest span the tree's
+        # one-launch window maximum takes, and one past it (sparse-table passes)
+        pos = np.vstack([rng.random((3000, 3)), 0.3 + 0.01 * rng.random((3000, 3))])
+        leaf = int(kind[5:])
     else:
         pos = rng.random((300, 3))
         leaf = 1000
