@@ -222,7 +222,9 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
     return u.r;
   };
   const int lane = __lane_id();
-  const int w = uniform((int)(threadIdx.x / WAVE));
+  // fp64: the wave index in a scalar register (fewer vector registers and
+  // instructions); the fp32 kernel ran slower with it on the 256^3 lattice
+  const int w = sizeof(T) == 8 ? uniform((int)(threadIdx.x / WAVE)) : (int)(threadIdx.x / WAVE);
   for (int64_t ti = (int64_t)blockIdx.x * P2P_WAVES + w; ti < n_tasks;
        ti += (int64_t)gridDim.x * P2P_WAVES) {
     const P2PTask task = tasks[ti];
@@ -280,9 +282,11 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
             const int q = q0 + k;
             if (k < TT && q < tot) {
               // record k of the stage straight into LDS, piece h into plane h
-              // (the record index in 32 bits: particle indices fit an int)
-              const unsigned char* g =
-                  (const unsigned char*)(pts + (sh.sbase[one ? 0 : sh.owner[q]] + q));
+              // (fp64: the record index in 32 bits, particle indices fit an int;
+              // the fp32 kernel ran slower on the 256^3 lattice with it)
+              const int32_t sbq = sh.sbase[one ? 0 : sh.owner[q]];
+              const unsigned char* g = (const unsigned char*)(sizeof(T) == 8 ? pts + (sbq + q)
+                                                                             : pts + sbq + q);
 #pragma unroll
               for (int h = 0; h < NH; h++)
                 __builtin_amdgcn_global_load_lds((p2p_gvoid_t*)(g + 16 * h),
@@ -368,8 +372,9 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
           const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
           T* __restrict__ part) {
   __shared__ P2PShared<T, P4<T>, ForcePair<T>::MAXQ> sh_all[P2P_WAVES];
+  const int w = sizeof(T) == 8 ? uniform((int)(threadIdx.x / WAVE)) : (int)(threadIdx.x / WAVE);
   p2p_tasks<T, ForcePair<T>>(tasks, n_tasks, begin, count, src, pts, far, perm, phi, acc, part,
-                             sh_all[uniform((int)(threadIdx.x / WAVE))]);
+                             sh_all[w]);
 }
 
 // VJP near field: out1 = dS/dm, out3 = dS/dx, with `far` holding the far-field
@@ -382,8 +387,9 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
               const int32_t* __restrict__ perm, T* __restrict__ mbar, T* __restrict__ xbar,
               T* __restrict__ part) {
   __shared__ P2PShared<T, P8<T>, VjpPair<T>::MAXQ> sh_all[P2P_WAVES];
+  const int w = sizeof(T) == 8 ? uniform((int)(threadIdx.x / WAVE)) : (int)(threadIdx.x / WAVE);
   p2p_tasks<T, VjpPair<T>>(tasks, n_tasks, begin, count, src, recs, far, perm, mbar, xbar, part,
-                           sh_all[uniform((int)(threadIdx.x / WAVE))]);
+                           sh_all[w]);
 }
 
 // Leaves split over several tasks, one block per leaf: thread (t, s) adds the
