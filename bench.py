@@ -437,7 +437,7 @@ def main():
                     help="time forward + VJP steps (build, eval, fmm_vjp) instead of the forward step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+        print("bench.py: the library runs on one GPU only (no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
