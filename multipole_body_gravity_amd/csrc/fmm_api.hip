@@ -186,18 +186,31 @@ int issue_upward(fmm_plan_t p) {
 
 // The sibling M2L on the second stream: after the upward pass (same stream)
 // and the launch order (ev_order on the walk's stream).  ev_up marks its end.
-int issue_sibling_m2l(fmm_plan_t p, hipStream_t st) {
+// `capped`: two blocks (one wave per SIMD each) per compute unit, so that its
+// waves never take all of a SIMD's registers and the walk's short kernels
+// beside it (which raise their issue priority) find room on every unit.
+int issue_sibling_m2l(fmm_plan_t p, hipStream_t st, bool capped) {
   hipStream_t us = p->up_stream;
   TRY_HIP(hipEventRecord(p->ev_order, st));
   TRY_HIP(hipStreamWaitEvent(us, p->ev_order, 0));
   M2LArgs ma = m2l_args(p);
   ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_SIB : nullptr;
   ma.ran = p->kran + FMM_KERNEL_M2L_SIB;
+  ma.max_blocks = capped ? 2 * (int64_t)std::max(p->n_cu, 1) : 0;
   rec(p, FMM_STAGE_M2L, 0, us);
   TRY_HIP(launch_m2l_sib(p->dtype, p->order, ma, us));
   rec(p, FMM_STAGE_M2L, 1, us);
   TRY_HIP(hipEventRecord(p->ev_up, us));
   return FMM_OK;
+}
+
+// Expected duration of the sibling M2L over `own` own entries: about
+// 444 ((p + 1) / 5)^4 flops per entry at the rate the kernel reaches
+// (36 TFLOP/s in fp64, 60 in fp32 on this part).
+static double sibling_seconds(const fmm_plan_t p, int64_t own) {
+  const double q = (p->order + 1) / 5.0;
+  const double flops = 444.0 * q * q * q * q * (double)own;
+  return flops / (p->dtype == FMM_F64 ? 36e12 : 60e12);
 }
 
 int run_walk(fmm_plan_t p, hipStream_t st) {
@@ -317,6 +330,12 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   // second stream, where it overlaps the rest of the walk
   TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
   TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, dctrl, P<int32_t>(p->m2l_order), st));
+  // A short sibling M2L (under a millisecond) starts now on a capped grid, so
+  // that it runs beside the transposed sort and the rest of the walk (2 % off
+  // the 10^6 step); a long one waits for the transposed sort and takes the
+  // whole GPU (capped, it ran 12 % slower on the 4*10^7 sphere).
+  const bool sib_early = sibling_seconds(p, own_m) < 1e-3;
+  if (sib_early) TRY(issue_sibling_m2l(p, st, true));
 
   // transposed entries: emitted in group order (ascending source for each
   // target), then stably sorted on (kind, target); run lengths per target
@@ -343,9 +362,9 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     TRY_HIP(launch_tr_runs(sorted, ntr, a.key_shift, kind_bit, nn, tr_start, tr_cnt, st));
   }
   p->tr_sorted = sorted;
-  // the sibling M2L beside the rest of the walk (after the transposed sort:
-  // beside that sort it was slower, the sort's kernels being starved)
-  TRY(issue_sibling_m2l(p, st));
+  // a long sibling M2L beside the rest of the walk, after the transposed sort
+  // (beside that sort, on a full grid, the sort's kernels were starved)
+  if (!sib_early) TRY(issue_sibling_m2l(p, st, false));
 
   // P2P lists: own entries (from the parents' P2P unions) then transposed ones
   int64_t* p2p_off = P<int64_t>(p->p2p_off);
@@ -499,7 +518,10 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
     fmm_destroy(p);
     return r;
   };
-  if (hipGetDevice(&p->device) != hipSuccess) return fail(FMM_ERR_HIP);
+  if (hipGetDevice(&p->device) != hipSuccess ||
+      hipDeviceGetAttribute(&p->n_cu, hipDeviceAttributeMultiprocessorCount, p->device) !=
+          hipSuccess)
+    return fail(FMM_ERR_HIP);
   const size_t w = wbytes(dtype);
   if ((rc = grow(p->keys, 8 * n)) || (rc = grow(p->keys_alt, 8 * n)) || (rc = grow(p->idx, 4 * n)) ||
       (rc = grow(p->idx_alt, 4 * n)) || (rc = grow(p->pts, 4 * w * n)) ||

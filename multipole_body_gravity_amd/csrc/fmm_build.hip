@@ -38,6 +38,7 @@ __device__ I block_excl_scan(I v, I* total) {
 
 template <typename I>
 __global__ void __launch_bounds__(SCAN_THREADS) k_scan_reduce(const I* in, int64_t n, I* sums) {
+  bookkeeping_priority();
   int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
   I s = 0;
 #pragma unroll
@@ -50,6 +51,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_reduce(const I* in, int64
 
 template <typename I>
 __global__ void __launch_bounds__(SCAN_THREADS) k_scan_top(I* sums, int64_t nb, I* total) {
+  bookkeeping_priority();
   __shared__ I carry_s;
   if (threadIdx.x == 0) carry_s = 0;
   __syncthreads();
@@ -70,6 +72,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_top(I* sums, int64_t nb, 
 template <typename I>
 __global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply(const I* in, I* out, int64_t n,
                                                              const I* sums) {
+  bookkeeping_priority();
   int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
   I v[SCAN_ITEMS];
   I s = 0;
@@ -93,6 +96,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply(const I* in, I* out
 template <typename I>
 __global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply_direct(const I* in, I* out, int64_t n,
                                                                     const I* sums, I* total) {
+  bookkeeping_priority();
   I part = 0;
   if (sums)
     for (int64_t i = threadIdx.x; i < (int64_t)blockIdx.x; i += SCAN_THREADS) part += sums[i];
@@ -123,6 +127,7 @@ size_t scan_tmp_bytes(int64_t n) {
 
 template <typename I>
 __global__ void k_set_zero(I* p) {
+  bookkeeping_priority();
   if (threadIdx.x == 0) *p = 0;
 }
 
@@ -161,6 +166,7 @@ struct ScanMulti {
 template <int R>
 __global__ void __launch_bounds__(SCAN_THREADS) k_scan_multi_reduce(ScanMulti<R> a, int64_t n,
                                                                     int64_t* sums) {
+  bookkeeping_priority();
   const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
 #pragma unroll
   for (int r = 0; r < R; r++) {
@@ -178,6 +184,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_multi_reduce(ScanMulti<R>
 template <int R>
 __global__ void __launch_bounds__(SCAN_THREADS) k_scan_multi_apply(ScanMulti<R> a, int64_t n,
                                                                    const int64_t* sums) {
+  bookkeeping_priority();
   const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
 #pragma unroll
   for (int r = 0; r < R; r++) {
@@ -425,6 +432,7 @@ template <int RB, int RS_ROUNDS>
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_hist(const uint64_t* keys, int64_t n, int shift, uint32_t dmask, int32_t* hist,
                  int nblk) {
+  bookkeeping_priority();
   constexpr int R = 1 << RB;
   constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
   __shared__ int h[R];
@@ -461,6 +469,7 @@ template <int RB, int RS_ROUNDS>
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
                     int64_t n, int shift, uint32_t dmask, const int32_t* hist_scan, int nblk) {
+  bookkeeping_priority();
   constexpr int R = 1 << RB;
   constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
   constexpr int DPT = R / RS_THREADS;  // digits per thread in the digit scan (1 or 2)

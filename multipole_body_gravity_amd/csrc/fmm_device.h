@@ -25,6 +25,12 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Issue priority of a wave among those on its SIMD.  The short, latency-bound
+// kernels that build the lists and tasks can run beside the ALU-bound sibling
+// M2L on the other stream; raising their waves' priority lets their few
+// instructions through ahead of the M2L's long arithmetic stream.
+__device__ __forceinline__ void bookkeeping_priority() { __builtin_amdgcn_s_setprio(3); }
+
 // ---- cross-lane moves inside rows of 16 lanes (DPP), no LDS round trip ----
 // DPP controls: quad_perm, row_shr:n, row_mirror, row_half_mirror.  A lane
 // whose source lies outside its row receives 0.

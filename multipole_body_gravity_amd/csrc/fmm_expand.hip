@@ -1002,6 +1002,7 @@ hipError_t launch_l2p_vjp(int dtype, int order, int64_t n, const void* rec, cons
 
 // ---------------- helpers ----------------
 __global__ void k_fill_zero(uint32_t* p, size_t n_words) {
+  bookkeeping_priority();
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_words;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0u;

@@ -77,6 +77,7 @@ struct fmm_plan_s {
   int order, K, leaf, dtype;
   double theta, t2;
   int device;
+  int n_cu = 0;  // compute units of the device
   bool built = false, evaluated = false, timing = false;
   bool l2l_pulled = false;  // last eval used the one-launch downward pass
 
@@ -301,6 +302,7 @@ struct M2LArgs {
   void* local;
   hipEvent_t* ev;         // null, or begin/end events of the sibling and tail kernels
   bool* ran;              // with ev: set when the kernel was launched
+  int64_t max_blocks;     // > 0: grid cap of the sibling kernel (its waves loop over parents)
 };
 // own entries: clears the root's local, then the sibling kernel writes the
 // local of every other node (a.local)

@@ -381,6 +381,7 @@ __global__ void k_m2l_tail_combine(int64_t n_leaves, int K, const int32_t* __res
 
 __global__ void k_tail_fill(const int32_t* leaves, int64_t n_leaves, const int64_t* tr_start,
                             const int32_t* tr_cnt, const int64_t* toff, TailTask* tasks) {
+  bookkeeping_priority();
   const int64_t li = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (li >= n_leaves) return;
   const int64_t a = leaves[li];
@@ -474,7 +475,8 @@ static unsigned m2l_grid(int64_t waves) {
 
 template <typename T>
 static void m2l_sib_dispatch(int order, hipStream_t st, const M2LArgs& a) {
-  const unsigned gs = m2l_grid(a.n_parents);
+  unsigned gs = m2l_grid(a.n_parents);
+  if (a.max_blocks > 0 && (int64_t)gs > a.max_blocks) gs = (unsigned)a.max_blocks;
   const unsigned char* rec = (const unsigned char*)a.mrec;
   if (a.n_parents <= 0) return;
   // a.ev (optional): begin/end events of the sibling kernel

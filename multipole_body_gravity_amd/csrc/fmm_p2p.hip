@@ -47,6 +47,7 @@ __device__ __forceinline__ float p2p_rsqrt(float x) { return __builtin_amdgcn_rs
 __global__ void k_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
                                    const int32_t* count, const int32_t* tr_cnt, int64_t* ntask,
                                    int64_t* npart, int64_t* ntail, Control* ctrl) {
+  bookkeeping_priority();
   __shared__ int oct[ORDER_OCT];
   for (int b = threadIdx.x; b < ORDER_OCT; b += blockDim.x) oct[b] = 0;
   __syncthreads();
@@ -78,6 +79,7 @@ __global__ void __launch_bounds__(256)
     k_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
                     const int64_t* task_off, const int64_t* part_off, const int64_t* off,
                     const int32_t* count, Control* ctrl, P2PTask* tasks) {
+  bookkeeping_priority();
   const int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   P2PTask t{};
   int o = -1;

@@ -308,6 +308,7 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
 // candidate, children in order.
 __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a, int32_t* run_cnt,
                                                          int64_t run_n) {
+  bookkeeping_priority();
   // the run lengths of the next step start at zero (targets without a run)
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < run_n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -373,6 +374,7 @@ __global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf, int32
 // Runs of equal (kind, target) in the sorted keys: first index and end index.
 __global__ void k_tr_runs(const uint64_t* keys, int64_t n, int sh, int kind_bit, int64_t n_nodes,
                           int64_t* start, int32_t* cnt) {
+  bookkeeping_priority();
   int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (k >= n) return;
   const uint64_t g = keys[k] >> sh;  // kind and target
@@ -385,12 +387,14 @@ __global__ void k_tr_runs(const uint64_t* keys, int64_t n, int sh, int kind_bit,
 
 // run ends -> run lengths
 __global__ void k_tr_lengths(int64_t m, const int64_t* start, int32_t* cnt) {
+  bookkeeping_priority();
   int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i < m && cnt[i] > 0) cnt[i] = (int32_t)(cnt[i] - start[i]);
 }
 
 __global__ void k_walk_offsets(int64_t n, const int32_t* own, const int32_t* tr_cnt,
                                int64_t* tot) {
+  bookkeeping_priority();
   int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= n) return;
   tot[i] = (int64_t)own[i] + tr_cnt[i];
@@ -401,6 +405,7 @@ __global__ void k_walk_offsets(int64_t n, const int32_t* own, const int32_t* tr_
 __global__ void k_tr_scatter(const uint64_t* keys, int64_t n, int sh, int kind_bit, int kind,
                              int64_t n_nodes, const int64_t* off, const int32_t* own,
                              const int64_t* start, int32_t* src) {
+  bookkeeping_priority();
   int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (k >= n) return;
   const uint64_t key = keys[k];
@@ -415,6 +420,7 @@ __global__ void __launch_bounds__(WK_THREADS)
     k_union_scatter(const int32_t* parents, int64_t n_parents, const int32_t* first_child,
                     const uint8_t* n_child, const uint64_t* pool, const int64_t* uoff,
                     const int32_t* ucnt, const int64_t* off, int32_t* src) {
+  bookkeeping_priority();
   const uint64_t lt = lanemask_lt();
   const int lane = __lane_id();
   for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < n_parents;
@@ -446,6 +452,7 @@ __global__ void __launch_bounds__(WK_THREADS)
 // single list entry P2P(root <- root).
 // A root that is a leaf: its only P2P entry is itself.
 __global__ void k_walk_root_leaf(const int64_t* p2p_off, int32_t* p2p_src) {
+  bookkeeping_priority();
   if (threadIdx.x == 0) p2p_src[p2p_off[0]] = 0;
 }
 hipError_t launch_walk_root_leaf(const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st) {
