@@ -387,8 +387,9 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   // near-field tasks, their partial slots and the transposed-tail M2L tasks,
   // per leaf; offsets and totals (to the control block) in one scan
   int64_t* ttoff = P<int64_t>(p->tail_toff);
+  TRY(grow(p->split_leaves, (size_t)std::max<int64_t>(nl, 1) * 4));
   TRY_HIP(launch_leaf_task_counts(leaves, nl, p2p_off, P<int32_t>(p->ncount), tr_cnt, toff, poff,
-                                  ttoff, dctrl, st));
+                                  ttoff, P<int32_t>(p->split_leaves), dctrl, st));
   {
     const int64_t* in[3] = {toff, poff, ttoff};
     int64_t* out[3] = {toff, poff, ttoff};
@@ -399,6 +400,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   if (p->ctrl_host->n_p2p != p->n_p2p) return FMM_ERR_HIP;
   p->n_p2p_tasks = p->ctrl_host->n_p2p_tasks;
   p->n_p2p_part = p->ctrl_host->n_p2p_part;
+  p->n_split = p->ctrl_host->n_split;
   p->n_tail_tasks = p->ctrl_host->n_tail_tasks;
   TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
   TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
@@ -575,6 +577,7 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->tr_start_m2l, &p->tr_keys,   &p->tr_keys_alt, &p->tr_vals,
                   &p->tr_vals_alt, &p->m2l_off,    &p->m2l_src,     &p->p2p_off,
                   &p->p2p_src,    &p->p2p_task,    &p->p2p_part,    &p->p2p_toff,
+                  &p->split_leaves,
                   &p->p2p_poff,   &p->tot_m2l,     &p->tot_p2p,     &p->parents,
                   &p->m2l_order,
                   &p->tail_toff,  &p->tail_task,   &p->tail_part};
@@ -731,7 +734,8 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   TRY_HIP(launch_p2p(p->dtype, p->p2p_task.p, p->n_p2p_tasks, leaves, p->n_leaves,
                      P<int64_t>(p->p2p_toff), P<int64_t>(p->p2p_poff), P<int32_t>(p->nbegin),
                      P<int32_t>(p->ncount), P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
-                     P<int32_t>(p->idx), phi, acc, p->p2p_part.p, p->n_p2p_part > 0,
+                     P<int32_t>(p->idx), phi, acc, p->p2p_part.p,
+                     P<int32_t>(p->split_leaves), p->n_split,
                      p->timing ? p->kev + 2 * FMM_KERNEL_P2P : nullptr,
                      p->kran + FMM_KERNEL_P2P, st));
   rec(p, FMM_STAGE_P2P, 1, st);
@@ -805,7 +809,7 @@ int fmm_vjp(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_ba
                          P<int64_t>(p->p2p_toff), P<int64_t>(p->p2p_poff), P<int32_t>(p->nbegin),
                          P<int32_t>(p->ncount), P<int32_t>(p->p2p_src), p->vrec.p, p->vfar.p,
                          P<int32_t>(p->idx), mass_bar, pos_bar, p->p2p_part.p,
-                         p->n_p2p_part > 0,
+                         P<int32_t>(p->split_leaves), p->n_split,
                          p->timing ? p->kev + 2 * FMM_KERNEL_VJP_P2P : nullptr,
                          p->kran + FMM_KERNEL_VJP_P2P, st));
   rec(p, FMM_STAGE_VJP, 1, st);

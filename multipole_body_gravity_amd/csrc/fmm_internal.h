@@ -61,6 +61,8 @@ struct Control {
   // of the sibling M2L groups: per-octave counts and placement cursors
   int32_t task_oct[ORDER_OCT], task_cur[ORDER_OCT];
   int32_t group_oct[ORDER_OCT], group_cur[ORDER_OCT];
+  int32_t n_split;  // leaves whose near field is split over several tasks
+  int32_t pad1;
 };
 // Grow-only device buffer.
 struct DBuf {
@@ -112,6 +114,8 @@ struct fmm_plan_s {
   bool m2l_lists_ready = false;  // per-target M2L lists materialized (on request only)
   // near-field tasks (target leaf x bounded slice of its list)
   mbg::DBuf p2p_task, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
+  mbg::DBuf split_leaves;  // positions (in the leaf list) of the split leaves, any order
+  int64_t n_split = 0;
   // non-leaf nodes in id order; the parents of level l are parents[pbeg[l] .. pbeg[l+1])
   mbg::DBuf parents, m2l_order;
   int64_t n_parents = 0, n_union = 0;
@@ -341,7 +345,8 @@ size_t p2p_task_bytes();
 // transposed-tail M2L tasks (tr_cnt: the leaves' transposed M2L run lengths)
 hipError_t launch_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
                                    const int32_t* count, const int32_t* tr_cnt, int64_t* ntask,
-                                   int64_t* npart, int64_t* ntail, Control* ctrl, hipStream_t st);
+                                   int64_t* npart, int64_t* ntail, int32_t* split, Control* ctrl,
+                                   hipStream_t st);
 // the tasks in launch order (heavier octaves of work first; ctrl->task_oct
 // counted by launch_leaf_task_counts, task_cur zero at the start)
 hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t n_tasks,
@@ -352,7 +357,8 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                       const int32_t* begin, const int32_t* count, const int32_t* src,
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
-                      void* part, bool any_multi, hipEvent_t* ev, bool* ran, hipStream_t st);
+                      void* part, const int32_t* split, int64_t n_split, hipEvent_t* ev, bool* ran,
+                      hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 // ---- integer-lattice kick-drift-kick ----
@@ -385,8 +391,8 @@ hipError_t launch_p2p_vjp(int dtype, const void* tasks, int64_t n_tasks, const i
                           int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                           const int32_t* begin, const int32_t* count, const int32_t* src,
                           const void* recs, const void* far, const int32_t* perm, void* mbar,
-                          void* xbar, void* part, bool any_multi, hipEvent_t* ev, bool* ran,
-                          hipStream_t st);
+                          void* xbar, void* part, const int32_t* split, int64_t n_split,
+                          hipEvent_t* ev, bool* ran, hipStream_t st);
 // expansions in the plan's dtype/convention -> fp64 raw moments / derivatives
 // traceless source records for the M2L: folded moments + centre, per node
 hipError_t launch_m2l_records(int dtype, int order, int64_t n_nodes, const double* centre,

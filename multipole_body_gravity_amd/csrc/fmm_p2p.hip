@@ -46,7 +46,7 @@ __device__ __forceinline__ float p2p_rsqrt(float x) { return __builtin_amdgcn_rs
 // ---- task construction (build time) ----
 __global__ void k_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
                                    const int32_t* count, const int32_t* tr_cnt, int64_t* ntask,
-                                   int64_t* npart, int64_t* ntail, Control* ctrl) {
+                                   int64_t* npart, int64_t* ntail, int32_t* split, Control* ctrl) {
   bookkeeping_priority();
   __shared__ int oct[ORDER_OCT];
   for (int b = threadIdx.x; b < ORDER_OCT; b += blockDim.x) oct[b] = 0;
@@ -59,6 +59,7 @@ __global__ void k_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, cons
     ntask[li] = nt;
     npart[li] = nt > 1 ? nt * (int64_t)count[a] : 0;
     ntail[li] = ((int64_t)tr_cnt[a] + TAIL_E - 1) / TAIL_E;
+    if (nt > 1) split[atomicAdd(&ctrl->n_split, 1)] = (int32_t)li;  // for the combine
     // launch-order octaves of the leaf's tasks: nt - 1 full ones and the last
     const uint64_t c = (uint64_t)count[a];
     if (nt > 1) atomicAdd(&oct[work_octave(c * TASK_E)], (int)(nt - 1));
@@ -401,13 +402,14 @@ constexpr int CB_THREADS = 256;
 
 template <typename T>
 __global__ void __launch_bounds__(CB_THREADS)
-    k_p2p_combine(const int32_t* leaves, int64_t n_leaves, const int64_t* task_off,
+    k_p2p_combine(const int32_t* leaves, const int32_t* split, int64_t n_split,
+                  const int64_t* task_off,
                   const int64_t* part_off, const int32_t* begin, const int32_t* count,
                   const T* part, const P4<T>* far, const int32_t* perm, T* phi, T* acc) {
   __shared__ T red[4][CB_THREADS];
-  for (int64_t li = blockIdx.x; li < n_leaves; li += gridDim.x) {
+  for (int64_t j = blockIdx.x; j < n_split; j += gridDim.x) {  // the split leaves only
+    const int64_t li = split[j];
     const int64_t nt = task_off[li + 1] - task_off[li];
-    if (nt <= 1) continue;
     const int32_t a = leaves[li];
     const int32_t tn = count[a], tb = begin[a];
     for (int32_t t0 = 0; t0 < tn; t0 += CB_THREADS) {
@@ -454,10 +456,11 @@ size_t p2p_task_bytes() { return sizeof(P2PTask); }
 
 hipError_t launch_leaf_task_counts(const int32_t* leaves, int64_t n_leaves, const int64_t* off,
                                    const int32_t* count, const int32_t* tr_cnt, int64_t* ntask,
-                                   int64_t* npart, int64_t* ntail, Control* ctrl, hipStream_t st) {
+                                   int64_t* npart, int64_t* ntail, int32_t* split, Control* ctrl,
+                                   hipStream_t st) {
   if (n_leaves == 0) return hipSuccess;
   k_leaf_task_counts<<<(unsigned)((n_leaves + 255) / 256), 256, 0, st>>>(
-      leaves, n_leaves, off, count, tr_cnt, ntask, npart, ntail, ctrl);
+      leaves, n_leaves, off, count, tr_cnt, ntask, npart, ntail, split, ctrl);
   return hipGetLastError();
 }
 
@@ -476,12 +479,13 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                       const int32_t* begin, const int32_t* count, const int32_t* src,
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
-                      void* part, bool any_multi, hipEvent_t* ev, bool* ran, hipStream_t st) {
+                      void* part, const int32_t* split, int64_t n_split, hipEvent_t* ev, bool* ran,
+                      hipStream_t st) {
   // ev (optional): begin/end of the pair kernel, then of the combine
   if (n_tasks == 0) return hipSuccess;
   int64_t blocks = (n_tasks + P2P_WAVES - 1) / P2P_WAVES;
   if (blocks > 65535) blocks = 65535;
-  int64_t cblocks = n_leaves < 65535 ? n_leaves : 65535;
+  const int64_t cblocks = n_split < 65535 ? n_split : 65535;
   if (ev) (void)hipEventRecord(ev[0], st);
   if (dtype == FMM_F64)
     k_p2p<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
@@ -495,15 +499,15 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
     (void)hipEventRecord(ev[1], st);
     ran[0] = true;
   }
-  if (any_multi) {
+  if (n_split > 0) {
     if (ev) (void)hipEventRecord(ev[2], st);
     if (dtype == FMM_F64)
       k_p2p_combine<double><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
-          leaves, n_leaves, task_off, part_off, begin, count, (const double*)part,
+          leaves, split, n_split, task_off, part_off, begin, count, (const double*)part,
           (const P4<double>*)far, perm, (double*)phi, (double*)acc);
     else
       k_p2p_combine<float><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
-          leaves, n_leaves, task_off, part_off, begin, count, (const float*)part,
+          leaves, split, n_split, task_off, part_off, begin, count, (const float*)part,
           (const P4<float>*)far, perm, (float*)phi, (float*)acc);
     if (ev) {
       (void)hipEventRecord(ev[3], st);
@@ -517,13 +521,13 @@ hipError_t launch_p2p_vjp(int dtype, const void* tasks, int64_t n_tasks, const i
                           int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
                           const int32_t* begin, const int32_t* count, const int32_t* src,
                           const void* recs, const void* far, const int32_t* perm, void* mbar,
-                          void* xbar, void* part, bool any_multi, hipEvent_t* ev, bool* ran,
-                          hipStream_t st) {
+                          void* xbar, void* part, const int32_t* split, int64_t n_split,
+                          hipEvent_t* ev, bool* ran, hipStream_t st) {
   // ev (optional): begin/end of the pair kernel
   if (n_tasks == 0) return hipSuccess;
   int64_t blocks = (n_tasks + P2P_WAVES - 1) / P2P_WAVES;
   if (blocks > 65535) blocks = 65535;
-  int64_t cblocks = n_leaves < 65535 ? n_leaves : 65535;
+  const int64_t cblocks = n_split < 65535 ? n_split : 65535;
   if (ev) (void)hipEventRecord(ev[0], st);
   if (dtype == FMM_F64)
     k_p2p_vjp<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
@@ -537,15 +541,15 @@ hipError_t launch_p2p_vjp(int dtype, const void* tasks, int64_t n_tasks, const i
     (void)hipEventRecord(ev[1], st);
     ran[0] = true;
   }
-  if (any_multi) {
+  if (n_split > 0) {
     // the split leaves' partials: the same ordered combine as the forward
     if (dtype == FMM_F64)
       k_p2p_combine<double><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
-          leaves, n_leaves, task_off, part_off, begin, count, (const double*)part,
+          leaves, split, n_split, task_off, part_off, begin, count, (const double*)part,
           (const P4<double>*)far, perm, (double*)mbar, (double*)xbar);
     else
       k_p2p_combine<float><<<(unsigned)cblocks, CB_THREADS, 0, st>>>(
-          leaves, n_leaves, task_off, part_off, begin, count, (const float*)part,
+          leaves, split, n_split, task_off, part_off, begin, count, (const float*)part,
           (const P4<float>*)far, perm, (float*)mbar, (float*)xbar);
   }
   return hipGetLastError();
