@@ -49,6 +49,10 @@ extern "C" {
 #endif
 
 #define FMM_MAX_ORDER 8
+/* Largest octree a build accepts: node ids are 32-bit.  (Clustered inputs with
+ * a small leaf size can need more cells than particles, so N < 2^31 alone does
+ * not bound it.) */
+#define FMM_MAX_NODES 2147483647LL
 
 typedef struct fmm_plan_s* fmm_plan_t; /* opaque, owned by the library */
 
@@ -123,7 +127,12 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
  * starts after the tree and overlaps the walk; the next fmm_eval or fmm_build
  * on any stream waits for it.  Synchronizes `stream` three times (tree size,
  * list sizes twice).  Returns FMM_ERR_NONFINITE (and leaves the plan un-built)
- * if any input is NaN/Inf. */
+ * if any input is NaN/Inf, FMM_ERR_OOM if the octree of these positions would
+ * need more than FMM_MAX_NODES cells.
+ *
+ * Builds, evals and VJPs of one plan run in the order they are called, on
+ * whatever streams: a call on a stream other than the previous call's waits
+ * (on the device) for the end of that call before its first launch. */
 int fmm_build(fmm_plan_t plan, const void* pos, const void* mass, void* stream);
 
 /* Evaluate potential and acceleration of every particle: the M2L of the
@@ -148,9 +157,8 @@ int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
  * forward evaluation to keep the accuracy of that evaluation.  All arrays are
  * device arrays in the plan's dtype, in the caller's order.  Requires a built
  * plan (FMM_ERR_STATE otherwise); runs the forward's leaf locals itself if no
- * fmm_eval followed the build.  Asynchronous on `stream`; repeatable; must not
- * overlap an fmm_eval of the same plan on another stream (they share the
- * split-task partial buffers).  Its own workspace (sensitivity records and
+ * fmm_eval followed the build.  Asynchronous on `stream`; repeatable; ordered
+ * after the plan's previous call like fmm_build.  Its own workspace (sensitivity records and
  * expansions, about 2 N + 3 n_nodes K values of the dtype) is allocated by the
  * first call after a build that needs more, grow-only like the plan's. */
 int fmm_vjp(fmm_plan_t plan, const void* phi_bar, const void* acc_bar, void* pos_bar,
@@ -180,6 +188,14 @@ int fmm_destroy(fmm_plan_t plan);
 
 /* Static string for a status code. */
 const char* fmm_strerror(int code);
+
+/* Bits with which the walk packs a node id into its transposed
+ * (kind, target, source) keys, for a tree of n_nodes cells: the smallest
+ * b >= 1 with 2^b > n_nodes.  A key takes 2 b + 1 bits, at most 63 for
+ * n_nodes <= FMM_MAX_NODES.
+ * FMM_ERR_ARG for a null pointer or n_nodes outside [1, FMM_MAX_NODES].
+ * Host only; touches no device. */
+int fmm_node_id_bits(int64_t n_nodes, int* bits);
 
 /* Turn HIP-event timing of the stages and of the main kernels on (1) or off
  * (0).  Events are recorded between launches on the stream that runs them

@@ -122,6 +122,21 @@ void collect_pending(fmm_plan_t p) {
   }
 }
 
+// Calls on one plan run in the order they are issued: a build, eval or VJP
+// on a stream other than the previous call's first waits for the end of that
+// call (they rewrite or read the same workspace: sorted particles, lists,
+// task tables, partial sums), and records its own end for the next one.
+int order_after_previous(fmm_plan_t p, hipStream_t st) {
+  if (p->done_issued && st != p->last_stream) TRY_HIP(hipStreamWaitEvent(st, p->ev_done, 0));
+  return FMM_OK;
+}
+int mark_done(fmm_plan_t p, hipStream_t st) {
+  TRY_HIP(hipEventRecord(p->ev_done, st));
+  p->last_stream = st;
+  p->done_issued = true;
+  return FMM_OK;
+}
+
 int sync_ctrl(fmm_plan_t p, hipStream_t st) {
   TRY_HIP(hipMemcpyAsync(p->ctrl_host, p->ctrl.p, sizeof(Control), hipMemcpyDeviceToHost, st));
   TRY_HIP(hipStreamSynchronize(st));
@@ -130,7 +145,7 @@ int sync_ctrl(fmm_plan_t p, hipStream_t st) {
 
 
 // ---------------- walk ----------------
-int bits_for(int64_t v) {  // bits to hold 0..v
+int bits_for(int64_t v) {  // bits to hold 0..v (v < 2^62)
   int b = 1;
   while (b < 62 && ((int64_t)1 << b) <= v) b++;
   return b;
@@ -548,7 +563,8 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
       hipEventCreateWithFlags(&p->ev_tree, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_order, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_up, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&p->ev_rec, hipEventDisableTiming) != hipSuccess)
+      hipEventCreateWithFlags(&p->ev_rec, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_done, hipEventDisableTiming) != hipSuccess)
     return fail(FMM_ERR_HIP);
   *out = p;
   return FMM_OK;
@@ -591,8 +607,15 @@ int fmm_destroy(fmm_plan_t p) {
   if (p->ev_order) (void)hipEventDestroy(p->ev_order);
   if (p->ev_up) (void)hipEventDestroy(p->ev_up);
   if (p->ev_rec) (void)hipEventDestroy(p->ev_rec);
+  if (p->ev_done) (void)hipEventDestroy(p->ev_done);
   if (p->up_stream) (void)hipStreamDestroy(p->up_stream);
   delete p;
+  return FMM_OK;
+}
+
+int fmm_node_id_bits(int64_t n_nodes, int* bits) {
+  if (!bits || n_nodes < 1 || n_nodes > FMM_MAX_NODES) return FMM_ERR_ARG;
+  *bits = bits_for(n_nodes);
   return FMM_OK;
 }
 
@@ -610,11 +633,52 @@ int fmm_set_timing(fmm_plan_t p, int enable) {
   return FMM_OK;
 }
 
+namespace {
+int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st);
+int eval_impl(fmm_plan_t p, void* phi, void* acc, hipStream_t st);
+int vjp_impl(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_bar,
+             void* mass_bar, hipStream_t st);
+}  // namespace
+
 int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   if (!p || !pos || !mass) return FMM_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
   TRY_HIP(hipSetDevice(p->device));
   p->built = false;
+  TRY(order_after_previous(p, st));
+  const int rc = build_impl(p, pos, mass, st);
+  const int rd = mark_done(p, st);
+  return rc != FMM_OK ? rc : rd;
+}
+
+int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
+  if (!p || !phi || !acc) return FMM_ERR_ARG;
+  if (!p->built) return FMM_ERR_STATE;
+  hipStream_t st = (hipStream_t)stream;
+  TRY_HIP(hipSetDevice(p->device));
+  TRY(order_after_previous(p, st));
+  const int rc = eval_impl(p, phi, acc, st);
+  const int rd = mark_done(p, st);
+  return rc != FMM_OK ? rc : rd;
+}
+
+int fmm_vjp(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_bar,
+            void* mass_bar, void* stream) {
+  if (!p || !phi_bar || !acc_bar || !pos_bar || !mass_bar) return FMM_ERR_ARG;
+  if (!p->built) return FMM_ERR_STATE;
+  hipStream_t st = (hipStream_t)stream;
+  TRY_HIP(hipSetDevice(p->device));
+  TRY(order_after_previous(p, st));
+  const int rc = vjp_impl(p, phi_bar, acc_bar, pos_bar, mass_bar, st);
+  const int rd = mark_done(p, st);
+  return rc != FMM_OK ? rc : rd;
+}
+
+}  // extern "C"
+
+namespace {
+
+int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) {
   p->evaluated = false;
   const int64_t n = p->n;
   Control* ctrl = P<Control>(p->ctrl);
@@ -653,6 +717,9 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;
   const Control& c = *p->ctrl_host;
   const int64_t nn = c.level_off[MAX_LEVELS];
+  // node ids are 32-bit, and the walk packs (kind, target, source) node ids
+  // into 64-bit keys of 2 * fmm_node_id_bits(nn) + 1 bits
+  if (nn > FMM_MAX_NODES) return FMM_ERR_OOM;
   p->n_nodes = nn;
   p->depth = 0;
   p->n_leaves = 0;
@@ -712,11 +779,7 @@ int fmm_build(fmm_plan_t p, const void* pos, const void* mass, void* stream) {
   return FMM_OK;
 }
 
-int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
-  if (!p || !phi || !acc) return FMM_ERR_ARG;
-  if (!p->built) return FMM_ERR_STATE;
-  hipStream_t st = (hipStream_t)stream;
-  TRY_HIP(hipSetDevice(p->device));
+int eval_impl(fmm_plan_t p, void* phi, void* acc, hipStream_t st) {
   // source records and the own-entry locals come from the build's second
   // stream (leaf_locals waits for each); `local` is only read from here on
   TRY(leaf_locals(p, st));
@@ -744,12 +807,8 @@ int fmm_eval(fmm_plan_t p, void* phi, void* acc, void* stream) {
   return FMM_OK;
 }
 
-int fmm_vjp(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_bar,
-            void* mass_bar, void* stream) {
-  if (!p || !phi_bar || !acc_bar || !pos_bar || !mass_bar) return FMM_ERR_ARG;
-  if (!p->built) return FMM_ERR_STATE;
-  hipStream_t st = (hipStream_t)stream;
-  TRY_HIP(hipSetDevice(p->device));
+int vjp_impl(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_bar,
+             void* mass_bar, hipStream_t st) {
   const int dt = p->dtype, ord = p->order;
   const int64_t n = p->n, nn = p->n_nodes;
   const size_t w = wbytes(dt);
@@ -817,6 +876,10 @@ int fmm_vjp(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_ba
   return FMM_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 int fmm_lattice_steps(fmm_plan_t p, int64_t* q, int64_t* u, const void* mass, double dx,
                       double dv, double dt, int n_steps, int direction, void* stream) {
   if (!p || !q || !u || !mass || n_steps < 0 || (direction != 1 && direction != -1) ||
@@ -826,6 +889,7 @@ int fmm_lattice_steps(fmm_plan_t p, int64_t* q, int64_t* u, const void* mass, do
   if (n_steps == 0) return FMM_OK;
   hipStream_t st = (hipStream_t)stream;
   TRY_HIP(hipSetDevice(p->device));
+  TRY(order_after_previous(p, st));  // the lattice buffers feed the builds below
   const int dt_ = p->dtype;
   const int64_t n = p->n;
   const size_t w = wbytes(dt_);

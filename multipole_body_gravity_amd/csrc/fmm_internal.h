@@ -148,6 +148,13 @@ struct fmm_plan_s {
   hipEvent_t ev_tree = nullptr, ev_order = nullptr, ev_up = nullptr;
   hipEvent_t ev_rec = nullptr;  // the M2L source records are written (second stream)
   bool up_issued = false;
+  // Every build, eval and VJP records ev_done on its stream at its end, and
+  // the next call on another stream waits for it: calls on one plan run in the
+  // order they are issued, whatever streams they are given (they rewrite or
+  // read the same workspace).
+  hipEvent_t ev_done = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool done_issued = false;
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
   hipEvent_t kev[2 * FMM_N_KERNELS] = {};  // begin/end of single kernel launches
   bool kran[FMM_N_KERNELS] = {};          // the kernel ran in the last eval

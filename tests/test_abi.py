@@ -26,7 +26,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for want in ["fmm_plan", "fmm_build", "fmm_eval", "fmm_destroy", "fmm_strerror",
                  "fmm_set_timing", "fmm_stats", "fmm_copy_keys", "fmm_copy_tree",
-                 "fmm_copy_lists", "fmm_copy_expansions", "fmm_direct", "fmm_vjp", "fmm_lattice_steps"]:
+                 "fmm_copy_lists", "fmm_copy_expansions", "fmm_direct", "fmm_vjp", "fmm_lattice_steps",
+                 "fmm_node_id_bits"]:
         assert want in names
 
 
@@ -70,3 +71,25 @@ def test_null_plan_calls(lib):
     assert lib.fmm_set_timing(None, 1) == -1
     assert lib.fmm_copy_keys(None, None, None) == -1
     assert lib.fmm_plan(None, 10, 4, 0.7, 32, 1) == -1
+
+
+def test_node_id_bits(lib):
+    """The walk packs (kind, target, source) node ids into 2 b + 1 bits, b the
+    bits that hold every id of the tree; the largest tree a build accepts
+    (FMM_MAX_NODES = 2^31 - 1 cells) still fits 64 bits, one more cell does
+    not, and is refused."""
+    lib.fmm_node_id_bits.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int)]
+    b = ctypes.c_int()
+    max_nodes = 2 ** 31 - 1
+    text = open(HEADER).read()
+    assert re.search(r"#define FMM_MAX_NODES 2147483647LL", text)
+    for nn, want in [(1, 1), (2, 2), (3, 2), (4, 3), (125390, 17), (2 ** 30, 31),
+                     (2 ** 31 - 1, 31)]:
+        assert lib.fmm_node_id_bits(nn, ctypes.byref(b)) == 0
+        assert b.value == want, (nn, b.value)
+        assert (1 << b.value) > nn >= (1 << (b.value - 1)) or nn == 1
+    assert lib.fmm_node_id_bits(max_nodes, ctypes.byref(b)) == 0
+    assert 2 * b.value + 1 <= 64
+    for bad in (0, -1, max_nodes + 1, 2 ** 40):
+        assert lib.fmm_node_id_bits(bad, ctypes.byref(b)) == -1
+    assert lib.fmm_node_id_bits(10, None) == -1
