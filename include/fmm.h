@@ -246,6 +246,20 @@ int fmm_copy_expansions(fmm_plan_t plan, double* mpole, double* local);
 int fmm_direct(const void* pos, const void* mass, int64_t n, const int64_t* targets,
                int64_t n_targets, int dtype, void* phi, void* acc, void* stream);
 
+/* fmm_direct for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and the same results bit for bit, with the workspace in a
+ * static device array of the library (8 MiB per device, held until the
+ * process ends) instead of a temporary allocation.  Calls no hipMalloc,
+ * hipFree or other allocating routine, and does not synchronize: the results
+ * are ready when `stream` passes the call.  Every call on one device shares
+ * that array: calls that overlap on one device (on different streams, or from
+ * different threads) race and give undefined results.  FMM_ERR_ARG as
+ * fmm_direct, and for n_targets > FMM_DIRECT_NOALLOC_MAX_TARGETS. */
+#define FMM_DIRECT_NOALLOC_MAX_TARGETS 4096
+int fmm_direct_noalloc(const void* pos, const void* mass, int64_t n, const int64_t* targets,
+                       int64_t n_targets, int dtype, void* phi, void* acc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

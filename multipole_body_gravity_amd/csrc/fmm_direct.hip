@@ -11,6 +11,8 @@
 // sums one slice of the sources, staged 256 at a time in LDS; the slices'
 // partial sums are added per target in slice order by a second kernel, so the
 // result has a fixed summation order.
+#include <mutex>
+
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -97,6 +99,52 @@ __global__ void k_direct_sum(const double* __restrict__ part, int64_t n_targets,
   acc[3 * t + 2] = (T)s[3];
 }
 
+// Workspace of the allocation-free variant: the slices' partial sums of up to
+// FMM_DIRECT_NOALLOC_MAX_TARGETS targets (8 MiB), one copy per device, held
+// until the process ends.  Host code never passes this name to a kernel: it
+// is a host-side stand-in, and the device address comes from
+// hipGetSymbolAddress (per device, on the first call there).
+static __device__ __align__(256) double scratch[(size_t)DT_SLICES * FMM_DIRECT_NOALLOC_MAX_TARGETS * 4];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+double* scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device (looked up once).
+hipError_t scratch_address(double** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = static_cast<double*>(ptr);
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Both kernels on `st` over the workspace `part`.
+hipError_t direct_launch(const void* pos, const void* mass, int64_t n, const int64_t* targets,
+                         int64_t n_targets, int dtype, void* phi, void* acc, double* part,
+                         hipStream_t st) {
+  const dim3 grid((unsigned)((n_targets + DT_THREADS - 1) / DT_THREADS), DT_SLICES);
+  const unsigned g2 = (unsigned)((n_targets + 255) / 256);
+  if (dtype == FMM_F64) {
+    k_direct_part<double><<<grid, DT_THREADS, 0, st>>>((const double*)pos, (const double*)mass, n,
+                                                       targets, n_targets, part);
+    k_direct_sum<double><<<g2, 256, 0, st>>>(part, n_targets, (double*)phi, (double*)acc);
+  } else {
+    k_direct_part<float><<<grid, DT_THREADS, 0, st>>>((const float*)pos, (const float*)mass, n,
+                                                      targets, n_targets, part);
+    k_direct_sum<float><<<g2, 256, 0, st>>>(part, n_targets, (float*)phi, (float*)acc);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace mbg
 
 using namespace mbg;
@@ -111,19 +159,24 @@ extern "C" int fmm_direct(const void* pos, const void* mass, int64_t n, const in
   double* part = nullptr;
   const size_t bytes = (size_t)DT_SLICES * (size_t)n_targets * 4 * sizeof(double);
   if (hipMalloc(&part, bytes) != hipSuccess) return FMM_ERR_OOM;
-  const dim3 grid((unsigned)((n_targets + DT_THREADS - 1) / DT_THREADS), DT_SLICES);
-  const unsigned g2 = (unsigned)((n_targets + 255) / 256);
-  if (dtype == FMM_F64) {
-    k_direct_part<double><<<grid, DT_THREADS, 0, st>>>((const double*)pos, (const double*)mass, n,
-                                                       targets, n_targets, part);
-    k_direct_sum<double><<<g2, 256, 0, st>>>(part, n_targets, (double*)phi, (double*)acc);
-  } else {
-    k_direct_part<float><<<grid, DT_THREADS, 0, st>>>((const float*)pos, (const float*)mass, n,
-                                                      targets, n_targets, part);
-    k_direct_sum<float><<<g2, 256, 0, st>>>(part, n_targets, (float*)phi, (float*)acc);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e = direct_launch(pos, mass, n, targets, n_targets, dtype, phi, acc, part, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   (void)hipFree(part);
+  return e == hipSuccess ? FMM_OK : FMM_ERR_HIP;
+}
+
+extern "C" int fmm_direct_noalloc(const void* pos, const void* mass, int64_t n,
+                                  const int64_t* targets, int64_t n_targets, int dtype, void* phi,
+                                  void* acc, void* stream) {
+  if (!pos || !mass || !targets || !phi || !acc || n < 1 || n_targets < 0 ||
+      n_targets > FMM_DIRECT_NOALLOC_MAX_TARGETS || (dtype != FMM_F32 && dtype != FMM_F64))
+    return FMM_ERR_ARG;
+  if (n_targets == 0) return FMM_OK;
+  double* part = nullptr;
+  // every slot of the workspace that the sums read is written first by the
+  // partial kernel of the same call: nothing needs clearing
+  if (scratch_address(&part) != hipSuccess) return FMM_ERR_HIP;
+  const hipError_t e = direct_launch(pos, mass, n, targets, n_targets, dtype, phi, acc, part,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? FMM_OK : FMM_ERR_HIP;
 }

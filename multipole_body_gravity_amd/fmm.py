@@ -68,6 +68,7 @@ def load_library():
     lib.fmm_copy_lists.argtypes = [P] * 5
     lib.fmm_copy_expansions.argtypes = [P, P, P]
     lib.fmm_direct.argtypes = [P, P, i64, P, i64, i32, P, P, P]
+    lib.fmm_direct_noalloc.argtypes = [P, P, i64, P, i64, i32, P, P, P]
     _lib = lib
     return lib
 
@@ -243,26 +244,47 @@ class Plan:
             pass
 
 
+def _direct_call(name, pos, mass, targets, phi, acc, stream):
+    if pos.dim() != 2 or pos.shape[1] != 3 or mass.shape != (pos.shape[0],):
+        raise FmmError(-1, f"{name}: pos must be [N,3] and mass [N]")
+    if pos.dtype not in (torch.float32, torch.float64) or mass.dtype != pos.dtype:
+        raise FmmError(-1, f"{name}: pos and mass of one float dtype")
+    if targets.dtype != torch.int64 or not (pos.is_cuda and mass.is_cuda and targets.is_cuda):
+        raise FmmError(-1, f"{name}: device tensors, int64 targets")
+    pos, mass, targets = pos.contiguous(), mass.contiguous(), targets.contiguous()
+    nt = targets.shape[0]
+    if phi is None:
+        phi = torch.empty(nt, dtype=pos.dtype, device=pos.device)
+    if acc is None:
+        acc = torch.empty(nt, 3, dtype=pos.dtype, device=pos.device)
+    if phi.shape != (nt,) or acc.shape != (nt, 3) or phi.dtype != pos.dtype \
+            or acc.dtype != pos.dtype or not phi.is_contiguous() or not acc.is_contiguous():
+        raise FmmError(-1, f"{name}: phi [T] and acc [T,3] contiguous, the inputs' dtype")
+    lib = load_library()
+    with torch.cuda.device(pos.device):
+        rc = getattr(lib, name)(ctypes.c_void_p(pos.data_ptr()), ctypes.c_void_p(mass.data_ptr()),
+                                pos.shape[0], ctypes.c_void_p(targets.data_ptr()), nt,
+                                FMM_F64 if pos.dtype == torch.float64 else FMM_F32,
+                                ctypes.c_void_p(phi.data_ptr()), ctypes.c_void_p(acc.data_ptr()),
+                                _stream_handle(stream))
+    if rc:
+        raise FmmError(rc, name)
+    return phi, acc
+
+
 def direct(pos: torch.Tensor, mass: torch.Tensor, targets: torch.Tensor, stream=None):
     """Direct-sum potential and acceleration of particles `targets` (int64 device
     tensor of indices) from all particles (fp64 sums; fmm_direct)."""
-    if pos.dim() != 2 or pos.shape[1] != 3 or mass.shape != (pos.shape[0],):
-        raise FmmError(-1, "fmm_direct: pos must be [N,3] and mass [N]")
-    if pos.dtype not in (torch.float32, torch.float64) or mass.dtype != pos.dtype:
-        raise FmmError(-1, "fmm_direct: pos and mass of one float dtype")
-    if targets.dtype != torch.int64 or not (pos.is_cuda and mass.is_cuda and targets.is_cuda):
-        raise FmmError(-1, "fmm_direct: device tensors, int64 targets")
-    pos, mass, targets = pos.contiguous(), mass.contiguous(), targets.contiguous()
-    nt = targets.shape[0]
-    phi = torch.empty(nt, dtype=pos.dtype, device=pos.device)
-    acc = torch.empty(nt, 3, dtype=pos.dtype, device=pos.device)
-    lib = load_library()
-    with torch.cuda.device(pos.device):
-        rc = lib.fmm_direct(ctypes.c_void_p(pos.data_ptr()), ctypes.c_void_p(mass.data_ptr()),
-                            pos.shape[0], ctypes.c_void_p(targets.data_ptr()), nt,
-                            FMM_F64 if pos.dtype == torch.float64 else FMM_F32,
-                            ctypes.c_void_p(phi.data_ptr()), ctypes.c_void_p(acc.data_ptr()),
-                            _stream_handle(stream))
-    if rc:
-        raise FmmError(rc, "fmm_direct")
-    return phi, acc
+    return _direct_call("fmm_direct", pos, mass, targets, None, None, stream)
+
+
+DIRECT_NOALLOC_MAX_TARGETS = 4096
+
+
+def direct_noalloc(pos: torch.Tensor, mass: torch.Tensor, targets: torch.Tensor,
+                   phi: torch.Tensor | None = None, acc: torch.Tensor | None = None, stream=None):
+    """fmm_direct_noalloc: the same sums with the library's static workspace (at
+    most DIRECT_NOALLOC_MAX_TARGETS targets; asynchronous on the stream).  Pass
+    phi [T] and acc [T,3] to keep the call free of any allocation."""
+    return _direct_call("fmm_direct_noalloc", pos, mass, targets, phi, acc, stream)
+

@@ -27,7 +27,7 @@ def test_header_declares_entry_points():
     for want in ["fmm_plan", "fmm_build", "fmm_eval", "fmm_destroy", "fmm_strerror",
                  "fmm_set_timing", "fmm_stats", "fmm_copy_keys", "fmm_copy_tree",
                  "fmm_copy_lists", "fmm_copy_expansions", "fmm_direct", "fmm_vjp", "fmm_lattice_steps",
-                 "fmm_node_id_bits"]:
+                 "fmm_node_id_bits", "fmm_direct_noalloc"]:
         assert want in names
 
 
@@ -68,6 +68,12 @@ def test_null_plan_calls(lib):
     assert lib.fmm_direct(P(1), P(1), 10, P(1), -1, 1, P(1), P(1), None) == -1
     assert lib.fmm_direct(P(1), P(1), 10, P(1), 1, 7, P(1), P(1), None) == -1
     assert lib.fmm_direct(P(1), P(1), 10, P(1), 0, 1, P(1), P(1), None) == 0
+    # the allocation-free variant: the same checks, and at most 4096 targets
+    assert lib.fmm_direct_noalloc(None, P(1), 10, P(1), 1, 1, P(1), P(1), None) == -1
+    assert lib.fmm_direct_noalloc(P(1), P(1), 0, P(1), 1, 1, P(1), P(1), None) == -1
+    assert lib.fmm_direct_noalloc(P(1), P(1), 10, P(1), 4097, 1, P(1), P(1), None) == -1
+    assert lib.fmm_direct_noalloc(P(1), P(1), 10, P(1), 1, 7, P(1), P(1), None) == -1
+    assert lib.fmm_direct_noalloc(P(1), P(1), 10, P(1), 0, 1, P(1), P(1), None) == 0
     assert lib.fmm_set_timing(None, 1) == -1
     assert lib.fmm_copy_keys(None, None, None) == -1
     assert lib.fmm_plan(None, 10, 4, 0.7, 32, 1) == -1
