@@ -541,6 +541,7 @@ struct oracle_result {
   int64_t n_m2l, n_p2p;
   int64_t *m2l_off, *p2p_off;
   int32_t *m2l_src, *p2p_src;
+  uint64_t *dcnt[2], *dhash[2]; /* digest mode: per-target list digests */
   double *M, *L;
   double *phi, *acc; /* caller's order */
   double times[8];
@@ -565,6 +566,10 @@ void oracle_free(oracle_result* r) {
   free(r->p2p_off);
   free(r->m2l_src);
   free(r->p2p_src);
+  for (int k = 0; k < 2; k++) {
+    free(r->dcnt[k]);
+    free(r->dhash[k]);
+  }
   free(r->M);
   free(r->L);
   free(r->phi);
@@ -715,7 +720,41 @@ typedef struct {
   double t2;
   pairvec m2l, p2p;
   int err;
+  /* digest mode: entries are counted and hashed per target (below) instead of
+   * stored; pairs that reach level split_at are set aside in `tasks` and
+   * walked afterwards, in parallel (every pair is walked exactly once either
+   * way, so the entries emitted are the same) */
+  int digest;
+  uint64_t *dcnt[2], *dhash[2]; /* [0] M2L, [1] P2P; per target node */
+  pairvec* tasks;
+  int split_at;
 } walkctx;
+
+/* Digest of a list: its entry count and the sum (mod 2^64) of h(s) over its
+ * sources s, which does not depend on their order.  h(s) is the (s+1)-th
+ * output of SplitMix64 (S. Vigna) seeded with 0: state (s+1) * 0x9e3779b97f4a7c15,
+ * then the generator's finalizer. */
+static uint64_t digest_h(int32_t s) {
+  uint64_t z = ((uint64_t)(uint32_t)s + 1u) * 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+/* kind 0: M2L(A <- B); kind 1: P2P(A <- B) */
+static void emit(walkctx* w, int kind, int32_t A, int32_t B) {
+  if (w->digest) {
+    const uint64_t h = digest_h(B);
+    uint64_t* c = w->dcnt[kind] + A;
+    uint64_t* d = w->dhash[kind] + A;
+#pragma omp atomic
+    *c += 1u;
+#pragma omp atomic
+    *d += h;
+    return;
+  }
+  if (pv_push(kind == 0 ? &w->m2l : &w->p2p, A, B)) w->err = 1;
+}
 
 static void cell_coords(const oracle_result* r, int32_t i, int64_t* q) {
   int lev = r->level[i];
@@ -754,9 +793,13 @@ static void walk(walkctx* w, int32_t A, int32_t B) {
   const oracle_result* r = w->r;
   if (w->err) return;
   if (r->mark && !r->mark[A]) return; /* sampled mode: no requested target below A */
+  if (w->tasks && (r->level[A] >= w->split_at || r->level[B] >= w->split_at)) {
+    if (pv_push(w->tasks, A, B)) w->err = 1; /* walked later, in parallel */
+    return;
+  }
   if (A == B) {
     if (is_leaf(r, A)) {
-      if (pv_push(&w->p2p, A, A)) w->err = 1;
+      emit(w, 1, A, A);
     } else {
       for (int i = 0; i < r->n_child[A]; i++)
         for (int j = 0; j < r->n_child[A]; j++)
@@ -765,7 +808,7 @@ static void walk(walkctx* w, int32_t A, int32_t B) {
     return;
   }
   if (accept(w, A, B)) {
-    if (pv_push(&w->m2l, A, B)) w->err = 1;
+    emit(w, 0, A, B);
     return;
   }
   int canA = !is_leaf(r, A), canB = !is_leaf(r, B);
@@ -785,8 +828,30 @@ static void walk(walkctx* w, int32_t A, int32_t B) {
   } else if (canB) {
     for (int j = 0; j < r->n_child[B]; j++) walk(w, A, r->first_child[B] + j);
   } else {
-    if (pv_push(&w->p2p, A, B)) w->err = 1;
+    emit(w, 1, A, B);
   }
+}
+
+/* Digest mode: the walk from (root, root) down to the pairs that reach level
+ * split_at, then those pairs' walks in parallel. */
+static int walk_digests(walkctx* w) {
+  pairvec tasks;
+  memset(&tasks, 0, sizeof(tasks));
+  w->tasks = &tasks;
+  w->split_at = 4;
+  walk(w, 0, 0);
+  w->tasks = NULL;
+  int err = w->err;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : err)
+  for (int64_t k = 0; k < tasks.n; k++) {
+    walkctx lw = *w;
+    lw.err = 0;
+    walk(&lw, tasks.t[k], tasks.s[k]);
+    err |= lw.err;
+  }
+  free(tasks.t);
+  free(tasks.s);
+  return err;
 }
 
 static int cmp_i32(const void* a, const void* b) {
@@ -924,6 +989,31 @@ int oracle_fmm(int64_t n, const double* pos, const double* mass, int order, doub
   memset(&w, 0, sizeof(w));
   w.r = r;
   w.t2 = theta * theta; /* fl(theta^2), one rounding (R11) */
+  if (stage_mask & 2) { /* digest mode: no lists, no numeric passes */
+    w.digest = 1;
+    for (int k = 0; k < 2; k++) {
+      r->dcnt[k] = (uint64_t*)calloc((size_t)r->n_nodes, sizeof(uint64_t));
+      r->dhash[k] = (uint64_t*)calloc((size_t)r->n_nodes, sizeof(uint64_t));
+      if (!r->dcnt[k] || !r->dhash[k]) {
+        oracle_free(r);
+        return ORACLE_ERR_OOM;
+      }
+      w.dcnt[k] = r->dcnt[k];
+      w.dhash[k] = r->dhash[k];
+    }
+    if (walk_digests(&w)) {
+      oracle_free(r);
+      return ORACLE_ERR_OOM;
+    }
+    r->n_m2l = r->n_p2p = 0;
+    for (int64_t i = 0; i < r->n_nodes; i++) {
+      r->n_m2l += (int64_t)r->dcnt[0][i];
+      r->n_p2p += (int64_t)r->dcnt[1][i];
+    }
+    r->times[2] = wall() - t0;
+    *out = r;
+    return ORACLE_OK;
+  }
   walk(&w, 0, 0);
   if (w.err) {
     free(w.m2l.t);
@@ -1367,11 +1457,35 @@ void oracle_copy_tree(const oracle_result* r, uint8_t* level, uint64_t* prefix, 
 void oracle_copy_lists(const oracle_result* r, int64_t* m2l_off, int32_t* m2l_src,
                        int64_t* p2p_off, int32_t* p2p_src) {
   size_t m = (size_t)r->n_nodes + 1;
+  if (!r->m2l_off) return; /* digest mode: no lists */
   if (m2l_off) memcpy(m2l_off, r->m2l_off, 8 * m);
   if (m2l_src) memcpy(m2l_src, r->m2l_src, 4 * (size_t)r->n_m2l);
   if (p2p_off) memcpy(p2p_off, r->p2p_off, 8 * m);
   if (p2p_src) memcpy(p2p_src, r->p2p_src, 4 * (size_t)r->n_p2p);
 }
+int oracle_copy_digests(const oracle_result* r, uint64_t* m2l_cnt, uint64_t* m2l_hash,
+                        uint64_t* p2p_cnt, uint64_t* p2p_hash) {
+  uint64_t* cnt[2] = {m2l_cnt, p2p_cnt};
+  uint64_t* hash[2] = {m2l_hash, p2p_hash};
+  for (int k = 0; k < 2; k++) {
+    if (r->dcnt[k]) { /* digest mode */
+      memcpy(cnt[k], r->dcnt[k], sizeof(uint64_t) * (size_t)r->n_nodes);
+      memcpy(hash[k], r->dhash[k], sizeof(uint64_t) * (size_t)r->n_nodes);
+      continue;
+    }
+    const int64_t* off = k == 0 ? r->m2l_off : r->p2p_off;
+    const int32_t* src = k == 0 ? r->m2l_src : r->p2p_src;
+    if (!off) return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < r->n_nodes; i++) {
+      uint64_t h = 0;
+      for (int64_t e = off[i]; e < off[i + 1]; e++) h += digest_h(src[e]);
+      cnt[k][i] = (uint64_t)(off[i + 1] - off[i]);
+      hash[k][i] = h;
+    }
+  }
+  return ORACLE_OK;
+}
+
 void oracle_copy_mark(const oracle_result* r, uint8_t* mark) {
   if (r->mark)
     memcpy(mark, r->mark, (size_t)r->n_nodes);

@@ -54,7 +54,10 @@ int oracle_direct(int64_t n, const double* pos, const double* mass,
  * all multipoles are complete, the interaction lists are exact for the marked
  * targets and empty for the others, and phi/acc are valid for every particle
  * of a marked leaf (NaN elsewhere).  stage_mask bit 0 = run the numeric
- * passes (clear it to stop after the walk). */
+ * passes (clear it to stop after the walk).  stage_mask bit 1 = digest mode:
+ * the walk stores no lists but a digest of every target's two lists (see
+ * oracle_copy_digests), walking the pairs below level 4 in parallel; no
+ * numeric pass runs.  It serves sizes whose lists would not fit host memory. */
 int oracle_fmm(int64_t n, const double* pos, const double* mass, int order,
                double theta, int leaf_size, int64_t n_sample,
                const int64_t* sample, int stage_mask, oracle_result** out);
@@ -73,6 +76,12 @@ void oracle_copy_tree(const oracle_result* r, uint8_t* level, uint64_t* prefix,
 void oracle_copy_lists(const oracle_result* r, int64_t* m2l_off, int32_t* m2l_src,
                        int64_t* p2p_off, int32_t* p2p_src);
 void oracle_copy_mark(const oracle_result* r, uint8_t* node_mark);
+/* Per target node [n_nodes]: the number of entries of its M2L and P2P lists
+ * and the order-independent hash sum_s h(s) mod 2^64 of their sources, h(s) =
+ * the (s+1)-th output of SplitMix64 seeded with 0.  From the walk in digest
+ * mode, else from the stored lists. */
+int oracle_copy_digests(const oracle_result* r, uint64_t* m2l_cnt, uint64_t* m2l_hash,
+                        uint64_t* p2p_cnt, uint64_t* p2p_hash);
 /* node_count x K arrays in the layout above; NULL skips one */
 void oracle_copy_expansions(const oracle_result* r, double* mpole, double* local);
 /* results in the caller's particle order */

@@ -62,6 +62,7 @@ def _load():
     lib.oracle_copy_tree.restype = None
     lib.oracle_copy_lists.argtypes = [P] * 5
     lib.oracle_copy_lists.restype = None
+    lib.oracle_copy_digests.argtypes = [P] * 5
     lib.oracle_copy_expansions.argtypes = [P, P, P]
     lib.oracle_copy_expansions.restype = None
     lib.oracle_copy_result.argtypes = [P, P, P]
@@ -160,20 +161,34 @@ class OracleResult:
     local: np.ndarray | None = None
     phi: np.ndarray | None = None
     acc: np.ndarray | None = None
+    # per target node: entry counts and order-independent source hashes of the
+    # M2L and P2P lists (oracle_copy_digests)
+    digests: dict | None = None
+    n_m2l: int = 0
+    n_p2p: int = 0
 
 
 def fmm(pos, mass, order=4, theta=0.7, leaf_size=32, sample=None, numeric=True,
-        expansions=False) -> OracleResult:
-    """Run the oracle FMM.  `sample` (particle indices) restricts the targets."""
+        expansions=False, digests=None) -> OracleResult:
+    """Run the oracle FMM.  `sample` (particle indices) restricts the targets.
+
+    digests: None, "lists" (also form every target's list digests from the
+    stored lists) or "walk" (digest mode: the walk stores no lists, only the
+    digests; no numeric passes, empty list arrays)."""
     lib = _load()
     pos = _f64(pos, (-1, 3))
     mass = _f64(mass)
     n = pos.shape[0]
     smp = np.zeros(0, dtype=np.int64) if sample is None else np.ascontiguousarray(sample, dtype=np.int64)
+    if digests not in (None, "lists", "walk"):
+        raise ValueError(digests)
+    walk_digests = digests == "walk"
+    if walk_digests:
+        numeric = False
     h = ctypes.c_void_p()
     rc = lib.oracle_fmm(n, _p(pos), _p(mass), int(order), float(theta), int(leaf_size),
                         smp.shape[0], _p(smp) if smp.shape[0] else None,
-                        1 if numeric else 0, ctypes.byref(h))
+                        (1 if numeric else 0) | (2 if walk_digests else 0), ctypes.byref(h))
     if rc:
         raise OracleError(rc)
     try:
@@ -197,16 +212,29 @@ def fmm(pos, mass, order=4, theta=0.7, leaf_size=32, sample=None, numeric=True,
                              _p(first_child), _p(n_child))
         mark = np.zeros(nn, dtype=np.uint8)
         lib.oracle_copy_mark(h, _p(mark))
-        m2l_off = np.zeros(nn + 1, dtype=np.int64)
-        p2p_off = np.zeros(nn + 1, dtype=np.int64)
-        m2l_src = np.zeros(max(nm2l, 1), dtype=np.int32)
-        p2p_src = np.zeros(max(np2p, 1), dtype=np.int32)
-        lib.oracle_copy_lists(h, _p(m2l_off), _p(m2l_src), _p(p2p_off), _p(p2p_src))
+        if walk_digests:
+            m2l_off = p2p_off = np.zeros(0, dtype=np.int64)
+            m2l_src = p2p_src = np.zeros(0, dtype=np.int32)
+        else:
+            m2l_off = np.zeros(nn + 1, dtype=np.int64)
+            p2p_off = np.zeros(nn + 1, dtype=np.int64)
+            m2l_src = np.zeros(max(nm2l, 1), dtype=np.int32)
+            p2p_src = np.zeros(max(np2p, 1), dtype=np.int32)
+            lib.oracle_copy_lists(h, _p(m2l_off), _p(m2l_src), _p(p2p_off), _p(p2p_src))
         times = np.zeros(8)
         lib.oracle_times(h, _p(times))
         res = OracleResult(n, order, K, lo, float(side[0]), keys, perm, level, prefix, begin,
                            count, parent, first_child, n_child, mark.astype(bool), m2l_off,
-                           m2l_src[:nm2l], p2p_off, p2p_src[:np2p], depth, nl, times)
+                           m2l_src[:nm2l], p2p_off, p2p_src[:np2p], depth, nl, times,
+                           n_m2l=nm2l, n_p2p=np2p)
+        if digests is not None:
+            d = {k: np.zeros(nn, dtype=np.uint64)
+                 for k in ("m2l_cnt", "m2l_hash", "p2p_cnt", "p2p_hash")}
+            rc = lib.oracle_copy_digests(h, _p(d["m2l_cnt"]), _p(d["m2l_hash"]),
+                                         _p(d["p2p_cnt"]), _p(d["p2p_hash"]))
+            if rc:
+                raise OracleError(rc)
+            res.digests = d
         if numeric:
             res.phi = np.zeros(n)
             res.acc = np.zeros((n, 3))

@@ -278,11 +278,75 @@ def test_expansions_match_oracle(orc, order):
     plan.close()
 
 
+def golden_level_totals(name):
+    """Per-level totals of the oracle's list digests for a lattice workload
+    (tests/golden/lattice_256_digests.txt, written by make_lattice_digests.py)."""
+    import os
+    rows = {}
+    path = os.path.join(os.path.dirname(__file__), "golden", "lattice_256_digests.txt")
+    for ln in open(path):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        w, lv, nt, mc, mh, pc, ph = ln.split()
+        if w == name:
+            rows[int(lv)] = (int(nt), int(mc), int(mh, 16), int(pc), int(ph, 16))
+    return rows
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,n_sample", [("lattice_256_f32", 256), ("lattice_256_p8", 24),
-                                           ("hernquist_4e7", 64)])
+@pytest.mark.parametrize("name", ["lattice_256_f32", "lattice_256_p8"])
+def test_parity_lattice_full_lists(orc, name):
+    """256^3 displaced lattice (fp32 order 4 theta 0.7 leaf 64; fp64 order 8
+    theta 0.5 leaf 64), in the launch configuration the benchmark uses: keys,
+    permutation and tree in full; every target's M2L and P2P lists through
+    their digests (entry count and order-independent source hash, formed here
+    from the GPU's copied lists and by the oracle's digest-mode walk), target
+    by target, and their per-level totals against the stored ones; values at
+    256 seeded particles."""
+    from listdigest import csr_digests
+    c = W.CONFIGS[name]
+    say(f"  case {name}: generating")
+    pos, mass = inputs(c["dist"], c["n"], c["seed"], c["dtype"])
+    say("  gpu")
+    plan, phi, acc = gpu_run(pos, mass, c["order"], c["theta"], c["leaf"], c["dtype"])
+    say("  oracle digest walk")
+    ref = orc.fmm(pos, mass, c["order"], c["theta"], c["leaf"], digests="walk")
+    keys, perm = plan.copy_keys()
+    assert np.array_equal(keys, ref.keys) and np.array_equal(perm, ref.perm)
+    tree = plan.copy_tree()
+    for f in ("level", "prefix", "begin", "count", "parent", "first_child", "n_child"):
+        assert np.array_equal(tree[f], getattr(ref, f)), f"tree field {f} differs"
+    say("  gpu lists -> digests")
+    lists = plan.copy_lists()
+    st = plan.stats()
+    assert st["n_m2l"] == ref.n_m2l and st["n_p2p"] == ref.n_p2p
+    gold = golden_level_totals(name)
+    level = tree["level"]
+    for kind in ("m2l", "p2p"):
+        cnt, h = csr_digests(lists[kind + "_off"], lists[kind + "_src"])
+        assert np.array_equal(cnt, ref.digests[kind + "_cnt"]), f"{kind} entry counts differ"
+        bad = np.nonzero(h != ref.digests[kind + "_hash"])[0]
+        assert bad.size == 0, f"{kind} lists of {bad.size} targets differ (first {bad[:5]})"
+        col = 1 if kind == "m2l" else 3
+        with np.errstate(over="ignore"):
+            for lv, row in gold.items():
+                sel = level == lv
+                assert int(sel.sum()) == row[0], (kind, lv)
+                assert int(cnt[sel].sum(dtype=np.uint64)) == row[col], (kind, lv)
+                assert int(h[sel].sum(dtype=np.uint64)) == row[col + 1], (kind, lv)
+        assert set(gold) == set(range(int(level.max()) + 1))
+    del lists, ref
+    smp = np.random.default_rng(78).choice(c["n"], 256, replace=False)
+    say("  oracle (sampled values)")
+    ref = orc.fmm(pos, mass, c["order"], c["theta"], c["leaf"], sample=smp)
+    check_values(phi, acc, ref, c["dtype"], idx=smp, no_floor=True)
+    plan.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,n_sample", [("hernquist_4e7", 64)])
 def test_parity_large_sampled(orc, name, n_sample):
-    """256^3 displaced lattice and the 4e7-particle Hernquist sphere: keys,
+    """The 4e7-particle Hernquist sphere of the accuracy-runtime sweep: keys,
     permutation and tree in full; lists and values for the leaves of a seeded
     particle sample (the oracle's walk is restricted to those targets)."""
     c = W.CONFIGS[name]

@@ -195,6 +195,53 @@ def test_walk_brute_force(orc, name, n, S, theta):
     assert pp == {(b, a) for a, b in pp}
 
 
+def test_list_digest_hash_golden(orc):
+    """The digest hash is SplitMix64 seeded with 0 (output s + 1 for source s):
+    the first outputs of the generator's reference implementation, from the
+    numpy helper and from the oracle (a two-particle set has one leaf whose only
+    list is P2P(root <- root), so its P2P hash is h(0))."""
+    from listdigest import splitmix_h
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "splitmix64.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    want = np.array([int(v, 16) for _, v in rows], dtype=np.uint64)
+    idx = np.array([int(k) for k, _ in rows]) - 1
+    assert np.array_equal(splitmix_h(idx), want)
+    r = orc.fmm(np.array([[0.1, 0.2, 0.3], [0.4, 0.1, 0.9]]), np.ones(2), 4, 0.7, 4,
+                numeric=False, digests="lists")
+    assert r.digests["p2p_cnt"].tolist() == [1] and r.digests["p2p_hash"][0] == want[0]
+
+
+@pytest.mark.parametrize("name,n,S,theta", [("uniform", 30000, 8, 0.7), ("plummer", 40000, 16, 0.5),
+                                            ("clustered", 60000, 32, 0.6),
+                                            ("lattice_small", 32768, 12, 0.5)])
+def test_list_digests_walk_equals_lists(orc, name, n, S, theta):
+    """The digest-mode walk (pairs below level 4 walked in parallel, entries
+    hashed instead of stored) gives the digests of the stored lists of the
+    plain walk, target by target, and the numpy digests of those lists agree
+    with the oracle's."""
+    from listdigest import csr_digests
+    if name == "lattice_small":  # a 32^3 jittered lattice: uniform deep tree
+        g = (np.indices((32, 32, 32)).reshape(3, -1).T + 0.5) / 32.0
+        pos = g + 0.01 * np.random.default_rng(3).standard_normal(g.shape) / 32.0
+    else:
+        pos, _ = W.make(name, n, 17)
+    mass = np.ones(pos.shape[0])
+    r = orc.fmm(pos, mass, 2, theta, S, numeric=False, digests="lists")
+    rw = orc.fmm(pos, mass, 2, theta, S, digests="walk")
+    assert rw.n_m2l == r.n_m2l and rw.n_p2p == r.n_p2p
+    for k in r.digests:
+        assert np.array_equal(r.digests[k], rw.digests[k]), k
+    for kind in ("m2l", "p2p"):
+        cnt, h = csr_digests(getattr(r, kind + "_off"), getattr(r, kind + "_src"), chunk=4099)
+        assert np.array_equal(cnt, r.digests[kind + "_cnt"])
+        assert np.array_equal(h, r.digests[kind + "_hash"])
+    # a dropped or changed entry changes the digest of its target
+    src = r.m2l_src.copy()
+    src[len(src) // 2] += 1
+    _, h = csr_digests(r.m2l_off, src)
+    assert (h != r.digests["m2l_hash"]).sum() == 1
+
+
 def test_walk_theta_tie_golden(orc):
     rows = [l.split() for l in open(os.path.join(GOLDEN, "theta_tie.txt"))
             if l.strip() and not l.startswith("#")]
