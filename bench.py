@@ -3,7 +3,14 @@
 A step is one fmm_build + fmm_eval (Morton keys, radix sort, octree, dual-tree
 walk, P2M, M2M, M2L, L2L, L2P, P2P, combine) over the headline workload:
 N = 10^6 particles, 64-Plummer clustered set (seed 1005), fp64, order 4,
-theta 0.7, leaf 32, inputs resident in HBM.  Prints one JSON line.
+theta 0.7, leaf 32, inputs resident in HBM.  Prints one JSON line: the
+throughput over the timed steps, the per-step best of 3 and median of 10, the
+roofline of the dominant kernel (and of the other compute kernels) against the
+published and the measured peaks, the HBM rates of the memory-bound stages,
+and, outside the timed region, the accuracy (p99 and largest relative
+acceleration error against direct summation at 4096 seeded targets, the
+momentum residual), the cheapest setting that meets the 1e-3 p99 bar on the
+same particles, and the CPU oracle's time and its agreement with the GPU.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --sweep [--sweep-n N] [--sweep-orders 2,4,6,8] [--sweep-thetas ...]
@@ -90,13 +97,21 @@ def hbm_stages(cfg, st, stage_ms, kernel_ms):
     and writes the record; P2M reads the records and writes K moments per
     leaf; L2P reads the record, the leaf index, and per leaf the centre and K
     locals, and writes four results."""
-    n, nl = cfg["n"], st["n_leaves"]
+    n, nl, nn = cfg["n"], st["n_leaves"], st["n_nodes"]
     w = 8 if cfg["dtype"] == "f64" else 4
     K = (cfg["order"] + 1) * (cfg["order"] + 2) * (cfg["order"] + 3) // 6
     passes = 7
     items = {
         "keys": (n * (4 * w + 3 * w + 8 + 4), stage_ms["keys"], "stage"),
         "sort": (n * (passes * (8 + 12 + 12) + 4 + 4 * w + 4 * w), stage_ms["sort"], "stage"),
+        # the sorted keys read once, the leaf index of every particle written,
+        # and the node arrays written (level 1, prefix 8, begin, count, parent,
+        # first child 4 each, child count 1, centre 24, cell coords 8, criterion
+        # record 16: 74 B per node)
+        "tree": (n * (8 + 4) + nn * 74, stage_ms["tree"], "stage"),
+        # 8 B per emitted list entry (a source id written and read back once)
+        # and 16 B per node (its criterion record read once per level)
+        "walk": ((st["n_m2l"] + st["n_p2p"]) * 8 + nn * 16, stage_ms["walk"], "stage"),
         "p2m": (n * 4 * w + nl * (12 + 24 + K * w), kernel_ms["p2m"], "kernel"),
         "l2p": (n * (4 * w + 4 + 4 * w) + nl * (24 + K * w), kernel_ms["l2p"], "kernel"),
     }
@@ -166,15 +181,137 @@ def copy_probe(nbytes=1 << 30, reps=5):
                       "reps": reps}))
 
 
-def cpu_baseline(pos, mass, cfg):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def copy_rate_gbs(nbytes=1 << 30, reps=5):
+    """A plain 1 GiB device-to-device copy, best of `reps` after one warm-up:
+    bytes read + bytes written over its event time."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = 1e30
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (best * 1e-3) / 1e9
+
+
+def measured_peaks():
+    from multipole_body_gravity_amd import fmm
+    f64, f32 = fmm.measure_peaks()
+    return {"fp64_vector_tflops": round(f64, 2), "fp32_vector_unpacked_tflops": round(f32, 2),
+            "hbm_copy_gbs": round(copy_rate_gbs(), 1),
+            "how": "fma-chain kernel (fmm_measure_peaks, best of 3) and a 1 GiB device copy "
+                   "(read + write bytes, best of 5)"}
+
+
+def _rel(got, ref):
+    nref = np.linalg.norm(ref, axis=-1) if ref.ndim == 2 else np.abs(ref)
+    d = np.linalg.norm(got - ref, axis=-1) if ref.ndim == 2 else np.abs(got - ref)
+    return d / nref
+
+
+def direct_reference(tpos, tmass, n, n_targets=4096, seed=4242):
+    """fp64 direct sums (fmm_direct) at a seeded sample of targets."""
+    import torch
+
+    from multipole_body_gravity_amd import direct
+    tg = np.sort(np.random.default_rng(seed).choice(n, min(n_targets, n), replace=False))
+    ttg = torch.from_numpy(tg).to(tpos.device)
+    rphi, racc = direct(tpos, tmass, ttg)
+    return tg, rphi.double().cpu().numpy(), racc.double().cpu().numpy()
+
+
+def accuracy_vs_direct(ref, phi, acc):
+    tg, rphi, racc = ref
+    ea = _rel(acc[tg].double().cpu().numpy(), racc)
+    ep = _rel(phi[tg].double().cpu().numpy(), rphi)
+    return {"targets": int(tg.size), "acc_rel_err_p99": float(np.percentile(ea, 99)),
+            "acc_rel_err_max": float(ea.max()), "phi_rel_err_p99": float(np.percentile(ep, 99))}
+
+
+def momentum_residual(acc, mass):
+    """|sum_i m_i a_i| / sum_i m_i |a_i| of the evaluated accelerations (fp64)."""
+    a = acc.double()
+    m = mass.double()[:, None]
+    return float(((m * a).sum(0).norm() / (m[:, 0] * a.norm(dim=1)).sum()).item())
+
+
+def accuracy_matched(cfg, tpos, tmass, ref, bar=1e-3, steps=5):
+    """The cheapest (order, theta) among a few candidates whose p99 relative
+    acceleration error against direct summation is within `bar` on the same
+    particles: build + eval time (mean of `steps` after two untimed steps) and
+    the error of each candidate."""
+    import torch
+
+    from multipole_body_gravity_amd import Plan
+    n = cfg["n"]
+    rows = []
+    for order, theta in [(5, 0.6), (6, 0.6), (5, 0.5), (6, 0.5)]:
+        plan = Plan(n, order=order, theta=theta, leaf_size=cfg["leaf"], dtype=tpos.dtype,
+                    device=tpos.device)
+        phi = torch.empty(n, dtype=tpos.dtype, device=tpos.device)
+        acc = torch.empty(n, 3, dtype=tpos.dtype, device=tpos.device)
+        for _ in range(2):
+            plan.build(tpos, tmass)
+            plan.eval(phi, acc)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            plan.build(tpos, tmass)
+            plan.eval(phi, acc)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        err = accuracy_vs_direct(ref, phi, acc)
+        rows.append({"order": order, "theta": theta, "ms_per_step": round(ms, 3),
+                     "value": round(n / (ms * 1e-3), 1), "acc_rel_err_p99": err["acc_rel_err_p99"],
+                     "acc_rel_err_max": err["acc_rel_err_max"]})
+        plan.close()
+        del phi, acc
+    ok = [r for r in rows if r["acc_rel_err_p99"] <= bar]
+    best = min(ok, key=lambda r: r["ms_per_step"]) if ok else None
+    return {"bar_p99": bar, "chosen": best, "candidates": rows,
+            "how": f"mean of {steps} build+eval steps each, errors at the same targets as 'accuracy'"}
+
+
+def cpu_baseline(pos, mass, cfg, phi=None, acc=None):
+    """The oracle on the same workload on the host's cores; also the largest
+    per-particle relative error of the GPU's outputs (phi, acc: host arrays in
+    the caller's order, or None) against it."""
     from oracle import oracle as orc
     cores = len(os.sched_getaffinity(0))
     orc.set_threads(cores)
     t0 = time.perf_counter()
-    orc.fmm(pos, mass, cfg["order"], cfg["theta"], cfg["leaf"])
+    ref = orc.fmm(pos, mass, cfg["order"], cfg["theta"], cfg["leaf"])
     dt = time.perf_counter() - t0
-    return {"value": round(cfg["n"] / dt, 1), "unit": "particles/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full workload ({cfg['n']} particles, one oracle build+eval, {dt:.1f} s)"}
+    out = {"value": round(cfg["n"] / dt, 1), "unit": "particles/s", "cores": cores,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"the full workload ({cfg['n']} particles, one oracle build+eval, {dt:.1f} s)"}
+    if acc is not None:
+        ea = _rel(acc, ref.acc)
+        ep = _rel(phi, ref.phi)
+        out["gpu_vs_oracle"] = {"particles": int(cfg["n"]), "acc_rel_err_max": float(ea.max()),
+                                "phi_rel_err_max": float(ep.max()),
+                                "tolerance": 1e-11 if cfg["dtype"] == "f64" else 1e-4}
+    return out
 
 
 def sweep(args):
@@ -422,6 +559,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-accuracy-matched", action="store_true",
+                    help="skip the search for the cheapest setting within the 1e-3 p99 bar")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
@@ -484,18 +623,31 @@ def main():
     # stream; the library reads them at the synchronizations a build makes
     # anyway, so the timed loop carries no extra synchronization
     plan.set_timing(True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        evs[k][0].record()
         plan.build(tpos, tmass)
         plan.eval(phi, acc)
+        evs[k][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in evs]
     s = plan.stats()  # means over the K timed steps
     assert s["timed_builds"] == args.steps and s["timed_evals"] == args.steps, s
     stage_avg = s["stage_ms"]
     kern_avg = s["kernel_ms"]
     ms_step = wall / args.steps * 1e3
+
+    # accuracy of the last step's outputs, outside the timed region
+    ref = direct_reference(tpos, tmass, cfg["n"])
+    accuracy = accuracy_vs_direct(ref, phi, acc)
+    accuracy["bar_p99"] = 1e-3
+    accuracy["bar_met"] = bool(accuracy["acc_rel_err_p99"] <= 1e-3)
+    accuracy["momentum_residual"] = momentum_residual(acc, tmass)
+    peaks = measured_peaks()
 
     # algorithmic flops per launch of each compute kernel, over its measured
     # average launch time (HIP events recorded on the launch stream)
@@ -505,9 +657,14 @@ def main():
     peak = FP64_VECTOR_PEAK_TFLOPS if cfg["dtype"] == "f64" else FP32_VECTOR_PEAK_TFLOPS
     rl = {k: roofline_obj(flops[k], kern_avg[k], peak, measured_traffic(k, args.workload))
           for k in flops if kern_avg[k] > 0}
+    mpeak = peaks["fp64_vector_tflops"] if cfg["dtype"] == "f64" else \
+        peaks["fp32_vector_unpacked_tflops"]
+    for v in rl.values():
+        v["frac_of_measured_peak"] = round(v["achieved"] / mpeak, 4)
     dominant = max(rl, key=lambda k: kern_avg[k])
     roof = dict(rl[dominant])
     roof["kernel"] = dominant
+    sorted_ms = sorted(step_ms)
 
     out = {
         "metric": METRIC,
@@ -517,6 +674,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": {"best_of_3": round(min(step_ms[:3]), 4),
+                    "median_of_10": round(float(np.median(step_ms[:10])), 4),
+                    "min": round(sorted_ms[0], 4), "max": round(sorted_ms[-1], 4),
+                    "how": "HIP events on the launch stream around each timed build + eval; "
+                           "best of the first 3, median of the first 10"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -528,6 +690,8 @@ def main():
         "roofline": roof,
         "roofline_other": {k: v for k, v in rl.items() if k != dominant},
         "hbm": hbm_stages(cfg, st, stage_avg, kern_avg),
+        "accuracy": accuracy,
+        "measured_peaks": peaks,
         "stage_ms": {k: round(v, 4) for k, v in stage_avg.items() if k != "vjp"},
         "kernel_ms": {k: round(v, 4) for k, v in kern_avg.items() if not k.startswith("vjp")},
         "work": {"n_m2l": n_m2l, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,
@@ -536,9 +700,12 @@ def main():
                  "m2l_flops_per_pair": fpp, "p2p_flops_per_pair": P2P_FLOPS_PER_PAIR,
                  "m2l_flops_per_pair_plain_cartesian": m2l_flops_per_pair_plain(cfg["order"])},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(pos, mass, cfg)
     plan.close()
+    if not args.no_accuracy_matched:
+        out["accuracy_matched"] = accuracy_matched(cfg, tpos, tmass, ref)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pos, mass, cfg, phi.double().cpu().numpy(),
+                                           acc.double().cpu().numpy())
     print(json.dumps(out))
 
 

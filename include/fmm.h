@@ -260,6 +260,16 @@ int fmm_direct(const void* pos, const void* mass, int64_t n, const int64_t* targ
 int fmm_direct_noalloc(const void* pos, const void* mass, int64_t n, const int64_t* targets,
                        int64_t n_targets, int dtype, void* phi, void* acc, void* stream);
 
+/* ---- measurement ---- */
+
+/* Measured vector multiply-add rates of the current device, in TFLOP/s (two
+ * flops per multiply-add): a kernel of independent fma chains filling every
+ * compute unit, best of three timed runs after one warm-up, for fp64 and for
+ * fp32 as this library compiles it (no packed two-wide fp32 operations).  The
+ * benchmark reports the fraction of these next to the published peaks.
+ * Allocates a small output buffer and synchronizes `stream`. */
+int fmm_measure_peaks(double* fp64_tflops, double* fp32_tflops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,7 @@ def load_library():
     lib.fmm_copy_lists.argtypes = [P] * 5
     lib.fmm_copy_expansions.argtypes = [P, P, P]
     lib.fmm_direct.argtypes = [P, P, i64, P, i64, i32, P, P, P]
+    lib.fmm_measure_peaks.argtypes = [P, P, P]
     lib.fmm_direct_noalloc.argtypes = [P, P, i64, P, i64, i32, P, P, P]
     _lib = lib
     return lib
@@ -288,3 +289,13 @@ def direct_noalloc(pos: torch.Tensor, mass: torch.Tensor, targets: torch.Tensor,
     phi [T] and acc [T,3] to keep the call free of any allocation."""
     return _direct_call("fmm_direct_noalloc", pos, mass, targets, phi, acc, stream)
 
+
+def measure_peaks(stream=None):
+    """Measured fp64 and fp32 (unpacked) vector multiply-add rates of the
+    current device in TFLOP/s (fmm_measure_peaks)."""
+    lib = load_library()
+    f64, f32 = ctypes.c_double(), ctypes.c_double()
+    rc = lib.fmm_measure_peaks(ctypes.byref(f64), ctypes.byref(f32), _stream_handle(stream))
+    if rc:
+        raise FmmError(rc, "fmm_measure_peaks")
+    return f64.value, f32.value
