@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FMM_MAX_ORDER 8
+#define FMM_MAX_ORDER 10
 /* Largest octree a build accepts: node ids are 32-bit.  (Clustered inputs with
  * a small leaf size can need more cells than particles, so N < 2^31 alone does
  * not bound it.) */
@@ -196,6 +196,14 @@ const char* fmm_strerror(int code);
  * FMM_ERR_ARG for a null pointer or n_nodes outside [1, FMM_MAX_NODES].
  * Host only; touches no device. */
 int fmm_node_id_bits(int64_t n_nodes, int* bits);
+
+/* Size of the walk's work pools at the start of each build, in entries per
+ * tree node (-1, the default: 128 per node, grown from build to build as
+ * needed).  A pool that runs out during a build is regrown from the measured
+ * use and the walk repeated (fmm_stats_t.walk_retries counts the repeats;
+ * FMM_ERR_OOM after 12); small values trade memory for repeats.  Lists and
+ * results do not depend on it.  FMM_ERR_ARG for values below -1. */
+int fmm_set_walk_pool_hint(fmm_plan_t plan, int64_t entries_per_node);
 
 /* Turn HIP-event timing of the stages and of the main kernels on (1) or off
  * (0).  Events are recorded between launches on the stream that runs them

@@ -258,10 +258,18 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   }
   if (p->pbeg[MAX_LEVELS + 1] != np) return FMM_ERR_HIP;
   // first guesses for the pools (regrown from the measured use on overflow)
-  // (a group reserves its candidate count in each of the three unions)
-  const int64_t guess[N_POOLS] = {128 * nn + 4096, 128 * nn + 4096, 128 * nn + 4096};
-  for (int k = 0; k < N_POOLS; k++)
-    p->shard_cap[k] = std::max<int64_t>(p->shard_cap[k], std::max<int64_t>(guess[k] / POOL_SHARDS, 2048));
+  // (a group reserves its candidate count in each of the three unions): 128
+  // entries per node and at least 2048 per shard, kept from build to build;
+  // with a caller's hint, exactly hint entries per node at every build
+  if (p->pool_hint >= 0) {
+    const int64_t cap = std::max<int64_t>((p->pool_hint * nn + 4096) / POOL_SHARDS, 1);
+    for (int k = 0; k < N_POOLS; k++) p->shard_cap[k] = cap;
+  } else {
+    const int64_t guess = 128 * nn + 4096;
+    for (int k = 0; k < N_POOLS; k++)
+      p->shard_cap[k] =
+          std::max<int64_t>(p->shard_cap[k], std::max<int64_t>(guess / POOL_SHARDS, 2048));
+  }
 
   WalkArgs a{};
   a.geo = P<int4>(p->ngeo);
@@ -616,6 +624,12 @@ int fmm_destroy(fmm_plan_t p) {
 int fmm_node_id_bits(int64_t n_nodes, int* bits) {
   if (!bits || n_nodes < 1 || n_nodes > FMM_MAX_NODES) return FMM_ERR_ARG;
   *bits = bits_for(n_nodes);
+  return FMM_OK;
+}
+
+int fmm_set_walk_pool_hint(fmm_plan_t p, int64_t entries_per_node) {
+  if (!p || entries_per_node < -1) return FMM_ERR_ARG;
+  p->pool_hint = entries_per_node;
   return FMM_OK;
 }
 

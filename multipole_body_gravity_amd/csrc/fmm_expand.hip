@@ -52,9 +52,9 @@ static hipError_t ensure_table() {
   return e;
 }
 
-__constant__ double c_inv_int[FMM_MAX_ORDER + 2] = {0.0,       1.0,       0.5,
-                                                     1.0 / 3.0, 0.25,      0.2,
-                                                     1.0 / 6.0, 1.0 / 7.0, 0.125, 1.0 / 9.0};
+__constant__ double c_inv_int[FMM_MAX_ORDER + 2] = {0.0,        1.0,       0.5,       1.0 / 3.0,
+                                                     0.25,       0.2,       1.0 / 6.0, 1.0 / 7.0,
+                                                     0.125,      1.0 / 9.0, 0.1,       1.0 / 11.0};
 
 // x^n / n!
 __device__ __forceinline__ double pow_over_fact(double x, int n) {
@@ -67,6 +67,7 @@ constexpr int EX_THREADS = 256;
 constexpr int EX_WAVES = EX_THREADS / WAVE;
 constexpr int PP = FMM_MAX_ORDER + 1;  // entries of a 1-d power table
 constexpr int MAXCH = 8;
+constexpr int KSLOTS = (MAXK + WAVE - 1) / WAVE;  // coefficients per lane in the wave-per-leaf kernels
 
 // ---------------- register-resident variants ----------------
 // Used wherever they beat the wave-per-node kernels further down: P2M, M2M
@@ -472,7 +473,7 @@ __global__ void __launch_bounds__(EX_THREADS)
        li += (int64_t)gridDim.x * EX_WAVES) {
     const int32_t node = leaves[li];
     const double c[3] = {centre[3 * node], centre[3 * node + 1], centre[3 * node + 2]};
-    double acc[3] = {0.0, 0.0, 0.0};  // coefficients lane, lane+64, lane+128
+    double acc[KSLOTS] = {};  // coefficients lane, lane + 64, ...
     const int32_t j0 = begin[node], j1 = j0 + count[node];
     for (int32_t jb = j0; jb < j1; jb += WAVE) {
       const int nj = min(WAVE, j1 - jb);
@@ -490,7 +491,7 @@ __global__ void __launch_bounds__(EX_THREADS)
         ms[w][lane] = (double)p.m;
       }
       __builtin_amdgcn_wave_barrier();
-      for (int r = 0; r < 3; r++) {
+      for (int r = 0; r < KSLOTS; r++) {
         const int m = lane + WAVE * r;
         if (m >= K) break;
         const int a = c_mi.a[m], b = c_mi.b[m], cc = c_mi.c[m];
@@ -500,7 +501,7 @@ __global__ void __launch_bounds__(EX_THREADS)
       }
       __builtin_amdgcn_wave_barrier();
     }
-    for (int r = 0; r < 3; r++) {
+    for (int r = 0; r < KSLOTS; r++) {
       const int m = lane + WAVE * r;
       if (m < K) mpole[(int64_t)node * K + m] = (T)acc[r];
     }
@@ -716,7 +717,7 @@ static void l2p_dispatch(int order, unsigned g, hipStream_t st, int64_t n, const
     k_l2p<T, P><<<g, 256, 0, st>>>(n, pts, leaf_of, centre, local, far); \
     break;
     L2P_CASE(0) L2P_CASE(1) L2P_CASE(2) L2P_CASE(3) L2P_CASE(4)
-    L2P_CASE(5) L2P_CASE(6) L2P_CASE(7) L2P_CASE(8)
+    L2P_CASE(5) L2P_CASE(6) L2P_CASE(7) L2P_CASE(8) L2P_CASE(9) L2P_CASE(10)
 #undef L2P_CASE
     default:
       break;
@@ -782,7 +783,7 @@ __global__ void __launch_bounds__(EX_THREADS)
        li += (int64_t)gridDim.x * EX_WAVES) {
     const int32_t node = leaves[li];
     const double c[3] = {centre[3 * node], centre[3 * node + 1], centre[3 * node + 2]};
-    double acc[3] = {0.0, 0.0, 0.0};  // coefficients lane, lane+64, lane+128
+    double acc[KSLOTS] = {};  // coefficients lane, lane + 64, ...
     const int32_t j0 = begin[node], j1 = j0 + count[node];
     for (int32_t jb = j0; jb < j1; jb += WAVE) {
       const int nj = min(WAVE, j1 - jb);
@@ -803,7 +804,7 @@ __global__ void __launch_bounds__(EX_THREADS)
         wq[w][lane][3] = (double)r.c.m;
       }
       __builtin_amdgcn_wave_barrier();
-      for (int rr = 0; rr < 3; rr++) {
+      for (int rr = 0; rr < KSLOTS; rr++) {
         const int m = lane + WAVE * rr;
         if (m >= K) break;
         const int a = c_mi.a[m], b = c_mi.b[m], cc = c_mi.c[m];
@@ -820,7 +821,7 @@ __global__ void __launch_bounds__(EX_THREADS)
       }
       __builtin_amdgcn_wave_barrier();
     }
-    for (int rr = 0; rr < 3; rr++) {
+    for (int rr = 0; rr < KSLOTS; rr++) {
       const int m = lane + WAVE * rr;
       if (m < K) mpole[(int64_t)node * K + m] = (T)acc[rr];
     }
@@ -980,7 +981,7 @@ static void l2p_vjp_dispatch(int order, unsigned g, hipStream_t st, int64_t n, c
     k_l2p_vjp<T, P><<<g, 256, 0, st>>>(n, rec, leaf_of, centre, local, blocal, out); \
     break;
     L2PV_CASE(0) L2PV_CASE(1) L2PV_CASE(2) L2PV_CASE(3) L2PV_CASE(4)
-    L2PV_CASE(5) L2PV_CASE(6) L2PV_CASE(7) L2PV_CASE(8)
+    L2PV_CASE(5) L2PV_CASE(6) L2PV_CASE(7) L2PV_CASE(8) L2PV_CASE(9) L2PV_CASE(10)
 #undef L2PV_CASE
     default:
       break;

@@ -134,6 +134,7 @@ struct fmm_plan_s {
   mbg::RootInfo root_host{};
 
   int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0};  // entries per shard, per pool
+  int64_t pool_hint = -1;  // walk pool entries per node at each build; -1: automatic
 
   mbg::Control* ctrl_host = nullptr;  // pinned
   // The upward pass (P2M, M2M, M2L source records) depends only on the tree, so

@@ -446,7 +446,7 @@ static void records_dispatch(int order, unsigned g, hipStream_t st, int64_t n, c
     k_m2l_records<T, P><<<g, 256, 0, st>>>(n, c, m, r); \
     break;
     REC_CASE(0) REC_CASE(1) REC_CASE(2) REC_CASE(3) REC_CASE(4)
-    REC_CASE(5) REC_CASE(6) REC_CASE(7) REC_CASE(8)
+    REC_CASE(5) REC_CASE(6) REC_CASE(7) REC_CASE(8) REC_CASE(9) REC_CASE(10)
 #undef REC_CASE
     default:
       break;
@@ -489,7 +489,7 @@ static void m2l_sib_dispatch(int order, hipStream_t st, const M2LArgs& a) {
                                                 a.centre, rec, (T*)a.local);                 \
     break;
     M2L_SIB(0) M2L_SIB(1) M2L_SIB(2) M2L_SIB(3) M2L_SIB(4)
-    M2L_SIB(5) M2L_SIB(6) M2L_SIB(7) M2L_SIB(8)
+    M2L_SIB(5) M2L_SIB(6) M2L_SIB(7) M2L_SIB(8) M2L_SIB(9) M2L_SIB(10)
 #undef M2L_SIB
     default:
       break;
@@ -514,7 +514,7 @@ static void m2l_tail_dispatch(int order, hipStream_t st, const M2LArgs& a, bool 
                                                  a.src_mask, a.centre, rec, (T*)a.part);     \
     break;
     M2L_TAIL(0) M2L_TAIL(1) M2L_TAIL(2) M2L_TAIL(3) M2L_TAIL(4)
-    M2L_TAIL(5) M2L_TAIL(6) M2L_TAIL(7) M2L_TAIL(8)
+    M2L_TAIL(5) M2L_TAIL(6) M2L_TAIL(7) M2L_TAIL(8) M2L_TAIL(9) M2L_TAIL(10)
 #undef M2L_TAIL
     default:
       break;

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmbg_fmm.so")
 
 FMM_F32, FMM_F64 = 0, 1
-MAX_ORDER = 8
+MAX_ORDER = 10
 STAGES = ["keys", "sort", "tree", "walk", "up", "m2l", "down", "p2p", "tail", "vjp"]  # stage_ms order
 KERNELS = ["m2l_sib", "m2l_tail", "p2p", "p2p_combine", "vjp_m2l_sib", "vjp_p2p", "p2m",
            "l2p"]  # kernel_ms order
@@ -62,6 +62,7 @@ def load_library():
     lib.fmm_strerror.argtypes = [i32]
     lib.fmm_strerror.restype = ctypes.c_char_p
     lib.fmm_set_timing.argtypes = [P, i32]
+    lib.fmm_set_walk_pool_hint.argtypes = [P, i64]
     lib.fmm_stats.argtypes = [P, ctypes.POINTER(_Stats)]
     lib.fmm_copy_keys.argtypes = [P, P, P]
     lib.fmm_copy_tree.argtypes = [P] * 8
@@ -182,6 +183,12 @@ class Plan:
                                             _stream_handle(stream))
         self._check(rc, "fmm_lattice_steps")
         return q, u
+
+    def set_walk_pool_hint(self, entries_per_node: int = -1) -> None:
+        """Walk pool size at each build's start, entries per node (-1: automatic;
+        fmm_set_walk_pool_hint)."""
+        self._check(self.lib.fmm_set_walk_pool_hint(self._h, int(entries_per_node)),
+                    "fmm_set_walk_pool_hint")
 
     def set_timing(self, enable: bool = True) -> None:
         self._check(self.lib.fmm_set_timing(self._h, 1 if enable else 0), "fmm_set_timing")

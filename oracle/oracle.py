@@ -23,13 +23,26 @@ ERR_OOM = -3
 ERR_NONFINITE = -5
 
 
-def build_library() -> str:
-    """Compile oracle.c with gcc (no fused multiply-add, OpenMP over targets)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-D_POSIX_C_SOURCE=200809L", "-fopenmp",
-           "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-o", LIB + ".tmp", SRC, "-lm"]
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+# ORACLE_SANITIZE=1: build and load the oracle with AddressSanitizer and
+# UndefinedBehaviorSanitizer (CPU code only; python itself is not
+# instrumented, so the run needs the ASan runtime preloaded:
+#   ORACLE_SANITIZE=1 LD_PRELOAD=$(gcc -print-file-name=libasan.so) \
+#   ASAN_OPTIONS=detect_leaks=0 python -m pytest tests/test_oracle.py)
+SANITIZE = os.environ.get("ORACLE_SANITIZE", "0") == "1"
+
+
+def build_library(sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc (no fused multiply-add, OpenMP over targets);
+    sanitize: with -fsanitize=address,undefined (aborting on the first report)."""
+    out = SAN_LIB if sanitize else LIB
+    flags = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer"] if sanitize else ["-O2"]
+    cmd = ["gcc", *flags, "-std=c11", "-D_POSIX_C_SOURCE=200809L", "-fopenmp",
+           "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-o", out + ".tmp", SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None
@@ -39,9 +52,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        build_library()
-    lib = ctypes.CDLL(LIB)
+    path = SAN_LIB if SANITIZE else LIB
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):
+        build_library(sanitize=SANITIZE)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lib.oracle_ncoef.argtypes = [i32]

@@ -27,7 +27,8 @@ def test_header_declares_entry_points():
     for want in ["fmm_plan", "fmm_build", "fmm_eval", "fmm_destroy", "fmm_strerror",
                  "fmm_set_timing", "fmm_stats", "fmm_copy_keys", "fmm_copy_tree",
                  "fmm_copy_lists", "fmm_copy_expansions", "fmm_direct", "fmm_vjp", "fmm_lattice_steps",
-                 "fmm_node_id_bits", "fmm_direct_noalloc"]:
+                 "fmm_node_id_bits", "fmm_direct_noalloc", "fmm_set_walk_pool_hint",
+                 "fmm_measure_peaks"]:
         assert want in names
 
 
@@ -45,10 +46,12 @@ def test_strerror(lib):
 
 @pytest.mark.parametrize("args", [
     (0, 4, 0.7, 32, 1), (-5, 4, 0.7, 32, 1), (2 ** 31, 4, 0.7, 32, 1),
-    (10, -1, 0.7, 32, 1), (10, 9, 0.7, 32, 1),
+    (10, -1, 0.7, 32, 1), (10, 11, 0.7, 32, 1),
     (10, 4, 0.0, 32, 1), (10, 4, 1.0, 32, 1), (10, 4, float("nan"), 32, 1),
     (10, 4, 0.7, 0, 1), (10, 4, 0.7, 32, 2), (10, 4, 0.7, 32, -1)])
 def test_plan_rejects_bad_arguments(lib, args):
+    """Orders 0..10 are accepted (FMM_MAX_ORDER = 10); everything outside the
+    documented ranges is refused before any device call."""
     h = ctypes.c_void_p()
     assert lib.fmm_plan(ctypes.byref(h), *args) == -1
     assert not h.value
@@ -75,6 +78,8 @@ def test_null_plan_calls(lib):
     assert lib.fmm_direct_noalloc(P(1), P(1), 10, P(1), 1, 7, P(1), P(1), None) == -1
     assert lib.fmm_direct_noalloc(P(1), P(1), 10, P(1), 0, 1, P(1), P(1), None) == 0
     assert lib.fmm_set_timing(None, 1) == -1
+    lib.fmm_set_walk_pool_hint.argtypes = [P, ctypes.c_int64]
+    assert lib.fmm_set_walk_pool_hint(None, 4) == -1
     assert lib.fmm_copy_keys(None, None, None) == -1
     assert lib.fmm_plan(None, 10, 4, 0.7, 32, 1) == -1
 

@@ -109,6 +109,10 @@ CASES = [
     ("plummer", 3000, 37, 7, 0.7, 40, "f64"),
     ("plummer", 3000, 37, 8, 0.5, 40, "f64"),
     ("plummer", 3000, 37, 8, 0.5, 40, "f32"),
+    ("plummer", 3000, 38, 9, 0.6, 24, "f64"),
+    ("clustered", 4000, 39, 10, 0.5, 32, "f64"),
+    ("uniform", 2500, 40, 9, 0.7, 16, "f32"),
+    ("plummer", 2000, 41, 10, 0.6, 40, "f32"),
 ]
 
 
@@ -237,6 +241,37 @@ def test_deterministic_and_reusable(orc):
     plan.close()
 
 
+@pytest.mark.parametrize("hint", [0, 3])
+def test_walk_pool_regrowth(orc, hint):
+    """Walk pools started far too small (hint entries per node) overflow, are
+    regrown from the measured use and the walk repeated: the lists, the tree
+    and the values are those of the oracle all the same, and a later build
+    with the automatic size needs no repeat."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    dev = torch.device("cuda:0")
+    pos, mass = W.make("clustered", 40000, 55)
+    plan = Plan(40000, order=4, theta=0.6, leaf_size=16, dtype=torch.float64, device=dev)
+    plan.set_walk_pool_hint(hint)
+    tp, tm = torch.from_numpy(pos).to(dev), torch.from_numpy(mass).to(dev)
+    plan.build(tp, tm)
+    phi, acc = plan.eval()
+    torch.cuda.synchronize()
+    retries = plan.stats()["walk_retries"]
+    say(f"    walk repeats {retries}")
+    assert retries > 0
+    ref = orc.fmm(pos, mass, 4, 0.6, 16)
+    check_structure(plan, ref)
+    check_values(phi.cpu().numpy(), acc.cpu().numpy(), ref, "f64")
+    plan.set_walk_pool_hint(-1)
+    plan.build(tp, tm)
+    phi2, acc2 = plan.eval()
+    torch.cuda.synchronize()
+    assert plan.stats()["walk_retries"] == 0
+    assert torch.equal(phi, phi2) and torch.equal(acc, acc2)
+    plan.close()
+
+
 def test_nonfinite_input_rejected():
     torch = _torch()
     from multipole_body_gravity_amd import FmmError, Plan
@@ -262,11 +297,12 @@ def test_nonfinite_input_rejected():
     plan.close()
 
 
-@pytest.mark.parametrize("order", [5, 6, 7])
+@pytest.mark.parametrize("order", [5, 6, 7, 10])
 def test_expansions_match_oracle(orc, order):
     """Moments and locals of every cell (after the downward pass): orders 5
     and 6 take the one-launch downward pass (internal locals rebuilt on a
-    copy), order 7 the level-by-level one."""
+    copy), orders 7 and 10 the level-by-level one (order 10 with the
+    wave-per-node upward and downward kernels)."""
     pos, mass = W.make("plummer", 4000, 61)
     plan, phi, acc = gpu_run(pos, mass, order, 0.6, 16, "f64")
     mp, lc = plan.copy_expansions()
@@ -460,6 +496,7 @@ VJP_CASES = [
     ("uniform", 3000, 36, 0, 0.7, 20, "f64"),
     ("plummer", 3000, 37, 8, 0.5, 40, "f64"),
     ("plummer", 3000, 37, 8, 0.5, 40, "f32"),
+    ("clustered", 3000, 42, 10, 0.6, 24, "f64"),
 ]
 
 
