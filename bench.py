@@ -559,6 +559,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mutual", action="store_true",
+                    help="sum the sibling leaves' near field mutually (fmm_set_mutual_near_field)")
     ap.add_argument("--no-accuracy-matched", action="store_true",
                     help="skip the search for the cheapest setting within the 1e-3 p99 bar")
     ap.add_argument("--workload", default=WORKLOAD)
@@ -607,6 +609,8 @@ def main():
     tmass = torch.from_numpy(mass).to(dev, tdt)
     plan = Plan(cfg["n"], order=cfg["order"], theta=cfg["theta"], leaf_size=cfg["leaf"], dtype=tdt,
                 device=dev)
+    if args.mutual:
+        plan.set_mutual_near_field(True)
     phi = torch.empty(cfg["n"], dtype=tdt, device=dev)
     acc = torch.empty(cfg["n"], 3, dtype=tdt, device=dev)
 
@@ -686,7 +690,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "distribution": cfg["dist"], "n": cfg["n"],
                    "order": cfg["order"], "theta": cfg["theta"], "leaf_size": cfg["leaf"],
-                   "seed": cfg["seed"]},
+                   "seed": cfg["seed"], "near_field": "mutual siblings" if args.mutual else "directed"},
         "roofline": roof,
         "roofline_other": {k: v for k, v in rl.items() if k != dominant},
         "hbm": hbm_stages(cfg, st, stage_avg, kern_avg),

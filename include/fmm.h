@@ -197,6 +197,17 @@ const char* fmm_strerror(int code);
  * Host only; touches no device. */
 int fmm_node_id_bits(int64_t n_nodes, int* bits);
 
+/* Near field of sibling leaves summed mutually (1) or directed (0, the
+ * default).  The leaf children of one parent touch, so all their particle
+ * pairs (a leaf with itself included) are near-field pairs in both
+ * directions; with 1, one kernel sums each such unordered pair once and adds
+ * it to both particles (for groups of at most 256 particles), and the directed
+ * near field skips those list entries (the jaccpot issue's mutual
+ * interactions, restricted to pairs whose two sides one workgroup holds).
+ * Results agree with the directed form to rounding and stay bitwise
+ * reproducible.  Takes effect at the next fmm_build; the VJP is unaffected. */
+int fmm_set_mutual_near_field(fmm_plan_t plan, int enable);
+
 /* Size of the walk's work pools at the start of each build, in entries per
  * tree node (-1, the default: 128 per node, grown from build to build as
  * needed).  A pool that runs out during a build is regrown from the measured

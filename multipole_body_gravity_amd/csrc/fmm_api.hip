@@ -433,6 +433,13 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   TRY(grow(p->tail_part,
            (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * p->K * wbytes(p->dtype)));
   TRY_HIP(launch_tail_fill(leaves, nl, tr_start, tr_cnt, ttoff, P<TailTask>(p->tail_task), st));
+  p->mut_built = false;
+  if (p->mutual) {
+    TRY(grow(p->mut_flag, (size_t)nn));
+    TRY_HIP(launch_mutual_flags(a.parents, np, a.first_child, a.n_child, P<int32_t>(p->ncount),
+                                P<uint8_t>(p->mut_flag), nn, st));
+    p->mut_built = true;
+  }
   return FMM_OK;
 }
 
@@ -601,7 +608,7 @@ int fmm_destroy(fmm_plan_t p) {
                   &p->tr_start_m2l, &p->tr_keys,   &p->tr_keys_alt, &p->tr_vals,
                   &p->tr_vals_alt, &p->m2l_off,    &p->m2l_src,     &p->p2p_off,
                   &p->p2p_src,    &p->p2p_task,    &p->p2p_part,    &p->p2p_toff,
-                  &p->split_leaves,
+                  &p->split_leaves, &p->mut_flag,
                   &p->p2p_poff,   &p->tot_m2l,     &p->tot_p2p,     &p->parents,
                   &p->m2l_order,
                   &p->tail_toff,  &p->tail_task,   &p->tail_part};
@@ -624,6 +631,12 @@ int fmm_destroy(fmm_plan_t p) {
 int fmm_node_id_bits(int64_t n_nodes, int* bits) {
   if (!bits || n_nodes < 1 || n_nodes > FMM_MAX_NODES) return FMM_ERR_ARG;
   *bits = bits_for(n_nodes);
+  return FMM_OK;
+}
+
+int fmm_set_mutual_near_field(fmm_plan_t p, int enable) {
+  if (!p || (enable != 0 && enable != 1)) return FMM_ERR_ARG;
+  p->mutual = enable == 1;
   return FMM_OK;
 }
 
@@ -808,9 +821,18 @@ int eval_impl(fmm_plan_t p, void* phi, void* acc, hipStream_t st) {
 
   rec(p, FMM_STAGE_P2P, 0, st);
   int32_t* leaves = P<int32_t>(p->leaves);
+  const uint8_t* mut = nullptr;
+  if (p->mut_built) {  // the sibling groups' pairs, both sides at once, into `far`
+    TRY_HIP(launch_p2p_mutual(p->dtype, p->n_parents, P<int32_t>(p->parents),
+                              P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild),
+                              P<int32_t>(p->nbegin), P<int32_t>(p->ncount), p->pts.p, p->far.p,
+                              st));
+    mut = P<uint8_t>(p->mut_flag);
+  }
   TRY_HIP(launch_p2p(p->dtype, p->p2p_task.p, p->n_p2p_tasks, leaves, p->n_leaves,
                      P<int64_t>(p->p2p_toff), P<int64_t>(p->p2p_poff), P<int32_t>(p->nbegin),
-                     P<int32_t>(p->ncount), P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
+                     P<int32_t>(p->ncount), mut, P<int32_t>(p->nparent),
+                     P<int32_t>(p->p2p_src), p->pts.p, p->far.p,
                      P<int32_t>(p->idx), phi, acc, p->p2p_part.p,
                      P<int32_t>(p->split_leaves), p->n_split,
                      p->timing ? p->kev + 2 * FMM_KERNEL_P2P : nullptr,

@@ -115,6 +115,10 @@ struct fmm_plan_s {
   // near-field tasks (target leaf x bounded slice of its list)
   mbg::DBuf p2p_task, p2p_part, p2p_toff, p2p_poff, tot_m2l, tot_p2p;
   mbg::DBuf split_leaves;  // positions (in the leaf list) of the split leaves, any order
+  // mutual near field of sibling groups (optional): per-node flags
+  mbg::DBuf mut_flag;
+  bool mutual = false;      // the plan's setting
+  bool mut_built = false;   // the flags of the current build exist
   int64_t n_split = 0;
   // non-leaf nodes in id order; the parents of level l are parents[pbeg[l] .. pbeg[l+1])
   mbg::DBuf parents, m2l_order;
@@ -361,9 +365,22 @@ hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t
                                 const int64_t* task_off, const int64_t* part_off,
                                 const int64_t* off, const int32_t* count, Control* ctrl,
                                 void* tasks, hipStream_t st);
+// mutual near field of sibling groups: mut[leaf] = 1 where the group (the
+// leaf children of one parent) holds 1..256 particles, 0 elsewhere
+hipError_t launch_mutual_flags(const int32_t* parents, int64_t np, const int32_t* first_child,
+                               const uint8_t* n_child, const int32_t* count, uint8_t* mut,
+                               int64_t n_nodes, hipStream_t st);
+// far[k] += the flagged groups' own pair sums (both sides of every pair once)
+hipError_t launch_p2p_mutual(int dtype, int64_t np, const int32_t* parents,
+                             const int32_t* first_child, const uint8_t* n_child,
+                             const int32_t* begin, const int32_t* count, const void* pts,
+                             void* far, hipStream_t st);
+// mut / parent: null, or the flags above (entries of flagged groups' siblings
+// and of the leaf itself are skipped)
 hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
-                      const int32_t* begin, const int32_t* count, const int32_t* src,
+                      const int32_t* begin, const int32_t* count, const uint8_t* mut,
+                      const int32_t* parent, const int32_t* src,
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
                       void* part, const int32_t* split, int64_t n_split, hipEvent_t* ev, bool* ran,
                       hipStream_t st);

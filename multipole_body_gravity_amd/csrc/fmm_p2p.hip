@@ -201,10 +201,15 @@ struct P2PShared {
 // The tasks of one wave.  Per target, out1[perm] = far.x + sum0 and
 // out3[3 perm + a] = far.(y, z, m)[a] + sum(a + 1); a split leaf writes its
 // four sums per task into `part` instead.
+// mut (null: none): per leaf, 1 when its sibling group's near field (its own
+// leaf and its sibling leaves) is summed by the mutual kernel; those entries
+// are then skipped here (parent: the node parents, to recognise siblings).
 template <typename T, class Pair>
 __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int64_t n_tasks,
                                           const int32_t* __restrict__ begin,
                                           const int32_t* __restrict__ count,
+                                          const uint8_t* __restrict__ mut,
+                                          const int32_t* __restrict__ parent,
                                           const int32_t* __restrict__ src,
                                           const typename Pair::Rec* __restrict__ pts,
                                           const P4<T>* __restrict__ far,
@@ -233,6 +238,8 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
     const P2PTask task = tasks[ti];
     const int32_t a = task.leaf;
     const int32_t tb = begin[a], tn = count[a];
+    // sibling entries (the leaf itself included) summed by the mutual kernel
+    const int32_t skip_par = (mut && mut[a]) ? uniform(parent[a]) : -2;
     for (int32_t t0 = 0; t0 < tn; t0 += 2 * WAVE) {
       const int tc = min(2 * WAVE, tn - t0);
       const int G = (tc + 1) >> 1;
@@ -255,7 +262,9 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
         int32_t sb = 0, sc = 0;
         if (eg + lane < task.e1) {
           const int32_t b = src[eg + lane];
-          if (b == a) {
+          if (skip_par >= 0 && parent[b] == skip_par) {
+            // a sibling leaf or the leaf itself: in the mutual kernel's sums
+          } else if (b == a) {
             self = true;  // the target leaf itself: summed below with the self test
           } else {
             sb = begin[b];
@@ -370,14 +379,15 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
 template <typename T>
 __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_eu(5, 8)))
     k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
-          const int32_t* __restrict__ count, const int32_t* __restrict__ src,
+          const int32_t* __restrict__ count, const uint8_t* __restrict__ mut,
+          const int32_t* __restrict__ parent, const int32_t* __restrict__ src,
           const P4<T>* __restrict__ pts, const P4<T>* __restrict__ far,
           const int32_t* __restrict__ perm, T* __restrict__ phi, T* __restrict__ acc,
           T* __restrict__ part) {
   __shared__ P2PShared<T, P4<T>, ForcePair<T>::MAXQ> sh_all[P2P_WAVES];
   const int w = sizeof(T) == 8 ? uniform((int)(threadIdx.x / WAVE)) : (int)(threadIdx.x / WAVE);
-  p2p_tasks<T, ForcePair<T>>(tasks, n_tasks, begin, count, src, pts, far, perm, phi, acc, part,
-                             sh_all[w]);
+  p2p_tasks<T, ForcePair<T>>(tasks, n_tasks, begin, count, mut, parent, src, pts, far, perm, phi,
+                             acc, part, sh_all[w]);
 }
 
 // VJP near field: out1 = dS/dm, out3 = dS/dx, with `far` holding the far-field
@@ -391,8 +401,152 @@ __global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_e
               T* __restrict__ part) {
   __shared__ P2PShared<T, P8<T>, VjpPair<T>::MAXQ> sh_all[P2P_WAVES];
   const int w = sizeof(T) == 8 ? uniform((int)(threadIdx.x / WAVE)) : (int)(threadIdx.x / WAVE);
-  p2p_tasks<T, VjpPair<T>>(tasks, n_tasks, begin, count, src, recs, far, perm, mbar, xbar, part,
-                           sh_all[w]);
+  p2p_tasks<T, VjpPair<T>>(tasks, n_tasks, begin, count, nullptr, nullptr, src, recs, far, perm,
+                           mbar, xbar, part, sh_all[w]);
+}
+
+// ---- mutual near field of sibling groups ----
+// The leaf children of one parent are adjacent cells, so every pair of them
+// (and every leaf with itself) is a near-field pair in both directions: the
+// group's particles U interact all with all.  One wave per parent sums each
+// unordered particle pair of U once and adds it to both particles (the pair's
+// terms are equal and opposite in the acceleration, equal in the potential),
+// in a fixed order, into the far-field records (which L2P has written); the
+// directed kernel then skips these entries.  The group's records are staged in
+// LDS.  Rows i come in tiles of 16 (lane & 15), four columns j at a time
+// (lane >> 4), j > i only: the i-side terms stay in registers and are summed
+// over the four lanes of a row at the end of the tile, the j-side terms of one
+// column are summed over its 16 lanes by DPP moves inside the row; both go
+// into per-particle sums in LDS.  Groups of more than MUT_MAX particles are
+// left to the directed kernel.
+constexpr int MUT_MAX = 256;
+
+// sum over the 16 lanes of a row; every lane of the row gets it
+template <typename T>
+__device__ __forceinline__ T sum16(T x) {
+  x += dpp_move<DPP_QUAD_XOR1>(x);
+  x += dpp_move<DPP_QUAD_XOR2>(x);
+  x += dpp_move<DPP_ROW_HALF_MIRROR>(x);
+  x += dpp_move<DPP_ROW_MIRROR>(x);
+  return x;
+}
+
+// Build time: mut[c] = 1 for the leaf children c of parents whose leaf children
+// hold 1 .. MUT_MAX particles (a root leaf keeps the 0 it was cleared to).
+__global__ void k_mutual_flags(const int32_t* parents, int64_t np, const int32_t* first_child,
+                               const uint8_t* n_child, const int32_t* count, uint8_t* mut) {
+  bookkeeping_priority();
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= np) return;
+  const int32_t X = parents[i], fc = first_child[X];
+  const int nc = n_child[X];
+  int u = 0;
+  for (int c = 0; c < nc; c++)
+    if (n_child[fc + c] == 0) u += count[fc + c];
+  const uint8_t on = (u > 0 && u <= MUT_MAX) ? 1 : 0;
+  for (int c = 0; c < nc; c++)
+    if (n_child[fc + c] == 0) mut[fc + c] = on;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(P2P_THREADS)
+    k_p2p_mutual(int64_t np, const int32_t* __restrict__ parents,
+                 const int32_t* __restrict__ first_child, const uint8_t* __restrict__ n_child,
+                 const int32_t* __restrict__ begin, const int32_t* __restrict__ count,
+                 const P4<T>* __restrict__ pts, P4<T>* __restrict__ far) {
+  __shared__ P4<T> urec_all[P2P_WAVES][MUT_MAX];
+  __shared__ int32_t uidx_all[P2P_WAVES][MUT_MAX];
+  __shared__ T acc_all[P2P_WAVES][4][MUT_MAX];
+  __shared__ T red_all[P2P_WAVES][4][WAVE];
+  const int lane = __lane_id();
+  const int w = uniform((int)(threadIdx.x / WAVE));
+  P4<T>* urec = urec_all[w];
+  int32_t* uidx = uidx_all[w];
+  T(*acc)[MUT_MAX] = acc_all[w];
+  T(*red)[WAVE] = red_all[w];
+  for (int64_t pi = (int64_t)blockIdx.x * P2P_WAVES + w; pi < np;
+       pi += (int64_t)gridDim.x * P2P_WAVES) {
+    const int32_t X = uniform(parents[pi]);
+    const int nc = uniform((int)n_child[X]);
+    const int32_t fc = uniform(first_child[X]);
+    int lc = 0, lb = 0;
+    if (lane < nc && n_child[fc + lane] == 0) {
+      lc = count[fc + lane];
+      lb = begin[fc + lane];
+    }
+    const int incl = wave_incl_scan(lc);
+    const int u = uniform(read_lane(incl, WAVE - 1));
+    if (u == 0 || u > MUT_MAX) continue;
+    const int excl = incl - lc;
+    // U: the leaf children's particles in child order
+    for (int t = 0; t < nc; t++) {
+      const int s0 = uniform(read_lane(excl, t)), c0 = uniform(read_lane(lc, t)),
+                b0 = uniform(read_lane(lb, t));
+      for (int q = lane; q < c0; q += WAVE) {
+        urec[s0 + q] = pts[b0 + q];
+        uidx[s0 + q] = b0 + q;
+      }
+    }
+    for (int q = lane; q < u; q += WAVE) acc[0][q] = acc[1][q] = acc[2][q] = acc[3][q] = (T)0;
+    __builtin_amdgcn_wave_barrier();
+    const int ri = lane & 15, g = lane >> 4;
+    for (int r0 = 0; r0 < u; r0 += 16) {
+      const int i = r0 + ri;
+      const P4<T> pi_ = urec[i < u ? i : 0];
+      T s0 = 0, s1 = 0, s2 = 0, s3 = 0;  // i side
+      for (int j0 = r0; j0 < u; j0 += 4) {
+        const int j = j0 + g;
+        T v0 = 0, v1 = 0, v2 = 0, v3 = 0;  // j side
+        if (i < u && j < u && j > i) {
+          const P4<T> pj = urec[j];
+          const T dx = pi_.x - pj.x, dy = pi_.y - pj.y, dz = pi_.z - pj.z;
+          const T r2 = dx * dx + dy * dy + dz * dz;
+          const T rinv = p2p_rsqrt(r2);
+          const T rinv2 = rinv * rinv;
+          const T mjr = pj.m * rinv, mir = pi_.m * rinv;
+          const T mjr3 = mjr * rinv2, mir3 = mir * rinv2;
+          s0 -= mjr;
+          s1 -= mjr3 * dx;
+          s2 -= mjr3 * dy;
+          s3 -= mjr3 * dz;
+          v0 = -mir;
+          v1 = mir3 * dx;
+          v2 = mir3 * dy;
+          v3 = mir3 * dz;
+        }
+        v0 = sum16(v0);
+        v1 = sum16(v1);
+        v2 = sum16(v2);
+        v3 = sum16(v3);
+        if (ri == 0 && j < u) {
+          acc[0][j] += v0;
+          acc[1][j] += v1;
+          acc[2][j] += v2;
+          acc[3][j] += v3;
+        }
+      }
+      red[0][lane] = s0;
+      red[1][lane] = s1;
+      red[2][lane] = s2;
+      red[3][lane] = s3;
+      __builtin_amdgcn_wave_barrier();
+      if (lane < 16 && i < u) {
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+          acc[c][i] += ((red[c][lane] + red[c][lane + 16]) + red[c][lane + 32]) + red[c][lane + 48];
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    for (int q = lane; q < u; q += WAVE) {
+      P4<T> f = far[uidx[q]];
+      f.x += acc[0][q];
+      f.y += acc[1][q];
+      f.z += acc[2][q];
+      f.m += acc[3][q];
+      far[uidx[q]] = f;
+    }
+    __builtin_amdgcn_wave_barrier();  // the stage and sums are read before the next group
+  }
 }
 
 // Leaves split over several tasks, one block per leaf: thread (t, s) adds the
@@ -475,9 +629,36 @@ hipError_t launch_p2p_task_fill(const int32_t* leaves, int64_t n_leaves, int64_t
   return hipGetLastError();
 }
 
+hipError_t launch_mutual_flags(const int32_t* parents, int64_t np, const int32_t* first_child,
+                               const uint8_t* n_child, const int32_t* count, uint8_t* mut,
+                               int64_t n_nodes, hipStream_t st) {
+  hipError_t e = launch_fill_zero(mut, (size_t)n_nodes, st);
+  if (e != hipSuccess || np <= 0) return e;
+  k_mutual_flags<<<(unsigned)((np + 255) / 256), 256, 0, st>>>(parents, np, first_child, n_child,
+                                                               count, mut);
+  return hipGetLastError();
+}
+
+hipError_t launch_p2p_mutual(int dtype, int64_t np, const int32_t* parents,
+                             const int32_t* first_child, const uint8_t* n_child,
+                             const int32_t* begin, const int32_t* count, const void* pts,
+                             void* far, hipStream_t st) {
+  if (np <= 0) return hipSuccess;
+  int64_t blocks = (np + P2P_WAVES - 1) / P2P_WAVES;
+  if (blocks > 65535) blocks = 65535;
+  if (dtype == FMM_F64)
+    k_p2p_mutual<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
+        np, parents, first_child, n_child, begin, count, (const P4<double>*)pts, (P4<double>*)far);
+  else
+    k_p2p_mutual<float><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
+        np, parents, first_child, n_child, begin, count, (const P4<float>*)pts, (P4<float>*)far);
+  return hipGetLastError();
+}
+
 hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32_t* leaves,
                       int64_t n_leaves, const int64_t* task_off, const int64_t* part_off,
-                      const int32_t* begin, const int32_t* count, const int32_t* src,
+                      const int32_t* begin, const int32_t* count, const uint8_t* mut,
+                      const int32_t* parent, const int32_t* src,
                       const void* pts, const void* far, const int32_t* perm, void* phi, void* acc,
                       void* part, const int32_t* split, int64_t n_split, hipEvent_t* ev, bool* ran,
                       hipStream_t st) {
@@ -489,11 +670,11 @@ hipError_t launch_p2p(int dtype, const void* tasks, int64_t n_tasks, const int32
   if (ev) (void)hipEventRecord(ev[0], st);
   if (dtype == FMM_F64)
     k_p2p<double><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
-        (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<double>*)pts,
+        (const P2PTask*)tasks, n_tasks, begin, count, mut, parent, src, (const P4<double>*)pts,
         (const P4<double>*)far, perm, (double*)phi, (double*)acc, (double*)part);
   else
     k_p2p<float><<<(unsigned)blocks, P2P_THREADS, 0, st>>>(
-        (const P2PTask*)tasks, n_tasks, begin, count, src, (const P4<float>*)pts,
+        (const P2PTask*)tasks, n_tasks, begin, count, mut, parent, src, (const P4<float>*)pts,
         (const P4<float>*)far, perm, (float*)phi, (float*)acc, (float*)part);
   if (ev) {
     (void)hipEventRecord(ev[1], st);

@@ -63,6 +63,7 @@ def load_library():
     lib.fmm_strerror.restype = ctypes.c_char_p
     lib.fmm_set_timing.argtypes = [P, i32]
     lib.fmm_set_walk_pool_hint.argtypes = [P, i64]
+    lib.fmm_set_mutual_near_field.argtypes = [P, i32]
     lib.fmm_stats.argtypes = [P, ctypes.POINTER(_Stats)]
     lib.fmm_copy_keys.argtypes = [P, P, P]
     lib.fmm_copy_tree.argtypes = [P] * 8
@@ -183,6 +184,12 @@ class Plan:
                                             _stream_handle(stream))
         self._check(rc, "fmm_lattice_steps")
         return q, u
+
+    def set_mutual_near_field(self, enable: bool = True) -> None:
+        """Sum the sibling leaves' near field mutually (fmm_set_mutual_near_field);
+        takes effect at the next build."""
+        self._check(self.lib.fmm_set_mutual_near_field(self._h, 1 if enable else 0),
+                    "fmm_set_mutual_near_field")
 
     def set_walk_pool_hint(self, entries_per_node: int = -1) -> None:
         """Walk pool size at each build's start, entries per node (-1: automatic;

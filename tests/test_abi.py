@@ -28,7 +28,7 @@ def test_header_declares_entry_points():
                  "fmm_set_timing", "fmm_stats", "fmm_copy_keys", "fmm_copy_tree",
                  "fmm_copy_lists", "fmm_copy_expansions", "fmm_direct", "fmm_vjp", "fmm_lattice_steps",
                  "fmm_node_id_bits", "fmm_direct_noalloc", "fmm_set_walk_pool_hint",
-                 "fmm_measure_peaks"]:
+                 "fmm_measure_peaks", "fmm_set_mutual_near_field"]:
         assert want in names
 
 
@@ -80,6 +80,7 @@ def test_null_plan_calls(lib):
     assert lib.fmm_set_timing(None, 1) == -1
     lib.fmm_set_walk_pool_hint.argtypes = [P, ctypes.c_int64]
     assert lib.fmm_set_walk_pool_hint(None, 4) == -1
+    assert lib.fmm_set_mutual_near_field(None, 1) == -1
     assert lib.fmm_copy_keys(None, None, None) == -1
     assert lib.fmm_plan(None, 10, 4, 0.7, 32, 1) == -1
 

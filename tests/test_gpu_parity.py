@@ -28,12 +28,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_run(pos, mass, order, theta, leaf, dt, timing=False):
+def gpu_run(pos, mass, order, theta, leaf, dt, timing=False, mutual=None):
     torch = _torch()
     from multipole_body_gravity_amd import Plan
     tdt = torch.float64 if dt == "f64" else torch.float32
     dev = torch.device("cuda:0")
     plan = Plan(pos.shape[0], order=order, theta=theta, leaf_size=leaf, dtype=tdt, device=dev)
+    if mutual is not None:
+        plan.set_mutual_near_field(mutual)
     if timing:
         plan.set_timing(True)
     plan.build(torch.from_numpy(pos).to(dev, tdt), torch.from_numpy(mass).to(dev, tdt))
@@ -125,6 +127,37 @@ def test_parity_small(orc, dist, n, seed, order, theta, leaf, dt):
     check_structure(plan, ref)
     check_values(phi, acc, ref, dt, no_floor=(seed in (1001, 1002)))
     plan.close()
+
+
+MUTUAL_CASES = [
+    # dist, n, seed, order, theta, leaf, dtype
+    ("uniform", 4096, 1001, 4, 0.7, 32, "f64"),
+    ("clustered", 20000, 31, 4, 0.7, 32, "f32"),
+    ("plummer", 6000, 32, 6, 0.5, 16, "f64"),
+    ("uniform", 1037, 33, 3, 0.6, 7, "f64"),
+    ("plummer", 777, 34, 2, 0.4, 1, "f64"),
+    ("clustered", 5000, 35, 5, 0.55, 100, "f64"),  # groups over 256 particles stay directed
+    ("uniform", 300, 36, 4, 0.7, 1000, "f64"),      # the root is the only leaf
+]
+
+
+@pytest.mark.parametrize("dist,n,seed,order,theta,leaf,dt", MUTUAL_CASES)
+def test_mutual_near_field_parity(orc, dist, n, seed, order, theta, leaf, dt):
+    """The mutual near field of sibling groups (fmm_set_mutual_near_field):
+    the same lists and tree as the oracle, values to the same tolerance,
+    bitwise repeatable, and equal to the directed form to rounding."""
+    say(f"  mutual case {dist} n={n} p={order} theta={theta} leaf={leaf} {dt}")
+    pos, mass = inputs(dist, n, seed, dt)
+    plan, phi, acc = gpu_run(pos, mass, order, theta, leaf, dt, mutual=True)
+    ref = orc.fmm(pos, mass, order, theta, leaf)
+    check_structure(plan, ref)
+    check_values(phi, acc, ref, dt)
+    phi2, acc2 = (t.double().cpu().numpy() for t in plan.eval())
+    assert np.array_equal(phi, phi2) and np.array_equal(acc, acc2)
+    plan.close()
+    _, dphi, dacc = gpu_run(pos, mass, order, theta, leaf, dt, mutual=False)
+    ea, _ = rel_err(acc, dacc)
+    assert ea.max() <= TOL[dt]
 
 
 def test_two_body_and_single(orc):
