@@ -716,22 +716,32 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
 
   rec(p, FMM_STAGE_KEYS, 0, st);
   TRY_HIP(launch_fill_zero(ctrl, sizeof(Control), st));
-  const int nbb = bbox_blocks(n);
-  TRY_HIP(launch_bbox(pos, mass, n, p->dtype, P<double>(p->bbox_part), nbb, root, ctrl, st));
-  TRY_HIP(launch_keys(pos, n, p->dtype, root, P<uint64_t>(p->keys), P<int32_t>(p->idx), st));
-  rec(p, FMM_STAGE_KEYS, 1, st);
+  if (n <= FRONT_MAX) {
+    // small sets: box, keys, sort and gather in one launch (timed as the keys stage)
+    TRY_HIP(launch_front_small(pos, mass, n, p->dtype, P<uint64_t>(p->keys), P<int32_t>(p->idx),
+                               p->pts.p, root, ctrl, st));
+    rec(p, FMM_STAGE_KEYS, 1, st);
+    rec(p, FMM_STAGE_SORT, 0, st);
+    rec(p, FMM_STAGE_SORT, 1, st);
+  } else {
+    const int nbb = bbox_blocks(n);
+    TRY_HIP(launch_bbox(pos, mass, n, p->dtype, P<double>(p->bbox_part), nbb, root, ctrl, st));
+    TRY_HIP(launch_keys(pos, n, p->dtype, root, P<uint64_t>(p->keys), P<int32_t>(p->idx), st));
+    rec(p, FMM_STAGE_KEYS, 1, st);
 
-  rec(p, FMM_STAGE_SORT, 0, st);
-  bool sorted_alt = false;
-  TRY_HIP(launch_radix_sort(P<uint64_t>(p->keys), P<int32_t>(p->idx), P<uint64_t>(p->keys_alt),
-                            P<int32_t>(p->idx_alt), n, P<int32_t>(p->radix_hist),
-                            P<int32_t>(p->scan_tmp), &sorted_alt, st));
-  if (sorted_alt) {  // the sorted keys and permutation are the plan's from here on
-    std::swap(p->keys, p->keys_alt);
-    std::swap(p->idx, p->idx_alt);
+    rec(p, FMM_STAGE_SORT, 0, st);
+    bool sorted_alt = false;
+    TRY_HIP(launch_radix_sort(P<uint64_t>(p->keys), P<int32_t>(p->idx),
+                              P<uint64_t>(p->keys_alt), P<int32_t>(p->idx_alt), n,
+                              P<int32_t>(p->radix_hist), P<int32_t>(p->scan_tmp), &sorted_alt,
+                              st));
+    if (sorted_alt) {  // the sorted keys and permutation are the plan's from here on
+      std::swap(p->keys, p->keys_alt);
+      std::swap(p->idx, p->idx_alt);
+    }
+    TRY_HIP(launch_gather(pos, mass, P<int32_t>(p->idx), n, p->dtype, p->pts.p, st));
+    rec(p, FMM_STAGE_SORT, 1, st);
   }
-  TRY_HIP(launch_gather(pos, mass, P<int32_t>(p->idx), n, p->dtype, p->pts.p, st));
-  rec(p, FMM_STAGE_SORT, 1, st);
 
   rec(p, FMM_STAGE_TREE, 0, st);
   TRY_HIP(launch_tree_phase1(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),

@@ -271,6 +271,27 @@ hipError_t scan_exclusive_i32(const int32_t* in, int32_t* out, int64_t n, int32_
 // ===================================================================
 constexpr int BB_THREADS = 256;
 
+// The root cube of a box: anchored at its minimum corner, side the smallest
+// power of two >= the largest extent (1 if every extent is 0); scale = 2^21/side.
+__device__ RootInfo root_cube(const double (&lo)[3], const double (&hi)[3]) {
+  double ext = 0.0;
+  for (int a = 0; a < 3; a++) ext = fmax(ext, __dsub_rn(hi[a], lo[a]));
+  // smallest power of two >= ext (1 if ext == 0)
+  double side = 1.0;
+  if (ext > 0.0 && isfinite(ext)) {
+    int e;
+    double f = frexp(ext, &e);
+    side = (f == 0.5) ? ext : ldexp(1.0, e);
+  }
+  int e2;
+  frexp(side, &e2);
+  RootInfo r;
+  for (int a = 0; a < 3; a++) r.lo[a] = isfinite(lo[a]) ? lo[a] : 0.0;
+  r.side = side;
+  r.scale = ldexp(1.0, KEY_BITS - (e2 - 1));
+  return r;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(BB_THREADS)
     k_bbox_partial(const T* pos, const T* mass, int64_t n, double* part, Control* ctrl) {
@@ -332,22 +353,8 @@ __global__ void __launch_bounds__(BB_THREADS) k_bbox_final(const double* part, i
     __syncthreads();
   }
   if (threadIdx.x != 0) return;
-  double lo[3] = {s[0][0], s[1][0], s[2][0]}, hi[3] = {s[3][0], s[4][0], s[5][0]};
-  double ext = 0.0;
-  for (int a = 0; a < 3; a++) ext = fmax(ext, __dsub_rn(hi[a], lo[a]));
-  // smallest power of two >= ext (1 if ext == 0)
-  double side = 1.0;
-  if (ext > 0.0 && isfinite(ext)) {
-    int e;
-    double f = frexp(ext, &e);
-    side = (f == 0.5) ? ext : ldexp(1.0, e);
-  }
-  int e2;
-  frexp(side, &e2);
-  RootInfo r;
-  for (int a = 0; a < 3; a++) r.lo[a] = isfinite(lo[a]) ? lo[a] : 0.0;
-  r.side = side;
-  r.scale = ldexp(1.0, KEY_BITS - (e2 - 1));
+  const double lo[3] = {s[0][0], s[1][0], s[2][0]}, hi[3] = {s[3][0], s[4][0], s[5][0]};
+  const RootInfo r = root_cube(lo, hi);
   *root = r;
   ctrl->root = r;  // the host's copy comes with the control block
 }
@@ -367,22 +374,28 @@ hipError_t launch_bbox(const void* pos, const void* mass, int64_t n, int dtype, 
 // ===================================================================
 // Morton keys: u = floor((x - lo) * 2^21 / side) clamped, bits interleaved
 // ===================================================================
+// Morton key of particle i (positions in the dtype, widened exactly).
 template <typename T>
-__global__ void k_keys(const T* pos, int64_t n, const RootInfo* root, uint64_t* keys,
-                       int32_t* idx) {
-  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= n) return;
+__device__ __forceinline__ uint64_t morton_key(const T* pos, int64_t i, const RootInfo& root) {
   const double umax = (double)((1u << KEY_BITS) - 1u);
   uint32_t u[3];
 #pragma unroll
   for (int a = 0; a < 3; a++) {
     // one rounding in the subtraction; the scale is an exact power of two
-    double s = __dsub_rn((double)pos[3 * i + a], root->lo[a]);
-    double v = floor(__dmul_rn(s, root->scale));
+    double s = __dsub_rn((double)pos[3 * i + a], root.lo[a]);
+    double v = floor(__dmul_rn(s, root.scale));
     v = fmin(fmax(v, 0.0), umax);
     u[a] = (uint32_t)v;
   }
-  keys[i] = (spread3(u[0]) << 2) | (spread3(u[1]) << 1) | spread3(u[2]);
+  return (spread3(u[0]) << 2) | (spread3(u[1]) << 1) | spread3(u[2]);
+}
+
+template <typename T>
+__global__ void k_keys(const T* pos, int64_t n, const RootInfo* root, uint64_t* keys,
+                       int32_t* idx) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  keys[i] = morton_key(pos, i, *root);
   idx[i] = (int32_t)i;
 }
 
@@ -625,6 +638,174 @@ hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, i
   // 7 passes of 9 bits over the 63-bit keys: the result is in (keys_alt, idx_alt)
   return launch_radix_sort_bits(keys, idx, keys_alt, idx_alt, n, 0, 63, hist, scan_tmp, in_alt,
                                 st);
+}
+
+// ===================================================================
+// small sets: box, keys, sort and gather in one launch
+//
+// For N <= FRONT_MAX one block of 1024 threads does all of it: the box by a
+// block reduction (min / max are exact, so the order does not matter), the
+// keys as k_keys, then the same stable LSD sort (seven 9-bit digits) with the
+// keys held in LDS and the permutation ping-ponged there (16 bytes per
+// particle): wave w owns the w-th sixteenth of the current order, counts its digits
+// (ballots, as in the multi-block sort), the counts are scanned over waves and
+// digits, and the wave places its elements in order, so equal digits keep
+// their order.  Replaces the 33 dependent launches of the multi-block path,
+// which are what a small step costs.
+// ===================================================================
+constexpr int FRONT_THREADS = 1024;
+constexpr int FRONT_WAVES = FRONT_THREADS / WAVE;
+// 64-element batches of a wave's part, at most
+constexpr int FRONT_BATCH = ((FRONT_MAX + FRONT_WAVES - 1) / FRONT_WAVES + WAVE - 1) / WAVE;
+
+template <typename T>
+__global__ void __launch_bounds__(FRONT_THREADS)
+    k_front_small(const T* __restrict__ pos, const T* __restrict__ mass, int n,
+                  uint64_t* __restrict__ keys_sorted,
+                  int32_t* __restrict__ perm, P4<T>* __restrict__ pts, RootInfo* root,
+                  Control* ctrl) {
+  __shared__ uint64_t skey[FRONT_MAX];
+  __shared__ int32_t ping[2][FRONT_MAX];
+  __shared__ int wc[FRONT_WAVES][512];
+  __shared__ double bs[6][FRONT_WAVES];
+  __shared__ int wsum[8];
+  __shared__ RootInfo rs;
+  const int tid = threadIdx.x, w = tid / WAVE, lane = __lane_id();
+  // box and non-finite check
+  double lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+  int bad = 0;
+  for (int i = tid; i < n; i += FRONT_THREADS) {
+#pragma unroll
+    for (int a = 0; a < 3; a++) {
+      const double v = (double)pos[3 * i + a];
+      bad |= !isfinite(v);
+      lo[a] = fmin(lo[a], v);
+      hi[a] = fmax(hi[a], v);
+    }
+    bad |= !isfinite((double)mass[i]);
+  }
+#pragma unroll
+  for (int a = 0; a < 3; a++) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo[a] = fmin(lo[a], __shfl_xor(lo[a], o, WAVE));
+      hi[a] = fmax(hi[a], __shfl_xor(hi[a], o, WAVE));
+    }
+  }
+  if (lane == 0)
+    for (int a = 0; a < 3; a++) {
+      bs[a][w] = lo[a];
+      bs[3 + a][w] = hi[a];
+    }
+  if (__ballot(bad) != 0ull && lane == 0) atomicOr(&ctrl->nonfinite, 1);
+  __syncthreads();
+  if (tid == 0) {
+    double l[3], h[3];
+    for (int a = 0; a < 3; a++) {
+      l[a] = bs[a][0];
+      h[a] = bs[3 + a][0];
+      for (int q = 1; q < FRONT_WAVES; q++) {
+        l[a] = fmin(l[a], bs[a][q]);
+        h[a] = fmax(h[a], bs[3 + a][q]);
+      }
+    }
+    const RootInfo r = root_cube(l, h);
+    rs = r;
+    *root = r;
+    ctrl->root = r;
+  }
+  __syncthreads();
+  const RootInfo r = rs;
+  for (int i = tid; i < n; i += FRONT_THREADS) {
+    skey[i] = morton_key(pos, i, r);
+    ping[0][i] = i;
+  }
+  __syncthreads();
+  // wave w's sixteenth of the order, whole batches of 64
+  const int per = ((n + FRONT_WAVES - 1) / FRONT_WAVES + WAVE - 1) / WAVE * WAVE;
+  const int c0 = min(n, w * per), c1 = min(n, c0 + per);
+  const uint64_t lt = lanemask_lt();
+  for (int pass = 0; pass < 7; pass++) {
+    const int32_t* src = ping[pass & 1];
+    int32_t* dst = ping[(pass & 1) ^ 1];
+    const int shift = 9 * pass;
+    for (int d = lane; d < 512; d += WAVE) wc[w][d] = 0;
+    __builtin_amdgcn_wave_barrier();
+    // this lane's elements of the wave's part: index and digit (loaded first)
+    int32_t sv[FRONT_BATCH];
+    int dg[FRONT_BATCH];
+#pragma unroll
+    for (int b = 0; b < FRONT_BATCH; b++) {
+      const int i = c0 + b * WAVE + lane;
+      sv[b] = i < c1 ? src[i] : 0;
+      dg[b] = i < c1 ? (int)((skey[sv[b]] >> shift) & 511u) : -1;
+    }
+    // digit counts (integer LDS atomics: the order does not matter here)
+#pragma unroll
+    for (int b = 0; b < FRONT_BATCH; b++)
+      if (dg[b] >= 0) atomicAdd(&wc[w][dg[b]], 1);
+    __syncthreads();
+    int incl = 0, acc = 0;
+    if (tid < 512) {  // digit tid: start of each wave's part within the digit
+      for (int q = 0; q < FRONT_WAVES; q++) {
+        const int c = wc[q][tid];
+        wc[q][tid] = acc;
+        acc += c;
+      }
+      incl = wave_incl_scan(acc);  // waves 0..7: digits in order
+      if (lane == WAVE - 1) wsum[w] = incl;
+    }
+    __syncthreads();
+    if (tid < 512) {
+      int dstart = incl - acc;
+      for (int q = 0; q < w; q++) dstart += wsum[q];
+      for (int q = 0; q < FRONT_WAVES; q++) wc[q][tid] += dstart;
+    }
+    __syncthreads();
+    // each wave places its elements in order: ranks among equal digits from
+    // ballots, after the wave's running position for the digit
+#pragma unroll
+    for (int b = 0; b < FRONT_BATCH; b++) {
+      if (c0 + b * WAVE >= c1) break;  // wave-uniform
+      const int d = dg[b];
+      const uint64_t mask = same_digit<9>(d, d >= 0);
+      const int before = d >= 0 ? wc[w][d] : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (d >= 0) {
+        dst[before + __popcll(mask & lt)] = sv[b];
+        if ((mask & lt) == 0) wc[w][d] = before + __popcll(mask);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+  }
+  // seven passes: the order is in ping[1]
+  for (int k = tid; k < n; k += FRONT_THREADS) {
+    const int32_t i = ping[1][k];
+    perm[k] = i;
+    keys_sorted[k] = skey[i];
+    P4<T> q;
+    q.x = pos[3 * i];
+    q.y = pos[3 * i + 1];
+    q.z = pos[3 * i + 2];
+    q.m = mass[i];
+    pts[k] = q;
+  }
+}
+
+hipError_t launch_front_small(const void* pos, const void* mass, int64_t n, int dtype,
+                              uint64_t* keys_sorted, int32_t* perm, void* pts, RootInfo* root,
+                              Control* ctrl, hipStream_t st) {
+  if (n < 1 || n > FRONT_MAX) return hipErrorInvalidValue;
+  if (dtype == FMM_F64)
+    k_front_small<double><<<1, FRONT_THREADS, 0, st>>>((const double*)pos, (const double*)mass,
+                                                       (int)n, keys_sorted, perm,
+                                                       (P4<double>*)pts, root, ctrl);
+  else
+    k_front_small<float><<<1, FRONT_THREADS, 0, st>>>((const float*)pos, (const float*)mass,
+                                                      (int)n, keys_sorted, perm,
+                                                      (P4<float>*)pts, root, ctrl);
+  return hipGetLastError();
 }
 
 // ===================================================================

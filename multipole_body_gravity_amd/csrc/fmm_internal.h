@@ -180,6 +180,13 @@ hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, i
                              hipStream_t st);
 hipError_t launch_gather(const void* pos, const void* mass, const int32_t* perm, int64_t n,
                          int dtype, void* pts, hipStream_t st);
+// Box, keys, stable sort and gather of a set of at most FRONT_MAX particles in
+// one launch: the same root, sorted keys, permutation and records as
+// launch_bbox + launch_keys + launch_radix_sort + launch_gather.
+constexpr int FRONT_MAX = 8000;
+hipError_t launch_front_small(const void* pos, const void* mass, int64_t n, int dtype,
+                              uint64_t* keys_sorted, int32_t* perm, void* pts, RootInfo* root,
+                              Control* ctrl, hipStream_t st);
 size_t radix_hist_ints(int64_t n);
 size_t scan_tmp_bytes(int64_t n);
 
