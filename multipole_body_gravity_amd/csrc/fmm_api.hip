@@ -212,6 +212,7 @@ int issue_sibling_m2l(fmm_plan_t p, hipStream_t st, bool capped) {
   ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_SIB : nullptr;
   ma.ran = p->kran + FMM_KERNEL_M2L_SIB;
   ma.max_blocks = capped ? 2 * (int64_t)std::max(p->n_cu, 1) : 0;
+  ma.stop = P<Control>(p->ctrl);  // the walk may still be repeated
   rec(p, FMM_STAGE_M2L, 0, us);
   TRY_HIP(launch_m2l_sib(p->dtype, p->order, ma, us));
   rec(p, FMM_STAGE_M2L, 1, us);
@@ -301,10 +302,25 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   int64_t* toff = P<int64_t>(p->p2p_toff);
   int64_t* poff = P<int64_t>(p->p2p_poff);
 
+  // Room for the transposed keys and the near-field lists, kept from build to
+  // build (first guesses per node; exact after a repeat)
+  p->cap_tr = std::max<int64_t>(p->cap_tr, 48 * nn + 4096);
+  p->cap_p2p = std::max<int64_t>(p->cap_p2p, 128 * nn + 4096);
+
+  // The whole walk, its lists and its task counts are issued without a host
+  // check: a pool or list that runs out of room sets a flag, every later
+  // kernel that indexes the walk's results then does nothing, and the one
+  // synchronization at the end finds the flag, regrows from the counts and
+  // repeats.
   p->walk_retries = 0;
   for (;;) {
     for (int k = 0; k < N_POOLS; k++)
       TRY(grow(p->pool[k], (size_t)p->shard_cap[k] * POOL_SHARDS * 8));
+    TRY(grow(p->tr_keys, (size_t)p->cap_tr * 8));
+    TRY(grow(p->tr_keys_alt, (size_t)p->cap_tr * 8));
+    TRY(grow(p->radix_hist, 4 * radix_hist_ints(p->cap_tr)));
+    TRY(grow(p->scan_tmp, scan_tmp_bytes((int64_t)radix_hist_ints(p->cap_tr))));
+    TRY(grow(p->p2p_src, (size_t)p->cap_p2p * 4));
     Pool<uint64_t>* pools[N_POOLS] = {&a.cu, &a.u, &a.pu};
     for (int k = 0; k < N_POOLS; k++)
       *pools[k] = Pool<uint64_t>{P<uint64_t>(p->pool[k]), p->shard_cap[k], dctrl->pool_used[k]};
@@ -321,17 +337,92 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
       int64_t* dst[2] = {&dctrl->n_trm, &dctrl->n_trp};
       TRY_HIP(scan_exclusive_multi_i64(2, in, out, dst, np, p->scan_tmp.p, st));
     }
-    // the upward pass, once this attempt's walk launches are all queued (its
-    // host launch time then overlaps the walk instead of delaying it)
+    // the upward pass, once the first attempt's walk launches are all queued
+    // (its host launch time then overlaps the walk instead of delaying it)
     if (p->walk_retries == 0) TRY(issue_upward(p));
+
+    // launch order of the M2L sibling blocks; then the sibling M2L itself on
+    // the second stream, where it overlaps the rest of the walk.  A short one
+    // (under a millisecond, estimated from the last build's own entries)
+    // starts now on a capped grid, so that it runs beside the transposed sort
+    // and the rest of the walk (2 % off the 10^6 step); a long one waits for
+    // the transposed sort and takes the whole GPU (capped, it ran 12 % slower
+    // on the 4*10^7 sphere).
+    TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
+    TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, dctrl, P<int32_t>(p->m2l_order), st));
+    const bool sib_early = sibling_seconds(p, p->last_own_m2l) < 1e-3;
+    if (sib_early) TRY(issue_sibling_m2l(p, st, true));
+
+    // transposed entries: emitted in group order (ascending source for each
+    // target), then stably sorted on (kind, target); run lengths per target
+    int32_t* tr_cnt = P<int32_t>(p->tr_cnt_m2l);
+    int64_t* tr_start = P<int64_t>(p->tr_start_m2l);
+    a.tr_keys = P<uint64_t>(p->tr_keys);
+    a.tr_cap = p->cap_tr;
+    a.n_trm = &dctrl->n_trm;
+    a.pbeg = 0;
+    a.pcnt = np;
+    TRY_HIP(launch_tr_emit(a, tr_cnt, 2 * nn, st));  // also clears tr_cnt
+    bool in_alt = false;
+    TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), nullptr, P<uint64_t>(p->tr_keys_alt),
+                                   nullptr, p->cap_tr, a.key_shift, a.key_shift + 1,
+                                   P<int32_t>(p->radix_hist), P<int32_t>(p->scan_tmp), &in_alt,
+                                   st, &dctrl->n_tr, dctrl));
+    const uint64_t* sorted = in_alt ? P<uint64_t>(p->tr_keys_alt) : P<uint64_t>(p->tr_keys);
+    TRY_HIP(launch_tr_runs(sorted, p->cap_tr, &dctrl->n_tr, dctrl, a.key_shift, kind_bit, nn,
+                           tr_start, tr_cnt, st));
+    p->tr_sorted = sorted;
+    // a long sibling M2L beside the rest of the walk, after the transposed sort
+    // (beside that sort, on a full grid, the sort's kernels were starved)
+    if (!sib_early) TRY(issue_sibling_m2l(p, st, false));
+
+    // P2P lists: own entries (from the parents' P2P unions) then transposed ones
+    int64_t* p2p_off = P<int64_t>(p->p2p_off);
+    TRY_HIP(launch_walk_offsets(nn, a.own_p2p, tr_cnt + nn, P<int64_t>(p->tot_p2p), st));
+    {
+      const int64_t* in[1] = {P<int64_t>(p->tot_p2p)};
+      int64_t* out[1] = {p2p_off};
+      int64_t* dst[1] = {&dctrl->n_p2p};
+      TRY_HIP(scan_exclusive_multi_i64(1, in, out, dst, nn, p->scan_tmp.p, st));
+    }
+    int32_t* p2p_src = P<int32_t>(p->p2p_src);
+    TRY_HIP(launch_union_scatter(a.parents, np, a.first_child, a.n_child, a.pu.data, a.pu_off,
+                                 a.pu_cnt, p2p_off, p2p_src, p->cap_p2p, dctrl, st));
+    if (root_leaf) TRY_HIP(launch_walk_root_leaf(p2p_off, p2p_src, st));
+    TRY_HIP(launch_tr_scatter(sorted, p->cap_tr, &dctrl->n_tr, dctrl, a.key_shift, kind_bit, 1,
+                              nn, p2p_off, a.own_p2p, tr_start + nn, p2p_src, p->cap_p2p, st));
+
+    // near-field tasks, their partial slots and the transposed-tail M2L tasks,
+    // per leaf; offsets and totals (to the control block) in one scan
+    int64_t* ttoff = P<int64_t>(p->tail_toff);
+    TRY(grow(p->split_leaves, (size_t)std::max<int64_t>(nl, 1) * 4));
+    TRY_HIP(launch_leaf_task_counts(leaves, nl, p2p_off, P<int32_t>(p->ncount), tr_cnt, toff,
+                                    poff, ttoff, P<int32_t>(p->split_leaves), dctrl, st));
+    {
+      const int64_t* in[3] = {toff, poff, ttoff};
+      int64_t* out[3] = {toff, poff, ttoff};
+      int64_t* dst[3] = {&dctrl->n_p2p_tasks, &dctrl->n_p2p_part, &dctrl->n_tail_tasks};
+      TRY_HIP(scan_exclusive_multi_i64(3, in, out, dst, nl, p->scan_tmp.p, st));
+    }
     TRY(sync_ctrl(p, st));
-    if (!p->ctrl_host->pool_overflow) break;
-    // the levels after the first overflow did not run: grow at least twofold
+    const Control& c = *p->ctrl_host;
+    if (!c.pool_overflow && !c.list_overflow) break;
+    // repeat with more room: the second stream's kernels of this attempt
+    // (the sibling M2L reads the pools) end first
     if (++p->walk_retries > 12) return FMM_ERR_OOM;
-    for (int k = 0; k < N_POOLS; k++) {
-      int64_t mx = 0;
-      for (int sh = 0; sh < POOL_SHARDS; sh++) mx = std::max(mx, p->ctrl_host->pool_used[k][sh]);
-      if (mx > p->shard_cap[k]) p->shard_cap[k] = std::max(mx + mx / 2, 2 * p->shard_cap[k]);
+    TRY_HIP(hipStreamSynchronize(p->up_stream));
+    if (c.pool_overflow) {  // the levels after the first overflow did not run: grow at least twofold
+      for (int k = 0; k < N_POOLS; k++) {
+        int64_t mx = 0;
+        for (int sh = 0; sh < POOL_SHARDS; sh++) mx = std::max(mx, c.pool_used[k][sh]);
+        if (mx > p->shard_cap[k]) p->shard_cap[k] = std::max(mx + mx / 2, 2 * p->shard_cap[k]);
+      }
+    } else {  // the walk is complete: the exact sizes are known
+      int64_t own_p = c.own_p2p_total;
+      for (int sh = 0; sh < POOL_SHARDS; sh++) own_p += c.own_used[1][sh];
+      const int64_t ntr = c.n_trm + c.n_trp, np2p = own_p + c.n_trp;
+      if (ntr > p->cap_tr) p->cap_tr = ntr + ntr / 8;
+      if (np2p > p->cap_p2p) p->cap_p2p = np2p + np2p / 8;
     }
   }
   const Control& c = *p->ctrl_host;
@@ -342,97 +433,26 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     own_p += c.own_used[1][sh];
   }
   const int64_t ntm = c.n_trm, ntp = c.n_trp;
-  const int64_t ntr = ntm + ntp;
   p->n_union = nu;  // room reserved for the M2L unions (an upper bound)
   p->n_m2l = own_m + ntm;
   p->n_p2p = own_p + ntp;
-  p->n_tr = ntr;
+  p->n_tr = ntm + ntp;
+  p->last_own_m2l = own_m;
   p->m2l_lists_ready = false;
-
-  // launch order of the M2L sibling blocks; then the sibling M2L itself on the
-  // second stream, where it overlaps the rest of the walk
-  TRY(grow(p->m2l_order, (size_t)std::max<int64_t>(np, 1) * 4));
-  TRY_HIP(launch_m2l_order(a.parents, np, a.u_cnt, dctrl, P<int32_t>(p->m2l_order), st));
-  // A short sibling M2L (under a millisecond) starts now on a capped grid, so
-  // that it runs beside the transposed sort and the rest of the walk (2 % off
-  // the 10^6 step); a long one waits for the transposed sort and takes the
-  // whole GPU (capped, it ran 12 % slower on the 4*10^7 sphere).
-  const bool sib_early = sibling_seconds(p, own_m) < 1e-3;
-  if (sib_early) TRY(issue_sibling_m2l(p, st, true));
-
-  // transposed entries: emitted in group order (ascending source for each
-  // target), then stably sorted on (kind, target); run lengths per target
-  int32_t* tr_cnt = P<int32_t>(p->tr_cnt_m2l);
-  int64_t* tr_start = P<int64_t>(p->tr_start_m2l);
-  const uint64_t* sorted = nullptr;
-  if (ntr == 0) TRY_HIP(launch_fill_zero(tr_cnt, (size_t)2 * nn * 4, st));
-  if (ntr > 0) {
-    TRY(grow(p->tr_keys, (size_t)ntr * 8));
-    TRY(grow(p->tr_keys_alt, (size_t)ntr * 8));
-    TRY(grow(p->radix_hist, 4 * radix_hist_ints(ntr)));
-    TRY(grow(p->scan_tmp, scan_tmp_bytes((int64_t)radix_hist_ints(ntr))));
-    a.tr_keys = P<uint64_t>(p->tr_keys);
-    a.n_trm = &dctrl->n_trm;
-    a.pbeg = 0;
-    a.pcnt = np;
-    TRY_HIP(launch_tr_emit(a, tr_cnt, 2 * nn, st));  // also clears tr_cnt
-    bool in_alt = false;
-    TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), nullptr, P<uint64_t>(p->tr_keys_alt),
-                                   nullptr, ntr, a.key_shift, a.key_shift + 1,
-                                   P<int32_t>(p->radix_hist), P<int32_t>(p->scan_tmp), &in_alt,
-                                   st));
-    sorted = in_alt ? P<uint64_t>(p->tr_keys_alt) : P<uint64_t>(p->tr_keys);
-    TRY_HIP(launch_tr_runs(sorted, ntr, a.key_shift, kind_bit, nn, tr_start, tr_cnt, st));
-  }
-  p->tr_sorted = sorted;
-  // a long sibling M2L beside the rest of the walk, after the transposed sort
-  // (beside that sort, on a full grid, the sort's kernels were starved)
-  if (!sib_early) TRY(issue_sibling_m2l(p, st, false));
-
-  // P2P lists: own entries (from the parents' P2P unions) then transposed ones
-  int64_t* p2p_off = P<int64_t>(p->p2p_off);
-  TRY_HIP(launch_walk_offsets(nn, a.own_p2p, tr_cnt + nn, P<int64_t>(p->tot_p2p), st));
-  {
-    const int64_t* in[1] = {P<int64_t>(p->tot_p2p)};
-    int64_t* out[1] = {p2p_off};
-    int64_t* dst[1] = {&dctrl->n_p2p};
-    TRY_HIP(scan_exclusive_multi_i64(1, in, out, dst, nn, p->scan_tmp.p, st));
-  }
-  TRY(grow(p->p2p_src, (size_t)std::max<int64_t>(p->n_p2p, 1) * 4));
-  int32_t* p2p_src = P<int32_t>(p->p2p_src);
-  TRY_HIP(launch_union_scatter(a.parents, np, a.first_child, a.n_child, a.pu.data, a.pu_off,
-                               a.pu_cnt, p2p_off, p2p_src, st));
-  if (root_leaf) TRY_HIP(launch_walk_root_leaf(p2p_off, p2p_src, st));
-  if (ntr > 0)
-    TRY_HIP(launch_tr_scatter(sorted, ntr, a.key_shift, kind_bit, 1, nn, p2p_off, a.own_p2p,
-                              tr_start + nn, p2p_src, st));
-
-  // near-field tasks, their partial slots and the transposed-tail M2L tasks,
-  // per leaf; offsets and totals (to the control block) in one scan
-  int64_t* ttoff = P<int64_t>(p->tail_toff);
-  TRY(grow(p->split_leaves, (size_t)std::max<int64_t>(nl, 1) * 4));
-  TRY_HIP(launch_leaf_task_counts(leaves, nl, p2p_off, P<int32_t>(p->ncount), tr_cnt, toff, poff,
-                                  ttoff, P<int32_t>(p->split_leaves), dctrl, st));
-  {
-    const int64_t* in[3] = {toff, poff, ttoff};
-    int64_t* out[3] = {toff, poff, ttoff};
-    int64_t* dst[3] = {&dctrl->n_p2p_tasks, &dctrl->n_p2p_part, &dctrl->n_tail_tasks};
-    TRY_HIP(scan_exclusive_multi_i64(3, in, out, dst, nl, p->scan_tmp.p, st));
-  }
-  TRY(sync_ctrl(p, st));
-  if (p->ctrl_host->n_p2p != p->n_p2p) return FMM_ERR_HIP;
-  p->n_p2p_tasks = p->ctrl_host->n_p2p_tasks;
-  p->n_p2p_part = p->ctrl_host->n_p2p_part;
-  p->n_split = p->ctrl_host->n_split;
-  p->n_tail_tasks = p->ctrl_host->n_tail_tasks;
+  if (c.n_p2p != p->n_p2p || c.n_tr != p->n_tr) return FMM_ERR_HIP;
+  p->n_p2p_tasks = c.n_p2p_tasks;
+  p->n_p2p_part = c.n_p2p_part;
+  p->n_split = c.n_split;
+  p->n_tail_tasks = c.n_tail_tasks;
   TRY(grow(p->p2p_task, (size_t)std::max<int64_t>(p->n_p2p_tasks, 1) * p2p_task_bytes()));
   TRY(grow(p->p2p_part, (size_t)std::max<int64_t>(p->n_p2p_part, 1) * 4 * wbytes(p->dtype)));
-  TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, p2p_off,
+  TRY_HIP(launch_p2p_task_fill(leaves, nl, p->n_p2p_tasks, toff, poff, P<int64_t>(p->p2p_off),
                                P<int32_t>(p->ncount), dctrl, p->p2p_task.p, st));
   TRY(grow(p->tail_task, (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * sizeof(TailTask)));
   TRY(grow(p->tail_part,
            (size_t)std::max<int64_t>(p->n_tail_tasks, 1) * p->K * wbytes(p->dtype)));
-  TRY_HIP(launch_tail_fill(leaves, nl, tr_start, tr_cnt, ttoff, P<TailTask>(p->tail_task), st));
+  TRY_HIP(launch_tail_fill(leaves, nl, P<int64_t>(p->tr_start_m2l), P<int32_t>(p->tr_cnt_m2l),
+                           P<int64_t>(p->tail_toff), P<TailTask>(p->tail_task), st));
   p->mut_built = false;
   if (p->mutual) {
     TRY(grow(p->mut_flag, (size_t)nn));
@@ -458,10 +478,11 @@ int materialize_m2l_lists(fmm_plan_t p, hipStream_t st) {
   TRY_HIP(launch_union_scatter(P<int32_t>(p->parents), p->n_parents, P<int32_t>(p->nfirst),
                                P<uint8_t>(p->nnchild), P<uint64_t>(p->pool[POOL_U]),
                                P<int64_t>(p->u_off), P<int32_t>(p->u_cnt), off,
-                               P<int32_t>(p->m2l_src), st));
+                               P<int32_t>(p->m2l_src), p->n_m2l, nullptr, st));
   if (p->n_tr > 0)
-    TRY_HIP(launch_tr_scatter(p->tr_sorted, p->n_tr, p->key_shift, 2 * p->key_shift, 0, nn, off,
-                              own, P<int64_t>(p->tr_start_m2l), P<int32_t>(p->m2l_src), st));
+    TRY_HIP(launch_tr_scatter(p->tr_sorted, p->n_tr, nullptr, nullptr, p->key_shift,
+                              2 * p->key_shift, 0, nn, off, own, P<int64_t>(p->tr_start_m2l),
+                              P<int32_t>(p->m2l_src), p->n_m2l, st));
   TRY_HIP(hipStreamSynchronize(st));
   p->m2l_lists_ready = true;
   return FMM_OK;

@@ -444,8 +444,12 @@ __device__ __forceinline__ uint64_t same_digit(int d, bool valid) {
 template <int RB, int RS_ROUNDS>
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_hist(const uint64_t* keys, int64_t n, int shift, uint32_t dmask, int32_t* hist,
-                 int nblk) {
+                 int nblk, const int64_t* n_dev, const Control* stop) {
   bookkeeping_priority();
+  // keys present: n, or min(*n_dev, n), or none after a walk abort (the
+  // blocks past the end still write their empty histograms)
+  if (n_dev) n = min(*n_dev, n);
+  if (stop && walk_aborted(stop)) n = 0;
   constexpr int R = 1 << RB;
   constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
   __shared__ int h[R];
@@ -481,8 +485,11 @@ __global__ void __launch_bounds__(RS_THREADS)
 template <int RB, int RS_ROUNDS>
 __global__ void __launch_bounds__(RS_THREADS)
     k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
-                    int64_t n, int shift, uint32_t dmask, const int32_t* hist_scan, int nblk) {
+                    int64_t n, int shift, uint32_t dmask, const int32_t* hist_scan, int nblk,
+                    const int64_t* n_dev, const Control* stop) {
   bookkeeping_priority();
+  if (n_dev) n = min(*n_dev, n);
+  if (stop && walk_aborted(stop)) n = 0;
   constexpr int R = 1 << RB;
   constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
   constexpr int DPT = R / RS_THREADS;  // digits per thread in the digit scan (1 or 2)
@@ -584,7 +591,7 @@ __global__ void __launch_bounds__(RS_THREADS)
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
                                   int32_t* idx_alt, int64_t n, int lo_bit, int bits,
                                   int32_t* hist, int32_t* scan_tmp, bool* in_alt,
-                                  hipStream_t st) {
+                                  hipStream_t st, const int64_t* n_dev, const Control* stop) {
   *in_alt = false;
   if (n <= 0 || bits <= 0) return hipSuccess;
   const int64_t tile = rs_tile(n);
@@ -600,27 +607,31 @@ hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_a
     const uint32_t dmask = (1u << db) - 1u;
     const int64_t nh = ((int64_t)1 << rb) * nblk;
     if (rb == 9 && shortt)
-      k_radix_hist<9, 8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+      k_radix_hist<9, 8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk, n_dev,
+                                                              stop);
     else if (rb == 9)
-      k_radix_hist<9, 16><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+      k_radix_hist<9, 16><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk, n_dev,
+                                                              stop);
     else if (shortt)
-      k_radix_hist<8, 8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+      k_radix_hist<8, 8><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk, n_dev,
+                                                              stop);
     else
-      k_radix_hist<8, 16><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk);
+      k_radix_hist<8, 16><<<nblk, RS_THREADS, 0, st>>>(ka, n, shift, dmask, hist, nblk, n_dev,
+                                                              stop);
     hipError_t e = scan_excl<int32_t>(hist, hist, nh, nullptr, scan_tmp, st);
     if (e != hipSuccess) return e;
     if (rb == 9 && shortt)
       k_radix_scatter<9, 8><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
-                                                           nblk);
+                                                           nblk, n_dev, stop);
     else if (rb == 9)
       k_radix_scatter<9, 16><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
-                                                            nblk);
+                                                            nblk, n_dev, stop);
     else if (shortt)
       k_radix_scatter<8, 8><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
-                                                           nblk);
+                                                           nblk, n_dev, stop);
     else
       k_radix_scatter<8, 16><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, shift, dmask, hist,
-                                                            nblk);
+                                                            nblk, n_dev, stop);
     uint64_t* tk = ka;
     ka = kb;
     kb = tk;

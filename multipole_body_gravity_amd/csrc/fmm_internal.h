@@ -37,6 +37,11 @@ constexpr int ORDER_OCT = 64;
 // Device scalars written by kernels and read back at the build syncs.
 constexpr int POOL_SHARDS = 512;
 enum { POOL_CU = 0, POOL_U = 1, POOL_PU = 2, N_POOLS = 3 };
+struct Control;
+// The walk's bookkeeping runs without a host check in between: after a pool
+// or list overflow every kernel that indexes the walk's results does nothing,
+// and the host repeats the walk with larger buffers.
+__host__ __device__ inline bool walk_aborted(const Control* c);
 struct Control {
   RootInfo root;  // the root cell, for the host
   int32_t nonfinite;
@@ -54,7 +59,8 @@ struct Control {
   int64_t n_p2p_tasks, n_p2p_part;        // near-field tasks and partial-sum slots
   int64_t n_tail_tasks;                   // transposed-tail M2L tasks
   int32_t pool_overflow;                  // a sharded pool ran out of room
-  int32_t max_leaf_count;
+  int32_t list_overflow;                  // the transposed keys or the P2P lists ran out of room
+  int64_t n_tr;                           // walk: n_trm + n_trp (the transposed keys)
   int64_t pool_used[N_POOLS][POOL_SHARDS];  // per pool and shard: entries handed out
   int64_t own_used[2][POOL_SHARDS];          // per shard: own M2L / P2P entries found
   // launch orders (work octaves, heaviest first) of the near-field tasks and
@@ -64,6 +70,9 @@ struct Control {
   int32_t n_split;  // leaves whose near field is split over several tasks
   int32_t pad1;
 };
+__host__ __device__ inline bool walk_aborted(const Control* c) {
+  return (c->pool_overflow | c->list_overflow) != 0;
+}
 // Grow-only device buffer.
 struct DBuf {
   void* p = nullptr;
@@ -138,6 +147,8 @@ struct fmm_plan_s {
   mbg::RootInfo root_host{};
 
   int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0};  // entries per shard, per pool
+  int64_t cap_tr = 0, cap_p2p = 0;  // room for transposed keys / near-field list entries
+  int64_t last_own_m2l = 0;         // own M2L entries of the last build (sibling M2L issue)
   int64_t pool_hint = -1;  // walk pool entries per node at each build; -1: automatic
 
   mbg::Control* ctrl_host = nullptr;  // pinned
@@ -248,6 +259,7 @@ struct WalkArgs {
   int64_t *trm_cnt, *trp_cnt;  // per parent index: transposed entries it emits
   const int64_t *trm_base, *trp_base;  // their exclusive scans (emission pass)
   uint64_t* tr_keys;           // transposed keys, M2L then P2P (emission pass)
+  int64_t tr_cap;              // room in tr_keys (more keys: list_overflow)
   const int64_t* n_trm;        // device total of the M2L ones
   const uint64_t* rootgen;     // the root's generator: one entry, the root itself
   int key_shift;
@@ -262,19 +274,25 @@ hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, in
                              int32_t* own_p2p, hipStream_t st);
 hipError_t launch_walk_root_leaf(const int64_t* p2p_off, int32_t* p2p_src, hipStream_t st);
 
-hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
-                          int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st);
+// n: room in keys; the keys present are min(*n_dev, n) (nothing after a walk abort)
+hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, const int64_t* n_dev,
+                          const Control* ctrl, int key_shift, int kind_bit, int64_t n_nodes,
+                          int64_t* start, int32_t* cnt, hipStream_t st);
 hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_t* tr_cnt,
                                int64_t* tot, hipStream_t st);
 // sorted transposed keys of one kind -> after each target's own entries
-hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
-                             int kind, int64_t n_nodes, const int64_t* off, const int32_t* own,
-                             const int64_t* start, int32_t* src, hipStream_t st);
+// (keys as launch_tr_runs; src has room for cap entries, more: list_overflow)
+hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, const int64_t* n_dev,
+                             Control* ctrl, int key_shift, int kind_bit, int kind,
+                             int64_t n_nodes, const int64_t* off, const int32_t* own,
+                             const int64_t* start, int32_t* src, int64_t cap, hipStream_t st);
 // per-target own entries from the unions of their parents (root-leaf case included)
+// (ctrl: null, or stop after a walk abort; src has room for cap entries)
 hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
                                 const int32_t* first_child, const uint8_t* n_child,
                                 const uint64_t* pool, const int64_t* uoff, const int32_t* ucnt,
-                                const int64_t* off, int32_t* src, hipStream_t st);
+                                const int64_t* off, int32_t* src, int64_t cap, Control* ctrl,
+                                hipStream_t st);
 
 
 // LSD radix sort over the low `bits` bits; returns in *in_alt whether the
@@ -284,7 +302,10 @@ hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
                                   int32_t* idx_alt, int64_t n, int lo_bit, int bits,
                                   int32_t* hist, int32_t* scan_tmp, bool* in_alt,
-                                  hipStream_t st);
+                                  hipStream_t st, const int64_t* n_dev = nullptr,
+                                  const Control* stop = nullptr);
+// (n_dev: sort min(*n_dev, n) keys, n being the room in the buffers; stop:
+// sort nothing after a walk abort)
 
 // ---- numeric passes ----
 hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leaves,
@@ -323,6 +344,7 @@ struct M2LArgs {
   const void* mrec;       // source records (folded moments + centre)
   void* part;             // task partials (n_tasks x K)
   void* local;
+  const Control* stop;    // null, or: the sibling kernel does nothing after a pool overflow
   hipEvent_t* ev;         // null, or begin/end events of the sibling and tail kernels
   bool* ran;              // with ev: set when the kernel was launched
   int64_t max_blocks;     // > 0: grid cap of the sibling kernel (its waves loop over parents)

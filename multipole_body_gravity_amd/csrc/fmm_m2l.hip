@@ -174,7 +174,10 @@ __global__ void __launch_bounds__(M2L_THREADS) __attribute__((amdgpu_waves_per_e
               const int32_t* __restrict__ first_child, const uint8_t* __restrict__ n_child,
               const uint64_t* __restrict__ upool, const int64_t* __restrict__ u_off,
               const int32_t* __restrict__ u_cnt, const double* __restrict__ centre,
-              const unsigned char* __restrict__ mrec, T* __restrict__ local) {
+              const unsigned char* __restrict__ mrec, T* __restrict__ local,
+              const Control* __restrict__ stop) {
+  // after a pool overflow the unions are incomplete: the walk is repeated
+  if (stop && stop->pool_overflow) return;
   using C = SibCfg<T, P>;
   constexpr int K = Tabs<P>::K, KR = C::KR;
   constexpr int WPB = M2L_THREADS / WAVE;
@@ -486,7 +489,7 @@ static void m2l_sib_dispatch(int order, hipStream_t st, const M2LArgs& a) {
   case P:                                                                                    \
     k_m2l_sib<T, P><<<gs, M2L_THREADS, 0, st>>>(a.n_parents, a.parents, a.first_child,        \
                                                 a.n_child, a.upool, a.u_off, a.u_cnt,        \
-                                                a.centre, rec, (T*)a.local);                 \
+                                                a.centre, rec, (T*)a.local, a.stop);         \
     break;
     M2L_SIB(0) M2L_SIB(1) M2L_SIB(2) M2L_SIB(3) M2L_SIB(4)
     M2L_SIB(5) M2L_SIB(6) M2L_SIB(7) M2L_SIB(8) M2L_SIB(9) M2L_SIB(10)

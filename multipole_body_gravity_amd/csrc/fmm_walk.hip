@@ -313,9 +313,16 @@ __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a, int32_t* run
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < run_n;
        i += (int64_t)gridDim.x * blockDim.x)
     run_cnt[i] = 0;
+  if (a.ctrl->pool_overflow) return;  // the unions are incomplete
   const uint64_t lt = lanemask_lt();
   const int lane = __lane_id();
   const int64_t ntm_all = *a.n_trm;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const int64_t ntr = ntm_all + a.ctrl->n_trp;
+    a.ctrl->n_tr = ntr;
+    if (ntr > a.tr_cap) a.ctrl->list_overflow = 1;
+  }
+  if (ntm_all + a.ctrl->n_trp > a.tr_cap) return;  // no room: repeated with more
   for (int64_t pi = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; pi < a.pcnt;
        pi += (int64_t)gridDim.x * WK_WAVES) {
     if (uniform(a.trm_cnt[pi]) + uniform(a.trp_cnt[pi]) == 0) continue;
@@ -351,6 +358,11 @@ __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a, int32_t* run
 // totals start with the root's (itself as its only P2P entry when it is a leaf).
 __global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf, int32_t* own_m2l,
                              int32_t* own_p2p) {
+  if (threadIdx.x == 0) {  // (also when the walk is repeated within one build)
+    c->list_overflow = 0;
+    c->n_tr = 0;
+    c->n_split = 0;
+  }
   for (int i = threadIdx.x; i < N_POOLS * POOL_SHARDS; i += blockDim.x)
     (&c->pool_used[0][0])[i] = 0;
   for (int i = threadIdx.x; i < 2 * POOL_SHARDS; i += blockDim.x) (&c->own_used[0][0])[i] = 0;
@@ -372,9 +384,12 @@ __global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf, int32
 // block partial sums are added with integer atomics (order-independent).
 
 // Runs of equal (kind, target) in the sorted keys: first index and end index.
-__global__ void k_tr_runs(const uint64_t* keys, int64_t n, int sh, int kind_bit, int64_t n_nodes,
+__global__ void k_tr_runs(const uint64_t* keys, int64_t cap, const int64_t* n_dev,
+                          const Control* ctrl, int sh, int kind_bit, int64_t n_nodes,
                           int64_t* start, int32_t* cnt) {
   bookkeeping_priority();
+  if (walk_aborted(ctrl)) return;
+  const int64_t n = min(*n_dev, cap);
   int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (k >= n) return;
   const uint64_t g = keys[k] >> sh;  // kind and target
@@ -402,16 +417,23 @@ __global__ void k_walk_offsets(int64_t n, const int32_t* own, const int32_t* tr_
 
 
 // Sorted transposed keys of one kind -> after each target's own entries.
-__global__ void k_tr_scatter(const uint64_t* keys, int64_t n, int sh, int kind_bit, int kind,
-                             int64_t n_nodes, const int64_t* off, const int32_t* own,
-                             const int64_t* start, int32_t* src) {
+__global__ void k_tr_scatter(const uint64_t* keys, int64_t kcap, const int64_t* n_dev,
+                             Control* ctrl, int sh, int kind_bit, int kind, int64_t n_nodes,
+                             const int64_t* off, const int32_t* own, const int64_t* start,
+                             int32_t* src, int64_t cap) {
   bookkeeping_priority();
+  if (ctrl && walk_aborted(ctrl)) return;
+  const int64_t n = n_dev ? min(*n_dev, kcap) : kcap;
   int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (k >= n) return;
   const uint64_t key = keys[k];
   if ((int)(key >> kind_bit) != kind) return;
   const int64_t c = (int64_t)((key >> sh) & ((1ull << (kind_bit - sh)) - 1ull));
-  src[off[c] + own[c] + (k - start[c])] = (int32_t)(key & ((1ull << sh) - 1ull));
+  const int64_t o = off[c] + own[c] + (k - start[c]);
+  if (o < cap)
+    src[o] = (int32_t)(key & ((1ull << sh) - 1ull));
+  else if (ctrl)
+    ctrl->list_overflow = 1;
 }
 
 // One wave per parent X: child t's own entries are the entries of X's union
@@ -419,8 +441,10 @@ __global__ void k_tr_scatter(const uint64_t* keys, int64_t n, int sh, int kind_b
 __global__ void __launch_bounds__(WK_THREADS)
     k_union_scatter(const int32_t* parents, int64_t n_parents, const int32_t* first_child,
                     const uint8_t* n_child, const uint64_t* pool, const int64_t* uoff,
-                    const int32_t* ucnt, const int64_t* off, int32_t* src) {
+                    const int32_t* ucnt, const int64_t* off, int32_t* src, int64_t cap,
+                    Control* ctrl) {
   bookkeeping_priority();
+  if (ctrl && walk_aborted(ctrl)) return;
   const uint64_t lt = lanemask_lt();
   const int lane = __lane_id();
   for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < n_parents;
@@ -441,7 +465,13 @@ __global__ void __launch_bounds__(WK_THREADS)
       for (int t = 0; t < 8; t++) {
         const bool has = (v >> t) & 1u;
         const uint64_t b = __ballot(has);
-        if (has) src[base[t] + __popcll(b & lt)] = id;
+        if (has) {
+          const int64_t o = base[t] + __popcll(b & lt);
+          if (o < cap)
+            src[o] = id;
+          else if (ctrl)
+            ctrl->list_overflow = 1;
+        }
         base[t] += __popcll(b);
       }
     }
@@ -465,11 +495,12 @@ hipError_t launch_walk_reset(Control* ctrl, uint64_t* rootgen, int root_leaf, in
   k_walk_reset<<<1, 256, 0, st>>>(ctrl, rootgen, root_leaf, own_m2l, own_p2p);
   return hipGetLastError();
 }
-hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
-                          int64_t n_nodes, int64_t* start, int32_t* cnt, hipStream_t st) {
+hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, const int64_t* n_dev,
+                          const Control* ctrl, int key_shift, int kind_bit, int64_t n_nodes,
+                          int64_t* start, int32_t* cnt, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  k_tr_runs<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, key_shift, kind_bit, n_nodes,
-                                                         start, cnt);
+  k_tr_runs<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, n_dev, ctrl, key_shift,
+                                                         kind_bit, n_nodes, start, cnt);
   k_tr_lengths<<<(unsigned)((2 * n_nodes + 255) / 256), 256, 0, st>>>(2 * n_nodes, start, cnt);
   return hipGetLastError();
 }
@@ -479,23 +510,26 @@ hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_
   k_walk_offsets<<<(unsigned)((n_nodes + 255) / 256), 256, 0, st>>>(n_nodes, own, tr_cnt, tot);
   return hipGetLastError();
 }
-hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, int key_shift, int kind_bit,
-                             int kind, int64_t n_nodes, const int64_t* off, const int32_t* own,
-                             const int64_t* start, int32_t* src, hipStream_t st) {
+hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, const int64_t* n_dev,
+                             Control* ctrl, int key_shift, int kind_bit, int kind,
+                             int64_t n_nodes, const int64_t* off, const int32_t* own,
+                             const int64_t* start, int32_t* src, int64_t cap, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  k_tr_scatter<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, key_shift, kind_bit, kind,
-                                                            n_nodes, off, own, start, src);
+  k_tr_scatter<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(keys, n, n_dev, ctrl, key_shift,
+                                                            kind_bit, kind, n_nodes, off, own,
+                                                            start, src, cap);
   return hipGetLastError();
 }
 hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
                                 const int32_t* first_child, const uint8_t* n_child,
                                 const uint64_t* pool, const int64_t* uoff, const int32_t* ucnt,
-                                const int64_t* off, int32_t* src, hipStream_t st) {
+                                const int64_t* off, int32_t* src, int64_t cap, Control* ctrl,
+                                hipStream_t st) {
   if (n_parents <= 0) return hipSuccess;
   int64_t blocks = (n_parents + WK_WAVES - 1) / WK_WAVES;
   if (blocks > 16384) blocks = 16384;
-  k_union_scatter<<<(unsigned)blocks, WK_THREADS, 0, st>>>(parents, n_parents, first_child,
-                                                           n_child, pool, uoff, ucnt, off, src);
+  k_union_scatter<<<(unsigned)blocks, WK_THREADS, 0, st>>>(
+      parents, n_parents, first_child, n_child, pool, uoff, ucnt, off, src, cap, ctrl);
   return hipGetLastError();
 }
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {
