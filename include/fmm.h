@@ -109,6 +109,9 @@ typedef struct {
   int32_t timed_builds;  /* builds, evals and VJPs the means are taken over */
   int32_t timed_evals;
   int32_t timed_vjps;
+  int32_t walk_one_block; /* 1: the last walk sorted its transposed keys (and formed the
+                           * near-field list offsets) in the one-block path, taken when the
+                           * plan's previous walk had few of them; 0: multi-block path */
 } fmm_stats_t;
 
 /* Create a plan for N particles.  N in [1, 2^31), order in [0, FMM_MAX_ORDER],
@@ -125,8 +128,9 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
  * this call.  The multipoles need the tree only and the own-entry M2L the
  * walk's unions only: both run on a second stream owned by the plan, which
  * starts after the tree and overlaps the walk; the next fmm_eval or fmm_build
- * on any stream waits for it.  Synchronizes `stream` three times (tree size,
- * list sizes twice).  Returns FMM_ERR_NONFINITE (and leaves the plan un-built)
+ * on any stream waits for it.  Synchronizes `stream` twice (tree size, list
+ * sizes), once more per walk repeat when the list pools have to grow (see
+ * fmm_set_walk_pool_hint).  Returns FMM_ERR_NONFINITE (and leaves the plan un-built)
  * if any input is NaN/Inf, FMM_ERR_OOM if the octree of these positions would
  * need more than FMM_MAX_NODES cells.
  *

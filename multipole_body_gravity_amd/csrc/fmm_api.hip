@@ -363,23 +363,35 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     a.pbeg = 0;
     a.pcnt = np;
     TRY_HIP(launch_tr_emit(a, tr_cnt, 2 * nn, st));  // also clears tr_cnt
-    bool in_alt = false;
-    TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), nullptr, P<uint64_t>(p->tr_keys_alt),
-                                   nullptr, p->cap_tr, a.key_shift, a.key_shift + 1,
-                                   P<int32_t>(p->radix_hist), P<int32_t>(p->scan_tmp), &in_alt,
-                                   st, &dctrl->n_tr, dctrl));
-    const uint64_t* sorted = in_alt ? P<uint64_t>(p->tr_keys_alt) : P<uint64_t>(p->tr_keys);
-    TRY_HIP(launch_tr_runs(sorted, p->cap_tr, &dctrl->n_tr, dctrl, a.key_shift, kind_bit, nn,
-                           tr_start, tr_cnt, st));
+    int64_t* p2p_off = P<int64_t>(p->p2p_off);
+    const uint64_t* sorted = nullptr;
+    // few transposed keys (as many as the last walk had, when that fitted
+    // comfortably): sort, runs and the near-field offsets in one launch
+    const bool tr_small = p->tr_small_ok && a.key_shift <= 17 && nn <= TRS_MAX_NODES;
+    p->walk_one_block = tr_small;
+    if (tr_small) {
+      TRY_HIP(launch_tr_small(P<uint64_t>(p->tr_keys), p->cap_tr, dctrl, a.key_shift, nn,
+                              P<uint64_t>(p->tr_keys_alt), tr_start, tr_cnt, a.own_p2p,
+                              P<int64_t>(p->tot_p2p), p2p_off, st));
+      sorted = P<uint64_t>(p->tr_keys_alt);
+    } else {
+      bool in_alt = false;
+      TRY_HIP(launch_radix_sort_bits(P<uint64_t>(p->tr_keys), nullptr,
+                                     P<uint64_t>(p->tr_keys_alt), nullptr, p->cap_tr,
+                                     a.key_shift, a.key_shift + 1, P<int32_t>(p->radix_hist),
+                                     P<int32_t>(p->scan_tmp), &in_alt, st, &dctrl->n_tr, dctrl));
+      sorted = in_alt ? P<uint64_t>(p->tr_keys_alt) : P<uint64_t>(p->tr_keys);
+      TRY_HIP(launch_tr_runs(sorted, p->cap_tr, &dctrl->n_tr, dctrl, a.key_shift, kind_bit, nn,
+                             tr_start, tr_cnt, st));
+    }
     p->tr_sorted = sorted;
     // a long sibling M2L beside the rest of the walk, after the transposed sort
     // (beside that sort, on a full grid, the sort's kernels were starved)
     if (!sib_early) TRY(issue_sibling_m2l(p, st, false));
 
     // P2P lists: own entries (from the parents' P2P unions) then transposed ones
-    int64_t* p2p_off = P<int64_t>(p->p2p_off);
-    TRY_HIP(launch_walk_offsets(nn, a.own_p2p, tr_cnt + nn, P<int64_t>(p->tot_p2p), st));
-    {
+    if (!tr_small) {
+      TRY_HIP(launch_walk_offsets(nn, a.own_p2p, tr_cnt + nn, P<int64_t>(p->tot_p2p), st));
       const int64_t* in[1] = {P<int64_t>(p->tot_p2p)};
       int64_t* out[1] = {p2p_off};
       int64_t* dst[1] = {&dctrl->n_p2p};
@@ -411,6 +423,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
     // (the sibling M2L reads the pools) end first
     if (++p->walk_retries > 12) return FMM_ERR_OOM;
     TRY_HIP(hipStreamSynchronize(p->up_stream));
+    if (c.tr_small_over) p->tr_small_ok = false;  // the multi-block path from here on
     if (c.pool_overflow) {  // the levels after the first overflow did not run: grow at least twofold
       for (int k = 0; k < N_POOLS; k++) {
         int64_t mx = 0;
@@ -437,6 +450,7 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   p->n_m2l = own_m + ntm;
   p->n_p2p = own_p + ntp;
   p->n_tr = ntm + ntp;
+  p->tr_small_ok = p->n_tr <= 3 * TRS_MAX / 4;  // for the next build
   p->last_own_m2l = own_m;
   p->m2l_lists_ready = false;
   if (c.n_p2p != p->n_p2p || c.n_tr != p->n_tr) return FMM_ERR_HIP;
@@ -994,6 +1008,7 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
   out->dtype = p->dtype;
   out->theta = p->theta;
   out->walk_retries = p->walk_retries;
+  out->walk_one_block = p->walk_one_block ? 1 : 0;
   if (p->built) {
     out->n_nodes = p->n_nodes;
     out->n_leaves = p->n_leaves;

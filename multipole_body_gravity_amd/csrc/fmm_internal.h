@@ -68,7 +68,7 @@ struct Control {
   int32_t task_oct[ORDER_OCT], task_cur[ORDER_OCT];
   int32_t group_oct[ORDER_OCT], group_cur[ORDER_OCT];
   int32_t n_split;  // leaves whose near field is split over several tasks
-  int32_t pad1;
+  int32_t tr_small_over;  // the one-block transposed-key path had too many keys
 };
 __host__ __device__ inline bool walk_aborted(const Control* c) {
   return (c->pool_overflow | c->list_overflow) != 0;
@@ -149,6 +149,8 @@ struct fmm_plan_s {
   int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0};  // entries per shard, per pool
   int64_t cap_tr = 0, cap_p2p = 0;  // room for transposed keys / near-field list entries
   int64_t last_own_m2l = 0;         // own M2L entries of the last build (sibling M2L issue)
+  bool tr_small_ok = false;  // the last walk's transposed keys fit the one-block path
+  bool walk_one_block = false;  // the last walk attempt took it
   int64_t pool_hint = -1;  // walk pool entries per node at each build; -1: automatic
 
   mbg::Control* ctrl_host = nullptr;  // pinned
@@ -280,6 +282,16 @@ hipError_t launch_tr_runs(const uint64_t* keys, int64_t n, const int64_t* n_dev,
                           int64_t* start, int32_t* cnt, hipStream_t st);
 hipError_t launch_walk_offsets(int64_t n_nodes, const int32_t* own, const int32_t* tr_cnt,
                                int64_t* tot, hipStream_t st);
+// At most TRS_MAX transposed keys and TRS_MAX_NODES nodes (key_shift <= 17):
+// the transposed sort, runs, run lengths, near-field list sizes and offsets
+// (launch_radix_sort_bits + launch_tr_runs + launch_walk_offsets + the
+// offsets scan) in one launch; keys_out gets the sorted keys.  More keys:
+// list_overflow and tr_small_over are set.
+constexpr int TRS_MAX = 8192;
+constexpr int64_t TRS_MAX_NODES = 65536;
+hipError_t launch_tr_small(const uint64_t* keys_in, int64_t cap, Control* ctrl, int key_shift,
+                           int64_t n_nodes, uint64_t* keys_out, int64_t* start, int32_t* cnt,
+                           const int32_t* own, int64_t* tot, int64_t* p2p_off, hipStream_t st);
 // sorted transposed keys of one kind -> after each target's own entries
 // (keys as launch_tr_runs; src has room for cap entries, more: list_overflow)
 hipError_t launch_tr_scatter(const uint64_t* keys, int64_t n, const int64_t* n_dev,

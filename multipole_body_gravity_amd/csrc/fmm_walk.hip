@@ -362,6 +362,7 @@ __global__ void k_walk_reset(Control* c, uint64_t* rootgen, int root_leaf, int32
     c->list_overflow = 0;
     c->n_tr = 0;
     c->n_split = 0;
+    c->tr_small_over = 0;
   }
   for (int i = threadIdx.x; i < N_POOLS * POOL_SHARDS; i += blockDim.x)
     (&c->pool_used[0][0])[i] = 0;
@@ -415,6 +416,167 @@ __global__ void k_walk_offsets(int64_t n, const int32_t* own, const int32_t* tr_
   tot[i] = (int64_t)own[i] + tr_cnt[i];
 }
 
+
+// Few transposed keys (at most TRS_MAX, nodes at most TRS_MAX_NODES): one
+// block of 1024 threads does what the multi-block path does in twelve
+// dependent launches.  The keys are stably sorted on their (kind, target)
+// bits in LDS (two 9-bit passes; wave w owns the w-th sixteenth of the current
+// order, counts its digits, the counts are scanned over waves and digits and
+// each wave places its elements in order, so equal digits keep their order),
+// written to keys_out, and their runs give start[slot] and cnt[slot] (slot =
+// kind * n_nodes + target; cnt was cleared by the emission).  Then tot[i] =
+// own[i] + cnt[n_nodes + i] and p2p_off = its exclusive scan, with the total
+// at p2p_off[n_nodes] and in ctrl->n_p2p.  More keys than TRS_MAX: the lists
+// are marked as overflowing (the walk is repeated, on the multi-block path).
+constexpr int TRS_THREADS = 1024;
+constexpr int TRS_WAVES = TRS_THREADS / WAVE;
+constexpr int TRS_BATCH = TRS_MAX / TRS_THREADS;  // 64-element batches per wave and pass
+
+__global__ void __launch_bounds__(TRS_THREADS)
+    k_tr_small(const uint64_t* __restrict__ keys_in, int64_t cap, Control* ctrl, int sh,
+               int64_t n_nodes, uint64_t* __restrict__ keys_out, int64_t* __restrict__ start,
+               int32_t* __restrict__ cnt, const int32_t* __restrict__ own,
+               int64_t* __restrict__ tot, int64_t* __restrict__ p2p_off) {
+  bookkeeping_priority();
+  __shared__ uint64_t skey[TRS_MAX];
+  __shared__ int16_t ping[2][TRS_MAX];
+  __shared__ int wc[TRS_WAVES][512];
+  __shared__ int64_t wsum64[TRS_WAVES];
+  __shared__ int wsum[TRS_WAVES];
+  if (walk_aborted(ctrl)) return;
+  const int64_t nd = min(ctrl->n_tr, cap);
+  if (nd > TRS_MAX) {
+    if (threadIdx.x == 0) {
+      ctrl->list_overflow = 1;
+      ctrl->tr_small_over = 1;
+    }
+    return;
+  }
+  const int n = (int)nd;
+  const int tid = threadIdx.x, w = tid / WAVE, lane = __lane_id();
+  for (int i = tid; i < n; i += TRS_THREADS) {
+    skey[i] = keys_in[i];
+    ping[0][i] = (int16_t)i;
+  }
+  __syncthreads();
+  const int per = TRS_BATCH * WAVE;  // the wave's part of the order
+  const int c0 = min(n, w * per), c1 = min(n, c0 + per);
+  const uint64_t lt = lanemask_lt();
+  const int bits = sh + 1;  // kind and target
+  const int passes = (bits + 8) / 9;
+  for (int pass = 0; pass < passes; pass++) {
+    const int16_t* src = ping[pass & 1];
+    int16_t* dst = ping[(pass & 1) ^ 1];
+    const int shift = sh + 9 * pass;
+    const uint32_t dmask = (1u << min(9, sh + bits - shift)) - 1u;
+    for (int d = lane; d < 512; d += WAVE) wc[w][d] = 0;
+    __builtin_amdgcn_wave_barrier();
+    int16_t sv[TRS_BATCH];
+    int dg[TRS_BATCH];
+#pragma unroll
+    for (int b = 0; b < TRS_BATCH; b++) {
+      const int i = c0 + b * WAVE + lane;
+      sv[b] = i < c1 ? src[i] : (int16_t)0;
+      dg[b] = i < c1 ? (int)((skey[sv[b]] >> shift) & dmask) : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < TRS_BATCH; b++)
+      if (dg[b] >= 0) atomicAdd(&wc[w][dg[b]], 1);
+    __syncthreads();
+    int incl = 0, acc = 0;
+    if (tid < 512) {  // digit tid: start of each wave's part within the digit
+      for (int q = 0; q < TRS_WAVES; q++) {
+        const int c = wc[q][tid];
+        wc[q][tid] = acc;
+        acc += c;
+      }
+      incl = wave_incl_scan(acc);
+      if (lane == WAVE - 1) wsum[w] = incl;
+    }
+    __syncthreads();
+    if (tid < 512) {
+      int dstart = incl - acc;
+      for (int q = 0; q < w; q++) dstart += wsum[q];
+      for (int q = 0; q < TRS_WAVES; q++) wc[q][tid] += dstart;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < TRS_BATCH; b++) {
+      if (c0 + b * WAVE >= c1) break;  // wave-uniform
+      const int d = dg[b];
+      uint64_t mask = __ballot(d >= 0);
+#pragma unroll
+      for (int k = 0; k < 9; k++) {
+        const uint64_t bb = __ballot((d >> k) & 1);
+        mask &= ((d >> k) & 1) ? bb : ~bb;
+      }
+      const int before = d >= 0 ? wc[w][d] : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (d >= 0) {
+        dst[before + __popcll(mask & lt)] = sv[b];
+        if ((mask & lt) == 0) wc[w][d] = before + __popcll(mask);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+  }
+  const int16_t* ord = ping[passes & 1];
+  const uint64_t gmask = (1ull << (sh + 1)) - 1ull;  // kind and target, above the source
+  // sorted keys and the run starts
+  for (int k = tid; k < n; k += TRS_THREADS) {
+    const uint64_t key = skey[ord[k]];
+    keys_out[k] = key;
+    const uint64_t g = (key >> sh) & gmask;
+    if (k == 0 || ((skey[ord[k - 1]] >> sh) & gmask) != g) {
+      const int64_t slot = (int64_t)(g >> sh) * n_nodes + (int64_t)(g & ((1ull << sh) - 1ull));
+      start[slot] = k;
+    }
+  }
+  __syncthreads();  // the starts are visible to the whole block
+  for (int k = tid; k < n; k += TRS_THREADS) {
+    const uint64_t g = (skey[ord[k]] >> sh) & gmask;
+    if (k == n - 1 || ((skey[ord[k + 1]] >> sh) & gmask) != g) {
+      const int64_t slot = (int64_t)(g >> sh) * n_nodes + (int64_t)(g & ((1ull << sh) - 1ull));
+      cnt[slot] = (int32_t)(k + 1 - start[slot]);
+    }
+  }
+  __syncthreads();  // the run lengths are visible to the whole block
+  // near-field list sizes and their exclusive scan: thread t takes a
+  // contiguous range of nodes
+  const int64_t chunk = (n_nodes + TRS_THREADS - 1) / TRS_THREADS;
+  const int64_t i0 = min(n_nodes, (int64_t)tid * chunk), i1 = min(n_nodes, i0 + chunk);
+  int64_t part = 0;
+  for (int64_t i = i0; i < i1; i++) {
+    const int64_t t = (int64_t)own[i] + cnt[n_nodes + i];
+    tot[i] = t;
+    part += t;
+  }
+  const int64_t winc = wave_incl_scan(part);
+  if (lane == WAVE - 1) wsum64[w] = winc;
+  __syncthreads();
+  int64_t off = winc - part, total = 0;
+  for (int q = 0; q < TRS_WAVES; q++) {
+    if (q < w) off += wsum64[q];
+    total += wsum64[q];
+  }
+  for (int64_t i = i0; i < i1; i++) {
+    p2p_off[i] = off;
+    off += tot[i];
+  }
+  if (tid == 0) {
+    p2p_off[n_nodes] = total;
+    ctrl->n_p2p = total;
+  }
+}
+
+hipError_t launch_tr_small(const uint64_t* keys_in, int64_t cap, Control* ctrl, int key_shift,
+                           int64_t n_nodes, uint64_t* keys_out, int64_t* start, int32_t* cnt,
+                           const int32_t* own, int64_t* tot, int64_t* p2p_off, hipStream_t st) {
+  if (key_shift > 17 || n_nodes > TRS_MAX_NODES) return hipErrorInvalidValue;
+  k_tr_small<<<1, TRS_THREADS, 0, st>>>(keys_in, cap, ctrl, key_shift, n_nodes, keys_out, start,
+                                        cnt, own, tot, p2p_off);
+  return hipGetLastError();
+}
 
 // Sorted transposed keys of one kind -> after each target's own entries.
 __global__ void k_tr_scatter(const uint64_t* keys, int64_t kcap, const int64_t* n_dev,

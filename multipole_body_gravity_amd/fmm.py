@@ -38,7 +38,8 @@ class _Stats(ctypes.Structure):
                 ("theta", ctypes.c_double), ("lo", ctypes.c_double * 3), ("side", ctypes.c_double),
                 ("stage_ms", ctypes.c_float * len(STAGES)), ("walk_retries", ctypes.c_int32),
                 ("kernel_ms", ctypes.c_float * len(KERNELS)), ("timed_builds", ctypes.c_int32),
-                ("timed_evals", ctypes.c_int32), ("timed_vjps", ctypes.c_int32)]
+                ("timed_evals", ctypes.c_int32), ("timed_vjps", ctypes.c_int32),
+                ("walk_one_block", ctypes.c_int32)]
 
 
 _lib = None
@@ -209,7 +210,7 @@ class Plan:
                 "stage_ms": {k: float(v) for k, v in zip(STAGES, s.stage_ms)},
                 "kernel_ms": {k: float(v) for k, v in zip(KERNELS, s.kernel_ms)},
                 "timed_builds": s.timed_builds, "timed_evals": s.timed_evals,
-                "timed_vjps": s.timed_vjps}
+                "timed_vjps": s.timed_vjps, "walk_one_block": bool(s.walk_one_block)}
 
     def copy_keys(self):
         keys = np.zeros(self.n, dtype=np.uint64)

@@ -115,17 +115,76 @@ CASES = [
     ("clustered", 4000, 39, 10, 0.5, 32, "f64"),
     ("uniform", 2500, 40, 9, 0.7, 16, "f32"),
     ("plummer", 2000, 41, 10, 0.6, 40, "f32"),
+    # 4041, 4104 and 5233 transposed entries: the one-block walk tail on the
+    # second build with one and two sort passes (131, 290 and 157 nodes)
+    ("plummer", 1500, 42, 4, 0.7, 64, "f64"),
+    ("clustered", 3000, 44, 4, 0.7, 64, "f32"),
+    ("plummer", 2500, 46, 2, 0.7, 128, "f64"),
 ]
 
 
 @pytest.mark.parametrize("dist,n,seed,order,theta,leaf,dt", CASES)
 def test_parity_small(orc, dist, n, seed, order, theta, leaf, dt):
+    """Structure and values against the oracle after the first build (the
+    walk's multi-block path for the transposed keys) and after a second build
+    on the same plan (the one-block path wherever the first walk found at most
+    3/4 of its capacity, 6144 keys, with 17-bit node ids at most)."""
     say(f"  case {dist} n={n} p={order} theta={theta} leaf={leaf} {dt}")
     pos, mass = inputs(dist, n, seed, dt)
     plan, phi, acc = gpu_run(pos, mass, order, theta, leaf, dt)
     ref = orc.fmm(pos, mass, order, theta, leaf)
+    assert not plan.stats()["walk_one_block"]
     check_structure(plan, ref)
     check_values(phi, acc, ref, dt, no_floor=(seed in (1001, 1002)))
+    torch = _torch()
+    phi1, acc1 = phi, acc
+    tdt = torch.float64 if dt == "f64" else torch.float32
+    dev = torch.device("cuda:0")
+    plan.build(torch.from_numpy(pos).to(dev, tdt), torch.from_numpy(mass).to(dev, tdt))
+    p2, a2 = plan.eval()
+    torch.cuda.synchronize()
+    st = plan.stats()
+    # the transposed entries: sources deeper than their target
+    lev = ref.level.astype(np.int64)
+    n_tr = 0
+    for k in ("m2l", "p2p"):
+        off, src = getattr(ref, k + "_off"), getattr(ref, k + "_src")
+        tgt = np.repeat(np.arange(len(off) - 1), np.diff(off))
+        n_tr += int(np.count_nonzero(lev[src] > lev[tgt]))
+    say(f"    second build: one-block walk tail {st['walk_one_block']} ({n_tr} transposed entries)")
+    nn = len(ref.level)
+    assert st["walk_one_block"] == (n_tr <= 6144 and nn <= 65536), "walk tail path"
+    check_structure(plan, ref)
+    phi2, acc2 = p2.double().cpu().numpy(), a2.double().cpu().numpy()
+    assert np.array_equal(phi2, phi1) and np.array_equal(acc2, acc1), "second build differs"
+    plan.close()
+
+
+def test_walk_one_block_overflow(orc):
+    """A plan whose last walk had no transposed entries takes the one-block
+    path; the next positions have 58637 of them, more than it holds: the walk
+    is repeated on the multi-block path and the lists and values match the
+    oracle."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    dev = torch.device("cuda:0")
+    n = 10000
+    plan = Plan(n, order=4, theta=0.7, leaf_size=32, dtype=torch.float64, device=dev)
+    pos_u, mass_u = inputs("uniform", n, 1001, "f64")
+    for _ in range(2):
+        plan.build(torch.from_numpy(pos_u).to(dev), torch.from_numpy(mass_u).to(dev))
+    pos, mass = inputs("plummer", n, 1002, "f64")
+    say(f"  after uniform builds: one-block {plan.stats()['walk_one_block']}")
+    plan.build(torch.from_numpy(pos).to(dev), torch.from_numpy(mass).to(dev))
+    phi, acc = plan.eval()
+    torch.cuda.synchronize()
+    st = plan.stats()
+    say(f"  plummer build: one-block {st['walk_one_block']}, walk repeats {st['walk_retries']}")
+    assert st["walk_retries"] >= 1 and not st["walk_one_block"]
+    ref = orc.fmm(pos, mass, 4, 0.7, 32)
+    check_structure(plan, ref)
+    check_values(phi.double().cpu().numpy(), acc.double().cpu().numpy(), ref, "f64",
+                 no_floor=True)
     plan.close()
 
 
