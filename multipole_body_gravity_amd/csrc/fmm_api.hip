@@ -784,8 +784,6 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
                              P<int64_t>(p->lvl_blkcnt), p->scan_tmp.p, ctrl, st));
   TRY(sync_ctrl(p, st));
   p->root_host = p->ctrl_host->root;
-  collect_pending(p);  // the previous step's events have completed
-  for (int k = 0; k < FMM_N_KERNELS; k++) p->kran[k] = false;
   if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;
   const Control& c = *p->ctrl_host;
   const int64_t nn = c.level_off[MAX_LEVELS];
@@ -830,6 +828,11 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
                              P<int32_t>(p->leaf_of), P<int32_t>(p->parents), p->scan_tmp.p, ctrl,
                              st));
   rec(p, FMM_STAGE_TREE, 1, st);
+  // the previous step's events completed before the synchronization above;
+  // they are read while the tree's second phase runs, before this build
+  // records the walk's, the upward pass's and the kernels' events again
+  collect_pending(p);
+  for (int k = 0; k < FMM_N_KERNELS; k++) p->kran[k] = false;
 
   // the upward pass goes on the second stream after the tree; it is issued
   // by the walk once its level launches are queued (host launch time then
