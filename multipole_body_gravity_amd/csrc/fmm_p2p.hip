@@ -212,7 +212,10 @@ struct P2PShared {
     Piece16 tile[NH][TILE];
     T red[8][WAVE];
   };
-  uint8_t owner[MAXQ];  // list entry (within the group of 64) of each source particle
+  union {
+    uint8_t owner[MAXQ];  // list entry (within the group of 64) of each source particle
+    T fin[WAVE];  // after the staging: the targets' sums, one per lane (rounds of <= 16 targets)
+  };
   int32_t sbase[WAVE];  // per entry: first particle minus its first source index
 };
 
@@ -363,15 +366,38 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
       sh.red[6][lane] = b2;
       sh.red[7][lane] = b3;
       __builtin_amdgcn_wave_barrier();
-      // target t0 + l (l < tc) is finished by lane l % 64: pair l / 2, member l % 2
+      // Each target's four sums add its ns slices in slice order; lane pair g
+      // holds targets 2g, 2g + 1 (member 4 (l & 1) of red).  Up to 16 targets
+      // in the round, the 4 tc sums (target l = v / 4, component c = v % 4)
+      // are formed one per lane, so most lanes work, and staged in fin; then
+      // one lane per target writes all four.
+      const bool spread = tc <= WAVE / 4;
+      if (spread) {
+        if (lane < 4 * tc) {
+          const int l = lane >> 2, c = lane & 3;
+          const int gg = l >> 1, m = 4 * (l & 1) + c;
+          T sv = 0;
+          for (int q = 0; q < ns; q++) sv += sh.red[m][q * G + gg];
+          sh.fin[lane] = sv;
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
       for (int l = lane; l < tc; l += WAVE) {
-        const int gg = l >> 1, m = 4 * (l & 1);
-        T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-        for (int q = 0; q < ns; q++) {
-          s0 += sh.red[m][q * G + gg];
-          s1 += sh.red[m + 1][q * G + gg];
-          s2 += sh.red[m + 2][q * G + gg];
-          s3 += sh.red[m + 3][q * G + gg];
+        T s0, s1, s2, s3;
+        if (spread) {
+          s0 = sh.fin[4 * l];
+          s1 = sh.fin[4 * l + 1];
+          s2 = sh.fin[4 * l + 2];
+          s3 = sh.fin[4 * l + 3];
+        } else {
+          const int gg = l >> 1, m = 4 * (l & 1);
+          s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+          for (int q = 0; q < ns; q++) {
+            s0 += sh.red[m][q * G + gg];
+            s1 += sh.red[m + 1][q * G + gg];
+            s2 += sh.red[m + 2][q * G + gg];
+            s3 += sh.red[m + 3][q * G + gg];
+          }
         }
         s0 *= Pair::S_PHI;  // exact powers of two
         s1 *= Pair::S_ACC;
@@ -399,7 +425,7 @@ __device__ __forceinline__ void p2p_tasks(const P2PTask* __restrict__ tasks, int
 }
 
 template <typename T>
-__global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_eu(5, 8)))
+__global__ void __launch_bounds__(P2P_THREADS) __attribute__((amdgpu_waves_per_eu(6, 8)))
     k_p2p(const P2PTask* __restrict__ tasks, int64_t n_tasks, const int32_t* __restrict__ begin,
           const int32_t* __restrict__ count, const uint8_t* __restrict__ mut,
           const int32_t* __restrict__ parent, const int32_t* __restrict__ src,
