@@ -46,6 +46,11 @@ namespace mbg {
 constexpr int WK_THREADS = 256;
 constexpr int WK_WAVES = WK_THREADS / WAVE;
 constexpr int WALK_TAB = 8 * WAVE;  // candidates of 64 carried entries (<= 8 children each)
+// Generators of at most GEN_T entries are read once, by the counting pass,
+// which also keeps each entry's child count and first candidate in the wave's
+// LDS for both enumeration passes (each pass over memory is a chain of
+// dependent loads per 64 entries).
+constexpr int GEN_T = 4 * WAVE;
 
 // Opening criterion, theta = |l_A + l_B| / |c_A - c_B| with l = (h, h, h):
 // accept iff 3 (h_A + h_B)^2 < fl(theta^2) |c_A - c_B|^2.  Centres and
@@ -69,10 +74,12 @@ __device__ __forceinline__ bool accept_pair(const int4& A, const int4& B, double
 // root).  f(active, cand, geo of cand, phase) is called by the whole wave; the
 // geometry of the next 64 candidates is loaded before f runs on the current
 // ones, so its latency overlaps their classification.  tab: the wave's LDS
-// table of WALK_TAB candidates.
+// table of WALK_TAB candidates.  gk, gf (null: read the generator): per entry
+// its node's child count (-1 without X's bit) and its first candidate (the
+// node itself when it is a leaf, else its first child), from the counting pass.
 template <typename F>
 __device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int32_t X, int32_t* tab,
-                                                   F&& f) {
+                                                   const int* gk, const int32_t* gf, F&& f) {
   const int lane = __lane_id();
   const uint64_t* gen;
   int gc, slot;
@@ -91,16 +98,24 @@ __device__ __forceinline__ void for_each_candidate(const WalkArgs& a, int32_t X,
       const int j = c0 + lane;
       int nc = 0, fc = 0;
       if (j < gc) {
-        const uint64_t e = gen[j];
-        if ((e >> slot) & 1u) {
-          const int32_t g = (int32_t)(e >> 8);
-          const int k = a.n_child[g];
-          if (phase == 0 && k == 0) {
-            nc = 1;
-            fc = g;
-          } else if (phase == 1 && k != 0) {
-            nc = k;
-            fc = a.first_child[g];
+        if (gk) {
+          const int k = gk[j];
+          if ((phase == 0 && k == 0) || (phase == 1 && k > 0)) {
+            nc = k == 0 ? 1 : k;
+            fc = gf[j];
+          }
+        } else {
+          const uint64_t e = gen[j];
+          if ((e >> slot) & 1u) {
+            const int32_t g = (int32_t)(e >> 8);
+            const int k = a.n_child[g];
+            if (phase == 0 && k == 0) {
+              nc = 1;
+              fc = g;
+            } else if (phase == 1 && k != 0) {
+              nc = k;
+              fc = a.first_child[g];
+            }
           }
         }
       }
@@ -203,7 +218,11 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
   // regrows the pools and repeats the walk
   if (a.ctrl->pool_overflow) return;
   __shared__ int32_t tab_all[WK_WAVES][WALK_TAB];
+  __shared__ int gk_all[WK_WAVES][GEN_T];
+  __shared__ int32_t gf_all[WK_WAVES][GEN_T];
   int32_t* tab = tab_all[threadIdx.x / WAVE];
+  int* gk = gk_all[threadIdx.x / WAVE];
+  int32_t* gf = gf_all[threadIdx.x / WAVE];
   const int lane = __lane_id();
   const uint64_t lt = lanemask_lt();
   for (int64_t j = (int64_t)blockIdx.x * WK_WAVES + threadIdx.x / WAVE; j < a.pcnt;
@@ -213,12 +232,33 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
     const Group G = load_group(a, X);
     // number of candidates: carried leaves count 1, carried non-leaves their children
     const Gen gen = generator(a, X);
+    const bool inlds = gen.n <= GEN_T;
     int nc_lane = 0;
-    for (int c0 = lane; c0 < gen.n; c0 += WAVE) {
-      const uint64_t e = gen.e[c0];
-      if ((e >> gen.slot) & 1u) {
-        const int k = a.n_child[(int32_t)(e >> 8)];
-        nc_lane += k == 0 ? 1 : k;
+    if (inlds) {  // all loads of a step issued before the first is used
+      constexpr int R = GEN_T / WAVE;
+      uint64_t e[R];
+      int k[R];
+#pragma unroll
+      for (int r = 0; r < R; r++) e[r] = r * WAVE + lane < gen.n ? gen.e[r * WAVE + lane] : 0ull;
+#pragma unroll
+      for (int r = 0; r < R; r++)
+        k[r] = r * WAVE + lane < gen.n && ((e[r] >> gen.slot) & 1u)
+                   ? (int)a.n_child[(int32_t)(e[r] >> 8)]
+                   : -1;
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        const int32_t g = (int32_t)(e[r] >> 8);
+        gk[r * WAVE + lane] = k[r];
+        gf[r * WAVE + lane] = k[r] > 0 ? a.first_child[g] : g;
+        nc_lane += k[r] < 0 ? 0 : (k[r] == 0 ? 1 : k[r]);
+      }
+    } else {
+      for (int c0 = lane; c0 < gen.n; c0 += WAVE) {
+        const uint64_t e = gen.e[c0];
+        if ((e >> gen.slot) & 1u) {
+          const int k = a.n_child[(int32_t)(e >> 8)];
+          nc_lane += k == 0 ? 1 : k;
+        }
       }
     }
     const int64_t ncand = wave_sum((int64_t)nc_lane);
@@ -245,7 +285,8 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
     int64_t kU = 0, kPU = 0, kCU = 0;
     uint32_t ntm = 0, ntp = 0;  // per lane
     uint64_t cm[4] = {0, 0, 0, 0}, cp[4] = {0, 0, 0, 0};
-    for_each_candidate(a, X, tab, [&](bool act, int32_t c, const int4& g, int phase) {
+    const int* gkp = inlds ? gk : nullptr;
+    for_each_candidate(a, X, tab, gkp, gf, [&](bool act, int32_t c, const int4& g, int phase) {
       uint32_t mM = 0, mP = 0, mC = 0;
       if (act) classify(a, G, g, mM, mP, mC);
       const uint64_t packed = (uint64_t)(uint32_t)c << 8;
