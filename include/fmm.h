@@ -76,9 +76,9 @@ enum fmm_stage {
   FMM_STAGE_WALK = 3,  /* dual-tree walk, M2L and P2P lists     */
   FMM_STAGE_UP = 4,    /* P2M + M2M + M2L source records (build, second stream) */
   FMM_STAGE_M2L = 5,   /* M2L of the own entries, sibling kernel (build, second stream) */
-  FMM_STAGE_DOWN = 6,  /* L2L + L2P                             */
+  FMM_STAGE_DOWN = 6,  /* L2L (build; L2P is timed as a kernel)  */
   FMM_STAGE_P2P = 7,   /* the single P2P (+ combine) launch     */
-  FMM_STAGE_TAIL = 8,  /* M2L of the transposed tails (eval)    */
+  FMM_STAGE_TAIL = 8,  /* M2L of the transposed tails (build)   */
   FMM_STAGE_VJP = 9,   /* the whole fmm_vjp call                */
   FMM_N_STAGES = 10
 };
@@ -121,8 +121,9 @@ typedef struct {
 int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size, int dtype);
 
 /* Sort the particles, build the octree and the interaction lists, form the
- * multipoles (P2M, M2M) and translate them along the own M2L entries (every
- * pair whose source is at the target's level or coarser).  pos [N][3] and
+ * multipoles (P2M, M2M), translate them along every M2L entry and pass the
+ * locals down to the leaves (L2L): the whole far field up to the leaves'
+ * local expansions.  pos [N][3] and
  * mass [N] are device arrays in the plan's dtype; they are copied into the
  * plan's sorted layout, so the caller may reuse them once `stream` has passed
  * this call.  The multipoles need the tree only and the own-entry M2L the
@@ -139,11 +140,11 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
  * (on the device) for the end of that call before its first launch. */
 int fmm_build(fmm_plan_t plan, const void* pos, const void* mass, void* stream);
 
-/* Evaluate potential and acceleration of every particle: the M2L of the
- * transposed entries, L2L, L2P and P2P on top of the build's far-field work,
- * written in the caller's order.  phi [N] and acc [N][3] are device arrays in
- * the plan's dtype.  Asynchronous on `stream`; may be repeated after one
- * build (the build's results are only read). */
+/* Evaluate potential and acceleration of every particle: the leaves' local
+ * expansions at the particles (L2P) plus the near field (P2P), written in the
+ * caller's order.  phi [N] and acc [N][3] are device arrays in the plan's
+ * dtype.  Asynchronous on `stream`; may be repeated after one build (the
+ * build's results are only read). */
 int fmm_eval(fmm_plan_t plan, void* phi, void* acc, void* stream);
 
 /* Vector-Jacobian product of the evaluation (jz-fmm page, "Following
@@ -247,7 +248,7 @@ int fmm_copy_tree(fmm_plan_t plan, uint8_t* level, uint64_t* prefix, int32_t* be
 int fmm_copy_lists(fmm_plan_t plan, int64_t* m2l_off, int32_t* m2l_src, int64_t* p2p_off,
                    int32_t* p2p_src);
 
-/* Multipoles and locals after the last eval, [n_nodes][C(p+3,3)] fp64, for
+/* Multipoles and locals of the last build, [n_nodes][C(p+3,3)] fp64, for
  * multi-indices (a,b,c) ordered by degree, then a descending, then b
  * descending.  mpole = raw moments sum_j m_j s^(a,b,c) about the cell centre;
  * local = derivatives d^(a,b,c) phi at the cell centre (with every ancestor's

@@ -97,17 +97,17 @@ void collect_early_build(fmm_plan_t p) {
 }
 void collect_pending(fmm_plan_t p) {
   if (p->pend_build) {
-    for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP, FMM_STAGE_M2L})
+    for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP, FMM_STAGE_M2L, FMM_STAGE_TAIL, FMM_STAGE_DOWN})
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
-    for (int k : {FMM_KERNEL_M2L_SIB, FMM_KERNEL_P2M})
+    for (int k : {FMM_KERNEL_M2L_SIB, FMM_KERNEL_P2M, FMM_KERNEL_M2L_TAIL})
       if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_builds++;
     p->pend_build = false;
   }
   if (p->pend_eval) {
-    for (int s : {FMM_STAGE_TAIL, FMM_STAGE_DOWN, FMM_STAGE_P2P})
+    for (int s : {FMM_STAGE_P2P})
       p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
-    for (int k : {FMM_KERNEL_M2L_TAIL, FMM_KERNEL_P2P, FMM_KERNEL_P2P_COMBINE, FMM_KERNEL_L2P})
+    for (int k : {FMM_KERNEL_P2P, FMM_KERNEL_P2P_COMBINE, FMM_KERNEL_L2P})
       if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_evals++;
     p->pend_eval = false;
@@ -849,15 +849,19 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
     return wrc;
   }
   rec(p, FMM_STAGE_WALK, 1, st);
+  // the leaves' complete locals (transposed-tail M2L, downward pass) need
+  // nothing the eval brings: queued here, they run while the host returns
+  // and issues the eval
+  TRY(leaf_locals(p, st));
+  rec(p, FMM_STAGE_DOWN, 1, st);
   collect_early_build(p);  // keys, sort and tree ended before the walk's last sync
   p->built = true;
+  p->evaluated = true;  // the locals are complete
   return FMM_OK;
 }
 
 int eval_impl(fmm_plan_t p, void* phi, void* acc, hipStream_t st) {
-  // source records and the own-entry locals come from the build's second
-  // stream (leaf_locals waits for each); `local` is only read from here on
-  TRY(leaf_locals(p, st));
+  // the leaves' complete locals (lfin) come from the build
   if (p->timing) TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_L2P], st));
   TRY_HIP(launch_l2p(p->dtype, p->order, p->n, p->pts.p, P<int32_t>(p->leaf_of),
                      P<double>(p->ncentre), p->lfin.p, p->far.p, st));
@@ -865,7 +869,6 @@ int eval_impl(fmm_plan_t p, void* phi, void* acc, hipStream_t st) {
     TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_L2P + 1], st));
     p->kran[FMM_KERNEL_L2P] = true;
   }
-  rec(p, FMM_STAGE_DOWN, 1, st);
 
   rec(p, FMM_STAGE_P2P, 0, st);
   int32_t* leaves = P<int32_t>(p->leaves);
@@ -887,7 +890,6 @@ int eval_impl(fmm_plan_t p, void* phi, void* acc, hipStream_t st) {
                      p->kran + FMM_KERNEL_P2P, st));
   rec(p, FMM_STAGE_P2P, 1, st);
   p->pend_eval = p->timing;
-  p->evaluated = true;
   return FMM_OK;
 }
 
@@ -903,11 +905,7 @@ int vjp_impl(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_b
   TRY(grow(p->vlocal, w * p->K * nn));
   TRY(grow(p->vlfin, w * p->K * nn));
   TRY_HIP(hipStreamWaitEvent(st, p->ev_up, 0));
-  // the forward's leaf locals (lfin) give the Hessian term
-  if (!p->evaluated) {
-    TRY(leaf_locals(p, st));
-    p->evaluated = true;
-  }
+  // the forward's leaf locals (lfin, from the build) give the Hessian term
   rec(p, FMM_STAGE_VJP, 0, st);
   const double* centre = P<double>(p->ncentre);
   int32_t* leaves = P<int32_t>(p->leaves);
@@ -1028,17 +1026,17 @@ int fmm_stats(fmm_plan_t p, fmm_stats_t* out) {
     const double nb = std::max(1, p->n_timed_builds), ne = std::max(1, p->n_timed_evals),
                  nv = std::max(1, p->n_timed_vjps);
     for (int s = 0; s < FMM_N_STAGES; s++)
-      out->stage_ms[s] = (float)(p->stage_sum[s] / (s <= FMM_STAGE_WALK || s == FMM_STAGE_UP ||
-                                                             s == FMM_STAGE_M2L
-                                                         ? nb
+      out->stage_ms[s] = (float)(p->stage_sum[s] / (s == FMM_STAGE_P2P   ? ne
                                                      : s == FMM_STAGE_VJP ? nv
-                                                                          : ne));
+                                                                          : nb));
     for (int k = 0; k < FMM_N_KERNELS; k++)
-      out->kernel_ms[k] = (float)(p->kernel_sum[k] /
-                                  (k == FMM_KERNEL_M2L_SIB || k == FMM_KERNEL_P2M ? nb
-                                   : k == FMM_KERNEL_VJP_M2L_SIB || k == FMM_KERNEL_VJP_P2P
-                                       ? nv
-                                       : ne));
+      out->kernel_ms[k] =
+          (float)(p->kernel_sum[k] / (k == FMM_KERNEL_M2L_SIB || k == FMM_KERNEL_P2M ||
+                                              k == FMM_KERNEL_M2L_TAIL
+                                          ? nb
+                                      : k == FMM_KERNEL_VJP_M2L_SIB || k == FMM_KERNEL_VJP_P2P
+                                          ? nv
+                                          : ne));
     out->timed_builds = p->n_timed_builds;
     out->timed_evals = p->n_timed_evals;
     out->timed_vjps = p->n_timed_vjps;
