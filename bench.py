@@ -418,7 +418,7 @@ def vjp_bench(args):
     torch.cuda.synchronize()
     st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
 
-    plan.set_timing(True)
+    plan.set_timing(2)  # the main kernels and the fmm_vjp call, not every stage
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -460,7 +460,6 @@ def vjp_bench(args):
                    "seed": cfg["seed"], "sensitivities": "standard normal, seed 2024"},
         "roofline": roof,
         "roofline_other": {k: v for k, v in rl.items() if k != dominant},
-        "stage_ms": {k: round(v, 4) for k, v in s["stage_ms"].items()},
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
         "work": {"p2p_pairs": p2p_pairs, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,
                  "p2p_vjp_flops_per_pair": P2P_VJP_FLOPS_PER_PAIR,
@@ -506,7 +505,7 @@ def lattice_bench(args):
     torch.cuda.synchronize()
     qs, us = tq.clone(), tu.clone()
     st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
-    plan.set_timing(True)
+    plan.set_timing(2)  # the main kernels only: stage events slow the step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     plan.lattice_steps(tq, tu, tmass, dx, dv, dt, args.steps, +1)
@@ -546,7 +545,6 @@ def lattice_bench(args):
                    "seed": cfg["seed"], "dt": dt, "dx": dx, "dv": dv,
                    "velocities": "N(0, 0.1) per component, seed 301"},
         "roofline": roof,
-        "stage_ms": {k: round(v, 4) for k, v in s["stage_ms"].items() if k != "vjp"},
         "kernel_ms": {k: round(v, 4) for k, v in kern.items() if not k.startswith("vjp")},
     }
     plan.close()
@@ -623,12 +621,18 @@ def main():
     st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, cfg["n"])
     n_m2l = st["n_m2l"]
 
-    # HIP events around every stage and main kernel of each step, on the launch
-    # stream; the library reads them at the synchronizations a build makes
-    # anyway, so the timed loop carries no extra synchronization
-    plan.set_timing(True)
+    # HIP events around the near-field kernels of each step (timing mode 3), on
+    # the stream they are launched on; the library reads them at the
+    # synchronizations a build makes anyway, so the timed loop carries no
+    # extra synchronization.  Every event is a marker that slows the step a
+    # little by itself, so the other kernels' times (mode 2) and the stage
+    # times (mode 1) come from separate passes after the timed one.
+    plan.set_timing(3)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for e0, e1 in evs:  # torch creates an event at its first record: not in the timed loop
+        e0.record()
+        e1.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -641,9 +645,27 @@ def main():
     step_ms = [a.elapsed_time(b) for a, b in evs]
     s = plan.stats()  # means over the K timed steps
     assert s["timed_builds"] == args.steps and s["timed_evals"] == args.steps, s
-    stage_avg = s["stage_ms"]
-    kern_avg = s["kernel_ms"]
+    kern_timed = s["kernel_ms"]
     ms_step = wall / args.steps * 1e3
+    # side passes: every main kernel's events, then the stages'
+    k_side = min(args.steps, 20)
+    side_ms = {}
+    for mode in (2, 1):
+        plan.set_timing(mode)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(k_side):
+            plan.build(tpos, tmass)
+            plan.eval(phi, acc)
+        torch.cuda.synchronize()
+        side_ms[mode] = (time.perf_counter() - t1) / k_side * 1e3
+        if mode == 2:
+            kern_avg = dict(plan.stats()["kernel_ms"])
+        else:
+            stage_avg = plan.stats()["stage_ms"]
+    plan.set_timing(0)
+    for k in ("p2p", "p2p_combine"):  # the near field: from the timed steps
+        kern_avg[k] = kern_timed[k]
 
     # accuracy of the last step's outputs, outside the timed region
     ref = direct_reference(tpos, tmass, cfg["n"])
@@ -697,6 +719,11 @@ def main():
         "accuracy": accuracy,
         "measured_peaks": peaks,
         "stage_ms": {k: round(v, 4) for k, v in stage_avg.items() if k != "vjp"},
+        "stage_ms_how": f"a separate pass of {k_side} steps with the stage events on "
+                        f"({side_ms[1]:.4f} ms per step there)",
+        "kernel_ms_how": "p2p and p2p_combine from the timed steps (their events are the only "
+                         f"ones there); the others from a pass of {k_side} steps with every main "
+                         f"kernel's events ({side_ms[2]:.4f} ms per step there)",
         "kernel_ms": {k: round(v, 4) for k, v in kern_avg.items() if not k.startswith("vjp")},
         "work": {"n_m2l": n_m2l, "n_m2l_own": n_m2l_own, "n_m2l_transposed": n_m2l_tr,
                  "p2p_pairs": p2p_pairs, "n_nodes": st["n_nodes"],

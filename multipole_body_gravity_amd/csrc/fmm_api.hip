@@ -67,7 +67,9 @@ T* P(DBuf& b) {
 size_t wbytes(int dtype) { return dtype == FMM_F64 ? 8 : 4; }
 
 void rec(fmm_plan_t p, int stage, int end, hipStream_t st) {
-  if (p->timing) (void)hipEventRecord(p->ev[2 * stage + end], st);
+  // the whole fmm_vjp call is timed in either mode
+  if (p->timing && (p->timing_stages || stage == FMM_STAGE_VJP))
+    (void)hipEventRecord(p->ev[2 * stage + end], st);
 }
 
 int bbox_blocks(int64_t n) {
@@ -91,22 +93,25 @@ double elapsed(hipEvent_t a, hipEvent_t b) {
 }
 void collect_early_build(fmm_plan_t p) {
   if (!p->timing) return;
-  for (int s = FMM_STAGE_KEYS; s <= FMM_STAGE_TREE; s++)
-    p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
+  if (p->timing_stages)
+    for (int s = FMM_STAGE_KEYS; s <= FMM_STAGE_TREE; s++)
+      p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
   p->pend_build = true;  // the walk stage is still pending
 }
 void collect_pending(fmm_plan_t p) {
   if (p->pend_build) {
-    for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP, FMM_STAGE_M2L, FMM_STAGE_TAIL, FMM_STAGE_DOWN})
-      p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
+    if (p->timing_stages)
+      for (int s : {FMM_STAGE_WALK, FMM_STAGE_UP, FMM_STAGE_M2L, FMM_STAGE_TAIL, FMM_STAGE_DOWN})
+        p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
     for (int k : {FMM_KERNEL_M2L_SIB, FMM_KERNEL_P2M, FMM_KERNEL_M2L_TAIL})
       if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_builds++;
     p->pend_build = false;
   }
   if (p->pend_eval) {
-    for (int s : {FMM_STAGE_P2P})
-      p->stage_sum[s] += elapsed(p->ev[2 * s], p->ev[2 * s + 1]);
+    if (p->timing_stages)
+      p->stage_sum[FMM_STAGE_P2P] +=
+          elapsed(p->ev[2 * FMM_STAGE_P2P], p->ev[2 * FMM_STAGE_P2P + 1]);
     for (int k : {FMM_KERNEL_P2P, FMM_KERNEL_P2P_COMBINE, FMM_KERNEL_L2P})
       if (p->kran[k]) p->kernel_sum[k] += elapsed(p->kev[2 * k], p->kev[2 * k + 1]);
     p->n_timed_evals++;
@@ -183,10 +188,10 @@ int issue_upward(fmm_plan_t p) {
   const int dt = p->dtype, ord = p->order;
   const double* centre = P<double>(p->ncentre);
   rec(p, FMM_STAGE_UP, 0, us);
-  if (p->timing) TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_P2M], us));
+  if (p->timing_kernels) TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_P2M], us));
   TRY_HIP(launch_p2m(dt, ord, p->pts.p, P<int32_t>(p->leaves), p->n_leaves,
                      P<int32_t>(p->nbegin), P<int32_t>(p->ncount), centre, p->mpole.p, us));
-  if (p->timing) {
+  if (p->timing_kernels) {
     TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_P2M + 1], us));
     p->kran[FMM_KERNEL_P2M] = true;
   }
@@ -209,7 +214,7 @@ int issue_sibling_m2l(fmm_plan_t p, hipStream_t st, bool capped) {
   TRY_HIP(hipEventRecord(p->ev_order, st));
   TRY_HIP(hipStreamWaitEvent(us, p->ev_order, 0));
   M2LArgs ma = m2l_args(p);
-  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_SIB : nullptr;
+  ma.ev = p->timing_kernels ? p->kev + 2 * FMM_KERNEL_M2L_SIB : nullptr;
   ma.ran = p->kran + FMM_KERNEL_M2L_SIB;
   ma.max_blocks = capped ? 2 * (int64_t)std::max(p->n_cu, 1) : 0;
   ma.stop = P<Control>(p->ctrl);  // the walk may still be repeated
@@ -520,7 +525,7 @@ int leaf_locals(fmm_plan_t p, hipStream_t st) {
   TRY_HIP(hipStreamWaitEvent(st, pull ? p->ev_rec : p->ev_up, 0));
   rec(p, FMM_STAGE_TAIL, 0, st);
   M2LArgs ma = m2l_args(p);
-  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_M2L_TAIL : nullptr;
+  ma.ev = p->timing_kernels ? p->kev + 2 * FMM_KERNEL_M2L_TAIL : nullptr;
   ma.ran = p->kran + FMM_KERNEL_M2L_TAIL;
   if (!pull) {  // the level-by-level pass works on a copy
     TRY_HIP(hipMemcpyAsync(p->lfin.p, p->local.p, lbytes, hipMemcpyDeviceToDevice, st));
@@ -682,8 +687,10 @@ int fmm_set_walk_pool_hint(fmm_plan_t p, int64_t entries_per_node) {
 }
 
 int fmm_set_timing(fmm_plan_t p, int enable) {
-  if (!p) return FMM_ERR_ARG;
+  if (!p || enable < 0 || enable > 3) return FMM_ERR_ARG;
   p->timing = enable != 0;
+  p->timing_stages = enable == 1;
+  p->timing_kernels = enable == 1 || enable == 2;
   if (p->timing) {
     TRY_HIP(hipSetDevice(p->device));
     TRY_HIP(hipDeviceSynchronize());
@@ -862,10 +869,10 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
 
 int eval_impl(fmm_plan_t p, void* phi, void* acc, hipStream_t st) {
   // the leaves' complete locals (lfin) come from the build
-  if (p->timing) TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_L2P], st));
+  if (p->timing_kernels) TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_L2P], st));
   TRY_HIP(launch_l2p(p->dtype, p->order, p->n, p->pts.p, P<int32_t>(p->leaf_of),
                      P<double>(p->ncentre), p->lfin.p, p->far.p, st));
-  if (p->timing) {
+  if (p->timing_kernels) {
     TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_L2P + 1], st));
     p->kran[FMM_KERNEL_L2P] = true;
   }
@@ -921,7 +928,7 @@ int vjp_impl(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_b
   M2LArgs ma = m2l_args(p);
   ma.mrec = p->vmred.p;
   ma.local = p->vlocal.p;
-  ma.ev = p->timing ? p->kev + 2 * FMM_KERNEL_VJP_M2L_SIB : nullptr;
+  ma.ev = p->timing_kernels ? p->kev + 2 * FMM_KERNEL_VJP_M2L_SIB : nullptr;
   ma.ran = p->kran + FMM_KERNEL_VJP_M2L_SIB;
   TRY_HIP(launch_m2l_sib(dt, ord, ma, st));
   ma.ev = nullptr;

@@ -90,6 +90,8 @@ struct fmm_plan_s {
   int device;
   int n_cu = 0;  // compute units of the device
   bool built = false, evaluated = false, timing = false;
+  bool timing_stages = false;   // timing: the stage events
+  bool timing_kernels = false;  // timing: every main kernel's (else the near field's only)
   bool l2l_pulled = false;  // last eval used the one-launch downward pass
 
   // N-sized

@@ -198,8 +198,16 @@ class Plan:
         self._check(self.lib.fmm_set_walk_pool_hint(self._h, int(entries_per_node)),
                     "fmm_set_walk_pool_hint")
 
-    def set_timing(self, enable: bool = True) -> None:
-        self._check(self.lib.fmm_set_timing(self._h, 1 if enable else 0), "fmm_set_timing")
+    def set_timing(self, enable=True) -> None:
+        """HIP events read at the next synchronization a call makes anyway.
+
+        True or 1: stage and kernel events; 2: the main kernels' events only;
+        3: the near-field kernels' events (and the fmm_vjp stage) only;
+        False or 0: off.  Each event is a marker on the stream that costs a
+        little by itself, so fewer events disturb the timed work less.
+        """
+        mode = 1 if enable is True else (0 if enable is False else int(enable))
+        self._check(self.lib.fmm_set_timing(self._h, mode), "fmm_set_timing")
 
     def stats(self) -> dict:
         s = _Stats()

@@ -922,4 +922,37 @@ def test_streams_and_timing(orc):
         check_values(phi.cpu().numpy(), acc.cpu().numpy(), d["ref"], "f64")
         check_vjp(xb.cpu().numpy(), mb.cpu().numpy(), d["rx"], d["rm"], "f64",
                   inputs=(d["pos"], d["mass"], d["pb"], d["ab"]))
+    # timing mode 2: the kernels and the VJP call only, no other stage events
+    plan.set_timing(2)
+    for k in range(2):
+        d = sets[k % 2]
+        plan.build(d["tp"], d["tm"])
+        phi, acc = plan.eval()
+        plan.vjp(d["tpb"], d["tab"], xb, mb)
+    torch.cuda.synchronize()
+    st = plan.stats()
+    assert st["timed_builds"] == 2 and st["timed_evals"] == 2 and st["timed_vjps"] == 2, st
+    for k, v in st["stage_ms"].items():
+        assert (v > 0.0) if k == "vjp" else (v == 0.0), (k, st["stage_ms"])
+    for k in ("m2l_sib", "m2l_tail", "p2p", "vjp_m2l_sib", "vjp_p2p"):
+        assert st["kernel_ms"][k] > 0.0, (k, st["kernel_ms"])
+    check_values(phi.double().cpu().numpy(), acc.double().cpu().numpy(), sets[1]["ref"], "f64")
+    # timing mode 3: the near-field kernels and the VJP call only
+    plan.set_timing(3)
+    for k in range(2):
+        d = sets[k % 2]
+        plan.build(d["tp"], d["tm"])
+        phi, acc = plan.eval()
+        plan.vjp(d["tpb"], d["tab"], xb, mb)
+    torch.cuda.synchronize()
+    st = plan.stats()
+    assert st["timed_builds"] == 2 and st["timed_evals"] == 2 and st["timed_vjps"] == 2, st
+    for k, v in st["stage_ms"].items():
+        assert (v > 0.0) if k == "vjp" else (v == 0.0), (k, st["stage_ms"])
+    for k, v in st["kernel_ms"].items():
+        assert (v > 0.0) if k in ("p2p", "vjp_p2p") else (k == "p2p_combine" or v == 0.0), \
+            (k, st["kernel_ms"])
+    check_values(phi.double().cpu().numpy(), acc.double().cpu().numpy(), sets[1]["ref"], "f64")
+    with pytest.raises(RuntimeError):
+        plan.set_timing(4)
     plan.close()
