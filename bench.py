@@ -416,7 +416,6 @@ def vjp_bench(args):
         plan.eval(phi, acc)
         plan.vjp(tpb, tab, xb, mb)
     torch.cuda.synchronize()
-    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
 
     plan.set_timing(2)  # the main kernels and the fmm_vjp call, not every stage
     torch.cuda.synchronize()
@@ -430,6 +429,8 @@ def vjp_bench(args):
     s = plan.stats()
     assert s["timed_vjps"] == args.steps and s["timed_evals"] == args.steps, s
     kern = s["kernel_ms"]
+    # work counts of the last build (every build of these inputs is the same)
+    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
 
     fpp = m2l_flops_per_pair(cfg["order"])
     peak = FP64_VECTOR_PEAK_TFLOPS if cfg["dtype"] == "f64" else FP32_VECTOR_PEAK_TFLOPS
@@ -504,7 +505,6 @@ def lattice_bench(args):
         plan.lattice_steps(tq, tu, tmass, dx, dv, dt, args.warmup, +1)
     torch.cuda.synchronize()
     qs, us = tq.clone(), tu.clone()
-    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
     plan.set_timing(2)  # the main kernels only: stage events slow the step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -513,6 +513,8 @@ def lattice_bench(args):
     wall = time.perf_counter() - t0
     s = plan.stats()
     plan.set_timing(False)
+    # work counts of the last step's build (outside the timed region)
+    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, n)
     plan.lattice_steps(tq, tu, tmass, dx, dv, dt, args.steps, -1)
     torch.cuda.synchronize()
     reversible = bool(torch.equal(tq, qs) and torch.equal(tu, us))
@@ -555,7 +557,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mutual", action="store_true",
                     help="sum the sibling leaves' near field mutually (fmm_set_mutual_near_field)")
@@ -617,10 +619,6 @@ def main():
         plan.eval(phi, acc)
     torch.cuda.synchronize()
 
-    # work counts of this workload (outside the timed region)
-    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, cfg["n"])
-    n_m2l = st["n_m2l"]
-
     # HIP events around the near-field kernels of each step (timing mode 3), on
     # the stream they are launched on; the library reads them at the
     # synchronizations a build makes anyway, so the timed loop carries no
@@ -666,6 +664,11 @@ def main():
     plan.set_timing(0)
     for k in ("p2p", "p2p_combine"):  # the near field: from the timed steps
         kern_avg[k] = kern_timed[k]
+    # work counts of the last build (every build of these inputs is the same);
+    # taken after the timed steps, so that the GPU does not sit idle between
+    # the warm-up and the timed steps
+    st, p2p_pairs, n_m2l_own, n_m2l_tr = work_counts(plan, cfg["n"])
+    n_m2l = st["n_m2l"]
 
     # accuracy of the last step's outputs, outside the timed region
     ref = direct_reference(tpos, tmass, cfg["n"])
