@@ -347,6 +347,7 @@ __global__ void __launch_bounds__(WK_THREADS) k_walk(WalkArgs a) {
 // tested again against X's children; (c <- child) keys go to the group's slot of
 // the M2L part (accepted) or the P2P part (leaf-leaf rejected), candidate by
 // candidate, children in order.
+constexpr int TRE_U = 4;  // chunks of generator entries per round of k_tr_emit
 __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a, int32_t* run_cnt,
                                                          int64_t run_n) {
   bookkeeping_priority();
@@ -371,24 +372,45 @@ __global__ void __launch_bounds__(WK_THREADS) k_tr_emit(WalkArgs a, int32_t* run
     const Group G = load_group(a, X);
     const Gen gen = generator(a, X);
     int64_t om = a.trm_base[pi], op = ntm_all + a.trp_base[pi];
-    for (int c0 = 0; c0 < gen.n; c0 += WAVE) {
-      uint32_t mM = 0, mP = 0, mC = 0;
-      int32_t c = 0;
-      if (c0 + lane < gen.n) {
-        const uint64_t e = gen.e[c0 + lane];
-        c = (int32_t)(e >> 8);
-        if (((e >> gen.slot) & 1u) && a.n_child[c] == 0) classify(a, G, a.geo[c], mM, mP, mC);
+    const uint64_t hiK = 1ull << (2 * a.key_shift);
+    // TRE_U chunks of 64 entries per round: their entries, child counts and
+    // geometry are loaded together, so that a long generator (a sparse leaf
+    // next to a dense cluster has ~10^5 carried candidates) costs one chain of
+    // dependent loads per TRE_U chunks; the keys are then written chunk by
+    // chunk, in entry order, as with one chunk per round
+    for (int c0 = 0; c0 < gen.n; c0 += TRE_U * WAVE) {
+      uint64_t e[TRE_U];
+#pragma unroll
+      for (int u = 0; u < TRE_U; u++) {
+        const int j = c0 + u * WAVE + lane;
+        e[u] = j < gen.n ? gen.e[j] : 0ull;  // 0: no slot bit, inactive
       }
-      const int nm = __popc(mM), np = __popc(mP);
-      const int im = wave_incl_scan(nm), ip = wave_incl_scan(np);
-      int64_t wm = om + (im - nm), wp = op + (ip - np);
-      const uint64_t hiC = (uint64_t)(uint32_t)c << a.key_shift;
-      const uint64_t kind = 1ull << (2 * a.key_shift);
-      for (uint32_t m = mM; m; m &= m - 1) a.tr_keys[wm++] = hiC | (uint32_t)(G.fc + __ffs(m) - 1);
-      for (uint32_t m = mP; m; m &= m - 1)
-        a.tr_keys[wp++] = kind | hiC | (uint32_t)(G.fc + __ffs(m) - 1);
-      om += __shfl(im, WAVE - 1, WAVE);
-      op += __shfl(ip, WAVE - 1, WAVE);
+      int kc[TRE_U];
+      int4 gc[TRE_U];
+#pragma unroll
+      for (int u = 0; u < TRE_U; u++) {
+        kc[u] = 1;
+        gc[u] = make_int4(0, 0, 0, 0);
+        if ((e[u] >> gen.slot) & 1u) {
+          const int32_t c = (int32_t)(e[u] >> 8);
+          kc[u] = a.n_child[c];
+          gc[u] = a.geo[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TRE_U; u++) {
+        uint32_t mM = 0, mP = 0, mC = 0;
+        if (kc[u] == 0) classify(a, G, gc[u], mM, mP, mC);
+        const int nm = __popc(mM), np = __popc(mP);
+        const int im = wave_incl_scan(nm), ip = wave_incl_scan(np);
+        int64_t wm = om + (im - nm), wp = op + (ip - np);
+        const uint64_t hiC = (uint64_t)(uint32_t)(e[u] >> 8) << a.key_shift;
+        for (uint32_t m = mM; m; m &= m - 1) a.tr_keys[wm++] = hiC | (uint32_t)(G.fc + __ffs(m) - 1);
+        for (uint32_t m = mP; m; m &= m - 1)
+          a.tr_keys[wp++] = hiK | hiC | (uint32_t)(G.fc + __ffs(m) - 1);
+        om += __shfl(im, WAVE - 1, WAVE);
+        op += __shfl(ip, WAVE - 1, WAVE);
+      }
     }
     (void)lt;
   }
