@@ -226,12 +226,14 @@ int issue_sibling_m2l(fmm_plan_t p, hipStream_t st, bool capped) {
 }
 
 // Expected duration of the sibling M2L over `own` own entries: about
-// 444 ((p + 1) / 5)^4 flops per entry at the rate the kernel reaches
-// (36 TFLOP/s in fp64, 60 in fp32 on this part).
+// 444 ((p + 1) / 5)^4 flops per entry, at the fraction of the device's vector
+// rate (compute units x 128 fp64 or unpacked fp32 flops per clock x clock)
+// that the kernel reaches: about 0.46 in fp64 and 0.76 in fp32.
 static double sibling_seconds(const fmm_plan_t p, int64_t own) {
   const double q = (p->order + 1) / 5.0;
   const double flops = 444.0 * q * q * q * q * (double)own;
-  return flops / (p->dtype == FMM_F64 ? 36e12 : 60e12);
+  const double rate = 128.0 * (double)std::max(p->n_cu, 1) * p->clock_hz;
+  return flops / ((p->dtype == FMM_F64 ? 0.46 : 0.76) * rate);
 }
 
 int run_walk(fmm_plan_t p, hipStream_t st) {
@@ -594,6 +596,12 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
       hipDeviceGetAttribute(&p->n_cu, hipDeviceAttributeMultiprocessorCount, p->device) !=
           hipSuccess)
     return fail(FMM_ERR_HIP);
+  {
+    int khz = 0;  // peak engine clock; only the scheduling estimate above uses it
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, p->device) == hipSuccess &&
+        khz > 0)
+      p->clock_hz = 1e3 * (double)khz;
+  }
   const size_t w = wbytes(dtype);
   if ((rc = grow(p->keys, 8 * n)) || (rc = grow(p->keys_alt, 8 * n)) || (rc = grow(p->idx, 4 * n)) ||
       (rc = grow(p->idx_alt, 4 * n)) || (rc = grow(p->pts, 4 * w * n)) ||
@@ -758,7 +766,7 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
 
   rec(p, FMM_STAGE_KEYS, 0, st);
   TRY_HIP(launch_fill_zero(ctrl, sizeof(Control), st));
-  if (n <= FRONT_MAX) {
+  if (n <= FRONT_MID_MAX) {
     // small sets: box, keys, sort and gather in one launch (timed as the keys stage)
     TRY_HIP(launch_front_small(pos, mass, n, p->dtype, P<uint64_t>(p->keys), P<int32_t>(p->idx),
                                p->pts.p, root, ctrl, st));

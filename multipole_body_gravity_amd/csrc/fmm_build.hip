@@ -654,71 +654,84 @@ hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, i
 // ===================================================================
 // small sets: box, keys, sort and gather in one launch
 //
-// For N <= FRONT_MAX one block of 1024 threads does all of it: the box by a
+// For N <= FRONT_MID_MAX one block of 1024 threads does all of it: the box by a
 // block reduction (min / max are exact, so the order does not matter), the
-// keys as k_keys, then the same stable LSD sort (seven 9-bit digits) with the
-// keys held in LDS and the permutation ping-ponged there (16 bytes per
-// particle): wave w owns the w-th sixteenth of the current order, counts its digits
-// (ballots, as in the multi-block sort), the counts are scanned over waves and
+// keys as k_keys, then the same stable LSD sort with the keys and the current
+// order held in LDS (12 bytes per particle): wave w owns the w-th sixteenth of
+// the current order, counts its digits, the counts are scanned over waves and
 // digits, and the wave places its elements in order, so equal digits keep
-// their order.  Each thread reads its particles once and keeps them in
-// registers, and writes their records at their ranks at the end (through the
-// inverse permutation), so the only global reads are one batch at the start.
+// their order.  Every thread reads its part of the order before any is
+// written (a block barrier between), so one order buffer serves all passes.
 // Replaces the 33 dependent launches of the multi-block path, which are what a
-// small step costs.  The sort is bound by the ballots that rank equal digits
-// (vector instructions of one compute unit): about 4.7 us per pass at 4096
-// particles.
+// small step costs.  Two instances:
+//   * N <= FRONT_MAX: seven 9-bit digits; each thread reads its particles once
+//     and keeps them in registers, and writes their records at their ranks at
+//     the end (through the inverse permutation), so the only global reads are
+//     one batch at the start.  The sort is bound by the ballots that rank equal
+//     digits (vector instructions of one compute unit): about 4.7 us per pass
+//     at 4096 particles.
+//   * N <= FRONT_MID_MAX: eight 8-bit digits (the per-wave digit counts then
+//     take 16 KB of LDS instead of 32, which leaves room for the keys and the
+//     order of 11264 particles); the particles are read again for the records,
+//     in sorted order (the set is small enough to stay in the caches).
 // ===================================================================
 constexpr int FRONT_THREADS = 1024;
 constexpr int FRONT_WAVES = FRONT_THREADS / WAVE;
-// 64-element batches of a wave's part, at most
-constexpr int FRONT_BATCH = ((FRONT_MAX + FRONT_WAVES - 1) / FRONT_WAVES + WAVE - 1) / WAVE;
 
-// particles per thread
-constexpr int FRONT_PER = (FRONT_MAX + FRONT_THREADS - 1) / FRONT_THREADS;
-
-template <typename T>
+template <typename T, int MAXN, int RB, bool KEEP>
 __global__ void __launch_bounds__(FRONT_THREADS)
     k_front_small(const T* __restrict__ pos, const T* __restrict__ mass, int n,
                   uint64_t* __restrict__ keys_sorted,
                   int32_t* __restrict__ perm, P4<T>* __restrict__ pts, RootInfo* root,
                   Control* ctrl) {
-  __shared__ uint64_t skey[FRONT_MAX];
-  __shared__ int32_t ping[2][FRONT_MAX];
-  __shared__ int wc[FRONT_WAVES][512];
+  constexpr int R = 1 << RB;
+  constexpr int PASSES = (63 + RB - 1) / RB;
+  // 64-element batches of a wave's part, at most
+  constexpr int BATCH = ((MAXN + FRONT_WAVES - 1) / FRONT_WAVES + WAVE - 1) / WAVE;
+  // particles per thread
+  constexpr int PER = (MAXN + FRONT_THREADS - 1) / FRONT_THREADS;
+  constexpr int KPER = KEEP ? PER : 1;
+  __shared__ uint64_t skey[MAXN];
+  __shared__ int32_t ord[MAXN];
+  __shared__ int wc[FRONT_WAVES][R];
   __shared__ double bs[6][FRONT_WAVES];
   __shared__ int wsum[8];
   __shared__ RootInfo rs;
   const int tid = threadIdx.x, w = tid / WAVE, lane = __lane_id();
   // the thread's particles tid + FRONT_THREADS b, read once (all loads in
-  // flight together) and kept in registers until they are written in order
-  T px[FRONT_PER], py[FRONT_PER], pz[FRONT_PER], pm[FRONT_PER];
-#pragma unroll
-  for (int b = 0; b < FRONT_PER; b++) {
-    const int i = tid + b * FRONT_THREADS;
-    px[b] = py[b] = pz[b] = pm[b] = 0;
-    if (i < n) {
-      px[b] = pos[3 * i];
-      py[b] = pos[3 * i + 1];
-      pz[b] = pos[3 * i + 2];
-      pm[b] = mass[i];
-    }
-  }
-  // box and non-finite check
+  // flight together); kept in registers until they are written in order when
+  // KEEP
+  T px[KPER], py[KPER], pz[KPER], pm[KPER];
   double lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
   int bad = 0;
+  auto see = [&](T x, T y, T z, T m) {  // box and non-finite check
+    const double v[3] = {(double)x, (double)y, (double)z};
 #pragma unroll
-  for (int b = 0; b < FRONT_PER; b++) {
-    if (tid + b * FRONT_THREADS < n) {
-      const double v[3] = {(double)px[b], (double)py[b], (double)pz[b]};
-#pragma unroll
-      for (int a = 0; a < 3; a++) {
-        bad |= !isfinite(v[a]);
-        lo[a] = fmin(lo[a], v[a]);
-        hi[a] = fmax(hi[a], v[a]);
-      }
-      bad |= !isfinite((double)pm[b]);
+    for (int a = 0; a < 3; a++) {
+      bad |= !isfinite(v[a]);
+      lo[a] = fmin(lo[a], v[a]);
+      hi[a] = fmax(hi[a], v[a]);
     }
+    bad |= !isfinite((double)m);
+  };
+  if constexpr (KEEP) {
+#pragma unroll
+    for (int b = 0; b < PER; b++) {
+      const int i = tid + b * FRONT_THREADS;
+      px[b] = py[b] = pz[b] = pm[b] = 0;
+      if (i < n) {
+        px[b] = pos[3 * i];
+        py[b] = pos[3 * i + 1];
+        pz[b] = pos[3 * i + 2];
+        pm[b] = mass[i];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < PER; b++)
+      if (tid + b * FRONT_THREADS < n) see(px[b], py[b], pz[b], pm[b]);
+  } else {
+    for (int i = tid; i < n; i += FRONT_THREADS)
+      see(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], mass[i]);
   }
 #pragma unroll
   for (int a = 0; a < 3; a++) {
@@ -759,13 +772,21 @@ __global__ void __launch_bounds__(FRONT_THREADS)
   }
   __syncthreads();
   const RootInfo r = rs;
+  if constexpr (KEEP) {
 #pragma unroll
-  for (int b = 0; b < FRONT_PER; b++) {
-    const int i = tid + b * FRONT_THREADS;
-    if (i < n) {
-      const T v3[3] = {px[b], py[b], pz[b]};
+    for (int b = 0; b < PER; b++) {
+      const int i = tid + b * FRONT_THREADS;
+      if (i < n) {
+        const T v3[3] = {px[b], py[b], pz[b]};
+        skey[i] = morton_key(v3, 0, r);
+        ord[i] = i;
+      }
+    }
+  } else {
+    for (int i = tid; i < n; i += FRONT_THREADS) {
+      const T v3[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
       skey[i] = morton_key(v3, 0, r);
-      ping[0][i] = i;
+      ord[i] = i;
     }
   }
   __syncthreads();
@@ -773,38 +794,36 @@ __global__ void __launch_bounds__(FRONT_THREADS)
   const int per = ((n + FRONT_WAVES - 1) / FRONT_WAVES + WAVE - 1) / WAVE * WAVE;
   const int c0 = min(n, w * per), c1 = min(n, c0 + per);
   const uint64_t lt = lanemask_lt();
-  for (int pass = 0; pass < 7; pass++) {
-    const int32_t* src = ping[pass & 1];
-    int32_t* dst = ping[(pass & 1) ^ 1];
-    const int shift = 9 * pass;
-    for (int d = lane; d < 512; d += WAVE) wc[w][d] = 0;
+  for (int pass = 0; pass < PASSES; pass++) {
+    const int shift = RB * pass;
+    for (int d = lane; d < R; d += WAVE) wc[w][d] = 0;
     __builtin_amdgcn_wave_barrier();
     // this lane's elements of the wave's part: index and digit (loaded first)
-    int32_t sv[FRONT_BATCH];
-    int dg[FRONT_BATCH];
+    int32_t sv[BATCH];
+    int dg[BATCH];
 #pragma unroll
-    for (int b = 0; b < FRONT_BATCH; b++) {
+    for (int b = 0; b < BATCH; b++) {
       const int i = c0 + b * WAVE + lane;
-      sv[b] = i < c1 ? src[i] : 0;
-      dg[b] = i < c1 ? (int)((skey[sv[b]] >> shift) & 511u) : -1;
+      sv[b] = i < c1 ? ord[i] : 0;
+      dg[b] = i < c1 ? (int)((skey[sv[b]] >> shift) & (uint64_t)(R - 1)) : -1;
     }
     // digit counts (integer LDS atomics: the order does not matter here)
 #pragma unroll
-    for (int b = 0; b < FRONT_BATCH; b++)
+    for (int b = 0; b < BATCH; b++)
       if (dg[b] >= 0) atomicAdd(&wc[w][dg[b]], 1);
-    __syncthreads();
+    __syncthreads();  // also: every part of the order has been read
     int incl = 0, acc = 0;
-    if (tid < 512) {  // digit tid: start of each wave's part within the digit
+    if (tid < R) {  // digit tid: start of each wave's part within the digit
       for (int q = 0; q < FRONT_WAVES; q++) {
         const int c = wc[q][tid];
         wc[q][tid] = acc;
         acc += c;
       }
-      incl = wave_incl_scan(acc);  // waves 0..7: digits in order
+      incl = wave_incl_scan(acc);  // the first R / 64 waves: digits in order
       if (lane == WAVE - 1) wsum[w] = incl;
     }
     __syncthreads();
-    if (tid < 512) {
+    if (tid < R) {
       int dstart = incl - acc;
       for (int q = 0; q < w; q++) dstart += wsum[q];
       for (int q = 0; q < FRONT_WAVES; q++) wc[q][tid] += dstart;
@@ -813,55 +832,89 @@ __global__ void __launch_bounds__(FRONT_THREADS)
     // each wave places its elements in order: ranks among equal digits from
     // ballots, after the wave's running position for the digit
 #pragma unroll
-    for (int b = 0; b < FRONT_BATCH; b++) {
+    for (int b = 0; b < BATCH; b++) {
       if (c0 + b * WAVE >= c1) break;  // wave-uniform
       const int d = dg[b];
-      const uint64_t mask = same_digit<9>(d, d >= 0);
+      const uint64_t mask = same_digit<RB>(d, d >= 0);
       const int before = d >= 0 ? wc[w][d] : 0;
       __builtin_amdgcn_wave_barrier();
       if (d >= 0) {
-        dst[before + __popcll(mask & lt)] = sv[b];
+        ord[before + __popcll(mask & lt)] = sv[b];
         if ((mask & lt) == 0) wc[w][d] = before + __popcll(mask);
       }
       __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
   }
-  // seven passes: the order is in ping[1]; its inverse goes to ping[0], and
-  // each thread writes its own particles' records at their places
-  for (int k = tid; k < n; k += FRONT_THREADS) {
-    const int32_t i = ping[1][k];
-    perm[k] = i;
-    keys_sorted[k] = skey[i];
-    ping[0][i] = k;
-  }
-  __syncthreads();
+  if constexpr (KEEP) {
+    // the inverse of the order replaces it, and each thread writes its own
+    // particles' records at their places
+    int32_t ik[PER];
 #pragma unroll
-  for (int b = 0; b < FRONT_PER; b++) {
-    const int i = tid + b * FRONT_THREADS;
-    if (i < n) {
+    for (int b = 0; b < PER; b++) {
+      const int k = tid + b * FRONT_THREADS;
+      ik[b] = 0;
+      if (k < n) {
+        const int32_t i = ord[k];
+        ik[b] = i;
+        perm[k] = i;
+        keys_sorted[k] = skey[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < PER; b++) {
+      const int k = tid + b * FRONT_THREADS;
+      if (k < n) ord[ik[b]] = k;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < PER; b++) {
+      const int i = tid + b * FRONT_THREADS;
+      if (i < n) {
+        P4<T> q;
+        q.x = px[b];
+        q.y = py[b];
+        q.z = pz[b];
+        q.m = pm[b];
+        pts[ord[i]] = q;
+      }
+    }
+  } else {
+    for (int k = tid; k < n; k += FRONT_THREADS) {
+      const int32_t i = ord[k];
+      perm[k] = i;
+      keys_sorted[k] = skey[i];
       P4<T> q;
-      q.x = px[b];
-      q.y = py[b];
-      q.z = pz[b];
-      q.m = pm[b];
-      pts[ping[0][i]] = q;
+      q.x = pos[3 * i];
+      q.y = pos[3 * i + 1];
+      q.z = pos[3 * i + 2];
+      q.m = mass[i];
+      pts[k] = q;
     }
   }
+}
+
+template <typename T>
+static void front_small_launch(const void* pos, const void* mass, int64_t n, uint64_t* keys_sorted,
+                               int32_t* perm, void* pts, RootInfo* root, Control* ctrl,
+                               hipStream_t st) {
+  if (n <= FRONT_MAX)
+    k_front_small<T, FRONT_MAX, 9, true><<<1, FRONT_THREADS, 0, st>>>(
+        (const T*)pos, (const T*)mass, (int)n, keys_sorted, perm, (P4<T>*)pts, root, ctrl);
+  else
+    k_front_small<T, FRONT_MID_MAX, 8, false><<<1, FRONT_THREADS, 0, st>>>(
+        (const T*)pos, (const T*)mass, (int)n, keys_sorted, perm, (P4<T>*)pts, root, ctrl);
 }
 
 hipError_t launch_front_small(const void* pos, const void* mass, int64_t n, int dtype,
                               uint64_t* keys_sorted, int32_t* perm, void* pts, RootInfo* root,
                               Control* ctrl, hipStream_t st) {
-  if (n < 1 || n > FRONT_MAX) return hipErrorInvalidValue;
+  if (n < 1 || n > FRONT_MID_MAX) return hipErrorInvalidValue;
   if (dtype == FMM_F64)
-    k_front_small<double><<<1, FRONT_THREADS, 0, st>>>((const double*)pos, (const double*)mass,
-                                                       (int)n, keys_sorted, perm,
-                                                       (P4<double>*)pts, root, ctrl);
+    front_small_launch<double>(pos, mass, n, keys_sorted, perm, pts, root, ctrl, st);
   else
-    k_front_small<float><<<1, FRONT_THREADS, 0, st>>>((const float*)pos, (const float*)mass,
-                                                      (int)n, keys_sorted, perm,
-                                                      (P4<float>*)pts, root, ctrl);
+    front_small_launch<float>(pos, mass, n, keys_sorted, perm, pts, root, ctrl, st);
   return hipGetLastError();
 }
 

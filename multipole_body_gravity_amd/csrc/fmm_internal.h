@@ -89,6 +89,7 @@ struct fmm_plan_s {
   double theta, t2;
   int device;
   int n_cu = 0;  // compute units of the device
+  double clock_hz = 2.4e9;  // their peak clock (from the device when it reports one)
   bool built = false, evaluated = false, timing = false;
   bool timing_stages = false;   // timing: the stage events
   bool timing_kernels = false;  // timing: every main kernel's (else the near field's only)
@@ -195,10 +196,12 @@ hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, i
                              hipStream_t st);
 hipError_t launch_gather(const void* pos, const void* mass, const int32_t* perm, int64_t n,
                          int dtype, void* pts, hipStream_t st);
-// Box, keys, stable sort and gather of a set of at most FRONT_MAX particles in
-// one launch: the same root, sorted keys, permutation and records as
-// launch_bbox + launch_keys + launch_radix_sort + launch_gather.
+// Box, keys, stable sort and gather of a set of at most FRONT_MID_MAX particles
+// in one launch: the same root, sorted keys, permutation and records as
+// launch_bbox + launch_keys + launch_radix_sort + launch_gather (two instances:
+// up to FRONT_MAX particles, and up to FRONT_MID_MAX).
 constexpr int FRONT_MAX = 8000;
+constexpr int FRONT_MID_MAX = 11264;
 hipError_t launch_front_small(const void* pos, const void* mass, int64_t n, int dtype,
                               uint64_t* keys_sorted, int32_t* perm, void* pts, RootInfo* root,
                               Control* ctrl, hipStream_t st);

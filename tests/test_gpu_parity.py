@@ -120,10 +120,15 @@ CASES = [
     ("plummer", 1500, 42, 4, 0.7, 64, "f64"),
     ("clustered", 3000, 44, 4, 0.7, 64, "f32"),
     ("plummer", 2500, 46, 2, 0.7, 128, "f64"),
-    # the largest set of the one-block front (every thread holds eight
-    # particles, the last ones partly) and the smallest of the multi-block one
+    # the one-block front: the largest set of its first instance (every
+    # thread holds eight particles, the last ones partly), the smallest and
+    # the largest of its second (8-bit digits), and the smallest set of the
+    # multi-block path
     ("uniform", 8000, 47, 4, 0.7, 32, "f64"),
     ("clustered", 8001, 48, 3, 0.6, 16, "f32"),
+    ("plummer", 11264, 49, 4, 0.7, 32, "f64"),
+    ("clustered", 11264, 50, 5, 0.6, 24, "f32"),
+    ("uniform", 11265, 51, 4, 0.7, 32, "f64"),
 ]
 
 
