@@ -63,7 +63,8 @@ enum fmm_status {
   FMM_ERR_ARG = -1,       /* argument out of range / NULL pointer */
   FMM_ERR_STATE = -2,     /* eval or copy before a successful build */
   FMM_ERR_OOM = -3,       /* device allocation failed */
-  FMM_ERR_HIP = -4,       /* a HIP runtime call failed */
+  FMM_ERR_HIP = -4,       /* a HIP runtime call failed, or a bounded wait of a kernel
+                           * (the sort's look-back over its tiles) was given up */
   FMM_ERR_NONFINITE = -5, /* NaN or Inf in positions or masses */
   FMM_ERR_NODEVICE = -6   /* no HIP device visible */
 };

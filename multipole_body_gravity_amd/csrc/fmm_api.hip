@@ -53,6 +53,17 @@ int grow(DBuf& b, size_t bytes) {
   return FMM_OK;
 }
 
+// grow(), and a new allocation cleared to zero (in stream order)
+int grow_cleared(DBuf& b, size_t bytes, hipStream_t st) {
+  const void* before = b.p;
+  const size_t cap0 = b.cap;
+  TRY(grow(b, bytes));
+  // a new allocation, even at the old address
+  if (b.p != before || b.cap != cap0) TRY_HIP(hipMemsetAsync(b.p, 0, b.cap, st));
+  return FMM_OK;
+}
+
+
 void release(DBuf& b) {
   if (b.p) (void)hipFree(b.p);
   b.p = nullptr;
@@ -62,6 +73,25 @@ void release(DBuf& b) {
 template <typename T>
 T* P(DBuf& b) {
   return static_cast<T*>(b.p);
+}
+
+// The particle sort places each digit in one launch (look-back over the
+// tiles) for up to OS_SORT_MAX keys, where that measured faster than per-tile
+// histograms, their scan and a scatter; above, with all of a pass's tiles
+// resident at once, the chains of the look-back made it slower (10^6 keys:
+// 0.246 -> 0.320 ms; 4*10^7: 5.94 -> 6.60 ms), and so they did for the walk's
+// transposed-key sort at every size measured.
+constexpr int64_t OS_SORT_MAX = (int64_t)1 << 17;
+// The sort's buffers for up to n keys (grown, new status words cleared).
+static int os_bufs(fmm_plan_t p, int64_t n, hipStream_t st, OsBufs* out, const OsBufs** use) {
+  *use = nullptr;
+  if (n > OS_SORT_MAX) return FMM_OK;
+  TRY(grow(p->os_state, sizeof(OsState)));
+  TRY(grow_cleared(p->os_dword, 8 * os_dword_words(n), st));
+  *out = OsBufs{P<OsState>(p->os_state), P<uint64_t>(p->os_dword),
+                &P<Control>(p->ctrl)->sort_err};
+  *use = out;
+  return FMM_OK;
 }
 
 size_t wbytes(int dtype) { return dtype == FMM_F64 ? 8 : 4; }
@@ -639,7 +669,8 @@ int fmm_destroy(fmm_plan_t p) {
   DBuf* bufs[] = {&p->keys,       &p->keys_alt,    &p->idx,         &p->idx_alt,
                   &p->pts,        &p->far,         &p->perm_inv,    &p->lcp,
                   &p->wlev,       &p->wtmp,        &p->leaf_level,  &p->leaf_of,
-                  &p->radix_hist, &p->scan_tmp,    &p->root,        &p->ctrl,
+                  &p->radix_hist, &p->scan_tmp,    &p->os_state,    &p->os_dword,
+                  &p->root,       &p->ctrl,
                   &p->bbox_part,  &p->nlevel,      &p->nprefix,     &p->nbegin,
                   &p->ncount,     &p->nparent,     &p->nfirst,      &p->nnchild,
                   &p->ncentre,    &p->nq,          &p->ngeo,        &p->leaves,
@@ -781,10 +812,13 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
 
     rec(p, FMM_STAGE_SORT, 0, st);
     bool sorted_alt = false;
+    OsBufs osb;
+    const OsBufs* os = nullptr;
+    TRY(os_bufs(p, n, st, &osb, &os));
     TRY_HIP(launch_radix_sort(P<uint64_t>(p->keys), P<int32_t>(p->idx),
                               P<uint64_t>(p->keys_alt), P<int32_t>(p->idx_alt), n,
                               P<int32_t>(p->radix_hist), P<int32_t>(p->scan_tmp), &sorted_alt,
-                              st));
+                              st, os));
     if (sorted_alt) {  // the sorted keys and permutation are the plan's from here on
       std::swap(p->keys, p->keys_alt);
       std::swap(p->idx, p->idx_alt);
@@ -800,6 +834,7 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
   TRY(sync_ctrl(p, st));
   p->root_host = p->ctrl_host->root;
   if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;
+  if (p->ctrl_host->sort_err) return FMM_ERR_HIP;  // a sort gave up a wait: its order is wrong
   const Control& c = *p->ctrl_host;
   const int64_t nn = c.level_off[MAX_LEVELS];
   // node ids are 32-bit, and the walk packs (kind, target, source) node ids

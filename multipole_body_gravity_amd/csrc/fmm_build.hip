@@ -5,6 +5,7 @@
 // construction on the GPU with neighbouring particles and sibling nodes next to
 // each other in memory; the layout rules (root cube, 21-bit keys, leaf rule,
 // breadth-first numbering) are documented in include/fmm.h.
+#include <atomic>
 #include "fmm_device.h"
 #include "fmm_internal.h"
 
@@ -482,33 +483,45 @@ __global__ void __launch_bounds__(RS_THREADS)
 // of the digit.  The per-wave counts are then combined in wave order (earlier
 // quarters first) and over digits, the tile is reordered by digit in LDS and
 // written out in that order, so each digit's run goes to consecutive addresses.
+// LDS of one tile of the scatter: its keys and values reordered by digit,
+// the per-wave digit counts (then starts), each digit's start in the tile and
+// its global start.
 template <int RB, int RS_ROUNDS>
-__global__ void __launch_bounds__(RS_THREADS)
-    k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
-                    int64_t n, int shift, uint32_t dmask, const int32_t* hist_scan, int nblk,
-                    const int64_t* n_dev, const Control* stop) {
-  bookkeeping_priority();
-  if (n_dev) n = min(*n_dev, n);
-  if (stop && walk_aborted(stop)) n = 0;
-  constexpr int R = 1 << RB;
-  constexpr int RS_TILE = RS_THREADS * RS_ROUNDS;
+struct RsTile {
+  static constexpr int R = 1 << RB;
+  static constexpr int TILE = RS_THREADS * RS_ROUNDS;
+  static constexpr int NW = RS_THREADS / WAVE;
+  uint64_t skey[TILE];
+  int32_t sval[TILE];
+  int wcnt[NW][R];
+  int dstart[R];
+  int gbase[R];
+  int wsum[NW];
+};
+
+// Rank one tile, stable: wave w ranks the w-th quarter of the tile on its own,
+// 64 elements per round in input order: ranks among equal digits come from
+// wave ballots (lower lanes first) added to the wave's running count of the
+// digit.  The per-wave counts are then combined in wave order (earlier
+// quarters first) and over digits; the tile is reordered by digit in LDS.
+// On return tot[k] is the tile's count of digit DPT tid + k, sh.dstart the
+// tile-local start of each digit's run, and the tile sits in sh.skey/sh.sval
+// in digit order (a block barrier has passed).
+template <int RB, int RS_ROUNDS>
+__device__ __forceinline__ void rs_rank_tile(const uint64_t* kin, const int32_t* vin, int64_t n,
+                                             int64_t tile, int shift, uint32_t dmask,
+                                             RsTile<RB, RS_ROUNDS>& sh,
+                                             int (&tot)[(1 << RB) / RS_THREADS]) {
+  using S = RsTile<RB, RS_ROUNDS>;
+  constexpr int R = S::R, NW = S::NW;
   constexpr int DPT = R / RS_THREADS;  // digits per thread in the digit scan (1 or 2)
-  constexpr int NW = RS_THREADS / WAVE;
-  constexpr int WTILE = RS_TILE / NW;  // elements per wave
-  __shared__ uint64_t skey[RS_TILE];
-  __shared__ int32_t sval[RS_TILE];
-  __shared__ int wcnt[NW][R];  // per-wave digit counts; then per-wave starts
-  __shared__ int dstart[R];    // tile-local start of each digit's run
-  __shared__ int gbase[R];     // global start of this tile's part of each digit
-  __shared__ int wsum[NW];
+  constexpr int WTILE = S::TILE / NW;  // elements per wave
   const int tid = threadIdx.x, w = tid / WAVE, lane = __lane_id();
-  for (int d = tid; d < R; d += RS_THREADS) {
-    gbase[d] = hist_scan[(int64_t)d * nblk + blockIdx.x];
+  for (int d = tid; d < R; d += RS_THREADS)
 #pragma unroll
-    for (int q = 0; q < NW; q++) wcnt[q][d] = 0;
-  }
+    for (int q = 0; q < NW; q++) sh.wcnt[q][d] = 0;
   __syncthreads();
-  const int64_t wbase = (int64_t)blockIdx.x * RS_TILE + (int64_t)w * WTILE;
+  const int64_t wbase = tile * S::TILE + (int64_t)w * WTILE;
   const uint64_t lt = lanemask_lt();
   int rk[RS_ROUNDS];  // rank of this lane's element of each round among its digit in the wave
   uint64_t kk[RS_ROUNDS];
@@ -526,38 +539,38 @@ __global__ void __launch_bounds__(RS_THREADS)
     const int d = (int)((kk[r] >> shift) & dmask);
     const uint64_t mask = same_digit<RB>(d, valid);
     const int rank = __popcll(mask & lt);
-    const int before = valid ? wcnt[w][d] : 0;
+    const int before = valid ? sh.wcnt[w][d] : 0;
     __builtin_amdgcn_wave_barrier();
-    if (valid && rank == 0) wcnt[w][d] = before + __popcll(mask);
+    if (valid && rank == 0) sh.wcnt[w][d] = before + __popcll(mask);
     __builtin_amdgcn_wave_barrier();
     rk[r] = before + rank;
   }
   __syncthreads();
   // thread t: digits DPT t .. DPT t + DPT - 1: starts in each wave's quarter,
   // and the tile totals
-  int tot[DPT], tsum = 0;
+  int tsum = 0;
 #pragma unroll
   for (int k = 0; k < DPT; k++) {
     const int d = DPT * tid + k;
     tot[k] = 0;
 #pragma unroll
     for (int q = 0; q < NW; q++) {
-      const int c = wcnt[q][d];
-      wcnt[q][d] = tot[k];
+      const int c = sh.wcnt[q][d];
+      sh.wcnt[q][d] = tot[k];
       tot[k] += c;
     }
     tsum += tot[k];
   }
   {
     const int incl = wave_incl_scan(tsum);
-    if (lane == WAVE - 1) wsum[w] = incl;
+    if (lane == WAVE - 1) sh.wsum[w] = incl;
     __syncthreads();
     int off = 0;
-    for (int q = 0; q < w; q++) off += wsum[q];
+    for (int q = 0; q < w; q++) off += sh.wsum[q];
     int e = off + incl - tsum;
 #pragma unroll
     for (int k = 0; k < DPT; k++) {
-      dstart[DPT * tid + k] = e;
+      sh.dstart[DPT * tid + k] = e;
       e += tot[k];
     }
   }
@@ -568,30 +581,284 @@ __global__ void __launch_bounds__(RS_THREADS)
     if (i < n) {
       const uint64_t key = kk[r];
       const int d = (int)((key >> shift) & dmask);
-      const int lp = dstart[d] + wcnt[w][d] + rk[r];
-      skey[lp] = key;
-      sval[lp] = vv[r];
+      const int lp = sh.dstart[d] + sh.wcnt[w][d] + rk[r];
+      sh.skey[lp] = key;
+      sh.sval[lp] = vv[r];
     }
   }
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * RS_TILE;
-  const int tn = (int)min((int64_t)RS_TILE, n - base);
-  for (int j = tid; j < tn; j += RS_THREADS) {
-    const uint64_t key = skey[j];
+}
+
+// The tile's elements, in digit order, to their places: a digit's run goes to
+// consecutive addresses from sh.gbase[d].
+template <int RB, int RS_ROUNDS>
+__device__ __forceinline__ void rs_write_tile(uint64_t* kout, int32_t* vout, int64_t n,
+                                              int64_t tile, int shift, uint32_t dmask,
+                                              const RsTile<RB, RS_ROUNDS>& sh) {
+  using S = RsTile<RB, RS_ROUNDS>;
+  const int64_t base = tile * S::TILE;
+  const int tn = (int)max((int64_t)0, min((int64_t)S::TILE, n - base));
+  for (int j = threadIdx.x; j < tn; j += RS_THREADS) {
+    const uint64_t key = sh.skey[j];
     const int d = (int)((key >> shift) & dmask);
-    const int64_t o = (int64_t)gbase[d] + (j - dstart[d]);
+    const int64_t o = (int64_t)sh.gbase[d] + (j - sh.dstart[d]);
     kout[o] = key;
-    if (vout) vout[o] = sval[j];
+    if (vout) vout[o] = sh.sval[j];
   }
+}
+
+// Scatter of one tile, stable, its digits' global starts from the scanned
+// per-tile histograms.
+template <int RB, int RS_ROUNDS>
+__global__ void __launch_bounds__(RS_THREADS)
+    k_radix_scatter(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout,
+                    int64_t n, int shift, uint32_t dmask, const int32_t* hist_scan, int nblk,
+                    const int64_t* n_dev, const Control* stop) {
+  bookkeeping_priority();
+  if (n_dev) n = min(*n_dev, n);
+  if (stop && walk_aborted(stop)) n = 0;
+  constexpr int R = 1 << RB;
+  __shared__ RsTile<RB, RS_ROUNDS> sh;
+  for (int d = threadIdx.x; d < R; d += RS_THREADS)
+    sh.gbase[d] = hist_scan[(int64_t)d * nblk + blockIdx.x];
+  int tot[R / RS_THREADS];
+  rs_rank_tile<RB, RS_ROUNDS>(kin, vin, n, blockIdx.x, shift, dmask, sh, tot);
+  rs_write_tile<RB, RS_ROUNDS>(kout, vout, n, blockIdx.x, shift, dmask, sh);
+}
+
+// ---- one launch per digit: decoupled look-back over the tiles ----
+//
+// The digit counts of every pass (they do not depend on the order) come from
+// one histogram launch.  Each tile of a pass then takes the next tile number
+// (an integer atomic: a tile waits only on tiles that started before it,
+// which are resident or done), ranks its keys, publishes its digit counts and
+// adds, per digit, the words of the tiles before it, newest first, up to the
+// first one that holds inclusive sums (the sums of that tile and every
+// earlier one); then it publishes its own inclusive sums.  The words are read
+// OS_BATCH tiles at a time.  Each status word carries the pass's epoch
+// (unique to the pass, so the array is never cleared) and its kind, and is
+// written and read with device-scope atomic stores and loads: a word is seen
+// whole or not at all, across the XCDs.  Waits are bounded: a wait that does
+// not end sets an error flag (the build then fails) and the pass runs on,
+// with wrong places but no hang.
+constexpr int OS_BATCH = 8;           // earlier tiles' words read together
+constexpr uint32_t OS_AGG = 1u;       // the tile's own digit counts
+constexpr uint32_t OS_INC = 2u;       // the digit sums of the tile and every earlier one
+constexpr int OS_SPIN_MAX = 1 << 20;  // polls before a wait is given up
+constexpr int OS_HIST_BLOCKS = 256;   // blocks of the histogram launch (fewer atomics per counter)
+
+__device__ __forceinline__ uint64_t os_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void os_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t os_word(uint32_t epoch, uint32_t kind, uint32_t v) {
+  return ((uint64_t)epoch << 34) | ((uint64_t)kind << 32) | (uint64_t)v;
+}
+// kind of a status word of this pass (0: not written in this pass yet)
+__device__ __forceinline__ uint32_t os_kind(uint64_t w, uint32_t epoch) {
+  return (uint32_t)(w >> 34) == epoch ? (uint32_t)(w >> 32) & 3u : 0u;
+}
+
+// Digit counts of every pass: one block per chunk of keys, counts in LDS,
+// then added to st->hist with integer atomics (the order does not matter).
+template <int RB>
+__global__ void __launch_bounds__(RS_THREADS)
+    k_os_hist(const uint64_t* keys, int64_t n, int lo_bit, int passes, int last_bits,
+              OsState* st, const int64_t* n_dev, const Control* stop) {
+  bookkeeping_priority();
+  if (n_dev) n = min(*n_dev, n);
+  if (stop && walk_aborted(stop)) n = 0;
+  constexpr int R = 1 << RB;
+  __shared__ int h[OS_MAX_PASSES][R];
+  for (int e = threadIdx.x; e < OS_MAX_PASSES * R; e += RS_THREADS) (&h[0][0])[e] = 0;
+  __syncthreads();
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t i0 = blockIdx.x * per, i1 = min(n, i0 + per);
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += RS_THREADS) {
+    const uint64_t k = keys[i];
+    for (int p = 0; p < passes; p++) {
+      const uint32_t m = p == passes - 1 ? (1u << last_bits) - 1u : (uint32_t)(R - 1);
+      atomicAdd(&h[p][(int)((k >> (lo_bit + RB * p)) & m)], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < passes * R; e += RS_THREADS) {
+    const int v = (&h[0][0])[e];
+    if (v) atomicAdd(&st->hist[e / R][e % R], v);
+  }
+}
+
+template <int RB, int RS_ROUNDS>
+__global__ void __launch_bounds__(RS_THREADS)
+    k_os_pass(const uint64_t* kin, const int32_t* vin, uint64_t* kout, int32_t* vout, int64_t n,
+              int pass, int shift, uint32_t dmask, OsState* st, uint64_t* dword, uint32_t epoch,
+              int32_t* err, const int64_t* n_dev, const Control* stop) {
+  bookkeeping_priority();
+  if (n_dev) n = min(*n_dev, n);
+  if (stop && walk_aborted(stop)) n = 0;
+  constexpr int R = 1 << RB;
+  constexpr int DPT = R / RS_THREADS;
+  __shared__ RsTile<RB, RS_ROUNDS> sh;
+  __shared__ int tile_s, err_s;
+  const int tid = threadIdx.x, lane = __lane_id();
+  if (tid == 0) {
+    tile_s = (int)atomicAdd(&st->tile_ctr[pass], 1u);
+    err_s = 0;
+  }
+  // the pass's digit starts over the whole array (exclusive scan of its counts)
+  int c[DPT], cs = 0;
+#pragma unroll
+  for (int k = 0; k < DPT; k++) {
+    c[k] = st->hist[pass][DPT * tid + k];
+    cs += c[k];
+  }
+  {
+    const int incl = wave_incl_scan(cs);
+    if (lane == WAVE - 1) sh.wsum[tid / WAVE] = incl;
+    __syncthreads();
+    int e = incl - cs;
+    for (int q = 0; q < tid / WAVE; q++) e += sh.wsum[q];
+#pragma unroll
+    for (int k = 0; k < DPT; k++) {
+      sh.gbase[DPT * tid + k] = e;
+      e += c[k];
+    }
+  }
+  const int t = tile_s;  // read after the barrier above
+  int tot[DPT];
+  rs_rank_tile<RB, RS_ROUNDS>(kin, vin, n, t, shift, dmask, sh, tot);
+  // publish the tile's counts (tile 0: they are already its inclusive sums)
+#pragma unroll
+  for (int k = 0; k < DPT; k++)
+    os_store(&dword[(int64_t)t * R + DPT * tid + k],
+             os_word(epoch, t == 0 ? OS_INC : OS_AGG, (uint32_t)tot[k]));
+  if (t > 0) {
+#pragma unroll
+    for (int k = 0; k < DPT; k++) {
+      const int d = DPT * tid + k;
+      uint32_t sum = 0;
+      int spins = 0;
+      // the tile just before: in the steady state it has its inclusive sums
+      // already, and one word is all that needs reading
+      int j = t - 1;
+      for (;;) {
+        const uint64_t w1 = os_load(&dword[(int64_t)j * R + d]);
+        const uint32_t kind = os_kind(w1, epoch);
+        if (kind != 0u) {
+          sum = (uint32_t)w1;
+          j = kind == OS_INC ? -1 : j - 1;
+          break;
+        }
+        if (++spins > OS_SPIN_MAX) {
+          err_s = 1;
+          j = -1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      for (; j >= 0;) {
+        uint64_t wv[OS_BATCH];
+#pragma unroll
+        for (int b = 0; b < OS_BATCH; b++)  // below tile 0: inclusive zeros
+          wv[b] = j - b >= 0 ? os_load(&dword[(int64_t)(j - b) * R + d]) : os_word(epoch, OS_INC, 0);
+        uint32_t part = 0;
+        bool found = false, wait = false;
+#pragma unroll
+        for (int b = 0; b < OS_BATCH; b++) {
+          if (!found && !wait) {
+            const uint32_t kind = os_kind(wv[b], epoch);
+            if (kind == 0u) {
+              wait = true;
+            } else {
+              part += (uint32_t)wv[b];
+              found = kind == OS_INC;
+            }
+          }
+        }
+        if (wait) {  // a tile not yet published before the first inclusive word: read again
+          if (++spins > OS_SPIN_MAX) {
+            err_s = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          continue;
+        }
+        sum += part;
+        if (found) break;
+        j -= OS_BATCH;
+      }
+      os_store(&dword[(int64_t)t * R + d], os_word(epoch, OS_INC, sum + (uint32_t)tot[k]));
+      sh.gbase[d] += (int)sum;
+    }
+  }
+  __syncthreads();
+  if (tid == 0 && err_s && err) atomicOr(err, 1);
+  rs_write_tile<RB, RS_ROUNDS>(kout, vout, n, t, shift, dmask, sh);
+}
+
+size_t os_dword_words(int64_t n) {
+  const int64_t tile = rs_tile(n);
+  return (size_t)(RS_MAX_RADIX * ((n + tile - 1) / tile));
 }
 
 // Sorts on bits [lo_bit, lo_bit + bits): 9-bit digits when that saves a pass
 // (63-bit Morton keys: 7 passes instead of 8), else 8-bit ones; the last
-// digit is masked to the remaining bits.
+// digit is masked to the remaining bits.  With `os`, each digit is placed in
+// one launch (the digit counts of all passes from one histogram launch, the
+// tile offsets by look-back); otherwise per-tile histograms, their scan and a
+// scatter, three to four launches per digit.
+// Epochs of the single-pass sorts: one counter for every sort of the process
+// (every instance of os_sort), so that no two passes that may write the same
+// status array ever carry the same epoch (with a counter per instance, two
+// instances sharing an array reused each other's epochs, and a tile took a
+// stale word for a current one).
+static std::atomic<uint32_t> os_next_epoch{0};
+constexpr uint32_t OS_EPOCHS = (1u << 30) - 2;  // epochs 1 .. 2^30 - 2 (0: cleared memory)
+
+template <int RB, int RS_ROUNDS>
+static hipError_t os_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
+                          int64_t n, int lo_bit, int bits, int passes, bool* in_alt,
+                          hipStream_t st, const int64_t* n_dev, const Control* stop,
+                          const OsBufs& os) {
+  constexpr uint32_t EPOCHS = OS_EPOCHS;
+  std::atomic<uint32_t>& next_epoch = os_next_epoch;
+  const int64_t tile = RS_THREADS * RS_ROUNDS;
+  const int nblk = (int)((n + tile - 1) / tile);
+  const uint32_t e0 = next_epoch.fetch_add((uint32_t)passes) % EPOCHS;
+  if (e0 + (uint32_t)passes > EPOCHS) {  // the epochs start again: no old word may match
+    hipError_t e = hipMemsetAsync(os.dword, 0, os_dword_words(n) * 8, st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_fill_zero(os.state, sizeof(OsState), st);
+  if (e != hipSuccess) return e;
+  const int last_bits = bits - RB * (passes - 1);
+  const int hb = (int)std::max<int64_t>(1, std::min<int64_t>(OS_HIST_BLOCKS, (n + 4095) / 4096));
+  k_os_hist<RB><<<hb, RS_THREADS, 0, st>>>(keys, n, lo_bit, passes, last_bits, os.state, n_dev,
+                                           stop);
+  uint64_t *ka = keys, *kb = keys_alt;
+  int32_t *va = idx, *vb = idx_alt;
+  for (int pass = 0; pass < passes; pass++) {
+    const int shift = lo_bit + RB * pass;
+    const int db = std::min(RB, lo_bit + bits - shift);
+    const uint32_t dmask = (1u << db) - 1u;
+    const uint32_t epoch = 1u + (e0 + (uint32_t)pass) % EPOCHS;
+    k_os_pass<RB, RS_ROUNDS><<<nblk, RS_THREADS, 0, st>>>(ka, va, kb, vb, n, pass, shift, dmask,
+                                                          os.state, os.dword, epoch, os.err, n_dev,
+                                                          stop);
+    std::swap(ka, kb);
+    std::swap(va, vb);
+    *in_alt = !*in_alt;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
                                   int32_t* idx_alt, int64_t n, int lo_bit, int bits,
                                   int32_t* hist, int32_t* scan_tmp, bool* in_alt,
-                                  hipStream_t st, const int64_t* n_dev, const Control* stop) {
+                                  hipStream_t st, const int64_t* n_dev, const Control* stop,
+                                  const OsBufs* os) {
   *in_alt = false;
   if (n <= 0 || bits <= 0) return hipSuccess;
   const int64_t tile = rs_tile(n);
@@ -599,6 +866,19 @@ hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_a
   const int nblk = (int)((n + tile - 1) / tile);
   const int rb = (bits + 8) / 9 < (bits + 7) / 8 ? 9 : 8;
   const int passes = (bits + rb - 1) / rb;
+  if (os && passes <= OS_MAX_PASSES) {
+    if (rb == 9 && shortt)
+      return os_sort<9, 8>(keys, idx, keys_alt, idx_alt, n, lo_bit, bits, passes, in_alt, st,
+                           n_dev, stop, *os);
+    if (rb == 9)
+      return os_sort<9, 16>(keys, idx, keys_alt, idx_alt, n, lo_bit, bits, passes, in_alt, st,
+                            n_dev, stop, *os);
+    if (shortt)
+      return os_sort<8, 8>(keys, idx, keys_alt, idx_alt, n, lo_bit, bits, passes, in_alt, st,
+                           n_dev, stop, *os);
+    return os_sort<8, 16>(keys, idx, keys_alt, idx_alt, n, lo_bit, bits, passes, in_alt, st,
+                          n_dev, stop, *os);
+  }
   uint64_t *ka = keys, *kb = keys_alt;
   int32_t *va = idx, *vb = idx_alt;  // both null: keys only
   for (int pass = 0; pass < passes; pass++) {
@@ -645,10 +925,10 @@ hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_a
 
 hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
                              int64_t n, int32_t* hist, int32_t* scan_tmp, bool* in_alt,
-                             hipStream_t st) {
+                             hipStream_t st, const OsBufs* os) {
   // 7 passes of 9 bits over the 63-bit keys: the result is in (keys_alt, idx_alt)
   return launch_radix_sort_bits(keys, idx, keys_alt, idx_alt, n, 0, 63, hist, scan_tmp, in_alt,
-                                st);
+                                st, nullptr, nullptr, os);
 }
 
 // ===================================================================

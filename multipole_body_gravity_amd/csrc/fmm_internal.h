@@ -38,6 +38,7 @@ constexpr int ORDER_OCT = 64;
 constexpr int POOL_SHARDS = 512;
 enum { POOL_CU = 0, POOL_U = 1, POOL_PU = 2, N_POOLS = 3 };
 struct Control;
+struct OsBufs;
 // The walk's bookkeeping runs without a host check in between: after a pool
 // or list overflow every kernel that indexes the walk's results does nothing,
 // and the host repeats the walk with larger buffers.
@@ -69,6 +70,8 @@ struct Control {
   int32_t group_oct[ORDER_OCT], group_cur[ORDER_OCT];
   int32_t n_split;  // leaves whose near field is split over several tasks
   int32_t tr_small_over;  // the one-block transposed-key path had too many keys
+  int32_t sort_err;       // a single-pass sort gave up a wait (its order is wrong)
+  int32_t pad1;
 };
 __host__ __device__ inline bool walk_aborted(const Control* c) {
   return (c->pool_overflow | c->list_overflow) != 0;
@@ -99,6 +102,7 @@ struct fmm_plan_s {
   mbg::DBuf keys, keys_alt, idx, idx_alt, pts, far, perm_inv;
   mbg::DBuf lcp, wlev, wtmp, leaf_level, leaf_of;
   mbg::DBuf radix_hist, scan_tmp;
+  mbg::DBuf os_state, os_dword;  // single-pass sorts: counters and histograms, tile status words
   mbg::DBuf root, ctrl, bbox_part;
   // node-sized
   mbg::DBuf nlevel, nprefix, nbegin, ncount, nparent, nfirst, nnchild, ncentre, nq, ngeo;
@@ -193,7 +197,7 @@ hipError_t launch_keys(const void* pos, int64_t n, int dtype, const RootInfo* ro
                        uint64_t* keys, int32_t* idx, hipStream_t st);
 hipError_t launch_radix_sort(uint64_t* keys, int32_t* idx, uint64_t* keys_alt, int32_t* idx_alt,
                              int64_t n, int32_t* hist, int32_t* scan_tmp, bool* in_alt,
-                             hipStream_t st);
+                             hipStream_t st, const OsBufs* os = nullptr);
 hipError_t launch_gather(const void* pos, const void* mass, const int32_t* perm, int64_t n,
                          int dtype, void* pts, hipStream_t st);
 // Box, keys, stable sort and gather of a set of at most FRONT_MID_MAX particles
@@ -316,13 +320,26 @@ hipError_t launch_union_scatter(const int32_t* parents, int64_t n_parents,
 // result ended in (keys_alt, idx_alt).
 // stable LSD sort of keys by bits [lo_bit, lo_bit + bits) (idx/idx_alt may be
 // null for keys only); *in_alt tells which buffer holds the result
+// Single-pass placement of each digit (decoupled look-back over the tiles):
+// the passes' digit counts and tile counters, and the tiles' status words.
+constexpr int OS_MAX_PASSES = 8;
+struct OsState {
+  uint32_t tile_ctr[OS_MAX_PASSES];
+  int32_t hist[OS_MAX_PASSES][512];
+};
+struct OsBufs {
+  OsState* state;   // cleared by the sort itself
+  uint64_t* dword;  // os_dword_words(n) words, all zero when first allocated
+  int32_t* err;     // set to 1 when a wait of the look-back was given up
+};
+size_t os_dword_words(int64_t n);
 hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_alt,
                                   int32_t* idx_alt, int64_t n, int lo_bit, int bits,
                                   int32_t* hist, int32_t* scan_tmp, bool* in_alt,
                                   hipStream_t st, const int64_t* n_dev = nullptr,
-                                  const Control* stop = nullptr);
+                                  const Control* stop = nullptr, const OsBufs* os = nullptr);
 // (n_dev: sort min(*n_dev, n) keys, n being the room in the buffers; stop:
-// sort nothing after a walk abort)
+// sort nothing after a walk abort; os: one launch per digit instead of three)
 
 // ---- numeric passes ----
 hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leaves,
