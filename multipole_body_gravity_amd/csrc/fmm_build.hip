@@ -590,8 +590,10 @@ __device__ __forceinline__ void rs_rank_tile(const uint64_t* kin, const int32_t*
 }
 
 // The tile's elements, in digit order, to their places: a digit's run goes to
-// consecutive addresses from sh.gbase[d].
-template <int RB, int RS_ROUNDS>
+// consecutive addresses from sh.gbase[d].  GUARD: places outside [0, n) are
+// skipped (they arise only after a wait of the look-back was given up, when
+// the sort is reported as failed).
+template <int RB, int RS_ROUNDS, bool GUARD = false>
 __device__ __forceinline__ void rs_write_tile(uint64_t* kout, int32_t* vout, int64_t n,
                                               int64_t tile, int shift, uint32_t dmask,
                                               const RsTile<RB, RS_ROUNDS>& sh) {
@@ -602,6 +604,7 @@ __device__ __forceinline__ void rs_write_tile(uint64_t* kout, int32_t* vout, int
     const uint64_t key = sh.skey[j];
     const int d = (int)((key >> shift) & dmask);
     const int64_t o = (int64_t)sh.gbase[d] + (j - sh.dstart[d]);
+    if (GUARD && (o < 0 || o >= n)) continue;
     kout[o] = key;
     if (vout) vout[o] = sh.sval[j];
   }
@@ -794,8 +797,11 @@ __global__ void __launch_bounds__(RS_THREADS)
     }
   }
   __syncthreads();
-  if (tid == 0 && err_s && err) atomicOr(err, 1);
-  rs_write_tile<RB, RS_ROUNDS>(kout, vout, n, t, shift, dmask, sh);
+  if (err_s) {  // this tile's offsets are unknown: nothing is written, the build fails
+    if (tid == 0 && err) atomicOr(err, 1);
+    return;
+  }
+  rs_write_tile<RB, RS_ROUNDS, true>(kout, vout, n, t, shift, dmask, sh);
 }
 
 size_t os_dword_words(int64_t n) {
