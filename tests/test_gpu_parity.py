@@ -274,6 +274,28 @@ def test_degenerate_inputs(orc, kind):
     plan.close()
 
 
+@pytest.mark.parametrize("n,dist,dt", [(131072, "clustered", "f64"), (131073, "clustered", "f32"),
+                                         (131072, "uniform", "f32")])
+def test_particle_sort_paths(orc, n, dist, dt):
+    """The particle sort places each digit in one launch (look-back over the
+    tiles) up to 2^17 keys and in three launches (histograms, scan, scatter)
+    above: keys, permutation, tree and lists against the oracle at both
+    sides of the threshold, twice on one plan (the second sort's status words
+    meet the first's)."""
+    say(f"  sort paths {dist} n={n} {dt}")
+    pos, mass = inputs(dist, n, 61, dt)
+    plan, _, _ = gpu_run(pos, mass, 4, 0.7, 32, dt)
+    ref = orc.fmm(pos, mass, 4, 0.7, 32, numeric=False)
+    check_structure(plan, ref)
+    torch = _torch()
+    tdt = torch.float64 if dt == "f64" else torch.float32
+    dev = torch.device("cuda:0")
+    plan.build(torch.from_numpy(pos).to(dev, tdt), torch.from_numpy(mass).to(dev, tdt))
+    torch.cuda.synchronize()
+    check_structure(plan, ref)
+    plan.close()
+
+
 @pytest.mark.parametrize("name", ["plummer_1e5", "uniform_1e5", "hernquist_1e5"])
 def test_parity_1e5(orc, name):
     c = W.CONFIGS[name]
