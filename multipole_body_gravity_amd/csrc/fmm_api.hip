@@ -339,9 +339,13 @@ int run_walk(fmm_plan_t p, hipStream_t st) {
   int64_t* toff = P<int64_t>(p->p2p_toff);
   int64_t* poff = P<int64_t>(p->p2p_poff);
 
-  // Room for the transposed keys and the near-field lists, kept from build to
-  // build (first guesses per node; exact after a repeat)
-  p->cap_tr = std::max<int64_t>(p->cap_tr, 48 * nn + 4096);
+  // Room for the transposed keys and the near-field lists.  The transposed
+  // keys' sort, run search and scatter are launched over their room, so it
+  // follows the previous walk's exact count with 1/16 slack (a first guess
+  // per node before any walk; 48 per node was 5x the use on the 4*10^7
+  // sphere); a walk that finds more repeats with the exact count.  The lists'
+  // room only takes memory and is kept from build to build.
+  p->cap_tr = p->n_tr > 0 ? p->n_tr + p->n_tr / 16 + 4096 : 48 * nn + 4096;
   p->cap_p2p = std::max<int64_t>(p->cap_p2p, 128 * nn + 4096);
 
   // The whole walk, its lists and its task counts are issued without a host
