@@ -637,13 +637,17 @@ __global__ void __launch_bounds__(RS_THREADS)
 // which are resident or done), ranks its keys, publishes its digit counts and
 // adds, per digit, the words of the tiles before it, newest first, up to the
 // first one that holds inclusive sums (the sums of that tile and every
-// earlier one); then it publishes its own inclusive sums.  The words are read
-// OS_BATCH tiles at a time.  Each status word carries the pass's epoch
-// (unique to the pass, so the array is never cleared) and its kind, and is
-// written and read with device-scope atomic stores and loads: a word is seen
-// whole or not at all, across the XCDs.  Waits are bounded: a wait that does
-// not end sets an error flag (the build then fails) and the pass runs on,
-// with wrong places but no hang.
+// earlier one); then it publishes its own inclusive sums.  The tile just
+// before is read first (in the steady state it has its inclusive sums
+// already), then OS_BATCH tiles at a time.  Each status word carries the
+// pass's epoch (unique to the pass, so the array is never cleared) and its
+// kind, and is written and read with device-scope atomic stores and loads: a
+// word is seen whole or not at all, across the XCDs.  Waits are bounded: a
+// tile that gives one up writes nothing and sets an error flag (the build
+// then fails), and places outside the array are skipped, so the pass ends
+// with wrong places but no hang and no access out of bounds.  Used for
+// particle sorts of up to 2^17 keys, where it measured faster than three
+// launches per digit.
 constexpr int OS_BATCH = 8;           // earlier tiles' words read together
 constexpr uint32_t OS_AGG = 1u;       // the tile's own digit counts
 constexpr uint32_t OS_INC = 2u;       // the digit sums of the tile and every earlier one
