@@ -225,9 +225,8 @@ int issue_upward(fmm_plan_t p) {
     TRY_HIP(hipEventRecord(p->kev[2 * FMM_KERNEL_P2M + 1], us));
     p->kran[FMM_KERNEL_P2M] = true;
   }
-  for (int l = p->depth - 1; l >= 0; l--)
-    TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
-                       P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->mpole.p, us));
+  TRY_HIP(launch_m2m_levels(dt, ord, p->level_off, p->depth, P<int32_t>(p->nfirst),
+                            P<uint8_t>(p->nnchild), centre, p->mpole.p, us));
   TRY_HIP(launch_m2l_records(dt, ord, p->n_nodes, centre, p->mpole.p, p->mred.p, us));
   TRY_HIP(hipEventRecord(p->ev_rec, us));  // the M2L source records are written
   rec(p, FMM_STAGE_UP, 1, us);
@@ -968,9 +967,8 @@ int vjp_impl(fmm_plan_t p, const void* phi_bar, const void* acc_bar, void* pos_b
   TRY_HIP(launch_vjp_gather(dt, n, p->pts.p, P<int32_t>(p->idx), phi_bar, acc_bar, p->vrec.p, st));
   TRY_HIP(launch_p2m_dip(dt, ord, p->vrec.p, leaves, p->n_leaves, P<int32_t>(p->nbegin),
                          P<int32_t>(p->ncount), centre, p->vmpole.p, st));
-  for (int l = p->depth - 1; l >= 0; l--)
-    TRY_HIP(launch_m2m(dt, ord, p->level_off[l], p->level_off[l + 1] - p->level_off[l],
-                       P<int32_t>(p->nfirst), P<uint8_t>(p->nnchild), centre, p->vmpole.p, st));
+  TRY_HIP(launch_m2m_levels(dt, ord, p->level_off, p->depth, P<int32_t>(p->nfirst),
+                            P<uint8_t>(p->nnchild), centre, p->vmpole.p, st));
   TRY_HIP(launch_m2l_records(dt, ord, nn, centre, p->vmpole.p, p->vmred.p, st));
   M2LArgs ma = m2l_args(p);
   ma.mrec = p->vmred.p;

@@ -143,16 +143,16 @@ struct M2MTab {
 template <int P>
 inline constexpr M2MTab<P> m2m_tab{};
 
+// Parent pi of a level (nodes lvl_begin .. lvl_begin + lvl_count - 1) on a
+// group of 8 lanes, lane c shifting child c; the children's terms are summed
+// by shuffles inside the group, so all 8 lanes take part.
 template <typename T, int P>
-__global__ void __launch_bounds__(256)
-    k_m2m_reg(int64_t lvl_begin, int64_t lvl_count, const int32_t* first_child,
-              const uint8_t* n_child, const double* centre, T* mpole) {
+__device__ __forceinline__ void m2m_group(int64_t pi, int c, int64_t lvl_begin, int64_t lvl_count,
+                                          const int32_t* first_child, const uint8_t* n_child,
+                                          const double* centre, T* mpole) {
   constexpr int K = Tabs<P>::K;
   constexpr int RS = K;  // moments stored densely
   constexpr int NTM = m2m_tab<P>.nt;
-  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int64_t pi = g >> 3;
-  const int c = (int)(g & 7);
   const bool valid_p = pi < lvl_count;
   const int64_t Pn = lvl_begin + (valid_p ? pi : 0);
   const int nc = valid_p ? n_child[Pn] : 0;
@@ -195,6 +195,39 @@ __global__ void __launch_bounds__(256)
       constexpr int k = decltype(kc)::value;
       if ((k & 7) == c) out[k] = (T)acc[k];
     });
+  }
+}
+
+template <typename T, int P>
+__global__ void __launch_bounds__(256)
+    k_m2m_reg(int64_t lvl_begin, int64_t lvl_count, const int32_t* first_child,
+              const uint8_t* n_child, const double* centre, T* mpole) {
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  m2m_group<T, P>(g >> 3, (int)(g & 7), lvl_begin, lvl_count, first_child, n_child, centre,
+                  mpole);
+}
+
+// The top of the tree, where each level has few parents, in one block: level
+// by level up to the root, a block barrier between levels (a level's moments
+// are read by the next one up).  One launch instead of one per level, whose
+// fixed cost exceeds these levels' work.
+constexpr int64_t M2M_TOP_MAX = 64;  // parents per level taken by the one-block pass
+template <int P>
+constexpr int m2m_top_threads() { return P <= 4 ? 512 : 256; }  // as the registers allow
+struct M2MLevels {
+  int64_t off[MAX_LEVELS + 1];
+};
+template <typename T, int P>
+__global__ void __launch_bounds__(m2m_top_threads<P>())
+    k_m2m_top(M2MLevels lv, int l_top, const int32_t* first_child, const uint8_t* n_child,
+              const double* centre, T* mpole) {
+  constexpr int G = m2m_top_threads<P>() / 8;  // parents per round
+  for (int l = l_top; l >= 0; l--) {
+    const int64_t b = lv.off[l], cnt = lv.off[l + 1] - b;
+    for (int64_t p0 = 0; p0 < cnt; p0 += G)
+      m2m_group<T, P>(p0 + threadIdx.x / 8, (int)(threadIdx.x & 7), b, cnt, first_child, n_child,
+                      centre, mpole);
+    __syncthreads();
   }
 }
 
@@ -493,6 +526,35 @@ static bool m2m_reg_dispatch(int order, int64_t lvl_begin, int64_t lvl_count,
   }
 }
 
+template <typename T>
+static bool m2m_top_dispatch(int order, const M2MLevels& lv, int l_top,
+                             const int32_t* first_child, const uint8_t* n_child,
+                             const double* centre, void* mpole, hipStream_t st) {
+  switch (order) {
+#define M2MT(P)                                                                          \
+  case P:                                                                                \
+    k_m2m_top<T, P><<<1, m2m_top_threads<P>(), 0, st>>>(lv, l_top, first_child, n_child, \
+                                                        centre, (T*)mpole);              \
+    return true;
+    M2MT(0) M2MT(1) M2MT(2) M2MT(3) M2MT(4) M2MT(5) M2MT(6)
+#undef M2MT
+    case 7:  // fp64 only
+    case 8:
+      if constexpr (std::is_same<T, double>::value) {
+        if (order == 7)
+          k_m2m_top<T, 7><<<1, m2m_top_threads<7>(), 0, st>>>(lv, l_top, first_child, n_child,
+                                                              centre, (T*)mpole);
+        else
+          k_m2m_top<T, 8><<<1, m2m_top_threads<8>(), 0, st>>>(lv, l_top, first_child, n_child,
+                                                              centre, (T*)mpole);
+        return true;
+      }
+      return false;
+    default:
+      return false;
+  }
+}
+
 // ---------------- P2M: one wave per leaf, lanes over coefficients ----------------
 // Particles are staged 64 at a time: lane j tabulates (-s_j)^a / a! per axis in
 // LDS, then lane m accumulates m_j * ex[a] ey[b] ez[c] over the staged particles
@@ -616,9 +678,9 @@ __global__ void __launch_bounds__(EX_THREADS)
   }
 }
 
-hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
-                      const int32_t* first_child, const uint8_t* n_child, const double* centre,
-                      void* mpole, hipStream_t st) {
+static hipError_t launch_m2m_level(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
+                                   const int32_t* first_child, const uint8_t* n_child,
+                                   const double* centre, void* mpole, hipStream_t st) {
   hipError_t e = ensure_table();
   if (e != hipSuccess) return e;
   const int K = ncoef(order);
@@ -638,6 +700,33 @@ hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count
                                                            first_child, n_child, centre,
                                                            (float*)mpole);
   return hipGetLastError();
+}
+
+hipError_t launch_m2m_levels(int dtype, int order, const int64_t* level_off, int depth,
+                             const int32_t* first_child, const uint8_t* n_child,
+                             const double* centre, void* mpole, hipStream_t st) {
+  // the levels from the root down whose parents all fit the one-block pass
+  int l_top = -1;
+  while (l_top + 1 < depth && level_off[l_top + 2] - level_off[l_top + 1] <= M2M_TOP_MAX) l_top++;
+  for (int l = depth - 1; l > l_top; l--) {
+    const hipError_t e = launch_m2m_level(dtype, order, level_off[l], level_off[l + 1] - level_off[l],
+                                          first_child, n_child, centre, mpole, st);
+    if (e != hipSuccess) return e;
+  }
+  if (l_top < 0) return hipSuccess;
+  M2MLevels lv{};
+  for (int l = 0; l <= l_top + 1; l++) lv.off[l] = level_off[l];
+  if (dtype == FMM_F64 ? m2m_top_dispatch<double>(order, lv, l_top, first_child, n_child, centre,
+                                                  mpole, st)
+                       : m2m_top_dispatch<float>(order, lv, l_top, first_child, n_child, centre,
+                                                 mpole, st))
+    return hipGetLastError();
+  for (int l = l_top; l >= 0; l--) {  // orders without register kernels
+    const hipError_t e = launch_m2m_level(dtype, order, level_off[l], level_off[l + 1] - level_off[l],
+                                          first_child, n_child, centre, mpole, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------- L2L: one wave per child, lanes over coefficients ----------------

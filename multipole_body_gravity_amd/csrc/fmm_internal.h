@@ -345,9 +345,11 @@ hipError_t launch_radix_sort_bits(uint64_t* keys, int32_t* idx, uint64_t* keys_a
 hipError_t launch_p2m(int dtype, int order, const void* pts, const int32_t* leaves,
                       int64_t n_leaves, const int32_t* begin, const int32_t* count,
                       const double* centre, void* mpole, hipStream_t st);
-hipError_t launch_m2m(int dtype, int order, int64_t lvl_begin, int64_t lvl_count,
-                      const int32_t* first_child, const uint8_t* n_child, const double* centre,
-                      void* mpole, hipStream_t st);
+// M2M over every level of the tree, deepest parents first (level_off: the
+// node ranges of levels 0 .. depth; parents at levels depth - 1 .. 0)
+hipError_t launch_m2m_levels(int dtype, int order, const int64_t* level_off, int depth,
+                             const int32_t* first_child, const uint8_t* n_child,
+                             const double* centre, void* mpole, hipStream_t st);
 // M2L: the root's local is cleared, the sibling blocks write every child's own
 // entries (from its parent's M2L union), and the leaves' transposed tails (runs
 // of the sorted transposed keys) are evaluated as tasks of at most TAIL_E
