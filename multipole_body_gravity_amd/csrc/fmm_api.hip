@@ -660,7 +660,8 @@ int fmm_plan(fmm_plan_t* out, int64_t n, int order, double theta, int leaf_size,
       hipEventCreateWithFlags(&p->ev_order, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_up, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_rec, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&p->ev_done, hipEventDisableTiming) != hipSuccess)
+      hipEventCreateWithFlags(&p->ev_done, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_ctrl, hipEventDisableTiming) != hipSuccess)
     return fail(FMM_ERR_HIP);
   *out = p;
   return FMM_OK;
@@ -705,6 +706,7 @@ int fmm_destroy(fmm_plan_t p) {
   if (p->ev_up) (void)hipEventDestroy(p->ev_up);
   if (p->ev_rec) (void)hipEventDestroy(p->ev_rec);
   if (p->ev_done) (void)hipEventDestroy(p->ev_done);
+  if (p->ev_ctrl) (void)hipEventDestroy(p->ev_ctrl);
   if (p->up_stream) (void)hipStreamDestroy(p->up_stream);
   delete p;
   return FMM_OK;
@@ -834,7 +836,49 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
   TRY_HIP(launch_tree_phase1(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
                              P<int8_t>(p->wlev), P<int8_t>(p->wtmp), P<int8_t>(p->leaf_level),
                              P<int64_t>(p->lvl_blkcnt), p->scan_tmp.p, ctrl, st));
-  TRY(sync_ctrl(p, st));
+  // The second phase needs no host value of the node count: with room from
+  // the previous build it is queued before the count is read back and runs
+  // while the host waits for the copy; the phase is repeated with room when
+  // the tree has more nodes than that.
+  const size_t w = wbytes(p->dtype);
+  auto grow_nodes = [&](int64_t m) -> int {
+    TRY(grow(p->nlevel, m));
+    TRY(grow(p->nprefix, 8 * m));
+    TRY(grow(p->nbegin, 4 * m));
+    TRY(grow(p->ncount, 4 * m));
+    TRY(grow(p->nparent, 4 * m));
+    TRY(grow(p->nfirst, 4 * m));
+    TRY(grow(p->nnchild, m));
+    TRY(grow(p->ncentre, 24 * m));
+    TRY(grow(p->nq, 8 * m));
+    TRY(grow(p->ngeo, 16 * m));
+    TRY(grow(p->leaves, 4 * (3 * m + 2)));
+    TRY(grow(p->parents, 4 * m));
+    TRY(grow(p->scan_tmp, scan_tmp_bytes(m + 1)));
+    return FMM_OK;
+  };
+  auto phase2 = [&](int64_t cap) -> int {
+    TreeArrays t{P<uint8_t>(p->nlevel),  P<uint64_t>(p->nprefix), P<int32_t>(p->nbegin),
+                 P<int32_t>(p->ncount),  P<int32_t>(p->nparent),  P<int32_t>(p->nfirst),
+                 P<uint8_t>(p->nnchild), P<double>(p->ncentre),   P<uint64_t>(p->nq),
+                 P<int4>(p->ngeo)};
+    int32_t* lv = P<int32_t>(p->leaves);
+    TRY_HIP(launch_tree_phase2(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
+                               P<int8_t>(p->leaf_level), P<int64_t>(p->lvl_blkcnt), cap, root, t,
+                               lv + cap, lv + 2 * cap + 1, lv, P<int32_t>(p->leaf_of),
+                               P<int32_t>(p->parents), p->scan_tmp.p, ctrl, st));
+    return FMM_OK;
+  };
+  const int64_t cap = p->cap_nodes;
+  if (cap > 0) {
+    TRY(grow_nodes(cap));
+    TRY_HIP(hipMemcpyAsync(p->ctrl_host, p->ctrl.p, sizeof(Control), hipMemcpyDeviceToHost, st));
+    TRY_HIP(hipEventRecord(p->ev_ctrl, st));
+    TRY(phase2(cap));
+    TRY_HIP(hipEventSynchronize(p->ev_ctrl));
+  } else {
+    TRY(sync_ctrl(p, st));
+  }
   p->root_host = p->ctrl_host->root;
   if (p->ctrl_host->nonfinite) return FMM_ERR_NONFINITE;
   if (p->ctrl_host->sort_err) return FMM_ERR_HIP;  // a sort gave up a wait: its order is wrong
@@ -852,34 +896,16 @@ int build_impl(fmm_plan_t p, const void* pos, const void* mass, hipStream_t st) 
     p->n_leaves += c.leaves_at_level[l];
     if (c.level_off[l + 1] > c.level_off[l]) p->depth = l;
   }
-  const size_t w = wbytes(p->dtype);
-  TRY(grow(p->nlevel, nn));
-  TRY(grow(p->nprefix, 8 * nn));
-  TRY(grow(p->nbegin, 4 * nn));
-  TRY(grow(p->ncount, 4 * nn));
-  TRY(grow(p->nparent, 4 * nn));
-  TRY(grow(p->nfirst, 4 * nn));
-  TRY(grow(p->nnchild, nn));
-  TRY(grow(p->ncentre, 24 * nn));
-  TRY(grow(p->nq, 8 * nn));
-  TRY(grow(p->ngeo, 16 * nn));
-  TRY(grow(p->leaves, 4 * (3 * nn + 2)));
-  TRY(grow(p->parents, 4 * nn));
+  if (nn > cap) {  // no room queued (first build), or too little: the phase with room
+    if (cap > 0) TRY_HIP(hipStreamSynchronize(st));  // the queued phase ends before any regrowth
+    TRY(grow_nodes(nn));
+    TRY(phase2(nn));
+  }
+  p->cap_nodes = nn + nn / 8 + 1024;  // the next build's room
   TRY(grow(p->mpole, w * p->K * nn));
   TRY(grow(p->mred, (size_t)mrec_bytes((p->order + 1) * (p->order + 1), (int)w) * nn));
   TRY(grow(p->local, w * p->K * nn));
   TRY(grow(p->lfin, w * p->K * nn));
-  TRY(grow(p->scan_tmp, scan_tmp_bytes(nn + 1)));
-  TreeArrays t{P<uint8_t>(p->nlevel),  P<uint64_t>(p->nprefix), P<int32_t>(p->nbegin),
-               P<int32_t>(p->ncount),  P<int32_t>(p->nparent),  P<int32_t>(p->nfirst),
-               P<uint8_t>(p->nnchild), P<double>(p->ncentre),   P<uint64_t>(p->nq),
-               P<int4>(p->ngeo)};
-  int32_t* leaves = P<int32_t>(p->leaves);
-  TRY_HIP(launch_tree_phase2(P<uint64_t>(p->keys), n, p->leaf, P<int8_t>(p->lcp),
-                             P<int8_t>(p->leaf_level), P<int64_t>(p->lvl_blkcnt), nn, p->level_off,
-                             root, t, leaves + nn, leaves + 2 * nn + 1, leaves,
-                             P<int32_t>(p->leaf_of), P<int32_t>(p->parents), p->scan_tmp.p, ctrl,
-                             st));
   rec(p, FMM_STAGE_TREE, 1, st);
   // the previous step's events completed before the synchronization above;
   // they are read while the tree's second phase runs, before this build

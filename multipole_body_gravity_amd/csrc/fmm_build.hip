@@ -1418,7 +1418,7 @@ hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t*
 // ---- phase 2: node records ----
 __global__ void __launch_bounds__(TR_THREADS)
     k_tree_emit(const uint64_t* keys, int64_t n, const int8_t* lcp, const int8_t* leaf_level,
-                const int64_t* scanned, int nblk, uint8_t* level, uint64_t* prefix,
+                const int64_t* scanned, int nblk, int64_t cap, uint8_t* level, uint64_t* prefix,
                 int32_t* begin) {
   int64_t k = blockIdx.x * (int64_t)TR_THREADS + threadIdx.x;
   int lo = 99, ll = -1;
@@ -1436,9 +1436,12 @@ __global__ void __launch_bounds__(TR_THREADS)
     uint64_t b = __ballot(f);
     if (lane == 0) wtot[w] = __popcll(b);
     __syncthreads();
+    int64_t id = 0;
     if (f) {
-      int64_t id = scanned[(int64_t)l * nblk + blockIdx.x] + __popcll(b & lt);
+      id = scanned[(int64_t)l * nblk + blockIdx.x] + __popcll(b & lt);
       for (int j = 0; j < w; j++) id += wtot[j];
+    }
+    if (f && id < cap) {  // more nodes than the arrays hold: the build repeats this phase
       level[id] = (uint8_t)l;
       begin[id] = (int32_t)k;
       prefix[id] = (l == 0) ? 0ull : (key >> (3 * (KEY_BITS - l)));
@@ -1470,14 +1473,22 @@ __device__ int64_t lower_bound_i32(const int32_t* a, int64_t lo, int64_t hi, int
   return lo;
 }
 
-struct LevelOff {
-  int64_t o[MAX_LEVELS + 2];
-};
-
-__global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t n_nodes, LevelOff lo_,
-                             const RootInfo* root, TreeArrays t, int32_t* leaf_flag) {
+// The node count and the levels' node ranges come from the control block
+// (written by the first phase); the arrays hold `cap` nodes.  With more nodes
+// than that the launch does nothing (the build repeats the phase with room);
+// flags past the last node are cleared for the scan over `cap` entries.
+__global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t cap,
+                             const Control* ctrl, const RootInfo* root, TreeArrays t,
+                             int32_t* leaf_flag) {
+  const int64_t n_nodes = ctrl->level_off[MAX_LEVELS];
+  if (n_nodes > cap) return;
   int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (id >= n_nodes) return;
+  if (id >= cap) return;
+  if (id >= n_nodes) {
+    leaf_flag[id] = 0;
+    return;
+  }
+  const int64_t* lo = ctrl->level_off;  // lo[l] .. lo[l + 1]: the nodes of level l
   const int l = t.level[id];
   const int64_t k = t.begin[id];
   const uint64_t P = t.prefix[id];
@@ -1488,7 +1499,7 @@ __global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t n_n
   // parent: the level l-1 node whose range starts at or before k (last such)
   int32_t par = -1;
   if (l > 0) {
-    int64_t j = lower_bound_i32(t.begin, lo_.o[l - 1], lo_.o[l], (int32_t)(k + 1));
+    int64_t j = lower_bound_i32(t.begin, lo[l - 1], lo[l], (int32_t)(k + 1));
     par = (int32_t)(j - 1);
   }
   t.parent[id] = par;
@@ -1496,8 +1507,9 @@ __global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t n_n
   int32_t fc = -1;
   int nc = 0;
   if (!leaf) {
-    int64_t a = lower_bound_i32(t.begin, lo_.o[l + 1], lo_.o[l + 2], (int32_t)k);
-    int64_t b = lower_bound_i32(t.begin, a, lo_.o[l + 2], (int32_t)(k + cnt));
+    // a non-leaf has l < KEY_BITS, so lo[l + 2] is within the control block's ranges
+    int64_t a = lower_bound_i32(t.begin, lo[l + 1], lo[l + 2], (int32_t)k);
+    int64_t b = lower_bound_i32(t.begin, a, lo[l + 2], (int32_t)(k + cnt));
     fc = (int32_t)a;
     nc = (int)(b - a);
   }
@@ -1523,9 +1535,11 @@ __global__ void k_tree_nodes(const uint64_t* keys, int64_t n, int S, int64_t n_n
     t.centre[3 * id + a] = __dadd_rn(root->lo[a], __dmul_rn((double)q[a] + 0.5, w));
 }
 
-__global__ void k_tree_leaves(const int32_t* leaf_flag, const int32_t* scan, int64_t n_nodes,
-                              const int32_t* begin, const int32_t* count, int32_t* leaves,
-                              int32_t* leaf_of, int32_t* parents) {
+__global__ void k_tree_leaves(const int32_t* leaf_flag, const int32_t* scan, int64_t cap,
+                              const Control* ctrl, const int32_t* begin, const int32_t* count,
+                              int32_t* leaves, int32_t* leaf_of, int32_t* parents) {
+  const int64_t n_nodes = ctrl->level_off[MAX_LEVELS];
+  if (n_nodes > cap) return;
   int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (id >= n_nodes) return;
   if (!leaf_flag[id]) {  // non-leaf: its rank among non-leaves is id - (leaves before id)
@@ -1538,23 +1552,19 @@ __global__ void k_tree_leaves(const int32_t* leaf_flag, const int32_t* scan, int
 
 hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const int8_t* lcp,
                               const int8_t* leaf_level, const int64_t* blkcnt_scanned,
-                              int64_t n_nodes, const int64_t* level_off_host, const RootInfo* root,
-                              const TreeArrays& t, int32_t* leaf_flag, int32_t* leaf_scan,
-                              int32_t* leaves, int32_t* leaf_of, int32_t* parents, void* scan_tmp,
-                              Control* ctrl, hipStream_t st) {
+                              int64_t cap, const RootInfo* root, const TreeArrays& t,
+                              int32_t* leaf_flag, int32_t* leaf_scan, int32_t* leaves,
+                              int32_t* leaf_of, int32_t* parents, void* scan_tmp,
+                              const Control* ctrl, hipStream_t st) {
   int nblk = (int)((n + TR_THREADS - 1) / TR_THREADS);
-  k_tree_emit<<<nblk, TR_THREADS, 0, st>>>(keys, n, lcp, leaf_level, blkcnt_scanned, nblk,
+  k_tree_emit<<<nblk, TR_THREADS, 0, st>>>(keys, n, lcp, leaf_level, blkcnt_scanned, nblk, cap,
                                            t.level, t.prefix, t.begin);
-  LevelOff lo_;
-  for (int l = 0; l <= MAX_LEVELS; l++) lo_.o[l] = level_off_host[l];
-  lo_.o[MAX_LEVELS + 1] = level_off_host[MAX_LEVELS];
-  unsigned g = (unsigned)((n_nodes + 255) / 256);
-  k_tree_nodes<<<g, 256, 0, st>>>(keys, n, leaf, n_nodes, lo_, root, t, leaf_flag);
-  hipError_t e = scan_excl<int32_t>(leaf_flag, leaf_scan, n_nodes, nullptr, scan_tmp, st);
+  unsigned g = (unsigned)((cap + 255) / 256);
+  k_tree_nodes<<<g, 256, 0, st>>>(keys, n, leaf, cap, ctrl, root, t, leaf_flag);
+  hipError_t e = scan_excl<int32_t>(leaf_flag, leaf_scan, cap, nullptr, scan_tmp, st);
   if (e != hipSuccess) return e;
-  k_tree_leaves<<<g, 256, 0, st>>>(leaf_flag, leaf_scan, n_nodes, t.begin, t.count, leaves,
+  k_tree_leaves<<<g, 256, 0, st>>>(leaf_flag, leaf_scan, cap, ctrl, t.begin, t.count, leaves,
                                    leaf_of, parents);
-  (void)ctrl;
   return hipGetLastError();
 }
 

@@ -155,6 +155,7 @@ struct fmm_plan_s {
 
   int64_t shard_cap[mbg::N_POOLS] = {0, 0, 0};  // entries per shard, per pool
   int64_t cap_tr = 0, cap_p2p = 0;  // room for transposed keys / near-field list entries
+  int64_t cap_nodes = 0;  // room for nodes of the tree's second phase (0: none yet)
   int64_t last_own_m2l = 0;         // own M2L entries of the last build (sibling M2L issue)
   bool tr_small_ok = false;  // the last walk's transposed keys fit the one-block path
   bool walk_one_block = false;  // the last walk attempt took it
@@ -178,6 +179,7 @@ struct fmm_plan_s {
   // order they are issued, whatever streams they are given (they rewrite or
   // read the same workspace).
   hipEvent_t ev_done = nullptr;
+  hipEvent_t ev_ctrl = nullptr;  // the tree's control block copied to the host
   hipStream_t last_stream = nullptr;
   bool done_issued = false;
   hipEvent_t ev[2 * FMM_N_STAGES] = {};
@@ -238,12 +240,17 @@ hipError_t launch_tree_phase1(const uint64_t* keys, int64_t n, int leaf, int8_t*
                               int8_t* wtmp, int8_t* leaf_level, int64_t* blkcnt, void* scan_tmp,
                               Control* ctrl, hipStream_t st);
 size_t tree_blkcnt_len(int64_t n);
+// The nodes from the first phase's counts in `ctrl`, into arrays of `cap`
+// nodes (leaf_flag and leaf_scan: cap + 1 entries each).  It needs no host
+// value of the node count, so it can be queued before that count is read
+// back; with more nodes than `cap` it writes no node and the caller repeats it
+// with room.
 hipError_t launch_tree_phase2(const uint64_t* keys, int64_t n, int leaf, const int8_t* lcp,
                               const int8_t* leaf_level, const int64_t* blkcnt_scanned,
-                              int64_t n_nodes, const int64_t* level_off_host, const RootInfo* root,
-                              const TreeArrays& t, int32_t* leaf_flag, int32_t* leaf_scan,
-                              int32_t* leaves, int32_t* leaf_of, int32_t* parents, void* scan_tmp,
-                              Control* ctrl, hipStream_t st);
+                              int64_t cap, const RootInfo* root, const TreeArrays& t,
+                              int32_t* leaf_flag, int32_t* leaf_scan, int32_t* leaves,
+                              int32_t* leaf_of, int32_t* parents, void* scan_tmp,
+                              const Control* ctrl, hipStream_t st);
 
 // ---- walk ----
 // Sharded bump allocator: shard sh owns [sh * shard_cap, (sh+1) * shard_cap).

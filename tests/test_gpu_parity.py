@@ -274,6 +274,42 @@ def test_degenerate_inputs(orc, kind):
     plan.close()
 
 
+def test_tree_room_regrowth(orc):
+    """The tree's second phase is queued with the previous build's node count
+    plus slack as room, before the count is read back: a set with many more
+    nodes (pairs 1e-6 apart, whose cells go down to the deepest level) on a
+    plan sized by a uniform set takes the repeat with room, and the uniform
+    set after it the queued phase again; structure and values against the
+    oracle each time."""
+    torch = _torch()
+    from multipole_body_gravity_amd import Plan
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(73)
+    n = 4096
+    uni = rng.random((n, 3))
+    centres = rng.random((n // 2, 3))
+    d = rng.standard_normal((n // 2, 3))
+    d *= 1e-6 / np.linalg.norm(d, axis=1, keepdims=True)
+    pairs = np.empty((n, 3))
+    pairs[0::2] = centres
+    pairs[1::2] = centres + d
+    mass = 0.5 + rng.random(n)
+    plan = Plan(n, order=4, theta=0.6, leaf_size=1, dtype=torch.float64, device=dev)
+    counts = []
+    for label, pos in (("uniform", uni), ("pairs", pairs), ("uniform again", uni)):
+        say(f"  tree room: {label}")
+        plan.build(torch.from_numpy(pos).to(dev), torch.from_numpy(mass).to(dev))
+        phi, acc = plan.eval()
+        torch.cuda.synchronize()
+        ref = orc.fmm(pos, mass, 4, 0.6, 1)
+        check_structure(plan, ref)
+        check_values(phi.cpu().numpy(), acc.cpu().numpy(), ref, "f64")
+        counts.append(plan.stats()["n_nodes"])
+    # the pairs' tree outgrows the room the first build left (n + n/8 + 1024)
+    assert counts[1] > counts[0] + counts[0] // 8 + 1024, counts
+    plan.close()
+
+
 @pytest.mark.parametrize("n,dist,dt", [(131072, "clustered", "f64"), (131073, "clustered", "f32"),
                                          (131072, "uniform", "f32")])
 def test_particle_sort_paths(orc, n, dist, dt):
