@@ -452,7 +452,17 @@ def test_nonfinite_input_rejected():
     assert ei.value.code == -5
     mass[3] = 1.0
     plan.build(pos, mass)
-    plan.eval()
+    p1, a1 = plan.eval()
+    # again with a plan that has room from a good build: the tree's second
+    # phase is queued before the check and runs on the rejected set's keys
+    pos[17, 2] = float("nan")
+    with pytest.raises(FmmError) as ei:
+        plan.build(pos, mass)
+    assert ei.value.code == -5
+    pos[17, 2] = 0.5
+    plan.build(pos, mass)
+    p2, a2 = plan.eval()
+    assert torch.equal(p1, p2) and torch.equal(a1, a2)
     plan.close()
 
 
